@@ -1,0 +1,68 @@
+"""The workloads the library is checked and measured on.
+
+Each entry names one tensor-parallel rank's unit of work at the shapes of a
+model the pages discuss: the 8.3B-parameter GPT-style model trained with an
+8-way split and a 51,200-entry padded vocabulary ("LIT-022: Megatron-LM ...",
+dmarx anthology, "Key takeaways"), and a 70B dense decoder with hidden size
+8,192 at sequence length 4,096 and micro-batch 1 ("Megatron-LM, in depth",
+aicassindra, "Worked example: 70B parameters on 512 GPUs").
+
+Initialisation follows the same "Key takeaways": N(0, 0.02) (standard
+deviation 0.02) for every weight, and the weight just before each residual
+(here the row-parallel B) scaled by 1/sqrt(2N), N the number of attention plus
+MLP blocks.
+"""
+
+from dataclasses import dataclass, field
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "mlp_fwd" | "mlp_bwd" | "xent"
+    b: int
+    s: int
+    h: int
+    t: int
+    dtype: str           # "f32" | "bf16"
+    seed: int
+    ffn: int = 0         # MLP inner width (all ranks)
+    vocab: int = 0       # padded vocabulary (all ranks)
+    n_blocks: int = 0    # N of the 1/sqrt(2N) residual scaling
+    dz_seed: int = 0     # backward: seed of the incoming gradient
+    dz_std: float = 0.0  # backward: its standard deviation
+    note: str = field(default="", compare=False)
+
+    @property
+    def M(self):
+        return self.b * self.s
+
+    @property
+    def f_i(self):
+        return self.ffn // self.t
+
+    @property
+    def v_r(self):
+        return self.vocab // self.t
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_mlp_t2_f32", "mlp_fwd", b=2, s=64, h=256, t=2, dtype="f32", seed=1,
+                 ffn=1024, n_blocks=2,
+                 note="tiny GeLU MLP block, both shards run and summed, fp32"),
+        Workload("mlp_8p3b_fwd", "mlp_fwd", b=8, s=1024, h=3072, t=8, dtype="bf16", seed=2,
+                 ffn=12288, n_blocks=144,
+                 note="8.3B-shape MLP shard forward, one rank of t=8"),
+        Workload("xent_8p3b", "xent", b=8, s=1024, h=3072, t=8, dtype="bf16", seed=3,
+                 vocab=51200,
+                 note="vocab-parallel fused cross-entropy, one rank of t=8"),
+        Workload("mlp_70b_fwd", "mlp_fwd", b=1, s=4096, h=8192, t=8, dtype="bf16", seed=4,
+                 ffn=28672, n_blocks=160,
+                 note="70B-shape GeLU MLP shard forward, one rank of t=8"),
+        Workload("mlp_70b_bwd", "mlp_bwd", b=1, s=4096, h=8192, t=8, dtype="bf16", seed=4,
+                 ffn=28672, n_blocks=160, dz_seed=5, dz_std=0.01,
+                 note="70B-shape MLP shard backward, one rank of t=8"),
+    ]
+}

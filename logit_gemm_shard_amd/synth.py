@@ -1,0 +1,70 @@
+"""Seeded synthetic inputs, shared by the tests, the benchmark and the smoke run.
+
+This module only draws random numbers: it holds none of the method's
+arithmetic.  Every draw uses a CPU ``torch.Generator`` seeded per workload, in
+a fixed order, in float32, scaled to the stated standard deviation and cast
+once to the workload's dtype (round-to-nearest-even for bfloat16).  Both the
+HIP path and the fp64 oracle then read those same rounded values.
+"""
+
+import math
+
+import torch
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def torch_dtype(name):
+    return _DT[name]
+
+
+def _gen(seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def normal(shape, std, seed_or_gen, dtype="f32"):
+    """std * N(0, 1) draws of ``shape`` from a seeded CPU generator."""
+    g = seed_or_gen if isinstance(seed_or_gen, torch.Generator) else _gen(seed_or_gen)
+    x = torch.randn(*shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(_DT[dtype])
+
+
+def residual_std(n_blocks, base=0.02):
+    """Standard deviation of a weight placed just before a residual."""
+    return base / math.sqrt(2.0 * n_blocks)
+
+
+def mlp_weights(w, dtype=None):
+    """X [M, h], A [h, ffn], B [ffn, h] for an MLP workload (draw order X, A, B)."""
+    dt = dtype or w.dtype
+    g = _gen(w.seed)
+    X = normal((w.M, w.h), 1.0, g, dt)
+    A = normal((w.h, w.ffn), 0.02, g, dt)
+    B = normal((w.ffn, w.h), residual_std(w.n_blocks), g, dt)
+    return X, A, B
+
+
+def mlp_grad(w, dtype=None):
+    """The incoming gradient dZ [M, h] of a backward workload."""
+    return normal((w.M, w.h), w.dz_std, _gen(w.dz_seed), dtype or w.dtype)
+
+
+def xent_inputs(w, dtype=None):
+    """H [M, h], E [vocab, h] and int32 targets [M] uniform over the whole
+    padded vocabulary (draw order H, E, targets)."""
+    dt = dtype or w.dtype
+    g = _gen(w.seed)
+    H = normal((w.M, w.h), 1.0, g, dt)
+    E = normal((w.vocab, w.h), 0.02, g, dt)
+    y = torch.randint(0, w.vocab, (w.M,), generator=g, dtype=torch.int64).to(torch.int32)
+    return H, E, y
+
+
+def small(seed, *shapes, std=1.0, dtype="f32"):
+    """Independent std*N(0,1) tensors of the given shapes from one seed (tests)."""
+    g = _gen(seed)
+    return [normal(s, std, g, dtype) for s in shapes]

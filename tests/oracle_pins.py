@@ -1,0 +1,357 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with:
+brute-force pure-Python loops, printed normal-table values, hand-worked
+examples (``tests/golden/``), central finite differences, or identities that
+the pages state (the split sum, the elementwise commutation of the
+nonlinearity, fused == full-logit cross-entropy).
+
+They take the oracle modules as arguments so that ``test_oracle_mutations.py``
+can plant mistakes in the oracle (on the CPU) and show that some check fails.
+"""
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(np.abs(b).max(), 1e-300)
+    return np.abs(a - b).max() / den
+
+
+def read_rows(name):
+    """Parse a golden file: {key: [row, row, ...]} of float lists."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out.setdefault(key, []).append([float(v) for v in vals])
+    return out
+
+
+# ----------------------------------------------------------------- brute force
+
+def bf_matmul(P, Q):
+    n, k = len(P), len(P[0])
+    m = len(Q[0])
+    assert len(Q) == k
+    return [[sum(P[i][kk] * Q[kk][j] for kk in range(k)) for j in range(m)] for i in range(n)]
+
+
+def bf_gelu(u):
+    return 0.5 * u * (1.0 + math.erf(u / math.sqrt(2.0)))
+
+
+def bf_mlp(X, A, B):
+    """The unsplit block by nested loops (exact GeLU through math.erf)."""
+    U = bf_matmul(X, A)
+    Y = [[bf_gelu(v) for v in row] for row in U]
+    return U, Y, bf_matmul(Y, B)
+
+
+def bf_xent(H, E, y):
+    """Per-token full-vocabulary cross-entropy by nested loops."""
+    out = []
+    for k, hrow in enumerate(H):
+        z = [sum(hrow[c] * erow[c] for c in range(len(hrow))) for erow in E]
+        mx = max(z)
+        s = sum(math.exp(v - mx) for v in z)
+        out.append(mx + math.log(s) - z[y[k]])
+    return out
+
+
+# ------------------------------------------------------------------ MLP checks
+
+def check_gelu_table(mlp):
+    pts = []
+    with open(os.path.join(GOLDEN, "gelu_normal_table.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                u, p = line.split()
+                pts.append((float(u), float(p)))
+    for u, phi in pts:
+        got = float(mlp.gelu(np.array([u]), "erf")[0])
+        assert abs(got - u * phi) <= 1e-15 * max(1.0, abs(u)), (u, got, u * phi)
+    # GeLU'(0) = Phi(0) = 1/2, and GeLU'(u) -> 1 / 0 far out
+    assert abs(float(mlp.gelu_grad(np.array([0.0]), "erf")[0]) - 0.5) < 1e-15
+    assert abs(float(mlp.gelu_grad(np.array([12.0]), "erf")[0]) - 1.0) < 1e-12
+    assert abs(float(mlp.gelu_grad(np.array([-12.0]), "erf")[0])) < 1e-12
+
+
+def check_gelu_shape(mlp):
+    """Odd-part identity GeLU(u) - GeLU(-u) = u (both variants), asymptotes,
+    and the tanh form within its known distance of the exact form."""
+    u = np.linspace(-8, 8, 4001)
+    for v in ("erf", "tanh"):
+        g = mlp.gelu(u, v)
+        assert np.abs(g - mlp.gelu(-u, v) - u).max() < 1e-13, v
+        assert abs(float(mlp.gelu(np.array([40.0]), v)[0]) - 40.0) < 1e-12, v
+        assert abs(float(mlp.gelu(np.array([-40.0]), v)[0])) < 1e-12, v
+        assert float(mlp.gelu(np.array([0.0]), v)[0]) == 0.0, v
+    exact = np.array([bf_gelu(x) for x in u])
+    assert np.abs(mlp.gelu(u, "erf") - exact).max() < 1e-14
+    dev = np.abs(mlp.gelu(u, "tanh") - exact).max()
+    assert 1e-4 < dev < 5e-4, dev  # the tanh approximation's max error is about 4.7e-4
+
+
+def check_gelu_grad_fd(mlp):
+    u = np.linspace(-6, 6, 1201)
+    eps = 1e-6
+    for v in ("erf", "tanh"):
+        fd = (mlp.gelu(u + eps, v) - mlp.gelu(u - eps, v)) / (2 * eps)
+        assert np.abs(mlp.gelu_grad(u, v) - fd).max() < 1e-8, v
+
+
+def check_mlp_hand_example(mlp):
+    g = read_rows("mlp_hand_example.txt")
+    X, A, B = (np.array(g[k]) for k in ("X", "A", "B"))
+    U, Y, Z = mlp.mlp_forward(X, A, B, "erf")
+    assert np.array_equal(U, np.array(g["U"]))
+    assert _rel(Y, g["Y"]) < 1e-15
+    assert _rel(Z, g["Z"]) < 1e-15
+    Z1 = mlp.shard_forward(X, mlp.column_shard(A, 2, 0), mlp.row_shard(B, 2, 0), "erf")[2]
+    Z2 = mlp.shard_forward(X, mlp.column_shard(A, 2, 1), mlp.row_shard(B, 2, 1), "erf")[2]
+    assert _rel(Z1, g["Z1"]) < 1e-15 and _rel(Z2, g["Z2"]) < 1e-15
+    assert _rel(mlp.partial_sum([Z1, Z2]), g["Z"]) < 1e-15
+
+
+def check_mlp_brute_force(mlp):
+    for seed, (M, h, ffn, t) in enumerate([(3, 5, 8, 2), (4, 3, 6, 3), (2, 7, 4, 1), (5, 4, 12, 4)]):
+        r = _rng(100 + seed)
+        X, A, B = r.normal(size=(M, h)), r.normal(size=(h, ffn)), r.normal(size=(ffn, h))
+        bU, bY, bZ = bf_mlp(X.tolist(), A.tolist(), B.tolist())
+        U, Y, Z = mlp.mlp_forward(X, A, B, "erf")
+        assert _rel(U, bU) < 1e-13 and _rel(Y, bY) < 1e-13 and _rel(Z, bZ) < 1e-13
+        f = ffn // t
+        for i in range(t):
+            Ai = [row[i * f:(i + 1) * f] for row in A.tolist()]
+            Bi = B.tolist()[i * f:(i + 1) * f]
+            cU, cY, cZ = bf_mlp(X.tolist(), Ai, Bi)
+            U_i, Y_i, Z_i = mlp.shard_forward(X, mlp.column_shard(A, t, i), mlp.row_shard(B, t, i), "erf")
+            assert _rel(U_i, cU) < 1e-13 and _rel(Y_i, cY) < 1e-13 and _rel(Z_i, cZ) < 1e-13
+
+
+def check_split_identity(mlp):
+    """Z = sum_i GeLU(X A_i) B_i, sigma commutes with the column split, and
+    t = 1 is the unsplit layer."""
+    r = _rng(7)
+    M, h, ffn = 16, 24, 64
+    X, A, B = r.normal(size=(M, h)), r.normal(size=(h, ffn)) * 0.3, r.normal(size=(ffn, h)) * 0.3
+    U, Y, Z = mlp.mlp_forward(X, A, B, "erf")
+    for t in (1, 2, 8):
+        parts, Ys = [], []
+        for i in range(t):
+            U_i, Y_i, Z_i = mlp.shard_forward(X, mlp.column_shard(A, t, i), mlp.row_shard(B, t, i), "erf")
+            parts.append(Z_i)
+            Ys.append(Y_i)
+        assert _rel(mlp.partial_sum(parts), Z) < 1e-12, t
+        assert _rel(np.concatenate(Ys, axis=1), Y) < 1e-15, t
+        if t == 1:
+            assert _rel(parts[0], Z) < 1e-15
+
+
+def check_partial_sum_exact(mlp):
+    r = _rng(11)
+    parts = [r.integers(-1000, 1000, size=(7, 9)).astype(np.float64) for _ in range(5)]
+    want = np.zeros((7, 9))
+    for p in parts:
+        for a in range(7):
+            for b in range(9):
+                want[a, b] += p[a, b]
+    assert np.array_equal(mlp.partial_sum(parts), want)
+
+
+def _loss(mlp, X, A_i, B_i, dZ, v):
+    return float((mlp.shard_forward(X, A_i, B_i, v)[2] * dZ).sum())
+
+
+def check_backward_fd(mlp):
+    """Every entry of dX_i, dA_i, dB_i equals a central difference of
+    L = <dZ, Z_i(X, A_i, B_i)>, on tiny shapes."""
+    eps = 1e-6
+    for v in ("erf", "tanh"):
+        r = _rng(21)
+        M, h, f = 3, 4, 5
+        X, A_i, B_i, dZ = (r.normal(size=s) for s in ((M, h), (h, f), (f, h), (M, h)))
+        U_i = X @ A_i
+        g = mlp.shard_backward(X, A_i, B_i, U_i, dZ, v)
+        for name, P in (("dX", X), ("dA", A_i), ("dB", B_i)):
+            fd = np.zeros_like(P)
+            for idx in np.ndindex(P.shape):
+                old = P[idx]
+                P[idx] = old + eps
+                lp = _loss(mlp, X, A_i, B_i, dZ, v)
+                P[idx] = old - eps
+                lm = _loss(mlp, X, A_i, B_i, dZ, v)
+                P[idx] = old
+                fd[idx] = (lp - lm) / (2 * eps)
+            assert _rel(g[name], fd) < 1e-6, (v, name, _rel(g[name], fd))
+        assert _rel(g["Y"], mlp.gelu(U_i, v)) < 1e-15
+
+
+def check_backward_directional(mlp):
+    """At a moderate size: <dP, dir> equals the central difference of L along
+    a random direction, for P in X, A_i, B_i (a check over every entry at once)."""
+    r = _rng(31)
+    M, h, f = 48, 40, 56
+    X, A_i, B_i = r.normal(size=(M, h)), r.normal(size=(h, f)) * 0.2, r.normal(size=(f, h)) * 0.2
+    dZ = r.normal(size=(M, h))
+    g = mlp.shard_backward(X, A_i, B_i, X @ A_i, dZ, "erf")
+    eps = 1e-5
+    for name in ("dX", "dA", "dB"):
+        D = r.normal(size={"dX": X, "dA": A_i, "dB": B_i}[name].shape)
+        args_p = [X, A_i, B_i]
+        args_m = [X, A_i, B_i]
+        k = {"dX": 0, "dA": 1, "dB": 2}[name]
+        args_p = args_p[:k] + [args_p[k] + eps * D] + args_p[k + 1:]
+        args_m = args_m[:k] + [args_m[k] - eps * D] + args_m[k + 1:]
+        fd = (_loss(mlp, *args_p, dZ, "erf") - _loss(mlp, *args_m, dZ, "erf")) / (2 * eps)
+        an = float((g[name] * D).sum())
+        assert abs(an - fd) <= 1e-7 * max(1.0, abs(fd)), (name, an, fd)
+
+
+def check_backward_shards(mlp):
+    """Concatenated dA_i / dB_i equal the unsplit layer's dA / dB, and the
+    sum of the partials dX_i equals the unsplit dX (the f* all-reduce)."""
+    r = _rng(41)
+    M, h, ffn, t = 20, 16, 48, 4
+    X, A, B, dZ = r.normal(size=(M, h)), r.normal(size=(h, ffn)) * 0.3, r.normal(size=(ffn, h)) * 0.3, r.normal(size=(M, h))
+    full = mlp.mlp_backward(X, A, B, dZ, "erf")
+    dAs, dBs, dXs = [], [], []
+    for i in range(t):
+        A_i, B_i = mlp.column_shard(A, t, i), mlp.row_shard(B, t, i)
+        g = mlp.shard_backward(X, A_i, B_i, X @ A_i, dZ, "erf")
+        dAs.append(g["dA"])
+        dBs.append(g["dB"])
+        dXs.append(g["dX"])
+    assert _rel(np.concatenate(dAs, axis=1), full["dA"]) < 1e-13
+    assert _rel(np.concatenate(dBs, axis=0), full["dB"]) < 1e-13
+    assert _rel(mlp.partial_sum(dXs), full["dX"]) < 1e-12
+
+
+# ------------------------------------------------------------------- CE checks
+
+def check_xent_hand_example(xent):
+    g = read_rows("xent_hand_example.txt")
+    H, E = np.array(g["H"]), np.array(g["E"])
+    y = np.array(g["targets"][0], dtype=np.int64)
+    want = np.array(g["loss"][0])
+    assert _rel(xent.naive_loss(H.repeat(4, 0), E, y), want) < 1e-15
+    assert _rel(xent.vocab_parallel_loss(H.repeat(4, 0), E, y, 2), want) < 1e-15
+    H4 = H.repeat(4, 0)
+    m0, l0, T0, a0 = xent.shard_partials(H4, E[0:2], y, 0)
+    m1, l1, T1, a1 = xent.shard_partials(H4, E[2:4], y, 2)
+    assert np.all(np.abs(m0 - g["m0"][0][0]) < 1e-16) and np.all(np.abs(l0 - g["l0"][0][0]) < 1e-15)
+    assert np.all(np.abs(m1 - g["m1"][0][0]) < 1e-16) and np.all(np.abs(l1 - g["l1"][0][0]) < 1e-15)
+    # targets 0, 1 are rank 0's, targets 2, 3 rank 1's; the other rank's T is +0.0
+    z = E[:, 0]
+    assert list(T0) == [z[0], z[1], 0.0, 0.0] and list(T1) == [0.0, 0.0, z[2], z[3]]
+    assert np.all(a0 == int(g["argmax0"][0][0])) and np.all(a1 == int(g["argmax1"][0][0]))
+    am = xent.merge_argmax(np.stack([m0, m1]), np.stack([a0, a1]))
+    assert np.all(am == int(g["argmax"][0][0]))
+
+
+def check_xent_brute_force(xent):
+    r = _rng(51)
+    M, h, V, t = 6, 5, 16, 4
+    H, E = r.normal(size=(M, h)), r.normal(size=(V, h))
+    y = r.integers(0, V, size=M)
+    want = bf_xent(H.tolist(), E.tolist(), y.tolist())
+    assert _rel(xent.naive_loss(H, E, y, chunk=4), want) < 1e-13
+    assert _rel(xent.vocab_parallel_loss(H, E, y, t), want) < 1e-13
+    # per-rank partials by loops
+    n = V // t
+    for rank in range(t):
+        m, l, T, am = xent.shard_partials(H, E[rank * n:(rank + 1) * n], y, rank * n)
+        for k in range(M):
+            z = [sum(H[k, c] * E[j, c] for c in range(h)) for j in range(rank * n, (rank + 1) * n)]
+            mx = max(z)
+            assert abs(m[k] - mx) < 1e-13
+            assert abs(l[k] - sum(math.exp(v - mx) for v in z)) < 1e-12
+            if rank * n <= y[k] < (rank + 1) * n:
+                assert abs(T[k] - z[y[k] - rank * n]) < 1e-13
+            else:
+                assert T[k] == 0.0 and not math.copysign(1.0, T[k]) < 0
+            assert am[k] == rank * n + z.index(mx)
+
+
+def check_xent_fused_equals_naive(xent):
+    r = _rng(61)
+    M, h, V = 64, 32, 1024
+    H, E = r.normal(size=(M, h)), r.normal(size=(V, h)) * 0.5
+    y = r.integers(0, V, size=M)
+    base = xent.naive_loss(H, E, y, chunk=17)
+    for t in (1, 2, 8, 16):
+        assert _rel(xent.vocab_parallel_loss(H, E, y, t), base) < 1e-12, t
+    # the merge does not depend on the rank order
+    parts = [xent.shard_partials(H, E[a:a + 128], y, a) for a in range(0, V, 128)]
+    m, l, T = (np.stack([p[j] for p in parts]) for j in range(3))
+    perm = r.permutation(len(parts))
+    assert np.abs(xent.merge(m[perm], l[perm], T[perm]) - xent.merge(m, l, T)).max() < 1e-13
+    # t = 1: the partials give the loss directly
+    m1, l1, T1, _ = xent.shard_partials(H, E, y, 0)
+    assert _rel(m1 + np.log(l1) - T1, base) < 1e-13
+
+
+def check_xent_uniform(xent):
+    """E = 0: every logit is 0, so the loss is ln V, each rank's max is 0 and
+    its sum-exp is its slice size."""
+    V, t = 51200, 8
+    H = _rng(71).normal(size=(3, 8))
+    E = np.zeros((V, 8))
+    y = np.array([0, 25600, 51199])
+    loss = xent.vocab_parallel_loss(H, E, y, t)
+    assert np.abs(loss - math.log(51200)).max() < 1e-12
+    assert abs(math.log(51200) - 10.843494811027599) < 1e-15
+    m, l, T, am = xent.shard_partials(H, E[:6400], y, 0)
+    assert np.all(m == 0.0) and np.all(l == 6400.0) and np.all(T == 0.0)
+    assert np.all(am == 0)  # all tied: the lowest id
+
+
+def check_xent_shift(xent):
+    """A large common shift of every logit of a token leaves its loss
+    unchanged (the max subtraction; a plain exp would overflow)."""
+    r = _rng(81)
+    M, h, V = 8, 6, 64
+    H, E = r.normal(size=(M, h)), r.normal(size=(V, h))
+    y = r.integers(0, V, size=M)
+    base = xent.naive_loss(H, E, y)
+    H2 = np.concatenate([H, np.full((M, 1), 1000.0)], axis=1)
+    E2 = np.concatenate([E, np.ones((V, 1))], axis=1)
+    for fn in (lambda: xent.naive_loss(H2, E2, y), lambda: xent.vocab_parallel_loss(H2, E2, y, 4)):
+        got = fn()
+        assert np.all(np.isfinite(got))
+        assert np.abs(got - base).max() < 1e-9
+
+
+def check_xent_argmax_ties(xent):
+    """Exact ties resolve to the lowest global id, within and across ranks."""
+    H = np.array([[1.0, 0.0], [0.0, 1.0]])
+    E = np.array([[0.0, 0.0], [2.0, 1.0], [1.0, 3.0], [2.0, 3.0], [0.0, 0.0], [2.0, 0.0]])
+    # token 0 logits: 0 2 1 2 0 2 -> max 2 at ids 1, 3, 5 -> 1
+    # token 1 logits: 0 1 3 3 0 0 -> max 3 at ids 2, 3 -> 2
+    parts = [xent.shard_partials(H, E[a:a + 2], np.array([0, 0]), a) for a in (0, 2, 4)]
+    m = np.stack([p[0] for p in parts])
+    am = np.stack([p[3] for p in parts])
+    assert list(xent.merge_argmax(m, am)) == [1, 2]
+
+
+MLP_CHECKS = [check_gelu_table, check_gelu_shape, check_gelu_grad_fd, check_mlp_hand_example,
+              check_mlp_brute_force, check_split_identity, check_partial_sum_exact,
+              check_backward_fd, check_backward_directional, check_backward_shards]
+XENT_CHECKS = [check_xent_hand_example, check_xent_brute_force, check_xent_fused_equals_naive,
+               check_xent_uniform, check_xent_shift, check_xent_argmax_ties]

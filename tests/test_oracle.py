@@ -1,0 +1,16 @@
+"""The fp64 oracle against its pins (CPU only)."""
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+
+@pytest.mark.parametrize("check", pins.MLP_CHECKS, ids=lambda f: f.__name__)
+def test_mlp_oracle(check):
+    check(oracle.mlp)
+
+
+@pytest.mark.parametrize("check", pins.XENT_CHECKS, ids=lambda f: f.__name__)
+def test_xent_oracle(check):
+    check(oracle.xent)

@@ -1,0 +1,196 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and show that the pins
+catch each one: a dropped term, a wrong sign, a wrong index or slice, a
+transposed operand, a missing max subtraction.  A mutation that no pin
+caught would mean the pins leave that part of the oracle unchecked."""
+
+import numpy as np
+import pytest
+from scipy.special import erf
+
+import oracle
+import oracle_pins as pins
+
+mlp, xent = oracle.mlp, oracle.xent
+_orig_gelu, _orig_grad = mlp.gelu, mlp.gelu_grad
+
+
+def _caught(checks, module):
+    for c in checks:
+        try:
+            c(module)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            return True
+    return False
+
+
+def _gelu_no_half(u, variant="erf"):
+    u = np.asarray(u, dtype=np.float64)
+    return u * (1.0 + erf(u / np.sqrt(2.0))) if variant == "erf" else _orig_gelu(u, variant)
+
+
+def _gelu_no_sqrt2(u, variant="erf"):
+    u = np.asarray(u, dtype=np.float64)
+    return 0.5 * u * (1.0 + erf(u)) if variant == "erf" else _orig_gelu(u, variant)
+
+
+def _gelu_tanh_no_cubic(u, variant="erf"):
+    u = np.asarray(u, dtype=np.float64)
+    if variant == "tanh":
+        return 0.5 * u * (1.0 + np.tanh(np.sqrt(2 / np.pi) * u))
+    return _orig_gelu(u, variant)
+
+
+def _grad_dropped_term(u, variant="erf"):
+    u = np.asarray(u, dtype=np.float64)
+    return 0.5 * (1.0 + erf(u / np.sqrt(2.0))) if variant == "erf" else _orig_grad(u, variant)
+
+
+def _grad_wrong_sign(u, variant="erf"):
+    u = np.asarray(u, dtype=np.float64)
+    if variant == "erf":
+        return 0.5 * (1.0 + erf(u / np.sqrt(2.0))) - u * np.exp(-0.5 * u * u) / np.sqrt(2 * np.pi)
+    return _orig_grad(u, variant)
+
+
+def _column_shard_off_by_one(A, t, i):
+    A = np.asarray(A, dtype=np.float64)
+    f = A.shape[1] // t
+    j = (i + 1) % t
+    return A[:, j * f:(j + 1) * f]
+
+
+def _row_shard_uses_columns(B, t, i):
+    B = np.asarray(B, dtype=np.float64)
+    f = B.shape[0] // t
+    return B[i * f:(i + 1) * f, :][:, ::-1]
+
+
+def _backward_missing_gelu_grad(X, A_i, B_i, U_i, dZ, variant="erf"):
+    g = _REAL_BWD(X, A_i, B_i, U_i, dZ, variant)
+    X = np.asarray(X, dtype=np.float64)
+    g["dA"] = X.T @ g["dY"]
+    return g
+
+
+def _backward_dx_no_transpose(X, A_i, B_i, U_i, dZ, variant="erf"):
+    g = _REAL_BWD(X, A_i, B_i, U_i, dZ, variant)
+    A_i = np.asarray(A_i, dtype=np.float64)
+    if A_i.shape[0] == A_i.shape[1]:
+        g["dX"] = g["dU"] @ A_i
+    else:
+        g["dX"] = g["dU"][:, :A_i.shape[0]] @ A_i[:, :A_i.shape[0]]
+    return g
+
+
+def _backward_db_uses_u(X, A_i, B_i, U_i, dZ, variant="erf"):
+    g = _REAL_BWD(X, A_i, B_i, U_i, dZ, variant)
+    g["dB"] = np.asarray(U_i, dtype=np.float64).T @ np.asarray(dZ, dtype=np.float64)
+    return g
+
+
+def _partial_sum_skips_first(parts):
+    parts = [np.asarray(p, dtype=np.float64) for p in parts]
+    out = np.zeros_like(parts[0])
+    for p in parts[1:]:
+        out = out + p
+    return out if len(parts) > 1 else parts[0]
+
+
+_REAL_BWD = mlp.shard_backward
+
+MLP_MUTANTS = {
+    "gelu_no_half": ("gelu", _gelu_no_half),
+    "gelu_no_sqrt2": ("gelu", _gelu_no_sqrt2),
+    "gelu_tanh_no_cubic": ("gelu", _gelu_tanh_no_cubic),
+    "grad_dropped_term": ("gelu_grad", _grad_dropped_term),
+    "grad_wrong_sign": ("gelu_grad", _grad_wrong_sign),
+    "column_shard_wrong_block": ("column_shard", _column_shard_off_by_one),
+    "row_shard_scrambled": ("row_shard", _row_shard_uses_columns),
+    "bwd_missing_gelu_grad": ("shard_backward", _backward_missing_gelu_grad),
+    "bwd_dx_no_transpose": ("shard_backward", _backward_dx_no_transpose),
+    "bwd_db_uses_preact": ("shard_backward", _backward_db_uses_u),
+    "partial_sum_skips_rank0": ("partial_sum", _partial_sum_skips_first),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MLP_MUTANTS))
+def test_mlp_mutant_is_caught(name, monkeypatch):
+    attr, fn = MLP_MUTANTS[name]
+    monkeypatch.setattr(mlp, attr, fn)  # module-level, so the oracle's own callers see it too
+    assert _caught(pins.MLP_CHECKS, mlp), f"no pin caught the planted mistake {name}"
+
+
+def _naive_no_max(H, E, y, chunk=1024):
+    H, E = np.asarray(H, dtype=np.float64), np.asarray(E, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        z = H @ E.T
+        return np.log(np.exp(z).sum(axis=1)) - z[np.arange(z.shape[0]), np.asarray(y)]
+
+
+def _naive_log2(H, E, y, chunk=1024):
+    H, E = np.asarray(H, dtype=np.float64), np.asarray(E, dtype=np.float64)
+    z = H @ E.T
+    mx = z.max(axis=1)
+    return mx + np.log2(np.exp(z - mx[:, None]).sum(axis=1)) - z[np.arange(z.shape[0]), np.asarray(y)]
+
+
+_REAL_PARTIALS = xent.shard_partials
+
+
+def _partials_global_target(H, E_r, y, vocab_start):
+    m, l, T, am = _REAL_PARTIALS(H, E_r, y, vocab_start)
+    z = np.asarray(H, dtype=np.float64) @ np.asarray(E_r, dtype=np.float64).T
+    y = np.asarray(y)
+    own = y < z.shape[1]
+    T = np.where(own, z[np.arange(z.shape[0]), np.minimum(y, z.shape[1] - 1)], 0.0)
+    return m, l, T, am
+
+
+def _partials_local_argmax(H, E_r, y, vocab_start):
+    m, l, T, am = _REAL_PARTIALS(H, E_r, y, vocab_start)
+    return m, l, T, am - vocab_start
+
+
+def _partials_last_tie(H, E_r, y, vocab_start):
+    m, l, T, am = _REAL_PARTIALS(H, E_r, y, vocab_start)
+    z = np.asarray(H, dtype=np.float64) @ np.asarray(E_r, dtype=np.float64).T
+    am = vocab_start + z.shape[1] - 1 - np.argmax(z[:, ::-1], axis=1)
+    return m, l, T, am
+
+
+def _merge_wrong_sign(m, l, T):
+    m, l, T = (np.asarray(a, dtype=np.float64) for a in (m, l, T))
+    Mx = m.max(axis=0)
+    return Mx + np.log((l * np.exp(Mx[None, :] - m)).sum(axis=0)) - T.sum(axis=0)
+
+
+def _merge_drops_max(m, l, T):
+    m, l, T = (np.asarray(a, dtype=np.float64) for a in (m, l, T))
+    Mx = m.max(axis=0)
+    return np.log((l * np.exp(m - Mx[None, :])).sum(axis=0)) - T.sum(axis=0)
+
+
+def _merge_argmax_last_rank(m, am):
+    m = np.asarray(m, dtype=np.float64)
+    r = m.shape[0] - 1 - np.argmax(m[::-1], axis=0)
+    return np.asarray(am)[r, np.arange(m.shape[1])]
+
+
+XENT_MUTANTS = {
+    "naive_no_max_subtraction": ("naive_loss", _naive_no_max),
+    "naive_log2": ("naive_loss", _naive_log2),
+    "partials_global_target_index": ("shard_partials", _partials_global_target),
+    "partials_local_argmax_id": ("shard_partials", _partials_local_argmax),
+    "partials_last_tie": ("shard_partials", _partials_last_tie),
+    "merge_wrong_sign": ("merge", _merge_wrong_sign),
+    "merge_drops_max": ("merge", _merge_drops_max),
+    "merge_argmax_last_rank": ("merge_argmax", _merge_argmax_last_rank),
+}
+
+
+@pytest.mark.parametrize("name", sorted(XENT_MUTANTS))
+def test_xent_mutant_is_caught(name, monkeypatch):
+    attr, fn = XENT_MUTANTS[name]
+    monkeypatch.setattr(xent, attr, fn)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        assert _caught(pins.XENT_CHECKS, xent), f"no pin caught the planted mistake {name}"
