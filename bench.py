@@ -1,0 +1,263 @@
+"""Benchmark: one tensor-parallel rank's transformer-block shard on one MI355X.
+
+A step is one pass of the whole path over one batch, for rank 0 of t = 8 at
+the 8.3B-parameter model's shapes (b = 8, s = 1024, h = 3072, ffn = 12288,
+padded vocabulary 51,200):
+
+  1. tp_mlp_fwd               U_0 = X A_0, Y_0 = GeLU(U_0), Z_0 = Y_0 B_0
+  2. shard_partial_sum(SUM)   Z = sum of the 8 ranks' partials (rank 0's just
+                              written, the other 7 resident synthetic partials)
+  3. tp_mlp_bwd               dY, dU = dY GeLU'(U_0), dB_0, dA_0, dX_0
+  4. shard_partial_sum(SUM)   dX = sum of the 8 ranks' dX partials
+  5. vocab_parallel_xent_fwd  fused logit GEMM + CE partials of slice 0
+  6. shard_partial_sum(XENT)  per-token loss from the 8 ranks' partials
+
+All inputs are resident in HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --copy-calibration   # plain copy for counter scaling
+"""
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % bf16 MFMA peak for TP-shard MLP fwd+bwd; CE tokens/s"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD's published figure
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_8p3b_hbm_counters.txt")
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP sources: counters are only valid for the code they were taken on."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "logit_gemm_shard_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def step_flops(M, h, f, Vr):
+    """Algorithmic FLOPs (2*M*N*K per GEMM): forward 2 GEMMs, backward 4, plus the logit GEMM."""
+    return {"mlp_fwd": 2 * 2 * M * h * f, "mlp_bwd": 4 * 2 * M * h * f, "xent": 2 * M * h * Vr}
+
+
+def read_counters():
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256") != kernel_sources_digest():
+        return None  # the kernels changed since the counters were taken
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 28  # 256 Mi floats = 1 GiB read + 1 GiB written per copy
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 5}))
+
+
+def cpu_baseline(w, xw, inputs, budget_s=10.0):
+    """The fp64 oracle on the host, on a token sample of the same step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    X, A0, B0, dZ, H, E0, y = inputs
+    f, h, Vr, t = w.f_i, w.h, xw.v_r, w.t
+    rng = np.random.default_rng(0)
+    best = None
+    for m in (256, 512, 1024, 2048, 4096, 8192):
+        Xs, dZs = X[:m].astype(np.float64), dZ[:m].astype(np.float64)
+        Hs, ys = H[:m].astype(np.float64), y[:m]
+        others = [rng.normal(size=(m, h)) for _ in range(t - 1)]
+        stats = [(rng.normal(size=m), rng.uniform(1, 10, m), np.zeros(m)) for _ in range(t - 1)]
+        t0 = time.perf_counter()
+        U, Y, Z = oracle.mlp.shard_forward(Xs, A0, B0)
+        oracle.mlp.partial_sum([Z] + others)
+        g = oracle.mlp.shard_backward(Xs, A0, B0, U, dZs)
+        oracle.mlp.partial_sum([g["dX"]] + others)
+        mr, lr, Tr, _ = oracle.xent.shard_partials(Hs, E0, ys, 0)
+        oracle.xent.merge(np.stack([mr] + [s[0] for s in stats]), np.stack([lr] + [s[1] for s in stats]),
+                          np.stack([Tr] + [s[2] for s in stats]))
+        dt = time.perf_counter() - t0
+        fl = sum(step_flops(m, h, f, Vr).values())
+        best = (m, dt, fl)
+        if dt >= budget_s:
+            break
+    m, dt, fl = best
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the same step (MLP fwd+bwd, both sums, slice-0 CE, merge) on the first {m} "
+                      f"of {w.M} tokens in fp64 numpy: {fl / 1e9:.1f} GFLOP in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's shard: this build runs on a single GPU only "
+              "(all t ranks of the split are timed or checked on that one device); use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from logit_gemm_shard_amd import binding as lgs
+    from logit_gemm_shard_amd import synth
+    from logit_gemm_shard_amd.configs import WORKLOADS
+
+    w, xw = WORKLOADS["mlp_8p3b_fwd"], WORKLOADS["xent_8p3b"]
+    M, h, f, t, ffn = w.M, w.h, w.f_i, w.t, w.ffn
+    V, Vr = xw.vocab, xw.v_r
+    bf = torch.bfloat16
+    dev = torch.device("cuda", 0)
+
+    # ---------------- inputs (host, seeded) -> HBM
+    X, A, B = synth.mlp_weights(w)
+    dZ = synth.normal((M, h), 0.01, 6, "bf16")
+    H, E, y = synth.xent_inputs(xw)
+    A0, B0, E0 = A[:, :f].contiguous(), B[:f].contiguous(), E[:Vr].contiguous()
+    Xd, A0d, B0d, dZd = X.to(dev), A0.to(dev), B0.to(dev), dZ.to(dev)
+    Hd, E0d, yd = H.to(dev), E0.to(dev), y.to(dev)
+    U = torch.empty(M, f, dtype=bf, device=dev)
+    Y = torch.empty(M, f, dtype=bf, device=dev)
+    zparts = torch.randn(t, M, h, device=dev).mul_(0.05).to(bf)   # ranks 1..7: "received" partials
+    dxparts = torch.randn(t, M, h, device=dev).mul_(0.01).to(bf)
+    Z = torch.empty(M, h, dtype=bf, device=dev)
+    dX = torch.empty(M, h, dtype=bf, device=dev)
+    dA = torch.empty(h, f, dtype=bf, device=dev)
+    dB = torch.empty(f, h, dtype=bf, device=dev)
+    stats = torch.empty(t, 3, M, dtype=torch.float32, device=dev)
+    stats[:, 0].normal_()
+    stats[:, 1].uniform_(1.0, 100.0)
+    stats[:, 2].zero_()
+    am = torch.empty(M, dtype=torch.int32, device=dev)
+    loss = torch.empty(M, dtype=torch.float32, device=dev)
+    ws_bwd = torch.empty(lgs.mlp_bwd_workspace_bytes(w.b, w.s, h, ffn, t, bf), dtype=torch.uint8, device=dev)
+    ws_xent = torch.empty(lgs.xent_workspace_bytes(xw.b, xw.s, h, V, t), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    names = ["mlp_fwd", "sum_z", "mlp_bwd", "sum_dx", "xent", "xent_merge"]
+
+    def one_step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        lgs.tp_mlp_fwd(w.b, w.s, h, ffn, t, 0, Xd, A0d, B0d, zparts[0], U_i=U, Y_i=Y, stream=stream)
+        mark(1)
+        lgs.shard_partial_sum("sum", t, M * h, zparts, M * h, Z, stream=stream)
+        mark(2)
+        lgs.tp_mlp_bwd(w.b, w.s, h, ffn, t, 0, Xd, A0d, B0d, U, dZd, dxparts[0], dA, dB,
+                       workspace=ws_bwd, stream=stream)
+        mark(3)
+        lgs.shard_partial_sum("sum", t, M * h, dxparts, M * h, dX, stream=stream)
+        mark(4)
+        lgs.vocab_parallel_xent_fwd(xw.b, xw.s, h, V, t, 0, Hd, E0d, yd, stats[0, 0], stats[0, 1],
+                                    stats[0, 2], argmax_r=am, workspace=ws_xent, stream=stream)
+        mark(5)
+        lgs.shard_partial_sum("xent", t, M, stats, 3 * M, loss, stream=stream)
+        mark(6)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+
+    per = {n: 0.0 for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            per[n] += ev[j].elapsed_time(ev[j + 1])
+    per = {n: v / args.steps for n, v in per.items()}   # ms per launch of each entry point
+
+    fl = step_flops(M, h, f, Vr)
+    total_flops = sum(fl.values())
+    tflops = total_flops / (ms * 1e-3) / 1e12
+    sum_bytes = (t + 1) * M * h * 2
+    xent_s = per["xent"] * 1e-3
+    traffic = read_counters()
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, residual weight scaled 1/sqrt(2N), uniform targets)",
+        "config": {"workload": "8.3B-shape TP shard step, rank 0 of t=8: GeLU MLP fwd+bwd "
+                               "(b=8, s=1024, h=3072, ffn=12288) + sums of 8 partials + vocab-parallel "
+                               "fused CE (vocab 51200) + CE merge",
+                   "b": w.b, "s": w.s, "h": h, "ffn": ffn, "t": t, "rank": 0, "vocab": V},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "mlp_fwd_bwd_tflops": round((fl["mlp_fwd"] + fl["mlp_bwd"]) / ((per["mlp_fwd"] + per["mlp_bwd"]) * 1e-3) / 1e12, 2),
+        "mlp_fwd_tflops": round(fl["mlp_fwd"] / (per["mlp_fwd"] * 1e-3) / 1e12, 2),
+        "mlp_bwd_tflops": round(fl["mlp_bwd"] / (per["mlp_bwd"] * 1e-3) / 1e12, 2),
+        "ce_tokens_per_s": round(M / xent_s, 0),
+        "ce_tflops": round(fl["xent"] / xent_s / 1e12, 2),
+        "sum_partials_gbs": round(sum_bytes / (per["sum_z"] * 1e-3) / 1e9, 1),
+        "entry_point_ms": {n: round(v, 4) for n, v in per.items()},
+        "roofline": {
+            "kernel": "vocab_parallel_xent_fwd (fused logit GEMM + CE partials, with its slab merge)",
+            "bound": "mfma",
+            "achieved": round(fl["xent"] / xent_s / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fl["xent"] / xent_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        inputs = (X.float().numpy(), A0.float().double().numpy(), B0.float().double().numpy(),
+                  dZ.float().numpy(), H.float().numpy(), E0.float().double().numpy(),
+                  y.numpy().astype(np.int64))
+        out["cpu_baseline"] = cpu_baseline(w, xw, inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * lgs.h -- C ABI of liblgs.so: one tensor-parallel (TP) rank's shard of a
+ * transformer block on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (Megatron-LM 1D tensor parallelism) as the source pages state it:
+ *   - "Tensor Parallelism and Pipeline Parallelism: Mathematical Foundations of
+ *     Megatron-LM 1D Slicing, Sequence Parallelism, and 1F1B Scheduling"
+ *     (llms.blog), sections "Column-Parallel Linear Layer", "Row-Parallel
+ *     Linear Layer" and "Conjugate Communication Operators";
+ *   - "Cutting a Model Into Pieces" (learn.kartikeya.me, lecture 3), section
+ *     "Megatron-LM: cutting inside the layer": Y = GeLU(X A), Z = Y B, A split
+ *     by columns, B by rows, one all-reduce per block;
+ *   - "LIT-022: Megatron-LM: Training Multi-Billion Parameter Language Models
+ *     Using Model Parallelism" (dmarx.github.io anthology), "Key takeaways":
+ *     the parallel logit GEMM fused into the cross-entropy, the vocabulary
+ *     padded so each rank's slice is a multiple of 128.
+ *
+ * Conventions shared by every entry point
+ *   - Shapes follow the pages: b (micro-batch), s (sequence length), h (hidden
+ *     size), ffn (MLP inner width over all ranks), t (TP size), rank in [0, t),
+ *     vocab (padded vocabulary over all ranks).  Tokens are the M = b*s rows of
+ *     every activation (the pages' (s, b, h) tensor flattened; each operation
+ *     here is per token, so the order of the rows is the caller's).
+ *   - Matrices are row-major with an explicit leading dimension ld (elements
+ *     between consecutive rows, ld >= row width).
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or keeps a pointer after the call returns, never
+ *     synchronizes, and keeps no mutable global state; calls on different
+ *     streams with disjoint outputs may run concurrently.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued asynchronously on it; a device-side fault surfaces at the
+ *     caller's next synchronization, as for any HIP launch.
+ *   - dtype LGS_BF16: bf16 in and out, fp32 accumulation, outputs rounded to
+ *     nearest-even.  LGS_F32: fp32 throughout.
+ *   - Alignment: h and ffn/t must be multiples of 8; for LGS_BF16
+ *     every matrix base pointer must be 16-byte aligned and every ld a multiple
+ *     of 8 (the kernels move 16-byte vectors).  Token counts are unrestricted.
+ *   - Errors are reported synchronously by the return value, before anything
+ *     is enqueued, except LGS_ERR_HIP (the runtime rejected a launch; earlier
+ *     launches of the same call may have run).  On any other non-zero return
+ *     nothing was enqueued.  lgs_last_error() gives a
+ *     thread-local message for the last failure on the calling thread.
+ *   - Device data such as target ids is not validated (documented
+ *     preconditions below).
+ */
+#ifndef LGS_H_
+#define LGS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LGS_OK = 0,
+  LGS_ERR_INVALID_ARG = 1, /* bad size, rank, leading dimension or NULL pointer */
+  LGS_ERR_UNSUPPORTED = 2, /* dtype / activation / alignment not supported    */
+  LGS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query       */
+  LGS_ERR_HIP = 4          /* the HIP runtime rejected a launch                 */
+} lgs_status;
+
+typedef enum { LGS_F32 = 0, LGS_BF16 = 1 } lgs_dtype;
+
+/* GeLU(u) = u * Phi(u) (ERF, the exact form) or its tanh approximation
+   u/2 * (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) (TANH). */
+typedef enum { LGS_GELU_ERF = 0, LGS_GELU_TANH = 1 } lgs_gelu;
+
+typedef enum { LGS_REDUCE_SUM = 0, LGS_REDUCE_XENT = 1 } lgs_reduce_op;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int lgs_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* lgs_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* lgs_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Workspace queries: bytes of device scratch the matching call needs.       */
+/* Return 0 when none is needed (or the arguments are invalid).              */
+
+/* tp_mlp_fwd: 0 if the caller passes Y_i, else M * ffn/t * sizeof(dtype). */
+size_t lgs_mlp_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype, int y_given);
+/* tp_mlp_bwd: room for the recomputed Y_i and for dU_i, both [M, ffn/t]. */
+size_t lgs_mlp_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype);
+/* vocab_parallel_xent_fwd: per-token partials of each column slab of the slice. */
+size_t lgs_xent_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype);
+
+/* ------------------------------------------------------------------------ */
+/*
+ * tp_mlp_fwd -- one rank's forward shard of the GeLU MLP block.
+ *
+ * "Mathematical Foundations of Megatron-LM", "Column-Parallel Linear Layer":
+ * A = [A_1 ... A_t] split by columns, every rank holds the full input X (the
+ * f operator is the identity forward), and the nonlinearity applies to each
+ * column block independently.  "Row-Parallel Linear Layer": B = [B_1; ...; B_t]
+ * split by rows, rank i computes the partial Z_i = Y_i B_i, and Z = sum_i Z_i
+ * (the g all-reduce; on one device, shard_partial_sum).  With f = ffn / t:
+ *
+ *   U_i = X A_i      [M, f]   (stored only if U_i != NULL; saved for backward)
+ *   Y_i = GeLU(U_i)  [M, f]   (stored in Y_i if given, else in the workspace)
+ *   Z_i = Y_i B_i    [M, h]   (this rank's partial)
+ *
+ * X    [M, h]  ldx >= h     (replicated input)
+ * A_i  [h, f]  lda >= f     (rank's column block: pass A + rank*f with lda = ffn
+ *                            to use a full A [h, ffn])
+ * B_i  [f, h]  ldb >= h     (rank's row block: B + rank*f*ldb of a full B [ffn, h])
+ * U_i, Y_i [M, f], Z_i [M, h]: outputs, same dtype.  rank only validates.
+ * Workspace: lgs_mlp_fwd_workspace_bytes(..., Y_i != NULL).
+ */
+int tp_mlp_fwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
+               const void* X, int64_t ldx, const void* A_i, int64_t lda, const void* B_i,
+               int64_t ldb, void* U_i, int64_t ldu, void* Y_i, int64_t ldy, void* Z_i,
+               int64_t ldz, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_mlp_bwd -- one rank's backward shard of the GeLU MLP block.
+ *
+ * "Mathematical Foundations of Megatron-LM", "Conjugate Communication
+ * Operators": g* is the identity, so the same dZ [M, h] reaches every rank;
+ * f* all-reduces the input gradient, so dX_i is a partial (dX = sum_i dX_i,
+ * shard_partial_sum on one device).  The products are the chain rule through
+ * the forward equations:
+ *
+ *   dY_i = dZ B_i^T,  dU_i = dY_i * GeLU'(U_i),  Y_i = GeLU(U_i) (recomputed)
+ *   dB_i = Y_i^T dZ   [f, h]
+ *   dA_i = X^T dU_i   [h, f]
+ *   dX_i = dU_i A_i^T [M, h]
+ *
+ * Inputs X [M,h], A_i [h,f], B_i [f,h] as in tp_mlp_fwd; U_i [M, f] the saved
+ * pre-activation; dZ [M, h].  Outputs dX_i, dA_i, dB_i (same dtype, each with
+ * its ld).  dA_i / dB_i may point into full [h, ffn] / [ffn, h] gradients.
+ * Workspace: lgs_mlp_bwd_workspace_bytes (holds Y_i and dU_i).
+ */
+int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
+               const void* X, int64_t ldx, const void* A_i, int64_t lda, const void* B_i,
+               int64_t ldb, const void* U_i, int64_t ldu, const void* dZ, int64_t lddz,
+               void* dX_i, int64_t lddx, void* dA_i, int64_t ldda, void* dB_i, int64_t lddb,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vocab_parallel_xent_fwd -- the fused vocab-parallel logit GEMM + cross-entropy
+ * partials of one rank ("LIT-022: Megatron-LM ...", "Key takeaways": the
+ * parallel logit GEMM is fused into the loss so ranks exchange O(b*s) numbers
+ * rather than all-gathering b*s*vocab logits).
+ *
+ * Rank r owns the contiguous vocabulary rows [r*V_r, (r+1)*V_r), V_r = vocab/t.
+ * With logits z = H E_r^T (never written to memory), per token k:
+ *   m_r[k]      = max_j z[k, j]
+ *   l_r[k]      = sum_j exp(z[k, j] - m_r[k])
+ *   tgt_r[k]    = z[k, targets[k] - r*V_r] if the target is in the slice, else +0.0
+ *   argmax_r[k] = global id of the slice's largest logit, lowest id on ties
+ *                 (-1 if the row has no ordered value, e.g. all NaN); may be NULL
+ *   loss[k]     = m_r + ln l_r - tgt_r, only for t == 1 (the full vocabulary);
+ *                 must be NULL when t > 1 (merge ranks with shard_partial_sum)
+ *
+ * H [M, h] ldh >= h (bf16 hidden rows), E_r [V_r, h] lde >= h (the rank's rows
+ * of the output embedding [vocab, h]: pass E + r*V_r*lde), targets [M] int32
+ * global ids in [0, vocab) (precondition, not checked).  Outputs are fp32 / int32
+ * [M] arrays.  dtype must be LGS_BF16.  Workspace: lgs_xent_workspace_bytes.
+ */
+int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype,
+                            const void* H, int64_t ldh, const void* E_r, int64_t lde,
+                            const int32_t* targets, float* m_r, float* l_r, float* tgt_r,
+                            int32_t* argmax_r, float* loss, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * shard_partial_sum -- the one-device stand-in for the exchanges of the path.
+ *
+ * LGS_REDUCE_SUM: out[j] = sum_{r=0}^{t-1} parts[r*part_stride + j], j < n,
+ *   accumulated in fp32 in ascending r (deterministic).  The g all-reduce of
+ *   the row-parallel exit (Z = sum_i Z_i, "Row-Parallel Linear Layer") and the
+ *   f* all-reduce of the input gradient (dX = sum_i dX_i).  in_dtype / out_dtype
+ *   each LGS_F32 or LGS_BF16.  Each rank's block is n dense elements.
+ * LGS_REDUCE_XENT: merge of the ranks' cross-entropy partials.  parts is fp32;
+ *   rank r's block at parts + r*part_stride holds m_r[n], l_r[n], tgt_r[n]
+ *   back to back (part_stride >= 3n).  out[j] (fp32) = M* + ln L* - sum_r tgt_r
+ *   with M* = max_r m_r and L* = sum_r l_r exp(m_r - M*): the log-sum-exp
+ *   identity, equal to the full-vocabulary loss.  Both dtypes must be LGS_F32.
+ * `out` must not overlap `parts`.
+ */
+int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dtype, const void* parts,
+                      int64_t part_stride, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LGS_H_ */

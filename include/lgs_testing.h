@@ -1,0 +1,45 @@
+/*
+ * lgs_testing.h -- the bf16 GEMM core of liblgs.so exposed for tests and
+ * tile-shape sweeps.  Not part of the method's interface (include/lgs.h);
+ * every entry point of lgs.h runs on this core.
+ *
+ * Conventions as in lgs.h (device pointers owned by the caller, row-major with
+ * leading dimensions, asynchronous on `stream`, status codes before launch).
+ */
+#ifndef LGS_TESTING_H_
+#define LGS_TESTING_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of block-tile shapes the core is built with; tile ids are 0..n-1. */
+int lgs_test_num_tiles(void);
+/* Block tile of id `tile` (rows x cols of C per workgroup); -1 if no such id. */
+int lgs_test_tile_shape(int tile, int* bm, int* bn);
+/* The tile id the library picks for an M x N output. */
+int lgs_test_pick_tile(int M, int N);
+
+/*
+ * C[M, N] = A B in bf16 (fp32 accumulation, round-to-nearest-even output) with
+ * the block tile `tile` (-1: the library's choice).
+ *   a_kmajor = 1: A is [M, K] row-major (element (m, k) at A[m*lda + k]);
+ *   a_kmajor = 0: A is stored transposed, [K, M] (element (m, k) at A[k*lda + m]).
+ *   b_kmajor = 1: B is stored transposed, [N, K] (element (k, n) at B[n*ldb + k]);
+ *   b_kmajor = 0: B is [K, N] row-major (element (k, n) at B[k*ldb + n]).
+ * Supported layout pairs (those the path uses): (1,0), (1,1), (0,0).
+ * The contiguous dimension of each operand must be a multiple of 8 (K for a
+ * K-major operand, M or N otherwise), as must N; 16-byte aligned bases, ld % 8 == 0.
+ */
+int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int N, int K, const void* A,
+                       int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LGS_TESTING_H_ */

@@ -1,0 +1,214 @@
+"""ctypes binding of liblgs.so (include/lgs.h), same names as the C entry points.
+
+Argument marshalling only: tensors become device pointers plus leading
+dimensions, the stream is torch's current HIP stream, and a workspace tensor
+is allocated through torch when the caller passes none.  Every step of the
+computation runs in the library's kernels; there is no fallback: if the
+library is not built, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblgs.so")
+
+LGS_OK, LGS_ERR_INVALID_ARG, LGS_ERR_UNSUPPORTED, LGS_ERR_WORKSPACE, LGS_ERR_HIP = range(5)
+LGS_F32, LGS_BF16 = 0, 1
+LGS_GELU_ERF, LGS_GELU_TANH = 0, 1
+LGS_REDUCE_SUM, LGS_REDUCE_XENT = 0, 1
+
+_ACT = {"erf": LGS_GELU_ERF, "tanh": LGS_GELU_TANH}
+_DT = {torch.float32: LGS_F32, torch.bfloat16: LGS_BF16}
+
+_lib = None
+
+# (name, restype, argtypes) of every exported entry point, in header order.
+_i, _i64, _p, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = [
+    ("lgs_version", _i, []),
+    ("lgs_status_string", ctypes.c_char_p, [_i]),
+    ("lgs_last_error", ctypes.c_char_p, []),
+    ("lgs_mlp_fwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i, _i]),
+    ("lgs_mlp_bwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
+    ("lgs_xent_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
+    ("tp_mlp_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                        _p, _i64, _p, _i64, _p, _sz, _p]),
+    ("tp_mlp_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                        _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _sz, _p]),
+    ("vocab_parallel_xent_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
+                                     _p, _p, _p, _p, _sz, _p]),
+    ("shard_partial_sum", _i, [_i, _i, _i64, _i, _i, _p, _i64, _p, _p]),
+    # include/lgs_testing.h
+    ("lgs_test_num_tiles", _i, []),
+    ("lgs_test_tile_shape", _i, [_i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    ("lgs_test_pick_tile", _i, [_i, _i]),
+    ("lgs_test_gemm_bf16", _i, [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
+]
+
+
+class LgsError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"lgs status {status}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m logit_gemm_shard_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def version():
+    return lib().lgs_version()
+
+
+def _check(status):
+    if status != LGS_OK:
+        L = lib()
+        raise LgsError(status, f"{L.lgs_status_string(status).decode()}: {L.lgs_last_error().decode()}")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _mat(x):
+    """(pointer, leading dimension) of a row-major 2-D tensor view, or (None, 0)."""
+    if x is None:
+        return None, 0
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return x.data_ptr(), x.stride(0)
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _dtype(x):
+    try:
+        return _DT[x.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {x.dtype}") from None
+
+
+def _workspace(nbytes, device, given):
+    if nbytes == 0:
+        return None, 0
+    if given is not None:
+        return given.data_ptr(), given.numel() * given.element_size()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, nbytes
+
+
+def mlp_fwd_workspace_bytes(b, s, h, ffn, t, dtype, y_given):
+    return lib().lgs_mlp_fwd_workspace_bytes(b, s, h, ffn, t, _DT[dtype], int(bool(y_given)))
+
+
+def mlp_bwd_workspace_bytes(b, s, h, ffn, t, dtype):
+    return lib().lgs_mlp_bwd_workspace_bytes(b, s, h, ffn, t, _DT[dtype])
+
+
+def xent_workspace_bytes(b, s, h, vocab, t, dtype=torch.bfloat16):
+    return lib().lgs_xent_workspace_bytes(b, s, h, vocab, t, _DT[dtype])
+
+
+def tp_mlp_fwd(b, s, h, ffn, t, rank, X, A_i, B_i, Z_i, U_i=None, Y_i=None, act="erf",
+               workspace=None, stream=None):
+    """One rank's forward shard: U_i = X A_i, Y_i = GeLU(U_i), Z_i = Y_i B_i."""
+    L = lib()
+    dt = _dtype(X)
+    need = L.lgs_mlp_fwd_workspace_bytes(b, s, h, ffn, t, dt, int(Y_i is not None))
+    ws, ws_bytes = _workspace(need, X.device, workspace)
+    x, ldx = _mat(X)
+    a, lda = _mat(A_i)
+    bb, ldb = _mat(B_i)
+    u, ldu = _mat(U_i)
+    y, ldy = _mat(Y_i)
+    z, ldz = _mat(Z_i)
+    _check(L.tp_mlp_fwd(b, s, h, ffn, t, rank, dt, _ACT[act], x, ldx, a, lda, bb, ldb, u, ldu, y,
+                        ldy, z, ldz, _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes,
+                        _stream(stream)))
+    return Z_i
+
+
+def tp_mlp_bwd(b, s, h, ffn, t, rank, X, A_i, B_i, U_i, dZ, dX_i, dA_i, dB_i, act="erf",
+               workspace=None, stream=None):
+    """One rank's backward shard: dX_i (partial), dA_i, dB_i from X, U_i and dZ."""
+    L = lib()
+    dt = _dtype(X)
+    need = L.lgs_mlp_bwd_workspace_bytes(b, s, h, ffn, t, dt)
+    ws, ws_bytes = _workspace(need, X.device, workspace)
+    args = []
+    for m in (X, A_i, B_i, U_i, dZ, dX_i, dA_i, dB_i):
+        args.extend(_mat(m))
+    _check(L.tp_mlp_bwd(b, s, h, ffn, t, rank, dt, _ACT[act], *args,
+                        _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes, _stream(stream)))
+    return dX_i, dA_i, dB_i
+
+
+def vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, H, E_r, targets, m_r, l_r, tgt_r,
+                            argmax_r=None, loss=None, workspace=None, stream=None):
+    """One rank's fused logit GEMM + CE partials over its vocabulary slice."""
+    L = lib()
+    dt = _dtype(H)
+    need = L.lgs_xent_workspace_bytes(b, s, h, vocab, t, dt)
+    ws, ws_bytes = _workspace(need, H.device, workspace)
+    hh, ldh = _mat(H)
+    e, lde = _mat(E_r)
+    _check(L.vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, dt, hh, ldh, e, lde, _ptr(targets),
+                                     _ptr(m_r), _ptr(l_r), _ptr(tgt_r), _ptr(argmax_r), _ptr(loss),
+                                     _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes,
+                                     _stream(stream)))
+    return m_r, l_r, tgt_r
+
+
+def shard_partial_sum(op, t, n, parts, part_stride, out, stream=None):
+    """SUM: out = sum_r parts[r]; XENT: out = per-token loss from [t][3][n] partials."""
+    L = lib()
+    opc = {"sum": LGS_REDUCE_SUM, "xent": LGS_REDUCE_XENT}[op] if isinstance(op, str) else op
+    _check(L.shard_partial_sum(opc, t, n, _dtype(parts), _dtype(out), parts.data_ptr(), part_stride,
+                               out.data_ptr(), _stream(stream)))
+    return out
+
+
+def tile_shapes():
+    """[(bm, bn)] of the GEMM core's block tiles, by tile id."""
+    L = lib()
+    out = []
+    for t in range(L.lgs_test_num_tiles()):
+        bm, bn = ctypes.c_int(), ctypes.c_int()
+        L.lgs_test_tile_shape(t, ctypes.byref(bm), ctypes.byref(bn))
+        out.append((bm.value, bn.value))
+    return out
+
+
+def pick_tile(M, N):
+    return lib().lgs_test_pick_tile(M, N)
+
+
+def gemm_bf16(A, B, C, a_kmajor=True, b_kmajor=False, tile=-1, stream=None):
+    """C = A B through the GEMM core (testing interface).  A is [M, K] if
+    a_kmajor else [K, M]; B is [K, N] if not b_kmajor else [N, K]."""
+    a, lda = _mat(A)
+    b, ldb = _mat(B)
+    c, ldc = _mat(C)
+    M, N = C.shape
+    K = A.shape[1] if a_kmajor else A.shape[0]
+    _check(lib().lgs_test_gemm_bf16(tile, int(a_kmajor), int(b_kmajor), M, N, K, a, lda, b, ldb, c,
+                                    ldc, _stream(stream)))
+    return C

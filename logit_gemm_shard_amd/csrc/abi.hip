@@ -1,0 +1,279 @@
+// The extern "C" entry points of liblgs.so (declared in include/lgs.h):
+// argument validation, workspace carving and dispatch to the launchers.
+// Validation touches no HIP API, so a rejected call never initialises the
+// runtime or enqueues anything.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <climits>
+
+#include "internal.hpp"
+#include "lgs.h"
+#include "lgs_testing.h"
+
+#define LGS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return LGS_OK;
+}
+
+size_t elt(int dtype) { return dtype == LGS_BF16 ? 2u : 4u; }
+size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shared shape checks.  Returns LGS_OK or a failure code (message set).
+int check_bst(int b, int s, int h, int t, int rank) {
+  if (b <= 0 || s <= 0 || h <= 0 || t <= 0)
+    return fail(LGS_ERR_INVALID_ARG, "b, s, h and t must be positive (got b=%d s=%d h=%d t=%d)", b,
+                s, h, t);
+  if ((int64_t)b * s > INT_MAX)
+    return fail(LGS_ERR_INVALID_ARG, "b*s = %lld tokens exceeds INT_MAX", (long long)b * s);
+  if (rank < 0 || rank >= t) return fail(LGS_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, t);
+  return LGS_OK;
+}
+
+int check_dtype(int dtype) {
+  if (dtype != LGS_F32 && dtype != LGS_BF16)
+    return fail(LGS_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  return LGS_OK;
+}
+
+// A matrix operand: non-null (if required), ld >= width, and the dtype's alignment.
+int check_mat(const char* name, const void* p, int64_t ld, int64_t width, int dtype, bool required) {
+  if (!p) {
+    if (required) return fail(LGS_ERR_INVALID_ARG, "%s is NULL", name);
+    return LGS_OK;
+  }
+  if (ld < width)
+    return fail(LGS_ERR_INVALID_ARG, "%s: leading dimension %lld < row width %lld", name,
+                (long long)ld, (long long)width);
+  if (dtype == LGS_BF16) {
+    if (!aligned(p, 16) || ld % 8 != 0)
+      return fail(LGS_ERR_UNSUPPORTED, "%s: bf16 operands need a 16-byte aligned base and ld %% 8 == 0",
+                  name);
+  } else if (!aligned(p, 4)) {
+    return fail(LGS_ERR_UNSUPPORTED, "%s: fp32 operands need a 4-byte aligned base", name);
+  }
+  return LGS_OK;
+}
+
+int check_mlp(int b, int s, int h, int ffn, int t, int rank, int dtype, int act) {
+  int st = check_bst(b, s, h, t, rank);
+  if (st) return st;
+  if (ffn <= 0 || ffn % t != 0)
+    return fail(LGS_ERR_INVALID_ARG, "ffn=%d must be positive and divisible by t=%d", ffn, t);
+  if ((st = check_dtype(dtype))) return st;
+  if (act != LGS_GELU_ERF && act != LGS_GELU_TANH)
+    return fail(LGS_ERR_UNSUPPORTED, "unknown GeLU variant %d", act);
+  if (h % 8 != 0 || (ffn / t) % 8 != 0)
+    return fail(LGS_ERR_UNSUPPORTED, "h=%d and ffn/t=%d must be multiples of 8", h, ffn / t);
+  return LGS_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(LGS_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+LGS_API int lgs_version(void) { return 100; }
+
+LGS_API const char* lgs_status_string(int status) {
+  switch (status) {
+    case LGS_OK: return "ok";
+    case LGS_ERR_INVALID_ARG: return "invalid argument";
+    case LGS_ERR_UNSUPPORTED: return "unsupported dtype, variant or alignment";
+    case LGS_ERR_WORKSPACE: return "workspace missing or too small";
+    case LGS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+LGS_API const char* lgs_last_error(void) { return g_err; }
+
+LGS_API size_t lgs_mlp_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype,
+                                           int y_given) {
+  if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || ffn <= 0 || ffn % t) return 0;
+  if (y_given) return 0;
+  return round256((size_t)b * s * (ffn / t) * elt(dtype));
+}
+
+LGS_API size_t lgs_mlp_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype) {
+  if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || ffn <= 0 || ffn % t) return 0;
+  return 2 * round256((size_t)b * s * (ffn / t) * elt(dtype));
+}
+
+LGS_API size_t lgs_xent_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype) {
+  (void)dtype;
+  if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || vocab <= 0 || vocab % t) return 0;
+  if ((int64_t)b * s > INT_MAX) return 0;
+  return round256(lgs::xent_scratch_bytes(b * s, vocab / t));
+}
+
+LGS_API int tp_mlp_fwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
+                       const void* X, int64_t ldx, const void* A_i, int64_t lda, const void* B_i,
+                       int64_t ldb, void* U_i, int64_t ldu, void* Y_i, int64_t ldy, void* Z_i,
+                       int64_t ldz, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mlp(b, s, h, ffn, t, rank, dtype, act);
+  if (st) return st;
+  const int M = b * s, f = ffn / t;
+  if ((st = check_mat("X", X, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("A_i", A_i, lda, f, dtype, true))) return st;
+  if ((st = check_mat("B_i", B_i, ldb, h, dtype, true))) return st;
+  if ((st = check_mat("U_i", U_i, ldu, f, dtype, false))) return st;
+  if ((st = check_mat("Y_i", Y_i, ldy, f, dtype, false))) return st;
+  if ((st = check_mat("Z_i", Z_i, ldz, h, dtype, true))) return st;
+  if (!Y_i) {
+    const size_t need = lgs_mlp_fwd_workspace_bytes(b, s, h, ffn, t, dtype, 0);
+    if (!workspace || workspace_bytes < need)
+      return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    Y_i = workspace;
+    ldy = f;
+  }
+  (void)hipGetLastError();  // start from a clean error state
+  return launched(lgs::mlp_fwd(dtype == LGS_BF16, M, h, f, act, X, ldx, A_i, lda, B_i, ldb, U_i,
+                               ldu, Y_i, ldy, Z_i, ldz, (hipStream_t)stream));
+}
+
+LGS_API int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
+                       const void* X, int64_t ldx, const void* A_i, int64_t lda, const void* B_i,
+                       int64_t ldb, const void* U_i, int64_t ldu, const void* dZ, int64_t lddz,
+                       void* dX_i, int64_t lddx, void* dA_i, int64_t ldda, void* dB_i,
+                       int64_t lddb, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_mlp(b, s, h, ffn, t, rank, dtype, act);
+  if (st) return st;
+  const int M = b * s, f = ffn / t;
+  if ((st = check_mat("X", X, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("A_i", A_i, lda, f, dtype, true))) return st;
+  if ((st = check_mat("B_i", B_i, ldb, h, dtype, true))) return st;
+  if ((st = check_mat("U_i", U_i, ldu, f, dtype, true))) return st;
+  if ((st = check_mat("dZ", dZ, lddz, h, dtype, true))) return st;
+  if ((st = check_mat("dX_i", dX_i, lddx, h, dtype, true))) return st;
+  if ((st = check_mat("dA_i", dA_i, ldda, f, dtype, true))) return st;
+  if ((st = check_mat("dB_i", dB_i, lddb, h, dtype, true))) return st;
+  const size_t need = lgs_mlp_bwd_workspace_bytes(b, s, h, ffn, t, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dU_i, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  char* y = (char*)workspace;
+  char* du = y + need / 2;
+  (void)hipGetLastError();
+  return launched(lgs::mlp_bwd(dtype == LGS_BF16, M, h, f, act, X, ldx, A_i, lda, B_i, ldb, U_i,
+                               ldu, dZ, lddz, dX_i, lddx, dA_i, ldda, dB_i, lddb, y, du,
+                               (hipStream_t)stream));
+}
+
+LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype,
+                                    const void* H, int64_t ldh, const void* E_r, int64_t lde,
+                                    const int32_t* targets, float* m_r, float* l_r, float* tgt_r,
+                                    int32_t* argmax_r, float* loss, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  int st = check_bst(b, s, h, t, rank);
+  if (st) return st;
+  if (vocab <= 0 || vocab % t != 0)
+    return fail(LGS_ERR_INVALID_ARG, "vocab=%d must be positive and divisible by t=%d", vocab, t);
+  if (dtype != LGS_BF16) return fail(LGS_ERR_UNSUPPORTED, "the fused cross-entropy takes bf16 only");
+  if (h % 8 != 0) return fail(LGS_ERR_UNSUPPORTED, "h=%d must be a multiple of 8", h);
+  const int M = b * s, Vr = vocab / t;
+  if ((st = check_mat("H", H, ldh, h, dtype, true))) return st;
+  if ((st = check_mat("E_r", E_r, lde, h, dtype, true))) return st;
+  if (!targets || !m_r || !l_r || !tgt_r)
+    return fail(LGS_ERR_INVALID_ARG, "targets, m_r, l_r and tgt_r are required");
+  if (!aligned(targets, 4) || !aligned(m_r, 4) || !aligned(l_r, 4) || !aligned(tgt_r, 4) ||
+      !aligned(argmax_r, 4) || !aligned(loss, 4))
+    return fail(LGS_ERR_UNSUPPORTED, "per-token arrays must be 4-byte aligned");
+  if (loss && t != 1)
+    return fail(LGS_ERR_INVALID_ARG, "loss needs the whole vocabulary (t == 1); merge ranks with shard_partial_sum");
+  const size_t need = lgs_xent_workspace_bytes(b, s, h, vocab, t, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  (void)hipGetLastError();
+  return launched(lgs::xent_fwd(M, h, Vr, rank * Vr, H, ldh, E_r, lde, targets, m_r, l_r, tgt_r,
+                                argmax_r, loss, workspace, (hipStream_t)stream));
+}
+
+LGS_API int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dtype,
+                              const void* parts, int64_t part_stride, void* out, void* stream) {
+  if (t <= 0 || n < 0) return fail(LGS_ERR_INVALID_ARG, "t must be positive and n non-negative");
+  int st;
+  if ((st = check_dtype(in_dtype)) || (st = check_dtype(out_dtype))) return st;
+  if (op == LGS_REDUCE_SUM) {
+    if (n > 0 && (!parts || !out)) return fail(LGS_ERR_INVALID_ARG, "parts and out are required");
+    if (t > 1 && part_stride < n)
+      return fail(LGS_ERR_INVALID_ARG, "part_stride %lld < n %lld", (long long)part_stride, (long long)n);
+    if (!aligned(parts, elt(in_dtype)) || !aligned(out, elt(out_dtype)))
+      return fail(LGS_ERR_UNSUPPORTED, "misaligned parts or out");
+    if (n == 0) return ok();
+    (void)hipGetLastError();
+    return launched(lgs::partial_sum(t, n, in_dtype == LGS_BF16, out_dtype == LGS_BF16, parts,
+                                     part_stride, out, (hipStream_t)stream));
+  }
+  if (op == LGS_REDUCE_XENT) {
+    if (in_dtype != LGS_F32 || out_dtype != LGS_F32)
+      return fail(LGS_ERR_UNSUPPORTED, "the cross-entropy merge is fp32 in and out");
+    if (n > 0 && (!parts || !out)) return fail(LGS_ERR_INVALID_ARG, "parts and out are required");
+    if (part_stride < 3 * n)
+      return fail(LGS_ERR_INVALID_ARG, "part_stride %lld < 3n = %lld", (long long)part_stride,
+                  (long long)(3 * n));
+    if (!aligned(parts, 4) || !aligned(out, 4)) return fail(LGS_ERR_UNSUPPORTED, "misaligned parts or out");
+    if (n == 0) return ok();
+    (void)hipGetLastError();
+    return launched(lgs::xent_combine(t, n, (const float*)parts, part_stride, (float*)out,
+                                      (hipStream_t)stream));
+  }
+  return fail(LGS_ERR_UNSUPPORTED, "unknown reduce op %d", op);
+}
+
+LGS_API int lgs_test_num_tiles(void) { return lgs::num_tiles(); }
+
+LGS_API int lgs_test_tile_shape(int tile, int* bm, int* bn) {
+  int m = 0, n = 0;
+  if (!lgs::tile_shape(tile, &m, &n)) return -1;
+  if (bm) *bm = m;
+  if (bn) *bn = n;
+  return 0;
+}
+
+LGS_API int lgs_test_pick_tile(int M, int N) {
+  if (M <= 0 || N <= 0) return -1;
+  return lgs::picked_tile(M, N);
+}
+
+LGS_API int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int N, int K,
+                               const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                               int64_t ldc, void* stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(LGS_ERR_INVALID_ARG, "M, N, K must be positive");
+  if (tile < -1 || tile >= lgs::num_tiles()) return fail(LGS_ERR_INVALID_ARG, "no tile id %d", tile);
+  if (!a_kmajor && b_kmajor) return fail(LGS_ERR_UNSUPPORTED, "layout pair (0, 1) is not built");
+  if (N % 8 != 0) return fail(LGS_ERR_UNSUPPORTED, "N must be a multiple of 8");
+  if ((a_kmajor || b_kmajor) && K % 8 != 0)
+    return fail(LGS_ERR_UNSUPPORTED, "K of a K-major operand must be a multiple of 8");
+  if (!a_kmajor && M % 8 != 0) return fail(LGS_ERR_UNSUPPORTED, "M of an M-major A must be a multiple of 8");
+  int st;
+  if ((st = check_mat("A", A, lda, a_kmajor ? K : M, LGS_BF16, true))) return st;
+  if ((st = check_mat("B", B, ldb, b_kmajor ? K : N, LGS_BF16, true))) return st;
+  if ((st = check_mat("C", C, ldc, N, LGS_BF16, true))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::gemm_store_bf16(tile, a_kmajor != 0, b_kmajor != 0, M, N, K, A, lda, B, ldb,
+                                       C, ldc, (hipStream_t)stream));
+}

@@ -1,0 +1,45 @@
+// Internal launchers behind the C ABI.  Arguments are already validated;
+// every function only enqueues kernels on `s` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lgs {
+
+// One rank's MLP shard forward.  M tokens, h hidden, f = ffn / t columns.
+//   U = X A_i (stored if U != null), Y = GeLU(U), Z = Y B_i.
+hipError_t mlp_fwd(bool bf16, int M, int h, int f, int act, const void* X, int64_t ldx,
+                   const void* A, int64_t lda, const void* B, int64_t ldb, void* U, int64_t ldu,
+                   void* Y, int64_t ldy, void* Z, int64_t ldz, hipStream_t s);
+
+// One rank's MLP shard backward from the saved X and U and the incoming dZ.
+//   dY = dZ B_i^T, dU = dY * GeLU'(U), Y = GeLU(U)  (Y, dU in scratch)
+//   dB_i = Y^T dZ, dA_i = X^T dU, dX_i = dU A_i^T
+hipError_t mlp_bwd(bool bf16, int M, int h, int f, int act, const void* X, int64_t ldx,
+                   const void* A, int64_t lda, const void* B, int64_t ldb, const void* U,
+                   int64_t ldu, const void* dZ, int64_t lddz, void* dX, int64_t lddx, void* dA,
+                   int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, hipStream_t s);
+
+// Fused logit GEMM + CE partials for one vocabulary slice of Vr rows.
+size_t xent_scratch_bytes(int M, int Vr);
+hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_t ldh,
+                    const void* E, int64_t lde, const int32_t* targets, float* m_r, float* l_r,
+                    float* t_r, int32_t* argmax_r, float* loss, void* scratch, hipStream_t s);
+
+// Sum of t partials (fp32 accumulate, ascending rank order) or the CE merge.
+hipError_t partial_sum(int t, int64_t n, bool in_bf16, bool out_bf16, const void* parts,
+                       int64_t stride, void* out, hipStream_t s);
+hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, float* loss,
+                        hipStream_t s);
+
+// The bf16 GEMM core with a store epilogue and an explicit tile (-1: picked).
+int num_tiles();
+bool tile_shape(int tile, int* bm, int* bn);
+int picked_tile(int M, int N);
+hipError_t gemm_store_bf16(int tile, bool a_kmajor, bool b_kmajor, int M, int N, int K,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                           int64_t ldc, hipStream_t s);
+
+}  // namespace lgs

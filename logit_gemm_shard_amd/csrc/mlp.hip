@@ -1,0 +1,108 @@
+// One tensor-parallel rank's GeLU MLP shard, forward and backward.
+//
+// "Tensor Parallelism and Pipeline Parallelism: Mathematical Foundations of
+// Megatron-LM ..." (llms.blog), "Column-Parallel Linear Layer" and
+// "Row-Parallel Linear Layer": with A split by columns and B by rows, rank i
+// computes Y_i = GeLU(X A_i) and the partial Z_i = Y_i B_i without any
+// exchange; the g operator then sums the partials.  The backward follows the
+// "Conjugate Communication Operators" section: dZ arrives unchanged on every
+// rank, and dX_i is a partial that f* sums.
+//
+// Operand layouts (row-major, explicit leading dimensions):
+//   X [M, h], A_i [h, f] (a column block of A [h, ffn]),
+//   B_i [f, h] (a row block of B [ffn, h]), U, Y, dU [M, f], Z, dZ, dX [M, h],
+//   dA_i [h, f], dB_i [f, h].
+// GEMM operand majorness per product (A operand rows x K, B operand K x cols):
+//   U  = X A_i      : X K-contiguous,            A_i N-contiguous
+//   Z  = Y B_i      : Y K-contiguous,            B_i N-contiguous
+//   dY = dZ B_i^T   : dZ K-contiguous,           B_i K-contiguous
+//   dX = dU A_i^T   : dU K-contiguous,           A_i K-contiguous
+//   dB = Y^T dZ     : Y M-contiguous (K=tokens), dZ N-contiguous
+//   dA = X^T dU     : X M-contiguous,            dU N-contiguous
+#include "dispatch.hpp"
+#include "epilogues.hpp"
+#include "gemm_f32.hpp"
+#include "internal.hpp"
+
+namespace lgs {
+
+hipError_t mlp_fwd(bool is_bf16, int M, int h, int f, int act, const void* X, int64_t ldx,
+                   const void* A, int64_t lda, const void* B, int64_t ldb, void* U, int64_t ldu,
+                   void* Y, int64_t ldy, void* Z, int64_t ldz, hipStream_t s) {
+  hipError_t e;
+  if (is_bf16) {
+    EpiGeluFwd<bf16> e1{(bf16*)U, ldu, (bf16*)Y, ldy, M, f, act};
+    e = gemm_bf16<true, false>(pick_tile(M, f), (const bf16*)X, ldx, (const bf16*)A, lda, M, f, h,
+                               e1, s);
+    if (e != hipSuccess) return e;
+    EpiStore<bf16> e2{(bf16*)Z, ldz, M, h};
+    return gemm_bf16<true, false>(pick_tile(M, h), (const bf16*)Y, ldy, (const bf16*)B, ldb, M, h,
+                                  f, e2, s);
+  }
+  EpiGeluFwd<float> e1{(float*)U, ldu, (float*)Y, ldy, M, f, act};
+  e = launch_gemm_f32<true, false>((const float*)X, ldx, (const float*)A, lda, M, f, h, e1, s);
+  if (e != hipSuccess) return e;
+  EpiStore<float> e2{(float*)Z, ldz, M, h};
+  return launch_gemm_f32<true, false>((const float*)Y, ldy, (const float*)B, ldb, M, h, f, e2, s);
+}
+
+hipError_t mlp_bwd(bool is_bf16, int M, int h, int f, int act, const void* X, int64_t ldx,
+                   const void* A, int64_t lda, const void* B, int64_t ldb, const void* U,
+                   int64_t ldu, const void* dZ, int64_t lddz, void* dX, int64_t lddx, void* dA,
+                   int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, hipStream_t s) {
+  hipError_t e;
+  const int64_t ldw = f;  // scratch Y / dU are dense [M, f]
+  if (is_bf16) {
+    const bf16 *x = (const bf16*)X, *a = (const bf16*)A, *b = (const bf16*)B, *dz = (const bf16*)dZ;
+    bf16 *y = (bf16*)Yws, *du = (bf16*)dUws;
+    EpiGeluBwd<bf16> e1{(const bf16*)U, ldu, du, ldw, y, ldw, M, f, act};
+    e = gemm_bf16<true, true>(pick_tile(M, f), dz, lddz, b, ldb, M, f, h, e1, s);
+    if (e != hipSuccess) return e;
+    EpiStore<bf16> eb{(bf16*)dB, lddb, f, h};
+    e = gemm_bf16<false, false>(pick_tile(f, h), y, ldw, dz, lddz, f, h, M, eb, s);
+    if (e != hipSuccess) return e;
+    EpiStore<bf16> ea{(bf16*)dA, ldda, h, f};
+    e = gemm_bf16<false, false>(pick_tile(h, f), x, ldx, du, ldw, h, f, M, ea, s);
+    if (e != hipSuccess) return e;
+    EpiStore<bf16> ex{(bf16*)dX, lddx, M, h};
+    return gemm_bf16<true, true>(pick_tile(M, h), du, ldw, a, lda, M, h, f, ex, s);
+  }
+  const float *x = (const float*)X, *a = (const float*)A, *b = (const float*)B, *dz = (const float*)dZ;
+  float *y = (float*)Yws, *du = (float*)dUws;
+  EpiGeluBwd<float> e1{(const float*)U, ldu, du, ldw, y, ldw, M, f, act};
+  e = launch_gemm_f32<true, true>(dz, lddz, b, ldb, M, f, h, e1, s);
+  if (e != hipSuccess) return e;
+  EpiStore<float> eb{(float*)dB, lddb, f, h};
+  e = launch_gemm_f32<false, false>(y, ldw, dz, lddz, f, h, M, eb, s);
+  if (e != hipSuccess) return e;
+  EpiStore<float> ea{(float*)dA, ldda, h, f};
+  e = launch_gemm_f32<false, false>(x, ldx, du, ldw, h, f, M, ea, s);
+  if (e != hipSuccess) return e;
+  EpiStore<float> ex{(float*)dX, lddx, M, h};
+  return launch_gemm_f32<true, true>(du, ldw, a, lda, M, h, f, ex, s);
+}
+
+int num_tiles() { return kNumTiles; }
+
+bool tile_shape(int tile, int* bm, int* bn) {
+  if (tile < 0 || tile >= kNumTiles) return false;
+  *bm = kTileShapes[tile].bm;
+  *bn = kTileShapes[tile].bn;
+  return true;
+}
+
+int picked_tile(int M, int N) { return pick_tile(M, N); }
+
+hipError_t gemm_store_bf16(int tile, bool a_kmajor, bool b_kmajor, int M, int N, int K,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                           int64_t ldc, hipStream_t s) {
+  const TileId t = tile < 0 ? pick_tile(M, N) : (TileId)tile;
+  EpiStore<bf16> e{(bf16*)C, ldc, M, N};
+  const bf16 *a = (const bf16*)A, *b = (const bf16*)B;
+  if (a_kmajor && !b_kmajor) return gemm_bf16<true, false>(t, a, lda, b, ldb, M, N, K, e, s);
+  if (a_kmajor && b_kmajor) return gemm_bf16<true, true>(t, a, lda, b, ldb, M, N, K, e, s);
+  if (!a_kmajor && !b_kmajor) return gemm_bf16<false, false>(t, a, lda, b, ldb, M, N, K, e, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lgs

@@ -1,0 +1,140 @@
+// One-device stand-ins for the two exchanges of the tensor-parallel path.
+//
+// * Sum of partials: out = sum_{r < t} part_r, fp32 accumulation in ascending
+//   rank order (so the result does not depend on timing).  This is the
+//   all-reduce of the row-parallel exit (g forward: Z = sum_i Z_i) and of the
+//   column-parallel entry (f backward: dX = sum_i dX_i), "Mathematical
+//   Foundations of Megatron-LM ...", "Row-Parallel Linear Layer" and
+//   "Conjugate Communication Operators".  A pure HBM stream: 16-byte loads of
+//   every rank's block per thread, t loads in flight before the adds.
+// * CE merge: loss = M* + ln(sum_r l_r exp(m_r - M*)) - sum_r T_r with
+//   M* = max_r m_r, the log-sum-exp identity over the ranks' slice partials.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace lgs {
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void add_to(float (&a)[8]) const {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] += (float)x[i];
+  }
+  __device__ __forceinline__ static void store(bf16* p, const float (&a)[8]) {
+    bf16x8 x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (bf16)a[i];
+    *reinterpret_cast<bf16x8*>(p) = x;
+  }
+};
+template <> struct Vec8<float> {
+  uint4 v0, v1;
+  __device__ __forceinline__ void load(const float* p) {
+    v0 = *reinterpret_cast<const uint4*>(p);
+    v1 = *reinterpret_cast<const uint4*>(p + 4);
+  }
+  __device__ __forceinline__ void add_to(float (&a)[8]) const {
+    a[0] += __uint_as_float(v0.x); a[1] += __uint_as_float(v0.y);
+    a[2] += __uint_as_float(v0.z); a[3] += __uint_as_float(v0.w);
+    a[4] += __uint_as_float(v1.x); a[5] += __uint_as_float(v1.y);
+    a[6] += __uint_as_float(v1.z); a[7] += __uint_as_float(v1.w);
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&a)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(a[0], a[1], a[2], a[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(a[4], a[5], a[6], a[7]);
+  }
+};
+
+constexpr int kChunkT = 8;  // ranks whose loads are issued together
+
+// Vector path: n % 8 == 0 and every rank block 16-byte aligned (checked on the host).
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void psum_vec_kernel(const TI* __restrict__ parts, int64_t stride,
+                                                       int t, int64_t n, TO* __restrict__ out) {
+  const int64_t step = (int64_t)gridDim.x * 256 * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += step) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < t; r0 += kChunkT) {
+      Vec8<TI> v[kChunkT];
+#pragma unroll
+      for (int r = 0; r < kChunkT; ++r)
+        if (r0 + r < t) v[r].load(parts + (int64_t)(r0 + r) * stride + i);
+#pragma unroll
+      for (int r = 0; r < kChunkT; ++r)
+        if (r0 + r < t) v[r].add_to(a);
+    }
+    Vec8<TO>::store(out + i, a);
+  }
+}
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void psum_scalar_kernel(const TI* __restrict__ parts,
+                                                          int64_t stride, int t, int64_t n,
+                                                          TO* __restrict__ out) {
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
+    float a = 0.f;
+    for (int r = 0; r < t; ++r) a += (float)parts[(int64_t)r * stride + i];
+    out[i] = (TO)a;
+  }
+}
+
+template <typename TI, typename TO>
+static hipError_t psum(int t, int64_t n, const void* parts, int64_t stride, void* out,
+                       hipStream_t s) {
+  const bool vec = (n % 8 == 0) && ((uintptr_t)parts % 16 == 0) && ((uintptr_t)out % 16 == 0) &&
+                   ((stride * (int64_t)sizeof(TI)) % 16 == 0);
+  const int64_t per_block = vec ? 256 * 8 : 256;
+  const int64_t want = (n + per_block - 1) / per_block;
+  const int blocks = (int)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
+  if (vec)
+    hipLaunchKernelGGL((psum_vec_kernel<TI, TO>), dim3(blocks), dim3(256), 0, s, (const TI*)parts,
+                       stride, t, n, (TO*)out);
+  else
+    hipLaunchKernelGGL((psum_scalar_kernel<TI, TO>), dim3(blocks), dim3(256), 0, s,
+                       (const TI*)parts, stride, t, n, (TO*)out);
+  return hipGetLastError();
+}
+
+hipError_t partial_sum(int t, int64_t n, bool in_bf16, bool out_bf16, const void* parts,
+                       int64_t stride, void* out, hipStream_t s) {
+  if (in_bf16)
+    return out_bf16 ? psum<bf16, bf16>(t, n, parts, stride, out, s)
+                    : psum<bf16, float>(t, n, parts, stride, out, s);
+  return out_bf16 ? psum<float, bf16>(t, n, parts, stride, out, s)
+                  : psum<float, float>(t, n, parts, stride, out, s);
+}
+
+// parts: rank r's block at parts + r*stride holds m[n], l[n], T[n].
+__global__ __launch_bounds__(256) void xent_combine_kernel(const float* __restrict__ parts,
+                                                           int64_t stride, int t, int64_t n,
+                                                           float* __restrict__ loss) {
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
+    float best = -INFINITY;
+    for (int r = 0; r < t; ++r) {
+      const float v = parts[(int64_t)r * stride + i];
+      best = v > best ? v : best;
+    }
+    float L = 0.f, T = 0.f;
+    for (int r = 0; r < t; ++r) {
+      const float* p = parts + (int64_t)r * stride;
+      L += p[n + i] * __expf(p[i] - best);
+      T += p[2 * n + i];
+    }
+    loss[i] = best + logf(L) - T;
+  }
+}
+
+hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, float* loss,
+                        hipStream_t s) {
+  const int64_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
+  hipLaunchKernelGGL(xent_combine_kernel, dim3(blocks), dim3(256), 0, s, parts, stride, t, n, loss);
+  return hipGetLastError();
+}
+
+}  // namespace lgs

@@ -1,0 +1,70 @@
+// Vocab-parallel cross-entropy forward for one rank's slice: the fused logit
+// GEMM (partials per wave column-slab, see xent.hpp) and the slab merge.
+//
+// Rank r owns vocabulary rows [vocab_start, vocab_start + Vr).  Per token it
+// produces the slice max m_r, the sum of exp(z - m_r) over the slice l_r, the
+// target logit T_r (exactly +0 when the target id is outside the slice) and
+// the global id of the slice's first maximum.  Ranks then exchange those
+// numbers instead of logits ("LIT-022: Megatron-LM ...", "Key takeaways").
+#include "dispatch.hpp"
+#include "internal.hpp"
+#include "xent.hpp"
+
+namespace lgs {
+
+// Upper bound on slabs over every tile shape: slabs = 2 * ceil(Vr / BN), BN >= 128.
+static int max_slabs(int Vr) { return 2 * ((Vr + 127) / 128); }
+
+size_t xent_scratch_bytes(int M, int Vr) {
+  return (size_t)max_slabs(Vr) * (size_t)M * 16u;
+}
+
+// One thread per token: fold the slabs (in increasing column order, so the
+// first maximum wins ties) into the rank's partials.
+__global__ __launch_bounds__(256) void xent_merge_kernel(XentSlabs s, int nslabs, int M,
+                                                         int vocab_start, float* m_r, float* l_r,
+                                                         float* t_r, int32_t* argmax_r,
+                                                         float* loss) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int k = 0; k < nslabs; ++k) {
+    const float v = s.m[(int64_t)k * M + m];
+    if (v > best) { best = v; bi = s.idx[(int64_t)k * M + m]; }
+  }
+  float L = 0.f, T = 0.f;
+  for (int k = 0; k < nslabs; ++k) {
+    const int64_t o = (int64_t)k * M + m;
+    L += s.l[o] * __expf(s.m[o] - best);
+    T += s.t[o];
+  }
+  m_r[m] = best;
+  l_r[m] = L;
+  t_r[m] = T;
+  if (argmax_r) argmax_r[m] = bi == 0x7fffffff ? -1 : vocab_start + bi;
+  if (loss) loss[m] = best + logf(L) - T;
+}
+
+hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_t ldh,
+                    const void* E, int64_t lde, const int32_t* targets, float* m_r, float* l_r,
+                    float* t_r, int32_t* argmax_r, float* loss, void* scratch, hipStream_t s) {
+  const TileId tile = pick_tile(M, Vr);
+  const int WN = tile_bn(tile) / 2;
+  const size_t slab_elems = (size_t)max_slabs(Vr) * M;
+  XentSlabs sl;
+  sl.m = (float*)scratch;
+  sl.l = sl.m + slab_elems;
+  sl.t = sl.l + slab_elems;
+  sl.idx = (int32_t*)(sl.t + slab_elems);
+  EpiXent epi{sl, targets, vocab_start, M, Vr, WN};
+  hipError_t e = gemm_bf16<true, true>(tile, (const bf16*)H, ldh, (const bf16*)E, lde, M, Vr, h,
+                                       epi, s);
+  if (e != hipSuccess) return e;
+  const int nslabs = (Vr + WN - 1) / WN;
+  hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 255) / 256), dim3(256), 0, s, sl, nslabs, M,
+                     vocab_start, m_r, l_r, t_r, argmax_r, loss);
+  return hipGetLastError();
+}
+
+}  // namespace lgs

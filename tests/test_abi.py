@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+* liblgs.so loads and exports every function include/lgs.h declares, and
+  nothing else under the library's names;
+* every validation rule returns its status code before any HIP call (the
+  pointers passed here are fake and would fault if anything were enqueued).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("lgs.h", "lgs_testing.h")]
+
+FAKE = 0x10000  # 64 KiB-aligned fake device address: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    from logit_gemm_shard_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.lib()
+
+
+def declared_functions():
+    names = []
+    for hdr in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for fn in ("tp_mlp_fwd", "tp_mlp_bwd", "vocab_parallel_xent_fwd", "shard_partial_sum"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from logit_gemm_shard_amd import binding
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in lgs.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    ours = {n for n in exported if n.startswith(("lgs_", "tp_", "vocab_", "shard_"))}
+    assert ours == set(declared_functions())
+    # the binding knows every declared function
+    assert {n for n, _, _ in binding.SIGNATURES} == set(declared_functions())
+
+
+def test_status_strings(L):
+    assert L.lgs_version() >= 100
+    for st in range(5):
+        assert L.lgs_status_string(st)
+    assert L.lgs_status_string(99) == b"unknown status"
+
+
+def _fwd(L, **kw):
+    a = dict(b=2, s=64, h=256, ffn=1024, t=2, rank=0, dtype=1, act=0, X=FAKE, ldx=256, A=FAKE,
+             lda=1024, B=FAKE, ldb=256, U=None, ldu=0, Y=FAKE, ldy=512, Z=FAKE, ldz=256, ws=None,
+             ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.tp_mlp_fwd(a["b"], a["s"], a["h"], a["ffn"], a["t"], a["rank"], a["dtype"], a["act"],
+                        a["X"], a["ldx"], a["A"], a["lda"], a["B"], a["ldb"], a["U"], a["ldu"],
+                        a["Y"], a["ldy"], a["Z"], a["ldz"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=0), 1), (dict(s=-1), 1), (dict(h=0), 1), (dict(t=0), 1),
+    (dict(rank=2), 1), (dict(rank=-1), 1),
+    (dict(ffn=1001), 1),                      # not divisible by t
+    (dict(dtype=7), 2), (dict(act=5), 2),
+    (dict(h=252, ldx=252, ldb=252, ldz=252), 2),  # h % 8
+    (dict(ffn=1020, ldy=510, lda=1020), 2),   # ffn/t % 8
+    (dict(X=None), 1), (dict(A=None), 1), (dict(B=None), 1), (dict(Z=None), 1),
+    (dict(ldx=255), 1), (dict(lda=500), 1), (dict(ldz=8), 1),
+    (dict(X=FAKE + 2), 2),                    # bf16 needs 16-byte alignment
+    (dict(ldx=260), 2),                       # bf16 ld % 8
+    (dict(Y=None), 3),                        # needs a workspace
+    (dict(Y=None, ws=FAKE, ws_bytes=10), 3),
+    (dict(Y=None, ws=FAKE + 16, ws_bytes=1 << 20), 2),
+    (dict(b=1 << 16, s=1 << 16), 1),          # more than INT_MAX tokens
+])
+def test_mlp_fwd_validation(L, kw, code):
+    assert _fwd(L, **kw) == code
+    assert L.lgs_last_error()
+
+
+def test_mlp_fwd_fp32_alignment_rules(L):
+    # fp32 needs only 4-byte alignment and no ld multiple
+    assert _fwd(L, dtype=0, X=FAKE + 2) == 2
+    assert _fwd(L, dtype=0, ldx=257, X=None) == 1
+
+
+def test_mlp_bwd_validation(L):
+    def bwd(**kw):
+        a = dict(b=1, s=16, h=64, ffn=128, t=2, rank=1, dtype=1, act=0, ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        p = [FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64]
+        for i, v in kw.get("mats", {}).items():
+            p[i] = v
+        return L.tp_mlp_bwd(a["b"], a["s"], a["h"], a["ffn"], a["t"], a["rank"], a["dtype"],
+                            a["act"], *p, a["ws"], a["ws_bytes"], None)
+    assert bwd(rank=2) == 1
+    assert bwd(mats={6: None}) == 1          # U_i required
+    assert bwd(mats={3: 32}) == 1            # lda < ffn/t = 64 ... (lda is index 3)
+    assert bwd(ws=None) == 3
+    assert bwd(ws_bytes=100) == 3
+    need = L.lgs_mlp_bwd_workspace_bytes(1, 16, 64, 128, 2, 1)
+    assert need == 2 * 2048
+    assert bwd(ws_bytes=need - 1) == 3
+
+
+def test_xent_validation(L):
+    def xe(**kw):
+        a = dict(b=2, s=8, h=64, vocab=1024, t=4, rank=0, dtype=1, H=FAKE, ldh=64, E=FAKE, lde=64,
+                 y=FAKE, m=FAKE, l=FAKE, T=FAKE, am=None, loss=None, ws=FAKE, ws_bytes=1 << 24)
+        a.update(kw)
+        return L.vocab_parallel_xent_fwd(a["b"], a["s"], a["h"], a["vocab"], a["t"], a["rank"],
+                                         a["dtype"], a["H"], a["ldh"], a["E"], a["lde"], a["y"],
+                                         a["m"], a["l"], a["T"], a["am"], a["loss"], a["ws"],
+                                         a["ws_bytes"], None)
+    assert xe(vocab=1022) == 1
+    assert xe(rank=4) == 1
+    assert xe(dtype=0) == 2
+    assert xe(h=60, ldh=60, lde=60) == 2
+    assert xe(loss=FAKE) == 1               # loss only for the whole vocabulary
+    assert xe(y=None) == 1
+    assert xe(ws=None) == 3
+    assert xe(ws_bytes=16) == 3
+    assert xe(lde=32) == 1
+    # the workspace bound covers every tile shape: 2 * ceil(Vr/128) slabs x M x 16 B
+    assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 2 * 50 * 8192 * 16
+
+
+def test_partial_sum_validation(L):
+    assert L.shard_partial_sum(0, 0, 16, 1, 1, FAKE, 16, FAKE, None) == 1
+    assert L.shard_partial_sum(0, 2, -1, 1, 1, FAKE, 16, FAKE, None) == 1
+    assert L.shard_partial_sum(0, 2, 16, 1, 1, FAKE, 8, FAKE, None) == 1   # stride < n
+    assert L.shard_partial_sum(0, 2, 16, 3, 1, FAKE, 16, FAKE, None) == 2
+    assert L.shard_partial_sum(9, 2, 16, 1, 1, FAKE, 16, FAKE, None) == 2
+    assert L.shard_partial_sum(1, 2, 16, 1, 0, FAKE, 48, FAKE, None) == 2  # xent is fp32
+    assert L.shard_partial_sum(1, 2, 16, 0, 0, FAKE, 40, FAKE, None) == 1  # stride < 3n
+    assert L.shard_partial_sum(0, 2, 16, 1, 1, None, 16, FAKE, None) == 1
+    # n == 0 is a no-op and touches nothing
+    assert L.shard_partial_sum(0, 3, 0, 1, 1, None, 0, None, None) == 0
+
+
+def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
+    from logit_gemm_shard_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+
+
+def test_testing_interface(L):
+    from logit_gemm_shard_amd import binding
+    shapes = binding.tile_shapes()
+    assert (256, 256) in shapes and (128, 128) in shapes
+    assert L.lgs_test_tile_shape(len(shapes), None, None) == -1
+    # the picker fills the 256 compute units: 4096 x 3584 -> 256 blocks of 256x224
+    assert shapes[binding.pick_tile(4096, 3584)] == (256, 224)
+    assert shapes[binding.pick_tile(8192, 1536)] == (256, 192)
+    assert shapes[binding.pick_tile(8192, 6400)] == (256, 160)
+    assert L.lgs_test_gemm_bf16(0, 0, 1, 64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 2
+    assert L.lgs_test_gemm_bf16(9, 1, 1, 64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 1
+    assert L.lgs_test_gemm_bf16(0, 1, 1, 64, 60, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 2

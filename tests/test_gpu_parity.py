@@ -1,0 +1,441 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small cases compare every element; cases spanning several tiles have ragged
+tails in M, N and K.  The full workloads (8.3B-shape and 70B-shape shards,
+the 51,200-entry vocabulary) run in the same launch configuration as the
+benchmark and are compared on sampled outputs that the oracle computes on
+exactly the needed rows / columns (every output entry depends only on those).
+
+Tolerance: max|gpu - ref| / max|ref| per output tensor, 1e-4 for fp32 and
+2e-2 for bf16 (fp32 accumulation); integer outputs (argmax ids, ownership of
+the target) exactly, up to near-ties within the fp32 dot-product error bound.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, assert_close, dev, f64, rel_err, round_like, step
+from logit_gemm_shard_amd import binding as lgs
+from logit_gemm_shard_amd import synth
+from logit_gemm_shard_amd.configs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+# ------------------------------------------------------------------ helpers
+
+def run_fwd(X, A, B, b, s, t, r, act, with_u=True):
+    """rank r's forward from full A [h, ffn] / B [ffn, h] on the device."""
+    M, h = X.shape
+    ffn = A.shape[1]
+    f = ffn // t
+    U = torch.empty(M, f, dtype=X.dtype, device=X.device) if with_u else None
+    Y = torch.empty(M, f, dtype=X.dtype, device=X.device)
+    Z = torch.empty(M, h, dtype=X.dtype, device=X.device)
+    lgs.tp_mlp_fwd(b, s, h, ffn, t, r, X, A[:, r * f:(r + 1) * f], B[r * f:(r + 1) * f], Z, U_i=U,
+                   Y_i=Y, act=act)
+    return U, Y, Z
+
+
+def run_bwd(X, A, B, U, dZ, b, s, t, r, act):
+    M, h = X.shape
+    ffn = A.shape[1]
+    f = ffn // t
+    dX = torch.empty(M, h, dtype=X.dtype, device=X.device)
+    dA = torch.empty(h, f, dtype=X.dtype, device=X.device)
+    dB = torch.empty(f, h, dtype=X.dtype, device=X.device)
+    lgs.tp_mlp_bwd(b, s, h, ffn, t, r, X, A[:, r * f:(r + 1) * f], B[r * f:(r + 1) * f], U, dZ, dX,
+                   dA, dB, act=act)
+    return dX, dA, dB
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------- tiny fp32 (t = 2)
+
+@pytest.mark.parametrize("act", ["erf", "tanh"])
+def test_tiny_mlp_t2_f32_shards_and_sum(act):
+    w = WORKLOADS["tiny_mlp_t2_f32"]
+    step(f"tiny_mlp_t2_f32 act={act}: both shards + sum")
+    d = dev()
+    X, A, B = synth.mlp_weights(w)
+    X64, A64, B64 = f64(X), f64(A), f64(B)
+    Xd, Ad, Bd = X.to(d), A.to(d), B.to(d)
+    parts = torch.empty(w.t, w.M, w.h, dtype=F32, device=d)
+    f = w.f_i
+    for r in range(w.t):
+        U, Y, Z = run_fwd(Xd, Ad, Bd, w.b, w.s, w.t, r, act)
+        parts[r].copy_(Z)
+        sync()
+        rU, rY, rZ = oracle.mlp.shard_forward(X64, A64[:, r * f:(r + 1) * f], B64[r * f:(r + 1) * f], act)
+        assert_close(f"U_{r}", U, rU, F32)
+        assert_close(f"Y_{r}", Y, rY, F32)
+        assert_close(f"Z_{r}", Z, rZ, F32)
+    Zs = torch.empty(w.M, w.h, dtype=F32, device=d)
+    lgs.shard_partial_sum("sum", w.t, w.M * w.h, parts, w.M * w.h, Zs)
+    sync()
+    assert_close("sum_i Z_i vs unsplit Z", Zs, oracle.mlp.mlp_forward(X64, A64, B64, act)[2], F32)
+
+
+# --------------------------------------------- the GEMM core, every tile shape
+
+@pytest.mark.parametrize("layout", [(True, False), (True, True), (False, False)])
+def test_gemm_core_every_tile_ragged(layout):
+    ak, bk = layout
+    d = dev()
+    shapes = lgs.tile_shapes()
+    for tid, (bm, bn) in enumerate(shapes):
+        # two tiles and a ragged tail in M and N, K not a multiple of the 64-wide step
+        M, N, K = 2 * bm + 24, 2 * bn + 40, 200
+        step(f"gemm core tile {bm}x{bn} layout a_kmajor={ak} b_kmajor={bk} M={M} N={N} K={K}")
+        a, b = synth.small(100 + tid, (M, K), (K, N), dtype="bf16")
+        A = (a if ak else a.t().contiguous()).to(d)
+        B = (b if not bk else b.t().contiguous()).to(d)
+        C = torch.empty(M, N, dtype=BF16, device=d)
+        lgs.gemm_bf16(A, B, C, a_kmajor=ak, b_kmajor=bk, tile=tid)
+        sync()
+        assert_close(f"C tile {bm}x{bn}", C, f64(a) @ f64(b), BF16)
+
+
+# ------------------------------------------------ ragged multi-tile MLP fwd/bwd
+
+RAGGED = [  # (b, s, h, ffn, t)
+    (3, 200, 136, 528, 2),
+    (1, 520, 328, 600, 3),
+    (1, 33, 72, 128, 8),
+    (2, 1100, 1064, 2 * 1048, 2),
+]
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_mlp_fwd_bwd_ragged(shape, dtype):
+    b, s, h, ffn, t = shape
+    M, f = b * s, ffn // t
+    d = dev()
+    dn = "bf16" if dtype == BF16 else "f32"
+    X, A, B, dZ = synth.small(7 + h, (M, h), (h, ffn), (ffn, h), (M, h), dtype=dn)
+    A, B = (A.float() * 0.05).to(dtype), (B.float() * 0.05).to(dtype)
+    X64, A64, B64, dZ64 = f64(X), f64(A), f64(B), f64(dZ)
+    Xd, Ad, Bd, dZd = X.to(d), A.to(d), B.to(d), dZ.to(d)
+    for act in ("erf", "tanh"):
+        for r in sorted({0, t - 1}):
+            step(f"ragged fwd/bwd {shape} {dn} act={act} rank={r}")
+            A_i, B_i = A64[:, r * f:(r + 1) * f], B64[r * f:(r + 1) * f]
+            U, Y, Z = run_fwd(Xd, Ad, Bd, b, s, t, r, act)
+            sync()
+            rU, rY, rZ = oracle.mlp.shard_forward(X64, A_i, B_i, act)
+            assert_close("U_i", U, rU, dtype)
+            assert_close("Y_i", Y, rY, dtype)
+            assert_close("Z_i", Z, rZ, dtype)
+            # backward from a U rounded on the host from the oracle's fp64 U
+            Uin = round_like(rU, dtype)
+            dX, dA, dB = run_bwd(Xd, Ad, Bd, Uin.to(d), dZd, b, s, t, r, act)
+            sync()
+            g = oracle.mlp.shard_backward(X64, A_i, B_i, f64(Uin), dZ64, act)
+            assert_close("dX_i", dX, g["dX"], dtype)
+            assert_close("dA_i", dA, g["dA"], dtype)
+            assert_close("dB_i", dB, g["dB"], dtype)
+
+
+def test_t1_is_the_unsplit_block():
+    d = dev()
+    b, s, h, ffn = 1, 300, 264, 520
+    X, A, B = synth.small(5, (b * s, h), (h, ffn), (ffn, h), dtype="bf16")
+    A, B = (A.float() * 0.05).to(BF16), (B.float() * 0.05).to(BF16)
+    step("t=1 forward equals the unsplit block")
+    U, Y, Z = run_fwd(X.to(d), A.to(d), B.to(d), b, s, 1, 0, "erf")
+    sync()
+    assert_close("Z (t=1)", Z, oracle.mlp.mlp_forward(f64(X), f64(A), f64(B))[2], BF16)
+
+
+# ----------------------------------------------------------------- sum kernels
+
+@pytest.mark.parametrize("t", [1, 2, 8])
+@pytest.mark.parametrize("n", [8192 + 8, 1001])
+@pytest.mark.parametrize("din,dout", [(BF16, BF16), (BF16, F32), (F32, F32), (F32, BF16)])
+def test_partial_sum_exact_on_integers(t, n, din, dout):
+    d = dev()
+    step(f"partial sum t={t} n={n} {din}->{dout}")
+    g = torch.Generator().manual_seed(t * 7 + n)
+    parts = torch.randint(-16, 17, (t, n), generator=g).to(din)
+    out = torch.full((n,), float("nan"), dtype=dout, device=d)
+    lgs.shard_partial_sum("sum", t, n, parts.to(d), n, out)
+    sync()
+    want = oracle.mlp.partial_sum([f64(p) for p in parts])
+    assert np.array_equal(f64(out), want)
+
+
+def test_partial_sum_strided_blocks():
+    d = dev()
+    step("partial sum with a padded rank stride")
+    t, n, stride = 3, 4096, 4096 + 64
+    buf = torch.randint(-8, 9, (t, stride), generator=torch.Generator().manual_seed(3)).to(BF16)
+    out = torch.empty(n, dtype=BF16, device=d)
+    lgs.shard_partial_sum("sum", t, n, buf.to(d), stride, out)
+    sync()
+    assert np.array_equal(f64(out), f64(buf[:, :n]).sum(axis=0))
+
+
+# ------------------------------------------------------------ cross-entropy
+
+def run_xent_all_ranks(H, E, y, b, s, t, with_argmax=True):
+    """every rank's partials into stats [t, 3, M] and argmax [t, M]."""
+    M, h = H.shape
+    V = E.shape[0]
+    Vr = V // t
+    stats = torch.empty(t, 3, M, dtype=F32, device=H.device)
+    am = torch.empty(t, M, dtype=torch.int32, device=H.device)
+    for r in range(t):
+        lgs.vocab_parallel_xent_fwd(b, s, h, V, t, r, H, E[r * Vr:(r + 1) * Vr], y, stats[r, 0],
+                                    stats[r, 1], stats[r, 2], argmax_r=am[r] if with_argmax else None)
+    return stats, am
+
+
+def check_argmax(H64, E64_slice, vocab_start, got_ids, rows):
+    """GPU argmax ids against fp64 logits: exact unless the top two are within
+    the fp32 dot-product error bound (then any id inside that band is valid)."""
+    K = H64.shape[1]
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    z = H64[rows] @ E64_slice.T
+    bound = gamma * (np.abs(H64[rows]) @ np.abs(E64_slice).T).max(axis=1)
+    got = np.asarray(got_ids)[rows] - vocab_start
+    zs = np.sort(z, axis=1)
+    for i in range(len(rows)):
+        top = z[i].max()
+        assert 0 <= got[i] < z.shape[1], (rows[i], got[i])
+        if zs[i, -1] - zs[i, -2] > 2 * bound[i]:
+            assert got[i] == int(np.argmax(z[i])), (rows[i], got[i], int(np.argmax(z[i])))
+        else:
+            assert z[i, got[i]] >= top - 2 * bound[i]
+
+
+@pytest.mark.parametrize("shape", [(1, 300, 72, 1400, 2), (2, 129, 136, 4 * 520, 4), (1, 64, 64, 8 * 136, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_xent_small_all_ranks(shape):
+    b, s, h, V, t = shape
+    M, Vr = b * s, V // t
+    d = dev()
+    H, E = synth.small(11 + h, (M, h), (V, h), dtype="bf16")
+    E = (E.float() * 0.5).to(BF16)
+    y = torch.randint(0, V, (M,), generator=torch.Generator().manual_seed(h), dtype=torch.int64).to(torch.int32)
+    H64, E64 = f64(H), f64(E)
+    step(f"xent small {shape}: all ranks")
+    stats, am = run_xent_all_ranks(H.to(d), E.to(d), y.to(d), b, s, t)
+    loss = torch.empty(M, dtype=F32, device=d)
+    lgs.shard_partial_sum("xent", t, M, stats, 3 * M, loss)
+    sync()
+    stats_h, am_h = stats.cpu(), am.cpu().numpy()
+    yn = y.numpy().astype(np.int64)
+    for r in range(t):
+        a, e = r * Vr, (r + 1) * Vr
+        m, l, T, ids = oracle.xent.shard_partials(H64, E64[a:e], yn, a)
+        assert_close(f"m_{r}", stats_h[r, 0], m, BF16)
+        assert_close(f"l_{r}", stats_h[r, 1], l, BF16)
+        own = (yn >= a) & (yn < e)
+        assert_close(f"T_{r} (owned)", stats_h[r, 2][own], T[own], BF16)
+        # not owned: exactly +0.0
+        Tn = stats_h[r, 2].numpy()[~own]
+        assert np.all(Tn == 0.0) and not np.any(np.signbit(Tn))
+        check_argmax(H64, E64[a:e], a, am_h[r], np.arange(M))
+    assert_close("loss (merged)", loss, oracle.xent.naive_loss(H64, E64, yn), BF16)
+    # exactly one rank owns every target
+    owners = np.stack([(yn >= r * Vr) & (yn < (r + 1) * Vr) for r in range(t)]).sum(axis=0)
+    assert np.all(owners == 1) and np.array_equal(yn // Vr, np.argmax(
+        np.stack([(yn >= r * Vr) & (yn < (r + 1) * Vr) for r in range(t)]), axis=0))
+
+
+def test_xent_t1_loss_output():
+    d = dev()
+    b, s, h, V = 1, 200, 128, 1000
+    H, E = synth.small(21, (b * s, h), (V, h), dtype="bf16")
+    E = (E.float() * 0.3).to(BF16)
+    y = torch.randint(0, V, (b * s,), generator=torch.Generator().manual_seed(1)).to(torch.int32)
+    step("xent t=1: loss written directly")
+    m = torch.empty(b * s, dtype=F32, device=d)
+    l, T, loss = torch.empty_like(m), torch.empty_like(m), torch.empty_like(m)
+    am = torch.empty(b * s, dtype=torch.int32, device=d)
+    lgs.vocab_parallel_xent_fwd(b, s, h, V, 1, 0, H.to(d), E.to(d), y.to(d), m, l, T, argmax_r=am, loss=loss)
+    sync()
+    assert_close("loss (t=1)", loss, oracle.xent.naive_loss(f64(H), f64(E), y.numpy()), BF16)
+    check_argmax(f64(H), f64(E), 0, am.cpu().numpy(), np.arange(b * s))
+
+
+def test_xent_uniform_embedding_gives_ln_v():
+    d = dev()
+    b, s, h, V, t = 1, 64, 64, 8 * 640, 8
+    H = synth.small(3, (b * s, h), dtype="bf16")[0].to(d)
+    E = torch.zeros(V, h, dtype=BF16, device=d)
+    y = torch.arange(b * s, dtype=torch.int32, device=d) * 79
+    step("xent with E = 0: loss = ln V")
+    stats, am = run_xent_all_ranks(H, E, y, b, s, t)
+    loss = torch.empty(b * s, dtype=F32, device=d)
+    lgs.shard_partial_sum("xent", t, b * s, stats, 3 * b * s, loss)
+    sync()
+    st = stats.cpu().numpy()
+    assert np.all(st[:, 0] == 0.0) and np.all(st[:, 1] == V // t) and np.all(st[:, 2] == 0.0)
+    assert np.all(am.cpu().numpy() == (np.arange(t) * (V // t))[:, None])  # ties -> lowest id
+    assert np.abs(loss.cpu().numpy() - math.log(V)).max() < 1e-6 * math.log(V)
+
+
+def test_xent_nan_row_stays_in_its_token():
+    d = dev()
+    b, s, h, V, t = 1, 96, 64, 2 * 512, 2
+    H, E = synth.small(31, (b * s, h), (V, h), dtype="bf16")
+    H[5, 3] = float("nan")
+    y = torch.randint(0, V, (b * s,), generator=torch.Generator().manual_seed(2)).to(torch.int32)
+    step("xent with a NaN in one hidden row")
+    stats, _ = run_xent_all_ranks(H.to(d), E.to(d), y.to(d), b, s, t)
+    loss = torch.empty(b * s, dtype=F32, device=d)
+    lgs.shard_partial_sum("xent", t, b * s, stats, 3 * b * s, loss)
+    sync()
+    got = loss.cpu().numpy()
+    assert np.isnan(got[5])
+    keep = np.arange(b * s) != 5
+    ref = oracle.xent.naive_loss(f64(H)[keep], f64(E), y.numpy()[keep])
+    assert np.all(np.isfinite(got[keep]))
+    assert_close("loss (other tokens)", got[keep], ref, BF16)
+
+
+def test_xent_merge_kernel_matches_oracle_merge():
+    d = dev()
+    t, n = 8, 5000
+    g = np.random.default_rng(4)
+    m = g.normal(size=(t, n)) * 5
+    l = g.uniform(1, 100, size=(t, n))
+    T = np.where(g.uniform(size=(t, n)) < 1 / t, g.normal(size=(t, n)), 0.0)
+    parts = torch.from_numpy(np.stack([m, l, T], axis=1).astype(np.float32)).to(d)
+    step("xent merge kernel")
+    out = torch.empty(n, dtype=F32, device=d)
+    lgs.shard_partial_sum("xent", t, n, parts, 3 * n, out)
+    sync()
+    p32 = parts.cpu().double().numpy()
+    assert_close("merge", out, oracle.xent.merge(p32[:, 0], p32[:, 1], p32[:, 2]), F32)
+
+
+# ----------------------------------------------------- full sizes, sampled
+
+_cache = {}
+
+
+def _mlp_inputs(name):
+    if name not in _cache:
+        _cache.clear()
+        w = WORKLOADS[name]
+        X, A, B = synth.mlp_weights(w)
+        _cache[name] = (w, X, A, B)
+    return _cache[name]
+
+
+def _rows(M, n=24, seed=0):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], g.choice(M, n, replace=False)]))
+
+
+@pytest.mark.parametrize("name", ["mlp_8p3b_fwd", "mlp_70b_fwd"])
+def test_full_size_forward_sampled(name):
+    w, X, A, B = _mlp_inputs(name)
+    d = dev()
+    Xd, Ad, Bd = X.to(d), A.to(d), B.to(d)
+    f = w.f_i
+    rows = _rows(w.M)
+    X64 = f64(X[rows])
+    for r in (0, w.t - 1):
+        step(f"{name}: rank {r} forward at full size")
+        U, Y, Z = run_fwd(Xd, Ad, Bd, w.b, w.s, w.t, r, "erf")
+        sync()
+        rU, rY, rZ = oracle.mlp.shard_forward(X64, f64(A[:, r * f:(r + 1) * f]), f64(B[r * f:(r + 1) * f]))
+        assert_close(f"U_{r} rows", U[rows], rU, BF16)
+        assert_close(f"Y_{r} rows", Y[rows], rY, BF16)
+        assert_close(f"Z_{r} rows", Z[rows], rZ, BF16)
+
+
+def test_full_size_all_shards_sum_to_unsplit():
+    w, X, A, B = _mlp_inputs("mlp_8p3b_fwd")
+    d = dev()
+    Xd, Ad, Bd = X.to(d), A.to(d), B.to(d)
+    parts = torch.empty(w.t, w.M, w.h, dtype=BF16, device=d)
+    f = w.f_i
+    step("mlp_8p3b_fwd: all 8 ranks + on-device sum")
+    for r in range(w.t):
+        Y = torch.empty(w.M, f, dtype=BF16, device=d)
+        lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, r, Xd, Ad[:, r * f:(r + 1) * f], Bd[r * f:(r + 1) * f],
+                       parts[r], Y_i=Y)
+    Z = torch.empty(w.M, w.h, dtype=BF16, device=d)
+    lgs.shard_partial_sum("sum", w.t, w.M * w.h, parts, w.M * w.h, Z)
+    sync()
+    rows = _rows(w.M, 16, 1)
+    ref = oracle.mlp.mlp_forward(f64(X[rows]), f64(A), f64(B))[2]
+    assert_close("sum_i Z_i vs unsplit Z (rows)", Z[rows], ref, BF16)
+
+
+def _bwd_check(w, X, A, B, r, seed):
+    d = dev()
+    f = w.f_i
+    A_i64 = f64(A[:, r * f:(r + 1) * f])
+    B_i64 = f64(B[r * f:(r + 1) * f])
+    X64 = f64(X)
+    step(f"{w.name}: oracle U_{r} = X A_{r} in fp64 (host)")
+    U = round_like(X64 @ A_i64, BF16)
+    dZ = synth.mlp_grad(w) if w.dz_std else synth.normal((w.M, w.h), 0.01, seed, "bf16")
+    step(f"{w.name}: rank {r} backward at full size")
+    dX, dA, dB = run_bwd(X.to(d), A.to(d), B.to(d), U.to(d), dZ.to(d), w.b, w.s, w.t, r, "erf")
+    sync()
+    U64, dZ64 = f64(U), f64(dZ)
+    rows = _rows(w.M, 16, 2)
+    g = oracle.mlp.shard_backward(X64[rows], A_i64, B_i64, U64[rows], dZ64[rows])
+    assert_close(f"dX_{r} rows", dX[rows], g["dX"], BF16)
+    hs = _rows(w.h, 24, 3)
+    fs = _rows(f, 24, 4)
+    g = oracle.mlp.shard_backward(X64[:, hs], A_i64[np.ix_(hs, fs)], B_i64[fs], U64[:, fs], dZ64)
+    assert_close(f"dA_{r} block", dA[hs][:, fs], g["dA"], BF16)
+    assert_close(f"dB_{r} rows", dB[fs], g["dB"], BF16)
+
+
+def test_full_size_backward_70b_sampled():
+    w, X, A, B = _mlp_inputs("mlp_70b_fwd")
+    _bwd_check(WORKLOADS["mlp_70b_bwd"], X, A, B, 0, 0)
+
+
+def test_full_size_backward_8p3b_sampled():
+    w, X, A, B = _mlp_inputs("mlp_8p3b_fwd")
+    _bwd_check(w, X, A, B, w.t - 1, 9)
+
+
+def test_full_size_xent_all_ranks_sampled():
+    w = WORKLOADS["xent_8p3b"]
+    d = dev()
+    H, E, y = synth.xent_inputs(w)
+    step("xent_8p3b: all 8 ranks at full size")
+    stats, am = run_xent_all_ranks(H.to(d), E.to(d), y.to(d), w.b, w.s, w.t)
+    loss = torch.empty(w.M, dtype=F32, device=d)
+    lgs.shard_partial_sum("xent", w.t, w.M, stats, 3 * w.M, loss)
+    sync()
+    st, amh, yn = stats.cpu(), am.cpu().numpy(), y.numpy().astype(np.int64)
+    Vr = w.v_r
+    # target ownership, every token: the owner's T is a logit, every other rank's is +0.0
+    for r in range(w.t):
+        own = (yn // Vr) == r
+        Tn = st[r, 2].numpy()[~own]
+        assert np.all(Tn == 0.0) and not np.any(np.signbit(Tn))
+    rows = _rows(w.M, 96, 5)
+    H64, E64 = f64(H[rows]), f64(E)
+    assert_close("loss (sampled tokens)", loss.cpu()[rows], oracle.xent.naive_loss(H64, E64, yn[rows]), BF16)
+    for r in (0, 3, w.t - 1):
+        a = r * Vr
+        m, l, T, ids = oracle.xent.shard_partials(H64, E64[a:a + Vr], yn[rows], a)
+        assert_close(f"m_{r}", st[r, 0][rows], m, BF16)
+        assert_close(f"l_{r}", st[r, 1][rows], l, BF16)
+        own = (yn[rows] // Vr) == r
+        if own.any():
+            assert_close(f"T_{r} owned", st[r, 2][rows][own], T[own], BF16)
+        check_argmax(f64(H), E64[a:a + Vr], a, amh[r], rows)
