@@ -52,8 +52,10 @@ int check_dtype(int dtype) {
   return LGS_OK;
 }
 
-// A matrix operand: non-null (if required), ld >= width, and the dtype's alignment.
-int check_mat(const char* name, const void* p, int64_t ld, int64_t width, int dtype, bool required) {
+// A matrix operand of `rows` rows: non-null (if required), ld >= width, the
+// dtype's alignment, and (bf16, read with 32-bit buffer offsets) < 2 GiB.
+int check_mat(const char* name, const void* p, int64_t rows, int64_t ld, int64_t width, int dtype,
+              bool required) {
   if (!p) {
     if (required) return fail(LGS_ERR_INVALID_ARG, "%s is NULL", name);
     return LGS_OK;
@@ -65,6 +67,8 @@ int check_mat(const char* name, const void* p, int64_t ld, int64_t width, int dt
     if (!aligned(p, 16) || ld % 8 != 0)
       return fail(LGS_ERR_UNSUPPORTED, "%s: bf16 operands need a 16-byte aligned base and ld %% 8 == 0",
                   name);
+    if (((rows - 1) * ld + width) * 2 >= ((int64_t)1 << 31))
+      return fail(LGS_ERR_UNSUPPORTED, "%s: bf16 operands must span less than 2 GiB", name);
   } else if (!aligned(p, 4)) {
     return fail(LGS_ERR_UNSUPPORTED, "%s: fp32 operands need a 4-byte aligned base", name);
   }
@@ -132,12 +136,12 @@ LGS_API int tp_mlp_fwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
   int st = check_mlp(b, s, h, ffn, t, rank, dtype, act);
   if (st) return st;
   const int M = b * s, f = ffn / t;
-  if ((st = check_mat("X", X, ldx, h, dtype, true))) return st;
-  if ((st = check_mat("A_i", A_i, lda, f, dtype, true))) return st;
-  if ((st = check_mat("B_i", B_i, ldb, h, dtype, true))) return st;
-  if ((st = check_mat("U_i", U_i, ldu, f, dtype, false))) return st;
-  if ((st = check_mat("Y_i", Y_i, ldy, f, dtype, false))) return st;
-  if ((st = check_mat("Z_i", Z_i, ldz, h, dtype, true))) return st;
+  if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("A_i", A_i, h, lda, f, dtype, true))) return st;
+  if ((st = check_mat("B_i", B_i, f, ldb, h, dtype, true))) return st;
+  if ((st = check_mat("U_i", U_i, M, ldu, f, dtype, false))) return st;
+  if ((st = check_mat("Y_i", Y_i, M, ldy, f, dtype, false))) return st;
+  if ((st = check_mat("Z_i", Z_i, M, ldz, h, dtype, true))) return st;
   if (!Y_i) {
     const size_t need = lgs_mlp_fwd_workspace_bytes(b, s, h, ffn, t, dtype, 0);
     if (!workspace || workspace_bytes < need)
@@ -160,14 +164,14 @@ LGS_API int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
   int st = check_mlp(b, s, h, ffn, t, rank, dtype, act);
   if (st) return st;
   const int M = b * s, f = ffn / t;
-  if ((st = check_mat("X", X, ldx, h, dtype, true))) return st;
-  if ((st = check_mat("A_i", A_i, lda, f, dtype, true))) return st;
-  if ((st = check_mat("B_i", B_i, ldb, h, dtype, true))) return st;
-  if ((st = check_mat("U_i", U_i, ldu, f, dtype, true))) return st;
-  if ((st = check_mat("dZ", dZ, lddz, h, dtype, true))) return st;
-  if ((st = check_mat("dX_i", dX_i, lddx, h, dtype, true))) return st;
-  if ((st = check_mat("dA_i", dA_i, ldda, f, dtype, true))) return st;
-  if ((st = check_mat("dB_i", dB_i, lddb, h, dtype, true))) return st;
+  if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("A_i", A_i, h, lda, f, dtype, true))) return st;
+  if ((st = check_mat("B_i", B_i, f, ldb, h, dtype, true))) return st;
+  if ((st = check_mat("U_i", U_i, M, ldu, f, dtype, true))) return st;
+  if ((st = check_mat("dZ", dZ, M, lddz, h, dtype, true))) return st;
+  if ((st = check_mat("dX_i", dX_i, M, lddx, h, dtype, true))) return st;
+  if ((st = check_mat("dA_i", dA_i, h, ldda, f, dtype, true))) return st;
+  if ((st = check_mat("dB_i", dB_i, f, lddb, h, dtype, true))) return st;
   const size_t need = lgs_mlp_bwd_workspace_bytes(b, s, h, ffn, t, dtype);
   if (!workspace || workspace_bytes < need)
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dU_i, %zu given", need,
@@ -193,8 +197,8 @@ LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int r
   if (dtype != LGS_BF16) return fail(LGS_ERR_UNSUPPORTED, "the fused cross-entropy takes bf16 only");
   if (h % 8 != 0) return fail(LGS_ERR_UNSUPPORTED, "h=%d must be a multiple of 8", h);
   const int M = b * s, Vr = vocab / t;
-  if ((st = check_mat("H", H, ldh, h, dtype, true))) return st;
-  if ((st = check_mat("E_r", E_r, lde, h, dtype, true))) return st;
+  if ((st = check_mat("H", H, M, ldh, h, dtype, true))) return st;
+  if ((st = check_mat("E_r", E_r, Vr, lde, h, dtype, true))) return st;
   if (!targets || !m_r || !l_r || !tgt_r)
     return fail(LGS_ERR_INVALID_ARG, "targets, m_r, l_r and tgt_r are required");
   if (!aligned(targets, 4) || !aligned(m_r, 4) || !aligned(l_r, 4) || !aligned(tgt_r, 4) ||
@@ -270,9 +274,9 @@ LGS_API int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int 
     return fail(LGS_ERR_UNSUPPORTED, "K of a K-major operand must be a multiple of 8");
   if (!a_kmajor && M % 8 != 0) return fail(LGS_ERR_UNSUPPORTED, "M of an M-major A must be a multiple of 8");
   int st;
-  if ((st = check_mat("A", A, lda, a_kmajor ? K : M, LGS_BF16, true))) return st;
-  if ((st = check_mat("B", B, ldb, b_kmajor ? K : N, LGS_BF16, true))) return st;
-  if ((st = check_mat("C", C, ldc, N, LGS_BF16, true))) return st;
+  if ((st = check_mat("A", A, a_kmajor ? M : K, lda, a_kmajor ? K : M, LGS_BF16, true))) return st;
+  if ((st = check_mat("B", B, b_kmajor ? N : K, ldb, b_kmajor ? K : N, LGS_BF16, true))) return st;
+  if ((st = check_mat("C", C, M, ldc, N, LGS_BF16, true))) return st;
   (void)hipGetLastError();
   return launched(lgs::gemm_store_bf16(tile, a_kmajor != 0, b_kmajor != 0, M, N, K, A, lda, B, ldb,
                                        C, ldc, (hipStream_t)stream));

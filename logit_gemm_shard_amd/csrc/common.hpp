@@ -1,5 +1,5 @@
-// Shared device helpers for the gfx950 (CDNA4) kernels: types, bf16
-// packing and the GeLU / GeLU' forms used by the GEMM epilogues.
+// Shared device helpers for the gfx950 (CDNA4) kernels: types, vector
+// loads / stores, and the GeLU / GeLU' forms used by the GEMM epilogues.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,44 +14,83 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum Act : int { ACT_ERF = 0, ACT_TANH = 1 };
 
-// GeLU(u) = u * Phi(u), Phi the standard normal CDF; the nonlinearity the
+// GeLU(u) = u * Phi(u), Phi the standard normal CDF: the nonlinearity the
 // pages put between the column-parallel and the row-parallel GEMM ("Cutting
-// a Model Into Pieces", "Megatron-LM: cutting inside the layer").
-// ACT_TANH is the published tanh approximation of the same function.
-// erff / tanhf / __expf are ROCm's device math library functions.
-__device__ __forceinline__ float gelu_f(float u, int act) {
-  if (act == ACT_ERF) return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
-  const float a = 0.79788456080286536f * (u + 0.044715f * u * u * u);
-  return 0.5f * u * (1.0f + tanhf(a));
+// a Model Into Pieces", "Megatron-LM: cutting inside the layer").  ACT_TANH
+// is the published tanh approximation of the same function.
+//
+// Phi comes from erf by Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26: for z >= 0, with t = 1 / (1 + p z),
+//   erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2) + e(z),
+//   |e(z)| <= 1.5e-7,
+// which is branch-free (one exp, one reciprocal) and shares exp(-u^2/2) with
+// the density phi(u) needed by GeLU'.  Both values come out of one call.
+struct GeluVals {
+  float y;   // GeLU(u)
+  float dy;  // GeLU'(u)
+};
+
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);  // v_exp_f32 computes 2^x
 }
 
-// d GeLU / du.  Exact form: Phi(u) + u * phi(u), phi(u) = exp(-u^2/2)/sqrt(2 pi).
-__device__ __forceinline__ float gelu_grad_f(float u, int act) {
-  if (act == ACT_ERF)
-    return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) +
-           u * __expf(-0.5f * u * u) * 0.39894228040143268f;
-  const float a = 0.79788456080286536f * (u + 0.044715f * u * u * u);
-  const float s = tanhf(a);
-  return 0.5f * (1.0f + s) +
-         0.5f * u * (1.0f - s * s) * 0.79788456080286536f * (1.0f + 0.134145f * u * u);
+__device__ __forceinline__ GeluVals gelu_both(float u, int act) {
+  if (act == ACT_ERF) {
+    const float z = fabsf(u) * 0.70710678118654752f;  // |u| / sqrt(2)
+    const float e = fast_exp(-z * z);                  // exp(-u^2/2)
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float p = fmaf(t, 1.061405429f, -1.453152027f);
+    p = fmaf(t, p, 1.421413741f);
+    p = fmaf(t, p, -0.284496736f);
+    p = fmaf(t, p, 0.254829592f);
+    const float tail = 0.5f * (p * t) * e;             // 1 - Phi(|u|)
+    const float phi = u >= 0.f ? 1.0f - tail : tail;   // Phi(u)
+    return {u * phi, fmaf(u * 0.39894228040143268f, e, phi)};
+  }
+  // tanh(a) = 1 - 2 / (1 + exp(2a)), finite at both ends (exp -> 0 or inf)
+  const float a = 0.79788456080286536f * fmaf(0.044715f * u, u * u, u);
+  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + fast_exp(2.0f * a));
+  const float da = 0.79788456080286536f * fmaf(0.134145f * u, u, 1.0f);
+  return {0.5f * u * (1.0f + th), fmaf(0.5f * u * (1.0f - th * th), da, 0.5f * (1.0f + th))};
 }
 
-template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
-
-// Store four consecutive values (round-to-nearest-even for bf16).
-__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
-  bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-  *reinterpret_cast<bf16x4*>(p) = o;
+// W consecutive values at p (W = 4 or 8); bf16 uses one vector access,
+// fp32 scalar accesses (the fp32 path only guarantees 4-byte alignment).
+template <int W>
+__device__ __forceinline__ void store_vec(bf16* p, const float* v) {
+  if constexpr (W == 8) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = o;
+  } else {
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x4*>(p) = o;
+  }
 }
-__device__ __forceinline__ void store4(float* p, f32x4 v) {
-  p[0] = v[0]; p[1] = v[1]; p[2] = v[2]; p[3] = v[3];
+template <int W>
+__device__ __forceinline__ void store_vec(float* p, const float* v) {
+#pragma unroll
+  for (int i = 0; i < W; ++i) p[i] = v[i];
 }
-__device__ __forceinline__ f32x4 load4(const bf16* p) {
-  bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+template <int W>
+__device__ __forceinline__ void load_vec(const bf16* p, float* v) {
+  if constexpr (W == 8) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+  } else {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)x[i];
+  }
 }
-__device__ __forceinline__ f32x4 load4(const float* p) {
-  return f32x4{p[0], p[1], p[2], p[3]};
+template <int W>
+__device__ __forceinline__ void load_vec(const float* p, float* v) {
+#pragma unroll
+  for (int i = 0; i < W; ++i) v[i] = p[i];
 }
 
 }  // namespace lgs

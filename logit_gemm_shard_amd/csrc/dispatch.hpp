@@ -37,15 +37,21 @@ inline TileId pick_tile(int M, int N) {
 
 inline int tile_bn(TileId t) { return kTileShapes[t].bn; }
 
+template <int BM, int BN, bool AK, bool BK, class Epi>
+inline GemmProblem<BM, BN, AK, BK, Epi> problem(const bf16* A, int64_t lda, const bf16* B,
+                                                int64_t ldb, int M, int N, int K, const Epi& epi) {
+  return GemmProblem<BM, BN, AK, BK, Epi>{A, lda, B, ldb, M, N, K, epi};
+}
+
 template <bool AK, bool BK, class Epi>
 inline hipError_t gemm_bf16(TileId t, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
                             int M, int N, int K, const Epi& epi, hipStream_t s) {
   switch (t) {
-    case T256x256: return launch_gemm_bf16<256, 256, AK, BK>(A, lda, B, ldb, M, N, K, epi, s);
-    case T256x224: return launch_gemm_bf16<256, 224, AK, BK>(A, lda, B, ldb, M, N, K, epi, s);
-    case T256x192: return launch_gemm_bf16<256, 192, AK, BK>(A, lda, B, ldb, M, N, K, epi, s);
-    case T256x160: return launch_gemm_bf16<256, 160, AK, BK>(A, lda, B, ldb, M, N, K, epi, s);
-    case T128x128: return launch_gemm_bf16<128, 128, AK, BK>(A, lda, B, ldb, M, N, K, epi, s);
+    case T256x256: return launch_gemm(problem<256, 256, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x224: return launch_gemm(problem<256, 224, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x192: return launch_gemm(problem<256, 192, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x160: return launch_gemm(problem<256, 160, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T128x128: return launch_gemm(problem<128, 128, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     default: return hipErrorInvalidValue;
   }
 }

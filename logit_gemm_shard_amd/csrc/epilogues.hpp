@@ -1,21 +1,27 @@
-// GEMM epilogues.  Each works on "quads": four consecutive output columns
-// n..n+3 of one row m, the unit both GEMM kernels hand out.  Columns come in
-// whole quads because every N the library accepts is a multiple of 8.
+// GEMM epilogues.  Each receives W consecutive output columns n..n+W-1 of
+// one row m (W = 8 from the bf16 MFMA kernel, 4 from the fp32 kernel).
+// Columns come in whole groups because every N routed here is a multiple
+// of 8.
 #pragma once
 
 #include "common.hpp"
+#include "gemm_bf16.hpp"
 
 namespace lgs {
 
 // C = acc
 template <typename T>
 struct EpiStore {
-  static constexpr bool kWholeTile = false;
   T* C;
   int64_t ldc;
   int M, N;
-  __device__ __forceinline__ void quad(int m, int n, f32x4 v) const {
-    if (m < M && n < N) store4(C + (int64_t)m * ldc + n, v);
+  template <int WN, int LD>
+  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
+    elementwise_slice<WN, LD>(*this, st, m0, nb, lane);
+  }
+  template <int W>
+  __device__ __forceinline__ void apply(int m, int n, const float* v) const {
+    if (m < M && n < N) store_vec<W>(C + (int64_t)m * ldc + n, v);
   }
 };
 
@@ -23,19 +29,23 @@ struct EpiStore {
 // Y = GeLU(U), the input of the row-parallel GEMM.
 template <typename T>
 struct EpiGeluFwd {
-  static constexpr bool kWholeTile = false;
   T* U;  // may be null
   int64_t ldu;
   T* Y;
   int64_t ldy;
   int M, N, act;
-  __device__ __forceinline__ void quad(int m, int n, f32x4 v) const {
+  template <int WN, int LD>
+  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
+    elementwise_slice<WN, LD>(*this, st, m0, nb, lane);
+  }
+  template <int W>
+  __device__ __forceinline__ void apply(int m, int n, const float* v) const {
     if (m >= M || n >= N) return;
-    if (U) store4(U + (int64_t)m * ldu + n, v);
-    f32x4 y;
+    if (U) store_vec<W>(U + (int64_t)m * ldu + n, v);
+    float y[W];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = gelu_f(v[i], act);
-    store4(Y + (int64_t)m * ldy + n, y);
+    for (int i = 0; i < W; ++i) y[i] = gelu_both(v[i], act).y;
+    store_vec<W>(Y + (int64_t)m * ldy + n, y);
   }
 };
 
@@ -43,7 +53,6 @@ struct EpiGeluFwd {
 // pre-activation U, writes dU = dY * GeLU'(U) and the recomputed Y = GeLU(U).
 template <typename T>
 struct EpiGeluBwd {
-  static constexpr bool kWholeTile = false;
   const T* U;
   int64_t ldu;
   T* dU;
@@ -51,17 +60,23 @@ struct EpiGeluBwd {
   T* Y;
   int64_t ldy;
   int M, N, act;
-  __device__ __forceinline__ void quad(int m, int n, f32x4 dy) const {
+  template <int WN, int LD>
+  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
+    elementwise_slice<WN, LD>(*this, st, m0, nb, lane);
+  }
+  template <int W>
+  __device__ __forceinline__ void apply(int m, int n, const float* dy) const {
     if (m >= M || n >= N) return;
-    const f32x4 u = load4(U + (int64_t)m * ldu + n);
-    f32x4 du, y;
+    float u[W], du[W], y[W];
+    load_vec<W>(U + (int64_t)m * ldu + n, u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      du[i] = dy[i] * gelu_grad_f(u[i], act);
-      y[i] = gelu_f(u[i], act);
+    for (int i = 0; i < W; ++i) {
+      const GeluVals g = gelu_both(u[i], act);
+      du[i] = dy[i] * g.dy;
+      y[i] = g.y;
     }
-    store4(dU + (int64_t)m * lddu + n, du);
-    store4(Y + (int64_t)m * ldy + n, y);
+    store_vec<W>(dU + (int64_t)m * lddu + n, du);
+    store_vec<W>(Y + (int64_t)m * ldy + n, y);
   }
 };
 

@@ -38,7 +38,23 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ swz(row)) << 4);
 }
 
-// Stage R rows of a K-contiguous operand: element (r, k) at base[r * ld + k].
+// Operand tiles are read with buffer loads: the resource covers the operand
+// from the tile's first row / column to its end, and the hardware range check
+// returns zeros for any offset past that, so ragged edges need no branches.
+// Offsets are 32-bit (operands are limited to 2 GiB, checked on the host).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Stage R rows of a K-contiguous operand: element (r, k) at base[r * ld + k],
+// `base` already offset to the tile's first row.
 template <int R, bool KMAJ>
 struct Stage;
 
@@ -46,18 +62,16 @@ template <int R>
 struct Stage<R, true> {
   static_assert((R * 8) % kThreads == 0, "tile rows must be a multiple of 32");
   static constexpr int kN = R * 8 / kThreads;
+  static constexpr int kSpareRows = 0;
   uint4 v[kN];
-  __device__ __forceinline__ void load(const bf16* __restrict__ base, int64_t ld, int row0,
-                                       int rows, int k0, int K, int tid) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int rows_left, int k0,
+                                       int K, int tid) {
 #pragma unroll
     for (int j = 0; j < kN; ++j) {
       const int q = tid + j * kThreads;
-      const int r = q >> 3, c = q & 7;
-      const int gr = row0 + r, gk = k0 + c * 8;
-      if (gr < rows && gk < K)
-        v[j] = *reinterpret_cast<const uint4*>(base + (int64_t)gr * ld + gk);
-      else
-        v[j] = make_uint4(0u, 0u, 0u, 0u);
+      const int r = q >> 3, gk = k0 + (q & 7) * 8;
+      const uint32_t off = (r < rows_left && gk < K) ? (uint32_t)(r * ld + gk) * 2u : kOutOfRange;
+      v[j] = buffer_load16(rs, off);
     }
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -69,30 +83,32 @@ struct Stage<R, true> {
   }
 };
 
-// Stage R rows of an M/N-contiguous operand: element (r, k) at base[k * ld + r].
-// Unit u covers rows 8q..8q+7 and k-block kb (8 k values): eight 16-byte
-// loads, one per k, then an in-register 8x8 transpose.
+// Stage R rows of an M/N-contiguous operand: element (r, k) at base[k * ld + r],
+// `base` already offset to the tile's first column.  Unit u covers rows
+// 8q..8q+7 and k-block kb (8 k values): eight 16-byte loads, one per k, then
+// an in-register 8x8 transpose.
 template <int R>
 struct Stage<R, false> {
   static_assert(R % 8 == 0, "tile rows must be a multiple of 8");
   static constexpr int kUnits = (R / 8) * (kBK / 8);
   static constexpr int kNU = (kUnits + kThreads - 1) / kThreads;
+  // Threads past the last unit still run the same code (no divergent branch
+  // around the loads): they read out of range (zeros) and write to spare rows.
+  static constexpr int kSpareRows = (kUnits % kThreads) ? 8 : 0;
   uint4 v[kNU][8];
-  __device__ __forceinline__ void load(const bf16* __restrict__ base, int64_t ld, int row0,
-                                       int rows, int k0, int K, int tid) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int rows_left, int k0,
+                                       int K, int tid) {
 #pragma unroll
     for (int u = 0; u < kNU; ++u) {
       const int unit = tid + u * kThreads;
-      if ((kUnits % kThreads) != 0 && unit >= kUnits) continue;
+      const bool active = kSpareRows == 0 || unit < kUnits;
       const int q = unit % (R / 8), kb = unit / (R / 8);
-      const int gr = row0 + q * 8;
+      const bool rv = active && q * 8 < rows_left;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int gk = k0 + kb * 8 + j;
-        if (gr < rows && gk < K)
-          v[u][j] = *reinterpret_cast<const uint4*>(base + (int64_t)gk * ld + gr);
-        else
-          v[u][j] = make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t off = (rv && gk < K) ? (uint32_t)(gk * ld + q * 8) * 2u : kOutOfRange;
+        v[u][j] = buffer_load16(rs, off);
       }
     }
   }
@@ -103,8 +119,9 @@ struct Stage<R, false> {
 #pragma unroll
     for (int u = 0; u < kNU; ++u) {
       const int unit = tid + u * kThreads;
-      if ((kUnits % kThreads) != 0 && unit >= kUnits) continue;
+      const bool active = kSpareRows == 0 || unit < kUnits;
       const int q = unit % (R / 8), kb = unit / (R / 8);
+      const int row0 = active ? q * 8 : R;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // output row 8q+i gathers element i of the eight k-rows; element i of a
@@ -117,11 +134,21 @@ struct Stage<R, false> {
         o.y = __builtin_amdgcn_perm(word(v[u][3], d), word(v[u][2], d), sel);
         o.z = __builtin_amdgcn_perm(word(v[u][5], d), word(v[u][4], d), sel);
         o.w = __builtin_amdgcn_perm(word(v[u][7], d), word(v[u][6], d), sel);
-        *reinterpret_cast<uint4*>(lds + lds_off(q * 8 + i, kb)) = o;
+        *reinterpret_cast<uint4*>(lds + lds_off(row0 + i, kb & 7)) = o;
       }
     }
   }
 };
+
+// Resource covering an operand from its tile's first row (K-contiguous) or
+// first column (M/N-contiguous) to the operand's last element.
+template <bool KMAJ>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, int64_t ld, int row0,
+                                                           int rows, int K) {
+  if (KMAJ)
+    return make_rsrc(base + (int64_t)row0 * ld, (uint32_t)(((int64_t)(rows - 1 - row0) * ld + K) * 2));
+  return make_rsrc(base + row0, (uint32_t)(((int64_t)(K - 1) * ld + (rows - row0)) * 2));
+}
 
 // Block index -> output tile.  The hardware deals consecutive workgroup ids
 // round-robin over the 8 XCDs (each with its own L2); renumber so that every
@@ -145,37 +172,81 @@ __device__ __forceinline__ void tile_of_block(int pid, int nblk, int tiles_m, in
   tn = in / gsz;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool AK, bool BK>
 struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int TM = WM / 16, TN = WN / 16;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
-  static constexpr int kLdsBytes = 2 * (BM + BN) * kRowBytes;
+  // one LDS buffer: A rows (+ spare rows), then B rows (+ spare rows)
+  static constexpr int kARows = BM + Stage<BM, AK>::kSpareRows;
+  static constexpr int kBufRows = kARows + BN + Stage<BN, BK>::kSpareRows;
+  static constexpr int kLdsBytes = 2 * kBufRows * kRowBytes;
 };
 
-// Hand every quad of a wave's accumulators to epi.quad(m, n, values).
-template <int TM, int TN, class Epi>
-__device__ __forceinline__ void for_quads(const f32x4 (&acc)[TM][TN], int mb, int nb, int lane,
-                                          const Epi& epi) {
+// Epilogue: each wave stages 16-row slices of its accumulators through LDS
+// (free once the K loop has passed its last barrier) and hands each slice to
+// the epilogue, which reads it back in whatever lane mapping suits it.  Global
+// stores become 16-byte and coalesced, and the epilogue math is one compact
+// loop body instead of being unrolled over every accumulator.
+template <int TM, int TN, int WN, class Epi>
+__device__ __forceinline__ void staged_epilogue(const f32x4 (&acc)[TM][TN], char* smem, int wave,
+                                                int lane, int mb, int nb, const Epi& epi) {
+  constexpr int LD = WN + 4;  // floats per staged row
+  float* st = reinterpret_cast<float*>(smem) + wave * 16 * LD;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      epi.quad(mb + i * 16 + (lane & 15), nb + j * 16 + 4 * (lane >> 4), acc[i][j]);
+      *reinterpret_cast<f32x4*>(st + (lane & 15) * LD + j * 16 + 4 * (lane >> 4)) = acc[i][j];
+    __syncthreads();
+    epi.template slice<WN, LD>(st, mb + i * 16, nb, lane);
+    __syncthreads();
+  }
 }
 
-template <int BM, int BN, bool AK, bool BK, class Epi>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ B,
-                      int64_t ldb, int M, int N, int K, Epi epi) {
-  using T = Tile<BM, BN>;
-  __shared__ __attribute__((aligned(16))) char smem[T::kLdsBytes];
+// Elementwise epilogues: lane c takes row c / (WN/8), columns 8*(c % (WN/8))..+7.
+template <int WN, int LD, class Epi>
+__device__ __forceinline__ void elementwise_slice(const Epi& epi, const float* st, int m0, int nb,
+                                                  int lane) {
+  constexpr int CHUNKS = 16 * WN / 8;
+#pragma unroll 1
+  for (int c = lane; c < CHUNKS; c += 64) {
+    const int r = c / (WN / 8), q = c - r * (WN / 8);
+    float v[8];
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(st + r * LD + q * 8);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(st + r * LD + q * 8 + 4);
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    epi.template apply<8>(m0 + r, nb + q * 8, v);
+  }
+}
 
+// One GEMM of the core: C[M, N] = A B with its epilogue, block tile BM x BN.
+template <int BM_, int BN_, bool AK_, bool BK_, class Epi_>
+struct GemmProblem {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr bool AK = AK_, BK = BK_;
+  using Epi = Epi_;
+  using T = Tile<BM, BN, AK, BK>;
+  const bf16* A;
+  int64_t lda;
+  const bf16* B;
+  int64_t ldb;
+  int M, N, K;
+  Epi epi;
+  __host__ __device__ int tiles_m() const { return (M + BM - 1) / BM; }
+  __host__ __device__ int tiles_n() const { return (N + BN - 1) / BN; }
+  __host__ __device__ int tiles() const { return tiles_m() * tiles_n(); }
+};
+
+// The block's work on output tile (tmi, tni) of problem p.
+template <class P>
+__device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int tni) {
+  using T = typename P::T;
+  constexpr int BM = P::BM, BN = P::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tmi, tni;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tmi, tni);
+  const int M = p.M, N = p.N, K = p.K;
   const int m0 = tmi * BM, n0 = tni * BN;
 
   f32x4 acc[T::TM][T::TN];
@@ -184,25 +255,27 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, const bf16* __res
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Stage<BM, AK> sa;
-  Stage<BN, BK> sb;
+  Stage<BM, P::AK> sa;
+  Stage<BN, P::BK> sb;
+  const __amdgpu_buffer_rsrc_t ra = tile_rsrc<P::AK>(p.A, p.lda, m0, M, K);
+  const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, n0, N, K);
   char* const buf0 = smem;
-  char* const buf1 = smem + (BM + BN) * kRowBytes;
+  char* const buf1 = smem + T::kBufRows * kRowBytes;
   const int nk = (K + kBK - 1) / kBK;
 
-  sa.load(A, lda, m0, M, 0, K, tid);
-  sb.load(B, ldb, n0, N, 0, K, tid);
+  sa.load(ra, p.lda, M - m0, 0, K, tid);
+  sb.load(rb, p.ldb, N - n0, 0, K, tid);
   sa.store(buf0, tid);
-  sb.store(buf0 + BM * kRowBytes, tid);
+  sb.store(buf0 + T::kARows * kRowBytes, tid);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
     const char* As = (kt & 1) ? buf1 : buf0;
-    const char* Bs = As + BM * kRowBytes;
+    const char* Bs = As + T::kARows * kRowBytes;
     const bool more = kt + 1 < nk;
     if (more) {
-      sa.load(A, lda, m0, M, (kt + 1) * kBK, K, tid);
-      sb.load(B, ldb, n0, N, (kt + 1) * kBK, K, tid);
+      sa.load(ra, p.lda, M - m0, (kt + 1) * kBK, K, tid);
+      sb.load(rb, p.ldb, N - n0, (kt + 1) * kBK, K, tid);
     }
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
@@ -223,27 +296,60 @@ void gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda, const bf16* __res
     if (more) {
       char* nxt = (kt & 1) ? buf0 : buf1;
       sa.store(nxt, tid);
-      sb.store(nxt + BM * kRowBytes, tid);
+      sb.store(nxt + T::kARows * kRowBytes, tid);
     }
     __syncthreads();
   }
 
   const int mb = m0 + wm * T::WM, nb = n0 + wn * T::WN;
-  // Quad-wise epilogues get their quads; whole-tile epilogues (the CE
-  // partials) reduce across the wave's accumulators themselves.
-  if constexpr (Epi::kWholeTile)
-    epi.template tile<T::TM, T::TN>(acc, mb, nb, lane);
-  else
-    for_quads(acc, mb, nb, lane, epi);
+  static_assert(4 * 16 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
+  staged_epilogue<T::TM, T::TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
 }
 
-// Host-side launch of one (BM, BN) instantiation; returns the grid size.
-template <int BM, int BN, bool AK, bool BK, class Epi>
-inline hipError_t launch_gemm_bf16(const bf16* A, int64_t lda, const bf16* B, int64_t ldb, int M,
-                                   int N, int K, const Epi& epi, hipStream_t stream) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BK, Epi>), dim3(tiles), dim3(kThreads), 0,
-                     stream, A, lda, B, ldb, M, N, K, epi);
+template <class P>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(P p) {
+  __shared__ __attribute__((aligned(16))) char smem[P::T::kLdsBytes];
+  int tmi, tni;
+  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m(), p.tiles_n(), tmi, tni);
+  gemm_tile(p, smem, tmi, tni);
+}
+
+// Several independent GEMMs in one launch: blocks [0, p0.tiles()) work on p0,
+// the next p1.tiles() on p1, the rest on p2.  Put the longest-K problems
+// first: blocks start in index order, so the short tiles of the later
+// problems fill the compute units the long ones leave free.
+template <class P0, class P1, class P2>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_group3_kernel(P0 p0, P1 p1, P2 p2) {
+  constexpr int kL0 = P0::T::kLdsBytes, kL1 = P1::T::kLdsBytes, kL2 = P2::T::kLdsBytes;
+  constexpr int kL = kL0 > kL1 ? (kL0 > kL2 ? kL0 : kL2) : (kL1 > kL2 ? kL1 : kL2);
+  __shared__ __attribute__((aligned(16))) char smem[kL];
+  int pid = blockIdx.x, tmi, tni;
+  const int t0 = p0.tiles(), t1 = p1.tiles();
+  if (pid < t0) {
+    tile_of_block(pid, t0, p0.tiles_m(), p0.tiles_n(), tmi, tni);
+    gemm_tile(p0, smem, tmi, tni);
+  } else if ((pid -= t0) < t1) {
+    tile_of_block(pid, t1, p1.tiles_m(), p1.tiles_n(), tmi, tni);
+    gemm_tile(p1, smem, tmi, tni);
+  } else {
+    pid -= t1;
+    tile_of_block(pid, p2.tiles(), p2.tiles_m(), p2.tiles_n(), tmi, tni);
+    gemm_tile(p2, smem, tmi, tni);
+  }
+}
+
+template <class P>
+inline hipError_t launch_gemm(const P& p, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<P>), dim3(p.tiles()), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <class P0, class P1, class P2>
+inline hipError_t launch_gemm_group3(const P0& p0, const P1& p1, const P2& p2, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_bf16_group3_kernel<P0, P1, P2>), dim3(p0.tiles() + p1.tiles() + p2.tiles()),
+                     dim3(kThreads), 0, stream, p0, p1, p2);
   return hipGetLastError();
 }
 

@@ -2,7 +2,8 @@
 // LDS-tiled vector-ALU kernel, 64x64 output tile, K step 16, 256 threads each
 // owning a 4x4 block (four quads of four consecutive columns).  Operands may
 // be K-contiguous or M/N-contiguous; every element is read once per tile with
-// scalar loads, so no alignment beyond 4 bytes is required.
+// scalar loads, so no alignment beyond 4 bytes is required.  Each thread
+// hands its rows to the epilogue four columns at a time.
 #pragma once
 
 #include "common.hpp"
@@ -50,8 +51,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    epi.quad(m0 + ty * 4 + i, n0 + tx * 4, f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]});
+  for (int i = 0; i < 4; ++i) epi.template apply<4>(m0 + ty * 4 + i, n0 + tx * 4, acc[i]);
 }
 
 template <bool AK, bool BK, class Epi>

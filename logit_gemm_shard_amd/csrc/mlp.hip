@@ -58,14 +58,19 @@ hipError_t mlp_bwd(bool is_bf16, int M, int h, int f, int act, const void* X, in
     EpiGeluBwd<bf16> e1{(const bf16*)U, ldu, du, ldw, y, ldw, M, f, act};
     e = gemm_bf16<true, true>(pick_tile(M, f), dz, lddz, b, ldb, M, f, h, e1, s);
     if (e != hipSuccess) return e;
+    // dB and dA reduce over all M tokens (the longest K), dX over f: one
+    // grouped launch, long tiles first, so the dX tiles fill the compute
+    // units the few weight-gradient tiles leave idle.
     EpiStore<bf16> eb{(bf16*)dB, lddb, f, h};
-    e = gemm_bf16<false, false>(pick_tile(f, h), y, ldw, dz, lddz, f, h, M, eb, s);
-    if (e != hipSuccess) return e;
     EpiStore<bf16> ea{(bf16*)dA, ldda, h, f};
-    e = gemm_bf16<false, false>(pick_tile(h, f), x, ldx, du, ldw, h, f, M, ea, s);
-    if (e != hipSuccess) return e;
     EpiStore<bf16> ex{(bf16*)dX, lddx, M, h};
-    return gemm_bf16<true, true>(pick_tile(M, h), du, ldw, a, lda, M, h, f, ex, s);
+    if (f >= 256 && h >= 256 && M >= 256)
+      return launch_gemm_group3(problem<256, 256, false, false>(y, ldw, dz, lddz, f, h, M, eb),
+                                problem<256, 256, false, false>(x, ldx, du, ldw, h, f, M, ea),
+                                problem<256, 256, true, true>(du, ldw, a, lda, M, h, f, ex), s);
+    return launch_gemm_group3(problem<128, 128, false, false>(y, ldw, dz, lddz, f, h, M, eb),
+                              problem<128, 128, false, false>(x, ldx, du, ldw, h, f, M, ea),
+                              problem<128, 128, true, true>(du, ldw, a, lda, M, h, f, ex), s);
   }
   const float *x = (const float*)X, *a = (const float*)A, *b = (const float*)B, *dz = (const float*)dZ;
   float *y = (float*)Yws, *du = (float*)dUws;

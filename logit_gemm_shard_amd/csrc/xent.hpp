@@ -1,8 +1,9 @@
 // Fused vocab-parallel cross-entropy: the logit GEMM's epilogue reduces each
 // row of the wave's logit tile to (max, sum of exp relative to that max,
 // target logit, first argmax) and writes those four numbers per row and per
-// wave column-slab.  Logits never leave registers.  A small merge kernel then
-// folds the slabs of the rank's vocabulary slice into the rank's partials.
+// wave column-slab.  Logits never leave the chip: they go from the matrix
+// cores' accumulators through LDS to the reductions.  A small merge kernel
+// then folds the slabs of the rank's vocabulary slice into the rank's partials.
 //
 // "LIT-022: Megatron-LM ..." (dmarx anthology), "Key takeaways": fusing the
 // parallel logit GEMM into the loss replaces the b*s*v all-gather of logits
@@ -10,6 +11,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "gemm_bf16.hpp"
 
 namespace lgs {
 
@@ -17,67 +19,65 @@ struct XentSlabs {
   float* m;      // [slabs][M] slab max
   float* l;      // [slabs][M] sum exp(z - slab max)
   float* t;      // [slabs][M] target logit if the target is in the slab, else +0
-  int32_t* idx;  // [slabs][M] slab-local column of the first maximum
+  int32_t* idx;  // [slabs][M] slice-local column of the slab's first maximum
 };
 
 struct EpiXent {
-  static constexpr bool kWholeTile = true;
   XentSlabs s;
   const int32_t* targets;  // [M] global vocabulary ids
   int vocab_start;         // first global id of this rank's slice
   int M, N;                // tokens, slice width
   int WN;                  // wave tile width: slab = wave column
 
-  template <int TM, int TN>
-  __device__ __forceinline__ void tile(const f32x4 (&acc)[TM][TN], int mb, int nb, int lane) const {
-    const int slab = nb / WN;
-    const int g = lane >> 4;
+  // A staged slice holds 16 rows x WN logits.  Four lanes share a row, each
+  // reducing a contiguous quarter of it (columns visited in increasing
+  // order), then the four combine with lane shuffles.
+  template <int WNt, int LD>
+  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
+    static_assert(WNt % 16 == 0, "a quarter row is read as float4s");
+    constexpr int Q = WNt / 4;
+    const int r = lane >> 2, part = lane & 3;
+    const int m = m0 + r;
+    const int c0 = part * Q;
+    const float* row = st + r * LD + c0;
+    const int ncols = min(Q, N - (nb + c0));  // valid columns of this quarter (may be <= 0)
+    const int tl = (m < M ? targets[m] - vocab_start : -1) - (nb + c0);
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll 4
+    for (int c = 0; c < Q; c += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = mb + i * 16 + (lane & 15);
-      const bool mv = m < M;
-      const int tl = mv ? targets[m] - vocab_start : -1;
-      // lane-local max / first argmax, columns visited in increasing order
-      float best = -INFINITY;
-      int bi = 0x7fffffff;
+      for (int k = 0; k < 4; ++k)
+        if (c + k < ncols && v[k] > best) { best = v[k]; bi = nb + c0 + c + k; }
+    }
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+    for (int off = 1; off <= 2; off <<= 1) {
+      const float ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    float sum = 0.f, tv = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < Q; c += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = nb + j * 16 + 4 * g + r;
-          const float v = acc[i][j][r];
-          if (n < N && v > best) { best = v; bi = n; }
+      for (int k = 0; k < 4; ++k)
+        if (c + k < ncols) {
+          sum += fast_exp(v[k] - best);
+          if (c + k == tl) tv = v[k];
         }
-      // the row is spread over the four 16-lane groups of the wave
-#pragma unroll
-      for (int off = 16; off <= 32; off <<= 1) {
-        const float ob = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-      }
-      float sum = 0.f, tv = 0.f;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = nb + j * 16 + 4 * g + r;
-          const float v = acc[i][j][r];
-          if (n < N) {
-            sum += __expf(v - best);
-            if (n == tl) tv = v;
-          }
-        }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      tv += __shfl_xor(tv, 16);
-      tv += __shfl_xor(tv, 32);
-      if (g == 0 && mv) {
-        const int64_t o = (int64_t)slab * M + m;
-        s.m[o] = best;
-        s.l[o] = sum;
-        s.t[o] = tv;
-        s.idx[o] = bi;
-      }
+    }
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    tv += __shfl_xor(tv, 1);
+    tv += __shfl_xor(tv, 2);
+    if (part == 0 && m < M) {
+      const int64_t o = (int64_t)(nb / WN) * M + m;
+      s.m[o] = best;
+      s.l[o] = sum;
+      s.t[o] = tv;
+      s.idx[o] = bi;
     }
   }
 };

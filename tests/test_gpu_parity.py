@@ -439,3 +439,30 @@ def test_full_size_xent_all_ranks_sampled():
         if own.any():
             assert_close(f"T_{r} owned", st[r, 2][rows][own], T[own], BF16)
         check_argmax(f64(H), E64[a:a + Vr], a, amh[r], rows)
+
+
+# ------------------------------------------------- the epilogue's GeLU math
+
+@pytest.mark.parametrize("act", ["erf", "tanh"])
+def test_gelu_epilogue_error_bound(act):
+    """fp32 path with X = I, dZ = I, B_i = 1: then U = A_i exactly, the
+    backward's dA_i = GeLU'(U) and dB_i = GeLU(U)^T exactly (one nonzero
+    product per sum), which isolates the device GeLU / GeLU' evaluation."""
+    d = dev()
+    n = 64
+    u = torch.linspace(-10.0, 10.0, n * n, dtype=F32).reshape(n, n)
+    eye = torch.eye(n, dtype=F32)
+    step(f"GeLU epilogue error bound ({act})")
+    U, Y, Z = run_fwd(eye.to(d), u.to(d), torch.ones(n, n, dtype=F32, device=d), 1, n, 1, 0, act)
+    dX, dA, dB = run_bwd(eye.to(d), u.to(d), torch.ones(n, n, dtype=F32, device=d), u.to(d), eye.to(d),
+                         1, n, 1, 0, act)
+    sync()
+    u64 = f64(u)
+    bound = 4e-7 * np.maximum(1.0, np.abs(u64))
+    assert np.array_equal(f64(U), u64)
+    for name, got, ref in (("Y", f64(Y), oracle.mlp.gelu(u64, act)),
+                           ("dB^T", f64(dB).T, oracle.mlp.gelu(u64, act)),
+                           ("dA", f64(dA), oracle.mlp.gelu_grad(u64, act))):
+        err = np.abs(got - ref)
+        print(f"    {name}: max |err| = {err.max():.2e}, max |err|/bound = {(err / bound).max():.2f}", flush=True)
+        assert np.all(err <= bound), name
