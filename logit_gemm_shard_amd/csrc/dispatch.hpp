@@ -9,12 +9,15 @@ namespace lgs {
 enum TileId : int { T256x256 = 0, T256x224, T256x192, T256x160, T128x128, kNumTiles };
 
 struct TileShape {
-  int bm, bn;
-  float eff;  // relative per-CU efficiency (bigger tiles reuse each LDS byte more)
+  int bm, bn, wgm;  // block tile and the waves' grid (wgm x 4/wgm)
+  float eff;        // relative per-CU efficiency (bigger tiles reuse each LDS byte more)
 };
 
-constexpr TileShape kTileShapes[kNumTiles] = {
-    {256, 256, 1.00f}, {256, 224, 0.98f}, {256, 192, 0.96f}, {256, 160, 0.93f}, {128, 128, 0.75f}};
+constexpr TileShape kTileShapes[kNumTiles] = {{256, 256, 2, 1.00f},
+                                              {256, 224, 4, 0.97f},
+                                              {256, 192, 2, 0.96f},
+                                              {256, 160, 4, 0.92f},
+                                              {128, 128, 2, 0.75f}};
 
 // The chip runs one 256x* block per compute unit at a time (the double
 // buffered tiles use 96-128 KB of the 160 KB LDS), so a launch proceeds in
@@ -36,22 +39,24 @@ inline TileId pick_tile(int M, int N) {
 }
 
 inline int tile_bn(TileId t) { return kTileShapes[t].bn; }
+inline int tile_wn(TileId t) { return kTileShapes[t].bn * kTileShapes[t].wgm / 4; }
 
-template <int BM, int BN, bool AK, bool BK, class Epi>
-inline GemmProblem<BM, BN, AK, BK, Epi> problem(const bf16* A, int64_t lda, const bf16* B,
-                                                int64_t ldb, int M, int N, int K, const Epi& epi) {
-  return GemmProblem<BM, BN, AK, BK, Epi>{A, lda, B, ldb, M, N, K, epi};
+template <int BM, int BN, int WGM, bool AK, bool BK, class Epi>
+inline GemmProblem<BM, BN, WGM, AK, BK, Epi> problem(const bf16* A, int64_t lda, const bf16* B,
+                                                     int64_t ldb, int M, int N, int K,
+                                                     const Epi& epi) {
+  return GemmProblem<BM, BN, WGM, AK, BK, Epi>{A, lda, B, ldb, M, N, K, epi};
 }
 
 template <bool AK, bool BK, class Epi>
 inline hipError_t gemm_bf16(TileId t, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
                             int M, int N, int K, const Epi& epi, hipStream_t s) {
   switch (t) {
-    case T256x256: return launch_gemm(problem<256, 256, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x224: return launch_gemm(problem<256, 224, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x192: return launch_gemm(problem<256, 192, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x160: return launch_gemm(problem<256, 160, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T128x128: return launch_gemm(problem<128, 128, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x256: return launch_gemm(problem<256, 256, 2, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x224: return launch_gemm(problem<256, 224, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x192: return launch_gemm(problem<256, 192, 2, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x160: return launch_gemm(problem<256, 160, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T128x128: return launch_gemm(problem<128, 128, 2, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     default: return hipErrorInvalidValue;
   }
 }

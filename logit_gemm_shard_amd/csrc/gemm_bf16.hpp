@@ -1,142 +1,122 @@
-// bf16 GEMM core for gfx950: C[M,N] = sum_k A(m,k) B(k,n), fp32 accumulate,
-// on the 16x16x32 bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
+// bf16 GEMM core for gfx950 (CDNA4): C[M,N] = sum_k A(m,k) B(k,n), fp32
+// accumulation on the 32x32x16 bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Block: 256 threads = 4 wave64s in a 2x2 grid; block tile BM x BN, K step 64.
-// Each wave owns a (BM/2) x (BN/2) tile of 16x16 accumulators.
+// Block: 256 threads = 4 wave64s in a WGM x WGN grid (2x2 or 4x1); block tile
+// BM x BN; K step 64, split into four 16-wide sub-steps.
 //
-// Data path per K step:
-//   global --(16 B per lane, vector loads into registers)--> registers
-//          --(ds_write_b128)--> LDS, double buffered, one barrier per step
-//          --(ds_read_b128)--> MFMA operands.
-// The next step's global loads are issued before the current step's MFMAs so
-// their latency hides behind the math.
+// Operand tiles go global -> LDS with direct-to-LDS buffer loads (each wave
+// instruction moves 64 x 16 B into 1 KB of LDS; the hardware range check
+// returns zeros past an operand's end, so ragged edges need no branches).
+// Two LDS stages: while tile kt is multiplied out of one stage, tile kt+1
+// lands in the other.
 //
-// LDS holds every tile "K-contiguous": row r (an m or an n) is 64 bf16 =
-// 128 B = eight 16-byte chunks, chunk c stored at slot c ^ swz(r) so that
-// both the fragment reads (16 consecutive rows, one chunk) and the transposed
-// stores (rows 8 apart) spread over all banks.  An operand whose memory is
-// K-contiguous is copied chunk by chunk; an operand whose memory is
-// M/N-contiguous is loaded as 8x8 bf16 blocks (8 k-rows of 16 B) and
-// transposed in registers with byte permutes before the LDS store.  After
-// staging, all operand layouts run the same MFMA loop.
+// LDS layout per operand and stage:
+//  * K-contiguous operand (element (r,k) at base[r*ld + k]): R rows of 64 k =
+//    128 B; 16-B chunk c of row r sits at slot c ^ swz(r), swz(r) =
+//    (r & 7) ^ ((r >> 3) & 1).  Fragment reads (32 consecutive rows, one
+//    chunk column per half-wave) then touch distinct banks, and the swizzle
+//    of a row only depends on r & 15, so every fragment row of a wave is the
+//    same per-lane address plus an immediate offset.
+//  * M/N-contiguous operand (element (r,k) at base[k*ld + r]): 64 k-rows of R
+//    values, kept in that orientation; row pitch padded so four consecutive
+//    k-rows start 64 B apart modulo 256 B.  Fragments come from two
+//    ds_read_b64_tr_b16 (LDS transpose reads: within each 16-lane group,
+//    lanes 4j..4j+3 address row j of a 4 x 16 block and lane i receives
+//    column i), so no register transposes are needed.
 //
 // MFMA operand roles are swapped (the B tile feeds the instruction's first
-// operand) so that each lane ends with four consecutive output columns of
-// one row: lane l of 16x16 tile (i, j) holds C[16i + l%16][16j + 4(l/16) + 0..3].
+// operand) so each lane ends with runs of four consecutive output columns:
+// lane l, accumulator element r of 32x32 tile (i, j) is
+// C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4].
 #pragma once
 
 #include "common.hpp"
 
 namespace lgs {
 
+#define LGS_AS3 __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 constexpr int kThreads = 256;
-constexpr int kBK = 64;
-constexpr int kRowBytes = kBK * 2;  // 128 B per LDS row
-
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
-}
-
-// Operand tiles are read with buffer loads: the resource covers the operand
-// from the tile's first row / column to its end, and the hardware range check
-// returns zeros for any offset past that, so ragged edges need no branches.
-// Offsets are 32-bit (operands are limited to 2 GiB, checked on the host).
+constexpr int kBK = 32;           // K per pipeline stage (two 16-wide MFMA sub-steps)
+constexpr int kLdsMax = 160 * 1024;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).  The direct-to-LDS
+// loads are waited for explicitly: a barrier alone does not wait for them.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(63 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
 }
 
-// Stage R rows of a K-contiguous operand: element (r, k) at base[r * ld + k],
-// `base` already offset to the tile's first row.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
 template <int R, bool KMAJ>
-struct Stage;
+struct OpLayout;
 
 template <int R>
-struct Stage<R, true> {
-  static_assert((R * 8) % kThreads == 0, "tile rows must be a multiple of 32");
-  static constexpr int kN = R * 8 / kThreads;
-  static constexpr int kSpareRows = 0;
-  uint4 v[kN];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int rows_left, int k0,
-                                       int K, int tid) {
-#pragma unroll
-    for (int j = 0; j < kN; ++j) {
-      const int q = tid + j * kThreads;
-      const int r = q >> 3, gk = k0 + (q & 7) * 8;
-      const uint32_t off = (r < rows_left && gk < K) ? (uint32_t)(r * ld + gk) * 2u : kOutOfRange;
-      v[j] = buffer_load16(rs, off);
-    }
+struct OpLayout<R, true> {
+  static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
+  static constexpr int kBytes = R * 64;
+  static constexpr int kInstr = R / 16;  // 1 KB loads per stage
+  static constexpr int kReadsPerFrag = 1;
+  // byte offset (from the tile's first row) that lane `lane` of load n reads
+  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left,
+                                                     int k0, int K) {
+    const int row = 16 * n + (lane >> 2);
+    const int gk = k0 + ((lane & 3) ^ swz(row)) * 8;
+    return (row < rows_left && gk < K) ? (uint32_t)(row * ld + gk) * 2u : kOutOfRange;
   }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int j = 0; j < kN; ++j) {
-      const int q = tid + j * kThreads;
-      *reinterpret_cast<uint4*>(lds + lds_off(q >> 3, q & 7)) = v[j];
-    }
+  // rows row0 + lane%32 (row0 a multiple of 32), k = 16 s + 8 (lane/32) .. +7
+  __device__ __forceinline__ static bf16x8 frag(const char* base, int row0, int s, int lane) {
+    const int row = row0 + (lane & 31);
+    const int c = 2 * s + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(base + row * 64 + ((c ^ swz(row)) << 4));
   }
 };
 
-// Stage R rows of an M/N-contiguous operand: element (r, k) at base[k * ld + r],
-// `base` already offset to the tile's first column.  Unit u covers rows
-// 8q..8q+7 and k-block kb (8 k values): eight 16-byte loads, one per k, then
-// an in-register 8x8 transpose.
 template <int R>
-struct Stage<R, false> {
-  static_assert(R % 8 == 0, "tile rows must be a multiple of 8");
-  static constexpr int kUnits = (R / 8) * (kBK / 8);
-  static constexpr int kNU = (kUnits + kThreads - 1) / kThreads;
-  // Threads past the last unit still run the same code (no divergent branch
-  // around the loads): they read out of range (zeros) and write to spare rows.
-  static constexpr int kSpareRows = (kUnits % kThreads) ? 8 : 0;
-  uint4 v[kNU][8];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int rows_left, int k0,
-                                       int K, int tid) {
-#pragma unroll
-    for (int u = 0; u < kNU; ++u) {
-      const int unit = tid + u * kThreads;
-      const bool active = kSpareRows == 0 || unit < kUnits;
-      const int q = unit % (R / 8), kb = unit / (R / 8);
-      const bool rv = active && q * 8 < rows_left;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gk = k0 + kb * 8 + j;
-        const uint32_t off = (rv && gk < K) ? (uint32_t)(gk * ld + q * 8) * 2u : kOutOfRange;
-        v[u][j] = buffer_load16(rs, off);
-      }
-    }
+struct OpLayout<R, false> {
+  static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
+  static constexpr int kPitch = 2 * R + (((2 * R) % 256 == 0 || (2 * R) % 256 == 128) ? 64 : 0);
+  static constexpr int kCpr = kPitch / 16;  // 16-B chunks per k-row (a multiple of 4)
+  static constexpr int kBytes = kBK * kPitch;
+  static constexpr int kInstr = kBK * kCpr / 64;  // kBK k-rows x kCpr chunks / 64 lanes
+  static constexpr int kReadsPerFrag = 2;
+  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left,
+                                                     int k0, int K) {
+    const int d = n * 64 + lane;
+    const int krow = d / kCpr, ch = d - krow * kCpr;
+    const int gk = k0 + krow;
+    return (ch * 8 < R && ch * 8 < rows_left && gk < K) ? (uint32_t)(gk * ld + ch * 8) * 2u
+                                                         : kOutOfRange;
   }
-  __device__ __forceinline__ static unsigned word(const uint4& x, int d) {
-    return d == 0 ? x.x : d == 1 ? x.y : d == 2 ? x.z : x.w;
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int u = 0; u < kNU; ++u) {
-      const int unit = tid + u * kThreads;
-      const bool active = kSpareRows == 0 || unit < kUnits;
-      const int q = unit % (R / 8), kb = unit / (R / 8);
-      const int row0 = active ? q * 8 : R;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // output row 8q+i gathers element i of the eight k-rows; element i of a
-        // row lives in 32-bit word i/2, low half for even i, high half for odd i.
-        // v_perm_b32 byte selectors: 0-3 pick from the second source, 4-7 from the first.
-        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        const int d = i >> 1;
-        uint4 o;
-        o.x = __builtin_amdgcn_perm(word(v[u][1], d), word(v[u][0], d), sel);
-        o.y = __builtin_amdgcn_perm(word(v[u][3], d), word(v[u][2], d), sel);
-        o.z = __builtin_amdgcn_perm(word(v[u][5], d), word(v[u][4], d), sel);
-        o.w = __builtin_amdgcn_perm(word(v[u][7], d), word(v[u][6], d), sel);
-        *reinterpret_cast<uint4*>(lds + lds_off(row0 + i, kb & 7)) = o;
-      }
-    }
+  // The transposed reads are issued as inline assembly: the compiler would
+  // otherwise treat them as possibly aliasing the direct-to-LDS loads in
+  // flight and wait for all of those first.  Their results are only valid
+  // after an explicit lgkmcnt wait (the pipeline waits at each sub-step).
+  __device__ __forceinline__ static bf16x8 frag(const char* base, int row0, int s, int lane) {
+    const int g = lane >> 4, i16 = lane & 15;
+    const int krow = 16 * s + 8 * (g >> 1) + (i16 >> 2);
+    const char* p0 = base + krow * kPitch + (row0 + 16 * (g & 1) + 4 * (i16 & 3)) * 2;
+    const uint32_t a = (uint32_t)(uintptr_t)(LGS_AS3 const char*)p0;
+    s16x4 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"(4 * kPitch));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
   }
 };
 
@@ -172,34 +152,38 @@ __device__ __forceinline__ void tile_of_block(int pid, int nblk, int tiles_m, in
   tn = in / gsz;
 }
 
-template <int BM, int BN, bool AK, bool BK>
+template <int BM, int BN, int WGM, bool AK, bool BK>
 struct Tile {
-  static constexpr int WM = BM / 2, WN = BN / 2;
-  static constexpr int TM = WM / 16, TN = WN / 16;
-  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
-  // one LDS buffer: A rows (+ spare rows), then B rows (+ spare rows)
-  static constexpr int kARows = BM + Stage<BM, AK>::kSpareRows;
-  static constexpr int kBufRows = kARows + BN + Stage<BN, BK>::kSpareRows;
-  static constexpr int kLdsBytes = 2 * kBufRows * kRowBytes;
+  static constexpr int WGN = 4 / WGM;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  using LA = OpLayout<BM, AK>;
+  using LB = OpLayout<BN, BK>;
+  static constexpr int kStage = LA::kBytes + LB::kBytes;
+  static constexpr int kStages = kLdsMax / kStage < 5 ? kLdsMax / kStage : 5;
+  static_assert(kStages >= 3, "need at least three stages");
+  static constexpr int kLdsBytes = kStages * kStage;
 };
 
-// Epilogue: each wave stages 16-row slices of its accumulators through LDS
+// Epilogue: each wave stages 32-row slices of its accumulators through LDS
 // (free once the K loop has passed its last barrier) and hands each slice to
-// the epilogue, which reads it back in whatever lane mapping suits it.  Global
-// stores become 16-byte and coalesced, and the epilogue math is one compact
-// loop body instead of being unrolled over every accumulator.
+// the epilogue, which reads it back in whatever lane mapping suits it.
 template <int TM, int TN, int WN, class Epi>
-__device__ __forceinline__ void staged_epilogue(const f32x4 (&acc)[TM][TN], char* smem, int wave,
+__device__ __forceinline__ void staged_epilogue(const f32x16 (&acc)[TM][TN], char* smem, int wave,
                                                 int lane, int mb, int nb, const Epi& epi) {
   constexpr int LD = WN + 4;  // floats per staged row
-  float* st = reinterpret_cast<float*>(smem) + wave * 16 * LD;
+  float* st = reinterpret_cast<float*>(smem) + wave * 32 * LD;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      *reinterpret_cast<f32x4*>(st + (lane & 15) * LD + j * 16 + 4 * (lane >> 4)) = acc[i][j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(st + (lane & 31) * LD + j * 32 + 8 * q + 4 * (lane >> 5)) =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     __syncthreads();
-    epi.template slice<WN, LD>(st, mb + i * 16, nb, lane);
+    epi.template slice<WN, LD>(st, mb + i * 32, nb, lane);
     __syncthreads();
   }
 }
@@ -208,7 +192,7 @@ __device__ __forceinline__ void staged_epilogue(const f32x4 (&acc)[TM][TN], char
 template <int WN, int LD, class Epi>
 __device__ __forceinline__ void elementwise_slice(const Epi& epi, const float* st, int m0, int nb,
                                                   int lane) {
-  constexpr int CHUNKS = 16 * WN / 8;
+  constexpr int CHUNKS = 32 * WN / 8;
 #pragma unroll 1
   for (int c = lane; c < CHUNKS; c += 64) {
     const int r = c / (WN / 8), q = c - r * (WN / 8);
@@ -222,12 +206,12 @@ __device__ __forceinline__ void elementwise_slice(const Epi& epi, const float* s
 }
 
 // One GEMM of the core: C[M, N] = A B with its epilogue, block tile BM x BN.
-template <int BM_, int BN_, bool AK_, bool BK_, class Epi_>
+template <int BM_, int BN_, int WGM_, bool AK_, bool BK_, class Epi_>
 struct GemmProblem {
-  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_;
   static constexpr bool AK = AK_, BK = BK_;
   using Epi = Epi_;
-  using T = Tile<BM, BN, AK, BK>;
+  using T = Tile<BM, BN, WGM, AK, BK>;
   const bf16* A;
   int64_t lda;
   const bf16* B;
@@ -243,73 +227,138 @@ struct GemmProblem {
 template <class P>
 __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int tni) {
   using T = typename P::T;
-  constexpr int BM = P::BM, BN = P::BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  using LA = typename T::LA;
+  using LB = typename T::LB;
+  constexpr int TM = T::TM, TN = T::TN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WGN, wn = wave % T::WGN;
   const int M = p.M, N = p.N, K = p.K;
-  const int m0 = tmi * BM, n0 = tni * BN;
+  const int m0 = tmi * P::BM, n0 = tni * P::BN;
 
-  f32x4 acc[T::TM][T::TN];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < T::TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  Stage<BM, P::AK> sa;
-  Stage<BN, P::BK> sb;
   const __amdgpu_buffer_rsrc_t ra = tile_rsrc<P::AK>(p.A, p.lda, m0, M, K);
   const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, n0, N, K);
-  char* const buf0 = smem;
-  char* const buf1 = smem + T::kBufRows * kRowBytes;
   const int nk = (K + kBK - 1) / kBK;
+  constexpr int IA = (LA::kInstr + 3) / 4, IB = (LB::kInstr + 3) / 4;
 
-  sa.load(ra, p.lda, M - m0, 0, K, tid);
-  sb.load(rb, p.ldb, N - n0, 0, K, tid);
-  sa.store(buf0, tid);
-  sb.store(buf0 + T::kARows * kRowBytes, tid);
+  // Direct-to-LDS loads of tile kt into stage `st`.  Load n of an operand
+  // fills bytes [1024 n, 1024 n + 1024) of its region; waves take every 4th
+  // load (a duplicate of the last load where the count is not a multiple of
+  // four: the same bytes written twice with the same values).
+  // Byte offsets each lane reads for tile kt (computed ahead of the issue).
+  uint32_t offa[IA], offb[IB];
+  auto load_offsets = [&](int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int t = 0; t < IA; ++t)
+      offa[t] = LA::src_off(min(wave + 4 * t, LA::kInstr - 1), lane, p.lda, M - m0, k0, K);
+#pragma unroll
+    for (int t = 0; t < IB; ++t)
+      offb[t] = LB::src_off(min(wave + 4 * t, LB::kInstr - 1), lane, p.ldb, N - n0, k0, K);
+  };
+  // Direct-to-LDS loads into stage `st`.  Load n of an operand fills bytes
+  // [1024 n, 1024 n + 1024) of its region; waves take every 4th load (a
+  // duplicate of the last load where the count is not a multiple of four: the
+  // same bytes written twice with the same values).
+  auto load_issue = [&](int st) {
+    char* base = smem + st * T::kStage;
+#pragma unroll
+    for (int t = 0; t < IA; ++t) {
+      const int n = min(wave + 4 * t, LA::kInstr - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LGS_AS3 void*)(base + n * 1024), 16, (int)offa[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < IB; ++t) {
+      const int n = min(wave + 4 * t, LB::kInstr - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LGS_AS3 void*)(base + LA::kBytes + n * 1024), 16, (int)offb[t], 0, 0, 0);
+    }
+  };
+  auto load_tile = [&](int st, int kt) {
+    load_offsets(kt);
+    load_issue(st);
+  };
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto read_frags = [&](const char* base, int s, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = LA::frag(base, wm * T::WM + i * 32, s, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = LB::frag(base + LA::kBytes, wn * T::WN + j * 32, s, lane);
+  };
+  auto mma = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+
+  // Ring of S stages of 32-wide K tiles.  Step kt (tile kt in stage kt % S):
+  // read the fragments of its second 16-wide sub-step, MFMAs on the first;
+  // wait for this wave's loads of tile kt+1, barrier (tile kt+1 visible to all
+  // waves; every read of tile kt-1's stage retired), start loading tile
+  // kt+S-1 into that stage; read tile kt+1's first fragments, MFMAs on the
+  // second sub-step.  Loads thus have S-2 steps to land.  Tiles past the end
+  // load zeros, so the loop body has no branches.
+  constexpr int S = T::kStages;
+  constexpr int kPer = IA + IB;  // loads per tile per wave
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) load_tile(t, t);
+  wait_vmcnt<(S - 2) * kPer>();  // this wave's loads of tile 0 done
+  __syncthreads();
+  read_frags(smem, 0, fa[0], fb[0]);
+  wait_lgkm0();
+  int st_cur = 0;
+  constexpr int kMfma = TM * TN;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st_nxt = st_cur + 1 == S ? 0 : st_cur + 1;
+    const int st_free = st_cur == 0 ? S - 1 : st_cur - 1;
+    const char* cur = smem + st_cur * T::kStage;
+    const char* nxt = smem + st_nxt * T::kStage;
+    // first sub-step: issue the second sub-step's fragment reads, then the
+    // first sub-step's MFMAs (and the address math of the next loads)
+    read_frags(cur, 1, fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa[0], fb[0]);
+    load_offsets(kt + S - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(S - 3) * kPer>();  // this wave's loads of tile kt+1 done
+    __syncthreads();
+    wait_lgkm0();                  // second sub-step's fragments in registers
+    // second sub-step: tile kt+1's first fragment reads, then its MFMAs with
+    // the loads of tile kt+S-1 issued between them
+    read_frags(nxt, 0, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_issue(st_free);
+    mma(fa[1], fb[1]);
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // 1 MFMA
+      if (q < kPer) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 direct-to-LDS load
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();                  // tile kt+1's first fragments in registers
+    st_cur = st_nxt;
+  }
+  wait_vmcnt<0>();  // the (zero) loads past the end must land before LDS is reused
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* As = (kt & 1) ? buf1 : buf0;
-    const char* Bs = As + T::kARows * kRowBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      sa.load(ra, p.lda, M - m0, (kt + 1) * kBK, K, tid);
-      sb.load(rb, p.ldb, N - n0, (kt + 1) * kBK, K, tid);
-    }
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int c = kk * 4 + (lane >> 4);
-      bf16x8 a[T::TM], b[T::TN];
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * T::WM + i * 16 + (lane & 15), c));
-#pragma unroll
-      for (int j = 0; j < T::TN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn * T::WN + j * 16 + (lane & 15), c));
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      char* nxt = (kt & 1) ? buf0 : buf1;
-      sa.store(nxt, tid);
-      sb.store(nxt + T::kARows * kRowBytes, tid);
-    }
-    __syncthreads();
-  }
-
   const int mb = m0 + wm * T::WM, nb = n0 + wn * T::WN;
-  static_assert(4 * 16 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
-  staged_epilogue<T::TM, T::TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
+  static_assert(4 * 32 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
+  staged_epilogue<TM, TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
 }
 
 template <class P>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(P p) {
-  __shared__ __attribute__((aligned(16))) char smem[P::T::kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[P::T::kLdsBytes];
   int tmi, tni;
   tile_of_block(blockIdx.x, gridDim.x, p.tiles_m(), p.tiles_n(), tmi, tni);
   gemm_tile(p, smem, tmi, tni);
@@ -324,7 +373,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void gemm_bf16_group3_kernel(P0 p0, P1 p1, P2 p2) {
   constexpr int kL0 = P0::T::kLdsBytes, kL1 = P1::T::kLdsBytes, kL2 = P2::T::kLdsBytes;
   constexpr int kL = kL0 > kL1 ? (kL0 > kL2 ? kL0 : kL2) : (kL1 > kL2 ? kL1 : kL2);
-  __shared__ __attribute__((aligned(16))) char smem[kL];
+  __shared__ __attribute__((aligned(1024))) char smem[kL];
   int pid = blockIdx.x, tmi, tni;
   const int t0 = p0.tiles(), t1 = p1.tiles();
   if (pid < t0) {

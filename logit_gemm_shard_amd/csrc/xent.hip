@@ -12,33 +12,51 @@
 
 namespace lgs {
 
-// Upper bound on slabs over every tile shape: slabs = 2 * ceil(Vr / BN), BN >= 128.
+// Upper bound on slabs over every tile shape: slabs = ceil(Vr / BN) * BN / WN,
+// wave tile width WN >= 64.
 static int max_slabs(int Vr) { return 2 * ((Vr + 127) / 128); }
 
 size_t xent_scratch_bytes(int M, int Vr) {
   return (size_t)max_slabs(Vr) * (size_t)M * 16u;
 }
 
-// One thread per token: fold the slabs (in increasing column order, so the
-// first maximum wins ties) into the rank's partials.
+// Four lanes per token fold the slabs into the rank's partials, each lane
+// walking every fourth slab (independent loads in flight), then combining with
+// lane shuffles.  Ties on the maximum go to the lowest column, i.e. the first
+// maximum of the slice.
 __global__ __launch_bounds__(256) void xent_merge_kernel(XentSlabs s, int nslabs, int M,
                                                          int vocab_start, float* m_r, float* l_r,
                                                          float* t_r, int32_t* argmax_r,
                                                          float* loss) {
-  const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m >= M) return;
+  const int m = blockIdx.x * 64 + (threadIdx.x >> 2), part = threadIdx.x & 3;
+  const bool valid = m < M;
+  const int mm = valid ? m : 0;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int k = 0; k < nslabs; ++k) {
-    const float v = s.m[(int64_t)k * M + m];
-    if (v > best) { best = v; bi = s.idx[(int64_t)k * M + m]; }
+#pragma unroll 4
+  for (int k = part; k < nslabs; k += 4) {
+    const float v = s.m[(int64_t)k * M + mm];
+    const int i = s.idx[(int64_t)k * M + mm];
+    if (v > best || (v == best && i < bi)) { best = v; bi = i; }
+  }
+#pragma unroll
+  for (int off = 1; off <= 2; off <<= 1) {
+    const float ob = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
   }
   float L = 0.f, T = 0.f;
-  for (int k = 0; k < nslabs; ++k) {
-    const int64_t o = (int64_t)k * M + m;
-    L += s.l[o] * __expf(s.m[o] - best);
+#pragma unroll 4
+  for (int k = part; k < nslabs; k += 4) {
+    const int64_t o = (int64_t)k * M + mm;
+    L += s.l[o] * fast_exp(s.m[o] - best);
     T += s.t[o];
   }
+  L += __shfl_xor(L, 1);
+  L += __shfl_xor(L, 2);
+  T += __shfl_xor(T, 1);
+  T += __shfl_xor(T, 2);
+  if (!valid || part != 0) return;
   m_r[m] = best;
   l_r[m] = L;
   t_r[m] = T;
@@ -50,7 +68,7 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
                     const void* E, int64_t lde, const int32_t* targets, float* m_r, float* l_r,
                     float* t_r, int32_t* argmax_r, float* loss, void* scratch, hipStream_t s) {
   const TileId tile = pick_tile(M, Vr);
-  const int WN = tile_bn(tile) / 2;
+  const int WN = tile_wn(tile);
   const size_t slab_elems = (size_t)max_slabs(Vr) * M;
   XentSlabs sl;
   sl.m = (float*)scratch;
@@ -62,7 +80,7 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
                                        epi, s);
   if (e != hipSuccess) return e;
   const int nslabs = (Vr + WN - 1) / WN;
-  hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 255) / 256), dim3(256), 0, s, sl, nslabs, M,
+  hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 63) / 64), dim3(256), 0, s, sl, nslabs, M,
                      vocab_start, m_r, l_r, t_r, argmax_r, loss);
   return hipGetLastError();
 }

@@ -29,18 +29,18 @@ struct EpiXent {
   int M, N;                // tokens, slice width
   int WN;                  // wave tile width: slab = wave column
 
-  // A staged slice holds 16 rows x WN logits.  Four lanes share a row, each
-  // reducing a contiguous quarter of it (columns visited in increasing
-  // order), then the four combine with lane shuffles.
+  // A staged slice holds 32 rows x WN logits.  Two lanes share a row, each
+  // reducing a contiguous half of it (columns visited in increasing order),
+  // then the two combine with a lane shuffle.
   template <int WNt, int LD>
   __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
-    static_assert(WNt % 16 == 0, "a quarter row is read as float4s");
-    constexpr int Q = WNt / 4;
-    const int r = lane >> 2, part = lane & 3;
+    static_assert(WNt % 8 == 0, "a half row is read as float4s");
+    constexpr int Q = WNt / 2;
+    const int r = lane >> 1, part = lane & 1;
     const int m = m0 + r;
     const int c0 = part * Q;
     const float* row = st + r * LD + c0;
-    const int ncols = min(Q, N - (nb + c0));  // valid columns of this quarter (may be <= 0)
+    const int ncols = min(Q, N - (nb + c0));  // valid columns of this half (may be <= 0)
     const int tl = (m < M ? targets[m] - vocab_start : -1) - (nb + c0);
     float best = -INFINITY;
     int bi = 0x7fffffff;
@@ -51,10 +51,9 @@ struct EpiXent {
       for (int k = 0; k < 4; ++k)
         if (c + k < ncols && v[k] > best) { best = v[k]; bi = nb + c0 + c + k; }
     }
-#pragma unroll
-    for (int off = 1; off <= 2; off <<= 1) {
-      const float ob = __shfl_xor(best, off);
-      const int oi = __shfl_xor(bi, off);
+    {
+      const float ob = __shfl_xor(best, 1);
+      const int oi = __shfl_xor(bi, 1);
       if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
     float sum = 0.f, tv = 0.f;
@@ -69,9 +68,7 @@ struct EpiXent {
         }
     }
     sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
     tv += __shfl_xor(tv, 1);
-    tv += __shfl_xor(tv, 2);
     if (part == 0 && m < M) {
       const int64_t o = (int64_t)(nb / WN) * M + m;
       s.m[o] = best;
