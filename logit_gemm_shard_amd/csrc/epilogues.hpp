@@ -12,6 +12,7 @@ namespace lgs {
 // C = acc
 template <typename T>
 struct EpiStore {
+  static constexpr bool kDirect = false;
   T* C;
   int64_t ldc;
   int M, N;
@@ -29,6 +30,7 @@ struct EpiStore {
 // Y = GeLU(U), the input of the row-parallel GEMM.
 template <typename T>
 struct EpiGeluFwd {
+  static constexpr bool kDirect = false;
   T* U;  // may be null
   int64_t ldu;
   T* Y;
@@ -53,6 +55,7 @@ struct EpiGeluFwd {
 // pre-activation U, writes dU = dY * GeLU'(U) and the recomputed Y = GeLU(U).
 template <typename T>
 struct EpiGeluBwd {
+  static constexpr bool kDirect = false;
   const T* U;
   int64_t ldu;
   T* dU;

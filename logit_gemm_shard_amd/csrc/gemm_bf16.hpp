@@ -348,11 +348,16 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
     st_cur = st_nxt;
   }
   wait_vmcnt<0>();  // the (zero) loads past the end must land before LDS is reused
-  __syncthreads();
 
   const int mb = m0 + wm * T::WM, nb = n0 + wn * T::WN;
-  static_assert(4 * 32 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
-  staged_epilogue<TM, TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
+  if constexpr (P::Epi::kDirect) {
+    // The epilogue reads the accumulators in their MFMA lane layout.
+    p.epi.template direct<TM, TN, T::WN>(acc, mb, nb, lane);
+  } else {
+    __syncthreads();
+    static_assert(4 * 32 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
+    staged_epilogue<TM, TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
+  }
 }
 
 template <class P>

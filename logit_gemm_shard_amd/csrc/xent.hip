@@ -33,11 +33,16 @@ __global__ __launch_bounds__(256) void xent_merge_kernel(XentSlabs s, int nslabs
   const int mm = valid ? m : 0;
   float best = -INFINITY;
   int bi = 0x7fffffff;
+  if (s.idx) {
 #pragma unroll 4
-  for (int k = part; k < nslabs; k += 4) {
-    const float v = s.m[(int64_t)k * M + mm];
-    const int i = s.idx[(int64_t)k * M + mm];
-    if (v > best || (v == best && i < bi)) { best = v; bi = i; }
+    for (int k = part; k < nslabs; k += 4) {
+      const float v = s.m[(int64_t)k * M + mm];
+      const int i = s.idx[(int64_t)k * M + mm];
+      if (v > best || (v == best && i < bi)) { best = v; bi = i; }
+    }
+  } else {
+#pragma unroll 4
+    for (int k = part; k < nslabs; k += 4) best = fmaxf(best, s.m[(int64_t)k * M + mm]);
   }
 #pragma unroll
   for (int off = 1; off <= 2; off <<= 1) {
@@ -74,7 +79,7 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
   sl.m = (float*)scratch;
   sl.l = sl.m + slab_elems;
   sl.t = sl.l + slab_elems;
-  sl.idx = (int32_t*)(sl.t + slab_elems);
+  sl.idx = argmax_r ? (int32_t*)(sl.t + slab_elems) : nullptr;  // argmax only when asked for
   EpiXent epi{sl, targets, vocab_start, M, Vr, WN};
   hipError_t e = gemm_bf16<true, true>(tile, (const bf16*)H, ldh, (const bf16*)E, lde, M, Vr, h,
                                        epi, s);

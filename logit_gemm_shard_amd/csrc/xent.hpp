@@ -1,8 +1,8 @@
 // Fused vocab-parallel cross-entropy: the logit GEMM's epilogue reduces each
 // row of the wave's logit tile to (max, sum of exp relative to that max,
 // target logit, first argmax) and writes those four numbers per row and per
-// wave column-slab.  Logits never leave the chip: they go from the matrix
-// cores' accumulators through LDS to the reductions.  A small merge kernel
+// wave column-slab.  Logits never leave the chip: the reductions read them
+// from the matrix cores' accumulator registers.  A small merge kernel
 // then folds the slabs of the rank's vocabulary slice into the rank's partials.
 //
 // "LIT-022: Megatron-LM ..." (dmarx anthology), "Key takeaways": fusing the
@@ -19,62 +19,94 @@ struct XentSlabs {
   float* m;      // [slabs][M] slab max
   float* l;      // [slabs][M] sum exp(z - slab max)
   float* t;      // [slabs][M] target logit if the target is in the slab, else +0
-  int32_t* idx;  // [slabs][M] slice-local column of the slab's first maximum
+  int32_t* idx;  // [slabs][M] slice-local column of the slab's first maximum (may be null)
 };
 
 struct EpiXent {
+  static constexpr bool kDirect = true;
   XentSlabs s;
   const int32_t* targets;  // [M] global vocabulary ids
   int vocab_start;         // first global id of this rank's slice
   int M, N;                // tokens, slice width
   int WN;                  // wave tile width: slab = wave column
 
-  // A staged slice holds 32 rows x WN logits.  Two lanes share a row, each
-  // reducing a contiguous half of it (columns visited in increasing order),
-  // then the two combine with a lane shuffle.
-  template <int WNt, int LD>
-  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
-    static_assert(WNt % 8 == 0, "a half row is read as float4s");
-    constexpr int Q = WNt / 2;
-    const int r = lane >> 1, part = lane & 1;
-    const int m = m0 + r;
-    const int c0 = part * Q;
-    const float* row = st + r * LD + c0;
-    const int ncols = min(Q, N - (nb + c0));  // valid columns of this half (may be <= 0)
-    const int tl = (m < M ? targets[m] - vocab_start : -1) - (nb + c0);
+  // Reduces the wave's logit tile straight from the accumulators.  In the
+  // 32x32 MFMA output layout lane l holds, for row 32i + l%32 of the wave
+  // tile, the 16 TN columns 32j + 8q + 4(l/32) + e (j < TN, q < 4, e < 4) in
+  // acc[i][j][4q + e]: every row is split over lanes l and l ^ 32.  Each lane
+  // reduces its half and the pair combines through one lane exchange.
+  template <int TM, int TN, int WNt>
+  __device__ __forceinline__ void direct(f32x16 (&acc)[TM][TN], int mb, int nb, int lane) const {
+    const int cb = nb + 4 * (lane >> 5);  // slice-local column of acc[.][0][0]
+    if (N - nb < WNt) {
+      // Last wave column of the slice: columns past its end become -inf,
+      // which neither wins the max nor adds to the sum.
+      const int left = N - cb;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * j + 8 * (r >> 2) + (r & 3) >= left) acc[i][j][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) row_tile<TN>(acc[i], mb + 32 * i + (lane & 31), nb, cb, lane);
+  }
+
+  template <int TN>
+  __device__ __forceinline__ void row_tile(const f32x16 (&a)[TN], int m, int nb, int cb,
+                                           int lane) const {
+    int tl = -0x40000000;  // target column relative to cb; far below 0 if not in the slice
+    if (m < M) {
+      const int tg = targets[m] - vocab_start;
+      if (tg >= 0 && tg < N) tl = tg - cb;
+    }
+    // Row maximum over both halves (NaNs never win: a NaN row stays NaN
+    // through its sum).
     float best = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll 4
-    for (int c = 0; c < Q; c += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (c + k < ncols && v[k] > best) { best = v[k]; bi = nb + c0 + c + k; }
-    }
-    {
-      const float ob = __shfl_xor(best, 1);
-      const int oi = __shfl_xor(bi, 1);
-      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-    }
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) best = __builtin_fmaxf(best, a[j][r]);
+    best = __builtin_fmaxf(best, __shfl_xor(best, 32));
+    // Sum of exponentials relative to the row maximum, and the target logit.
+    // A row with no finite maximum (only -inf entries, e.g. a wave column
+    // wholly past the slice end) is shifted by 0 so that they add exp(-inf) = 0.
+    const float shift = (best == -INFINITY ? 0.f : best) * 1.4426950408889634f;
     float sum = 0.f, tv = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < Q; c += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (c + k < ncols) {
-          sum += fast_exp(v[k] - best);
-          if (c + k == tl) tv = v[k];
-        }
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float v = a[j][r];
+        sum += __builtin_amdgcn_exp2f(fmaf(v, 1.4426950408889634f, -shift));
+        tv = 32 * j + 8 * (r >> 2) + (r & 3) == tl ? v : tv;
+      }
+    sum += __shfl_xor(sum, 32);
+    tv += __shfl_xor(tv, 32);
+    // First column holding the maximum: each lane walks its columns from the
+    // last to the first, so the lowest match survives; then the pair keeps
+    // the lower of the two.
+    int bi = 0x7fffffff;
+    if (s.idx) {
+      int bc = -1;
+      if (best > -INFINITY) {
+#pragma unroll
+        for (int j = TN - 1; j >= 0; --j)
+#pragma unroll
+          for (int r = 15; r >= 0; --r)
+            bc = a[j][r] == best ? 32 * j + 8 * (r >> 2) + (r & 3) : bc;
+      }
+      bi = bc < 0 ? 0x7fffffff : cb + bc;
+      bi = min(bi, __shfl_xor(bi, 32));
     }
-    sum += __shfl_xor(sum, 1);
-    tv += __shfl_xor(tv, 1);
-    if (part == 0 && m < M) {
+    if (lane < 32 && m < M) {
       const int64_t o = (int64_t)(nb / WN) * M + m;
       s.m[o] = best;
       s.l[o] = sum;
       s.t[o] = tv;
-      s.idx[o] = bi;
+      if (s.idx) s.idx[o] = bi;
     }
   }
 };

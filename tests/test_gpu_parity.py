@@ -439,6 +439,14 @@ def test_full_size_xent_all_ranks_sampled():
         if own.any():
             assert_close(f"T_{r} owned", st[r, 2][rows][own], T[own], BF16)
         check_argmax(f64(H), E64[a:a + Vr], a, amh[r], rows)
+    # without the optional argmax (the training step's call) the partials are the same bits
+    Hd, Ed, yd = H.to(d), E.to(d), y.to(d)
+    for r in (0, w.t - 1):
+        part = torch.empty(3, w.M, dtype=F32, device=d)
+        lgs.vocab_parallel_xent_fwd(w.b, w.s, w.h, w.vocab, w.t, r, Hd, Ed[r * Vr:(r + 1) * Vr], yd,
+                                    part[0], part[1], part[2], argmax_r=None)
+        sync()
+        assert torch.equal(part.cpu(), st[r]), r
 
 
 # ------------------------------------------------- the epilogue's GeLU math
