@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s and % bf16 MFMA peak for TP-shard MLP fwd+bwd; CE tokens/s"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_8p3b_hbm_counters.txt")
 
 
@@ -87,8 +88,8 @@ def cpu_baseline(w, xw, inputs, budget_s=10.0):
     X, A0, B0, dZ, H, E0, y = inputs
     f, h, Vr, t = w.f_i, w.h, xw.v_r, w.t
     rng = np.random.default_rng(0)
-    best = None
-    for m in (256, 512, 1024, 2048, 4096, 8192):
+
+    def one_pass(m):
         Xs, dZs = X[:m].astype(np.float64), dZ[:m].astype(np.float64)
         Hs, ys = H[:m].astype(np.float64), y[:m]
         others = [rng.normal(size=(m, h)) for _ in range(t - 1)]
@@ -101,16 +102,93 @@ def cpu_baseline(w, xw, inputs, budget_s=10.0):
         mr, lr, Tr, _ = oracle.xent.shard_partials(Hs, E0, ys, 0)
         oracle.xent.merge(np.stack([mr] + [s[0] for s in stats]), np.stack([lr] + [s[1] for s in stats]),
                           np.stack([Tr] + [s[2] for s in stats]))
-        dt = time.perf_counter() - t0
-        fl = sum(step_flops(m, h, f, Vr).values())
-        best = (m, dt, fl)
-        if dt >= budget_s:
+        return time.perf_counter() - t0
+
+    # grow the token sample until one pass takes the budget, or the whole
+    # step is covered; then repeat whole passes until the budget is spent
+    for m in (256, 512, 1024, 2048, 4096, 8192):
+        m = min(m, w.M)
+        total, passes = one_pass(m), 1
+        if total >= budget_s or m == w.M:
             break
-    m, dt, fl = best
+    while total < budget_s:
+        total += one_pass(m)
+        passes += 1
+    fl = sum(step_flops(m, h, f, Vr).values()) * passes
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": fl / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"the same step (MLP fwd+bwd, both sums, slice-0 CE, merge) on the first {m} "
-                      f"of {w.M} tokens in fp64 numpy: {fl / 1e9:.1f} GFLOP in {dt:.2f} s"}
+                      f"of {w.M} tokens in fp64 numpy, {passes} passes: {fl / 1e9:.1f} GFLOP in {total:.2f} s"}
+
+
+def time_calls(torch, fn, reps, warmup=3):
+    """Average ms per call of fn() over reps calls, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def per_config(torch, lgs, reps):
+    """The configurations the library is specified on, each timed alone:
+    the tiny fp32 block (both shards + sum), and the 70B-shape rank's forward
+    and backward.  Inputs are device-side draws with the workloads'
+    distributions (the kernels' cost does not depend on the values)."""
+    from logit_gemm_shard_amd import synth
+    from logit_gemm_shard_amd.configs import WORKLOADS
+    dev = torch.device("cuda", 0)
+    out = {}
+
+    w = WORKLOADS["tiny_mlp_t2_f32"]
+    X, A, B = (x.to(dev) for x in synth.mlp_weights(w))
+    f = w.f_i
+    Z = torch.empty(w.t, w.M, w.h, device=dev)
+    Zs = torch.empty(w.M, w.h, device=dev)
+    Ys = torch.empty(w.t, w.M, f, device=dev)
+
+    def tiny():
+        for r in range(w.t):
+            lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, r, X, A[:, r * f:(r + 1) * f], B[r * f:(r + 1) * f], Z[r],
+                           Y_i=Ys[r])
+        lgs.shard_partial_sum("sum", w.t, w.M * w.h, Z, w.M * w.h, Zs)
+    ms = time_calls(torch, tiny, reps)
+    fl = 2 * 2 * w.M * w.h * w.ffn
+    out["tiny_mlp_t2_f32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 3),
+                              "pct_fp32_peak": round(100 * fl / ms / 1e9 / PEAK_FP32_TFLOPS, 3),
+                              "note": "both shards' forward + sum, fp32; launch-bound"}
+
+    w = WORKLOADS["mlp_70b_fwd"]
+    f, bf = w.f_i, torch.bfloat16
+    X = torch.randn(w.M, w.h, device=dev).to(bf)
+    A0 = torch.randn(w.h, f, device=dev).mul_(0.02).to(bf)
+    B0 = torch.randn(f, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
+    U = torch.empty(w.M, f, dtype=bf, device=dev)
+    Y = torch.empty(w.M, f, dtype=bf, device=dev)
+    Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
+    ms = time_calls(torch, lambda: lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, Z, U_i=U, Y_i=Y), reps)
+    fl = 2 * 2 * w.M * w.h * f
+    out["mlp_70b_fwd"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                          "pct_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+
+    w = WORKLOADS["mlp_70b_bwd"]
+    dZ = torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf)
+    dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
+    dA = torch.empty(w.h, f, dtype=bf, device=dev)
+    dB = torch.empty(f, w.h, dtype=bf, device=dev)
+    ws = torch.empty(lgs.mlp_bwd_workspace_bytes(w.b, w.s, w.h, w.ffn, w.t, bf), dtype=torch.uint8, device=dev)
+    ms = time_calls(torch, lambda: lgs.tp_mlp_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, U, dZ, dX, dA, dB,
+                                                  workspace=ws), reps)
+    fl = 4 * 2 * w.M * w.h * f
+    out["mlp_70b_bwd"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                          "pct_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    return out
 
 
 def main():
@@ -249,6 +327,14 @@ def main():
             "traffic": traffic,
         },
     }
+    configs = per_config(torch, lgs, reps=20)
+    configs["mlp_8p3b_fwd"] = {"ms": round(per["mlp_fwd"], 4), "tflops": out["mlp_fwd_tflops"],
+                               "pct_bf16_peak": round(100 * out["mlp_fwd_tflops"] / PEAK_BF16_TFLOPS, 2),
+                               "note": "from the timed steps"}
+    configs["xent_8p3b"] = {"ms": round(per["xent"], 4), "tflops": out["ce_tflops"],
+                            "pct_bf16_peak": round(100 * out["ce_tflops"] / PEAK_BF16_TFLOPS, 2),
+                            "tokens_per_s": out["ce_tokens_per_s"], "note": "from the timed steps"}
+    out["per_config"] = configs
     if not args.no_cpu_baseline:
         import numpy as np
         inputs = (X.float().numpy(), A0.float().double().numpy(), B0.float().double().numpy(),
