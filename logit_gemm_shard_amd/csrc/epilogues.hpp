@@ -1,7 +1,8 @@
 // GEMM epilogues.  Each receives W consecutive output columns n..n+W-1 of
-// one row m (W = 8 from the bf16 MFMA kernel, 4 from the fp32 kernel).
-// Columns come in whole groups because every N routed here is a multiple
-// of 8.
+// one row m: apply8 from the bf16 MFMA kernel (with the chunk's 8 input
+// values when the epilogue has an input, kLoads), apply<4> from the fp32
+// kernel.  Columns come in whole groups because every N routed here is a
+// multiple of 8.
 #pragma once
 
 #include "common.hpp"
@@ -12,13 +13,13 @@ namespace lgs {
 // C = acc
 template <typename T>
 struct EpiStore {
-  static constexpr bool kDirect = false;
+  static constexpr bool kDirect = false, kLoads = false;
   T* C;
   int64_t ldc;
   int M, N;
-  template <int WN, int LD>
-  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
-    elementwise_slice<WN, LD>(*this, st, m0, nb, lane);
+  __device__ __forceinline__ bf16x8 load8(int, int) const { return bf16x8{}; }
+  __device__ __forceinline__ void apply8(int m, int n, const float* v, bf16x8) const {
+    apply<8>(m, n, v);
   }
   template <int W>
   __device__ __forceinline__ void apply(int m, int n, const float* v) const {
@@ -30,15 +31,15 @@ struct EpiStore {
 // Y = GeLU(U), the input of the row-parallel GEMM.
 template <typename T>
 struct EpiGeluFwd {
-  static constexpr bool kDirect = false;
+  static constexpr bool kDirect = false, kLoads = false;
   T* U;  // may be null
   int64_t ldu;
   T* Y;
   int64_t ldy;
   int M, N, act;
-  template <int WN, int LD>
-  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
-    elementwise_slice<WN, LD>(*this, st, m0, nb, lane);
+  __device__ __forceinline__ bf16x8 load8(int, int) const { return bf16x8{}; }
+  __device__ __forceinline__ void apply8(int m, int n, const float* v, bf16x8) const {
+    apply<8>(m, n, v);
   }
   template <int W>
   __device__ __forceinline__ void apply(int m, int n, const float* v) const {
@@ -55,7 +56,7 @@ struct EpiGeluFwd {
 // pre-activation U, writes dU = dY * GeLU'(U) and the recomputed Y = GeLU(U).
 template <typename T>
 struct EpiGeluBwd {
-  static constexpr bool kDirect = false;
+  static constexpr bool kDirect = false, kLoads = true;
   const T* U;
   int64_t ldu;
   T* dU;
@@ -63,15 +64,28 @@ struct EpiGeluBwd {
   T* Y;
   int64_t ldy;
   int M, N, act;
-  template <int WN, int LD>
-  __device__ __forceinline__ void slice(const float* st, int m0, int nb, int lane) const {
-    elementwise_slice<WN, LD>(*this, st, m0, nb, lane);
+  // bf16 path: the chunk's 8 values of U (zeros outside the matrix).
+  __device__ __forceinline__ bf16x8 load8(int m, int n) const {
+    if (m >= M || n >= N) return bf16x8{};
+    return *reinterpret_cast<const bf16x8*>(U + (int64_t)m * ldu + n);
+  }
+  __device__ __forceinline__ void apply8(int m, int n, const float* dy, bf16x8 u8) const {
+    float u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = (float)u8[i];
+    finish<8>(m, n, dy, u);
   }
   template <int W>
   __device__ __forceinline__ void apply(int m, int n, const float* dy) const {
     if (m >= M || n >= N) return;
-    float u[W], du[W], y[W];
+    float u[W];
     load_vec<W>(U + (int64_t)m * ldu + n, u);
+    finish<W>(m, n, dy, u);
+  }
+  template <int W>
+  __device__ __forceinline__ void finish(int m, int n, const float* dy, const float* u) const {
+    if (m >= M || n >= N) return;
+    float du[W], y[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) {
       const GeluVals g = gelu_both(u[i], act);

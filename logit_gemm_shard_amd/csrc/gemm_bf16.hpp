@@ -1,34 +1,35 @@
 // bf16 GEMM core for gfx950 (CDNA4): C[M,N] = sum_k A(m,k) B(k,n), fp32
 // accumulation on the 32x32x16 bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Block: 256 threads = 4 wave64s in a WGM x WGN grid (2x2 or 4x1); block tile
-// BM x BN; K step 64, split into four 16-wide sub-steps.
+// Block: 256 threads = 4 wave64s (one per SIMD) in a WGM x WGN grid (2x2 or
+// 4x1); block tile BM x BN; K tiles of 32 (two 16-wide MFMA sub-steps).
 //
 // Operand tiles go global -> LDS with direct-to-LDS buffer loads (each wave
 // instruction moves 64 x 16 B into 1 KB of LDS; the hardware range check
 // returns zeros past an operand's end, so ragged edges need no branches).
-// Two LDS stages: while tile kt is multiplied out of one stage, tile kt+1
-// lands in the other.
+// A ring of 3-5 LDS stages (as many as fit in 160 KB) gives the loads of a K
+// tile several steps to land; one barrier per K tile.
 //
 // LDS layout per operand and stage:
-//  * K-contiguous operand (element (r,k) at base[r*ld + k]): R rows of 64 k =
-//    128 B; 16-B chunk c of row r sits at slot c ^ swz(r), swz(r) =
-//    (r & 7) ^ ((r >> 3) & 1).  Fragment reads (32 consecutive rows, one
-//    chunk column per half-wave) then touch distinct banks, and the swizzle
-//    of a row only depends on r & 15, so every fragment row of a wave is the
-//    same per-lane address plus an immediate offset.
-//  * M/N-contiguous operand (element (r,k) at base[k*ld + r]): 64 k-rows of R
-//    values, kept in that orientation; row pitch padded so four consecutive
-//    k-rows start 64 B apart modulo 256 B.  Fragments come from two
-//    ds_read_b64_tr_b16 (LDS transpose reads: within each 16-lane group,
-//    lanes 4j..4j+3 address row j of a 4 x 16 block and lane i receives
-//    column i), so no register transposes are needed.
+//  * K-contiguous operand (element (r,k) at base[r*ld + k]): R rows of 32 k =
+//    64 B; 16-B chunk c of row r sits at slot c ^ swz(r), swz(r) =
+//    (r >> 2) & 3.  Fragment reads (32 consecutive rows, one chunk column per
+//    half-wave) touch distinct banks, and since the swizzle of a row only
+//    depends on r & 31, every fragment of a wave is one per-lane address plus
+//    an immediate offset.
+//  * M/N-contiguous operand (element (r,k) at base[k*ld + r]): 32 k-rows of R
+//    values, kept in that orientation, row pitch padded off multiples of
+//    128 B.  Fragments come from two ds_read_b64_tr_b16 (LDS transpose reads:
+//    within each 16-lane group, lanes 4j..4j+3 address row j of a 4 x 16
+//    block and lane i receives column i), so no register transposes are needed.
 //
 // MFMA operand roles are swapped (the B tile feeds the instruction's first
 // operand) so each lane ends with runs of four consecutive output columns:
 // lane l, accumulator element r of 32x32 tile (i, j) is
 // C[32i + l%32][32j + 8(r/4) + 4(l/32) + r%4].
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -63,6 +64,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
+// f(integral_constant<int, i>) for i = 0 .. n-1, unrolled at compile time.
+template <int n, class F, int i = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (i < n) {
+    f(std::integral_constant<int, i>{});
+    static_for<n, F, i + 1>(static_cast<F&&>(f));
+  }
+}
+
+// Per-lane parts of the loads and fragment reads are computed once per tile;
+// inside the K loop an operand only moves its buffer resource forward by one
+// K tile (scalar arithmetic), and every fragment read is one per-lane
+// register plus a compile-time offset.
 template <int R, bool KMAJ>
 struct OpLayout;
 
@@ -71,19 +85,28 @@ struct OpLayout<R, true> {
   static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
   static constexpr int kBytes = R * 64;
   static constexpr int kInstr = R / 16;  // 1 KB loads per stage
-  static constexpr int kReadsPerFrag = 1;
-  // byte offset (from the tile's first row) that lane `lane` of load n reads
-  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left,
-                                                     int k0, int K) {
+  // element offset of a k step within the operand
+  __device__ __forceinline__ static int64_t step_elems(int64_t) { return kBK; }
+  // byte offset (from the tile's first row, k0 = 0) that lane `lane` of load
+  // n reads; out of range past the operand's last row
+  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left) {
     const int row = 16 * n + (lane >> 2);
-    const int gk = k0 + ((lane & 3) ^ swz(row)) * 8;
-    return (row < rows_left && gk < K) ? (uint32_t)(row * ld + gk) * 2u : kOutOfRange;
+    return row < rows_left ? (uint32_t)(row * ld + kcol(n, lane)) * 2u : kOutOfRange;
   }
-  // rows row0 + lane%32 (row0 a multiple of 32), k = 16 s + 8 (lane/32) .. +7
-  __device__ __forceinline__ static bf16x8 frag(const char* base, int row0, int s, int lane) {
-    const int row = row0 + (lane & 31);
-    const int c = 2 * s + (lane >> 5);
-    return *reinterpret_cast<const bf16x8*>(base + row * 64 + ((c ^ swz(row)) << 4));
+  // k (within the K tile) of the 8 elements that lane reads in load n
+  __device__ __forceinline__ static int kcol(int n, int lane) {
+    return ((lane & 3) ^ swz(16 * n + (lane >> 2))) * 8;
+  }
+  // Fragment of rows row0 + lane%32 (row0 a multiple of 32), k = 16 s +
+  // 8 (lane/32) .. +7: the swizzle only depends on lane%32, so the address is
+  // lane_off(s) + 64 row0.
+  __device__ __forceinline__ static uint32_t lane_off(int s, int lane) {
+    const int r = lane & 31;
+    return (uint32_t)(r * 64 + (((2 * s) ^ (lane >> 5) ^ swz(r)) << 4));
+  }
+  template <int kRow0>
+  __device__ __forceinline__ static bf16x8 frag(const char* p) {  // p = base + wave part + lane_off(s)
+    return *reinterpret_cast<const bf16x8*>(p + kRow0 * 64);
   }
 };
 
@@ -94,40 +117,46 @@ struct OpLayout<R, false> {
   static constexpr int kCpr = kPitch / 16;  // 16-B chunks per k-row (a multiple of 4)
   static constexpr int kBytes = kBK * kPitch;
   static constexpr int kInstr = kBK * kCpr / 64;  // kBK k-rows x kCpr chunks / 64 lanes
-  static constexpr int kReadsPerFrag = 2;
-  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left,
-                                                     int k0, int K) {
+  __device__ __forceinline__ static int64_t step_elems(int64_t ld) { return kBK * ld; }
+  // byte offset (from the tile's first column, k0 = 0); out of range past the
+  // operand's last column or in the pitch padding.  Rows past K fall outside
+  // the buffer resource, which ends at the operand's last row.
+  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left) {
     const int d = n * 64 + lane;
     const int krow = d / kCpr, ch = d - krow * kCpr;
-    const int gk = k0 + krow;
-    return (ch * 8 < R && ch * 8 < rows_left && gk < K) ? (uint32_t)(gk * ld + ch * 8) * 2u
-                                                         : kOutOfRange;
+    return (ch * 8 < R && ch * 8 < rows_left) ? (uint32_t)(krow * ld + ch * 8) * 2u : kOutOfRange;
   }
-  // The transposed reads are issued as inline assembly: the compiler would
-  // otherwise treat them as possibly aliasing the direct-to-LDS loads in
-  // flight and wait for all of those first.  Their results are only valid
-  // after an explicit lgkmcnt wait (the pipeline waits at each sub-step).
-  __device__ __forceinline__ static bf16x8 frag(const char* base, int row0, int s, int lane) {
+  __device__ __forceinline__ static int kcol(int n, int lane) { return (n * 64 + lane) / kCpr; }
+  // Two ds_read_b64_tr_b16 per fragment (rows row0 .. row0+31 of the wave's
+  // columns, k = 16 s + 8 (lane/32) .. +7): lanes 4j..4j+3 of each 16-lane
+  // group address k-row j of a 4 x 16 block.  The per-lane part:
+  __device__ __forceinline__ static uint32_t lane_off(int, int lane) {
     const int g = lane >> 4, i16 = lane & 15;
-    const int krow = 16 * s + 8 * (g >> 1) + (i16 >> 2);
-    const char* p0 = base + krow * kPitch + (row0 + 16 * (g & 1) + 4 * (i16 & 3)) * 2;
-    const uint32_t a = (uint32_t)(uintptr_t)(LGS_AS3 const char*)p0;
+    return (uint32_t)((8 * (g >> 1) + (i16 >> 2)) * kPitch + (16 * (g & 1) + 4 * (i16 & 3)) * 2);
+  }
+  // Issued as inline assembly: the compiler would otherwise treat them as
+  // possibly aliasing the direct-to-LDS loads in flight and wait for all of
+  // those first.  Results are only valid after an explicit lgkmcnt wait.
+  template <int kS, int kRow0>
+  __device__ __forceinline__ static bf16x8 frag_tr(uint32_t a) {  // a = base + wave part + lane_off
     s16x4 lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"(4 * kPitch));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(a), "i"(16 * kS * kPitch + 2 * kRow0));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"((16 * kS + 4) * kPitch + 2 * kRow0));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
   }
 };
 
-// Resource covering an operand from its tile's first row (K-contiguous) or
-// first column (M/N-contiguous) to the operand's last element.
+// Resource covering an operand from element (row0, k0) of its tile
+// (K-contiguous) or (k0, row0) (M/N-contiguous) to the operand's last element;
+// empty once k0 is past K.
 template <bool KMAJ>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* base, int64_t ld, int row0,
-                                                           int rows, int K) {
-  if (KMAJ)
-    return make_rsrc(base + (int64_t)row0 * ld, (uint32_t)(((int64_t)(rows - 1 - row0) * ld + K) * 2));
-  return make_rsrc(base + row0, (uint32_t)(((int64_t)(K - 1) * ld + (rows - row0)) * 2));
+                                                           int rows, int K, int k0) {
+  const int64_t first = KMAJ ? (int64_t)row0 * ld + k0 : (int64_t)k0 * ld + row0;
+  const int64_t last = KMAJ ? (int64_t)(rows - 1) * ld + K : (int64_t)(K - 1) * ld + rows;  // one past
+  const int64_t bytes = k0 < K ? (last - first) * 2 : 0;
+  return make_rsrc(base + first, (uint32_t)bytes);
 }
 
 // Block index -> output tile.  The hardware deals consecutive workgroup ids
@@ -166,42 +195,67 @@ struct Tile {
   static constexpr int kLdsBytes = kStages * kStage;
 };
 
-// Epilogue: each wave stages 32-row slices of its accumulators through LDS
-// (free once the K loop has passed its last barrier) and hands each slice to
-// the epilogue, which reads it back in whatever lane mapping suits it.
+// Elementwise epilogues: each wave stages 32-row slices of its accumulators
+// through its own region of LDS (free once the K loop has passed its last
+// barrier) and reads each slice back as 8-column chunks: chunk c of a slice is
+// row c / (WN/8), columns 8 (c % (WN/8)) .. +7, and lane l takes chunks l,
+// l + 64, ...  Stores of 16 bytes per lane are then contiguous along rows.
+// Only the wave itself touches its region, so a slice needs no block barrier:
+// LDS requests of one wave complete in order, and the waits below make the
+// staged values visible to the other lanes before they are read.
+// Epilogues with an input of the output's shape (Epi::kLoads) get the chunk's
+// 8 input values loaded one slice ahead, so that their memory latency overlaps
+// the staging and math of the slice before.
+template <int WN>
+struct SliceShape {
+  static constexpr int kCpr = WN / 8;          // chunks per row
+  static constexpr int kChunks = 32 * kCpr;    // chunks per 32-row slice
+  static constexpr int kPerLane = kChunks / 64;
+  static_assert(kChunks % 64 == 0, "wave tile width must be a multiple of 16");
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  wait_lgkm0();
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int TM, int TN, int WN, class Epi>
 __device__ __forceinline__ void staged_epilogue(const f32x16 (&acc)[TM][TN], char* smem, int wave,
                                                 int lane, int mb, int nb, const Epi& epi) {
+  using SS = SliceShape<WN>;
   constexpr int LD = WN + 4;  // floats per staged row
   float* st = reinterpret_cast<float*>(smem) + wave * 32 * LD;
+  bf16x8 in[2][SS::kPerLane];
+  auto prefetch = [&](int i, bf16x8(&dst)[SS::kPerLane]) {
+#pragma unroll
+    for (int k = 0; k < SS::kPerLane; ++k) {
+      const int c = lane + 64 * k, r = c / SS::kCpr, q = c - r * SS::kCpr;
+      dst[k] = epi.load8(mb + 32 * i + r, nb + 8 * q);
+    }
+  };
+  if constexpr (Epi::kLoads) prefetch(0, in[0]);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    if constexpr (Epi::kLoads)
+      if (i + 1 < TM) prefetch(i + 1, in[(i + 1) & 1]);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(st + (lane & 31) * LD + j * 32 + 8 * q + 4 * (lane >> 5)) =
             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    __syncthreads();
-    epi.template slice<WN, LD>(st, mb + i * 32, nb, lane);
-    __syncthreads();
-  }
-}
-
-// Elementwise epilogues: lane c takes row c / (WN/8), columns 8*(c % (WN/8))..+7.
-template <int WN, int LD, class Epi>
-__device__ __forceinline__ void elementwise_slice(const Epi& epi, const float* st, int m0, int nb,
-                                                  int lane) {
-  constexpr int CHUNKS = 32 * WN / 8;
-#pragma unroll 1
-  for (int c = lane; c < CHUNKS; c += 64) {
-    const int r = c / (WN / 8), q = c - r * (WN / 8);
-    float v[8];
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(st + r * LD + q * 8);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(st + r * LD + q * 8 + 4);
-    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-    epi.template apply<8>(m0 + r, nb + q * 8, v);
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < SS::kPerLane; ++k) {
+      const int c = lane + 64 * k, r = c / SS::kCpr, q = c - r * SS::kCpr;
+      float v[8];
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(st + r * LD + q * 8);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(st + r * LD + q * 8 + 4);
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      epi.apply8(mb + 32 * i + r, nb + 8 * q, v, in[i & 1][k]);
+    }
+    wave_lds_sync();
   }
 }
 
@@ -244,60 +298,86 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const __amdgpu_buffer_rsrc_t ra = tile_rsrc<P::AK>(p.A, p.lda, m0, M, K);
-  const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, n0, N, K);
   const int nk = (K + kBK - 1) / kBK;
   constexpr int IA = (LA::kInstr + 3) / 4, IB = (LB::kInstr + 3) / 4;
+  constexpr int kPer = IA + IB;  // loads per tile per wave
 
-  // Direct-to-LDS loads of tile kt into stage `st`.  Load n of an operand
-  // fills bytes [1024 n, 1024 n + 1024) of its region; waves take every 4th
-  // load (a duplicate of the last load where the count is not a multiple of
-  // four: the same bytes written twice with the same values).
-  // Byte offsets each lane reads for tile kt (computed ahead of the issue).
+  // Direct-to-LDS loads.  Load n of an operand fills bytes [1024 n, 1024 n +
+  // 1024) of its region in a stage; waves take every 4th load (a duplicate of
+  // the last load where the count is not a multiple of four: the same bytes
+  // written twice with the same values).  The per-lane source offsets are
+  // fixed for the tile; each K tile moves the buffer resources instead.  A
+  // K-contiguous operand's last, partial K tile masks its lanes past K.
   uint32_t offa[IA], offb[IB];
-  auto load_offsets = [&](int kt) {
+  int kca[IA], kcb[IB];
+#pragma unroll
+  for (int t = 0; t < IA; ++t) {
+    const int n = min(wave + 4 * t, LA::kInstr - 1);
+    offa[t] = LA::src_off(n, lane, p.lda, M - m0);
+    kca[t] = LA::kcol(n, lane);
+  }
+#pragma unroll
+  for (int t = 0; t < IB; ++t) {
+    const int n = min(wave + 4 * t, LB::kInstr - 1);
+    offb[t] = LB::src_off(n, lane, p.ldb, N - n0);
+    kcb[t] = LB::kcol(n, lane);
+  }
+  __amdgpu_buffer_rsrc_t ra, rb;
+  bool kfull = true;
+  auto load_prep = [&](int kt) {
     const int k0 = kt * kBK;
-#pragma unroll
-    for (int t = 0; t < IA; ++t)
-      offa[t] = LA::src_off(min(wave + 4 * t, LA::kInstr - 1), lane, p.lda, M - m0, k0, K);
-#pragma unroll
-    for (int t = 0; t < IB; ++t)
-      offb[t] = LB::src_off(min(wave + 4 * t, LB::kInstr - 1), lane, p.ldb, N - n0, k0, K);
+    ra = tile_rsrc<P::AK>(p.A, p.lda, m0, M, K, k0);
+    rb = tile_rsrc<P::BK>(p.B, p.ldb, n0, N, K, k0);
+    kfull = k0 + kBK <= K;
   };
-  // Direct-to-LDS loads into stage `st`.  Load n of an operand fills bytes
-  // [1024 n, 1024 n + 1024) of its region; waves take every 4th load (a
-  // duplicate of the last load where the count is not a multiple of four: the
-  // same bytes written twice with the same values).
-  auto load_issue = [&](int st) {
+  auto load_one = [&](int st, int u, int kt) {
     char* base = smem + st * T::kStage;
-#pragma unroll
-    for (int t = 0; t < IA; ++t) {
-      const int n = min(wave + 4 * t, LA::kInstr - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LGS_AS3 void*)(base + n * 1024), 16, (int)offa[t], 0, 0, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < IB; ++t) {
-      const int n = min(wave + 4 * t, LB::kInstr - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LGS_AS3 void*)(base + LA::kBytes + n * 1024), 16, (int)offb[t], 0, 0, 0);
+    if (u < IA) {
+      const int n = min(wave + 4 * u, LA::kInstr - 1);
+      uint32_t off = offa[u];
+      if (P::AK && !kfull) off = kt * kBK + kca[u] < K ? off : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LGS_AS3 void*)(base + n * 1024), 16, (int)off, 0, 0, 0);
+    } else {
+      const int t = u - IA, n = min(wave + 4 * t, LB::kInstr - 1);
+      uint32_t off = offb[t];
+      if (P::BK && !kfull) off = kt * kBK + kcb[t] < K ? off : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LGS_AS3 void*)(base + LA::kBytes + n * 1024), 16, (int)off, 0, 0, 0);
     }
   };
-  auto load_tile = [&](int st, int kt) {
-    load_offsets(kt);
-    load_issue(st);
-  };
+
+  // Fragment reads: one per-lane register per operand and sub-step, plus the
+  // stage and a compile-time offset per fragment.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LGS_AS3 char*)smem;
+  const uint32_t fa_lane[2] = {LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u),
+                               LA::lane_off(1, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u)};
+  const uint32_t fb_lane[2] = {LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes,
+                               LB::lane_off(1, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes};
   bf16x8 fa[2][TM], fb[2][TN];
-  auto read_frags = [&](const char* base, int s, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = LA::frag(base, wm * T::WM + i * 32, s, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = LB::frag(base + LA::kBytes, wn * T::WN + j * 32, s, lane);
+  // fragments of sub-step s of the tile in stage st into buffer d
+  auto read_frags = [&](int st, auto s_c, int d) {
+    constexpr int s = decltype(s_c)::value;
+    const uint32_t sb = (uint32_t)(st * T::kStage);
+    if constexpr (P::AK) {
+      const char* pa = smem + sb + fa_lane[s];
+      static_for<TM>([&](auto i) { fa[d][i] = LA::template frag<32 * decltype(i)::value>(pa); });
+    } else {
+      const uint32_t a = lds0 + sb + fa_lane[0];
+      static_for<TM>([&](auto i) { fa[d][i] = LA::template frag_tr<s, 32 * decltype(i)::value>(a); });
+    }
+    if constexpr (P::BK) {
+      const char* pb = smem + sb + fb_lane[s];
+      static_for<TN>([&](auto j) { fb[d][j] = LB::template frag<32 * decltype(j)::value>(pb); });
+    } else {
+      const uint32_t b = lds0 + sb + fb_lane[0];
+      static_for<TN>([&](auto j) { fb[d][j] = LB::template frag_tr<s, 32 * decltype(j)::value>(b); });
+    }
   };
-  auto mma = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) {
+  auto mma = [&](int d) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[d][j], fa[d][i], acc[i][j], 0, 0, 0);
   };
 
   // Ring of S stages of 32-wide K tiles.  Step kt (tile kt in stage kt % S):
@@ -306,38 +386,40 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
   // waves; every read of tile kt-1's stage retired), start loading tile
   // kt+S-1 into that stage; read tile kt+1's first fragments, MFMAs on the
   // second sub-step.  Loads thus have S-2 steps to land.  Tiles past the end
-  // load zeros, so the loop body has no branches.
+  // load zeros (empty resources), so the loop body has no data branches.
   constexpr int S = T::kStages;
-  constexpr int kPer = IA + IB;  // loads per tile per wave
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) load_tile(t, t);
+  for (int t = 0; t < S - 1; ++t) {
+    load_prep(t);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) load_one(t, u, t);
+  }
   wait_vmcnt<(S - 2) * kPer>();  // this wave's loads of tile 0 done
   __syncthreads();
-  read_frags(smem, 0, fa[0], fb[0]);
+  read_frags(0, std::integral_constant<int, 0>{}, 0);
   wait_lgkm0();
   int st_cur = 0;
   constexpr int kMfma = TM * TN;
   for (int kt = 0; kt < nk; ++kt) {
     const int st_nxt = st_cur + 1 == S ? 0 : st_cur + 1;
     const int st_free = st_cur == 0 ? S - 1 : st_cur - 1;
-    const char* cur = smem + st_cur * T::kStage;
-    const char* nxt = smem + st_nxt * T::kStage;
     // first sub-step: issue the second sub-step's fragment reads, then the
-    // first sub-step's MFMAs (and the address math of the next loads)
-    read_frags(cur, 1, fa[1], fb[1]);
+    // first sub-step's MFMAs (and the resources of the next loads)
+    read_frags(st_cur, std::integral_constant<int, 1>{}, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fa[0], fb[0]);
-    load_offsets(kt + S - 1);
+    mma(0);
+    load_prep(kt + S - 1);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(S - 3) * kPer>();  // this wave's loads of tile kt+1 done
     __syncthreads();
     wait_lgkm0();                  // second sub-step's fragments in registers
     // second sub-step: tile kt+1's first fragment reads, then its MFMAs with
     // the loads of tile kt+S-1 issued between them
-    read_frags(nxt, 0, fa[0], fb[0]);
+    read_frags(st_nxt, std::integral_constant<int, 0>{}, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_issue(st_free);
-    mma(fa[1], fb[1]);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) load_one(st_free, u, kt + S - 1);
+    mma(1);
 #pragma unroll
     for (int q = 0; q < kMfma; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // 1 MFMA
@@ -354,7 +436,7 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
     // The epilogue reads the accumulators in their MFMA lane layout.
     p.epi.template direct<TM, TN, T::WN>(acc, mb, nb, lane);
   } else {
-    __syncthreads();
+    __syncthreads();  // every wave is past its last read of the LDS ring
     static_assert(4 * 32 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
     staged_epilogue<TM, TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
   }
