@@ -70,13 +70,14 @@ def read_counters():
 def copy_calibration():
     """A plain device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
-    n = 1 << 28  # 256 Mi floats = 1 GiB read + 1 GiB written per copy
+    n = 1 << 28  # 256 Mi floats = 1 GiB read + 1 GiB written per pass
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     for _ in range(5):
-        b.copy_(a)
+        torch.neg(a, out=b)  # an elementwise kernel (a same-dtype copy_ may be a DMA, not a kernel)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 5}))
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 5,
+                      "kernel": "torch.neg elementwise"}))
 
 
 def cpu_baseline(w, xw, inputs, budget_s=10.0):
@@ -209,6 +210,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-configuration timings (counter passes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard: the library is measured on one GPU "
@@ -338,7 +341,7 @@ def main():
             "traffic": traffic,
         },
     }
-    configs = per_config(torch, lgs, reps=20)
+    configs = {} if args.no_per_config else per_config(torch, lgs, reps=20)
     configs["mlp_8p3b_fwd"] = {"ms": round(per["mlp_fwd"], 4), "tflops": out["mlp_fwd_tflops"],
                                "pct_bf16_peak": round(100 * out["mlp_fwd_tflops"] / PEAK_BF16_TFLOPS, 2),
                                "note": "from the timed steps"}
