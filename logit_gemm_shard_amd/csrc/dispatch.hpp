@@ -1,29 +1,33 @@
-// Tile-shape choice for the bf16 GEMM core and the launch switch over the
-// instantiated shapes.
+// Tile-shape choice for the bf16 GEMM cores and the launch switch over the
+// instantiated shapes: 256x256, 256x192 and 128x128 tiles run on the 8-wave
+// ping-pong core (gemm_pp.hpp), 256x224 and 256x160 (whose widths do not
+// split into two 32-multiple column halves) on the 4-wave core.
 #pragma once
 
 #include "gemm_bf16.hpp"
+#include "gemm_pp.hpp"
 
 namespace lgs {
 
 enum TileId : int { T256x256 = 0, T256x224, T256x192, T256x160, T128x128, kNumTiles };
 
 struct TileShape {
-  int bm, bn, wgm;  // block tile and the waves' grid (wgm x 4/wgm)
-  float eff;        // relative per-CU efficiency (bigger tiles reuse each LDS byte more)
+  int bm, bn;
+  int wn;     // width of a wave's tile (one CE slab)
+  float eff;  // relative per-CU throughput, from sweeps of both cores
 };
 
-constexpr TileShape kTileShapes[kNumTiles] = {{256, 256, 2, 1.00f},
-                                              {256, 224, 4, 0.97f},
-                                              {256, 192, 2, 0.96f},
-                                              {256, 160, 4, 0.92f},
-                                              {128, 128, 2, 0.75f}};
+constexpr TileShape kTileShapes[kNumTiles] = {{256, 256, 128, 1.00f},   // ping-pong
+                                              {256, 224, 224, 0.87f},   // 4-wave, 4x1
+                                              {256, 192, 96, 0.85f},    // ping-pong
+                                              {256, 160, 160, 0.80f},   // 4-wave, 4x1
+                                              {128, 128, 64, 0.55f}};   // ping-pong
 
-// The chip runs one 256x* block per compute unit at a time (the double
-// buffered tiles use 96-128 KB of the 160 KB LDS), so a launch proceeds in
-// "waves" of 256 blocks.  Pick the shape minimising waves x tile area / eff:
-// e.g. a 4096 x 3584 output is 224 blocks of 256x256 (1/8 of the chip idle)
-// but exactly 256 blocks of 256x224.
+// One 256x* block per compute unit at a time (the LDS rings use 120-160 KB
+// of the 160 KB), so a launch proceeds in rounds of 256 blocks.  Pick the
+// shape minimising rounds x tile area / eff: e.g. an 8192 x 6400 output is
+// 1280 blocks of 256x160 (five full rounds) but 800 of 256x256 (the fourth
+// round one eighth full).
 inline TileId pick_tile(int M, int N) {
   constexpr int kCUs = 256;
   TileId best = T256x256;
@@ -39,7 +43,7 @@ inline TileId pick_tile(int M, int N) {
 }
 
 inline int tile_bn(TileId t) { return kTileShapes[t].bn; }
-inline int tile_wn(TileId t) { return kTileShapes[t].bn * kTileShapes[t].wgm / 4; }
+inline int tile_wn(TileId t) { return kTileShapes[t].wn; }
 
 template <int BM, int BN, int WGM, bool AK, bool BK, class Epi>
 inline GemmProblem<BM, BN, WGM, AK, BK, Epi> problem(const bf16* A, int64_t lda, const bf16* B,
@@ -52,11 +56,11 @@ template <bool AK, bool BK, class Epi>
 inline hipError_t gemm_bf16(TileId t, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
                             int M, int N, int K, const Epi& epi, hipStream_t s) {
   switch (t) {
-    case T256x256: return launch_gemm(problem<256, 256, 2, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x256: return launch_gemm_pp(pp_problem<256, 256, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     case T256x224: return launch_gemm(problem<256, 224, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x192: return launch_gemm(problem<256, 192, 2, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x192: return launch_gemm_pp(pp_problem<256, 192, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     case T256x160: return launch_gemm(problem<256, 160, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T128x128: return launch_gemm(problem<128, 128, 2, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T128x128: return launch_gemm_pp(pp_problem<128, 128, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,277 @@
+// 8-wave "ping-pong" variant of the bf16 GEMM core (same LDS layouts, loads
+// and epilogues as gemm_bf16.hpp).
+//
+// Why: on gfx950 the data an LDS read returns to a wave costs that wave's
+// own MFMA issue about 25 cycles per KB, while reads returning to ANOTHER
+// wave on the same SIMD cost the MFMA wave nothing (measured).  With one wave
+// per SIMD the fragment traffic of a 128x128 wave tile (16 KB per 32-wide K
+// tile) therefore adds ~40% to its 1024 MFMA cycles.  Here each SIMD runs two
+// waves, one from each of two groups (waves w and w+4 share a SIMD), and the
+// groups alternate between phases, separated by block barriers: while one
+// group multiplies the K tile whose fragments it holds in registers, the
+// other reads its fragments of that tile from LDS and issues the
+// direct-to-LDS loads of a later tile.  The matrix cores of a SIMD then see
+// back-to-back MFMAs of one wave or the other.
+//
+// Block: 512 threads; block tile BM x BN, wave w owns rows (w & 3) BM/4 and
+// columns (w >> 2) BN/2 (group g = w >> 2 owns one column half).  K tiles of
+// 32 in a ring of S LDS stages; tile kt is read by group 0 in phase 2kt and
+// by group 1 in phase 2kt+1, and computed by each in its next phase.
+//
+// Phase bookkeeping: in phase 2kt group 0 reads tile kt and issues its loads
+// of tile kt+S-1 (into the stage of tile kt-1, which group 1 finished
+// reading in phase 2kt-1); group 1 does the same one phase later.  Every wave
+// ends every phase by waiting until at most S-2 of its tiles' loads are in
+// flight, which covers every tile read in the next phase.
+#pragma once
+
+#include "gemm_bf16.hpp"
+
+namespace lgs {
+
+constexpr int kPPWaves = 8;
+
+// s_barrier without the memory fence of __syncthreads(): that fence makes the
+// compiler wait for every direct-to-LDS load in flight (vmcnt(0)) before the
+// barrier, which would drain the load pipeline at every phase.  The waits the
+// pipeline needs are explicit (vmcnt for this wave's loads, lgkmcnt for its
+// fragment reads); the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+constexpr int kPPThreads = 64 * kPPWaves;
+
+template <int BM, int BN, bool AK, bool BK>
+struct PPTile {
+  static constexpr int WM = BM / 4, WN = BN / 2;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  using LA = OpLayout<BM, AK>;
+  using LB = OpLayout<BN, BK>;
+  static constexpr int kStage = LA::kBytes + LB::kBytes;
+  static constexpr int kStages = kLdsMax / kStage < 5 ? kLdsMax / kStage : 5;
+  static_assert(kStages >= 3, "need at least three stages");
+  static constexpr int kLdsBytes = kStages * kStage;
+};
+
+template <int BM_, int BN_, bool AK_, bool BK_, class Epi_>
+struct PPProblem {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr bool AK = AK_, BK = BK_;
+  using Epi = Epi_;
+  using T = PPTile<BM, BN, AK, BK>;
+  const bf16* A;
+  int64_t lda;
+  const bf16* B;
+  int64_t ldb;
+  int M, N, K;
+  Epi epi;
+  __host__ __device__ int tiles_m() const { return (M + BM - 1) / BM; }
+  __host__ __device__ int tiles_n() const { return (N + BN - 1) / BN; }
+  __host__ __device__ int tiles() const { return tiles_m() * tiles_n(); }
+};
+
+template <class P>
+__device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, int tni) {
+  using T = typename P::T;
+  using LA = typename T::LA;
+  using LB = typename T::LB;
+  constexpr int TM = T::TM, TN = T::TN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wm = wave & 3, wn = grp;
+  const int M = p.M, N = p.N, K = p.K;
+  const int m0 = tmi * P::BM, n0 = tni * P::BN;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (K + kBK - 1) / kBK;
+  constexpr int IA = (LA::kInstr + kPPWaves - 1) / kPPWaves, IB = (LB::kInstr + kPPWaves - 1) / kPPWaves;
+  constexpr int kPer = IA + IB;  // loads per tile per wave
+
+  // Direct-to-LDS loads: load n of an operand fills bytes [1024 n, +1024) of
+  // its region; waves take every 8th load (duplicating the last one where the
+  // count is not a multiple of eight).  Offsets fixed per tile; the buffer
+  // resources move per K tile; a K-contiguous operand's partial last tile
+  // masks its lanes past K.
+  uint32_t offa[IA], offb[IB];
+  int kca[IA], kcb[IB];
+#pragma unroll
+  for (int t = 0; t < IA; ++t) {
+    const int n = min(wave + kPPWaves * t, LA::kInstr - 1);
+    offa[t] = LA::src_off(n, lane, p.lda, M - m0);
+    kca[t] = LA::kcol(n, lane);
+  }
+#pragma unroll
+  for (int t = 0; t < IB; ++t) {
+    const int n = min(wave + kPPWaves * t, LB::kInstr - 1);
+    offb[t] = LB::src_off(n, lane, p.ldb, N - n0);
+    kcb[t] = LB::kcol(n, lane);
+  }
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * kBK;
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc<P::AK>(p.A, p.lda, m0, M, K, k0);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, n0, N, K, k0);
+    const bool kfull = k0 + kBK <= K;
+    char* base = smem + (kt % T::kStages) * T::kStage;
+#pragma unroll
+    for (int t = 0; t < IA; ++t) {
+      const int n = min(wave + kPPWaves * t, LA::kInstr - 1);
+      uint32_t off = offa[t];
+      if (P::AK && !kfull) off = k0 + kca[t] < K ? off : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LGS_AS3 void*)(base + n * 1024), 16, (int)off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < IB; ++t) {
+      const int n = min(wave + kPPWaves * t, LB::kInstr - 1);
+      uint32_t off = offb[t];
+      if (P::BK && !kfull) off = k0 + kcb[t] < K ? off : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LGS_AS3 void*)(base + LA::kBytes + n * 1024), 16, (int)off, 0, 0, 0);
+    }
+  };
+
+  // Fragments of both 16-wide sub-steps of one K tile.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LGS_AS3 char*)smem;
+  const uint32_t fa_lane[2] = {LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u),
+                               LA::lane_off(1, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u)};
+  const uint32_t fb_lane[2] = {LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes,
+                               LB::lane_off(1, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes};
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto read_sub = [&](uint32_t sb, auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    if constexpr (P::AK) {
+      const char* pa = smem + sb + fa_lane[s];
+      static_for<TM>([&](auto i) { fa[s][i] = LA::template frag<32 * decltype(i)::value>(pa); });
+    } else {
+      const uint32_t a = lds0 + sb + fa_lane[0];
+      static_for<TM>([&](auto i) { fa[s][i] = LA::template frag_tr<s, 32 * decltype(i)::value>(a); });
+    }
+    if constexpr (P::BK) {
+      const char* pb = smem + sb + fb_lane[s];
+      static_for<TN>([&](auto j) { fb[s][j] = LB::template frag<32 * decltype(j)::value>(pb); });
+    } else {
+      const uint32_t b = lds0 + sb + fb_lane[0];
+      static_for<TN>([&](auto j) { fb[s][j] = LB::template frag_tr<s, 32 * decltype(j)::value>(b); });
+    }
+  };
+  // Read phase: this wave's fragments of tile kt, then the loads of tile
+  // kt+S-1 (into the stage that tile kt-1 left), then wait for the fragments.
+  auto read_phase = [&](int kt) {
+    asm volatile("s_nop 7" ::: "memory");  // earlier MFMAs' operand reads retire first
+    const uint32_t sb = (uint32_t)((kt % T::kStages) * T::kStage);
+    read_sub(sb, std::integral_constant<int, 0>{});
+    read_sub(sb, std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(kt + T::kStages - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();
+  };
+  auto compute_phase = [&]() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // End of a phase: this wave's loads older than the last S-2 tiles have
+  // landed (every tile read in the next phase is among them), then barrier.
+  constexpr int S = T::kStages;
+  auto phase_end = [&]() {
+    wait_vmcnt<(S - 2) * kPer>();
+    block_barrier();
+  };
+
+  // Both groups run the same loop; group 1 starts one barrier later (block
+  // barriers count arrivals, not program points), which staggers the groups
+  // by one phase, and group 0 ends with one extra barrier to match.
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) load_tile(t);
+  phase_end();
+  if (grp == 1) block_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    read_phase(kt);
+    phase_end();
+    compute_phase();
+    phase_end();
+  }
+  if (grp == 0) block_barrier();
+  wait_vmcnt<0>();  // the (zero) loads past the end must land before LDS is reused
+
+  const int mb = m0 + wm * T::WM, nb = n0 + wn * T::WN;
+  if constexpr (P::Epi::kDirect) {
+    p.epi.template direct<TM, TN, T::WN>(acc, mb, nb, lane);
+  } else {
+    __syncthreads();  // every wave is past its last read of the LDS ring
+    static_assert(kPPWaves * 32 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
+    staged_epilogue<TM, TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
+  }
+}
+
+template <class P>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_kernel(P p) {
+  __shared__ __attribute__((aligned(1024))) char smem[P::T::kLdsBytes];
+  int tmi, tni;
+  tile_of_block(blockIdx.x, gridDim.x, p.tiles_m(), p.tiles_n(), tmi, tni);
+  gemm_tile_pp(p, smem, tmi, tni);
+}
+
+// Three independent GEMMs in one launch (blocks [0, p0.tiles()) on p0, then
+// p1, then p2; longest-K problems first so the short tiles of the later ones
+// fill the compute units the long ones leave free).
+template <class P0, class P1, class P2>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_group3_kernel(P0 p0, P1 p1, P2 p2) {
+  constexpr int kL0 = P0::T::kLdsBytes, kL1 = P1::T::kLdsBytes, kL2 = P2::T::kLdsBytes;
+  constexpr int kL = kL0 > kL1 ? (kL0 > kL2 ? kL0 : kL2) : (kL1 > kL2 ? kL1 : kL2);
+  __shared__ __attribute__((aligned(1024))) char smem[kL];
+  int pid = blockIdx.x, tmi, tni;
+  const int t0 = p0.tiles(), t1 = p1.tiles();
+  if (pid < t0) {
+    tile_of_block(pid, t0, p0.tiles_m(), p0.tiles_n(), tmi, tni);
+    gemm_tile_pp(p0, smem, tmi, tni);
+  } else if ((pid -= t0) < t1) {
+    tile_of_block(pid, t1, p1.tiles_m(), p1.tiles_n(), tmi, tni);
+    gemm_tile_pp(p1, smem, tmi, tni);
+  } else {
+    pid -= t1;
+    tile_of_block(pid, p2.tiles(), p2.tiles_m(), p2.tiles_n(), tmi, tni);
+    gemm_tile_pp(p2, smem, tmi, tni);
+  }
+}
+
+template <class P0, class P1, class P2>
+inline hipError_t launch_gemm_pp_group3(const P0& p0, const P1& p1, const P2& p2, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_pp_group3_kernel<P0, P1, P2>), dim3(p0.tiles() + p1.tiles() + p2.tiles()),
+                     dim3(kPPThreads), 0, stream, p0, p1, p2);
+  return hipGetLastError();
+}
+
+template <class P>
+inline hipError_t launch_gemm_pp(const P& p, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_pp_kernel<P>), dim3(p.tiles()), dim3(kPPThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool AK, bool BK, class Epi>
+inline PPProblem<BM, BN, AK, BK, Epi> pp_problem(const bf16* A, int64_t lda, const bf16* B,
+                                                 int64_t ldb, int M, int N, int K, const Epi& epi) {
+  return PPProblem<BM, BN, AK, BK, Epi>{A, lda, B, ldb, M, N, K, epi};
+}
+
+}  // namespace lgs

@@ -65,12 +65,12 @@ hipError_t mlp_bwd(bool is_bf16, int M, int h, int f, int act, const void* X, in
     EpiStore<bf16> ea{(bf16*)dA, ldda, h, f};
     EpiStore<bf16> ex{(bf16*)dX, lddx, M, h};
     if (f >= 256 && h >= 256 && M >= 256)
-      return launch_gemm_group3(problem<256, 256, 2, false, false>(y, ldw, dz, lddz, f, h, M, eb),
-                                problem<256, 256, 2, false, false>(x, ldx, du, ldw, h, f, M, ea),
-                                problem<256, 256, 2, true, true>(du, ldw, a, lda, M, h, f, ex), s);
-    return launch_gemm_group3(problem<128, 128, 2, false, false>(y, ldw, dz, lddz, f, h, M, eb),
-                              problem<128, 128, 2, false, false>(x, ldx, du, ldw, h, f, M, ea),
-                              problem<128, 128, 2, true, true>(du, ldw, a, lda, M, h, f, ex), s);
+      return launch_gemm_pp_group3(pp_problem<256, 256, false, false>(y, ldw, dz, lddz, f, h, M, eb),
+                                   pp_problem<256, 256, false, false>(x, ldx, du, ldw, h, f, M, ea),
+                                   pp_problem<256, 256, true, true>(du, ldw, a, lda, M, h, f, ex), s);
+    return launch_gemm_pp_group3(pp_problem<128, 128, false, false>(y, ldw, dz, lddz, f, h, M, eb),
+                                 pp_problem<128, 128, false, false>(x, ldx, du, ldw, h, f, M, ea),
+                                 pp_problem<128, 128, true, true>(du, ldw, a, lda, M, h, f, ex), s);
   }
   const float *x = (const float*)X, *a = (const float*)A, *b = (const float*)B, *dz = (const float*)dZ;
   float *y = (float*)Yws, *du = (float*)dUws;

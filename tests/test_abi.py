@@ -166,8 +166,9 @@ def test_testing_interface(L):
     shapes = binding.tile_shapes()
     assert (256, 256) in shapes and (128, 128) in shapes
     assert L.lgs_test_tile_shape(len(shapes), None, None) == -1
-    # the picker fills the 256 compute units: 4096 x 3584 -> 256 blocks of 256x224
-    assert shapes[binding.pick_tile(4096, 3584)] == (256, 224)
+    # the picker weighs full rounds of 256 blocks against the cores' throughput:
+    # 4096 x 3584 -> 224 blocks of 256x256 (one round) beats 256 of 256x224
+    assert shapes[binding.pick_tile(4096, 3584)] == (256, 256)
     assert shapes[binding.pick_tile(8192, 1536)] == (256, 192)
     assert shapes[binding.pick_tile(8192, 6400)] == (256, 160)
     assert L.lgs_test_gemm_bf16(0, 0, 1, 64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 2
