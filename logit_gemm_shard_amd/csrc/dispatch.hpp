@@ -1,5 +1,5 @@
 // Tile-shape choice for the bf16 GEMM cores and the launch switch over the
-// instantiated shapes: 256x256, 256x192 and 128x128 tiles run on the 8-wave
+// instantiated shapes: 256x256, 256x320, 256x192 and 128x128 tiles run on the 8-wave
 // ping-pong core (gemm_pp.hpp), 256x224 and 256x160 (whose widths do not
 // split into two 32-multiple column halves) on the 4-wave core.
 #pragma once
@@ -9,7 +9,7 @@
 
 namespace lgs {
 
-enum TileId : int { T256x256 = 0, T256x224, T256x192, T256x160, T128x128, kNumTiles };
+enum TileId : int { T256x256 = 0, T256x224, T256x192, T256x160, T128x128, T256x320, kNumTiles };
 
 struct TileShape {
   int bm, bn;
@@ -20,14 +20,15 @@ struct TileShape {
 constexpr TileShape kTileShapes[kNumTiles] = {{256, 256, 128, 1.00f},   // ping-pong
                                               {256, 224, 224, 0.87f},   // 4-wave, 4x1
                                               {256, 192, 96, 0.85f},    // ping-pong
-                                              {256, 160, 160, 0.80f},   // 4-wave, 4x1
-                                              {128, 128, 64, 0.55f}};   // ping-pong
+                                              {256, 160, 160, 0.72f},   // 4-wave, 4x1
+                                              {128, 128, 64, 0.55f},    // ping-pong
+                                              {256, 320, 160, 1.02f}};  // ping-pong
 
 // One 256x* block per compute unit at a time (the LDS rings use 120-160 KB
 // of the 160 KB), so a launch proceeds in rounds of 256 blocks.  Pick the
 // shape minimising rounds x tile area / eff: e.g. an 8192 x 6400 output is
-// 1280 blocks of 256x160 (five full rounds) but 800 of 256x256 (the fourth
-// round one eighth full).
+// 640 blocks of 256x320 (two and a half rounds) but 800 of 256x256 (the
+// fourth round one eighth full).
 inline TileId pick_tile(int M, int N) {
   constexpr int kCUs = 256;
   TileId best = T256x256;
@@ -61,6 +62,7 @@ inline hipError_t gemm_bf16(TileId t, const bf16* A, int64_t lda, const bf16* B,
     case T256x192: return launch_gemm_pp(pp_problem<256, 192, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     case T256x160: return launch_gemm(problem<256, 160, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     case T128x128: return launch_gemm_pp(pp_problem<128, 128, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+    case T256x320: return launch_gemm_pp(pp_problem<256, 320, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
     default: return hipErrorInvalidValue;
   }
 }

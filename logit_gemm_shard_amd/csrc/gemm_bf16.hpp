@@ -206,12 +206,12 @@ struct Tile {
 // Epilogues with an input of the output's shape (Epi::kLoads) get the chunk's
 // 8 input values loaded one slice ahead, so that their memory latency overlaps
 // the staging and math of the slice before.
-template <int WN>
+template <int WN, int ROWS>
 struct SliceShape {
   static constexpr int kCpr = WN / 8;          // chunks per row
-  static constexpr int kChunks = 32 * kCpr;    // chunks per 32-row slice
+  static constexpr int kChunks = ROWS * kCpr;  // chunks per slice
   static constexpr int kPerLane = kChunks / 64;
-  static_assert(kChunks % 64 == 0, "wave tile width must be a multiple of 16");
+  static_assert(kChunks % 64 == 0, "wave tile width must be a multiple of 32");
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -219,31 +219,40 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int TM, int TN, int WN, class Epi>
+// Slices are ROWS = 32 rows (one MFMA row tile), or 16 (half a row tile,
+// written by the lanes holding those rows) where a wave's 32 x (WN+4) floats
+// times the block's waves would not fit in the LDS ring.
+template <int TM, int TN, int WN, int ROWS, class Epi>
 __device__ __forceinline__ void staged_epilogue(const f32x16 (&acc)[TM][TN], char* smem, int wave,
                                                 int lane, int mb, int nb, const Epi& epi) {
-  using SS = SliceShape<WN>;
+  static_assert(ROWS == 32 || ROWS == 16, "slice rows");
+  using SS = SliceShape<WN, ROWS>;
   constexpr int LD = WN + 4;  // floats per staged row
-  float* st = reinterpret_cast<float*>(smem) + wave * 32 * LD;
+  constexpr int kHalves = 32 / ROWS;
+  float* st = reinterpret_cast<float*>(smem) + wave * ROWS * LD;
   bf16x8 in[2][SS::kPerLane];
-  auto prefetch = [&](int i, bf16x8(&dst)[SS::kPerLane]) {
+  auto prefetch = [&](int sl, bf16x8(&dst)[SS::kPerLane]) {
 #pragma unroll
     for (int k = 0; k < SS::kPerLane; ++k) {
       const int c = lane + 64 * k, r = c / SS::kCpr, q = c - r * SS::kCpr;
-      dst[k] = epi.load8(mb + 32 * i + r, nb + 8 * q);
+      dst[k] = epi.load8(mb + ROWS * sl + r, nb + 8 * q);
     }
   };
   if constexpr (Epi::kLoads) prefetch(0, in[0]);
+  const int lrow = lane & 31;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int sl = 0; sl < TM * kHalves; ++sl) {
+    const int i = sl / kHalves, h = sl % kHalves;
     if constexpr (Epi::kLoads)
-      if (i + 1 < TM) prefetch(i + 1, in[(i + 1) & 1]);
+      if (sl + 1 < TM * kHalves) prefetch(sl + 1, in[(sl + 1) & 1]);
+    if (kHalves == 1 || (lrow >> 4) == h) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(st + (lane & 31) * LD + j * 32 + 8 * q + 4 * (lane >> 5)) =
-            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(st + (lrow - ROWS * h) * LD + j * 32 + 8 * q + 4 * (lane >> 5)) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
     wave_lds_sync();
 #pragma unroll
     for (int k = 0; k < SS::kPerLane; ++k) {
@@ -253,10 +262,16 @@ __device__ __forceinline__ void staged_epilogue(const f32x16 (&acc)[TM][TN], cha
       const f32x4 hi = *reinterpret_cast<const f32x4*>(st + r * LD + q * 8 + 4);
       v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
       v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-      epi.apply8(mb + 32 * i + r, nb + 8 * q, v, in[i & 1][k]);
+      epi.apply8(mb + ROWS * sl + r, nb + 8 * q, v, in[sl & 1][k]);
     }
     wave_lds_sync();
   }
+}
+
+// Rows per staged slice for `waves` waves of width WN in `lds` bytes.
+template <int WN>
+constexpr int stage_rows(int waves, int lds) {
+  return waves * 32 * (WN + 4) * 4 <= lds ? 32 : 16;
 }
 
 // One GEMM of the core: C[M, N] = A B with its epilogue, block tile BM x BN.
@@ -437,8 +452,9 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
     p.epi.template direct<TM, TN, T::WN>(acc, mb, nb, lane);
   } else {
     __syncthreads();  // every wave is past its last read of the LDS ring
-    static_assert(4 * 32 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
-    staged_epilogue<TM, TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
+    constexpr int R = stage_rows<T::WN>(4, T::kLdsBytes);
+    static_assert(4 * R * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
+    staged_epilogue<TM, TN, T::WN, R>(acc, smem, wave, lane, mb, nb, p.epi);
   }
 }
 

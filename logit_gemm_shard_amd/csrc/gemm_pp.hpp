@@ -217,8 +217,9 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
     p.epi.template direct<TM, TN, T::WN>(acc, mb, nb, lane);
   } else {
     __syncthreads();  // every wave is past its last read of the LDS ring
-    static_assert(kPPWaves * 32 * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
-    staged_epilogue<TM, TN, T::WN>(acc, smem, wave, lane, mb, nb, p.epi);
+    constexpr int R = stage_rows<T::WN>(kPPWaves, T::kLdsBytes);
+    static_assert(kPPWaves * R * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
+    staged_epilogue<TM, TN, T::WN, R>(acc, smem, wave, lane, mb, nb, p.epi);
   }
 }
 

@@ -170,7 +170,7 @@ def test_testing_interface(L):
     # 4096 x 3584 -> 224 blocks of 256x256 (one round) beats 256 of 256x224
     assert shapes[binding.pick_tile(4096, 3584)] == (256, 256)
     assert shapes[binding.pick_tile(8192, 1536)] == (256, 192)
-    assert shapes[binding.pick_tile(8192, 6400)] == (256, 160)
+    assert shapes[binding.pick_tile(8192, 6400)] == (256, 320)  # 640 blocks: 2.5 rounds
     assert L.lgs_test_gemm_bf16(0, 0, 1, 64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 2
     assert L.lgs_test_gemm_bf16(9, 1, 1, 64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 1
     assert L.lgs_test_gemm_bf16(0, 1, 1, 64, 60, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 2
