@@ -203,6 +203,30 @@ def per_config(torch, lgs, reps):
     return out
 
 
+def ce_reduction_stream(torch, lgs, xw, reps=30):
+    """The CE reductions alone, streamed from materialised bf16 logits of the
+    rank's slice (a testing entry point; the product path fuses them into the
+    logit GEMM and never writes logits).  Three logit buffers (315 MB, more
+    than the 256 MB Infinity Cache) are rotated so every launch reads HBM."""
+    dev = torch.device("cuda", 0)
+    M, Vr = xw.M, xw.v_r
+    bufs = [torch.randn(M, Vr, device=dev).to(torch.bfloat16) for _ in range(3)]
+    y = torch.randint(0, xw.vocab, (M,), device=dev, dtype=torch.int32)
+    out = torch.empty(3, M, device=dev)
+    i = [0]
+
+    def one():
+        lgs.xent_rows_bf16(bufs[i[0] % 3], y, 0, out[0], out[1], out[2])
+        i[0] += 1
+    ms = time_calls(torch, one, reps, warmup=3)
+    nbytes = M * Vr * 2 + M * 4 + 3 * M * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "xent_rows_kernel (lgs_test_xent_rows_bf16): CE slice reductions over "
+                      f"materialised bf16 logits [{M}, {Vr}]",
+            "us": round(ms * 1e3, 2), "bytes": nbytes, "achieved_GBs": round(gbs, 1),
+            "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +373,8 @@ def main():
                             "pct_bf16_peak": round(100 * out["ce_tflops"] / PEAK_BF16_TFLOPS, 2),
                             "tokens_per_s": out["ce_tokens_per_s"], "note": "from the timed steps"}
     out["per_config"] = configs
+    if not args.no_per_config:
+        out["ce_reduction_stream"] = ce_reduction_stream(torch, lgs, xw)
     if not args.no_cpu_baseline:
         import numpy as np
         inputs = (X.float().numpy(), A0.float().double().numpy(), B0.float().double().numpy(),

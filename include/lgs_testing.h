@@ -38,6 +38,18 @@ int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int N, int K
                        int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                        void* stream);
 
+/*
+ * Streaming form of the cross-entropy slice partials, for measuring the CE
+ * reductions against the HBM roofline (the product path fuses them into the
+ * logit GEMM, vocab_parallel_xent_fwd, and never writes logits).  Z holds a
+ * slice's logits, [M, Vr] bf16 row-major (ld ldz); per row it writes the
+ * slice max m, the sum of exp(z - m) l, and the target logit T (targets are
+ * global ids; T is +0.0 when targets[k] - vocab_start is outside [0, Vr)).
+ * Vr must be a multiple of 8; Z 16-byte aligned, ldz % 8 == 0.
+ */
+int lgs_test_xent_rows_bf16(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
+                            const int32_t* targets, float* m, float* l, float* T, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

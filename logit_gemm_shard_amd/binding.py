@@ -46,6 +46,7 @@ SIGNATURES = [
     ("lgs_test_tile_shape", _i, [_i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     ("lgs_test_pick_tile", _i, [_i, _i]),
     ("lgs_test_gemm_bf16", _i, [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
+    ("lgs_test_xent_rows_bf16", _i, [_i, _i, _i, _p, _i64, _p, _p, _p, _p, _p]),
 ]
 
 
@@ -212,3 +213,14 @@ def gemm_bf16(A, B, C, a_kmajor=True, b_kmajor=False, tile=-1, stream=None):
     _check(lib().lgs_test_gemm_bf16(tile, int(a_kmajor), int(b_kmajor), M, N, K, a, lda, b, ldb, c,
                                     ldc, _stream(stream)))
     return C
+
+
+def xent_rows_bf16(Z, targets, vocab_start, m, l, T, stream=None):
+    """Slice partials (m, l, T) from materialised bf16 logits Z [M, Vr]
+    (testing interface: the streaming form of the fused CE's reductions)."""
+    z, ldz = _mat(Z)
+    M, Vr = Z.shape
+    _check(lib().lgs_test_xent_rows_bf16(M, Vr, vocab_start, z, ldz, targets.data_ptr(), m.data_ptr(),
+                                         l.data_ptr(), T.data_ptr(), _stream(stream)))
+    return m, l, T
+

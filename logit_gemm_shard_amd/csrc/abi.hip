@@ -281,3 +281,17 @@ LGS_API int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int 
   return launched(lgs::gemm_store_bf16(tile, a_kmajor != 0, b_kmajor != 0, M, N, K, A, lda, B, ldb,
                                        C, ldc, (hipStream_t)stream));
 }
+
+LGS_API int lgs_test_xent_rows_bf16(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
+                                    const int32_t* targets, float* m, float* l, float* T,
+                                    void* stream) {
+  if (M < 0 || Vr <= 0) return fail(LGS_ERR_INVALID_ARG, "M must be >= 0 and Vr > 0");
+  if (Vr % 8 != 0) return fail(LGS_ERR_UNSUPPORTED, "Vr must be a multiple of 8");
+  int st;
+  if ((st = check_mat("Z", Z, M, ldz, Vr, LGS_BF16, M > 0))) return st;
+  if (M > 0 && (!targets || !m || !l || !T))
+    return fail(LGS_ERR_INVALID_ARG, "targets, m, l and T are required");
+  if (M == 0) return ok();
+  (void)hipGetLastError();
+  return launched(lgs::xent_rows(M, Vr, vocab_start, Z, ldz, targets, m, l, T, (hipStream_t)stream));
+}

@@ -70,9 +70,13 @@ def shard_partials(H, E_r, y, vocab_start):
       argmax_r = global vocabulary id of the slice's largest logit (lowest id
                  among exact ties)
     """
-    H, E_r = _f64(H), _f64(E_r)
+    return slice_partials(_f64(H) @ _f64(E_r).T, y, vocab_start)
+
+
+def slice_partials(z, y, vocab_start):
+    """The same partials from a slice's logits z [M, V_r] directly."""
+    z = _f64(z)
     y = np.asarray(y, dtype=np.int64)
-    z = H @ E_r.T
     Vr = z.shape[1]
     m = z.max(axis=1)
     l = np.exp(z - m[:, None]).sum(axis=1)

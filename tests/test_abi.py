@@ -174,3 +174,9 @@ def test_testing_interface(L):
     assert L.lgs_test_gemm_bf16(0, 0, 1, 64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 2
     assert L.lgs_test_gemm_bf16(9, 1, 1, 64, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 1
     assert L.lgs_test_gemm_bf16(0, 1, 1, 64, 60, 64, FAKE, 64, FAKE, 64, FAKE, 64, None) == 2
+    # streaming CE partials: Vr % 8, leading dimension, required pointers, empty input
+    assert L.lgs_test_xent_rows_bf16(4, 100, 0, FAKE, 104, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.lgs_test_xent_rows_bf16(4, 64, 0, FAKE, 32, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.lgs_test_xent_rows_bf16(4, 64, 0, FAKE, 64, None, FAKE, FAKE, FAKE, None) == 1
+    assert L.lgs_test_xent_rows_bf16(4, 64, 0, FAKE + 2, 64, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.lgs_test_xent_rows_bf16(0, 64, 0, None, 64, None, None, None, None, None) == 0

@@ -449,6 +449,68 @@ def test_full_size_xent_all_ranks_sampled():
         assert torch.equal(part.cpu(), st[r]), r
 
 
+# ------------------------------- streaming form of the CE reductions (testing)
+
+def _rows_partials(Z, y, start):
+    d = dev()
+    M = Z.shape[0]
+    out = torch.empty(3, M, dtype=F32, device=d)
+    lgs.xent_rows_bf16(Z.to(d), y.to(d), start, out[0], out[1], out[2])
+    sync()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("M,Vr,start", [(300, 1000, 0), (65, 6400, 6400), (1, 8, 3)])
+def test_xent_rows_match_oracle_slice_partials(M, Vr, start):
+    """bf16 logits of H E_r^T (ragged row counts, chunk counts that are not a
+    multiple of the wave) -> the oracle's slice partials on the same logits."""
+    h = 64
+    H, E = synth.small(11, (M, h), (Vr, h), std=0.5)
+    Z = round_like(f64(H) @ f64(E).T, BF16)
+    g = torch.Generator().manual_seed(3)
+    y = torch.randint(max(0, start - Vr // 2), start + Vr + Vr // 2, (M,), generator=g).to(torch.int32)
+    step(f"xent rows M={M} Vr={Vr} start={start}")
+    got = _rows_partials(Z, y, start)
+    m, l, T, _ = oracle.xent.slice_partials(f64(Z), y.numpy(), start)
+    assert np.array_equal(f64(got[0]), m)              # a max of bf16 values is exact
+    assert np.array_equal(f64(got[2]), T)              # so is the picked logit, or +0.0
+    assert not np.any(np.signbit(f64(got[2])[T == 0.0]))
+    assert_close("l", got[1], l, F32)
+
+
+def test_xent_rows_special_rows():
+    d = dev()
+    Vr = 256
+    Z = torch.zeros(4, Vr, dtype=BF16)
+    Z[1] = 3.0                                  # all equal: l = Vr exactly
+    Z[2, 17] = float("nan")                     # a NaN poisons the sum only
+    Z[3] = float("-inf")
+    Z[3, 5] = 1.0                               # one finite logit: l = 1
+    y = torch.tensor([0, 1, 17, 5], dtype=torch.int32)
+    step("xent rows special rows")
+    got = _rows_partials(Z, y, 0).numpy()
+    assert got[0, 1] == 3.0 and got[1, 1] == Vr
+    assert got[0, 2] == 0.0 and np.isnan(got[1, 2]) and np.isnan(got[2, 2])
+    assert got[0, 3] == 1.0 and got[1, 3] == 1.0 and got[2, 3] == 1.0
+
+
+def test_xent_rows_full_size_sampled():
+    w = WORKLOADS["xent_8p3b"]
+    H, E, y = synth.xent_inputs(w)
+    rows = _rows(w.M, 64, 9)
+    d = dev()
+    Zd = (H.to(d).float() @ E[:w.v_r].to(d).float().t().contiguous()).to(BF16)  # rank-0 slice logits
+    step("xent rows at full size (8192 x 6400)")
+    out = torch.empty(3, w.M, dtype=F32, device=d)
+    lgs.xent_rows_bf16(Zd, y.to(d), 0, out[0], out[1], out[2])
+    sync()
+    Zs = f64(Zd[rows].cpu())
+    m, l, T, _ = oracle.xent.slice_partials(Zs, y.numpy()[rows], 0)
+    got = out.cpu()[:, rows]
+    assert np.array_equal(f64(got[0]), m) and np.array_equal(f64(got[2]), T)
+    assert_close("l (sampled rows)", got[1], l, F32)
+
+
 # ------------------------------------------------- the epilogue's GeLU math
 
 @pytest.mark.parametrize("act", ["erf", "tanh"])
