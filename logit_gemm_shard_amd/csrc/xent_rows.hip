@@ -5,11 +5,11 @@
 // reductions against the HBM roofline (each logit is read once), and is not
 // part of the method's interface (declared in include/lgs_testing.h).
 //
-// One wave per row.  Each lane keeps a running (max, sum) over its 16-byte
-// chunks with the online rescaling sum' = sum * exp(m - m') + sum exp(z - m')
-// (one pass over the row), four chunk loads in flight, non-temporal loads
-// (every byte is read once).  The lanes then combine with the same identity
-// through lane shuffles.
+// One wave per row, non-temporal 16-byte loads (every byte is read once);
+// the lanes' (max, sum) pairs combine through lane shuffles with the online
+// log-sum-exp identity.  The exponentials (one per logit, quarter-rate on the
+// vector ALU) rather than HBM set the pace unless the per-logit work stays
+// at a handful of instructions, hence the batch structure below.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -18,9 +18,9 @@ namespace lgs {
 namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kRowsPerBlock = 4;  // one row per wave
-constexpr int kUnroll = 4;        // 16-byte chunks in flight per lane
-
+constexpr int kRowsPerBlock = 8;  // one row per wave
+constexpr int kBatch = 7;         // 16-byte chunks per lane held at once (3584 logits per wave)
+constexpr float kLog2e = 1.4426950408889634f;
 
 __global__ __launch_bounds__(64 * kRowsPerBlock) void xent_rows_kernel(
     const bf16* __restrict__ Z, int64_t ldz, int M, int Vr, int vocab_start,
@@ -34,32 +34,39 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void xent_rows_kernel(
   int tg = targets[row] - vocab_start;
   if (tg < 0 || tg >= Vr) tg = -1;  // not in this slice: the target logit stays +0
   float m = -INFINITY, l = 0.f, tv = 0.f;
-  for (int c0 = lane; c0 < nchunk; c0 += 64 * kUnroll) {
-    u32x4 raw[kUnroll];
+  // Batches of kBatch chunks per lane (two for a 6400-logit slice): all
+  // loads of a batch in flight together, one max pass over the registers,
+  // then one sum pass with a single shift; batches combine with the online
+  // identity l' = l exp(m - m') + sum exp(z - m').
+  for (int base = 0; base < nchunk; base += 64 * kBatch) {
+    u32x4 raw[kBatch];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = c0 + 64 * u;
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = base + lane + 64 * u;
       raw[u] = c < nchunk ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + 8 * c))
                           : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};  // bf16 -inf
     }
+    float bm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       const bf16x8 v = __builtin_bit_cast(bf16x8, raw[u]);
-      const int col = 8 * (c0 + 64 * u);
-      float cm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cm = fmaxf(cm, (float)v[e]);
-      const float nm = fmaxf(m, cm);
-      const float sm = nm == -INFINITY ? 0.f : nm;
-      float cs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        cs += fast_exp((float)v[e] - sm);
-        tv = col + e == tg ? (float)v[e] : tv;
-      }
-      l = l * fast_exp(m - sm) + cs;
-      m = nm;
+      for (int e = 0; e < 8; ++e) bm = fmaxf(bm, (float)v[e]);
     }
+    const float nm = fmaxf(m, bm);
+    const float sm = nm == -INFINITY ? 0.f : nm;  // a row of -inf adds exp(-inf) = 0
+    const float shift = sm * kLog2e;
+    float bs = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, raw[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bs += __builtin_amdgcn_exp2f(fmaf((float)v[e], kLog2e, -shift));
+      const int col = 8 * (base + lane + 64 * u);
+      if (tg >= col && tg < col + 8) tv = (float)v[tg - col];  // one lane, one chunk per row
+    }
+    l = l * __builtin_amdgcn_exp2f(fmaf(m, kLog2e, -shift)) + bs;
+    m = nm;
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
