@@ -117,7 +117,14 @@ def cpu_baseline(w, xw, inputs, budget_s=10.0):
         passes += 1
     fl = sum(step_flops(m, h, f, Vr).values()) * passes
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": fl / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "os_cpu_count": os.cpu_count(),
             "sample": f"the same step (MLP fwd+bwd, both sums, slice-0 CE, merge) on the first {m} "
                       f"of {w.M} tokens in fp64 numpy, {passes} passes: {fl / 1e9:.1f} GFLOP in {total:.2f} s"}
 
@@ -176,31 +183,60 @@ def per_config(torch, lgs, reps):
                               "pct_fp32_peak": round(100 * fl / ms / 1e9 / PEAK_FP32_TFLOPS, 3),
                               "note": "both shards' forward + sum, fp32, replayed as one HIP graph; launch-bound"}
 
+    # 70B-shape rank: three input sets (555 MB of operands, more than the
+    # 256 MB Infinity Cache) rotated between calls, 10 warm-up calls, then
+    # `reps` calls each timed alone; median and minimum reported.
     w = WORKLOADS["mlp_70b_fwd"]
     f, bf = w.f_i, torch.bfloat16
-    X = torch.randn(w.M, w.h, device=dev).to(bf)
-    A0 = torch.randn(w.h, f, device=dev).mul_(0.02).to(bf)
-    B0 = torch.randn(f, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
+    sets = []
+    for _ in range(3):
+        X = torch.randn(w.M, w.h, device=dev).to(bf)
+        A0 = torch.randn(w.h, f, device=dev).mul_(0.02).to(bf)
+        B0 = torch.randn(f, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
+        sets.append((X, A0, B0))
     U = torch.empty(w.M, f, dtype=bf, device=dev)
     Y = torch.empty(w.M, f, dtype=bf, device=dev)
     Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
-    ms = time_calls(torch, lambda: lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, Z, U_i=U, Y_i=Y), reps)
+
+    def fwd(i):
+        X, A0, B0 = sets[i % 3]
+        lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, Z, U_i=U, Y_i=Y)
     fl = 2 * 2 * w.M * w.h * f
-    out["mlp_70b_fwd"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-                          "pct_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    out["mlp_70b_fwd"] = _timed_report(torch, fwd, fl, reps)
 
     w = WORKLOADS["mlp_70b_bwd"]
-    dZ = torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf)
+    dZs = [torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf) for _ in range(3)]
     dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
     dA = torch.empty(w.h, f, dtype=bf, device=dev)
     dB = torch.empty(f, w.h, dtype=bf, device=dev)
     ws = torch.empty(lgs.mlp_bwd_workspace_bytes(w.b, w.s, w.h, w.ffn, w.t, bf), dtype=torch.uint8, device=dev)
-    ms = time_calls(torch, lambda: lgs.tp_mlp_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, U, dZ, dX, dA, dB,
-                                                  workspace=ws), reps)
+
+    def bwd(i):
+        X, A0, B0 = sets[i % 3]
+        lgs.tp_mlp_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, U, dZs[i % 3], dX, dA, dB, workspace=ws)
     fl = 4 * 2 * w.M * w.h * f
-    out["mlp_70b_bwd"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-                          "pct_bf16_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    out["mlp_70b_bwd"] = _timed_report(torch, bwd, fl, reps)
     return out
+
+
+def _timed_report(torch, fn, flops, reps, warmup=10):
+    """fn(i) timed call by call with HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med, mn = ms[len(ms) // 2], ms[0]
+    return {"ms": round(med, 4), "ms_min": round(mn, 4), "runs": reps,
+            "tflops": round(flops / med / 1e9, 2), "tflops_best": round(flops / mn / 1e9, 2),
+            "pct_bf16_peak": round(100 * flops / med / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "note": "median of per-call times, 3 rotated input sets"}
 
 
 def ce_reduction_stream(torch, lgs, xw, reps=30):
@@ -365,7 +401,7 @@ def main():
             "traffic": traffic,
         },
     }
-    configs = {} if args.no_per_config else per_config(torch, lgs, reps=20)
+    configs = {} if args.no_per_config else per_config(torch, lgs, reps=50)
     configs["mlp_8p3b_fwd"] = {"ms": round(per["mlp_fwd"], 4), "tflops": out["mlp_fwd_tflops"],
                                "pct_bf16_peak": round(100 * out["mlp_fwd_tflops"] / PEAK_BF16_TFLOPS, 2),
                                "note": "from the timed steps"}
