@@ -13,6 +13,7 @@ equations state:
 
 * ``oracle.mlp``  -- the GeLU MLP split column-then-row across ``t`` ranks
   (forward, backward and the sum of partials).
+* ``oracle.swiglu`` -- the SwiGLU (gated) MLP block with the same split.
 * ``oracle.xent`` -- full-logit softmax cross-entropy and its vocab-parallel
   form (per-rank max / sum-exp / target logit, then the merge).
 
@@ -22,4 +23,4 @@ finite differences and algebraic identities.  No function here is "parity
 unpinned".
 """
 
-from . import mlp, xent  # noqa: F401
+from . import mlp, swiglu, xent  # noqa: F401

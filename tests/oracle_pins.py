@@ -243,6 +243,188 @@ def check_backward_shards(mlp):
     assert _rel(mlp.partial_sum(dXs), full["dX"]) < 1e-12
 
 
+# --------------------------------------------------------------- SwiGLU checks
+
+def bf_swish(g):
+    return g / (1.0 + math.exp(-g)) if g >= 0 else g * math.exp(g) / (1.0 + math.exp(g))
+
+
+def bf_swiglu(X, Wg, Wu, Wd):
+    """The unsplit gated block by nested loops."""
+    G, U = bf_matmul(X, Wg), bf_matmul(X, Wu)
+    Y = [[bf_swish(g) * u for g, u in zip(gr, ur)] for gr, ur in zip(G, U)]
+    return G, U, Y, bf_matmul(Y, Wd)
+
+
+def check_swish_closed_forms(sw):
+    """sigmoid(ln k) = k / (k + 1) gives Swish and its slope in closed form at
+    g = ln k; Swish(0) = 0, Swish'(0) = 1/2; the odd-part identity
+    Swish(g) - Swish(-g) = g (from sigmoid(g) + sigmoid(-g) = 1); Swish
+    approaches g far right and 0 far left, its slope 1 and 0."""
+    for k in (0.25, 0.5, 1.0, 3.0, 9.0, 1e6):
+        g = math.log(k)
+        s = k / (k + 1.0)
+        assert abs(float(sw.swish(np.array([g]))[0]) - g * s) <= 1e-15 * max(1.0, abs(g)), k
+        assert abs(float(sw.swish_grad(np.array([g]))[0]) - (s + g * s / (k + 1.0))) <= 1e-15 * max(1.0, abs(g)), k
+    assert float(sw.swish(np.array([0.0]))[0]) == 0.0
+    assert abs(float(sw.swish_grad(np.array([0.0]))[0]) - 0.5) < 1e-16
+    g = np.linspace(-30, 30, 6001)
+    assert np.abs(sw.swish(g) - sw.swish(-g) - g).max() < 1e-13
+    assert np.abs(sw.sigmoid(g) + sw.sigmoid(-g) - 1.0).max() < 1e-15
+    assert abs(float(sw.swish(np.array([50.0]))[0]) - 50.0) < 1e-12
+    assert abs(float(sw.swish(np.array([-50.0]))[0])) < 1e-18
+    assert abs(float(sw.swish_grad(np.array([50.0]))[0]) - 1.0) < 1e-12
+    assert abs(float(sw.swish_grad(np.array([-50.0]))[0])) < 1e-18
+    # no overflow at the far ends of fp64
+    with np.errstate(over="raise", invalid="raise"):
+        ends = sw.swish(np.array([-800.0, 800.0]))
+    assert abs(ends[0]) < 1e-300 and ends[1] == 800.0
+    assert np.abs(sw.swish(g) - np.array([bf_swish(x) for x in g])).max() < 1e-13
+
+
+def check_swish_grad_fd(sw):
+    g = np.linspace(-12, 12, 2401)
+    eps = 1e-6
+    fd = (sw.swish(g + eps) - sw.swish(g - eps)) / (2 * eps)
+    assert np.abs(sw.swish_grad(g) - fd).max() < 1e-8
+
+
+def check_swiglu_brute_force(sw):
+    for seed, (M, h, ffn, t) in enumerate([(3, 5, 8, 2), (4, 3, 6, 3), (2, 7, 4, 1), (5, 4, 12, 4)]):
+        r = _rng(200 + seed)
+        X, Wg, Wu, Wd = (r.normal(size=s) for s in ((M, h), (h, ffn), (h, ffn), (ffn, h)))
+        bG, bU, bY, bZ = bf_swiglu(X.tolist(), Wg.tolist(), Wu.tolist(), Wd.tolist())
+        G, U, Y, Z = sw.swiglu_forward(X, Wg, Wu, Wd)
+        for a, b in ((G, bG), (U, bU), (Y, bY), (Z, bZ)):
+            assert _rel(a, b) < 1e-13
+        f = ffn // t
+        for i in range(t):
+            cols = slice(i * f, (i + 1) * f)
+            cG, cU, cY, cZ = bf_swiglu(X.tolist(), Wg[:, cols].tolist(), Wu[:, cols].tolist(),
+                                       Wd[cols, :].tolist())
+            G_i, U_i, Y_i, Z_i = sw.shard_forward(X, sw.column_shard(Wg, t, i), sw.column_shard(Wu, t, i),
+                                                  sw.row_shard(Wd, t, i))
+            for a, b in ((G_i, cG), (U_i, cU), (Y_i, cY), (Z_i, cZ)):
+                assert _rel(a, b) < 1e-13
+
+
+def check_swiglu_split_identity(sw):
+    """Z = sum_i Z_i, the gate product commutes with the column split, and
+    t = 1 is the unsplit block."""
+    r = _rng(8)
+    M, h, ffn = 16, 24, 64
+    X = r.normal(size=(M, h))
+    Wg, Wu, Wd = r.normal(size=(h, ffn)) * 0.3, r.normal(size=(h, ffn)) * 0.3, r.normal(size=(ffn, h)) * 0.3
+    Z = sw.swiglu_forward(X, Wg, Wu, Wd)[3]
+    Y = sw.swiglu_forward(X, Wg, Wu, Wd)[2]
+    for t in (1, 2, 8):
+        outs = [sw.shard_forward(X, sw.column_shard(Wg, t, i), sw.column_shard(Wu, t, i), sw.row_shard(Wd, t, i))
+                for i in range(t)]
+        assert _rel(sum(o[3] for o in outs), Z) < 1e-12, t
+        assert _rel(np.concatenate([o[2] for o in outs], axis=1), Y) < 1e-15, t
+
+
+def check_swiglu_gate_limits(sw):
+    """Special cases that reduce the block to plainer ones: an up projection
+    that yields all ones (a constant input column) leaves a Swish MLP; a gate
+    far in the positive range makes Swish the identity, leaving the bilinear
+    product (X Wg) * (X Wu); a gate far negative shuts the block off."""
+    r = _rng(9)
+    M, h, f = 6, 5, 7
+    X = r.normal(size=(M, h))
+    X[:, -1] = 1.0
+    Wg, Wd = r.normal(size=(h, f)), r.normal(size=(f, h))
+    Wu = np.zeros((h, f))
+    Wu[-1, :] = 1.0
+    G, U, Y, Z = sw.swiglu_forward(X, Wg, Wu, Wd)
+    assert np.array_equal(U, np.ones((M, f)))
+    gg = (X @ Wg).tolist()
+    assert _rel(Y, [[bf_swish(v) for v in row] for row in gg]) < 1e-15
+    Wg2 = np.zeros((h, f))
+    Wg2[-1, :] = 60.0  # G = 60 everywhere, Swish(60) = 60 to fp64 precision
+    Wu2 = r.normal(size=(h, f))
+    Y2 = sw.swiglu_forward(X, Wg2, Wu2, Wd)[2]
+    assert _rel(Y2, 60.0 * (X @ Wu2)) < 1e-15
+    Y3 = sw.swiglu_forward(X, -Wg2, Wu2, Wd)[2]
+    assert np.abs(Y3).max() < 1e-20 * np.abs(X @ Wu2).max()
+
+
+def _sw_loss(sw, X, Wg, Wu, Wd, dZ):
+    return float((sw.shard_forward(X, Wg, Wu, Wd)[3] * dZ).sum())
+
+
+def check_swiglu_backward_fd(sw):
+    """Every entry of dX_i, dWg_i, dWu_i, dWd_i equals a central difference of
+    L = <dZ, Z_i(X, Wg_i, Wu_i, Wd_i)>, on tiny shapes."""
+    eps = 1e-6
+    r = _rng(22)
+    M, h, f = 3, 4, 5
+    X, Wg, Wu, Wd, dZ = (r.normal(size=s) for s in ((M, h), (h, f), (h, f), (f, h), (M, h)))
+    g = sw.shard_backward(X, Wg, Wu, Wd, X @ Wg, X @ Wu, dZ)
+    for name, P in (("dX", X), ("dWg", Wg), ("dWu", Wu), ("dWd", Wd)):
+        fd = np.zeros_like(P)
+        for idx in np.ndindex(P.shape):
+            old = P[idx]
+            P[idx] = old + eps
+            lp = _sw_loss(sw, X, Wg, Wu, Wd, dZ)
+            P[idx] = old - eps
+            lm = _sw_loss(sw, X, Wg, Wu, Wd, dZ)
+            P[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert _rel(g[name], fd) < 1e-6, (name, _rel(g[name], fd))
+    G, U = X @ Wg, X @ Wu
+    assert _rel(g["Y"], [[bf_swish(a) * b for a, b in zip(ga, ua)] for ga, ua in zip(G.tolist(), U.tolist())]) < 1e-15
+    # the two pre-activation gradients are the derivative of L through Y_i
+    for name, P in (("dG", G), ("dU", U)):
+        fd = np.zeros_like(P)
+        for idx in np.ndindex(P.shape):
+            old = P[idx]
+            P[idx] = old + eps
+            Yp = [[bf_swish(a) * b for a, b in zip(ga, ua)] for ga, ua in zip(G.tolist(), U.tolist())]
+            P[idx] = old - eps
+            Ym = [[bf_swish(a) * b for a, b in zip(ga, ua)] for ga, ua in zip(G.tolist(), U.tolist())]
+            P[idx] = old
+            fd[idx] = float(((np.array(Yp) - np.array(Ym)) @ Wd * dZ).sum()) / (2 * eps)
+        assert _rel(g[name], fd) < 1e-6, (name, _rel(g[name], fd))
+
+
+def check_swiglu_backward_directional(sw):
+    """At a moderate size: <dP, D> equals the central difference of L along a
+    random direction D, for every operand P."""
+    r = _rng(32)
+    M, h, f = 48, 40, 56
+    X = r.normal(size=(M, h))
+    Wg, Wu, Wd = r.normal(size=(h, f)) * 0.2, r.normal(size=(h, f)) * 0.2, r.normal(size=(f, h)) * 0.2
+    dZ = r.normal(size=(M, h))
+    g = sw.shard_backward(X, Wg, Wu, Wd, X @ Wg, X @ Wu, dZ)
+    eps = 1e-5
+    for k, name in enumerate(("dX", "dWg", "dWu", "dWd")):
+        args = [X, Wg, Wu, Wd]
+        D = r.normal(size=args[k].shape)
+        ap = args[:k] + [args[k] + eps * D] + args[k + 1:]
+        am = args[:k] + [args[k] - eps * D] + args[k + 1:]
+        fd = (_sw_loss(sw, *ap, dZ) - _sw_loss(sw, *am, dZ)) / (2 * eps)
+        an = float((g[name] * D).sum())
+        assert abs(an - fd) <= 1e-7 * max(1.0, abs(fd)), (name, an, fd)
+
+
+def check_swiglu_backward_shards(sw):
+    """Concatenated weight gradients of the t shards equal the unsplit
+    block's, and the sum of the partials dX_i equals the unsplit dX."""
+    r = _rng(42)
+    M, h, ffn, t = 20, 16, 48, 4
+    X, dZ = r.normal(size=(M, h)), r.normal(size=(M, h))
+    Wg, Wu, Wd = r.normal(size=(h, ffn)) * 0.3, r.normal(size=(h, ffn)) * 0.3, r.normal(size=(ffn, h)) * 0.3
+    full = sw.swiglu_backward(X, Wg, Wu, Wd, dZ)
+    parts = []
+    for i in range(t):
+        Wg_i, Wu_i, Wd_i = sw.column_shard(Wg, t, i), sw.column_shard(Wu, t, i), sw.row_shard(Wd, t, i)
+        parts.append(sw.shard_backward(X, Wg_i, Wu_i, Wd_i, X @ Wg_i, X @ Wu_i, dZ))
+    for name, ax in (("dWg", 1), ("dWu", 1), ("dWd", 0), ("dG", 1), ("dU", 1)):
+        assert _rel(np.concatenate([p[name] for p in parts], axis=ax), full[name]) < 1e-13, name
+    assert _rel(sum(p["dX"] for p in parts), full["dX"]) < 1e-12
+
+
 # ------------------------------------------------------------------- CE checks
 
 def check_xent_hand_example(xent):
@@ -353,5 +535,8 @@ def check_xent_argmax_ties(xent):
 MLP_CHECKS = [check_gelu_table, check_gelu_shape, check_gelu_grad_fd, check_mlp_hand_example,
               check_mlp_brute_force, check_split_identity, check_partial_sum_exact,
               check_backward_fd, check_backward_directional, check_backward_shards]
+SWIGLU_CHECKS = [check_swish_closed_forms, check_swish_grad_fd, check_swiglu_brute_force,
+                 check_swiglu_split_identity, check_swiglu_gate_limits, check_swiglu_backward_fd,
+                 check_swiglu_backward_directional, check_swiglu_backward_shards]
 XENT_CHECKS = [check_xent_hand_example, check_xent_brute_force, check_xent_fused_equals_naive,
                check_xent_uniform, check_xent_shift, check_xent_argmax_ties]

@@ -14,3 +14,8 @@ def test_mlp_oracle(check):
 @pytest.mark.parametrize("check", pins.XENT_CHECKS, ids=lambda f: f.__name__)
 def test_xent_oracle(check):
     check(oracle.xent)
+
+
+@pytest.mark.parametrize("check", pins.SWIGLU_CHECKS, ids=lambda f: f.__name__)
+def test_swiglu_oracle(check):
+    check(oracle.swiglu)

@@ -10,7 +10,7 @@ from scipy.special import erf
 import oracle
 import oracle_pins as pins
 
-mlp, xent = oracle.mlp, oracle.xent
+mlp, xent, sw = oracle.mlp, oracle.xent, oracle.swiglu
 _orig_gelu, _orig_grad = mlp.gelu, mlp.gelu_grad
 
 
@@ -194,3 +194,105 @@ def test_xent_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(xent, attr, fn)
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         assert _caught(pins.XENT_CHECKS, xent), f"no pin caught the planted mistake {name}"
+
+
+# ----------------------------------------------------------------- SwiGLU
+
+_REAL_SIGMOID, _REAL_SWISH, _REAL_SWISH_GRAD = sw.sigmoid, sw.swish, sw.swish_grad
+_REAL_SW_BWD = sw.shard_backward
+
+
+def _sigmoid_flipped(g):
+    return _REAL_SIGMOID(-np.asarray(g, dtype=np.float64))
+
+
+def _swish_is_sigmoid(g):
+    return _REAL_SIGMOID(g)
+
+
+def _swish_grad_dropped_term(g):
+    return _REAL_SIGMOID(g)
+
+
+def _swish_grad_wrong_sign(g):
+    g = np.asarray(g, dtype=np.float64)
+    s = _REAL_SIGMOID(g)
+    return s - g * s * (1.0 - s)
+
+
+def _swish_grad_missing_one_minus(g):
+    g = np.asarray(g, dtype=np.float64)
+    s = _REAL_SIGMOID(g)
+    return s + g * s
+
+
+def _sw_forward_gate_on_up(X, Wg, Wu, Wd):
+    X, Wg, Wu, Wd = (np.asarray(a, dtype=np.float64) for a in (X, Wg, Wu, Wd))
+    G, U = X @ Wg, X @ Wu
+    Y = G * _REAL_SWISH(U)
+    return G, U, Y, Y @ Wd
+
+
+def _sw_bwd_dg_missing_u(X, Wg, Wu, Wd, G, U, dZ):
+    g = _REAL_SW_BWD(X, Wg, Wu, Wd, G, U, dZ)
+    g["dG"] = g["dY"] * sw.swish_grad(np.asarray(G, dtype=np.float64))
+    g["dWg"] = np.asarray(X, dtype=np.float64).T @ g["dG"]
+    g["dX"] = g["dG"] @ np.asarray(Wg, dtype=np.float64).T + g["dU"] @ np.asarray(Wu, dtype=np.float64).T
+    return g
+
+
+def _sw_bwd_du_uses_g(X, Wg, Wu, Wd, G, U, dZ):
+    g = _REAL_SW_BWD(X, Wg, Wu, Wd, G, U, dZ)
+    g["dU"] = g["dY"] * np.asarray(G, dtype=np.float64)
+    g["dWu"] = np.asarray(X, dtype=np.float64).T @ g["dU"]
+    return g
+
+
+def _sw_bwd_swapped_weight_grads(X, Wg, Wu, Wd, G, U, dZ):
+    g = _REAL_SW_BWD(X, Wg, Wu, Wd, G, U, dZ)
+    g["dWg"], g["dWu"] = g["dWu"], g["dWg"]
+    return g
+
+
+def _sw_bwd_dx_drops_up(X, Wg, Wu, Wd, G, U, dZ):
+    g = _REAL_SW_BWD(X, Wg, Wu, Wd, G, U, dZ)
+    g["dX"] = g["dG"] @ np.asarray(Wg, dtype=np.float64).T
+    return g
+
+
+def _sw_bwd_dwd_uses_g_times_u(X, Wg, Wu, Wd, G, U, dZ):
+    g = _REAL_SW_BWD(X, Wg, Wu, Wd, G, U, dZ)
+    Y = np.asarray(G, dtype=np.float64) * np.asarray(U, dtype=np.float64)
+    g["Y"], g["dWd"] = Y, Y.T @ np.asarray(dZ, dtype=np.float64)
+    return g
+
+
+def _sw_bwd_dx_wrong_operand(X, Wg, Wu, Wd, G, U, dZ):
+    g = _REAL_SW_BWD(X, Wg, Wu, Wd, G, U, dZ)
+    g["dX"] = g["dU"] @ np.asarray(Wg, dtype=np.float64).T + g["dG"] @ np.asarray(Wu, dtype=np.float64).T
+    return g
+
+
+SWIGLU_MUTANTS = {
+    "sigmoid_flipped": ("sigmoid", _sigmoid_flipped),
+    "swish_is_sigmoid": ("swish", _swish_is_sigmoid),
+    "swish_grad_dropped_term": ("swish_grad", _swish_grad_dropped_term),
+    "swish_grad_wrong_sign": ("swish_grad", _swish_grad_wrong_sign),
+    "swish_grad_missing_one_minus": ("swish_grad", _swish_grad_missing_one_minus),
+    "forward_gate_on_up": ("swiglu_forward", _sw_forward_gate_on_up),
+    "bwd_dg_missing_up": ("shard_backward", _sw_bwd_dg_missing_u),
+    "bwd_du_uses_preact": ("shard_backward", _sw_bwd_du_uses_g),
+    "bwd_swapped_weight_grads": ("shard_backward", _sw_bwd_swapped_weight_grads),
+    "bwd_dx_drops_up": ("shard_backward", _sw_bwd_dx_drops_up),
+    "bwd_dwd_ungated": ("shard_backward", _sw_bwd_dwd_uses_g_times_u),
+    "bwd_dx_crossed_operands": ("shard_backward", _sw_bwd_dx_wrong_operand),
+    "column_shard_wrong_block": ("column_shard", _column_shard_off_by_one),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWIGLU_MUTANTS))
+def test_swiglu_mutant_is_caught(name, monkeypatch):
+    attr, fn = SWIGLU_MUTANTS[name]
+    monkeypatch.setattr(sw, attr, fn)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        assert _caught(pins.SWIGLU_CHECKS, sw), f"no pin caught the planted mistake {name}"
