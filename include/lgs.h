@@ -13,7 +13,10 @@
  *   - "LIT-022: Megatron-LM: Training Multi-Billion Parameter Language Models
  *     Using Model Parallelism" (dmarx.github.io anthology), "Key takeaways":
  *     the parallel logit GEMM fused into the cross-entropy, the vocabulary
- *     padded so each rank's slice is a multiple of 128.
+ *     padded so each rank's slice is a multiple of 128;
+ *   - "Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs
+ *     with Megatron-LM" (mohashari.github.io), "The MLP Block": the gated
+ *     (SwiGLU) MLP of Llama-3 under the same column-then-row split.
  *
  * Conventions shared by every entry point
  *   - Shapes follow the pages: b (micro-batch), s (sequence length), h (hidden
@@ -86,6 +89,10 @@ const char* lgs_last_error(void);
 size_t lgs_mlp_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype, int y_given);
 /* tp_mlp_bwd: room for the recomputed Y_i and for dU_i, both [M, ffn/t]. */
 size_t lgs_mlp_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype);
+/* tp_swiglu_fwd: 0 if the caller passes Y_i, else M * ffn/t * 2 (bf16). */
+size_t lgs_swiglu_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype, int y_given);
+/* tp_swiglu_bwd: room for the recomputed Y_i [M, ffn/t] and for dGU_i [M, 2 ffn/t]. */
+size_t lgs_swiglu_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype);
 /* vocab_parallel_xent_fwd: per-token partials of each column slab of the slice. */
 size_t lgs_xent_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype);
 
@@ -140,6 +147,58 @@ int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act
                int64_t ldb, const void* U_i, int64_t ldu, const void* dZ, int64_t lddz,
                void* dX_i, int64_t lddx, void* dA_i, int64_t ldda, void* dB_i, int64_t lddb,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_swiglu_fwd -- one rank's forward shard of the SwiGLU (gated) MLP block.
+ *
+ * "Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs with
+ * Megatron-LM" (mohashari.github.io), "The MLP Block": the block is
+ * (Swish(X W_gate) * (X W_up)) W_down with * elementwise; W_gate and W_up are
+ * split by columns, W_down by rows, and rank i computes
+ *
+ *   G_i = X W_gate,i,  U_i = X W_up,i                [M, f] each
+ *   Y_i = Swish(G_i) * U_i, Swish(g) = g / (1 + exp(-g))      [M, f]
+ *   Z_i = Y_i W_down,i                                [M, h] (this rank's partial)
+ *
+ * and Z = sum_i Z_i (one all-reduce; on one device, shard_partial_sum).
+ * f = ffn / t, ffn the inner width of W_gate [h, ffn] over all ranks.
+ *
+ * X      [M, h]   ldx >= h      (replicated input)
+ * Wgu_i  [h, 2f]  ldwgu >= 2f   (the rank's two column blocks side by side:
+ *                                W_gate,i in columns [0, f), W_up,i in [f, 2f))
+ * Wd_i   [f, h]   ldwd >= h     (the rank's row block of W_down [ffn, h])
+ * GU_i   [M, 2f]: optional output (NULL: not stored), G_i in columns [0, f) and
+ *                 U_i in [f, 2f): the pre-activations tp_swiglu_bwd takes.
+ * Y_i    [M, f]:  optional output (NULL: kept in the workspace).
+ * Z_i    [M, h]:  output.  dtype must be LGS_BF16 (else LGS_ERR_UNSUPPORTED).
+ * Workspace: lgs_swiglu_fwd_workspace_bytes(..., Y_i != NULL).
+ */
+int tp_swiglu_fwd(int b, int s, int h, int ffn, int t, int rank, int dtype, const void* X,
+                  int64_t ldx, const void* Wgu_i, int64_t ldwgu, const void* Wd_i, int64_t ldwd,
+                  void* GU_i, int64_t ldgu, void* Y_i, int64_t ldy, void* Z_i, int64_t ldz,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tp_swiglu_bwd -- one rank's backward shard of the SwiGLU MLP block: the
+ * chain rule through the equations of tp_swiglu_fwd, with dZ reaching every
+ * rank unchanged and dX_i a partial (dX = sum_i dX_i), as for the GeLU block:
+ *
+ *   dY_i = dZ Wd_i^T
+ *   dG_i = dY_i * U_i * Swish'(G_i),  dU_i = dY_i * Swish(G_i)
+ *   Y_i  = Swish(G_i) * U_i                    (recomputed)
+ *   dWd_i  = Y_i^T dZ                          [f, h]
+ *   dWgu_i = X^T [dG_i | dU_i]                 [h, 2f] (gate, up side by side)
+ *   dX_i   = dG_i W_gate,i^T + dU_i W_up,i^T   [M, h]
+ *
+ * Inputs X, Wgu_i, Wd_i as in tp_swiglu_fwd; GU_i [M, 2f] the saved [G_i | U_i];
+ * dZ [M, h].  Outputs dX_i, dWgu_i, dWd_i (bf16, each with its ld).
+ * Workspace: lgs_swiglu_bwd_workspace_bytes (holds Y_i and [dG_i | dU_i]).
+ */
+int tp_swiglu_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, const void* X,
+                  int64_t ldx, const void* Wgu_i, int64_t ldwgu, const void* Wd_i, int64_t ldwd,
+                  const void* GU_i, int64_t ldgu, const void* dZ, int64_t lddz, void* dX_i,
+                  int64_t lddx, void* dWgu_i, int64_t lddwgu, void* dWd_i, int64_t lddwd,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * vocab_parallel_xent_fwd -- the fused vocab-parallel logit GEMM + cross-entropy

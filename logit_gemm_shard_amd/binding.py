@@ -33,11 +33,17 @@ SIGNATURES = [
     ("lgs_last_error", ctypes.c_char_p, []),
     ("lgs_mlp_fwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i, _i]),
     ("lgs_mlp_bwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
+    ("lgs_swiglu_fwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i, _i]),
+    ("lgs_swiglu_bwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
     ("lgs_xent_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
     ("tp_mlp_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                         _p, _i64, _p, _i64, _p, _sz, _p]),
     ("tp_mlp_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                         _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _sz, _p]),
+    ("tp_swiglu_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                           _p, _i64, _p, _i64, _p, _sz, _p]),
+    ("tp_swiglu_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                           _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _sz, _p]),
     ("vocab_parallel_xent_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
                                      _p, _p, _p, _p, _sz, _p]),
     ("shard_partial_sum", _i, [_i, _i, _i64, _i, _i, _p, _i64, _p, _p]),
@@ -160,6 +166,46 @@ def tp_mlp_bwd(b, s, h, ffn, t, rank, X, A_i, B_i, U_i, dZ, dX_i, dA_i, dB_i, ac
     _check(L.tp_mlp_bwd(b, s, h, ffn, t, rank, dt, _ACT[act], *args,
                         _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes, _stream(stream)))
     return dX_i, dA_i, dB_i
+
+
+def swiglu_fwd_workspace_bytes(b, s, h, ffn, t, dtype, y_given):
+    return lib().lgs_swiglu_fwd_workspace_bytes(b, s, h, ffn, t, _DT[dtype], int(bool(y_given)))
+
+
+def swiglu_bwd_workspace_bytes(b, s, h, ffn, t, dtype):
+    return lib().lgs_swiglu_bwd_workspace_bytes(b, s, h, ffn, t, _DT[dtype])
+
+
+def tp_swiglu_fwd(b, s, h, ffn, t, rank, X, Wgu_i, Wd_i, Z_i, GU_i=None, Y_i=None,
+                  workspace=None, stream=None):
+    """One rank's SwiGLU forward shard: [G | U] = X [W_gate,i | W_up,i],
+    Y_i = Swish(G) * U, Z_i = Y_i W_down,i."""
+    L = lib()
+    dt = _dtype(X)
+    need = L.lgs_swiglu_fwd_workspace_bytes(b, s, h, ffn, t, dt, int(Y_i is not None))
+    ws, ws_bytes = _workspace(need, X.device, workspace)
+    args = []
+    for m in (X, Wgu_i, Wd_i, GU_i, Y_i, Z_i):
+        args.extend(_mat(m))
+    _check(L.tp_swiglu_fwd(b, s, h, ffn, t, rank, dt, *args,
+                           _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes, _stream(stream)))
+    return Z_i
+
+
+def tp_swiglu_bwd(b, s, h, ffn, t, rank, X, Wgu_i, Wd_i, GU_i, dZ, dX_i, dWgu_i, dWd_i,
+                  workspace=None, stream=None):
+    """One rank's SwiGLU backward shard: dX_i (partial), dWgu_i, dWd_i from X,
+    the saved [G | U] and dZ."""
+    L = lib()
+    dt = _dtype(X)
+    need = L.lgs_swiglu_bwd_workspace_bytes(b, s, h, ffn, t, dt)
+    ws, ws_bytes = _workspace(need, X.device, workspace)
+    args = []
+    for m in (X, Wgu_i, Wd_i, GU_i, dZ, dX_i, dWgu_i, dWd_i):
+        args.extend(_mat(m))
+    _check(L.tp_swiglu_bwd(b, s, h, ffn, t, rank, dt, *args,
+                           _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes, _stream(stream)))
+    return dX_i, dWgu_i, dWd_i
 
 
 def vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, H, E_r, targets, m_r, l_r, tgt_r,

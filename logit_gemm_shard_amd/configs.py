@@ -7,6 +7,12 @@ dmarx anthology, "Key takeaways"), and a 70B dense decoder with hidden size
 8,192 at sequence length 4,096 and micro-batch 1 ("Megatron-LM, in depth",
 aicassindra, "Worked example: 70B parameters on 512 GPUs").
 
+The gated (SwiGLU) MLP block is that of Llama-3-70B, hidden size 8,192, as
+"Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs with
+Megatron-LM" (mohashari.github.io) describes it ("The MLP Block"; sequence
+length 4,096 and micro-batch 1 in its introduction), with the inner width
+28,672 of the 70B GeLU workload, split 8 ways.
+
 Initialisation follows the same "Key takeaways": N(0, 0.02) (standard
 deviation 0.02) for every weight, and the weight just before each residual
 (here the row-parallel B) scaled by 1/sqrt(2N), N the number of attention plus
@@ -19,7 +25,7 @@ from dataclasses import dataclass, field
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp_fwd" | "mlp_bwd" | "xent"
+    kind: str            # "mlp_fwd" | "mlp_bwd" | "xent" | "swiglu_fwd" | "swiglu_bwd"
     b: int
     s: int
     h: int
@@ -64,5 +70,11 @@ WORKLOADS = {
         Workload("mlp_70b_bwd", "mlp_bwd", b=1, s=4096, h=8192, t=8, dtype="bf16", seed=4,
                  ffn=28672, n_blocks=160, dz_seed=5, dz_std=0.01,
                  note="70B-shape MLP shard backward, one rank of t=8"),
+        Workload("swiglu_70b_fwd", "swiglu_fwd", b=1, s=4096, h=8192, t=8, dtype="bf16", seed=6,
+                 ffn=28672, n_blocks=160,
+                 note="70B-shape SwiGLU MLP shard forward, one rank of t=8"),
+        Workload("swiglu_70b_bwd", "swiglu_bwd", b=1, s=4096, h=8192, t=8, dtype="bf16", seed=6,
+                 ffn=28672, n_blocks=160, dz_seed=7, dz_std=0.01,
+                 note="70B-shape SwiGLU MLP shard backward, one rank of t=8"),
     ]
 }

@@ -122,6 +122,19 @@ LGS_API size_t lgs_mlp_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, 
   return 2 * round256((size_t)b * s * (ffn / t) * elt(dtype));
 }
 
+LGS_API size_t lgs_swiglu_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype,
+                                              int y_given) {
+  if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || ffn <= 0 || ffn % t) return 0;
+  if (y_given) return 0;
+  return round256((size_t)b * s * (ffn / t) * elt(dtype));
+}
+
+LGS_API size_t lgs_swiglu_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype) {
+  if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || ffn <= 0 || ffn % t) return 0;
+  const size_t mf = (size_t)b * s * (ffn / t) * elt(dtype);
+  return round256(mf) + round256(2 * mf);
+}
+
 LGS_API size_t lgs_xent_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype) {
   (void)dtype;
   if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || vocab <= 0 || vocab % t) return 0;
@@ -183,6 +196,77 @@ LGS_API int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
   return launched(lgs::mlp_bwd(dtype == LGS_BF16, M, h, f, act, X, ldx, A_i, lda, B_i, ldb, U_i,
                                ldu, dZ, lddz, dX_i, lddx, dA_i, ldda, dB_i, lddb, y, du,
                                (hipStream_t)stream));
+}
+
+namespace {
+
+// The SwiGLU calls share the GeLU block's shape rules; the gate takes no
+// variant and only bf16 is built.
+int check_swiglu(int b, int s, int h, int ffn, int t, int rank, int dtype) {
+  int st = check_mlp(b, s, h, ffn, t, rank, dtype, LGS_GELU_ERF);
+  if (st) return st;
+  if (dtype != LGS_BF16) return fail(LGS_ERR_UNSUPPORTED, "the SwiGLU block takes bf16 only");
+  return LGS_OK;
+}
+
+}  // namespace
+
+LGS_API int tp_swiglu_fwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
+                          const void* X, int64_t ldx, const void* Wgu_i, int64_t ldwgu,
+                          const void* Wd_i, int64_t ldwd, void* GU_i, int64_t ldgu, void* Y_i,
+                          int64_t ldy, void* Z_i, int64_t ldz, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_swiglu(b, s, h, ffn, t, rank, dtype);
+  if (st) return st;
+  const int M = b * s, f = ffn / t;
+  if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("Wgu_i", Wgu_i, h, ldwgu, 2 * f, dtype, true))) return st;
+  if ((st = check_mat("Wd_i", Wd_i, f, ldwd, h, dtype, true))) return st;
+  if ((st = check_mat("GU_i", GU_i, M, ldgu, 2 * f, dtype, false))) return st;
+  if ((st = check_mat("Y_i", Y_i, M, ldy, f, dtype, false))) return st;
+  if ((st = check_mat("Z_i", Z_i, M, ldz, h, dtype, true))) return st;
+  if (!Y_i) {
+    const size_t need = lgs_swiglu_fwd_workspace_bytes(b, s, h, ffn, t, dtype, 0);
+    if (!workspace || workspace_bytes < need)
+      return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    Y_i = workspace;
+    ldy = f;
+  }
+  (void)hipGetLastError();
+  return launched(lgs::swiglu_fwd(M, h, f, X, ldx, Wgu_i, ldwgu, Wd_i, ldwd, GU_i, ldgu, Y_i, ldy,
+                                  Z_i, ldz, (hipStream_t)stream));
+}
+
+LGS_API int tp_swiglu_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
+                          const void* X, int64_t ldx, const void* Wgu_i, int64_t ldwgu,
+                          const void* Wd_i, int64_t ldwd, const void* GU_i, int64_t ldgu,
+                          const void* dZ, int64_t lddz, void* dX_i, int64_t lddx, void* dWgu_i,
+                          int64_t lddwgu, void* dWd_i, int64_t lddwd, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_swiglu(b, s, h, ffn, t, rank, dtype);
+  if (st) return st;
+  const int M = b * s, f = ffn / t;
+  if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("Wgu_i", Wgu_i, h, ldwgu, 2 * f, dtype, true))) return st;
+  if ((st = check_mat("Wd_i", Wd_i, f, ldwd, h, dtype, true))) return st;
+  if ((st = check_mat("GU_i", GU_i, M, ldgu, 2 * f, dtype, true))) return st;
+  if ((st = check_mat("dZ", dZ, M, lddz, h, dtype, true))) return st;
+  if ((st = check_mat("dX_i", dX_i, M, lddx, h, dtype, true))) return st;
+  if ((st = check_mat("dWgu_i", dWgu_i, h, lddwgu, 2 * f, dtype, true))) return st;
+  if ((st = check_mat("dWd_i", dWd_i, f, lddwd, h, dtype, true))) return st;
+  const size_t need = lgs_swiglu_bwd_workspace_bytes(b, s, h, ffn, t, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dGU_i, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  char* y = (char*)workspace;
+  char* dgu = y + round256((size_t)M * f * 2);
+  (void)hipGetLastError();
+  return launched(lgs::swiglu_bwd(M, h, f, X, ldx, Wgu_i, ldwgu, Wd_i, ldwd, GU_i, ldgu, dZ, lddz,
+                                  dX_i, lddx, dWgu_i, lddwgu, dWd_i, lddwd, y, dgu,
+                                  (hipStream_t)stream));
 }
 
 LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype,

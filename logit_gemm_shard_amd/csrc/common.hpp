@@ -1,5 +1,6 @@
 // Shared device helpers for the gfx950 (CDNA4) kernels: types, vector
-// loads / stores, and the GeLU / GeLU' forms used by the GEMM epilogues.
+// loads / stores, and the GeLU / GeLU' and Swish / Swish' forms used by the
+// GEMM epilogues.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,6 +53,26 @@ __device__ __forceinline__ GeluVals gelu_both(float u, int act) {
   const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + fast_exp(2.0f * a));
   const float da = 0.79788456080286536f * fmaf(0.134145f * u, u, 1.0f);
   return {0.5f * u * (1.0f + th), fmaf(0.5f * u * (1.0f - th * th), da, 0.5f * (1.0f + th))};
+}
+
+// Swish(g) = g * sigmoid(g), the gate nonlinearity of the SwiGLU MLP block
+// ("Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs
+// with Megatron-LM", mohashari.github.io, "The MLP Block"), and its slope
+// sigmoid(g) (1 + g (1 - sigmoid(g))).  sigmoid = 1 / (1 + exp(-g)) stays
+// finite at both ends: exp(-g) overflows to inf for g << 0 (sigmoid -> 0)
+// and underflows to 0 for g >> 0 (sigmoid -> 1).
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp(-g));
+}
+
+struct SwishVals {
+  float y;   // Swish(g)
+  float dy;  // Swish'(g)
+};
+
+__device__ __forceinline__ SwishVals swish_both(float g) {
+  const float sg = sigmoid_fast(g);
+  return {g * sg, sg * fmaf(g, 1.0f - sg, 1.0f)};
 }
 
 // W consecutive values at p (W = 4 or 8); bf16 uses one vector access,

@@ -29,11 +29,19 @@ constexpr TileShape kTileShapes[kNumTiles] = {{256, 256, 128, 1.00f},   // ping-
 // shape minimising rounds x tile area / eff: e.g. an 8192 x 6400 output is
 // 640 blocks of 256x320 (two and a half rounds) but 800 of 256x256 (the
 // fourth round one eighth full).
-inline TileId pick_tile(int M, int N) {
+//
+// `allowed` is a bit mask over TileId (every mask includes 256x256).
+constexpr unsigned kAllTiles = (1u << kNumTiles) - 1;
+// ping-pong tiles whose wave width is a multiple of 64 (whole pairs of
+// 32-column groups per wave, for paired epilogues)
+constexpr unsigned kPairedTiles = (1u << T256x256) | (1u << T128x128);
+
+inline TileId pick_tile(int M, int N, unsigned allowed = kAllTiles) {
   constexpr int kCUs = 256;
   TileId best = T256x256;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; ++t) {
+    if (!(allowed & (1u << t))) continue;
     const TileShape& s = kTileShapes[t];
     const long tiles = (long)((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
     const long waves = (tiles + kCUs - 1) / kCUs;
@@ -53,18 +61,39 @@ inline GemmProblem<BM, BN, WGM, AK, BK, Epi> problem(const bf16* A, int64_t lda,
   return GemmProblem<BM, BN, WGM, AK, BK, Epi>{A, lda, B, ldb, M, N, K, epi};
 }
 
-template <bool AK, bool BK, class Epi>
+// Launch on tile t; only the shapes in kMask are instantiated (others fail).
+template <bool AK, bool BK, unsigned kMask = kAllTiles, class Epi>
 inline hipError_t gemm_bf16(TileId t, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
                             int M, int N, int K, const Epi& epi, hipStream_t s) {
+  if (!(kMask & (1u << t))) return hipErrorInvalidValue;
   switch (t) {
-    case T256x256: return launch_gemm_pp(pp_problem<256, 256, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x224: return launch_gemm(problem<256, 224, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x192: return launch_gemm_pp(pp_problem<256, 192, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x160: return launch_gemm(problem<256, 160, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T128x128: return launch_gemm_pp(pp_problem<128, 128, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    case T256x320: return launch_gemm_pp(pp_problem<256, 320, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
-    default: return hipErrorInvalidValue;
+    case T256x256:
+      if constexpr (kMask & (1u << T256x256))
+        return launch_gemm_pp(pp_problem<256, 256, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+      break;
+    case T256x224:
+      if constexpr (kMask & (1u << T256x224))
+        return launch_gemm(problem<256, 224, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+      break;
+    case T256x192:
+      if constexpr (kMask & (1u << T256x192))
+        return launch_gemm_pp(pp_problem<256, 192, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+      break;
+    case T256x160:
+      if constexpr (kMask & (1u << T256x160))
+        return launch_gemm(problem<256, 160, 4, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+      break;
+    case T128x128:
+      if constexpr (kMask & (1u << T128x128))
+        return launch_gemm_pp(pp_problem<128, 128, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+      break;
+    case T256x320:
+      if constexpr (kMask & (1u << T256x320))
+        return launch_gemm_pp(pp_problem<256, 320, AK, BK>(A, lda, B, ldb, M, N, K, epi), s);
+      break;
+    default: break;
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lgs

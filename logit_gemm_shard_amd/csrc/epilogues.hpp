@@ -97,4 +97,91 @@ struct EpiGeluBwd {
   }
 };
 
+// ---------------------------------------------------------------- SwiGLU
+//
+// "Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs with
+// Megatron-LM" (mohashari.github.io), "The MLP Block": rank i holds the
+// column blocks W_gate,i and W_up,i side by side as one [h, 2f] matrix and
+// computes Y_i = Swish(X W_gate,i) * (X W_up,i).  Pre-activations and their
+// gradients use the same side-by-side layout: G at columns [0, f), U at
+// [f, 2f) of one [M, 2f] matrix.
+
+// Store of a paired product: output column n of the interleaved product
+// (32-column groups alternating between the two blocks) goes to column
+// (n / 64) 32 + n % 32 of the first block of C, or of the second block,
+// `half` columns to the right.
+template <typename T>
+struct EpiPairStore {
+  static constexpr bool kDirect = false, kLoads = false;
+  T* C;  // may be null (nothing kept)
+  int64_t ldc;
+  int M, half;
+  __device__ __forceinline__ bf16x8 load8(int, int) const { return bf16x8{}; }
+  __device__ __forceinline__ void apply8(int m, int n, const float* v, bf16x8) const {
+    const int col = ((n >> 6) << 5) + (n & 31);
+    if (m < M && col < half) store_vec<8>(C + (int64_t)m * ldc + col + ((n >> 5) & 1) * half, v);
+  }
+};
+
+// Column-parallel exit of the gated block: the GEMM X [W_gate,i | W_up,i]
+// runs as a paired product, so each wave holds G (tiles 2q) and U (tiles
+// 2q+1) of the same columns and forms Y = Swish(G) * U in registers.  G and U
+// are kept for the backward pass when pairs.C is set.
+struct EpiSwigluFwd {
+  static constexpr bool kDirect = false, kLoads = false, kPaired = true;
+  EpiPairStore<bf16> pairs;
+  EpiStore<bf16> out;
+  int half;
+  __device__ __forceinline__ bool keeps_pairs() const { return pairs.C != nullptr; }
+  template <int TM, int TN>
+  __device__ __forceinline__ void combine(const f32x16 (&acc)[TM][TN], f32x16 (&y)[TM][TN / 2]) const {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < TN / 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[i][q][r] = swish_both(acc[i][2 * q][r]).y * acc[i][2 * q + 1][r];
+  }
+};
+
+// Backward through the gate: acc = dY = dZ W_down,i^T; reads the saved G and
+// U, writes dG = dY * U * Swish'(G) and dU = dY * Swish(G) side by side, and
+// the recomputed Y = Swish(G) * U.
+struct GateUp8 {
+  bf16x8 g, u;
+};
+
+struct EpiSwigluBwd {
+  static constexpr bool kDirect = false, kLoads = true;
+  static constexpr int kMaxRows = 16;  // two prefetched input chunks per output chunk
+  const bf16* GU;  // G at [m, n], U at [m, half + n]
+  int64_t ldgu;
+  bf16* dGU;       // dG at [m, n], dU at [m, half + n]
+  int64_t lddgu;
+  bf16* Y;
+  int64_t ldy;
+  int M, half;
+  __device__ __forceinline__ GateUp8 load8(int m, int n) const {
+    if (m >= M || n >= half) return GateUp8{};
+    const bf16* p = GU + (int64_t)m * ldgu + n;
+    return {*reinterpret_cast<const bf16x8*>(p), *reinterpret_cast<const bf16x8*>(p + half)};
+  }
+  __device__ __forceinline__ void apply8(int m, int n, const float* dy, GateUp8 in) const {
+    if (m >= M || n >= half) return;
+    float dg[8], du[8], y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float g = (float)in.g[i], u = (float)in.u[i];
+      const SwishVals sw = swish_both(g);
+      dg[i] = dy[i] * u * sw.dy;
+      du[i] = dy[i] * sw.y;
+      y[i] = sw.y * u;
+    }
+    bf16* q = dGU + (int64_t)m * lddgu + n;
+    store_vec<8>(q, dg);
+    store_vec<8>(q + half, du);
+    store_vec<8>(Y + (int64_t)m * ldy + n, y);
+  }
+};
+
 }  // namespace lgs

@@ -127,6 +127,21 @@ struct OpLayout<R, false> {
     return (ch * 8 < R && ch * 8 < rows_left) ? (uint32_t)(krow * ld + ch * 8) * 2u : kOutOfRange;
   }
   __device__ __forceinline__ static int kcol(int n, int lane) { return (n * 64 + lane) / kCpr; }
+  // The same load with the tile's columns taken from two blocks of the
+  // operand in alternating 32-column groups: tile column c holds column
+  // (c / 64) 32 + c % 32 of the first block (c / 32 even) or of the second
+  // block, `half` columns to the right (c / 32 odd).  cols_left bounds the
+  // column within a block.  Tiles start at multiples of 64 columns, so a
+  // tile column's group parity is that of its global column.
+  __device__ __forceinline__ static uint32_t src_off_paired(int n, int lane, int64_t ld, int cols_left,
+                                                           int half) {
+    static_assert(R % 64 == 0, "paired tiles hold whole pairs of 32-column groups");
+    const int d = n * 64 + lane;
+    const int krow = d / kCpr, c = (d - krow * kCpr) * 8;
+    const int col = ((c >> 6) << 5) + (c & 31);
+    return (c < R && col < cols_left) ? (uint32_t)(krow * ld + col + ((c >> 5) & 1) * half) * 2u
+                                      : kOutOfRange;
+  }
   // Two ds_read_b64_tr_b16 per fragment (rows row0 .. row0+31 of the wave's
   // columns, k = 16 s + 8 (lane/32) .. +7): lanes 4j..4j+3 of each 16-lane
   // group address k-row j of a 4 x 16 block.  The per-lane part:
@@ -181,6 +196,15 @@ __device__ __forceinline__ void tile_of_block(int pid, int nblk, int tiles_m, in
   tn = in / gsz;
 }
 
+// An epilogue with kPaired = true takes the B operand as two column blocks
+// read in alternating 32-column groups (OpLayout::src_off_paired), so that
+// each wave's accumulator tiles come in pairs (2q, 2q+1) over the same output
+// columns; only the ping-pong core (gemm_pp.hpp) builds it.
+template <class E, class = void>
+struct PairedEpi : std::false_type {};
+template <class E>
+struct PairedEpi<E, std::void_t<decltype(E::kPaired)>> : std::bool_constant<E::kPaired> {};
+
 template <int BM, int BN, int WGM, bool AK, bool BK>
 struct Tile {
   static constexpr int WGN = 4 / WGM;
@@ -227,11 +251,12 @@ __device__ __forceinline__ void staged_epilogue(const f32x16 (&acc)[TM][TN], cha
                                                 int lane, int mb, int nb, const Epi& epi) {
   static_assert(ROWS == 32 || ROWS == 16, "slice rows");
   using SS = SliceShape<WN, ROWS>;
+  using In = std::decay_t<decltype(epi.load8(0, 0))>;  // the chunk's input values
   constexpr int LD = WN + 4;  // floats per staged row
   constexpr int kHalves = 32 / ROWS;
   float* st = reinterpret_cast<float*>(smem) + wave * ROWS * LD;
-  bf16x8 in[2][SS::kPerLane];
-  auto prefetch = [&](int sl, bf16x8(&dst)[SS::kPerLane]) {
+  In in[2][SS::kPerLane];
+  auto prefetch = [&](int sl, In(&dst)[SS::kPerLane]) {
 #pragma unroll
     for (int k = 0; k < SS::kPerLane; ++k) {
       const int c = lane + 64 * k, r = c / SS::kCpr, q = c - r * SS::kCpr;
@@ -274,6 +299,19 @@ constexpr int stage_rows(int waves, int lds) {
   return waves * 32 * (WN + 4) * 4 <= lds ? 32 : 16;
 }
 
+// An epilogue with a large per-chunk input may cap the slice height
+// (Epi::kMaxRows = 16), which halves the registers its prefetched inputs take.
+template <class E, class = void>
+struct EpiMaxRows : std::integral_constant<int, 32> {};
+template <class E>
+struct EpiMaxRows<E, std::void_t<decltype(E::kMaxRows)>> : std::integral_constant<int, E::kMaxRows> {};
+
+template <class Epi, int WN>
+constexpr int slice_rows(int waves, int lds) {
+  return stage_rows<WN>(waves, lds) < EpiMaxRows<Epi>::value ? stage_rows<WN>(waves, lds)
+                                                               : EpiMaxRows<Epi>::value;
+}
+
 // One GEMM of the core: C[M, N] = A B with its epilogue, block tile BM x BN.
 template <int BM_, int BN_, int WGM_, bool AK_, bool BK_, class Epi_>
 struct GemmProblem {
@@ -298,6 +336,7 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
   using T = typename P::T;
   using LA = typename T::LA;
   using LB = typename T::LB;
+  static_assert(!PairedEpi<typename P::Epi>::value, "paired epilogues run on the ping-pong core");
   constexpr int TM = T::TM, TN = T::TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -452,7 +491,7 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
     p.epi.template direct<TM, TN, T::WN>(acc, mb, nb, lane);
   } else {
     __syncthreads();  // every wave is past its last read of the LDS ring
-    constexpr int R = stage_rows<T::WN>(4, T::kLdsBytes);
+    constexpr int R = slice_rows<typename P::Epi, T::WN>(4, T::kLdsBytes);
     static_assert(4 * R * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
     staged_epilogue<TM, TN, T::WN, R>(acc, smem, wave, lane, mb, nb, p.epi);
   }

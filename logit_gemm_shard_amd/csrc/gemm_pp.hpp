@@ -82,12 +82,22 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
   using LA = typename T::LA;
   using LB = typename T::LB;
   constexpr int TM = T::TM, TN = T::TN;
+  constexpr bool kPaired = PairedEpi<typename P::Epi>::value;
+  static_assert(!kPaired || (!P::BK && TN % 2 == 0),
+                "paired tiles: an N-contiguous B and whole pairs of 32-column groups per wave");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
   const int wm = wave & 3, wn = grp;
   const int M = p.M, N = p.N, K = p.K;
   const int m0 = tmi * P::BM, n0 = tni * P::BN;
+  // B columns the tile reads: BN of them from n0, or for a paired epilogue
+  // BN / 2 from each of the two blocks (the second `half` columns on).
+  int bcol0 = n0, bcols = N;
+  if constexpr (kPaired) {
+    bcol0 = tni * (P::BN / 2);
+    bcols = 2 * p.epi.half;
+  }
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -117,13 +127,16 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
 #pragma unroll
   for (int t = 0; t < IB; ++t) {
     const int n = min(wave + kPPWaves * t, LB::kInstr - 1);
-    offb[t] = LB::src_off(n, lane, p.ldb, N - n0);
+    if constexpr (kPaired)
+      offb[t] = LB::src_off_paired(n, lane, p.ldb, p.epi.half - bcol0, p.epi.half);
+    else
+      offb[t] = LB::src_off(n, lane, p.ldb, N - n0);
     kcb[t] = LB::kcol(n, lane);
   }
   auto load_tile = [&](int kt) {
     const int k0 = kt * kBK;
     const __amdgpu_buffer_rsrc_t ra = tile_rsrc<P::AK>(p.A, p.lda, m0, M, K, k0);
-    const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, n0, N, K, k0);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, bcol0, bcols, K, k0);
     const bool kfull = k0 + kBK <= K;
     char* base = smem + (kt % T::kStages) * T::kStage;
 #pragma unroll
@@ -217,9 +230,26 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
     p.epi.template direct<TM, TN, T::WN>(acc, mb, nb, lane);
   } else {
     __syncthreads();  // every wave is past its last read of the LDS ring
-    constexpr int R = stage_rows<T::WN>(kPPWaves, T::kLdsBytes);
+    constexpr int R = slice_rows<typename P::Epi, T::WN>(kPPWaves, T::kLdsBytes);
     static_assert(kPPWaves * R * (T::WN + 4) * 4 <= T::kLdsBytes, "staging does not fit the LDS tiles");
-    staged_epilogue<TM, TN, T::WN, R>(acc, smem, wave, lane, mb, nb, p.epi);
+    if constexpr (kPaired) {
+      // The pairs as computed (if kept), then their combination, which is
+      // WN / 2 columns wide starting at output column nb / 2.  The second
+      // staging lays the waves' LDS regions out with a narrower row, so one
+      // wave's region there overlaps others' regions of the first: a block
+      // barrier separates them (each wave has drained its LDS reads at the
+      // end of a staging).
+      if (p.epi.keeps_pairs()) {
+        staged_epilogue<TM, TN, T::WN, R>(acc, smem, wave, lane, mb, nb, p.epi.pairs);
+        block_barrier();
+      }
+      f32x16 out[TM][TN / 2];
+      p.epi.template combine<TM, TN>(acc, out);
+      constexpr int R2 = slice_rows<decltype(p.epi.out), T::WN / 2>(kPPWaves, T::kLdsBytes);
+      staged_epilogue<TM, TN / 2, T::WN / 2, R2>(out, smem, wave, lane, mb, nb / 2, p.epi.out);
+    } else {
+      staged_epilogue<TM, TN, T::WN, R>(acc, smem, wave, lane, mb, nb, p.epi);
+    }
   }
 }
 

@@ -22,6 +22,19 @@ hipError_t mlp_bwd(bool bf16, int M, int h, int f, int act, const void* X, int64
                    int64_t ldu, const void* dZ, int64_t lddz, void* dX, int64_t lddx, void* dA,
                    int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, hipStream_t s);
 
+// One rank's SwiGLU MLP shard (bf16).  f = ffn / t; W_gu = [W_gate,i | W_up,i].
+//   [G | U] = X W_gu (stored if GU != null), Y = Swish(G) * U, Z = Y W_down,i.
+hipError_t swiglu_fwd(int M, int h, int f, const void* X, int64_t ldx, const void* Wgu,
+                      int64_t ldwgu, const void* Wd, int64_t ldwd, void* GU, int64_t ldgu, void* Y,
+                      int64_t ldy, void* Z, int64_t ldz, hipStream_t s);
+//   dY = dZ W_down^T; dG = dY * U * Swish'(G), dU = dY * Swish(G), Y recomputed
+//   (Y, dGU in scratch); dX = dGU W_gu^T, dW_gu = X^T dGU, dW_down = Y^T dZ.
+hipError_t swiglu_bwd(int M, int h, int f, const void* X, int64_t ldx, const void* Wgu,
+                      int64_t ldwgu, const void* Wd, int64_t ldwd, const void* GU, int64_t ldgu,
+                      const void* dZ, int64_t lddz, void* dX, int64_t lddx, void* dWgu,
+                      int64_t lddwgu, void* dWd, int64_t lddwd, void* Yws, void* dGUws,
+                      hipStream_t s);
+
 // Fused logit GEMM + CE partials for one vocabulary slice of Vr rows.
 size_t xent_scratch_bytes(int M, int Vr);
 hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_t ldh,

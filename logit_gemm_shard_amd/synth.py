@@ -48,6 +48,26 @@ def mlp_weights(w, dtype=None):
     return X, A, B
 
 
+def swiglu_weights(w, dtype=None):
+    """X [M, h], W_gate [h, ffn], W_up [h, ffn], W_down [ffn, h] for a SwiGLU
+    workload (draw order X, W_gate, W_up, W_down; W_down is the weight before
+    the residual)."""
+    dt = dtype or w.dtype
+    g = _gen(w.seed)
+    X = normal((w.M, w.h), 1.0, g, dt)
+    Wg = normal((w.h, w.ffn), 0.02, g, dt)
+    Wu = normal((w.h, w.ffn), 0.02, g, dt)
+    Wd = normal((w.ffn, w.h), residual_std(w.n_blocks), g, dt)
+    return X, Wg, Wu, Wd
+
+
+def gate_up_shard(Wg, Wu, t, r):
+    """Rank r's column blocks of W_gate and W_up side by side, [h, 2 ffn/t]
+    (a copy in the layout the library takes; no arithmetic)."""
+    f = Wg.shape[1] // t
+    return torch.cat([Wg[:, r * f:(r + 1) * f], Wu[:, r * f:(r + 1) * f]], dim=1).contiguous()
+
+
 def mlp_grad(w, dtype=None):
     """The incoming gradient dZ [M, h] of a backward workload."""
     return normal((w.M, w.h), w.dz_std, _gen(w.dz_seed), dtype or w.dtype)

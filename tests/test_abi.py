@@ -36,9 +36,10 @@ def declared_functions():
     return sorted(set(names))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for fn in ("tp_mlp_fwd", "tp_mlp_bwd", "vocab_parallel_xent_fwd", "shard_partial_sum"):
+    for fn in ("tp_mlp_fwd", "tp_mlp_bwd", "vocab_parallel_xent_fwd", "shard_partial_sum",
+               "tp_swiglu_fwd", "tp_swiglu_bwd"):
         assert fn in names
 
 
@@ -116,6 +117,56 @@ def test_mlp_bwd_validation(L):
     need = L.lgs_mlp_bwd_workspace_bytes(1, 16, 64, 128, 2, 1)
     assert need == 2 * 2048
     assert bwd(ws_bytes=need - 1) == 3
+
+
+def _swiglu_fwd(L, **kw):
+    # f = ffn / t = 64: Wgu_i is [h, 2f] = [64, 128]
+    a = dict(b=1, s=16, h=64, ffn=128, t=2, rank=0, dtype=1, X=FAKE, ldx=64, W=FAKE, ldw=128,
+             D=FAKE, ldd=64, GU=None, ldgu=0, Y=FAKE, ldy=64, Z=FAKE, ldz=64, ws=None, ws_bytes=0)
+    a.update(kw)
+    return L.tp_swiglu_fwd(a["b"], a["s"], a["h"], a["ffn"], a["t"], a["rank"], a["dtype"], a["X"],
+                           a["ldx"], a["W"], a["ldw"], a["D"], a["ldd"], a["GU"], a["ldgu"], a["Y"],
+                           a["ldy"], a["Z"], a["ldz"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=0), 1), (dict(rank=2), 1), (dict(ffn=129), 1),  # ffn % t
+    (dict(dtype=0), 2),                       # bf16 only
+    (dict(dtype=5), 2),
+    (dict(ffn=120, ldy=64), 2),               # ffn/t = 60 not a multiple of 8
+    (dict(ldw=64), 1),                        # Wgu_i holds 2f = 128 columns
+    (dict(GU=FAKE, ldgu=64), 1),              # so does GU_i
+    (dict(GU=FAKE + 8, ldgu=128), 2),         # 16-byte alignment
+    (dict(W=None), 1), (dict(D=None), 1), (dict(Z=None), 1),
+    (dict(Y=None), 3), (dict(Y=None, ws=FAKE, ws_bytes=100), 3),
+])
+def test_swiglu_fwd_validation(L, kw, code):
+    assert _swiglu_fwd(L, **kw) == code
+    assert L.lgs_last_error()
+
+
+def test_swiglu_bwd_validation(L):
+    def bwd(**kw):
+        a = dict(b=1, s=16, h=64, ffn=128, t=2, rank=1, dtype=1, ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        # X, Wgu_i, Wd_i, GU_i, dZ, dX_i, dWgu_i, dWd_i with their ld
+        p = [FAKE, 64, FAKE, 128, FAKE, 64, FAKE, 128, FAKE, 64, FAKE, 64, FAKE, 128, FAKE, 64]
+        for i, v in kw.get("mats", {}).items():
+            p[i] = v
+        return L.tp_swiglu_bwd(a["b"], a["s"], a["h"], a["ffn"], a["t"], a["rank"], a["dtype"], *p,
+                               a["ws"], a["ws_bytes"], None)
+    assert bwd(rank=2) == 1
+    assert bwd(dtype=0) == 2
+    assert bwd(mats={6: None}) == 1          # GU_i required
+    assert bwd(mats={7: 64}) == 1            # ldgu < 2f
+    assert bwd(mats={13: 96}) == 1           # lddwgu < 2f
+    assert bwd(ws=None) == 3
+    # Y_i [16, 64] and dGU_i [16, 128] bf16, each rounded up to 256 bytes
+    need = L.lgs_swiglu_bwd_workspace_bytes(1, 16, 64, 128, 2, 1)
+    assert need == 2048 + 4096
+    assert bwd(ws_bytes=need - 1) == 3
+    assert L.lgs_swiglu_fwd_workspace_bytes(1, 16, 64, 128, 2, 1, 1) == 0
+    assert L.lgs_swiglu_fwd_workspace_bytes(1, 16, 64, 128, 2, 1, 0) == 2048
 
 
 def test_xent_validation(L):
