@@ -216,6 +216,40 @@ def per_config(torch, lgs, reps):
         lgs.tp_mlp_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, U, dZs[i % 3], dX, dA, dB, workspace=ws)
     fl = 4 * 2 * w.M * w.h * f
     out["mlp_70b_bwd"] = _timed_report(torch, bwd, fl, reps)
+    del sets, dZs, dX, dA, dB, ws, U, Y, Z
+
+    # 70B-shape SwiGLU rank (the gated MLP of the same model): forward is the
+    # paired [gate | up] GEMM (2 * M * h * 2f) and the down GEMM (2 * M * f * h);
+    # backward is dY, dX, dW_gu, dW_down (2 + 4 + 4 + 2) * M * h * f.
+    w = WORKLOADS["swiglu_70b_fwd"]
+    f = w.f_i
+    sets = []
+    for _ in range(3):
+        X = torch.randn(w.M, w.h, device=dev).to(bf)
+        Wgu = torch.randn(w.h, 2 * f, device=dev).mul_(0.02).to(bf)
+        Wd = torch.randn(f, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
+        sets.append((X, Wgu, Wd))
+    GU = torch.empty(w.M, 2 * f, dtype=bf, device=dev)
+    Y = torch.empty(w.M, f, dtype=bf, device=dev)
+    Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
+
+    def sfwd(i):
+        X, Wgu, Wd = sets[i % 3]
+        lgs.tp_swiglu_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, Wgu, Wd, Z, GU_i=GU, Y_i=Y)
+    out["swiglu_70b_fwd"] = _timed_report(torch, sfwd, 6 * w.M * w.h * f, reps)
+
+    w = WORKLOADS["swiglu_70b_bwd"]
+    dZs = [torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf) for _ in range(3)]
+    dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
+    dWgu = torch.empty(w.h, 2 * f, dtype=bf, device=dev)
+    dWd = torch.empty(f, w.h, dtype=bf, device=dev)
+    ws = torch.empty(lgs.swiglu_bwd_workspace_bytes(w.b, w.s, w.h, w.ffn, w.t, bf), dtype=torch.uint8,
+                     device=dev)
+
+    def sbwd(i):
+        X, Wgu, Wd = sets[i % 3]
+        lgs.tp_swiglu_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, Wgu, Wd, GU, dZs[i % 3], dX, dWgu, dWd, workspace=ws)
+    out["swiglu_70b_bwd"] = _timed_report(torch, sbwd, 12 * w.M * w.h * f, reps)
     return out
 
 

@@ -14,9 +14,9 @@
  *     Using Model Parallelism" (dmarx.github.io anthology), "Key takeaways":
  *     the parallel logit GEMM fused into the cross-entropy, the vocabulary
  *     padded so each rank's slice is a multiple of 128;
- *   - "Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs
- *     with Megatron-LM" (mohashari.github.io), "The MLP Block": the gated
- *     (SwiGLU) MLP of Llama-3 under the same column-then-row split.
+ *   - the mohashari.github.io page on tensor parallelism for fine-tuning 70B
+ *     models with Megatron-LM, section "The MLP Block": the gated (SwiGLU)
+ *     MLP of Llama-3 under the same column-then-row split.
  *
  * Conventions shared by every entry point
  *   - Shapes follow the pages: b (micro-batch), s (sequence length), h (hidden
@@ -151,8 +151,8 @@ int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act
 /*
  * tp_swiglu_fwd -- one rank's forward shard of the SwiGLU (gated) MLP block.
  *
- * "Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs with
- * Megatron-LM" (mohashari.github.io), "The MLP Block": the block is
+ * The mohashari.github.io page on tensor parallelism for fine-tuning 70B
+ * models with Megatron-LM, section "The MLP Block": the block is
  * (Swish(X W_gate) * (X W_up)) W_down with * elementwise; W_gate and W_up are
  * split by columns, W_down by rows, and rank i computes
  *

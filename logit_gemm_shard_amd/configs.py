@@ -7,11 +7,11 @@ dmarx anthology, "Key takeaways"), and a 70B dense decoder with hidden size
 8,192 at sequence length 4,096 and micro-batch 1 ("Megatron-LM, in depth",
 aicassindra, "Worked example: 70B parameters on 512 GPUs").
 
-The gated (SwiGLU) MLP block is that of Llama-3-70B, hidden size 8,192, as
-"Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs with
-Megatron-LM" (mohashari.github.io) describes it ("The MLP Block"; sequence
-length 4,096 and micro-batch 1 in its introduction), with the inner width
-28,672 of the 70B GeLU workload, split 8 ways.
+The gated (SwiGLU) MLP block is that of Llama-3-70B, hidden size 8,192, as the
+mohashari.github.io page on tensor parallelism for fine-tuning 70B models with
+Megatron-LM describes it ("The MLP Block"; sequence length 4,096 and batch
+size 1 in its introduction), with the inner width 28,672 of the 70B GeLU
+workload, split 8 ways.
 
 Initialisation follows the same "Key takeaways": N(0, 0.02) (standard
 deviation 0.02) for every weight, and the weight just before each residual

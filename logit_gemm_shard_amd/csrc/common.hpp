@@ -56,8 +56,8 @@ __device__ __forceinline__ GeluVals gelu_both(float u, int act) {
 }
 
 // Swish(g) = g * sigmoid(g), the gate nonlinearity of the SwiGLU MLP block
-// ("Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs
-// with Megatron-LM", mohashari.github.io, "The MLP Block"), and its slope
+// (the mohashari.github.io page on tensor parallelism for 70B models,
+// section "The MLP Block"), and its slope
 // sigmoid(g) (1 + g (1 - sigmoid(g))).  sigmoid = 1 / (1 + exp(-g)) stays
 // finite at both ends: exp(-g) overflows to inf for g << 0 (sigmoid -> 0)
 // and underflows to 0 for g >> 0 (sigmoid -> 1).

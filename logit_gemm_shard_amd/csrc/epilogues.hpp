@@ -99,8 +99,8 @@ struct EpiGeluBwd {
 
 // ---------------------------------------------------------------- SwiGLU
 //
-// "Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs with
-// Megatron-LM" (mohashari.github.io), "The MLP Block": rank i holds the
+// The mohashari.github.io page on tensor parallelism for fine-tuning 70B
+// models with Megatron-LM, section "The MLP Block": rank i holds the
 // column blocks W_gate,i and W_up,i side by side as one [h, 2f] matrix and
 // computes Y_i = Swish(X W_gate,i) * (X W_up,i).  Pre-activations and their
 // gradients use the same side-by-side layout: G at columns [0, f), U at

@@ -1,7 +1,7 @@
 // One tensor-parallel rank's SwiGLU MLP shard, forward and backward.
 //
-// "Distributed Tensor Parallelism: Scale Fine-tuning 70B Parameter LLMs with
-// Megatron-LM" (mohashari.github.io), "The MLP Block": the gate and up
+// The mohashari.github.io page on tensor parallelism for fine-tuning 70B
+// models with Megatron-LM, section "The MLP Block": the gate and up
 // weights are split by columns, the down weight by rows; rank i computes
 // Y_i = Swish(X W_gate,i) * (X W_up,i) and the partial Z_i = Y_i W_down,i,
 // and one all-reduce sums the partials.  The backward is the chain rule
