@@ -15,7 +15,8 @@ equations state:
   (forward, backward and the sum of partials).
 * ``oracle.swiglu`` -- the SwiGLU (gated) MLP block with the same split.
 * ``oracle.xent`` -- full-logit softmax cross-entropy and its vocab-parallel
-  form (per-rank max / sum-exp / target logit, then the merge).
+  form (per-rank max / sum-exp / target logit, then the merge), and its
+  backward (unsplit, and per rank from the merged log-sum-exp).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against things other
 than itself: brute-force loops, closed forms, printed normal-table values,

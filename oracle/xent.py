@@ -22,6 +22,17 @@ Plain definitions used here:
       loss = M* + ln L* - sum_r T_r
   which equals the full-logit loss in exact arithmetic.  (The pages state only
   the O(b*s) exchange; the partials and this merge are the plain reading.)
+
+The backward is the plain derivative of the summed per-token losses (the page
+states only the forward).  With upstream weights w_k (dloss, 1 by default),
+p_kj = exp(z_kj - lse_k), lse_k = ln sum_j exp(z_kj):
+
+      G = (p - onehot(y)) * w[:, None],   dH = G E,   dE = G^T H.
+
+Split by vocabulary, rank r needs only the merged lse_k = M* + ln L* (one
+more O(b*s) quantity from the same exchange): G_r = (exp(z_r - lse) -
+onehot_r) * w, its dH_r = G_r E_r is a partial (dH = sum_r dH_r) and its
+dE_r = G_r^T H is rank r's rows of dE.
 """
 
 import numpy as np
@@ -115,3 +126,46 @@ def vocab_parallel_loss(H, E, y, t):
     l = np.stack([p[1] for p in parts])
     T = np.stack([p[2] for p in parts])
     return merge(m, l, T)
+
+
+def merge_lse(m, l):
+    """Per-token log-sum-exp over the whole vocabulary from the ranks'
+    partials m, l [t, M]: M* + ln L*."""
+    m, l = _f64(m), _f64(l)
+    Mx = m.max(axis=0)
+    return Mx + np.log((l * np.exp(m - Mx[None, :])).sum(axis=0))
+
+
+def _weights(dloss, M):
+    return np.ones(M) if dloss is None else _f64(dloss)
+
+
+def xent_backward(H, E, y, dloss=None):
+    """Gradient of sum_k dloss_k * loss_k with respect to H and E (the whole
+    vocabulary): returns {"G", "dH", "dE"}."""
+    H, E = _f64(H), _f64(E)
+    y = np.asarray(y, dtype=np.int64)
+    z = H @ E.T
+    mx = z.max(axis=1)
+    p = np.exp(z - mx[:, None])
+    p /= p.sum(axis=1)[:, None]
+    G = p
+    G[np.arange(z.shape[0]), y] -= 1.0
+    G *= _weights(dloss, z.shape[0])[:, None]
+    return {"G": G, "dH": G @ E, "dE": G.T @ H}
+
+
+def shard_backward(H, E_r, y, vocab_start, lse, dloss=None):
+    """Rank r's share for the slice E_r = E[vocab_start : vocab_start + V_r],
+    given the merged per-token lse: returns {"G", "dH", "dE"} with
+    G_r = (exp(z_r - lse) - onehot_r) * dloss, dH_r = G_r E_r (a partial),
+    dE_r = G_r^T H (rank r's rows of dE)."""
+    H, E_r = _f64(H), _f64(E_r)
+    y = np.asarray(y, dtype=np.int64)
+    z = H @ E_r.T
+    G = np.exp(z - _f64(lse)[:, None])
+    local = y - vocab_start
+    rows = np.nonzero((local >= 0) & (local < z.shape[1]))[0]
+    G[rows, local[rows]] -= 1.0
+    G *= _weights(dloss, z.shape[0])[:, None]
+    return {"G": G, "dH": G @ E_r, "dE": G.T @ H}

@@ -532,6 +532,128 @@ def check_xent_argmax_ties(xent):
     assert list(xent.merge_argmax(m, am)) == [1, 2]
 
 
+# ---------------------------------------------------------- CE backward checks
+
+def _bf_weighted_loss(H, E, y, w):
+    return sum(wk * lk for wk, lk in zip(w, bf_xent(H.tolist(), E.tolist(), list(y))))
+
+
+def check_xent_backward_fd(xent):
+    """Every entry of dH and dE equals a central difference of
+    L = sum_k w_k loss_k(H, E), the loss evaluated by brute-force loops."""
+    r = _rng(51)
+    M, h, V = 3, 4, 7
+    H, E = r.normal(size=(M, h)), r.normal(size=(V, h))
+    y = np.array([2, 0, 6])
+    w = np.array([0.5, -1.25, 2.0])
+    g = xent.xent_backward(H, E, y, w)
+    eps = 1e-6
+    for name, P in (("dH", H), ("dE", E)):
+        fd = np.zeros_like(P)
+        for idx in np.ndindex(P.shape):
+            old = P[idx]
+            P[idx] = old + eps
+            lp = _bf_weighted_loss(H, E, y, w)
+            P[idx] = old - eps
+            lm = _bf_weighted_loss(H, E, y, w)
+            P[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert _rel(g[name], fd) < 1e-7, (name, _rel(g[name], fd))
+    # G is the derivative with respect to the logits themselves
+    z = H @ E.T
+    fd = np.zeros_like(z)
+    for k in range(M):
+        for j in range(V):
+            zp, zm = z[k].copy(), z[k].copy()
+            zp[j] += eps
+            zm[j] -= eps
+            lse = lambda v: max(v) + math.log(sum(math.exp(x - max(v)) for x in v))
+            fd[k, j] = w[k] * ((lse(zp) - zp[y[k]]) - (lse(zm) - zm[y[k]])) / (2 * eps)
+    assert _rel(g["G"], fd) < 1e-7
+
+
+def check_xent_backward_default_weights(xent):
+    """dloss omitted means weight 1 per token; each row of G then sums to 0
+    (softmax sums to 1, the one-hot to 1), and G's target entries are p - 1."""
+    r = _rng(52)
+    H, E = r.normal(size=(9, 5)), r.normal(size=(13, 5))
+    y = r.integers(0, 13, size=9)
+    g1 = xent.xent_backward(H, E, y)
+    gw = xent.xent_backward(H, E, y, np.ones(9))
+    assert np.array_equal(g1["G"], gw["G"])
+    assert np.abs(g1["G"].sum(axis=1)).max() < 1e-14
+    assert np.all(g1["G"][np.arange(9), y] < 0) and np.all(g1["G"][np.arange(9), y] > -1)
+    off = np.ones_like(g1["G"], dtype=bool)
+    off[np.arange(9), y] = False
+    assert np.all(g1["G"][off] > 0)
+
+
+def check_xent_backward_zero_embedding(xent):
+    """E = 0: every logit is 0, so G = 1/V - onehot, dH = 0, and
+    dE_j = sum_k w_k (1/V - [y_k = j]) H_k, for the unsplit form and the
+    shards with lse = ln V."""
+    r = _rng(53)
+    M, h, V, t = 6, 4, 12, 3
+    H, E = r.normal(size=(M, h)), np.zeros((V, h))
+    y = np.array([0, 5, 5, 11, 3, 7])
+    w = r.uniform(0.5, 2.0, size=M)
+    want_G = np.full((M, V), 1.0 / V)
+    want_G[np.arange(M), y] -= 1.0
+    want_G *= w[:, None]
+    want_dE = np.zeros((V, h))
+    for k in range(M):
+        for j in range(V):
+            want_dE[j] += w[k] * ((1.0 / V) - (1.0 if y[k] == j else 0.0)) * H[k]
+    g = xent.xent_backward(H, E, y, w)
+    assert _rel(g["G"], want_G) < 1e-15 and np.abs(g["dH"]).max() == 0.0
+    assert _rel(g["dE"], want_dE) < 1e-14
+    Vr = V // t
+    lse = np.full(M, math.log(V))
+    for rk in range(t):
+        gs = xent.shard_backward(H, E[rk * Vr:(rk + 1) * Vr], y, rk * Vr, lse, w)
+        assert _rel(gs["G"], want_G[:, rk * Vr:(rk + 1) * Vr]) < 1e-15
+        assert _rel(gs["dE"], want_dE[rk * Vr:(rk + 1) * Vr]) < 1e-14
+
+
+def check_xent_merge_lse(xent):
+    """The merged lse of the ranks' partials equals ln sum_j exp(z_kj) by
+    brute-force loops, and is unchanged by a constant shift of a token's
+    logits (up to that shift) and by the order of the ranks."""
+    r = _rng(54)
+    M, h, V, t = 5, 6, 20, 4
+    H, E = r.normal(size=(M, h)) * 3, r.normal(size=(V, h))
+    Vr = V // t
+    parts = [xent.shard_partials(H, E[k * Vr:(k + 1) * Vr], np.zeros(M, dtype=np.int64), k * Vr)
+             for k in range(t)]
+    m, l = np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts])
+    lse = xent.merge_lse(m, l)
+    z = (H @ E.T).tolist()
+    want = [math.log(sum(math.exp(v) for v in row)) for row in z]
+    assert _rel(lse, want) < 1e-14
+    perm = [2, 0, 3, 1]
+    assert _rel(xent.merge_lse(m[perm], l[perm]), lse) < 1e-15
+    assert _rel(xent.merge_lse(m + 1000.0, l), lse + 1000.0) < 1e-15
+
+
+def check_xent_backward_shards(xent):
+    """Sum over ranks of dH_r equals the unsplit dH, the ranks' dE_r stacked
+    equal dE, and their G_r side by side equal G, with lse merged from the
+    ranks' own partials."""
+    r = _rng(55)
+    M, h, V, t = 24, 16, 8 * 40, 8
+    H, E = r.normal(size=(M, h)), r.normal(size=(V, h)) * 0.5
+    y = r.integers(0, V, size=M)
+    w = r.normal(size=M)
+    full = xent.xent_backward(H, E, y, w)
+    Vr = V // t
+    parts = [xent.shard_partials(H, E[k * Vr:(k + 1) * Vr], y, k * Vr) for k in range(t)]
+    lse = xent.merge_lse(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    sh = [xent.shard_backward(H, E[k * Vr:(k + 1) * Vr], y, k * Vr, lse, w) for k in range(t)]
+    assert _rel(sum(g["dH"] for g in sh), full["dH"]) < 1e-12
+    assert _rel(np.concatenate([g["dE"] for g in sh], axis=0), full["dE"]) < 1e-12
+    assert _rel(np.concatenate([g["G"] for g in sh], axis=1), full["G"]) < 1e-12
+
+
 MLP_CHECKS = [check_gelu_table, check_gelu_shape, check_gelu_grad_fd, check_mlp_hand_example,
               check_mlp_brute_force, check_split_identity, check_partial_sum_exact,
               check_backward_fd, check_backward_directional, check_backward_shards]
@@ -540,3 +662,5 @@ SWIGLU_CHECKS = [check_swish_closed_forms, check_swish_grad_fd, check_swiglu_bru
                  check_swiglu_backward_directional, check_swiglu_backward_shards]
 XENT_CHECKS = [check_xent_hand_example, check_xent_brute_force, check_xent_fused_equals_naive,
                check_xent_uniform, check_xent_shift, check_xent_argmax_ties]
+XENT_BWD_CHECKS = [check_xent_backward_fd, check_xent_backward_default_weights,
+                   check_xent_backward_zero_embedding, check_xent_merge_lse, check_xent_backward_shards]

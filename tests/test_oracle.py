@@ -19,3 +19,8 @@ def test_xent_oracle(check):
 @pytest.mark.parametrize("check", pins.SWIGLU_CHECKS, ids=lambda f: f.__name__)
 def test_swiglu_oracle(check):
     check(oracle.swiglu)
+
+
+@pytest.mark.parametrize("check", pins.XENT_BWD_CHECKS, ids=lambda f: f.__name__)
+def test_xent_backward_oracle(check):
+    check(oracle.xent)

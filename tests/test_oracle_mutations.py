@@ -296,3 +296,73 @@ def test_swiglu_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(sw, attr, fn)
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         assert _caught(pins.SWIGLU_CHECKS, sw), f"no pin caught the planted mistake {name}"
+
+
+# ------------------------------------------------------------ CE backward
+
+_REAL_XBWD, _REAL_XSHARD, _REAL_LSE = xent.xent_backward, xent.shard_backward, xent.merge_lse
+
+
+def _xbwd_no_onehot(H, E, y, dloss=None):
+    g = _REAL_XBWD(H, E, y, dloss)
+    w = np.ones(len(y)) if dloss is None else np.asarray(dloss, dtype=np.float64)
+    G = g["G"].copy()
+    G[np.arange(len(y)), np.asarray(y)] += w  # the one-hot dropped
+    H, E = np.asarray(H, dtype=np.float64), np.asarray(E, dtype=np.float64)
+    return {"G": G, "dH": G @ E, "dE": G.T @ H}
+
+
+def _xbwd_unweighted(H, E, y, dloss=None):
+    return _REAL_XBWD(H, E, y, None)
+
+
+def _xbwd_de_uses_e(H, E, y, dloss=None):
+    g = _REAL_XBWD(H, E, y, dloss)
+    E = np.asarray(E, dtype=np.float64)
+    g["dE"] = g["G"].T @ (g["G"] @ E) if g["G"].shape[1] == E.shape[0] else g["dE"] * 2
+    return g
+
+
+def _xbwd_softmax_wrong_axis(H, E, y, dloss=None):
+    H, E = np.asarray(H, dtype=np.float64), np.asarray(E, dtype=np.float64)
+    z = H @ E.T
+    p = np.exp(z - z.max(axis=0)[None, :])
+    p /= p.sum(axis=0)[None, :]
+    p[np.arange(z.shape[0]), np.asarray(y)] -= 1.0
+    p *= (np.ones(z.shape[0]) if dloss is None else np.asarray(dloss, dtype=np.float64))[:, None]
+    return {"G": p, "dH": p @ E, "dE": p.T @ H}
+
+
+def _xshard_global_target(H, E_r, y, vocab_start, lse, dloss=None):
+    return _REAL_XSHARD(H, E_r, y, 0, lse, dloss)  # target column not shifted into the slice
+
+
+def _xshard_local_lse(H, E_r, y, vocab_start, lse, dloss=None):
+    z = np.asarray(H, dtype=np.float64) @ np.asarray(E_r, dtype=np.float64).T
+    mx = z.max(axis=1)
+    own = mx + np.log(np.exp(z - mx[:, None]).sum(axis=1))  # the slice's own lse, not the merged one
+    return _REAL_XSHARD(H, E_r, y, vocab_start, own, dloss)
+
+
+def _merge_lse_drops_max(m, l):
+    m, l = np.asarray(m, dtype=np.float64), np.asarray(l, dtype=np.float64)
+    return np.log((l * np.exp(m - m.max(axis=0)[None, :])).sum(axis=0))
+
+
+XENT_BWD_MUTANTS = {
+    "bwd_no_onehot": ("xent_backward", _xbwd_no_onehot),
+    "bwd_ignores_dloss": ("xent_backward", _xbwd_unweighted),
+    "bwd_de_wrong_operand": ("xent_backward", _xbwd_de_uses_e),
+    "bwd_softmax_over_tokens": ("xent_backward", _xbwd_softmax_wrong_axis),
+    "shard_target_not_shifted": ("shard_backward", _xshard_global_target),
+    "shard_uses_local_lse": ("shard_backward", _xshard_local_lse),
+    "merge_lse_drops_max": ("merge_lse", _merge_lse_drops_max),
+}
+
+
+@pytest.mark.parametrize("name", sorted(XENT_BWD_MUTANTS))
+def test_xent_backward_mutant_is_caught(name, monkeypatch):
+    attr, fn = XENT_BWD_MUTANTS[name]
+    monkeypatch.setattr(xent, attr, fn)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        assert _caught(pins.XENT_BWD_CHECKS, xent), f"no pin caught the planted mistake {name}"
