@@ -14,7 +14,7 @@ padded vocabulary 51,200):
 
 All inputs are resident in HBM before timing starts.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-per-config]
     python bench.py --copy-calibration   # plain copy for counter scaling
 """
 
@@ -442,6 +442,24 @@ def main():
     configs["xent_8p3b"] = {"ms": round(per["xent"], 4), "tflops": out["ce_tflops"],
                             "pct_bf16_peak": round(100 * out["ce_tflops"] / PEAK_BF16_TFLOPS, 2),
                             "tokens_per_s": out["ce_tokens_per_s"], "note": "from the timed steps"}
+    if not args.no_per_config:
+        # CE backward of the same slice from the merged log-sum-exp, dloss = 1/M:
+        # the recomputed logit GEMM with its gradient epilogue, then dH_0 = G E_0
+        # and dE_0 = G^T H in one launch (3 x 2 M h V_r FLOP).
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+        lgs.shard_partial_sum("xent_lse", t, M, stats, 3 * M, lse)
+        dl = torch.full((M,), 1.0 / M, dtype=torch.float32, device=dev)
+        dH0 = torch.empty(M, h, dtype=bf, device=dev)
+        dE0 = torch.empty(Vr, h, dtype=bf, device=dev)
+        ws_xb = torch.empty(lgs.xent_bwd_workspace_bytes(xw.b, xw.s, h, V, t), dtype=torch.uint8, device=dev)
+
+        def xbwd(i):
+            lgs.vocab_parallel_xent_bwd(xw.b, xw.s, h, V, t, 0, Hd, E0d, yd, lse, dH0, dE0, dloss=dl,
+                                        workspace=ws_xb, stream=stream)
+        rep = _timed_report(torch, xbwd, 3 * fl["xent"], 50)
+        rep["tokens_per_s"] = round(M / (rep["ms"] * 1e-3), 0)
+        rep["note"] = "median of per-call times; one input set (the step's)"
+        configs["xent_8p3b_bwd"] = rep
     out["per_config"] = configs
     if not args.no_per_config:
         out["ce_reduction_stream"] = ce_reduction_stream(torch, lgs, xw)

@@ -70,7 +70,7 @@ typedef enum { LGS_F32 = 0, LGS_BF16 = 1 } lgs_dtype;
    u/2 * (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) (TANH). */
 typedef enum { LGS_GELU_ERF = 0, LGS_GELU_TANH = 1 } lgs_gelu;
 
-typedef enum { LGS_REDUCE_SUM = 0, LGS_REDUCE_XENT = 1 } lgs_reduce_op;
+typedef enum { LGS_REDUCE_SUM = 0, LGS_REDUCE_XENT = 1, LGS_REDUCE_XENT_LSE = 2 } lgs_reduce_op;
 
 /* Library version as major*10000 + minor*100 + patch. */
 int lgs_version(void);
@@ -95,6 +95,8 @@ size_t lgs_swiglu_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, int d
 size_t lgs_swiglu_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype);
 /* vocab_parallel_xent_fwd: per-token partials of each column slab of the slice. */
 size_t lgs_xent_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype);
+/* vocab_parallel_xent_bwd: the slice's logit gradient G, M * vocab/t bf16. */
+size_t lgs_xent_bwd_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype);
 
 /* ------------------------------------------------------------------------ */
 /*
@@ -228,6 +230,32 @@ int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int
                             size_t workspace_bytes, void* stream);
 
 /*
+ * vocab_parallel_xent_bwd -- one rank's backward of the vocab-parallel
+ * cross-entropy.  The pages give the forward ("LIT-022: Megatron-LM ...",
+ * "Key takeaways"); this is the derivative of sum_k dloss[k] * loss[k].  With
+ * the per-token log-sum-exp over the whole vocabulary, lse[k] = M* + ln L*
+ * (shard_partial_sum(LGS_REDUCE_XENT_LSE) of the forward's partials), rank r
+ * needs nothing else from the other ranks:
+ *
+ *   z       = H E_r^T                 (recomputed, never stored)
+ *   G[k, j] = (exp(z[k, j] - lse[k]) - [j == targets[k] - r*V_r]) * dloss[k]
+ *   dH_r    = G E_r     [M, h]        (a partial: dH = sum_r dH_r)
+ *   dE_r    = G^T H     [V_r, h]      (rank r's rows of dE)
+ *
+ * H [M, h] ldh >= h and E_r [V_r, h] lde >= h as in vocab_parallel_xent_fwd;
+ * targets [M] int32 global ids (precondition: in [0, vocab)); lse [M] fp32;
+ * dloss [M] fp32 or NULL (1 for every token, the gradient of the summed loss;
+ * pass 1/M per token for the mean).  Outputs dH_r, dE_r bf16, each with its
+ * ld.  dtype must be LGS_BF16; h and vocab/t multiples of 8; G (M x V_r bf16)
+ * under 2 GiB.  Workspace: lgs_xent_bwd_workspace_bytes (holds G, bf16).
+ */
+int vocab_parallel_xent_bwd(int b, int s, int h, int vocab, int t, int rank, int dtype,
+                            const void* H, int64_t ldh, const void* E_r, int64_t lde,
+                            const int32_t* targets, const float* lse, const float* dloss,
+                            void* dH_r, int64_t lddh, void* dE_r, int64_t ldde, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * shard_partial_sum -- the one-device stand-in for the exchanges of the path.
  *
  * LGS_REDUCE_SUM: out[j] = sum_{r=0}^{t-1} parts[r*part_stride + j], j < n,
@@ -240,6 +268,9 @@ int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int
  *   back to back (part_stride >= 3n).  out[j] (fp32) = M* + ln L* - sum_r tgt_r
  *   with M* = max_r m_r and L* = sum_r l_r exp(m_r - M*): the log-sum-exp
  *   identity, equal to the full-vocabulary loss.  Both dtypes must be LGS_F32.
+ * LGS_REDUCE_XENT_LSE: the same merge's log-sum-exp alone, out[j] = M* + ln L*
+ *   (the lse that vocab_parallel_xent_bwd takes).  Rank blocks as for
+ *   LGS_REDUCE_XENT (tgt_r is not read); part_stride >= 2n.
  * `out` must not overlap `parts`.
  */
 int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dtype, const void* parts,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblgs.so")
 LGS_OK, LGS_ERR_INVALID_ARG, LGS_ERR_UNSUPPORTED, LGS_ERR_WORKSPACE, LGS_ERR_HIP = range(5)
 LGS_F32, LGS_BF16 = 0, 1
 LGS_GELU_ERF, LGS_GELU_TANH = 0, 1
-LGS_REDUCE_SUM, LGS_REDUCE_XENT = 0, 1
+LGS_REDUCE_SUM, LGS_REDUCE_XENT, LGS_REDUCE_XENT_LSE = 0, 1, 2
 
 _ACT = {"erf": LGS_GELU_ERF, "tanh": LGS_GELU_TANH}
 _DT = {torch.float32: LGS_F32, torch.bfloat16: LGS_BF16}
@@ -36,6 +36,7 @@ SIGNATURES = [
     ("lgs_swiglu_fwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i, _i]),
     ("lgs_swiglu_bwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
     ("lgs_xent_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
+    ("lgs_xent_bwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
     ("tp_mlp_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                         _p, _i64, _p, _i64, _p, _sz, _p]),
     ("tp_mlp_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
@@ -46,6 +47,8 @@ SIGNATURES = [
                            _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _sz, _p]),
     ("vocab_parallel_xent_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
                                      _p, _p, _p, _p, _sz, _p]),
+    ("vocab_parallel_xent_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
+                                     _p, _i64, _p, _i64, _p, _sz, _p]),
     ("shard_partial_sum", _i, [_i, _i, _i64, _i, _i, _p, _i64, _p, _p]),
     # include/lgs_testing.h
     ("lgs_test_num_tiles", _i, []),
@@ -224,10 +227,34 @@ def vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, H, E_r, targets, m_r, l_r, 
     return m_r, l_r, tgt_r
 
 
-def shard_partial_sum(op, t, n, parts, part_stride, out, stream=None):
-    """SUM: out = sum_r parts[r]; XENT: out = per-token loss from [t][3][n] partials."""
+def xent_bwd_workspace_bytes(b, s, h, vocab, t, dtype=torch.bfloat16):
+    return lib().lgs_xent_bwd_workspace_bytes(b, s, h, vocab, t, _DT[dtype])
+
+
+def vocab_parallel_xent_bwd(b, s, h, vocab, t, rank, H, E_r, targets, lse, dH_r, dE_r, dloss=None,
+                            workspace=None, stream=None):
+    """One rank's CE backward: dH_r (partial) and dE_r from the merged lse."""
     L = lib()
-    opc = {"sum": LGS_REDUCE_SUM, "xent": LGS_REDUCE_XENT}[op] if isinstance(op, str) else op
+    dt = _dtype(H)
+    need = L.lgs_xent_bwd_workspace_bytes(b, s, h, vocab, t, dt)
+    ws, ws_bytes = _workspace(need, H.device, workspace)
+    hh, ldh = _mat(H)
+    e, lde = _mat(E_r)
+    dh, lddh = _mat(dH_r)
+    de, ldde = _mat(dE_r)
+    _check(L.vocab_parallel_xent_bwd(b, s, h, vocab, t, rank, dt, hh, ldh, e, lde, _ptr(targets),
+                                     _ptr(lse), _ptr(dloss), dh, lddh, de, ldde,
+                                     _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes,
+                                     _stream(stream)))
+    return dH_r, dE_r
+
+
+def shard_partial_sum(op, t, n, parts, part_stride, out, stream=None):
+    """SUM: out = sum_r parts[r]; XENT: out = per-token loss from [t][3][n]
+    partials; XENT_LSE ("xent_lse"): the per-token log-sum-exp alone."""
+    L = lib()
+    opc = {"sum": LGS_REDUCE_SUM, "xent": LGS_REDUCE_XENT,
+           "xent_lse": LGS_REDUCE_XENT_LSE}[op] if isinstance(op, str) else op
     _check(L.shard_partial_sum(opc, t, n, _dtype(parts), _dtype(out), parts.data_ptr(), part_stride,
                                out.data_ptr(), _stream(stream)))
     return out

@@ -300,6 +300,45 @@ LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int r
                                 argmax_r, loss, workspace, (hipStream_t)stream));
 }
 
+LGS_API size_t lgs_xent_bwd_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype) {
+  (void)dtype;
+  if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || vocab <= 0 || vocab % t) return 0;
+  if ((int64_t)b * s > INT_MAX) return 0;
+  return round256(lgs::xent_bwd_scratch_bytes(b * s, vocab / t));
+}
+
+LGS_API int vocab_parallel_xent_bwd(int b, int s, int h, int vocab, int t, int rank, int dtype,
+                                    const void* H, int64_t ldh, const void* E_r, int64_t lde,
+                                    const int32_t* targets, const float* lse, const float* dloss,
+                                    void* dH_r, int64_t lddh, void* dE_r, int64_t ldde,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_bst(b, s, h, t, rank);
+  if (st) return st;
+  if (vocab <= 0 || vocab % t != 0)
+    return fail(LGS_ERR_INVALID_ARG, "vocab=%d must be positive and divisible by t=%d", vocab, t);
+  if (dtype != LGS_BF16) return fail(LGS_ERR_UNSUPPORTED, "the cross-entropy backward takes bf16 only");
+  const int M = b * s, Vr = vocab / t;
+  if (h % 8 != 0 || Vr % 8 != 0)
+    return fail(LGS_ERR_UNSUPPORTED, "h=%d and vocab/t=%d must be multiples of 8", h, Vr);
+  if ((st = check_mat("H", H, M, ldh, h, dtype, true))) return st;
+  if ((st = check_mat("E_r", E_r, Vr, lde, h, dtype, true))) return st;
+  if ((st = check_mat("dH_r", dH_r, M, lddh, h, dtype, true))) return st;
+  if ((st = check_mat("dE_r", dE_r, Vr, ldde, h, dtype, true))) return st;
+  if (!targets || !lse) return fail(LGS_ERR_INVALID_ARG, "targets and lse are required");
+  if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(dloss, 4))
+    return fail(LGS_ERR_UNSUPPORTED, "per-token arrays must be 4-byte aligned");
+  if ((int64_t)M * Vr * 2 >= ((int64_t)1 << 31))
+    return fail(LGS_ERR_UNSUPPORTED, "the slice's gradient G (M x vocab/t bf16) must span less than 2 GiB");
+  const size_t need = lgs_xent_bwd_workspace_bytes(b, s, h, vocab, t, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for G, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  (void)hipGetLastError();
+  return launched(lgs::xent_bwd(M, h, Vr, rank * Vr, H, ldh, E_r, lde, targets, lse, dloss, dH_r,
+                                lddh, dE_r, ldde, workspace, (hipStream_t)stream));
+}
+
 LGS_API int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dtype,
                               const void* parts, int64_t part_stride, void* out, void* stream) {
   if (t <= 0 || n < 0) return fail(LGS_ERR_INVALID_ARG, "t must be positive and n non-negative");
@@ -316,17 +355,19 @@ LGS_API int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dt
     return launched(lgs::partial_sum(t, n, in_dtype == LGS_BF16, out_dtype == LGS_BF16, parts,
                                      part_stride, out, (hipStream_t)stream));
   }
-  if (op == LGS_REDUCE_XENT) {
+  if (op == LGS_REDUCE_XENT || op == LGS_REDUCE_XENT_LSE) {
+    const bool lse_only = op == LGS_REDUCE_XENT_LSE;
+    const int64_t per = lse_only ? 2 : 3;  // planes read per rank block
     if (in_dtype != LGS_F32 || out_dtype != LGS_F32)
       return fail(LGS_ERR_UNSUPPORTED, "the cross-entropy merge is fp32 in and out");
     if (n > 0 && (!parts || !out)) return fail(LGS_ERR_INVALID_ARG, "parts and out are required");
-    if (part_stride < 3 * n)
-      return fail(LGS_ERR_INVALID_ARG, "part_stride %lld < 3n = %lld", (long long)part_stride,
-                  (long long)(3 * n));
+    if (part_stride < per * n)
+      return fail(LGS_ERR_INVALID_ARG, "part_stride %lld < %lldn = %lld", (long long)part_stride,
+                  (long long)per, (long long)(per * n));
     if (!aligned(parts, 4) || !aligned(out, 4)) return fail(LGS_ERR_UNSUPPORTED, "misaligned parts or out");
     if (n == 0) return ok();
     (void)hipGetLastError();
-    return launched(lgs::xent_combine(t, n, (const float*)parts, part_stride, (float*)out,
+    return launched(lgs::xent_combine(t, n, (const float*)parts, part_stride, lse_only, (float*)out,
                                       (hipStream_t)stream));
   }
   return fail(LGS_ERR_UNSUPPORTED, "unknown reduce op %d", op);

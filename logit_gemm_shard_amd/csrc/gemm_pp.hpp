@@ -286,6 +286,31 @@ void gemm_pp_group3_kernel(P0 p0, P1 p1, P2 p2) {
   }
 }
 
+// Two independent GEMMs in one launch (p0 first).
+template <class P0, class P1>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_group2_kernel(P0 p0, P1 p1) {
+  constexpr int kL = P0::T::kLdsBytes > P1::T::kLdsBytes ? P0::T::kLdsBytes : P1::T::kLdsBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kL];
+  int pid = blockIdx.x, tmi, tni;
+  const int t0 = p0.tiles();
+  if (pid < t0) {
+    tile_of_block(pid, t0, p0.tiles_m(), p0.tiles_n(), tmi, tni);
+    gemm_tile_pp(p0, smem, tmi, tni);
+  } else {
+    pid -= t0;
+    tile_of_block(pid, p1.tiles(), p1.tiles_m(), p1.tiles_n(), tmi, tni);
+    gemm_tile_pp(p1, smem, tmi, tni);
+  }
+}
+
+template <class P0, class P1>
+inline hipError_t launch_gemm_pp_group2(const P0& p0, const P1& p1, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_pp_group2_kernel<P0, P1>), dim3(p0.tiles() + p1.tiles()), dim3(kPPThreads), 0,
+                     stream, p0, p1);
+  return hipGetLastError();
+}
+
 template <class P0, class P1, class P2>
 inline hipError_t launch_gemm_pp_group3(const P0& p0, const P1& p1, const P2& p2, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_pp_group3_kernel<P0, P1, P2>), dim3(p0.tiles() + p1.tiles() + p2.tiles()),

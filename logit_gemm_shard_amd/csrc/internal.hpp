@@ -41,13 +41,22 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
                     const void* E, int64_t lde, const int32_t* targets, float* m_r, float* l_r,
                     float* t_r, int32_t* argmax_r, float* loss, void* scratch, hipStream_t s);
 
+// CE backward for one vocabulary slice: G = (exp(z - lse) - onehot) * dloss
+// (z = H E_r^T recomputed, G in bf16 scratch [M, Vr]), dH_r = G E_r,
+// dE_r = G^T H.  dloss may be null (1 per token).
+size_t xent_bwd_scratch_bytes(int M, int Vr);
+hipError_t xent_bwd(int M, int h, int Vr, int vocab_start, const void* H, int64_t ldh,
+                    const void* E, int64_t lde, const int32_t* targets, const float* lse,
+                    const float* dloss, void* dH, int64_t lddh, void* dE, int64_t ldde,
+                    void* scratch, hipStream_t s);
+
 // Sum of t partials (fp32 accumulate, ascending rank order) or the CE merge.
 hipError_t partial_sum(int t, int64_t n, bool in_bf16, bool out_bf16, const void* parts,
                        int64_t stride, void* out, hipStream_t s);
 hipError_t xent_rows(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
                      const int32_t* targets, float* m, float* l, float* t, hipStream_t s);
-hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, float* loss,
-                        hipStream_t s);
+hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, bool lse_only,
+                        float* loss, hipStream_t s);
 
 // The bf16 GEMM core with a store epilogue and an explicit tile (-1: picked).
 int num_tiles();

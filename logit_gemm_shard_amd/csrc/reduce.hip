@@ -10,7 +10,8 @@
 //   marked non-temporal (each byte is touched once, so caching it only evicts
 //   what the GEMMs around it reuse; measured ~15% faster than plain accesses).
 // * CE merge: loss = M* + ln(sum_r l_r exp(m_r - M*)) - sum_r T_r with
-//   M* = max_r m_r, the log-sum-exp identity over the ranks' slice partials.
+//   M* = max_r m_r, the log-sum-exp identity over the ranks' slice partials,
+//   or (for the backward) the log-sum-exp M* + ln L* alone.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -119,10 +120,11 @@ hipError_t partial_sum(int t, int64_t n, bool in_bf16, bool out_bf16, const void
                   : psum<float, float>(t, n, parts, stride, out, s);
 }
 
-// parts: rank r's block at parts + r*stride holds m[n], l[n], T[n].
+// parts: rank r's block at parts + r*stride holds m[n], l[n], T[n] (T is not
+// read for the log-sum-exp alone).
 __global__ __launch_bounds__(256) void xent_combine_kernel(const float* __restrict__ parts,
                                                            int64_t stride, int t, int64_t n,
-                                                           float* __restrict__ loss) {
+                                                           bool lse_only, float* __restrict__ loss) {
   const int64_t step = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
     float best = -INFINITY;
@@ -134,17 +136,18 @@ __global__ __launch_bounds__(256) void xent_combine_kernel(const float* __restri
     for (int r = 0; r < t; ++r) {
       const float* p = parts + (int64_t)r * stride;
       L += p[n + i] * __expf(p[i] - best);
-      T += p[2 * n + i];
+      if (!lse_only) T += p[2 * n + i];
     }
     loss[i] = best + logf(L) - T;
   }
 }
 
-hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, float* loss,
-                        hipStream_t s) {
+hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, bool lse_only,
+                        float* loss, hipStream_t s) {
   const int64_t want = (n + 255) / 256;
   const int blocks = (int)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
-  hipLaunchKernelGGL(xent_combine_kernel, dim3(blocks), dim3(256), 0, s, parts, stride, t, n, loss);
+  hipLaunchKernelGGL(xent_combine_kernel, dim3(blocks), dim3(256), 0, s, parts, stride, t, n,
+                     lse_only, loss);
   return hipGetLastError();
 }
 

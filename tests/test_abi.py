@@ -191,6 +191,31 @@ def test_xent_validation(L):
     assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 2 * 50 * 8192 * 16
 
 
+def test_xent_bwd_validation(L):
+    def xb(**kw):
+        a = dict(b=2, s=8, h=64, vocab=1024, t=4, rank=0, dtype=1, H=FAKE, ldh=64, E=FAKE, lde=64,
+                 y=FAKE, lse=FAKE, w=None, dH=FAKE, lddh=64, dE=FAKE, ldde=64, ws=FAKE, ws_bytes=1 << 24)
+        a.update(kw)
+        return L.vocab_parallel_xent_bwd(a["b"], a["s"], a["h"], a["vocab"], a["t"], a["rank"],
+                                         a["dtype"], a["H"], a["ldh"], a["E"], a["lde"], a["y"],
+                                         a["lse"], a["w"], a["dH"], a["lddh"], a["dE"], a["ldde"],
+                                         a["ws"], a["ws_bytes"], None)
+    assert xb(vocab=1022) == 1
+    assert xb(rank=4) == 1
+    assert xb(dtype=0) == 2
+    assert xb(vocab=4 * 260) == 2           # vocab/t = 260 not a multiple of 8
+    assert xb(lse=None) == 1 and xb(y=None) == 1
+    assert xb(dE=None) == 1 and xb(ldde=32) == 1
+    assert xb(w=FAKE + 2) == 2              # dloss 4-byte aligned when given
+    assert xb(ws=None) == 3
+    # G is M x vocab/t bf16: 16 tokens x 256 entries x 2 B
+    need = L.lgs_xent_bwd_workspace_bytes(2, 8, 64, 1024, 4, 1)
+    assert need == 16 * 256 * 2
+    assert xb(ws_bytes=need - 1) == 3
+    assert xb(b=1 << 12, s=1 << 12, h=8, ldh=8, lde=8, lddh=8, ldde=8, vocab=8 * 1024, t=1) == 2  # G over 2 GiB
+    assert b"G" in L.lgs_last_error()
+
+
 def test_partial_sum_validation(L):
     assert L.shard_partial_sum(0, 0, 16, 1, 1, FAKE, 16, FAKE, None) == 1
     assert L.shard_partial_sum(0, 2, -1, 1, 1, FAKE, 16, FAKE, None) == 1
@@ -202,6 +227,10 @@ def test_partial_sum_validation(L):
     assert L.shard_partial_sum(0, 2, 16, 1, 1, None, 16, FAKE, None) == 1
     # n == 0 is a no-op and touches nothing
     assert L.shard_partial_sum(0, 3, 0, 1, 1, None, 0, None, None) == 0
+    # the log-sum-exp merge reads two planes per rank block
+    assert L.shard_partial_sum(2, 2, 16, 0, 0, FAKE, 31, FAKE, None) == 1   # stride < 2n
+    assert L.shard_partial_sum(2, 2, 16, 1, 0, FAKE, 48, FAKE, None) == 2   # fp32 only
+    assert L.shard_partial_sum(3, 2, 16, 0, 0, FAKE, 48, FAKE, None) == 2   # no op 3
 
 
 def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
