@@ -14,6 +14,8 @@ equations state:
 * ``oracle.mlp``  -- the GeLU MLP split column-then-row across ``t`` ranks
   (forward, backward and the sum of partials).
 * ``oracle.swiglu`` -- the SwiGLU (gated) MLP block with the same split.
+* ``oracle.sp`` -- the sequence-parallel reduce-scatter exit and all-gather
+  entry that replace the row-parallel all-reduce.
 * ``oracle.xent`` -- full-logit softmax cross-entropy and its vocab-parallel
   form (per-rank max / sum-exp / target logit, then the merge), and its
   backward (unsplit, and per rank from the merged log-sum-exp).
@@ -24,4 +26,4 @@ finite differences and algebraic identities.  No function here is "parity
 unpinned".
 """
 
-from . import mlp, swiglu, xent  # noqa: F401
+from . import mlp, sp, swiglu, xent  # noqa: F401

@@ -1,0 +1,54 @@
+"""fp64 oracle: the sequence-parallel exit and entry around the row-parallel GEMM.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+"Tensor Parallelism and Pipeline Parallelism: Mathematical Foundations of
+Megatron-LM ..." (llms.blog), section "Sequence Parallelism", "Splitting
+All-Reduce into Reduce-Scatter and All-Gather": the row-parallel exit's
+all-reduce becomes a reduce-scatter that sums the t partials and leaves each
+rank the (s/t, b, h) chunk of the result along the sequence; LayerNorm,
+dropout and residual run on that chunk; an all-gather rebuilds the (s, b, h)
+tensor before the next column-parallel GEMM.
+
+Layout reading: activations are the pages' (s, b, h) tensor flattened with s
+outermost, so row k = s_idx * b + b_idx of an [s*b, h] matrix, and rank r's
+chunk is the contiguous rows [r*(s/t)*b, (r+1)*(s/t)*b).  s must divide by t.
+"""
+
+import numpy as np
+
+from .mlp import partial_sum
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def chunk_rows(s, b, t, r):
+    """[start, stop) of rank r's rows of the flattened (s, b) token axis."""
+    if s % t:
+        raise ValueError("the sequence length must divide by t")
+    n = (s // t) * b
+    return r * n, (r + 1) * n
+
+
+def reduce_scatter(parts, s, b, t, r):
+    """Rank r's chunk of sum_i parts[i], each part [s*b, h]."""
+    a, z = chunk_rows(s, b, t, r)
+    return partial_sum([_f64(p)[a:z] for p in parts])
+
+
+def all_gather(shards, s, b, t):
+    """The [s*b, h] tensor from the t ranks' chunks, rank order along s."""
+    shards = [_f64(x) for x in shards]
+    if len(shards) != t or any(x.shape[0] != (s // t) * b for x in shards):
+        raise ValueError("expected t chunks of (s/t)*b rows")
+    return np.concatenate(shards, axis=0)
+
+
+def comm_volume(kind, t, n):
+    """Elements each rank sends in a ring collective over a tensor of n
+    elements: (t-1)/t n for a reduce-scatter or an all-gather, twice that for
+    the all-reduce they compose (the section's volume identity)."""
+    one = (t - 1) / t * n
+    return {"reduce_scatter": one, "all_gather": one, "all_reduce": 2 * one}[kind]

@@ -654,6 +654,55 @@ def check_xent_backward_shards(xent):
     assert _rel(np.concatenate([g["G"] for g in sh], axis=1), full["G"]) < 1e-12
 
 
+# ---------------------------------------------------------------- SP checks
+
+def check_sp_reduce_scatter_brute(sp):
+    """Each rank's chunk equals the element-by-element sum of the parts over
+    its rows, by loops over the (s, b) index pairs that land in the chunk."""
+    r_ = _rng(61)
+    s, b, h, t = 8, 3, 5, 4
+    parts = [r_.integers(-50, 50, size=(s * b, h)).astype(np.float64) for _ in range(t)]
+    for r in range(t):
+        got = sp.reduce_scatter(parts, s, b, t, r)
+        want = []
+        for si in range(r * s // t, (r + 1) * s // t):
+            for bi in range(b):
+                k = si * b + bi
+                want.append([sum(p[k, c] for p in parts) for c in range(h)])
+        assert np.array_equal(got, np.array(want)), r
+
+
+def check_sp_identity(sp):
+    """All-gather of every rank's reduce-scatter = the all-reduce (the sum of
+    the partials), exactly; and the chunks tile the token axis in rank order."""
+    r_ = _rng(62)
+    s, b, h = 16, 2, 7
+    for t in (1, 2, 4, 8):
+        parts = [r_.normal(size=(s * b, h)) for _ in range(t)]
+        chunks = [sp.reduce_scatter(parts, s, b, t, r) for r in range(t)]
+        full = sp.all_gather(chunks, s, b, t)
+        want = parts[0].copy()
+        for p in parts[1:]:
+            want = want + p
+        assert np.array_equal(full, want), t
+        bounds = [sp.chunk_rows(s, b, t, r) for r in range(t)]
+        assert bounds[0][0] == 0 and bounds[-1][1] == s * b
+        assert all(bounds[i][1] == bounds[i + 1][0] for i in range(t - 1))
+
+
+def check_sp_volume(sp):
+    """The section's identity: (t-1)/t M + (t-1)/t M = 2 (t-1)/t M, and at
+    t = 8 each rank sends 7/8 of the tensor per half."""
+    for t in (2, 4, 8):
+        n = 8 * 1024 * 3072
+        rs, ag, ar = (sp.comm_volume(k, t, n) for k in ("reduce_scatter", "all_gather", "all_reduce"))
+        assert rs + ag == ar == 2 * (t - 1) * n / t
+    assert sp.comm_volume("all_gather", 8, 8) == 7.0
+
+
+SP_CHECKS = [check_sp_reduce_scatter_brute, check_sp_identity, check_sp_volume]
+
+
 MLP_CHECKS = [check_gelu_table, check_gelu_shape, check_gelu_grad_fd, check_mlp_hand_example,
               check_mlp_brute_force, check_split_identity, check_partial_sum_exact,
               check_backward_fd, check_backward_directional, check_backward_shards]

@@ -24,3 +24,8 @@ def test_swiglu_oracle(check):
 @pytest.mark.parametrize("check", pins.XENT_BWD_CHECKS, ids=lambda f: f.__name__)
 def test_xent_backward_oracle(check):
     check(oracle.xent)
+
+
+@pytest.mark.parametrize("check", pins.SP_CHECKS, ids=lambda f: f.__name__)
+def test_sp_oracle(check):
+    check(oracle.sp)

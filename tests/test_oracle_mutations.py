@@ -366,3 +366,47 @@ def test_xent_backward_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(xent, attr, fn)
     with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         assert _caught(pins.XENT_BWD_CHECKS, xent), f"no pin caught the planted mistake {name}"
+
+
+# ------------------------------------------------------ sequence parallelism
+
+sp = oracle.sp
+_REAL_CHUNK = sp.chunk_rows
+
+
+def _chunk_b_major(s, b, t, r):
+    # chunks taken along the flattened axis as if it were (b, s): wrong rows
+    a, z = _REAL_CHUNK(s, b, t, r)
+    return (a + b) % (s * b), (a + b) % (s * b) + (z - a)
+
+
+def _rs_skips_last(parts, s, b, t, r):
+    a, z = sp.chunk_rows(s, b, t, r)
+    out = np.zeros_like(np.asarray(parts[0], dtype=np.float64)[a:z])
+    for p in parts[:-1] if len(parts) > 1 else parts:
+        out = out + np.asarray(p, dtype=np.float64)[a:z]
+    return out
+
+
+def _ag_reversed(shards, s, b, t):
+    return np.concatenate([np.asarray(x, dtype=np.float64) for x in shards[::-1]], axis=0)
+
+
+def _volume_no_half(kind, t, n):
+    one = (t - 1) * n
+    return {"reduce_scatter": one, "all_gather": one, "all_reduce": one}[kind]
+
+
+SP_MUTANTS = {
+    "chunk_wrong_rows": ("chunk_rows", _chunk_b_major),
+    "rs_skips_last_rank": ("reduce_scatter", _rs_skips_last),
+    "ag_reversed_order": ("all_gather", _ag_reversed),
+    "volume_wrong": ("comm_volume", _volume_no_half),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SP_MUTANTS))
+def test_sp_mutant_is_caught(name, monkeypatch):
+    attr, fn = SP_MUTANTS[name]
+    monkeypatch.setattr(sp, attr, fn)
+    assert _caught(pins.SP_CHECKS, sp), f"no pin caught the planted mistake {name}"
