@@ -460,6 +460,22 @@ def main():
         rep["tokens_per_s"] = round(M / (rep["ms"] * 1e-3), 0)
         rep["note"] = "median of per-call times; one input set (the step's)"
         configs["xent_8p3b_bwd"] = rep
+        # sequence-parallel stand-ins at the same shape (s = 1024, b = 8, h = 3072,
+        # t = 8): rank 0's reduce-scatter of the 8 partials, and the all-gather of
+        # 8 chunks into [s*b, h]; both pure HBM streams
+        chunk = M * h // t
+        rs_out = torch.empty(M // t, h, dtype=bf, device=dev)
+        ag_in = torch.randn(t, M // t, h, device=dev).to(bf)
+        ag_out = torch.empty(M, h, dtype=bf, device=dev)
+        rs_ms = time_calls(torch, lambda: lgs.shard_reduce_scatter(t, 0, w.s, w.b, h, zparts, M * h, rs_out), 50)
+        ag_ms = time_calls(torch, lambda: lgs.shard_all_gather(t, w.s, w.b, h, ag_in, chunk, ag_out), 50)
+        rs_bytes, ag_bytes = (t + 1) * chunk * 2, 2 * M * h * 2
+        configs["sp_8p3b"] = {
+            "reduce_scatter_us": round(rs_ms * 1e3, 2),
+            "reduce_scatter_GBs": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1),
+            "all_gather_us": round(ag_ms * 1e3, 2),
+            "all_gather_GBs": round(ag_bytes / (ag_ms * 1e-3) / 1e9, 1),
+            "note": "bytes = every byte read once + written once; HBM peak 8000 GB/s"}
     out["per_config"] = configs
     if not args.no_per_config:
         out["ce_reduction_stream"] = ce_reduction_stream(torch, lgs, xw)

@@ -276,6 +276,35 @@ int vocab_parallel_xent_bwd(int b, int s, int h, int vocab, int t, int rank, int
 int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dtype, const void* parts,
                       int64_t part_stride, void* out, void* stream);
 
+/*
+ * shard_reduce_scatter / shard_all_gather -- one-device stand-ins for the
+ * sequence-parallel exit and entry ("Mathematical Foundations of Megatron-LM",
+ * "Sequence Parallelism", "Splitting All-Reduce into Reduce-Scatter and
+ * All-Gather").  The row-parallel exit's all-reduce becomes a reduce-scatter
+ * that sums the t partials and leaves rank r only its s/t chunk of the
+ * sequence; LayerNorm, dropout and the residual then run on (s/t, b, h); an
+ * all-gather rebuilds (s, b, h) before the next column-parallel GEMM.  Both
+ * halves together move what the all-reduce moves.
+ *
+ * Token rows are the pages' (s, b) order flattened s-outermost (row
+ * s_idx * b + b_idx of an [s*b, h] matrix), so rank r's chunk is the
+ * contiguous rows [r*(s/t)*b, (r+1)*(s/t)*b).  s must be divisible by t.
+ *
+ * shard_reduce_scatter: out[j] = sum_{i<t} parts[i*part_stride + r*c + j],
+ *   j < c = (s/t)*b*h, accumulated in fp32 in ascending i (the same bits as
+ *   the matching rows of shard_partial_sum(LGS_REDUCE_SUM)).  Each part is a
+ *   dense [s*b, h]; part_stride >= s*b*h.  in_dtype / out_dtype each LGS_F32
+ *   or LGS_BF16.
+ * shard_all_gather: out[q*c + j] = shards[q*shard_stride + j] for q < t,
+ *   j < c: the dense [s*b, h] tensor from the t chunks, rank order along s.
+ *   shard_stride >= c.  A copy (dtype in = out).
+ * `out` must not overlap the inputs.
+ */
+int shard_reduce_scatter(int t, int rank, int s, int b, int h, int in_dtype, int out_dtype,
+                         const void* parts, int64_t part_stride, void* out, void* stream);
+int shard_all_gather(int t, int s, int b, int h, int dtype, const void* shards,
+                     int64_t shard_stride, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,8 @@ SIGNATURES = [
     ("vocab_parallel_xent_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
                                      _p, _i64, _p, _i64, _p, _sz, _p]),
     ("shard_partial_sum", _i, [_i, _i, _i64, _i, _i, _p, _i64, _p, _p]),
+    ("shard_reduce_scatter", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _p]),
+    ("shard_all_gather", _i, [_i, _i, _i, _i, _i, _p, _i64, _p, _p]),
     # include/lgs_testing.h
     ("lgs_test_num_tiles", _i, []),
     ("lgs_test_tile_shape", _i, [_i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
@@ -257,6 +259,22 @@ def shard_partial_sum(op, t, n, parts, part_stride, out, stream=None):
            "xent_lse": LGS_REDUCE_XENT_LSE}[op] if isinstance(op, str) else op
     _check(L.shard_partial_sum(opc, t, n, _dtype(parts), _dtype(out), parts.data_ptr(), part_stride,
                                out.data_ptr(), _stream(stream)))
+    return out
+
+
+def shard_reduce_scatter(t, rank, s, b, h, parts, part_stride, out, stream=None):
+    """Rank's (s/t)*b rows of sum_i parts[i] (each part a dense [s*b, h])."""
+    _check(lib().shard_reduce_scatter(t, rank, s, b, h, _dtype(parts), _dtype(out), parts.data_ptr(),
+                                      part_stride, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def shard_all_gather(t, s, b, h, shards, shard_stride, out, stream=None):
+    """The dense [s*b, h] tensor from t chunks of (s/t)*b rows, rank order."""
+    if shards.dtype != out.dtype:
+        raise ValueError("the all-gather copies: shards and out share a dtype")
+    _check(lib().shard_all_gather(t, s, b, h, _dtype(out), shards.data_ptr(), shard_stride, out.data_ptr(),
+                                  _stream(stream)))
     return out
 
 

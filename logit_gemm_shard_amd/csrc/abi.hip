@@ -373,6 +373,54 @@ LGS_API int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dt
   return fail(LGS_ERR_UNSUPPORTED, "unknown reduce op %d", op);
 }
 
+namespace {
+
+int check_sp(int t, int s, int b, int h) {
+  if (t <= 0 || s <= 0 || b <= 0 || h <= 0)
+    return fail(LGS_ERR_INVALID_ARG, "t, s, b and h must be positive (got t=%d s=%d b=%d h=%d)", t,
+                s, b, h);
+  if (s % t != 0) return fail(LGS_ERR_INVALID_ARG, "s=%d must be divisible by t=%d", s, t);
+  return LGS_OK;
+}
+
+}  // namespace
+
+LGS_API int shard_reduce_scatter(int t, int rank, int s, int b, int h, int in_dtype, int out_dtype,
+                                 const void* parts, int64_t part_stride, void* out, void* stream) {
+  int st = check_sp(t, s, b, h);
+  if (st) return st;
+  if (rank < 0 || rank >= t) return fail(LGS_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, t);
+  if ((st = check_dtype(in_dtype)) || (st = check_dtype(out_dtype))) return st;
+  const int64_t n = (int64_t)s * b * h, chunk = n / t;
+  if (!parts || !out) return fail(LGS_ERR_INVALID_ARG, "parts and out are required");
+  if (t > 1 && part_stride < n)
+    return fail(LGS_ERR_INVALID_ARG, "part_stride %lld < s*b*h = %lld", (long long)part_stride,
+                (long long)n);
+  if (!aligned(parts, elt(in_dtype)) || !aligned(out, elt(out_dtype)))
+    return fail(LGS_ERR_UNSUPPORTED, "misaligned parts or out");
+  (void)hipGetLastError();
+  return launched(lgs::reduce_scatter(t, chunk, rank, in_dtype == LGS_BF16, out_dtype == LGS_BF16,
+                                      parts, part_stride, out, (hipStream_t)stream));
+}
+
+LGS_API int shard_all_gather(int t, int s, int b, int h, int dtype, const void* shards,
+                             int64_t shard_stride, void* out, void* stream) {
+  int st = check_sp(t, s, b, h);
+  if (st) return st;
+  if ((st = check_dtype(dtype))) return st;
+  const int64_t chunk = (int64_t)(s / t) * b * h;
+  if (!shards || !out) return fail(LGS_ERR_INVALID_ARG, "shards and out are required");
+  if (t > 1 && shard_stride < chunk)
+    return fail(LGS_ERR_INVALID_ARG, "shard_stride %lld < (s/t)*b*h = %lld", (long long)shard_stride,
+                (long long)chunk);
+  if (t > 65535) return fail(LGS_ERR_UNSUPPORTED, "t=%d exceeds the launch grid", t);
+  if (!aligned(shards, elt(dtype)) || !aligned(out, elt(dtype)))
+    return fail(LGS_ERR_UNSUPPORTED, "misaligned shards or out");
+  (void)hipGetLastError();
+  return launched(lgs::all_gather(t, chunk, dtype == LGS_BF16, shards, shard_stride, out,
+                                  (hipStream_t)stream));
+}
+
 LGS_API int lgs_test_num_tiles(void) { return lgs::num_tiles(); }
 
 LGS_API int lgs_test_tile_shape(int tile, int* bm, int* bn) {

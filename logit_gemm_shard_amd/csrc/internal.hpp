@@ -53,6 +53,12 @@ hipError_t xent_bwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
 // Sum of t partials (fp32 accumulate, ascending rank order) or the CE merge.
 hipError_t partial_sum(int t, int64_t n, bool in_bf16, bool out_bf16, const void* parts,
                        int64_t stride, void* out, hipStream_t s);
+// Sequence-parallel stand-ins: rank's chunk of the sum (chunk elements at
+// offset rank * chunk of every part), and the copy of t chunks into place.
+hipError_t reduce_scatter(int t, int64_t chunk, int rank, bool in_bf16, bool out_bf16,
+                          const void* parts, int64_t stride, void* out, hipStream_t s);
+hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64_t stride,
+                      void* out, hipStream_t s);
 hipError_t xent_rows(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
                      const int32_t* targets, float* m, float* l, float* t, hipStream_t s);
 hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, bool lse_only,

@@ -9,6 +9,10 @@
 //   every rank's block per thread, t loads in flight before the adds, all
 //   marked non-temporal (each byte is touched once, so caching it only evicts
 //   what the GEMMs around it reuse; measured ~15% faster than plain accesses).
+// * Sequence-parallel exit and entry ("Mathematical Foundations of
+//   Megatron-LM ...", "Sequence Parallelism"): the reduce-scatter is the same
+//   sum over only rank r's s/t rows of the (s, b, h) tensor (s outermost, so a
+//   contiguous range), and the all-gather a copy of the t chunks into place.
 // * CE merge: loss = M* + ln(sum_r l_r exp(m_r - M*)) - sum_r T_r with
 //   M* = max_r m_r, the log-sum-exp identity over the ranks' slice partials,
 //   or (for the backward) the log-sum-exp M* + ln L* alone.
@@ -118,6 +122,57 @@ hipError_t partial_sum(int t, int64_t n, bool in_bf16, bool out_bf16, const void
                     : psum<bf16, float>(t, n, parts, stride, out, s);
   return out_bf16 ? psum<float, bf16>(t, n, parts, stride, out, s)
                   : psum<float, float>(t, n, parts, stride, out, s);
+}
+
+hipError_t reduce_scatter(int t, int64_t chunk, int rank, bool in_bf16, bool out_bf16,
+                          const void* parts, int64_t stride, void* out, hipStream_t s) {
+  const char* base = (const char*)parts + (int64_t)rank * chunk * (in_bf16 ? 2 : 4);
+  return partial_sum(t, chunk, in_bf16, out_bf16, base, stride, out, s);
+}
+
+// out[q * chunk + j] = shards[q * stride + j]: blockIdx.y is the chunk q, the
+// blocks along x stride over it in 16-byte vectors (the vector path needs
+// chunk bytes, stride bytes and both bases 16-byte aligned).
+__global__ __launch_bounds__(256) void gather_vec_kernel(const char* __restrict__ shards,
+                                                         int64_t stride_bytes, int64_t vecs,
+                                                         char* __restrict__ out) {
+  const int q = blockIdx.y;
+  const char* src = shards + (int64_t)q * stride_bytes;
+  char* dst = out + (int64_t)q * vecs * 16;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < vecs; i += step)
+    st_nt(dst + i * 16, ld_nt(src + i * 16));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_scalar_kernel(const T* __restrict__ shards,
+                                                            int64_t stride, int64_t chunk,
+                                                            T* __restrict__ out) {
+  const int q = blockIdx.y;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < chunk; i += step)
+    out[(int64_t)q * chunk + i] = shards[(int64_t)q * stride + i];
+}
+
+hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64_t stride,
+                      void* out, hipStream_t s) {
+  const int64_t esz = bf16 ? 2 : 4, bytes = chunk * esz;
+  const bool vec = bytes % 16 == 0 && (stride * esz) % 16 == 0 && (uintptr_t)shards % 16 == 0 &&
+                   (uintptr_t)out % 16 == 0;
+  const int64_t units = vec ? bytes / 16 : chunk;
+  const int64_t want = (units + 255) / 256;
+  const int bx = (int)(want < 2048 ? (want < 1 ? 1 : want) : 2048);
+  const dim3 grid(bx, t);
+  if (vec)
+    hipLaunchKernelGGL(gather_vec_kernel, grid, dim3(256), 0, s, (const char*)shards, stride * esz,
+                       units, (char*)out);
+  else if (bf16)
+    hipLaunchKernelGGL((gather_scalar_kernel<uint16_t>), grid, dim3(256), 0, s,
+                       (const uint16_t*)shards, stride, chunk, (uint16_t*)out);
+  else
+    hipLaunchKernelGGL((gather_scalar_kernel<uint32_t>), grid, dim3(256), 0, s,
+                       (const uint32_t*)shards, stride, chunk, (uint32_t*)out);
+  return hipGetLastError();
 }
 
 // parts: rank r's block at parts + r*stride holds m[n], l[n], T[n] (T is not

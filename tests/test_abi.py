@@ -233,6 +233,25 @@ def test_partial_sum_validation(L):
     assert L.shard_partial_sum(3, 2, 16, 0, 0, FAKE, 48, FAKE, None) == 2   # no op 3
 
 
+def test_sp_validation(L):
+    rs = L.shard_reduce_scatter
+    ag = L.shard_all_gather
+    # (t, rank, s, b, h, in, out, parts, stride, out, stream)
+    assert rs(4, 0, 10, 2, 8, 1, 1, FAKE, 160, FAKE, None) == 1    # s % t
+    assert rs(4, 4, 8, 2, 8, 1, 1, FAKE, 128, FAKE, None) == 1     # rank
+    assert rs(4, 0, 8, 2, 8, 1, 1, FAKE, 100, FAKE, None) == 1     # stride < s*b*h
+    assert rs(4, 0, 8, 2, 8, 5, 1, FAKE, 128, FAKE, None) == 2     # dtype
+    assert rs(4, 0, 8, 2, 8, 0, 1, FAKE + 2, 128, FAKE, None) == 2  # fp32 alignment
+    assert rs(4, 0, 8, 2, 8, 1, 1, None, 128, FAKE, None) == 1
+    assert rs(0, 0, 8, 2, 8, 1, 1, FAKE, 128, FAKE, None) == 1
+    # (t, s, b, h, dtype, shards, stride, out, stream)
+    assert ag(4, 10, 2, 8, 1, FAKE, 40, FAKE, None) == 1           # s % t
+    assert ag(4, 8, 2, 8, 1, FAKE, 31, FAKE, None) == 1            # stride < (s/t)*b*h
+    assert ag(4, 8, 2, 8, 7, FAKE, 32, FAKE, None) == 2
+    assert ag(4, 8, 2, 8, 1, FAKE, 32, None, None) == 1
+    assert ag(4, 8, 2, 8, 1, FAKE + 1, 32, FAKE, None) == 2
+
+
 def test_binding_raises_when_library_missing(tmp_path, monkeypatch):
     from logit_gemm_shard_amd import binding
     monkeypatch.setattr(binding, "_lib", None)

@@ -1,0 +1,90 @@
+"""Parity of the sequence-parallel stand-ins (shard_reduce_scatter,
+shard_all_gather, through the C ABI) with the fp64 oracle ``oracle.sp``.
+
+Both are exact operations here: the reduce-scatter accumulates in fp32 in
+ascending rank order exactly as shard_partial_sum does, so on small-integer
+data both are exact, and on any data the chunk equals the matching rows of
+the all-reduce bit for bit; the all-gather is a copy.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev, f64, step
+from logit_gemm_shard_amd import binding as lgs
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def _ints(shape, seed, dtype):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(-16, 17, shape, generator=g).to(dtype)
+
+
+@pytest.mark.parametrize("din,dout", [(BF16, BF16), (BF16, F32), (F32, F32), (F32, BF16)])
+@pytest.mark.parametrize("shape", [(8, 1024, 8, 3072), (4, 96, 3, 7), (2, 2, 1, 5), (1, 16, 2, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_reduce_scatter_then_all_gather_exact(shape, din, dout):
+    t, s, b, h = shape
+    d = dev()
+    n, c = s * b * h, (s // t) * b * h
+    step(f"sp t={t} s={s} b={b} h={h} {din}->{dout}")
+    parts = _ints((t, s * b, h), t * 31 + h, din)
+    pd = parts.to(d)
+    chunks = torch.empty(t, (s // t) * b, h, dtype=dout, device=d)
+    for r in range(t):
+        lgs.shard_reduce_scatter(t, r, s, b, h, pd, n, chunks[r])
+    full = torch.empty(s * b, h, dtype=dout, device=d)
+    lgs.shard_all_gather(t, s, b, h, chunks, c, full)
+    ar = torch.empty(s * b, h, dtype=dout, device=d)
+    lgs.shard_partial_sum("sum", t, n, pd, n, ar)
+    torch.cuda.synchronize()
+    p64 = [f64(p) for p in parts]
+    for r in range(t):
+        assert np.array_equal(f64(chunks[r]), oracle.sp.reduce_scatter(p64, s, b, t, r)), r
+    assert np.array_equal(f64(full), oracle.sp.all_gather([f64(x) for x in chunks], s, b, t))
+    assert torch.equal(full, ar)
+
+
+def test_reduce_scatter_matches_all_reduce_bits_on_real_data():
+    """Non-integer partials (a row-parallel exit's Z_i): every rank's chunk is
+    bit-identical to its rows of the all-reduce, and the all-gather of the
+    chunks to the whole all-reduce."""
+    t, s, b, h = 8, 512, 2, 1024
+    d = dev()
+    n, c = s * b * h, (s // t) * b * h
+    step("sp reduce-scatter vs all-reduce bits (bf16 partials)")
+    g = torch.Generator().manual_seed(9)
+    stride = n + 64  # padded rank blocks
+    buf = (torch.randn(t, stride, generator=g) * 0.05).to(BF16).to(d)
+    ar = torch.empty(n, dtype=BF16, device=d)
+    lgs.shard_partial_sum("sum", t, n, buf, stride, ar)
+    chunks = torch.empty(t, c, dtype=BF16, device=d)
+    for r in range(t):
+        lgs.shard_reduce_scatter(t, r, s, b, h, buf, stride, chunks[r])
+    full = torch.empty(n, dtype=BF16, device=d)
+    lgs.shard_all_gather(t, s, b, h, chunks, c, full)
+    torch.cuda.synchronize()
+    for r in range(t):
+        assert torch.equal(chunks[r], ar[r * c:(r + 1) * c]), r
+    assert torch.equal(full, ar)
+
+
+def test_all_gather_strided_shards():
+    """Shards with a padded stride (and fp32 with a chunk that is not a
+    multiple of 16 bytes) land in rank order."""
+    d = dev()
+    for t, s, b, h, dt in ((4, 8, 3, 5, F32), (3, 6, 1, 8, BF16), (8, 64, 2, 96, BF16)):
+        step(f"all-gather t={t} s={s} b={b} h={h} {dt}")
+        c = (s // t) * b * h
+        stride = c + 3
+        shards = _ints((t, stride), 7 + h, dt).to(d)
+        out = torch.empty(s * b * h, dtype=dt, device=d)
+        lgs.shard_all_gather(t, s, b, h, shards, stride, out)
+        torch.cuda.synchronize()
+        want = oracle.sp.all_gather([f64(shards[q, :c]).reshape((s // t) * b, h) for q in range(t)], s, b, t)
+        assert np.array_equal(f64(out).reshape(s * b, h), want)
