@@ -14,6 +14,8 @@ equations state:
 * ``oracle.mlp``  -- the GeLU MLP split column-then-row across ``t`` ranks
   (forward, backward and the sum of partials).
 * ``oracle.swiglu`` -- the SwiGLU (gated) MLP block with the same split.
+* ``oracle.attn`` -- the attention block's QKV column-parallel and W_O
+  row-parallel projections (and a plain attention core to check the split).
 * ``oracle.sp`` -- the sequence-parallel reduce-scatter exit and all-gather
   entry that replace the row-parallel all-reduce.
 * ``oracle.xent`` -- full-logit softmax cross-entropy and its vocab-parallel
@@ -26,4 +28,4 @@ finite differences and algebraic identities.  No function here is "parity
 unpinned".
 """
 
-from . import mlp, sp, swiglu, xent  # noqa: F401
+from . import attn, mlp, sp, swiglu, xent  # noqa: F401

@@ -703,6 +703,103 @@ def check_sp_volume(sp):
 SP_CHECKS = [check_sp_reduce_scatter_brute, check_sp_identity, check_sp_volume]
 
 
+# ------------------------------------------------------ attention projections
+
+def check_attn_core_brute(at):
+    """The attention core against loops: every query head's softmax row by
+    math.exp, the scores scaled by 1/sqrt(d), query head k reading KV head
+    k // (n_q / n_kv)."""
+    r_ = _rng(71)
+    M, n_q, n_kv, d = 4, 4, 2, 3
+    QKV = r_.normal(size=(M, (n_q + 2 * n_kv) * d))
+    got = at.attention_core(QKV, n_q, n_kv, d)
+    for k in range(n_q):
+        g = k // (n_q // n_kv)
+        for i in range(M):
+            q = QKV[i, k * d:(k + 1) * d]
+            sc = [sum(q[c] * QKV[j, (n_q + g) * d + c] for c in range(d)) / math.sqrt(d) for j in range(M)]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            tot = sum(e)
+            for c in range(d):
+                want = sum(e[j] / tot * QKV[j, (n_q + n_kv + g) * d + c] for j in range(M))
+                assert abs(got[i, k * d + c] - want) < 1e-13
+
+
+def check_attn_projections_brute(at):
+    """The rank's fused weight holds its heads' columns (by explicit head
+    index loops), and the projections are plain products (brute force)."""
+    r_ = _rng(72)
+    M, h, n_q, n_kv, d, t = 3, 5, 4, 2, 2, 2
+    Wq, Wk, Wv = r_.normal(size=(h, n_q * d)), r_.normal(size=(h, n_kv * d)), r_.normal(size=(h, n_kv * d))
+    Wo = r_.normal(size=(n_q * d, h))
+    X = r_.normal(size=(M, h))
+    for i in range(t):
+        W = at.qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, i)
+        cols = []
+        for k in range(i * n_q // t, (i + 1) * n_q // t):
+            cols += [Wq[:, k * d + c] for c in range(d)]
+        for src in (Wk, Wv):
+            for k in range(i * n_kv // t, (i + 1) * n_kv // t):
+                cols += [src[:, k * d + c] for c in range(d)]
+        assert np.array_equal(W, np.stack(cols, axis=1))
+        assert _rel(at.qkv_forward(X, W), bf_matmul(X.tolist(), W.tolist())) < 1e-14
+        Wo_i = at.out_shard(Wo, n_q, d, t, i)
+        rows = [Wo[k * d + c] for k in range(i * n_q // t, (i + 1) * n_q // t) for c in range(d)]
+        assert np.array_equal(Wo_i, np.stack(rows, axis=0))
+        A = r_.normal(size=(M, n_q // t * d))
+        assert _rel(at.out_forward(A, Wo_i), bf_matmul(A.tolist(), Wo_i.tolist())) < 1e-14
+
+
+def check_attn_split_identity(at):
+    """Each rank's heads attended on their own, then its W_O rows: the sum of
+    the partials equals the unsplit block, for t = 1, 2, 4 with grouped KV
+    heads."""
+    r_ = _rng(73)
+    M, h, n_q, n_kv, d = 6, 16, 8, 4, 4
+    X = r_.normal(size=(M, h))
+    Wq, Wk, Wv = (r_.normal(size=(h, n * d)) * 0.3 for n in (n_q, n_kv, n_kv))
+    Wo = r_.normal(size=(n_q * d, h)) * 0.3
+    full = at.block_forward(X, Wq, Wk, Wv, Wo, n_q, n_kv, d)
+    for t in (1, 2, 4):
+        parts = []
+        for i in range(t):
+            qkv = at.qkv_forward(X, at.qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, i))
+            heads = at.attention_core(qkv, n_q // t, n_kv // t, d)
+            parts.append(at.out_forward(heads, at.out_shard(Wo, n_q, d, t, i)))
+        assert _rel(sum(parts), full) < 1e-13, t
+
+
+def check_attn_backward_fd(at):
+    """Gradients of L = <dY, X Wqkv> and L = <dZ, A Wo> by central
+    differences, every entry."""
+    r_ = _rng(74)
+    X, W, dY = r_.normal(size=(3, 4)), r_.normal(size=(4, 5)), r_.normal(size=(3, 5))
+    g = at.qkv_backward(X, W, dY)
+    A, Wo, dZ = r_.normal(size=(3, 2)), r_.normal(size=(2, 4)), r_.normal(size=(3, 4))
+    go = at.out_backward(A, Wo, dZ)
+    eps = 1e-6
+    for name, P, fwd, args, dd in (("dX", X, at.qkv_forward, (X, W), g["dX"]),
+                                   ("dW", W, at.qkv_forward, (X, W), g["dW"]),
+                                   ("dA", A, at.out_forward, (A, Wo), go["dA"]),
+                                   ("dWo", Wo, at.out_forward, (A, Wo), go["dW"])):
+        up = dY if fwd is at.qkv_forward else dZ
+        fd = np.zeros_like(P)
+        for idx in np.ndindex(P.shape):
+            old = P[idx]
+            P[idx] = old + eps
+            lp = float((fwd(*args) * up).sum())
+            P[idx] = old - eps
+            lm = float((fwd(*args) * up).sum())
+            P[idx] = old
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert _rel(dd, fd) < 1e-8, name
+
+
+ATTN_CHECKS = [check_attn_core_brute, check_attn_projections_brute, check_attn_split_identity,
+               check_attn_backward_fd]
+
+
 MLP_CHECKS = [check_gelu_table, check_gelu_shape, check_gelu_grad_fd, check_mlp_hand_example,
               check_mlp_brute_force, check_split_identity, check_partial_sum_exact,
               check_backward_fd, check_backward_directional, check_backward_shards]

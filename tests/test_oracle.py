@@ -29,3 +29,8 @@ def test_xent_backward_oracle(check):
 @pytest.mark.parametrize("check", pins.SP_CHECKS, ids=lambda f: f.__name__)
 def test_sp_oracle(check):
     check(oracle.sp)
+
+
+@pytest.mark.parametrize("check", pins.ATTN_CHECKS, ids=lambda f: f.__name__)
+def test_attn_oracle(check):
+    check(oracle.attn)

@@ -410,3 +410,79 @@ def test_sp_mutant_is_caught(name, monkeypatch):
     attr, fn = SP_MUTANTS[name]
     monkeypatch.setattr(sp, attr, fn)
     assert _caught(pins.SP_CHECKS, sp), f"no pin caught the planted mistake {name}"
+
+
+# ---------------------------------------------------- attention projections
+
+at = oracle.attn
+_REAL_QKV_SHARD, _REAL_OUT_SHARD, _REAL_CORE = at.qkv_shard, at.out_shard, at.attention_core
+_REAL_QKV_BWD, _REAL_OUT_BWD = at.qkv_backward, at.out_backward
+
+
+def _qkv_shard_k_from_q(Wq, Wk, Wv, n_q, n_kv, d, t, i):
+    return _REAL_QKV_SHARD(Wq, Wq[:, :Wk.shape[1]], Wv, n_q, n_kv, d, t, i)
+
+
+def _qkv_shard_kv_not_split(Wq, Wk, Wv, n_q, n_kv, d, t, i):
+    return _REAL_QKV_SHARD(Wq, Wk, Wv, n_q, n_kv, d, t, 0) if i else _REAL_QKV_SHARD(Wq, Wk, Wv, n_q, n_kv, d, t, i)
+
+
+def _out_shard_next_rank(Wo, n_q, d, t, i):
+    return _REAL_OUT_SHARD(Wo, n_q, d, t, (i + 1) % t)
+
+
+def _core_kv_interleaved(QKV, n_q, n_kv, d):
+    # query head k reading KV head k % n_kv instead of k // (n_q / n_kv)
+    QKV = np.asarray(QKV, dtype=np.float64)
+    Q, K, V = QKV[:, :n_q * d], QKV[:, n_q * d:(n_q + n_kv) * d], QKV[:, (n_q + n_kv) * d:]
+    out = np.empty((QKV.shape[0], n_q * d))
+    for k in range(n_q):
+        g = k % n_kv
+        a = Q[:, k * d:(k + 1) * d] @ K[:, g * d:(g + 1) * d].T / np.sqrt(d)
+        a = np.exp(a - a.max(axis=1)[:, None])
+        a /= a.sum(axis=1)[:, None]
+        out[:, k * d:(k + 1) * d] = a @ V[:, g * d:(g + 1) * d]
+    return out
+
+
+def _core_no_scale(QKV, n_q, n_kv, d):
+    return _REAL_CORE(np.asarray(QKV, dtype=np.float64) * np.concatenate(
+        [np.full(n_q * d, np.sqrt(np.sqrt(d))), np.full(n_kv * d, np.sqrt(np.sqrt(d))), np.ones(n_kv * d)]),
+        n_q, n_kv, d)
+
+
+def _qkv_bwd_dx_scaled(X, W, dY):
+    g = _REAL_QKV_BWD(X, W, dY)
+    g["dX"] = g["dX"] * (1 + 1e-3)  # a stray factor
+    return g
+
+
+def _qkv_bwd_dw_of_dx(X, W, dY):
+    g = _REAL_QKV_BWD(X, W, dY)
+    g["dW"] = np.asarray(dY, dtype=np.float64).T @ np.asarray(X, dtype=np.float64)  # transposed product
+    return g
+
+
+def _out_bwd_dw_swapped(A, Wo, dZ):
+    g = _REAL_OUT_BWD(A, Wo, dZ)
+    g["dW"] = np.asarray(A, dtype=np.float64).T @ np.asarray(dZ, dtype=np.float64)[::-1]
+    return g
+
+
+ATTN_MUTANTS = {
+    "qkv_shard_k_from_q": ("qkv_shard", _qkv_shard_k_from_q),
+    "qkv_shard_kv_not_split": ("qkv_shard", _qkv_shard_kv_not_split),
+    "out_shard_next_rank": ("out_shard", _out_shard_next_rank),
+    "core_kv_interleaved": ("attention_core", _core_kv_interleaved),
+    "core_no_scale": ("attention_core", _core_no_scale),
+    "qkv_bwd_dx_scaled": ("qkv_backward", _qkv_bwd_dx_scaled),
+    "qkv_bwd_dw_transposed": ("qkv_backward", _qkv_bwd_dw_of_dx),
+    "out_bwd_dw_rows_swapped": ("out_backward", _out_bwd_dw_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attn_mutant_is_caught(name, monkeypatch):
+    attr, fn = ATTN_MUTANTS[name]
+    monkeypatch.setattr(at, attr, fn)
+    assert _caught(pins.ATTN_CHECKS, at), f"no pin caught the planted mistake {name}"
