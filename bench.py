@@ -250,6 +250,43 @@ def per_config(torch, lgs, reps):
         X, Wgu, Wd = sets[i % 3]
         lgs.tp_swiglu_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, Wgu, Wd, GU, dZs[i % 3], dX, dWgu, dWd, workspace=ws)
     out["swiglu_70b_bwd"] = _timed_report(torch, sbwd, 12 * w.M * w.h * f, reps)
+    del sets, dZs, dX, dWgu, dWd, ws, GU, Y, Z
+
+    # 70B-shape attention projections of one rank (8 query heads, 1 KV head of
+    # 128): forward = QKV (2 M h (q + 2 kv)) + W_O (2 M q h); backward = their
+    # input and weight gradients (twice that).
+    w = WORKLOADS["attn_70b"]
+    q, kv = w.n_heads // w.t * w.head_dim, w.n_kv_heads // w.t * w.head_dim
+    nqkv = q + 2 * kv
+    sets = []
+    for _ in range(3):
+        X = torch.randn(w.M, w.h, device=dev).to(bf)
+        Wqkv = torch.randn(w.h, nqkv, device=dev).mul_(0.02).to(bf)
+        Wo = torch.randn(q, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
+        A = torch.randn(w.M, q, device=dev).to(bf)
+        dZ = torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf)
+        dQ = torch.randn(w.M, nqkv, device=dev).mul_(w.dz_std).to(bf)
+        sets.append((X, Wqkv, Wo, A, dZ, dQ))
+    QKV = torch.empty(w.M, nqkv, dtype=bf, device=dev)
+    Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
+    dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
+    dW = torch.empty(w.h, nqkv, dtype=bf, device=dev)
+    dA = torch.empty(w.M, q, dtype=bf, device=dev)
+    dWo = torch.empty(q, w.h, dtype=bf, device=dev)
+    a = (w.b, w.s, w.h)
+
+    def afwd(i):
+        X, Wqkv, Wo, A, _, _ = sets[i % 3]
+        lgs.tp_attn_qkv_fwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, QKV)
+        lgs.tp_attn_out_fwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, Z)
+
+    def abwd(i):
+        X, Wqkv, Wo, A, dZ, dQ = sets[i % 3]
+        lgs.tp_attn_qkv_bwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, dQ, dX, dW)
+        lgs.tp_attn_out_bwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, dZ, dA, dWo)
+    fl = 2 * w.M * w.h * (nqkv + q)
+    out["attn_70b_fwd"] = _timed_report(torch, afwd, fl, reps)
+    out["attn_70b_bwd"] = _timed_report(torch, abwd, 2 * fl, reps)
     return out
 
 

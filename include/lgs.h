@@ -277,6 +277,45 @@ int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dtype, con
                       int64_t part_stride, void* out, void* stream);
 
 /*
+ * Attention projections of one rank ("Mathematical Foundations of
+ * Megatron-LM", "Self-Attention Layer Decomposition"; the mohashari.github.io
+ * 70B page, "The Multi-Head Attention Block"): W_Q, W_K, W_V are split by
+ * columns so rank i holds whole heads, n_q/t query heads and n_kv/t key/value
+ * heads of head_dim d (grouped-query attention: query head k uses KV head
+ * k / (n_q/n_kv)); W_O is split by rows so rank i's product is a partial
+ * (Z = sum_i Z_i, one all-reduce; on one device shard_partial_sum).  The
+ * attention core on the rank's heads runs between the two projections and is
+ * not part of this library.  With q = (n_q/t) d and kv = (n_kv/t) d:
+ *
+ *   tp_attn_qkv_fwd: QKV_i = X Wqkv_i                      [M, q + 2 kv]
+ *   tp_attn_qkv_bwd: dX_i = dQKV_i Wqkv_i^T (a partial)    [M, h]
+ *                    dWqkv_i = X^T dQKV_i                  [h, q + 2 kv]
+ *   tp_attn_out_fwd: Z_i = A_i Wo_i (a partial)            [M, h]
+ *   tp_attn_out_bwd: dA_i = dZ Wo_i^T, dWo_i = A_i^T dZ    [M, q], [q, h]
+ *
+ * X [M, h]; Wqkv_i [h, q + 2 kv] = [W_Q^i | W_K^i | W_V^i], the rank's heads'
+ * columns side by side (head k of Q in columns [k d, (k+1) d) of W_Q);
+ * QKV_i and dQKV_i [M, q + 2 kv] in the same order; A_i [M, q] the rank's
+ * heads' outputs side by side; Wo_i [q, h] rows [i q, (i+1) q) of W_O.  Every
+ * matrix row-major with its ld.  dtype must be LGS_BF16; h and head_dim
+ * multiples of 8; n_q and n_kv divisible by t, n_q by n_kv.  No workspace.
+ */
+int tp_attn_qkv_fwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
+                    int rank, int dtype, const void* X, int64_t ldx, const void* Wqkv_i,
+                    int64_t ldw, void* QKV_i, int64_t ldqkv, void* stream);
+int tp_attn_qkv_bwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
+                    int rank, int dtype, const void* X, int64_t ldx, const void* Wqkv_i,
+                    int64_t ldw, const void* dQKV_i, int64_t lddqkv, void* dX_i, int64_t lddx,
+                    void* dWqkv_i, int64_t lddw, void* stream);
+int tp_attn_out_fwd(int b, int s, int h, int n_q_heads, int head_dim, int t, int rank, int dtype,
+                    const void* A_i, int64_t lda, const void* Wo_i, int64_t ldwo, void* Z_i,
+                    int64_t ldz, void* stream);
+int tp_attn_out_bwd(int b, int s, int h, int n_q_heads, int head_dim, int t, int rank, int dtype,
+                    const void* A_i, int64_t lda, const void* Wo_i, int64_t ldwo, const void* dZ,
+                    int64_t lddz, void* dA_i, int64_t ldda, void* dWo_i, int64_t lddwo,
+                    void* stream);
+
+/*
  * shard_reduce_scatter / shard_all_gather -- one-device stand-ins for the
  * sequence-parallel exit and entry ("Mathematical Foundations of Megatron-LM",
  * "Sequence Parallelism", "Splitting All-Reduce into Reduce-Scatter and

@@ -50,6 +50,12 @@ SIGNATURES = [
     ("vocab_parallel_xent_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
                                      _p, _i64, _p, _i64, _p, _sz, _p]),
     ("shard_partial_sum", _i, [_i, _i, _i64, _i, _i, _p, _i64, _p, _p]),
+    ("tp_attn_qkv_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
+    ("tp_attn_qkv_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                             _p, _i64, _p]),
+    ("tp_attn_out_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
+    ("tp_attn_out_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                             _p, _i64, _p]),
     ("shard_reduce_scatter", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _p]),
     ("shard_all_gather", _i, [_i, _i, _i, _i, _i, _p, _i64, _p, _p]),
     # include/lgs_testing.h
@@ -260,6 +266,42 @@ def shard_partial_sum(op, t, n, parts, part_stride, out, stream=None):
     _check(L.shard_partial_sum(opc, t, n, _dtype(parts), _dtype(out), parts.data_ptr(), part_stride,
                                out.data_ptr(), _stream(stream)))
     return out
+
+
+def tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, rank, X, Wqkv_i, QKV_i, stream=None):
+    """QKV_i = X [W_Q^i | W_K^i | W_V^i] (rank's heads)."""
+    args = []
+    for m in (X, Wqkv_i, QKV_i):
+        args.extend(_mat(m))
+    _check(lib().tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, rank, _dtype(X), *args, _stream(stream)))
+    return QKV_i
+
+
+def tp_attn_qkv_bwd(b, s, h, n_q, n_kv, d, t, rank, X, Wqkv_i, dQKV_i, dX_i, dWqkv_i, stream=None):
+    """dX_i = dQKV_i Wqkv_i^T (a partial), dWqkv_i = X^T dQKV_i."""
+    args = []
+    for m in (X, Wqkv_i, dQKV_i, dX_i, dWqkv_i):
+        args.extend(_mat(m))
+    _check(lib().tp_attn_qkv_bwd(b, s, h, n_q, n_kv, d, t, rank, _dtype(X), *args, _stream(stream)))
+    return dX_i, dWqkv_i
+
+
+def tp_attn_out_fwd(b, s, h, n_q, d, t, rank, A_i, Wo_i, Z_i, stream=None):
+    """The partial Z_i = A_i W_O^i."""
+    args = []
+    for m in (A_i, Wo_i, Z_i):
+        args.extend(_mat(m))
+    _check(lib().tp_attn_out_fwd(b, s, h, n_q, d, t, rank, _dtype(A_i), *args, _stream(stream)))
+    return Z_i
+
+
+def tp_attn_out_bwd(b, s, h, n_q, d, t, rank, A_i, Wo_i, dZ, dA_i, dWo_i, stream=None):
+    """dA_i = dZ W_O^i^T, dWo_i = A_i^T dZ."""
+    args = []
+    for m in (A_i, Wo_i, dZ, dA_i, dWo_i):
+        args.extend(_mat(m))
+    _check(lib().tp_attn_out_bwd(b, s, h, n_q, d, t, rank, _dtype(A_i), *args, _stream(stream)))
+    return dA_i, dWo_i
 
 
 def shard_reduce_scatter(t, rank, s, b, h, parts, part_stride, out, stream=None):

@@ -7,6 +7,10 @@ dmarx anthology, "Key takeaways"), and a 70B dense decoder with hidden size
 8,192 at sequence length 4,096 and micro-batch 1 ("Megatron-LM, in depth",
 aicassindra, "Worked example: 70B parameters on 512 GPUs").
 
+The attention projections are those of Llama-3-70B as that page gives them
+("The Multi-Head Attention Block"): 64 query heads and 8 key/value heads, 8
+and 1 per rank at t = 8, head size 8,192 / 64 = 128.
+
 The gated (SwiGLU) MLP block is that of Llama-3-70B, hidden size 8,192, as the
 mohashari.github.io page on tensor parallelism for fine-tuning 70B models with
 Megatron-LM describes it ("The MLP Block"; sequence length 4,096 and batch
@@ -25,7 +29,7 @@ from dataclasses import dataclass, field
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp_fwd" | "mlp_bwd" | "xent" | "swiglu_fwd" | "swiglu_bwd"
+    kind: str            # "mlp_fwd" | "mlp_bwd" | "xent" | "swiglu_fwd" | "swiglu_bwd" | "attn"
     b: int
     s: int
     h: int
@@ -37,6 +41,9 @@ class Workload:
     n_blocks: int = 0    # N of the 1/sqrt(2N) residual scaling
     dz_seed: int = 0     # backward: seed of the incoming gradient
     dz_std: float = 0.0  # backward: its standard deviation
+    n_heads: int = 0     # attention: query heads (all ranks)
+    n_kv_heads: int = 0  # attention: key/value heads (all ranks)
+    head_dim: int = 0
     note: str = field(default="", compare=False)
 
     @property
@@ -76,5 +83,9 @@ WORKLOADS = {
         Workload("swiglu_70b_bwd", "swiglu_bwd", b=1, s=4096, h=8192, t=8, dtype="bf16", seed=6,
                  ffn=28672, n_blocks=160, dz_seed=7, dz_std=0.01,
                  note="70B-shape SwiGLU MLP shard backward, one rank of t=8"),
+        Workload("attn_70b", "attn", b=1, s=4096, h=8192, t=8, dtype="bf16", seed=8, n_blocks=160,
+                 n_heads=64, n_kv_heads=8, head_dim=128, dz_seed=9, dz_std=0.01,
+                 note="70B-shape attention projections (QKV column-parallel, W_O row-parallel), "
+                      "one rank of t=8, forward and backward"),
     ]
 }

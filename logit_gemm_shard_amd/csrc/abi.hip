@@ -421,6 +421,97 @@ LGS_API int shard_all_gather(int t, int s, int b, int h, int dtype, const void* 
                                   (hipStream_t)stream));
 }
 
+namespace {
+
+// Shape rules of the attention projections; sets the per-rank widths.
+int check_attn(int b, int s, int h, int n_q, int n_kv, int d, int t, int rank, int dtype, int* nqkv,
+               int* hq) {
+  int st = check_bst(b, s, h, t, rank);
+  if (st) return st;
+  if (n_q <= 0 || n_kv <= 0 || d <= 0)
+    return fail(LGS_ERR_INVALID_ARG, "head counts and head_dim must be positive");
+  if (n_q % t != 0 || n_kv % t != 0)
+    return fail(LGS_ERR_INVALID_ARG, "n_q_heads=%d and n_kv_heads=%d must divide by t=%d", n_q, n_kv, t);
+  if (n_q % n_kv != 0)
+    return fail(LGS_ERR_INVALID_ARG, "n_q_heads=%d must be a multiple of n_kv_heads=%d", n_q, n_kv);
+  if (dtype != LGS_BF16) return fail(LGS_ERR_UNSUPPORTED, "the attention projections take bf16 only");
+  if (h % 8 != 0 || d % 8 != 0)
+    return fail(LGS_ERR_UNSUPPORTED, "h=%d and head_dim=%d must be multiples of 8", h, d);
+  const int64_t q = (int64_t)(n_q / t) * d, kv = (int64_t)(n_kv / t) * d;
+  if (q + 2 * kv > INT_MAX) return fail(LGS_ERR_INVALID_ARG, "per-rank projection width overflows");
+  *nqkv = (int)(q + 2 * kv);
+  *hq = (int)q;
+  return LGS_OK;
+}
+
+}  // namespace
+
+LGS_API int tp_attn_qkv_fwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
+                            int rank, int dtype, const void* X, int64_t ldx, const void* Wqkv_i,
+                            int64_t ldw, void* QKV_i, int64_t ldqkv, void* stream) {
+  int nqkv, hq;
+  int st = check_attn(b, s, h, n_q_heads, n_kv_heads, head_dim, t, rank, dtype, &nqkv, &hq);
+  if (st) return st;
+  const int M = b * s;
+  if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("Wqkv_i", Wqkv_i, h, ldw, nqkv, dtype, true))) return st;
+  if ((st = check_mat("QKV_i", QKV_i, M, ldqkv, nqkv, dtype, true))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::attn_qkv_fwd(M, h, nqkv, X, ldx, Wqkv_i, ldw, QKV_i, ldqkv, (hipStream_t)stream));
+}
+
+LGS_API int tp_attn_qkv_bwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
+                            int rank, int dtype, const void* X, int64_t ldx, const void* Wqkv_i,
+                            int64_t ldw, const void* dQKV_i, int64_t lddqkv, void* dX_i, int64_t lddx,
+                            void* dWqkv_i, int64_t lddw, void* stream) {
+  int nqkv, hq;
+  int st = check_attn(b, s, h, n_q_heads, n_kv_heads, head_dim, t, rank, dtype, &nqkv, &hq);
+  if (st) return st;
+  const int M = b * s;
+  if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("Wqkv_i", Wqkv_i, h, ldw, nqkv, dtype, true))) return st;
+  if ((st = check_mat("dQKV_i", dQKV_i, M, lddqkv, nqkv, dtype, true))) return st;
+  if ((st = check_mat("dX_i", dX_i, M, lddx, h, dtype, true))) return st;
+  if ((st = check_mat("dWqkv_i", dWqkv_i, h, lddw, nqkv, dtype, true))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::attn_qkv_bwd(M, h, nqkv, X, ldx, Wqkv_i, ldw, dQKV_i, lddqkv, dX_i, lddx,
+                                    dWqkv_i, lddw, (hipStream_t)stream));
+}
+
+LGS_API int tp_attn_out_fwd(int b, int s, int h, int n_q_heads, int head_dim, int t, int rank,
+                            int dtype, const void* A_i, int64_t lda, const void* Wo_i, int64_t ldwo,
+                            void* Z_i, int64_t ldz, void* stream) {
+  int nqkv, hq;
+  // (the output projection involves no KV heads: check the query heads only)
+  int st = check_attn(b, s, h, n_q_heads, n_q_heads, head_dim, t, rank, dtype, &nqkv, &hq);
+  if (st) return st;
+  const int M = b * s;
+  if ((st = check_mat("A_i", A_i, M, lda, hq, dtype, true))) return st;
+  if ((st = check_mat("Wo_i", Wo_i, hq, ldwo, h, dtype, true))) return st;
+  if ((st = check_mat("Z_i", Z_i, M, ldz, h, dtype, true))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::attn_out_fwd(M, hq, h, A_i, lda, Wo_i, ldwo, Z_i, ldz, (hipStream_t)stream));
+}
+
+LGS_API int tp_attn_out_bwd(int b, int s, int h, int n_q_heads, int head_dim, int t, int rank,
+                            int dtype, const void* A_i, int64_t lda, const void* Wo_i, int64_t ldwo,
+                            const void* dZ, int64_t lddz, void* dA_i, int64_t ldda, void* dWo_i,
+                            int64_t lddwo, void* stream) {
+  int nqkv, hq;
+  // (the output projection involves no KV heads: check the query heads only)
+  int st = check_attn(b, s, h, n_q_heads, n_q_heads, head_dim, t, rank, dtype, &nqkv, &hq);
+  if (st) return st;
+  const int M = b * s;
+  if ((st = check_mat("A_i", A_i, M, lda, hq, dtype, true))) return st;
+  if ((st = check_mat("Wo_i", Wo_i, hq, ldwo, h, dtype, true))) return st;
+  if ((st = check_mat("dZ", dZ, M, lddz, h, dtype, true))) return st;
+  if ((st = check_mat("dA_i", dA_i, M, ldda, hq, dtype, true))) return st;
+  if ((st = check_mat("dWo_i", dWo_i, hq, lddwo, h, dtype, true))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::attn_out_bwd(M, hq, h, A_i, lda, Wo_i, ldwo, dZ, lddz, dA_i, ldda, dWo_i,
+                                    lddwo, (hipStream_t)stream));
+}
+
 LGS_API int lgs_test_num_tiles(void) { return lgs::num_tiles(); }
 
 LGS_API int lgs_test_tile_shape(int tile, int* bm, int* bn) {

@@ -1,0 +1,79 @@
+// One rank's attention projections under tensor parallelism.
+//
+// "Mathematical Foundations of Megatron-LM ..." (llms.blog), "Self-Attention
+// Layer Decomposition", and the mohashari.github.io 70B page, "The
+// Multi-Head Attention Block": Q, K and V are split by columns so rank i
+// holds whole heads (n_q/t query and n_kv/t key/value heads), and the output
+// projection W_O by rows so rank i's product is a partial that one
+// all-reduce sums.  The attention core between the two runs on the rank's
+// own heads and is not part of this library.
+//
+// Products (row-major operands, explicit leading dimensions):
+//   QKV_i = X W_qkv,i     [M, nqkv]   X K-contiguous, W N-contiguous
+//   Z_i   = A_i W_O,i     [M, h]      A_i K-contiguous, W_O,i N-contiguous
+//   dX_i  = dQKV_i W_qkv,i^T [M, h]   both K-contiguous (K = nqkv)
+//   dW_qkv,i = X^T dQKV_i [h, nqkv]   X M-contiguous (K = tokens), dQKV N-contiguous
+//   dA_i  = dZ W_O,i^T    [M, hq]     both K-contiguous (K = h)
+//   dW_O,i = A_i^T dZ     [hq, h]     A_i M-contiguous, dZ N-contiguous
+// Each backward runs its two products in one grouped launch, the longer K
+// first.
+#include "dispatch.hpp"
+#include "epilogues.hpp"
+#include "internal.hpp"
+
+namespace lgs {
+
+namespace {
+
+// C1 = A1 B1 (K-major A, K-major B: the input gradient) and C2 = A2^T B2
+// (M-major A, N-major B: the weight gradient) in one launch.
+hipError_t input_and_weight_grads(const bf16* a1, int64_t lda1, const bf16* b1, int64_t ldb1, int M1,
+                                  int N1, int K1, const EpiStore<bf16>& e1, const bf16* a2, int64_t lda2,
+                                  const bf16* b2, int64_t ldb2, int M2, int N2, int K2,
+                                  const EpiStore<bf16>& e2, hipStream_t s) {
+  const bool big = M1 >= 256 && N1 >= 256 && M2 >= 256 && N2 >= 256;
+  if (big) {
+    const auto p1 = pp_problem<256, 256, true, true>(a1, lda1, b1, ldb1, M1, N1, K1, e1);
+    const auto p2 = pp_problem<256, 256, false, false>(a2, lda2, b2, ldb2, M2, N2, K2, e2);
+    return K2 >= K1 ? launch_gemm_pp_group2(p2, p1, s) : launch_gemm_pp_group2(p1, p2, s);
+  }
+  const auto p1 = pp_problem<128, 128, true, true>(a1, lda1, b1, ldb1, M1, N1, K1, e1);
+  const auto p2 = pp_problem<128, 128, false, false>(a2, lda2, b2, ldb2, M2, N2, K2, e2);
+  return K2 >= K1 ? launch_gemm_pp_group2(p2, p1, s) : launch_gemm_pp_group2(p1, p2, s);
+}
+
+}  // namespace
+
+hipError_t attn_qkv_fwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
+                        int64_t ldw, void* QKV, int64_t ldqkv, hipStream_t s) {
+  const EpiStore<bf16> e{(bf16*)QKV, ldqkv, M, nqkv};
+  return gemm_bf16<true, false>(pick_tile(M, nqkv), (const bf16*)X, ldx, (const bf16*)W, ldw, M, nqkv,
+                                h, e, s);
+}
+
+hipError_t attn_out_fwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,
+                        int64_t ldwo, void* Z, int64_t ldz, hipStream_t s) {
+  const EpiStore<bf16> e{(bf16*)Z, ldz, M, h};
+  return gemm_bf16<true, false>(pick_tile(M, h), (const bf16*)A, lda, (const bf16*)Wo, ldwo, M, h, hq,
+                                e, s);
+}
+
+hipError_t attn_qkv_bwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
+                        int64_t ldw, const void* dQKV, int64_t lddqkv, void* dX, int64_t lddx,
+                        void* dW, int64_t lddw, hipStream_t s) {
+  return input_and_weight_grads((const bf16*)dQKV, lddqkv, (const bf16*)W, ldw, M, h, nqkv,
+                                EpiStore<bf16>{(bf16*)dX, lddx, M, h}, (const bf16*)X, ldx,
+                                (const bf16*)dQKV, lddqkv, h, nqkv, M,
+                                EpiStore<bf16>{(bf16*)dW, lddw, h, nqkv}, s);
+}
+
+hipError_t attn_out_bwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,
+                        int64_t ldwo, const void* dZ, int64_t lddz, void* dA, int64_t ldda,
+                        void* dWo, int64_t lddwo, hipStream_t s) {
+  return input_and_weight_grads((const bf16*)dZ, lddz, (const bf16*)Wo, ldwo, M, hq, h,
+                                EpiStore<bf16>{(bf16*)dA, ldda, M, hq}, (const bf16*)A, lda,
+                                (const bf16*)dZ, lddz, hq, h, M,
+                                EpiStore<bf16>{(bf16*)dWo, lddwo, hq, h}, s);
+}
+
+}  // namespace lgs

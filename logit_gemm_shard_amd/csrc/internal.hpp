@@ -35,6 +35,19 @@ hipError_t swiglu_bwd(int M, int h, int f, const void* X, int64_t ldx, const voi
                       int64_t lddwgu, void* dWd, int64_t lddwd, void* Yws, void* dGUws,
                       hipStream_t s);
 
+// One rank's attention projections (bf16): nqkv = (n_q + 2 n_kv) d / t
+// columns of [Q | K | V], hq = n_q d / t columns of the heads' outputs.
+hipError_t attn_qkv_fwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
+                        int64_t ldw, void* QKV, int64_t ldqkv, hipStream_t s);
+hipError_t attn_out_fwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,
+                        int64_t ldwo, void* Z, int64_t ldz, hipStream_t s);
+hipError_t attn_qkv_bwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
+                        int64_t ldw, const void* dQKV, int64_t lddqkv, void* dX, int64_t lddx,
+                        void* dW, int64_t lddw, hipStream_t s);
+hipError_t attn_out_bwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,
+                        int64_t ldwo, const void* dZ, int64_t lddz, void* dA, int64_t ldda,
+                        void* dWo, int64_t lddwo, hipStream_t s);
+
 // Fused logit GEMM + CE partials for one vocabulary slice of Vr rows.
 size_t xent_scratch_bytes(int M, int Vr);
 hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_t ldh,

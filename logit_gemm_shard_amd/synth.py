@@ -68,6 +68,28 @@ def gate_up_shard(Wg, Wu, t, r):
     return torch.cat([Wg[:, r * f:(r + 1) * f], Wu[:, r * f:(r + 1) * f]], dim=1).contiguous()
 
 
+def attn_weights(w, dtype=None):
+    """X [M, h], W_Q [h, n_q d], W_K, W_V [h, n_kv d], W_O [n_q d, h] for an
+    attention workload (draw order X, W_Q, W_K, W_V, W_O; W_O is the weight
+    before the residual)."""
+    dt = dtype or w.dtype
+    g = _gen(w.seed)
+    X = normal((w.M, w.h), 1.0, g, dt)
+    Wq = normal((w.h, w.n_heads * w.head_dim), 0.02, g, dt)
+    Wk = normal((w.h, w.n_kv_heads * w.head_dim), 0.02, g, dt)
+    Wv = normal((w.h, w.n_kv_heads * w.head_dim), 0.02, g, dt)
+    Wo = normal((w.n_heads * w.head_dim, w.h), residual_std(w.n_blocks), g, dt)
+    return X, Wq, Wk, Wv, Wo
+
+
+def qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, r):
+    """Rank r's heads' columns of W_Q, W_K, W_V side by side (a copy in the
+    layout the library takes; no arithmetic)."""
+    q, kv = n_q // t * d, n_kv // t * d
+    return torch.cat([Wq[:, r * q:(r + 1) * q], Wk[:, r * kv:(r + 1) * kv], Wv[:, r * kv:(r + 1) * kv]],
+                     dim=1).contiguous()
+
+
 def mlp_grad(w, dtype=None):
     """The incoming gradient dZ [M, h] of a backward workload."""
     return normal((w.M, w.h), w.dz_std, _gen(w.dz_seed), dtype or w.dtype)

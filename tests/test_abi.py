@@ -233,6 +233,29 @@ def test_partial_sum_validation(L):
     assert L.shard_partial_sum(3, 2, 16, 0, 0, FAKE, 48, FAKE, None) == 2   # no op 3
 
 
+def test_attn_validation(L):
+    def qf(**kw):
+        a = dict(b=1, s=16, h=64, nq=8, nkv=4, d=8, t=2, rank=0, dtype=1, X=FAKE, ldx=64, W=FAKE,
+                 ldw=64, Y=FAKE, ldy=64)  # q = 4*8 = 32, kv = 2*8 = 16: 64 columns
+        a.update(kw)
+        return L.tp_attn_qkv_fwd(a["b"], a["s"], a["h"], a["nq"], a["nkv"], a["d"], a["t"], a["rank"],
+                                 a["dtype"], a["X"], a["ldx"], a["W"], a["ldw"], a["Y"], a["ldy"], None)
+    assert qf(nq=7) == 1                    # n_q % t
+    assert qf(nkv=3, t=1) == 1              # n_q % n_kv
+    assert qf(nkv=1) == 1                   # n_kv % t
+    assert qf(d=12) == 2                    # head_dim % 8
+    assert qf(dtype=0) == 2
+    assert qf(ldw=48) == 1 and qf(ldy=56) == 1  # widths q + 2 kv = 64
+    assert qf(rank=2) == 1
+    of = lambda **kw: L.tp_attn_out_fwd(1, 16, 64, kw.get("nq", 8), 8, 2, kw.get("rank", 0), 1, FAKE,
+                                        kw.get("lda", 32), FAKE, 64, FAKE, 64, None)
+    assert of(nq=7) == 1 and of(lda=24) == 1 and of(rank=5) == 1  # n_q % t, lda < q = 32, rank
+    ob = L.tp_attn_out_bwd(1, 16, 64, 8, 8, 2, 0, 1, FAKE, 32, FAKE, 64, FAKE, 64, None, 32, FAKE, 64, None)
+    assert ob == 1                          # dA_i required
+    qb = L.tp_attn_qkv_bwd(1, 16, 64, 8, 4, 8, 2, 0, 1, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 32, None)
+    assert qb == 1                          # lddw < q + 2 kv
+
+
 def test_sp_validation(L):
     rs = L.shard_reduce_scatter
     ag = L.shard_all_gather

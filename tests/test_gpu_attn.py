@@ -1,0 +1,150 @@
+"""Parity of the attention projections under TP (tp_attn_qkv_fwd / _bwd,
+tp_attn_out_fwd / _bwd, through the C ABI) with the fp64 oracle
+``oracle.attn``.
+
+Ragged multi-tile shapes compare every element.  The split identity runs on
+the device: each rank's heads' outputs (the oracle's attention core on the
+oracle's projections, rounded to bf16: the core is not part of the library)
+go through the rank's output projection, and the on-device sum of the
+partials equals the oracle's unsplit block.  The 70B-shape rank (8 query
+heads and 1 KV head of 128) is compared on sampled rows and columns.
+Tolerance: max|gpu - ref| / max|ref| <= 2e-2 per output (bf16 in and out,
+fp32 accumulation).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close, dev, f64, round_like, step
+from logit_gemm_shard_amd import binding as lgs
+from logit_gemm_shard_amd import synth
+from logit_gemm_shard_amd.configs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+BF16 = torch.bfloat16
+at = oracle.attn
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+RAGGED = [  # (b, s, h, n_q, n_kv, d, t)
+    (1, 300, 136, 8, 4, 16, 2),
+    (2, 130, 264, 12, 4, 24, 4),
+    (1, 520, 1032, 16, 8, 64, 8),
+    (1, 700, 512, 8, 8, 128, 2),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_attn_projections_ragged(shape):
+    b, s, h, n_q, n_kv, d, t = shape
+    M = b * s
+    q, kv = n_q // t * d, n_kv // t * d
+    dev_ = dev()
+    X, Wq, Wk, Wv, Wo, A, dZ, dQ = synth.small(
+        3 + h, (M, h), (h, n_q * d), (h, n_kv * d), (h, n_kv * d), (n_q * d, h), (M, q), (M, h), (M, q + 2 * kv),
+        dtype="bf16")
+    Wq, Wk, Wv, Wo = ((w.float() * 0.05).to(BF16) for w in (Wq, Wk, Wv, Wo))
+    X64 = f64(X)
+    Xd = X.to(dev_)
+    for r in sorted({0, t - 1}):
+        step(f"attn projections {shape} rank={r}")
+        W = synth.qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, r)
+        W64 = at.qkv_shard(f64(Wq), f64(Wk), f64(Wv), n_q, n_kv, d, t, r)
+        assert np.array_equal(f64(W), W64)  # the host-side layout copy matches the oracle's shard
+        Wo_r = Wo[r * q:(r + 1) * q].contiguous()
+        Wd, Wod = W.to(dev_), Wo_r.to(dev_)
+        QKV = torch.empty(M, q + 2 * kv, dtype=BF16, device=dev_)
+        lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, QKV)
+        Z = torch.empty(M, h, dtype=BF16, device=dev_)
+        lgs.tp_attn_out_fwd(b, s, h, n_q, d, t, r, A.to(dev_), Wod, Z)
+        dX = torch.empty(M, h, dtype=BF16, device=dev_)
+        dW = torch.empty(h, q + 2 * kv, dtype=BF16, device=dev_)
+        lgs.tp_attn_qkv_bwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, dQ.to(dev_), dX, dW)
+        dA = torch.empty(M, q, dtype=BF16, device=dev_)
+        dWo = torch.empty(q, h, dtype=BF16, device=dev_)
+        lgs.tp_attn_out_bwd(b, s, h, n_q, d, t, r, A.to(dev_), Wod, dZ.to(dev_), dA, dWo)
+        sync()
+        assert_close("QKV_i", QKV, at.qkv_forward(X64, W64), BF16)
+        assert_close("Z_i", Z, at.out_forward(f64(A), f64(Wo_r)), BF16)
+        g = at.qkv_backward(X64, W64, f64(dQ))
+        assert_close("dX_i", dX, g["dX"], BF16)
+        assert_close("dWqkv_i", dW, g["dW"], BF16)
+        g = at.out_backward(f64(A), f64(Wo_r), f64(dZ))
+        assert_close("dA_i", dA, g["dA"], BF16)
+        assert_close("dWo_i", dWo, g["dW"], BF16)
+
+
+def test_attn_split_identity_on_device():
+    """sum over ranks of (rank's heads attended) W_O^i == the unsplit block."""
+    b, s, h, n_q, n_kv, d, t = 1, 96, 256, 8, 4, 32, 4
+    M, q = b * s, n_q // 4 * d
+    dev_ = dev()
+    X, Wq, Wk, Wv, Wo = synth.small(12, (M, h), (h, n_q * d), (h, n_kv * d), (h, n_kv * d), (n_q * d, h),
+                                    dtype="bf16")
+    Wq, Wk, Wv, Wo = ((w.float() * 0.05).to(BF16) for w in (Wq, Wk, Wv, Wo))
+    X64, Wq64, Wk64, Wv64, Wo64 = f64(X), f64(Wq), f64(Wk), f64(Wv), f64(Wo)
+    parts = torch.empty(t, M, h, dtype=BF16, device=dev_)
+    step("attn: every rank's output projection of its own heads + on-device sum")
+    for r in range(t):
+        heads = at.attention_core(at.qkv_forward(X64, at.qkv_shard(Wq64, Wk64, Wv64, n_q, n_kv, d, t, r)),
+                                  n_q // t, n_kv // t, d)
+        lgs.tp_attn_out_fwd(b, s, h, n_q, d, t, r, round_like(heads, BF16).to(dev_),
+                            Wo[r * q:(r + 1) * q].contiguous().to(dev_), parts[r])
+    Z = torch.empty(M, h, dtype=BF16, device=dev_)
+    lgs.shard_partial_sum("sum", t, M * h, parts, M * h, Z)
+    sync()
+    assert_close("sum_i Z_i vs unsplit attention block", Z,
+                 at.block_forward(X64, Wq64, Wk64, Wv64, Wo64, n_q, n_kv, d), BF16)
+
+
+def _rows(M, n=24, seed=0):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], g.choice(M, n, replace=False)]))
+
+
+def test_attn_70b_sampled():
+    w = WORKLOADS["attn_70b"]
+    b, s, h, n_q, n_kv, d, t = w.b, w.s, w.h, w.n_heads, w.n_kv_heads, w.head_dim, w.t
+    M, q, kv = w.M, n_q // t * d, n_kv // t * d
+    dev_ = dev()
+    X, Wq, Wk, Wv, Wo = synth.attn_weights(w)
+    g = torch.Generator().manual_seed(w.dz_seed)
+    A = synth.normal((M, q), 1.0, g, "bf16")
+    dZ = synth.normal((M, h), w.dz_std, g, "bf16")
+    dQ = synth.normal((M, q + 2 * kv), w.dz_std, g, "bf16")
+    X64 = f64(X)
+    for r in (0, t - 1):
+        step(f"attn_70b: rank {r} projections, forward and backward, at full size")
+        W = synth.qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, r)
+        Wo_r = Wo[r * q:(r + 1) * q].contiguous()
+        Xd, Wd, Wod, Ad = X.to(dev_), W.to(dev_), Wo_r.to(dev_), A.to(dev_)
+        QKV = torch.empty(M, q + 2 * kv, dtype=BF16, device=dev_)
+        lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, QKV)
+        Z = torch.empty(M, h, dtype=BF16, device=dev_)
+        lgs.tp_attn_out_fwd(b, s, h, n_q, d, t, r, Ad, Wod, Z)
+        dX = torch.empty(M, h, dtype=BF16, device=dev_)
+        dW = torch.empty(h, q + 2 * kv, dtype=BF16, device=dev_)
+        lgs.tp_attn_qkv_bwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, dQ.to(dev_), dX, dW)
+        dA = torch.empty(M, q, dtype=BF16, device=dev_)
+        dWo = torch.empty(q, h, dtype=BF16, device=dev_)
+        lgs.tp_attn_out_bwd(b, s, h, n_q, d, t, r, Ad, Wod, dZ.to(dev_), dA, dWo)
+        sync()
+        W64 = at.qkv_shard(f64(Wq), f64(Wk), f64(Wv), n_q, n_kv, d, t, r)
+        rows = _rows(M, 24, r)
+        assert_close(f"QKV_{r} rows", QKV.cpu()[rows], at.qkv_forward(X64[rows], W64), BF16)
+        assert_close(f"Z_{r} rows", Z.cpu()[rows], at.out_forward(f64(A[rows]), f64(Wo_r)), BF16)
+        assert_close(f"dX_{r} rows", dX.cpu()[rows], at.qkv_backward(X64[rows], W64, f64(dQ[rows]))["dX"], BF16)
+        assert_close(f"dA_{r} rows", dA.cpu()[rows], at.out_backward(f64(A[rows]), f64(Wo_r), f64(dZ[rows]))["dA"],
+                     BF16)
+        hs, cs = _rows(h, 24, 5), _rows(q + 2 * kv, 24, 6)
+        assert_close(f"dWqkv_{r} block", dW.cpu()[hs][:, cs],
+                     at.qkv_backward(X64[:, hs], W64[np.ix_(hs, cs)], f64(dQ)[:, cs])["dW"], BF16)
+        qs = _rows(q, 24, 7)
+        assert_close(f"dWo_{r} rows", dWo.cpu()[qs], at.out_backward(f64(A)[:, qs], f64(Wo_r)[qs], f64(dZ))["dW"],
+                     BF16)
