@@ -51,6 +51,44 @@ inline TileId pick_tile(int M, int N, unsigned allowed = kAllTiles) {
   return best;
 }
 
+inline double tile_cost(TileId t, int M, int N) {
+  constexpr int kCUs = 256;
+  const TileShape& s = kTileShapes[t];
+  const long tiles = (long)((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+  return (double)((tiles + kCUs - 1) / kCUs) * s.bm * s.bn / s.eff;
+}
+
+// A launch plan over columns: the picked tile on columns [0, c1), then (if
+// c1 < N) a second launch with another tile on [c1, N).  Splitting pays when
+// the picked tile leaves a partly filled last round that smaller tiles on the
+// remaining columns fill: e.g. 8192 x 6400 is 640 blocks of 256x320 (2.5
+// rounds, cost 3), but 512 of them on the first 5120 columns (2 full rounds)
+// and 256 blocks of 256x160 on the last 1280 (one round of half-size tiles)
+// cost about 2.7.  Both launches' tiles must share `wn` (the caller's slab
+// numbering) when the caller needs it; `same_wn` enforces that.
+struct ColumnPlan {
+  TileId main;
+  int c1;  // columns of the first launch (a multiple of its tile width), N if not split
+  TileId tail;
+};
+
+inline ColumnPlan plan_columns(int M, int N, bool same_wn) {
+  const TileId t = pick_tile(M, N);
+  ColumnPlan best{t, N, t};
+  double best_cost = tile_cost(t, M, N);
+  const int bn = kTileShapes[t].bn;
+  for (int c1 = bn; c1 < N; c1 += bn)
+    for (int u = 0; u < kNumTiles; ++u) {
+      if (same_wn && kTileShapes[u].wn != kTileShapes[t].wn) continue;
+      const double c = tile_cost(t, M, c1) + tile_cost((TileId)u, M, N - c1);
+      if (c < best_cost * 0.97) {  // a second launch costs a few microseconds
+        best_cost = c;
+        best = ColumnPlan{t, c1, (TileId)u};
+      }
+    }
+  return best;
+}
+
 inline int tile_bn(TileId t) { return kTileShapes[t].bn; }
 inline int tile_wn(TileId t) { return kTileShapes[t].wn; }
 

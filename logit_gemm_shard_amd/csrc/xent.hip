@@ -72,19 +72,30 @@ __global__ __launch_bounds__(256) void xent_merge_kernel(XentSlabs s, int nslabs
 hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_t ldh,
                     const void* E, int64_t lde, const int32_t* targets, float* m_r, float* l_r,
                     float* t_r, int32_t* argmax_r, float* loss, void* scratch, hipStream_t s) {
-  const TileId tile = pick_tile(M, Vr);
-  const int WN = tile_wn(tile);
+  // The slice's columns in one launch, or two (plan_columns) whose tiles
+  // share the wave width, so that the slabs number consecutively.
+  const ColumnPlan plan = plan_columns(M, Vr, true);
+  const int WN = tile_wn(plan.main);
   const size_t slab_elems = (size_t)max_slabs(Vr) * M;
   XentSlabs sl;
   sl.m = (float*)scratch;
   sl.l = sl.m + slab_elems;
   sl.t = sl.l + slab_elems;
   sl.idx = argmax_r ? (int32_t*)(sl.t + slab_elems) : nullptr;  // argmax only when asked for
-  EpiXent epi{sl, targets, vocab_start, M, Vr, WN};
-  hipError_t e = gemm_bf16<true, true>(tile, (const bf16*)H, ldh, (const bf16*)E, lde, M, Vr, h,
-                                       epi, s);
-  if (e != hipSuccess) return e;
-  const int nslabs = (Vr + WN - 1) / WN;
+  const bf16 *hh = (const bf16*)H, *e = (const bf16*)E;
+  const EpiXent e1{sl, targets, vocab_start, M, plan.c1, WN, 0, 0};
+  hipError_t err = gemm_bf16<true, true>(plan.main, hh, ldh, e, lde, M, plan.c1, h, e1, s);
+  if (err != hipSuccess) return err;
+  int nslabs = plan.c1 / WN;
+  if (plan.c1 < Vr) {
+    const int rest = Vr - plan.c1;
+    const EpiXent e2{sl, targets, vocab_start + plan.c1, M, rest, WN, plan.c1, nslabs};
+    err = gemm_bf16<true, true>(plan.tail, hh, ldh, e + (int64_t)plan.c1 * lde, lde, M, rest, h, e2, s);
+    if (err != hipSuccess) return err;
+    nslabs += (rest + WN - 1) / WN;
+  } else {
+    nslabs = (Vr + WN - 1) / WN;
+  }
   hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 63) / 64), dim3(256), 0, s, sl, nslabs, M,
                      vocab_start, m_r, l_r, t_r, argmax_r, loss);
   return hipGetLastError();

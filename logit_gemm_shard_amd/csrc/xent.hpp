@@ -22,13 +22,17 @@ struct XentSlabs {
   int32_t* idx;  // [slabs][M] slice-local column of the slab's first maximum (may be null)
 };
 
+// One launch covers columns [col0, col0 + N) of the rank's slice (the whole
+// slice, or one of the column ranges a launch plan splits it into); its
+// slabs are numbered from slab0.
 struct EpiXent {
   static constexpr bool kDirect = true;
   XentSlabs s;
   const int32_t* targets;  // [M] global vocabulary ids
-  int vocab_start;         // first global id of this rank's slice
-  int M, N;                // tokens, slice width
-  int WN;                  // wave tile width: slab = wave column
+  int vocab_start;         // global id of this launch's column 0 (slice start + col0)
+  int M, N;                // tokens, columns of this launch
+  int WN;                  // wave tile width: slab = slab0 + wave column
+  int col0, slab0;         // slice-local column of this launch's column 0; its first slab
 
   // Reduces the wave's logit tile straight from the accumulators.  In the
   // 32x32 MFMA output layout lane l holds, for row 32i + l%32 of the wave
@@ -37,9 +41,9 @@ struct EpiXent {
   // reduces its half and the pair combines through one lane exchange.
   template <int TM, int TN, int WNt>
   __device__ __forceinline__ void direct(f32x16 (&acc)[TM][TN], int mb, int nb, int lane) const {
-    const int cb = nb + 4 * (lane >> 5);  // slice-local column of acc[.][0][0]
+    const int cb = nb + 4 * (lane >> 5);  // this launch's column of acc[.][0][0]
     if (N - nb < WNt) {
-      // Last wave column of the slice: columns past its end become -inf,
+      // Last wave column of the launch: columns past its end become -inf,
       // which neither wins the max nor adds to the sum.
       const int left = N - cb;
 #pragma unroll
@@ -57,7 +61,7 @@ struct EpiXent {
   template <int TN>
   __device__ __forceinline__ void row_tile(const f32x16 (&a)[TN], int m, int nb, int cb,
                                            int lane) const {
-    int tl = -0x40000000;  // target column relative to cb; far below 0 if not in the slice
+    int tl = -0x40000000;  // target column relative to cb; far below 0 if not in this launch
     if (m < M) {
       const int tg = targets[m] - vocab_start;
       if (tg >= 0 && tg < N) tl = tg - cb;
@@ -98,11 +102,11 @@ struct EpiXent {
           for (int r = 15; r >= 0; --r)
             bc = a[j][r] == best ? 32 * j + 8 * (r >> 2) + (r & 3) : bc;
       }
-      bi = bc < 0 ? 0x7fffffff : cb + bc;
+      bi = bc < 0 ? 0x7fffffff : col0 + cb + bc;  // slice-local column
       bi = min(bi, __shfl_xor(bi, 32));
     }
     if (lane < 32 && m < M) {
-      const int64_t o = (int64_t)(nb / WN) * M + m;
+      const int64_t o = (int64_t)(slab0 + nb / WN) * M + m;
       s.m[o] = best;
       s.l[o] = sum;
       s.t[o] = tv;

@@ -68,9 +68,18 @@ hipError_t xent_bwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
                     void* scratch, hipStream_t s) {
   const bf16 *hh = (const bf16*)H, *e = (const bf16*)E;
   bf16* g = (bf16*)scratch;  // G [M, Vr], dense
-  const EpiXentGrad eg{g, Vr, lse, dloss, targets, vocab_start, M, Vr};
-  hipError_t err = gemm_bf16<true, true>(pick_tile(M, Vr), hh, ldh, e, lde, M, Vr, h, eg, s);
+  // The slice's columns in one launch or two (plan_columns): the second
+  // covers columns [c1, Vr) with its own tile, writing G from column c1.
+  const ColumnPlan plan = plan_columns(M, Vr, false);
+  const EpiXentGrad eg{g, Vr, lse, dloss, targets, vocab_start, M, plan.c1};
+  hipError_t err = gemm_bf16<true, true>(plan.main, hh, ldh, e, lde, M, plan.c1, h, eg, s);
   if (err != hipSuccess) return err;
+  if (plan.c1 < Vr) {
+    const EpiXentGrad et{g + plan.c1, Vr, lse, dloss, targets, vocab_start + plan.c1, M, Vr - plan.c1};
+    err = gemm_bf16<true, true>(plan.tail, hh, ldh, e + (int64_t)plan.c1 * lde, lde, M, Vr - plan.c1, h,
+                                et, s);
+    if (err != hipSuccess) return err;
+  }
   // dE_r reduces over the M tokens, dH_r over the slice's Vr entries: the
   // longer K first.
   const EpiStore<bf16> ee{(bf16*)dE, ldde, Vr, h};
