@@ -274,16 +274,21 @@ def per_config(torch, lgs, reps):
     dA = torch.empty(w.M, q, dtype=bf, device=dev)
     dWo = torch.empty(q, w.h, dtype=bf, device=dev)
     a = (w.b, w.s, w.h)
+    ws_qkv = torch.empty(max(1, lgs.attn_qkv_fwd_workspace_bytes(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t)),
+                         dtype=torch.uint8, device=dev)
 
     def afwd(i):
         X, Wqkv, Wo, A, _, _ = sets[i % 3]
-        lgs.tp_attn_qkv_fwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, QKV)
+        lgs.tp_attn_qkv_fwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, QKV, workspace=ws_qkv)
         lgs.tp_attn_out_fwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, Z)
+
+    ws_ob = torch.empty(max(1, lgs.attn_out_bwd_workspace_bytes(*a, w.n_heads, w.head_dim, w.t)),
+                        dtype=torch.uint8, device=dev)
 
     def abwd(i):
         X, Wqkv, Wo, A, dZ, dQ = sets[i % 3]
         lgs.tp_attn_qkv_bwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, dQ, dX, dW)
-        lgs.tp_attn_out_bwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, dZ, dA, dWo)
+        lgs.tp_attn_out_bwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, dZ, dA, dWo, workspace=ws_ob)
     fl = 2 * w.M * w.h * (nqkv + q)
     out["attn_70b_fwd"] = _timed_report(torch, afwd, fl, reps)
     out["attn_70b_bwd"] = _timed_report(torch, abwd, 2 * fl, reps)

@@ -298,11 +298,24 @@ int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dtype, con
  * QKV_i and dQKV_i [M, q + 2 kv] in the same order; A_i [M, q] the rank's
  * heads' outputs side by side; Wo_i [q, h] rows [i q, (i+1) q) of W_O.  Every
  * matrix row-major with its ld.  dtype must be LGS_BF16; h and head_dim
- * multiples of 8; n_q and n_kv divisible by t, n_q by n_kv.  No workspace.
+ * multiples of 8; n_q and n_kv divisible by t, n_q by n_kv.
+ *
+ * Workspace (tp_attn_qkv_fwd and tp_attn_out_bwd, optional): when the
+ * rank's QKV product, or the dA_i product of the output projection's
+ * backward, has few output tiles and a long K (= h), a workspace of the
+ * queried size (256-byte aligned) lets it run split over K (fp32 partials,
+ * then summed into the bf16 output); NULL, or a smaller one, runs it unsplit
+ * with the same result up to fp32 summation order.  The queries return 0 when
+ * no split applies.  tp_attn_qkv_bwd and tp_attn_out_fwd take none.
  */
+size_t lgs_attn_qkv_fwd_workspace_bytes(int b, int s, int h, int n_q_heads, int n_kv_heads,
+                                        int head_dim, int t, int dtype);
+size_t lgs_attn_out_bwd_workspace_bytes(int b, int s, int h, int n_q_heads, int head_dim, int t,
+                                        int dtype);
 int tp_attn_qkv_fwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
                     int rank, int dtype, const void* X, int64_t ldx, const void* Wqkv_i,
-                    int64_t ldw, void* QKV_i, int64_t ldqkv, void* stream);
+                    int64_t ldw, void* QKV_i, int64_t ldqkv, void* workspace,
+                    size_t workspace_bytes, void* stream);
 int tp_attn_qkv_bwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
                     int rank, int dtype, const void* X, int64_t ldx, const void* Wqkv_i,
                     int64_t ldw, const void* dQKV_i, int64_t lddqkv, void* dX_i, int64_t lddx,
@@ -313,7 +326,7 @@ int tp_attn_out_fwd(int b, int s, int h, int n_q_heads, int head_dim, int t, int
 int tp_attn_out_bwd(int b, int s, int h, int n_q_heads, int head_dim, int t, int rank, int dtype,
                     const void* A_i, int64_t lda, const void* Wo_i, int64_t ldwo, const void* dZ,
                     int64_t lddz, void* dA_i, int64_t ldda, void* dWo_i, int64_t lddwo,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * shard_reduce_scatter / shard_all_gather -- one-device stand-ins for the

@@ -50,12 +50,15 @@ SIGNATURES = [
     ("vocab_parallel_xent_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
                                      _p, _i64, _p, _i64, _p, _sz, _p]),
     ("shard_partial_sum", _i, [_i, _i, _i64, _i, _i, _p, _i64, _p, _p]),
-    ("tp_attn_qkv_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
+    ("lgs_attn_qkv_fwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    ("tp_attn_qkv_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _sz,
+                             _p]),
     ("tp_attn_qkv_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                              _p, _i64, _p]),
     ("tp_attn_out_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
+    ("lgs_attn_out_bwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i, _i]),
     ("tp_attn_out_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
-                             _p, _i64, _p]),
+                             _p, _i64, _p, _sz, _p]),
     ("shard_reduce_scatter", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _p]),
     ("shard_all_gather", _i, [_i, _i, _i, _i, _i, _p, _i64, _p, _p]),
     # include/lgs_testing.h
@@ -268,12 +271,23 @@ def shard_partial_sum(op, t, n, parts, part_stride, out, stream=None):
     return out
 
 
-def tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, rank, X, Wqkv_i, QKV_i, stream=None):
-    """QKV_i = X [W_Q^i | W_K^i | W_V^i] (rank's heads)."""
+def attn_qkv_fwd_workspace_bytes(b, s, h, n_q, n_kv, d, t, dtype=torch.bfloat16):
+    return lib().lgs_attn_qkv_fwd_workspace_bytes(b, s, h, n_q, n_kv, d, t, _DT[dtype])
+
+
+def tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, rank, X, Wqkv_i, QKV_i, workspace=None, split=True,
+                    stream=None):
+    """QKV_i = X [W_Q^i | W_K^i | W_V^i] (rank's heads).  With split=False no
+    workspace is passed (the product runs unsplit)."""
+    L = lib()
+    dt = _dtype(X)
+    need = L.lgs_attn_qkv_fwd_workspace_bytes(b, s, h, n_q, n_kv, d, t, dt) if split else 0
+    ws, ws_bytes = _workspace(need, X.device, workspace)
     args = []
     for m in (X, Wqkv_i, QKV_i):
         args.extend(_mat(m))
-    _check(lib().tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, rank, _dtype(X), *args, _stream(stream)))
+    _check(L.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, rank, dt, *args,
+                             _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes, _stream(stream)))
     return QKV_i
 
 
@@ -295,12 +309,23 @@ def tp_attn_out_fwd(b, s, h, n_q, d, t, rank, A_i, Wo_i, Z_i, stream=None):
     return Z_i
 
 
-def tp_attn_out_bwd(b, s, h, n_q, d, t, rank, A_i, Wo_i, dZ, dA_i, dWo_i, stream=None):
-    """dA_i = dZ W_O^i^T, dWo_i = A_i^T dZ."""
+def attn_out_bwd_workspace_bytes(b, s, h, n_q, d, t, dtype=torch.bfloat16):
+    return lib().lgs_attn_out_bwd_workspace_bytes(b, s, h, n_q, d, t, _DT[dtype])
+
+
+def tp_attn_out_bwd(b, s, h, n_q, d, t, rank, A_i, Wo_i, dZ, dA_i, dWo_i, workspace=None, split=True,
+                    stream=None):
+    """dA_i = dZ W_O^i^T, dWo_i = A_i^T dZ.  With split=False no workspace is
+    passed (dA_i runs unsplit)."""
+    L = lib()
+    dt = _dtype(A_i)
+    need = L.lgs_attn_out_bwd_workspace_bytes(b, s, h, n_q, d, t, dt) if split else 0
+    ws, ws_bytes = _workspace(need, A_i.device, workspace)
     args = []
     for m in (A_i, Wo_i, dZ, dA_i, dWo_i):
         args.extend(_mat(m))
-    _check(lib().tp_attn_out_bwd(b, s, h, n_q, d, t, rank, _dtype(A_i), *args, _stream(stream)))
+    _check(L.tp_attn_out_bwd(b, s, h, n_q, d, t, rank, dt, *args,
+                             _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes, _stream(stream)))
     return dA_i, dWo_i
 
 

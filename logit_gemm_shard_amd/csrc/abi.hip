@@ -446,9 +446,20 @@ int check_attn(int b, int s, int h, int n_q, int n_kv, int d, int t, int rank, i
 
 }  // namespace
 
+LGS_API size_t lgs_attn_qkv_fwd_workspace_bytes(int b, int s, int h, int n_q_heads, int n_kv_heads,
+                                               int head_dim, int t, int dtype) {
+  int nqkv, hq;
+  if (check_attn(b, s, h, n_q_heads, n_kv_heads, head_dim, t, 0, dtype, &nqkv, &hq)) {
+    g_err[0] = 0;  // a query, not a failed call
+    return 0;
+  }
+  return round256(lgs::attn_qkv_scratch_bytes(b * s, h, nqkv));
+}
+
 LGS_API int tp_attn_qkv_fwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
                             int rank, int dtype, const void* X, int64_t ldx, const void* Wqkv_i,
-                            int64_t ldw, void* QKV_i, int64_t ldqkv, void* stream) {
+                            int64_t ldw, void* QKV_i, int64_t ldqkv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   int nqkv, hq;
   int st = check_attn(b, s, h, n_q_heads, n_kv_heads, head_dim, t, rank, dtype, &nqkv, &hq);
   if (st) return st;
@@ -456,8 +467,15 @@ LGS_API int tp_attn_qkv_fwd(int b, int s, int h, int n_q_heads, int n_kv_heads, 
   if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
   if ((st = check_mat("Wqkv_i", Wqkv_i, h, ldw, nqkv, dtype, true))) return st;
   if ((st = check_mat("QKV_i", QKV_i, M, ldqkv, nqkv, dtype, true))) return st;
+  // The workspace is optional: given (at least the queried size, 256-byte
+  // aligned) it enables the split-K schedule, else the product runs unsplit.
+  const size_t need = lgs::attn_qkv_scratch_bytes(M, h, nqkv);
+  if (workspace && !aligned(workspace, 256))
+    return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  void* scratch = (need && workspace && workspace_bytes >= need) ? workspace : nullptr;
   (void)hipGetLastError();
-  return launched(lgs::attn_qkv_fwd(M, h, nqkv, X, ldx, Wqkv_i, ldw, QKV_i, ldqkv, (hipStream_t)stream));
+  return launched(lgs::attn_qkv_fwd(M, h, nqkv, X, ldx, Wqkv_i, ldw, QKV_i, ldqkv, scratch,
+                                    (hipStream_t)stream));
 }
 
 LGS_API int tp_attn_qkv_bwd(int b, int s, int h, int n_q_heads, int n_kv_heads, int head_dim, int t,
@@ -493,10 +511,20 @@ LGS_API int tp_attn_out_fwd(int b, int s, int h, int n_q_heads, int head_dim, in
   return launched(lgs::attn_out_fwd(M, hq, h, A_i, lda, Wo_i, ldwo, Z_i, ldz, (hipStream_t)stream));
 }
 
+LGS_API size_t lgs_attn_out_bwd_workspace_bytes(int b, int s, int h, int n_q_heads, int head_dim,
+                                               int t, int dtype) {
+  int nqkv, hq;
+  if (check_attn(b, s, h, n_q_heads, n_q_heads, head_dim, t, 0, dtype, &nqkv, &hq)) {
+    g_err[0] = 0;  // a query, not a failed call
+    return 0;
+  }
+  return round256(lgs::attn_out_bwd_scratch_bytes(b * s, hq, h));
+}
+
 LGS_API int tp_attn_out_bwd(int b, int s, int h, int n_q_heads, int head_dim, int t, int rank,
                             int dtype, const void* A_i, int64_t lda, const void* Wo_i, int64_t ldwo,
                             const void* dZ, int64_t lddz, void* dA_i, int64_t ldda, void* dWo_i,
-                            int64_t lddwo, void* stream) {
+                            int64_t lddwo, void* workspace, size_t workspace_bytes, void* stream) {
   int nqkv, hq;
   // (the output projection involves no KV heads: check the query heads only)
   int st = check_attn(b, s, h, n_q_heads, n_q_heads, head_dim, t, rank, dtype, &nqkv, &hq);
@@ -507,9 +535,13 @@ LGS_API int tp_attn_out_bwd(int b, int s, int h, int n_q_heads, int head_dim, in
   if ((st = check_mat("dZ", dZ, M, lddz, h, dtype, true))) return st;
   if ((st = check_mat("dA_i", dA_i, M, ldda, hq, dtype, true))) return st;
   if ((st = check_mat("dWo_i", dWo_i, hq, lddwo, h, dtype, true))) return st;
+  const size_t need = lgs::attn_out_bwd_scratch_bytes(M, hq, h);
+  if (workspace && !aligned(workspace, 256))
+    return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  void* scratch = (need && workspace && workspace_bytes >= need) ? workspace : nullptr;
   (void)hipGetLastError();
   return launched(lgs::attn_out_bwd(M, hq, h, A_i, lda, Wo_i, ldwo, dZ, lddz, dA_i, ldda, dWo_i,
-                                    lddwo, (hipStream_t)stream));
+                                    lddwo, scratch, (hipStream_t)stream));
 }
 
 LGS_API int lgs_test_num_tiles(void) { return lgs::num_tiles(); }

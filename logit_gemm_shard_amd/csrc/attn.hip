@@ -25,6 +25,8 @@ namespace lgs {
 
 namespace {
 
+constexpr int kCUs = 256;
+
 // C1 = A1 B1 (K-major A, K-major B: the input gradient) and C2 = A2^T B2
 // (M-major A, N-major B: the weight gradient) in one launch.
 hipError_t input_and_weight_grads(const bf16* a1, int64_t lda1, const bf16* b1, int64_t ldb1, int M1,
@@ -44,8 +46,41 @@ hipError_t input_and_weight_grads(const bf16* a1, int64_t lda1, const bf16* b1, 
 
 }  // namespace
 
+// The QKV product is skinny (at the 70B shape 4096 x 1280 outputs: 80 tiles of
+// 256x256 for 256 compute units) and deep (K = h = 8192).  Split-K fills the
+// chip: S slices of K, each an ordinary GEMM writing an fp32 partial, then
+// one pass sums the slices into bf16.  Used when the unsplit tiles would
+// occupy at most half of the compute units and K is long enough for the
+// slices to stay efficient.
+namespace {
+int qkv_kchunk(int h, int splits) { return ((h + splits - 1) / splits + 31) / 32 * 32; }
+}  // namespace
+
+int attn_qkv_splits(int M, int h, int nqkv) {
+  if (M < 256 || nqkv < 256 || h < 2048) return 0;
+  const int tiles = ((M + 255) / 256) * ((nqkv + 255) / 256);
+  if (tiles > kCUs / 2) return 0;
+  int splits = kCUs / tiles < 4 ? kCUs / tiles : 4;
+  splits = (h + qkv_kchunk(h, splits) - 1) / qkv_kchunk(h, splits);
+  return splits >= 2 ? splits : 0;
+}
+
+size_t attn_qkv_scratch_bytes(int M, int h, int nqkv) {
+  return (size_t)attn_qkv_splits(M, h, nqkv) * (size_t)M * (size_t)nqkv * 4u;
+}
+
 hipError_t attn_qkv_fwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
-                        int64_t ldw, void* QKV, int64_t ldqkv, hipStream_t s) {
+                        int64_t ldw, void* QKV, int64_t ldqkv, void* scratch, hipStream_t s) {
+  const int splits = attn_qkv_splits(M, h, nqkv);
+  if (splits && scratch) {
+    float* part = (float*)scratch;
+    const EpiPartialF32 e{part, nqkv, (int64_t)M * nqkv, M, nqkv};
+    const hipError_t err = launch_gemm_pp_splitk(
+        pp_problem<256, 256, true, false>((const bf16*)X, ldx, (const bf16*)W, ldw, M, nqkv, h, e), splits,
+        qkv_kchunk(h, splits), s);
+    if (err != hipSuccess) return err;
+    return splitk_sum(part, splits, M, nqkv, QKV, ldqkv, s);
+  }
   const EpiStore<bf16> e{(bf16*)QKV, ldqkv, M, nqkv};
   return gemm_bf16<true, false>(pick_tile(M, nqkv), (const bf16*)X, ldx, (const bf16*)W, ldw, M, nqkv,
                                 h, e, s);
@@ -67,9 +102,42 @@ hipError_t attn_qkv_bwd(int M, int h, int nqkv, const void* X, int64_t ldx, cons
                                 EpiStore<bf16>{(bf16*)dW, lddw, h, nqkv}, s);
 }
 
+// The output projection's backward at the 70B shape: dA (4096 x 1024, K =
+// h = 8192) is 64 tiles and dW_O (1024 x 8192, K = 4096) 128, so one grouped
+// launch leaves a quarter of the chip idle while the dA tiles, twice as long,
+// finish.  Splitting dA's K in two makes 256 tiles of equal length: both
+// halves write fp32 partials, summed into dA afterwards.
+bool attn_out_bwd_split(int M, int hq, int h) {
+  if (M < 256 || hq < 256 || h < 4096 || h % 64 != 0) return false;
+  const int ta = ((M + 255) / 256) * ((hq + 255) / 256);
+  const int tw = ((hq + 255) / 256) * ((h + 255) / 256);
+  return 2 * ta + tw <= kCUs && ta + tw < kCUs;
+}
+
+size_t attn_out_bwd_scratch_bytes(int M, int hq, int h) {
+  return attn_out_bwd_split(M, hq, h) ? 2 * (size_t)M * (size_t)hq * 4u : 0;
+}
+
 hipError_t attn_out_bwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,
                         int64_t ldwo, const void* dZ, int64_t lddz, void* dA, int64_t ldda,
-                        void* dWo, int64_t lddwo, hipStream_t s) {
+                        void* dWo, int64_t lddwo, void* scratch, hipStream_t s) {
+  if (scratch && attn_out_bwd_split(M, hq, h)) {
+    // dA = dZ W_O^T over K = h in two halves (both operands K-contiguous, so a
+    // half is the operands moved by h/2 columns), and dW_O = A^T dZ.
+    float* part = (float*)scratch;
+    const int half = h / 2;
+    const EpiPartialF32 e0{part, hq, (int64_t)M * hq, M, hq};
+    const EpiPartialF32 e1{part + (int64_t)M * hq, hq, (int64_t)M * hq, M, hq};
+    const bf16 *dz = (const bf16*)dZ, *wo = (const bf16*)Wo;
+    const hipError_t err = launch_gemm_pp_group3(
+        pp_problem<256, 256, true, true>(dz, lddz, wo, ldwo, M, hq, half, e0),
+        pp_problem<256, 256, true, true>(dz + half, lddz, wo + half, ldwo, M, hq, h - half, e1),
+        pp_problem<256, 256, false, false>((const bf16*)A, lda, dz, lddz, hq, h, M,
+                                           EpiStore<bf16>{(bf16*)dWo, lddwo, hq, h}),
+        s);
+    if (err != hipSuccess) return err;
+    return splitk_sum(part, 2, M, hq, dA, ldda, s);
+  }
   return input_and_weight_grads((const bf16*)dZ, lddz, (const bf16*)Wo, ldwo, M, hq, h,
                                 EpiStore<bf16>{(bf16*)dA, ldda, M, hq}, (const bf16*)A, lda,
                                 (const bf16*)dZ, lddz, hq, h, M,

@@ -286,6 +286,36 @@ void gemm_pp_group3_kernel(P0 p0, P1 p1, P2 p2) {
   }
 }
 
+// Split-K: block b works on tile b % tiles over K range
+// [s * kchunk, min(K, (s + 1) * kchunk)), s = b / tiles, with the epilogue's
+// `split(s)` (e.g. a partial-sum slice per s).  kchunk is a multiple of the
+// 32-wide K tile; the operands move to the range's start (K-contiguous A by
+// elements, N-contiguous B by rows), so each range is an ordinary GEMM.
+template <class P>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_splitk_kernel(P p, int kchunk) {
+  static_assert(P::AK && !P::BK, "split-K is built for K-contiguous A and N-contiguous B");
+  __shared__ __attribute__((aligned(1024))) char smem[P::T::kLdsBytes];
+  const int tiles = p.tiles();
+  const int s = blockIdx.x / tiles, b = blockIdx.x - s * tiles;
+  P q = p;
+  const int k0 = s * kchunk;
+  q.A = p.A + k0;
+  q.B = p.B + (int64_t)k0 * p.ldb;
+  q.K = min(kchunk, p.K - k0);
+  q.epi = p.epi.split(s);
+  int tmi, tni;
+  tile_of_block(b, tiles, q.tiles_m(), q.tiles_n(), tmi, tni);
+  gemm_tile_pp(q, smem, tmi, tni);
+}
+
+template <class P>
+inline hipError_t launch_gemm_pp_splitk(const P& p, int splits, int kchunk, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_pp_splitk_kernel<P>), dim3(p.tiles() * splits), dim3(kPPThreads), 0, stream, p,
+                     kchunk);
+  return hipGetLastError();
+}
+
 // Two independent GEMMs in one launch (p0 first).
 template <class P0, class P1>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))

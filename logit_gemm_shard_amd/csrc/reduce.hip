@@ -175,6 +175,37 @@ hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64
   return hipGetLastError();
 }
 
+// out[m, n] = bf16(sum_s W[s][m][n]) for a split-K GEMM's fp32 partials
+// (W rows of pitch N, slices of M*N), 8 columns per thread; N % 8 == 0.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ W, int splits, int M,
+                                                         int N, bf16* __restrict__ out, int64_t ldo) {
+  const int64_t n8 = N / 8, total = (int64_t)M * n8;
+  const int64_t slice = (int64_t)M * N;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += step) {
+    const int64_t m = i / n8, c = (i - m * n8) * 8;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* p = W + sp * slice + m * N + c;
+      const u32x4 lo = ld_nt(p), hi = ld_nt(p + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] += __uint_as_float(lo[e]);
+        a[4 + e] += __uint_as_float(hi[e]);
+      }
+    }
+    Vec8<bf16>::store(out + m * ldo + c, a);
+  }
+}
+
+hipError_t splitk_sum(const float* W, int splits, int M, int N, void* out, int64_t ldo, hipStream_t s) {
+  const int64_t total = (int64_t)M * (N / 8);
+  const int64_t want = (total + 255) / 256;
+  const int blocks = (int)(want < 4096 ? (want < 1 ? 1 : want) : 4096);
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, W, splits, M, N, (bf16*)out, ldo);
+  return hipGetLastError();
+}
+
 // parts: rank r's block at parts + r*stride holds m[n], l[n], T[n] (T is not
 // read for the log-sum-exp alone).
 __global__ __launch_bounds__(256) void xent_combine_kernel(const float* __restrict__ parts,

@@ -239,7 +239,8 @@ def test_attn_validation(L):
                  ldw=64, Y=FAKE, ldy=64)  # q = 4*8 = 32, kv = 2*8 = 16: 64 columns
         a.update(kw)
         return L.tp_attn_qkv_fwd(a["b"], a["s"], a["h"], a["nq"], a["nkv"], a["d"], a["t"], a["rank"],
-                                 a["dtype"], a["X"], a["ldx"], a["W"], a["ldw"], a["Y"], a["ldy"], None)
+                                 a["dtype"], a["X"], a["ldx"], a["W"], a["ldw"], a["Y"], a["ldy"],
+                                 a.get("ws"), a.get("wsb", 0), None)
     assert qf(nq=7) == 1                    # n_q % t
     assert qf(nkv=3, t=1) == 1              # n_q % n_kv
     assert qf(nkv=1) == 1                   # n_kv % t
@@ -247,11 +248,24 @@ def test_attn_validation(L):
     assert qf(dtype=0) == 2
     assert qf(ldw=48) == 1 and qf(ldy=56) == 1  # widths q + 2 kv = 64
     assert qf(rank=2) == 1
+    assert qf(nq=7, ws=FAKE + 64, wsb=1 << 20) == 1  # shape errors come first
+    assert qf(d=12, ws=FAKE + 64, wsb=1 << 20) == 2
+    # the split-K workspace: none for small shapes, fp32 slices for the 70B rank
+    # (4096 x 1280 outputs, K = 8192: 80 tiles of 256x256 -> 3 slices)
+    ws = L.lgs_attn_qkv_fwd_workspace_bytes
+    assert ws(1, 16, 64, 8, 4, 8, 2, 1) == 0
+    assert ws(1, 4096, 8192, 64, 8, 128, 8, 1) == 3 * 4096 * 1280 * 4
+    assert ws(1, 4096, 8192, 64, 8, 128, 8, 0) == 0  # invalid (fp32): no workspace
+    assert L.lgs_last_error() == b""
     of = lambda **kw: L.tp_attn_out_fwd(1, 16, 64, kw.get("nq", 8), 8, 2, kw.get("rank", 0), 1, FAKE,
                                         kw.get("lda", 32), FAKE, 64, FAKE, 64, None)
     assert of(nq=7) == 1 and of(lda=24) == 1 and of(rank=5) == 1  # n_q % t, lda < q = 32, rank
-    ob = L.tp_attn_out_bwd(1, 16, 64, 8, 8, 2, 0, 1, FAKE, 32, FAKE, 64, FAKE, 64, None, 32, FAKE, 64, None)
+    ob = L.tp_attn_out_bwd(1, 16, 64, 8, 8, 2, 0, 1, FAKE, 32, FAKE, 64, FAKE, 64, None, 32, FAKE, 64, None, 0,
+                           None)
     assert ob == 1                          # dA_i required
+    # dA's split-K workspace at the 70B shape: two fp32 halves of [4096, 1024]
+    assert L.lgs_attn_out_bwd_workspace_bytes(1, 4096, 8192, 64, 128, 8, 1) == 2 * 4096 * 1024 * 4
+    assert L.lgs_attn_out_bwd_workspace_bytes(1, 16, 64, 8, 8, 2, 1) == 0
     qb = L.tp_attn_qkv_bwd(1, 16, 64, 8, 4, 8, 2, 0, 1, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 32, None)
     assert qb == 1                          # lddw < q + 2 kv
 

@@ -80,6 +80,55 @@ def test_attn_projections_ragged(shape):
         assert_close("dWo_i", dWo, g["dW"], BF16)
 
 
+def test_attn_qkv_split_k_every_element():
+    """A deep QKV product (h = 2600) with few output tiles runs split over K
+    (4 slices, the last one a partial K tile) when given its workspace: every
+    element against the oracle, and against the unsplit run (same values up to
+    the fp32 summation order)."""
+    b, s, h, n_q, n_kv, d, t = 1, 600, 2600, 8, 4, 128, 2
+    M, q, kv = b * s, n_q // t * d, n_kv // t * d
+    dev_ = dev()
+    assert lgs.attn_qkv_fwd_workspace_bytes(b, s, h, n_q, n_kv, d, t) == 4 * M * (q + 2 * kv) * 4
+    X, Wq, Wk, Wv = synth.small(21, (M, h), (h, n_q * d), (h, n_kv * d), (h, n_kv * d), dtype="bf16")
+    Wq, Wk, Wv = ((w.float() * 0.03).to(BF16) for w in (Wq, Wk, Wv))
+    W = synth.qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, 1)
+    step("attn QKV split-K vs unsplit vs oracle")
+    Xd, Wd = X.to(dev_), W.to(dev_)
+    QKVs = torch.empty(M, q + 2 * kv, dtype=BF16, device=dev_)
+    QKVu = torch.empty_like(QKVs)
+    lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, 1, Xd, Wd, QKVs)
+    lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, 1, Xd, Wd, QKVu, split=False)
+    sync()
+    ref = at.qkv_forward(f64(X), at.qkv_shard(f64(Wq), f64(Wk), f64(Wv), n_q, n_kv, d, t, 1))
+    assert_close("QKV_1 split-K", QKVs, ref, BF16)
+    assert_close("QKV_1 unsplit", QKVu, ref, BF16)
+    assert_close("split-K vs unsplit", QKVs, f64(QKVu), BF16)
+
+
+def test_attn_out_bwd_split_k_every_element():
+    """The output projection's backward with dA split over K in two (few dA
+    tiles, h = 4096): every element of dA and dW_O against the oracle and
+    against the unsplit run."""
+    b, s, h, n_q, d, t = 1, 520, 4096, 8, 128, 2
+    M, q = b * s, n_q // t * d
+    dev_ = dev()
+    assert lgs.attn_out_bwd_workspace_bytes(b, s, h, n_q, d, t) == 2 * M * q * 4
+    A, Wo, dZ = synth.small(23, (M, q), (n_q * d, h), (M, h), dtype="bf16")
+    Wo_r = (Wo[q:2 * q].float() * 0.05).to(BF16).contiguous()
+    step("attn out-proj backward split-K vs unsplit vs oracle")
+    Ad, Wod, dZd = A.to(dev_), Wo_r.to(dev_), dZ.to(dev_)
+    dA, dW = torch.empty(M, q, dtype=BF16, device=dev_), torch.empty(q, h, dtype=BF16, device=dev_)
+    dAu, dWu = torch.empty_like(dA), torch.empty_like(dW)
+    lgs.tp_attn_out_bwd(b, s, h, n_q, d, t, 1, Ad, Wod, dZd, dA, dW)
+    lgs.tp_attn_out_bwd(b, s, h, n_q, d, t, 1, Ad, Wod, dZd, dAu, dWu, split=False)
+    sync()
+    g = at.out_backward(f64(A), f64(Wo_r), f64(dZ))
+    assert_close("dA (split-K)", dA, g["dA"], BF16)
+    assert_close("dA (unsplit)", dAu, g["dA"], BF16)
+    assert_close("dWo (with split dA)", dW, g["dW"], BF16)
+    assert torch.equal(dW, dWu)  # dW_O takes the same path either way
+
+
 def test_attn_split_identity_on_device():
     """sum over ranks of (rank's heads attended) W_O^i == the unsplit block."""
     b, s, h, n_q, n_kv, d, t = 1, 96, 256, 8, 4, 32, 4
@@ -125,7 +174,9 @@ def test_attn_70b_sampled():
         Wo_r = Wo[r * q:(r + 1) * q].contiguous()
         Xd, Wd, Wod, Ad = X.to(dev_), W.to(dev_), Wo_r.to(dev_), A.to(dev_)
         QKV = torch.empty(M, q + 2 * kv, dtype=BF16, device=dev_)
-        lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, QKV)
+        lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, QKV)  # split over K (the bench's schedule)
+        QKVu = torch.empty_like(QKV)
+        lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, QKVu, split=False)
         Z = torch.empty(M, h, dtype=BF16, device=dev_)
         lgs.tp_attn_out_fwd(b, s, h, n_q, d, t, r, Ad, Wod, Z)
         dX = torch.empty(M, h, dtype=BF16, device=dev_)
@@ -138,6 +189,7 @@ def test_attn_70b_sampled():
         W64 = at.qkv_shard(f64(Wq), f64(Wk), f64(Wv), n_q, n_kv, d, t, r)
         rows = _rows(M, 24, r)
         assert_close(f"QKV_{r} rows", QKV.cpu()[rows], at.qkv_forward(X64[rows], W64), BF16)
+        assert_close(f"QKV_{r} rows (unsplit)", QKVu.cpu()[rows], at.qkv_forward(X64[rows], W64), BF16)
         assert_close(f"Z_{r} rows", Z.cpu()[rows], at.out_forward(f64(A[rows]), f64(Wo_r)), BF16)
         assert_close(f"dX_{r} rows", dX.cpu()[rows], at.qkv_backward(X64[rows], W64, f64(dQ[rows]))["dX"], BF16)
         assert_close(f"dA_{r} rows", dA.cpu()[rows], at.out_backward(f64(A[rows]), f64(Wo_r), f64(dZ[rows]))["dA"],

@@ -254,6 +254,35 @@ def test_xent_small_all_ranks(shape):
         np.stack([(yn >= r * Vr) & (yn < (r + 1) * Vr) for r in range(t)]), axis=0))
 
 
+def test_xent_two_launch_plan_every_element():
+    """A slice wide enough that the launch plan splits its columns (the first
+    19520 on 256x320 tiles in 2 full rounds, the rest on 256x160 tiles): every
+    token's partials, first argmax and loss against the oracle, with a K tail
+    (h = 136) and a ragged row count; targets chosen on both sides of the
+    split and on its boundary."""
+    d = dev()
+    b, s, h, V = 2, 1000, 136, 24640
+    M = b * s
+    H, E = synth.small(77, (M, h), (V, h), dtype="bf16")
+    E = (E.float() * 0.3).to(BF16)
+    g = torch.Generator().manual_seed(11)
+    y = torch.randint(0, V, (M,), generator=g, dtype=torch.int64).to(torch.int32)
+    y[:6] = torch.tensor([19519, 19520, 19521, 0, V - 1, 19680], dtype=torch.int32)
+    step("xent t=1, slice split over two launches: every element")
+    m = torch.empty(M, dtype=F32, device=d)
+    l, T, loss = torch.empty_like(m), torch.empty_like(m), torch.empty_like(m)
+    am = torch.empty(M, dtype=torch.int32, device=d)
+    lgs.vocab_parallel_xent_fwd(b, s, h, V, 1, 0, H.to(d), E.to(d), y.to(d), m, l, T, argmax_r=am, loss=loss)
+    sync()
+    H64, E64, yn = f64(H), f64(E), y.numpy().astype(np.int64)
+    rm, rl, rT, _ = oracle.xent.shard_partials(H64, E64, yn, 0)
+    assert_close("m (split plan)", m, rm, BF16)
+    assert_close("l (split plan)", l, rl, BF16)
+    assert_close("T (split plan)", T, rT, BF16)
+    assert_close("loss (split plan)", loss, oracle.xent.naive_loss(H64, E64, yn), BF16)
+    check_argmax(H64, E64, 0, am.cpu().numpy(), np.arange(M))
+
+
 def test_xent_t1_loss_output():
     d = dev()
     b, s, h, V = 1, 200, 128, 1000

@@ -57,6 +57,7 @@ SMALL = [  # (b, s, h, V, t): ragged token counts, slices of several tiles with 
     (2, 129, 136, 4 * 520, 4),
     (1, 64, 64, 8 * 136, 8),
     (1, 520, 264, 2 * 1288, 2),
+    (2, 1000, 136, 24640, 1),  # wide enough that the logit GEMM splits its columns over two launches
 ]
 
 
