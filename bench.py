@@ -16,6 +16,7 @@ All inputs are resident in HBM before timing starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-per-config]
     python bench.py --copy-calibration   # plain copy for counter scaling
+    python bench.py --blas-reference     # torch.matmul (hipBLASLt) at the same GEMM shapes
 """
 
 import argparse
@@ -127,6 +128,33 @@ def cpu_baseline(w, xw, inputs, budget_s=10.0):
             "cpu_model": model, "os_cpu_count": os.cpu_count(),
             "sample": f"the same step (MLP fwd+bwd, both sums, slice-0 CE, merge) on the first {m} "
                       f"of {w.M} tokens in fp64 numpy, {passes} passes: {fl / 1e9:.1f} GFLOP in {total:.2f} s"}
+
+
+# The library's GEMM shapes (M, N, K) with the per-configuration entry they
+# belong to, for the vendor-library reference below.
+BLAS_SHAPES = [
+    (4096, 8192, 3584, "70B GeLU / SwiGLU down GEMM (row-parallel)"),
+    (4096, 3584, 8192, "70B GeLU column-parallel GEMM / dY"),
+    (8192, 1536, 3072, "8.3B column-parallel GEMM / dY"),
+    (8192, 3072, 1536, "8.3B row-parallel GEMM"),
+    (8192, 6400, 3072, "8.3B CE logits (slice of t=8)"),
+]
+
+
+def blas_reference(reps=20):
+    """torch.matmul in bf16 (hipBLASLt on ROCm) at the library's GEMM shapes:
+    a vendor-library reference point for the same products (plain C = A B,
+    no epilogue), timed with HIP events."""
+    import torch
+    dev = torch.device("cuda", 0)
+    out = []
+    for M, N, K, what in BLAS_SHAPES:
+        a = torch.randn(M, K, device=dev).to(torch.bfloat16)
+        b = torch.randn(K, N, device=dev).to(torch.bfloat16)
+        ms = time_calls(torch, lambda: torch.matmul(a, b), reps, warmup=5)
+        out.append({"M": M, "N": N, "K": K, "what": what, "us": round(ms * 1e3, 1),
+                    "tflops": round(2 * M * N * K / ms / 1e9, 1)})
+    print(json.dumps({"blas_reference": out, "library": "torch.matmul bf16 (hipBLASLt)"}), flush=True)
 
 
 def time_calls(torch, fn, reps, warmup=3):
@@ -348,6 +376,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-configuration timings (counter passes)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="time torch.matmul (hipBLASLt) at the library's GEMM shapes and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard: the library is measured on one GPU "
@@ -358,6 +388,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.blas_reference:
+        blas_reference()
         return
 
     from logit_gemm_shard_amd import binding as lgs
