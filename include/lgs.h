@@ -203,6 +203,33 @@ int tp_swiglu_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, cons
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tp_mlp_bwd_dgelu / tp_mlp_bwd_dx / tp_mlp_bwd_dw -- tp_mlp_bwd in three
+ * parts, for callers that overlap the input gradient's exchange with the
+ * weight gradients ("Conjugate Communication Operators": only dX_i goes
+ * through f*'s all-reduce; dA_i and dB_i stay on the rank):
+ *
+ *   dgelu: dY_i = dZ B_i^T; dU_i = dY_i * GeLU'(U_i) and Y_i = GeLU(U_i) into
+ *          the workspace
+ *   dx:    dX_i = dU_i A_i^T                 (reads the workspace)
+ *   dw:    dB_i = Y_i^T dZ, dA_i = X^T dU_i  (reads the workspace)
+ *
+ * Arguments as in tp_mlp_bwd; the three calls share one workspace of
+ * lgs_mlp_bwd_workspace_bytes.  dx and dw may run in either order or
+ * concurrently on different streams once dgelu has completed (the caller
+ * orders them, e.g. with events); the results equal tp_mlp_bwd's.  tp_mlp_bwd
+ * runs dx and dw as one launch, which is faster when nothing overlaps them.
+ */
+int tp_mlp_bwd_dgelu(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
+                     const void* B_i, int64_t ldb, const void* U_i, int64_t ldu, const void* dZ,
+                     int64_t lddz, void* workspace, size_t workspace_bytes, void* stream);
+int tp_mlp_bwd_dx(int b, int s, int h, int ffn, int t, int rank, int dtype, const void* A_i,
+                  int64_t lda, void* dX_i, int64_t lddx, void* workspace, size_t workspace_bytes,
+                  void* stream);
+int tp_mlp_bwd_dw(int b, int s, int h, int ffn, int t, int rank, int dtype, const void* X,
+                  int64_t ldx, const void* dZ, int64_t lddz, void* dA_i, int64_t ldda, void* dB_i,
+                  int64_t lddb, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * vocab_parallel_xent_fwd -- the fused vocab-parallel logit GEMM + cross-entropy
  * partials of one rank ("LIT-022: Megatron-LM ...", "Key takeaways": the
  * parallel logit GEMM is fused into the loss so ranks exchange O(b*s) numbers

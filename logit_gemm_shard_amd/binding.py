@@ -41,6 +41,10 @@ SIGNATURES = [
                         _p, _i64, _p, _i64, _p, _sz, _p]),
     ("tp_mlp_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                         _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _sz, _p]),
+    ("tp_mlp_bwd_dgelu", _i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _sz, _p]),
+    ("tp_mlp_bwd_dx", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _sz, _p]),
+    ("tp_mlp_bwd_dw", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _sz,
+                           _p]),
     ("tp_swiglu_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                            _p, _i64, _p, _i64, _p, _sz, _p]),
     ("tp_swiglu_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
@@ -220,6 +224,47 @@ def tp_swiglu_bwd(b, s, h, ffn, t, rank, X, Wgu_i, Wd_i, GU_i, dZ, dX_i, dWgu_i,
     _check(L.tp_swiglu_bwd(b, s, h, ffn, t, rank, dt, *args,
                            _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes, _stream(stream)))
     return dX_i, dWgu_i, dWd_i
+
+
+def _ws_given(L, b, s, h, ffn, t, dt, workspace):
+    need = L.lgs_mlp_bwd_workspace_bytes(b, s, h, ffn, t, dt)
+    if workspace is None:
+        raise ValueError("the three-part backward shares one caller-owned workspace")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), need
+
+
+def tp_mlp_bwd_dgelu(b, s, h, ffn, t, rank, B_i, U_i, dZ, workspace, act="erf", stream=None):
+    """dY = dZ B_i^T, dU = dY GeLU'(U_i) and Y = GeLU(U_i) into the workspace."""
+    L = lib()
+    dt = _dtype(dZ)
+    ws, wsb, _ = _ws_given(L, b, s, h, ffn, t, dt, workspace)
+    args = []
+    for m in (B_i, U_i, dZ):
+        args.extend(_mat(m))
+    _check(L.tp_mlp_bwd_dgelu(b, s, h, ffn, t, rank, dt, _ACT[act], *args, ws, wsb, _stream(stream)))
+
+
+def tp_mlp_bwd_dx(b, s, h, ffn, t, rank, A_i, dX_i, workspace, stream=None):
+    """dX_i = dU A_i^T from the workspace (after tp_mlp_bwd_dgelu)."""
+    L = lib()
+    dt = _dtype(A_i)
+    ws, wsb, _ = _ws_given(L, b, s, h, ffn, t, dt, workspace)
+    a, lda = _mat(A_i)
+    x, ldx = _mat(dX_i)
+    _check(L.tp_mlp_bwd_dx(b, s, h, ffn, t, rank, dt, a, lda, x, ldx, ws, wsb, _stream(stream)))
+    return dX_i
+
+
+def tp_mlp_bwd_dw(b, s, h, ffn, t, rank, X, dZ, dA_i, dB_i, workspace, stream=None):
+    """dB_i = Y^T dZ and dA_i = X^T dU from the workspace (after tp_mlp_bwd_dgelu)."""
+    L = lib()
+    dt = _dtype(X)
+    ws, wsb, _ = _ws_given(L, b, s, h, ffn, t, dt, workspace)
+    args = []
+    for m in (X, dZ, dA_i, dB_i):
+        args.extend(_mat(m))
+    _check(L.tp_mlp_bwd_dw(b, s, h, ffn, t, rank, dt, *args, ws, wsb, _stream(stream)))
+    return dA_i, dB_i
 
 
 def vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, H, E_r, targets, m_r, l_r, tgt_r,

@@ -122,6 +122,14 @@ LGS_API size_t lgs_mlp_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, 
   return 2 * round256((size_t)b * s * (ffn / t) * elt(dtype));
 }
 
+namespace {
+
+// The workspace of the backward (and of its three parts): Y_i then dU_i.
+int bwd_workspace(int b, int s, int h, int ffn, int t, int dtype, void* workspace,
+                  size_t workspace_bytes, char** y, char** du);
+
+}  // namespace
+
 LGS_API size_t lgs_swiglu_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype,
                                               int y_given) {
   if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || ffn <= 0 || ffn % t) return 0;
@@ -267,6 +275,72 @@ LGS_API int tp_swiglu_bwd(int b, int s, int h, int ffn, int t, int rank, int dty
   return launched(lgs::swiglu_bwd(M, h, f, X, ldx, Wgu_i, ldwgu, Wd_i, ldwd, GU_i, ldgu, dZ, lddz,
                                   dX_i, lddx, dWgu_i, lddwgu, dWd_i, lddwd, y, dgu,
                                   (hipStream_t)stream));
+}
+
+namespace {
+
+int bwd_workspace(int b, int s, int h, int ffn, int t, int dtype, void* workspace,
+                  size_t workspace_bytes, char** y, char** du) {
+  const size_t need = lgs_mlp_bwd_workspace_bytes(b, s, h, ffn, t, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dU_i, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  *y = (char*)workspace;
+  *du = *y + need / 2;
+  return LGS_OK;
+}
+
+}  // namespace
+
+LGS_API int tp_mlp_bwd_dgelu(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
+                             const void* B_i, int64_t ldb, const void* U_i, int64_t ldu,
+                             const void* dZ, int64_t lddz, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int st = check_mlp(b, s, h, ffn, t, rank, dtype, act);
+  if (st) return st;
+  const int M = b * s, f = ffn / t;
+  if ((st = check_mat("B_i", B_i, f, ldb, h, dtype, true))) return st;
+  if ((st = check_mat("U_i", U_i, M, ldu, f, dtype, true))) return st;
+  if ((st = check_mat("dZ", dZ, M, lddz, h, dtype, true))) return st;
+  char *y, *du;
+  if ((st = bwd_workspace(b, s, h, ffn, t, dtype, workspace, workspace_bytes, &y, &du))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::mlp_bwd_dgelu(dtype == LGS_BF16, M, h, f, act, B_i, ldb, U_i, ldu, dZ, lddz, y,
+                                     du, (hipStream_t)stream));
+}
+
+LGS_API int tp_mlp_bwd_dx(int b, int s, int h, int ffn, int t, int rank, int dtype,
+                          const void* A_i, int64_t lda, void* dX_i, int64_t lddx, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_mlp(b, s, h, ffn, t, rank, dtype, LGS_GELU_ERF);
+  if (st) return st;
+  const int M = b * s, f = ffn / t;
+  if ((st = check_mat("A_i", A_i, h, lda, f, dtype, true))) return st;
+  if ((st = check_mat("dX_i", dX_i, M, lddx, h, dtype, true))) return st;
+  char *y, *du;
+  if ((st = bwd_workspace(b, s, h, ffn, t, dtype, workspace, workspace_bytes, &y, &du))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::mlp_bwd_dx(dtype == LGS_BF16, M, h, f, A_i, lda, du, dX_i, lddx,
+                                  (hipStream_t)stream));
+}
+
+LGS_API int tp_mlp_bwd_dw(int b, int s, int h, int ffn, int t, int rank, int dtype, const void* X,
+                          int64_t ldx, const void* dZ, int64_t lddz, void* dA_i, int64_t ldda,
+                          void* dB_i, int64_t lddb, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int st = check_mlp(b, s, h, ffn, t, rank, dtype, LGS_GELU_ERF);
+  if (st) return st;
+  const int M = b * s, f = ffn / t;
+  if ((st = check_mat("X", X, M, ldx, h, dtype, true))) return st;
+  if ((st = check_mat("dZ", dZ, M, lddz, h, dtype, true))) return st;
+  if ((st = check_mat("dA_i", dA_i, h, ldda, f, dtype, true))) return st;
+  if ((st = check_mat("dB_i", dB_i, f, lddb, h, dtype, true))) return st;
+  char *y, *du;
+  if ((st = bwd_workspace(b, s, h, ffn, t, dtype, workspace, workspace_bytes, &y, &du))) return st;
+  (void)hipGetLastError();
+  return launched(lgs::mlp_bwd_dw(dtype == LGS_BF16, M, h, f, X, ldx, dZ, lddz, y, du, dA_i, ldda, dB_i,
+                                  lddb, (hipStream_t)stream));
 }
 
 LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype,

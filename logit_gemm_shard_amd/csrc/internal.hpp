@@ -22,6 +22,18 @@ hipError_t mlp_bwd(bool bf16, int M, int h, int f, int act, const void* X, int64
                    int64_t ldu, const void* dZ, int64_t lddz, void* dX, int64_t lddx, void* dA,
                    int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, hipStream_t s);
 
+// The same backward in three parts: dgelu (dY, dU = dY GeLU'(U), Y into
+// scratch), then dx (dX_i = dU A_i^T) and dw (dB_i = Y^T dZ, dA_i = X^T dU),
+// independent of each other.
+hipError_t mlp_bwd_dgelu(bool bf16, int M, int h, int f, int act, const void* B, int64_t ldb,
+                         const void* U, int64_t ldu, const void* dZ, int64_t lddz, void* Yws,
+                         void* dUws, hipStream_t s);
+hipError_t mlp_bwd_dx(bool bf16, int M, int h, int f, const void* A, int64_t lda, const void* dUws,
+                      void* dX, int64_t lddx, hipStream_t s);
+hipError_t mlp_bwd_dw(bool bf16, int M, int h, int f, const void* X, int64_t ldx, const void* dZ,
+                      int64_t lddz, const void* Yws, const void* dUws, void* dA, int64_t ldda,
+                      void* dB, int64_t lddb, hipStream_t s);
+
 // One rank's SwiGLU MLP shard (bf16).  f = ffn / t; W_gu = [W_gate,i | W_up,i].
 //   [G | U] = X W_gu (stored if GU != null), Y = Swish(G) * U, Z = Y W_down,i.
 hipError_t swiglu_fwd(int M, int h, int f, const void* X, int64_t ldx, const void* Wgu,

@@ -87,6 +87,56 @@ hipError_t mlp_bwd(bool is_bf16, int M, int h, int f, int act, const void* X, in
   return launch_gemm_f32<true, true>(du, ldw, a, lda, M, h, f, ex, s);
 }
 
+// The backward in three parts, for callers that overlap the input gradient's
+// exchange with the weight gradients (dX's all-reduce needs dX only; dA and
+// dB need no exchange): dgelu writes dU and Y into the scratch, after which
+// dx and dw are independent and may run on different streams.
+hipError_t mlp_bwd_dgelu(bool is_bf16, int M, int h, int f, int act, const void* B, int64_t ldb,
+                         const void* U, int64_t ldu, const void* dZ, int64_t lddz, void* Yws,
+                         void* dUws, hipStream_t s) {
+  const int64_t ldw = f;
+  if (is_bf16) {
+    EpiGeluBwd<bf16> e1{(const bf16*)U, ldu, (bf16*)dUws, ldw, (bf16*)Yws, ldw, M, f, act};
+    return gemm_bf16<true, true>(pick_tile(M, f), (const bf16*)dZ, lddz, (const bf16*)B, ldb, M, f, h,
+                                 e1, s);
+  }
+  EpiGeluBwd<float> e1{(const float*)U, ldu, (float*)dUws, ldw, (float*)Yws, ldw, M, f, act};
+  return launch_gemm_f32<true, true>((const float*)dZ, lddz, (const float*)B, ldb, M, f, h, e1, s);
+}
+
+hipError_t mlp_bwd_dx(bool is_bf16, int M, int h, int f, const void* A, int64_t lda,
+                      const void* dUws, void* dX, int64_t lddx, hipStream_t s) {
+  if (is_bf16) {
+    EpiStore<bf16> ex{(bf16*)dX, lddx, M, h};
+    return gemm_bf16<true, true>(pick_tile(M, h), (const bf16*)dUws, f, (const bf16*)A, lda, M, h, f, ex,
+                                 s);
+  }
+  EpiStore<float> ex{(float*)dX, lddx, M, h};
+  return launch_gemm_f32<true, true>((const float*)dUws, f, (const float*)A, lda, M, h, f, ex, s);
+}
+
+hipError_t mlp_bwd_dw(bool is_bf16, int M, int h, int f, const void* X, int64_t ldx,
+                      const void* dZ, int64_t lddz, const void* Yws, const void* dUws, void* dA,
+                      int64_t ldda, void* dB, int64_t lddb, hipStream_t s) {
+  const int64_t ldw = f;
+  if (is_bf16) {
+    const bf16 *x = (const bf16*)X, *dz = (const bf16*)dZ, *y = (const bf16*)Yws, *du = (const bf16*)dUws;
+    EpiStore<bf16> eb{(bf16*)dB, lddb, f, h};
+    EpiStore<bf16> ea{(bf16*)dA, ldda, h, f};
+    if (f >= 256 && h >= 256 && M >= 256)
+      return launch_gemm_pp_group2(pp_problem<256, 256, false, false>(y, ldw, dz, lddz, f, h, M, eb),
+                                   pp_problem<256, 256, false, false>(x, ldx, du, ldw, h, f, M, ea), s);
+    return launch_gemm_pp_group2(pp_problem<128, 128, false, false>(y, ldw, dz, lddz, f, h, M, eb),
+                                 pp_problem<128, 128, false, false>(x, ldx, du, ldw, h, f, M, ea), s);
+  }
+  const float *x = (const float*)X, *dz = (const float*)dZ, *y = (const float*)Yws, *du = (const float*)dUws;
+  EpiStore<float> eb{(float*)dB, lddb, f, h};
+  hipError_t e = launch_gemm_f32<false, false>(y, ldw, dz, lddz, f, h, M, eb, s);
+  if (e != hipSuccess) return e;
+  EpiStore<float> ea{(float*)dA, ldda, h, f};
+  return launch_gemm_f32<false, false>(x, ldx, du, ldw, h, f, M, ea, s);
+}
+
 int num_tiles() { return kNumTiles; }
 
 bool tile_shape(int tile, int* bm, int* bn) {

@@ -169,6 +169,21 @@ def test_swiglu_bwd_validation(L):
     assert L.lgs_swiglu_fwd_workspace_bytes(1, 16, 64, 128, 2, 1, 0) == 2048
 
 
+def test_mlp_bwd_parts_validation(L):
+    # (b, s, h, ffn, t, rank, dtype, act, B, ldb, U, ldu, dZ, lddz, ws, ws_bytes, stream)
+    dg = lambda **k: L.tp_mlp_bwd_dgelu(1, 16, 64, 128, 2, k.get("rank", 1), 1, k.get("act", 0), FAKE, 64,
+                                        k.get("U", FAKE), 64, FAKE, 64, k.get("ws", FAKE), k.get("wsb", 1 << 20),
+                                        None)
+    assert dg(rank=2) == 1 and dg(act=9) == 2 and dg(U=None) == 1
+    assert dg(ws=None) == 3 and dg(wsb=100) == 3 and dg(ws=FAKE + 16) == 2
+    dx = L.tp_mlp_bwd_dx(1, 16, 64, 128, 2, 0, 1, FAKE, 32, FAKE, 64, None, 0, None)
+    assert dx == 1                          # lda < ffn/t = 64
+    dx = L.tp_mlp_bwd_dx(1, 16, 64, 128, 2, 0, 1, FAKE, 64, FAKE, 64, None, 0, None)
+    assert dx == 3                          # the shared workspace is required
+    dw = L.tp_mlp_bwd_dw(1, 16, 64, 128, 2, 0, 1, FAKE, 64, FAKE, 64, FAKE, 64, None, 64, FAKE, 1 << 20, None)
+    assert dw == 1                          # dB_i required
+
+
 def test_xent_validation(L):
     def xe(**kw):
         a = dict(b=2, s=8, h=64, vocab=1024, t=4, rank=0, dtype=1, H=FAKE, ldh=64, E=FAKE, lde=64,

@@ -146,6 +146,49 @@ def test_mlp_fwd_bwd_ragged(shape, dtype):
             assert_close("dB_i", dB, g["dB"], dtype)
 
 
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 200, 136, 528, 2), (2, 1100, 1064, 2 * 1048, 2), (1, 1024, 3072, 8 * 1536, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mlp_bwd_in_three_parts(shape, dtype):
+    """dgelu, then dx and dw on two streams running concurrently: the same
+    values as tp_mlp_bwd, and the oracle's."""
+    b, s, h, ffn, t = shape
+    M, f = b * s, ffn // t
+    d = dev()
+    dn = "bf16" if dtype == BF16 else "f32"
+    X, A, B, dZ = synth.small(5 + h, (M, h), (h, f), (f, h), (M, h), dtype=dn)
+    A, B = (A.float() * 0.05).to(dtype), (B.float() * 0.05).to(dtype)
+    X64, A64, B64, dZ64 = f64(X), f64(A), f64(B), f64(dZ)
+    U = round_like(X64 @ A64, dtype)
+    Xd, Ad, Bd, Ud, dZd = X.to(d), A.to(d), B.to(d), U.to(d), dZ.to(d)
+    step(f"backward in three parts {shape} {dn}")
+    ws = torch.empty(lgs.mlp_bwd_workspace_bytes(b, s, h, ffn, t, dtype), dtype=torch.uint8, device=d)
+    dX1 = torch.empty(M, h, dtype=dtype, device=d)
+    dA1 = torch.empty(h, f, dtype=dtype, device=d)
+    dB1 = torch.empty(f, h, dtype=dtype, device=d)
+    side = torch.cuda.Stream()
+    lgs.tp_mlp_bwd_dgelu(b, s, h, ffn, t, 0, Bd, Ud, dZd, ws)
+    done = torch.cuda.Event()
+    done.record()
+    side.wait_event(done)
+    with torch.cuda.stream(side):
+        lgs.tp_mlp_bwd_dw(b, s, h, ffn, t, 0, Xd, dZd, dA1, dB1, ws)
+    lgs.tp_mlp_bwd_dx(b, s, h, ffn, t, 0, Ad, dX1, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    # the one-launch backward on its own workspace, for comparison
+    dX2 = torch.empty_like(dX1)
+    dA2 = torch.empty_like(dA1)
+    dB2 = torch.empty_like(dB1)
+    lgs.tp_mlp_bwd(b, s, h, ffn, t, 0, Xd, Ad, Bd, Ud, dZd, dX2, dA2, dB2)
+    sync()
+    g = oracle.mlp.shard_backward(X64, A64, B64, f64(U), dZ64)
+    assert_close("dX (three parts)", dX1, g["dX"], dtype)
+    assert_close("dA (three parts)", dA1, g["dA"], dtype)
+    assert_close("dB (three parts)", dB1, g["dB"], dtype)
+    for name, x, y in (("dX", dX1, dX2), ("dA", dA1, dA2), ("dB", dB1, dB2)):
+        assert_close(f"{name}: three parts vs one launch", x, f64(y), dtype)
+
+
 def test_t1_is_the_unsplit_block():
     d = dev()
     b, s, h, ffn = 1, 300, 264, 520
