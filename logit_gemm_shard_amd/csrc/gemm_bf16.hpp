@@ -85,6 +85,7 @@ struct OpLayout<R, true> {
   static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
   static constexpr int kBytes = R * 64;
   static constexpr int kInstr = R / 16;  // 1 KB loads per stage
+  static constexpr uint32_t kColBytes = 64;  // LDS bytes per tile row
   // element offset of a k step within the operand
   __device__ __forceinline__ static int64_t step_elems(int64_t) { return kBK; }
   // byte offset (from the tile's first row, k0 = 0) that lane `lane` of load
@@ -112,21 +113,40 @@ struct OpLayout<R, true> {
 
 template <int R>
 struct OpLayout<R, false> {
+  // Layout in LDS: k-rows in groups of four; within a group the 64-byte
+  // blocks (32 columns) of the four rows alternate: columns 32 b .. 32 b + 31
+  // of k-row 4g + r sit at byte 8R g + 256 b + 64 r.  A transposing fragment
+  // read takes four consecutive k-rows of 32 columns per half-wave, which
+  // this puts in 256 consecutive bytes (all 64 banks, no conflict) without
+  // padding, so a stage holds exactly the tile's 64 R bytes.  Each group of
+  // four lanes of a load still reads 64 contiguous bytes of one row.
   static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
-  static constexpr int kPitch = 2 * R + (((2 * R) % 256 == 0 || (2 * R) % 256 == 128) ? 64 : 0);
-  static constexpr int kCpr = kPitch / 16;  // 16-B chunks per k-row (a multiple of 4)
-  static constexpr int kBytes = kBK * kPitch;
-  static constexpr int kInstr = kBK * kCpr / 64;  // kBK k-rows x kCpr chunks / 64 lanes
+  static constexpr int kGroupBytes = 8 * R;     // four k-rows
+  static constexpr int kGroupChunks = R / 2;    // 16-B chunks per group
+  static constexpr int kBytes = kBK * 2 * R;
+  static constexpr int kInstr = kBytes / 1024;  // 1 KB loads per stage
+  static constexpr uint32_t kColBytes = 8;      // LDS bytes per column, for column offsets that are multiples of 8
   __device__ __forceinline__ static int64_t step_elems(int64_t ld) { return kBK * ld; }
-  // byte offset (from the tile's first column, k0 = 0); out of range past the
-  // operand's last column or in the pitch padding.  Rows past K fall outside
-  // the buffer resource, which ends at the operand's last row.
-  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left) {
-    const int d = n * 64 + lane;
-    const int krow = d / kCpr, ch = d - krow * kCpr;
-    return (ch * 8 < R && ch * 8 < rows_left) ? (uint32_t)(krow * ld + ch * 8) * 2u : kOutOfRange;
+  // k-row and first column of the chunk that lane `lane` of load n fills
+  __device__ __forceinline__ static void chunk_of(int n, int lane, int& krow, int& col) {
+    const int p = n * 64 + lane;
+    const int g = p / kGroupChunks, w = p - g * kGroupChunks;
+    krow = 4 * g + ((w >> 2) & 3);
+    col = 32 * (w >> 4) + 8 * (w & 3);
   }
-  __device__ __forceinline__ static int kcol(int n, int lane) { return (n * 64 + lane) / kCpr; }
+  // byte offset (from the tile's first column, k0 = 0); out of range past the
+  // operand's last column.  Rows past K fall outside the buffer resource,
+  // which ends at the operand's last row.
+  __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left) {
+    int krow, col;
+    chunk_of(n, lane, krow, col);
+    return col < rows_left ? (uint32_t)(krow * ld + col) * 2u : kOutOfRange;
+  }
+  __device__ __forceinline__ static int kcol(int n, int lane) {
+    int krow, col;
+    chunk_of(n, lane, krow, col);
+    return krow;
+  }
   // The same load with the tile's columns taken from two blocks of the
   // operand in alternating 32-column groups: tile column c holds column
   // (c / 64) 32 + c % 32 of the first block (c / 32 even) or of the second
@@ -136,27 +156,29 @@ struct OpLayout<R, false> {
   __device__ __forceinline__ static uint32_t src_off_paired(int n, int lane, int64_t ld, int cols_left,
                                                            int half) {
     static_assert(R % 64 == 0, "paired tiles hold whole pairs of 32-column groups");
-    const int d = n * 64 + lane;
-    const int krow = d / kCpr, c = (d - krow * kCpr) * 8;
+    int krow, c;
+    chunk_of(n, lane, krow, c);
     const int col = ((c >> 6) << 5) + (c & 31);
-    return (c < R && col < cols_left) ? (uint32_t)(krow * ld + col + ((c >> 5) & 1) * half) * 2u
-                                      : kOutOfRange;
+    return col < cols_left ? (uint32_t)(krow * ld + col + ((c >> 5) & 1) * half) * 2u : kOutOfRange;
   }
-  // Two ds_read_b64_tr_b16 per fragment (rows row0 .. row0+31 of the wave's
-  // columns, k = 16 s + 8 (lane/32) .. +7): lanes 4j..4j+3 of each 16-lane
-  // group address k-row j of a 4 x 16 block.  The per-lane part:
+  // Two ds_read_b64_tr_b16 per fragment (columns row0 .. row0+31 of the
+  // wave's part, k = 16 s + 8 (lane/32) .. +7): lanes 4j..4j+3 of each
+  // 16-lane group address k-row j of a 4 x 16 block.  The per-lane part:
   __device__ __forceinline__ static uint32_t lane_off(int, int lane) {
     const int g = lane >> 4, i16 = lane & 15;
-    return (uint32_t)((8 * (g >> 1) + (i16 >> 2)) * kPitch + (16 * (g & 1) + 4 * (i16 & 3)) * 2);
+    const int col = 16 * (g & 1) + 4 * (i16 & 3);  // < 32: within one 64-byte block
+    return (uint32_t)(2 * (g >> 1) * kGroupBytes + (i16 >> 2) * 64 + col * 2);
   }
   // Issued as inline assembly: the compiler would otherwise treat them as
   // possibly aliasing the direct-to-LDS loads in flight and wait for all of
   // those first.  Results are only valid after an explicit lgkmcnt wait.
+  // k-rows 16 kS + 4 h + ... are group 4 kS + h; column row0 (a multiple of
+  // 32) starts block row0 / 32, 256 bytes each.
   template <int kS, int kRow0>
   __device__ __forceinline__ static bf16x8 frag_tr(uint32_t a) {  // a = base + wave part + lane_off
     s16x4 lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(a), "i"(16 * kS * kPitch + 2 * kRow0));
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"((16 * kS + 4) * kPitch + 2 * kRow0));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(a), "i"(4 * kS * kGroupBytes + 8 * kRow0));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"((4 * kS + 1) * kGroupBytes + 8 * kRow0));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
   }
@@ -402,10 +424,10 @@ __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int t
   // Fragment reads: one per-lane register per operand and sub-step, plus the
   // stage and a compile-time offset per fragment.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LGS_AS3 char*)smem;
-  const uint32_t fa_lane[2] = {LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u),
-                               LA::lane_off(1, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u)};
-  const uint32_t fb_lane[2] = {LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes,
-                               LB::lane_off(1, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes};
+  const uint32_t fa_lane[2] = {LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * LA::kColBytes,
+                               LA::lane_off(1, lane) + (uint32_t)(wm * T::WM) * LA::kColBytes};
+  const uint32_t fb_lane[2] = {LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * LB::kColBytes + LA::kBytes,
+                               LB::lane_off(1, lane) + (uint32_t)(wn * T::WN) * LB::kColBytes + LA::kBytes};
   bf16x8 fa[2][TM], fb[2][TN];
   // fragments of sub-step s of the tile in stage st into buffer d
   auto read_frags = [&](int st, auto s_c, int d) {

@@ -157,10 +157,10 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
 
   // Fragments of both 16-wide sub-steps of one K tile.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LGS_AS3 char*)smem;
-  const uint32_t fa_lane[2] = {LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u),
-                               LA::lane_off(1, lane) + (uint32_t)(wm * T::WM) * (P::AK ? 64u : 2u)};
-  const uint32_t fb_lane[2] = {LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes,
-                               LB::lane_off(1, lane) + (uint32_t)(wn * T::WN) * (P::BK ? 64u : 2u) + LA::kBytes};
+  const uint32_t fa_lane[2] = {LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * LA::kColBytes,
+                               LA::lane_off(1, lane) + (uint32_t)(wm * T::WM) * LA::kColBytes};
+  const uint32_t fb_lane[2] = {LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * LB::kColBytes + LA::kBytes,
+                               LB::lane_off(1, lane) + (uint32_t)(wn * T::WN) * LB::kColBytes + LA::kBytes};
   bf16x8 fa[2][TM], fb[2][TN];
   auto read_sub = [&](uint32_t sb, auto s_c) {
     constexpr int s = decltype(s_c)::value;
