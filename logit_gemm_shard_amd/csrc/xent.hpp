@@ -82,11 +82,15 @@ struct EpiXent {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = a[j][r];
-        sum += __builtin_amdgcn_exp2f(fmaf(v, 1.4426950408889634f, -shift));
-        tv = 32 * j + 8 * (r >> 2) + (r & 3) == tl ? v : tv;
-      }
+      for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(a[j][r], 1.4426950408889634f, -shift));
+    // The target pick runs only where some row of the wave has its target in
+    // this wave's columns (about one row tile in ten at V_r = 6400).
+    if (__any(tl >= -4 && tl < 32 * TN)) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tv = 32 * j + 8 * (r >> 2) + (r & 3) == tl ? a[j][r] : tv;
+    }
     sum += __shfl_xor(sum, 32);
     tv += __shfl_xor(tv, 32);
     // First column holding the maximum: each lane walks its columns from the
