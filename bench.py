@@ -52,6 +52,58 @@ def step_flops(M, h, f, Vr):
     return {"mlp_fwd": 2 * 2 * M * h * f, "mlp_bwd": 4 * 2 * M * h * f, "xent": 2 * M * h * Vr}
 
 
+def sample_gpu_clock(torch, run, seconds=3.0, n=4):
+    """The graphics clock while `run` (one step) repeats for `seconds`: n
+    readings of `amd-smi metric --clock --json` (a child process) spread over
+    the run, each the mean of the XCDs' clocks; the median is reported with
+    every reading.  None if the tool is missing or its output cannot be read."""
+    import json
+    import shutil
+    import subprocess
+    import threading
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    readings = []
+
+    def reader():
+        for _ in range(n):
+            delay = seconds / (n + 1)
+            time.sleep(delay)
+            try:
+                r = subprocess.run([tool, "metric", "--clock", "--json"], capture_output=True, text=True,
+                                   timeout=20)
+                data = json.loads(r.stdout)
+                gpus = data["gpu_data"] if isinstance(data, dict) else data
+                clk = gpus[0]["clock"]
+                vals = [v["clk"]["value"] for k, v in clk.items()
+                        if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                if vals:
+                    readings.append(sum(vals) / len(vals))
+            except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.TimeoutExpired):
+                pass
+
+    th = threading.Thread(target=reader)
+    t0 = time.perf_counter()
+    th.start()
+    k = 0
+    while time.perf_counter() - t0 < seconds or th.is_alive():
+        run()
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()  # keep the queue short so the readings see steps running
+        if time.perf_counter() - t0 > 4 * seconds + 30:
+            break
+    torch.cuda.synchronize()
+    th.join()
+    if not readings:
+        return None
+    med = sorted(readings)[len(readings) // 2]
+    return {"sclk_mhz": round(med, 1), "readings_mhz": [round(x, 1) for x in readings],
+            "spec_mhz": 2400, "source": "amd-smi metric --clock: median over readings taken while the "
+                                        "step repeats, each the mean of the XCD graphics clocks"}
+
+
 def read_counters():
     if not os.path.exists(COUNTERS_FILE):
         return None
@@ -374,6 +426,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the graphics clock while the step repeats (profiler runs)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-configuration timings (counter passes)")
     ap.add_argument("--blas-reference", action="store_true",
@@ -469,6 +523,8 @@ def main():
             per[n] += ev[j].elapsed_time(ev[j + 1])
     per = {n: v / args.steps for n, v in per.items()}   # ms per launch of each entry point
 
+    gpu_clock = None if args.no_clock else sample_gpu_clock(torch, one_step)
+
     fl = step_flops(M, h, f, Vr)
     total_flops = sum(fl.values())
     tflops = total_flops / (ms * 1e-3) / 1e12
@@ -493,6 +549,7 @@ def main():
                                "fused CE (vocab 51200) + CE merge",
                    "b": w.b, "s": w.s, "h": h, "ffn": ffn, "t": t, "rank": 0, "vocab": V},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "gpu_clock": gpu_clock,
         "mlp_fwd_bwd_tflops": round((fl["mlp_fwd"] + fl["mlp_bwd"]) / ((per["mlp_fwd"] + per["mlp_bwd"]) * 1e-3) / 1e12, 2),
         "mlp_fwd_tflops": round(fl["mlp_fwd"] / (per["mlp_fwd"] * 1e-3) / 1e12, 2),
         "mlp_bwd_tflops": round(fl["mlp_bwd"] / (per["mlp_bwd"] * 1e-3) / 1e12, 2),
