@@ -18,8 +18,9 @@
 //    depends on r & 31, every fragment of a wave is one per-lane address plus
 //    an immediate offset.
 //  * M/N-contiguous operand (element (r,k) at base[k*ld + r]): 32 k-rows of R
-//    values, kept in that orientation, row pitch padded off multiples of
-//    128 B.  Fragments come from two ds_read_b64_tr_b16 (LDS transpose reads:
+//    values, kept in that orientation, in groups of four k-rows whose 64-byte
+//    blocks (32 values) alternate, so no padding is needed for conflict-free
+//    reads.  Fragments come from two ds_read_b64_tr_b16 (LDS transpose reads:
 //    within each 16-lane group, lanes 4j..4j+3 address row j of a 4 x 16
 //    block and lane i receives column i), so no register transposes are needed.
 //
