@@ -208,21 +208,38 @@ hipError_t splitk_sum(const float* W, int splits, int M, int N, void* out, int64
 
 // parts: rank r's block at parts + r*stride holds m[n], l[n], T[n] (T is not
 // read for the log-sum-exp alone).
+// Ranks are taken in chunks of kCombineChunk whose loads are all issued
+// before any is used (a runtime-length loop would wait on each load in turn);
+// chunks merge with the online identity.  For t <= kCombineChunk this is the
+// single pass best = max_r m_r, L = sum_r l_r exp(m_r - best).
+constexpr int kCombineChunk = 8;
 __global__ __launch_bounds__(256) void xent_combine_kernel(const float* __restrict__ parts,
                                                            int64_t stride, int t, int64_t n,
                                                            bool lse_only, float* __restrict__ loss) {
   const int64_t step = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
-    float best = -INFINITY;
-    for (int r = 0; r < t; ++r) {
-      const float v = parts[(int64_t)r * stride + i];
-      best = v > best ? v : best;
-    }
-    float L = 0.f, T = 0.f;
-    for (int r = 0; r < t; ++r) {
-      const float* p = parts + (int64_t)r * stride;
-      L += p[n + i] * __expf(p[i] - best);
-      if (!lse_only) T += p[2 * n + i];
+    float best = -INFINITY, L = 0.f, T = 0.f;
+    for (int r0 = 0; r0 < t; r0 += kCombineChunk) {
+      float m[kCombineChunk], l[kCombineChunk], tt[kCombineChunk];
+#pragma unroll
+      for (int r = 0; r < kCombineChunk; ++r) {
+        const bool ok = r0 + r < t;
+        const float* p = parts + (int64_t)(ok ? r0 + r : 0) * stride;
+        m[r] = ok ? p[i] : -INFINITY;
+        l[r] = ok ? p[n + i] : 0.f;
+        tt[r] = ok && !lse_only ? p[2 * n + i] : 0.f;
+      }
+      float cm = best;
+#pragma unroll
+      for (int r = 0; r < kCombineChunk; ++r) cm = m[r] > cm ? m[r] : cm;
+      float cl = r0 == 0 ? 0.f : L * __expf(best - cm);
+#pragma unroll
+      for (int r = 0; r < kCombineChunk; ++r) {
+        if (r0 + r < t) cl += l[r] * __expf(m[r] - cm);
+        T += tt[r];
+      }
+      best = cm;
+      L = cl;
     }
     loss[i] = best + logf(L) - T;
   }

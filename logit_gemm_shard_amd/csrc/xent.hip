@@ -20,47 +20,49 @@ size_t xent_scratch_bytes(int M, int Vr) {
   return (size_t)max_slabs(Vr) * (size_t)M * 16u;
 }
 
-// Four lanes per token fold the slabs into the rank's partials, each lane
-// walking every fourth slab (independent loads in flight), then combining with
+// Eight lanes per token fold the slabs into the rank's partials, each lane
+// walking every eighth slab (independent loads in flight), then combining with
 // lane shuffles.  Ties on the maximum go to the lowest column, i.e. the first
 // maximum of the slice.
 __global__ __launch_bounds__(256) void xent_merge_kernel(XentSlabs s, int nslabs, int M,
                                                          int vocab_start, float* m_r, float* l_r,
                                                          float* t_r, int32_t* argmax_r,
                                                          float* loss) {
-  const int m = blockIdx.x * 64 + (threadIdx.x >> 2), part = threadIdx.x & 3;
+  constexpr int kLanes = 8;
+  const int m = blockIdx.x * (256 / kLanes) + threadIdx.x / kLanes, part = threadIdx.x % kLanes;
   const bool valid = m < M;
   const int mm = valid ? m : 0;
   float best = -INFINITY;
   int bi = 0x7fffffff;
   if (s.idx) {
 #pragma unroll 4
-    for (int k = part; k < nslabs; k += 4) {
+    for (int k = part; k < nslabs; k += kLanes) {
       const float v = s.m[(int64_t)k * M + mm];
       const int i = s.idx[(int64_t)k * M + mm];
       if (v > best || (v == best && i < bi)) { best = v; bi = i; }
     }
   } else {
 #pragma unroll 4
-    for (int k = part; k < nslabs; k += 4) best = fmaxf(best, s.m[(int64_t)k * M + mm]);
+    for (int k = part; k < nslabs; k += kLanes) best = fmaxf(best, s.m[(int64_t)k * M + mm]);
   }
 #pragma unroll
-  for (int off = 1; off <= 2; off <<= 1) {
+  for (int off = 1; off < kLanes; off <<= 1) {
     const float ob = __shfl_xor(best, off);
     const int oi = __shfl_xor(bi, off);
     if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
   }
   float L = 0.f, T = 0.f;
 #pragma unroll 4
-  for (int k = part; k < nslabs; k += 4) {
+  for (int k = part; k < nslabs; k += kLanes) {
     const int64_t o = (int64_t)k * M + mm;
     L += s.l[o] * fast_exp(s.m[o] - best);
     T += s.t[o];
   }
-  L += __shfl_xor(L, 1);
-  L += __shfl_xor(L, 2);
-  T += __shfl_xor(T, 1);
-  T += __shfl_xor(T, 2);
+#pragma unroll
+  for (int off = 1; off < kLanes; off <<= 1) {
+    L += __shfl_xor(L, off);
+    T += __shfl_xor(T, off);
+  }
   if (!valid || part != 0) return;
   m_r[m] = best;
   l_r[m] = L;
@@ -96,7 +98,7 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
   } else {
     nslabs = (Vr + WN - 1) / WN;
   }
-  hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 63) / 64), dim3(256), 0, s, sl, nslabs, M,
+  hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 31) / 32), dim3(256), 0, s, sl, nslabs, M,
                      vocab_start, m_r, l_r, t_r, argmax_r, loss);
   return hipGetLastError();
 }
