@@ -177,6 +177,7 @@ hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64
 
 // out[m, n] = bf16(sum_s W[s][m][n]) for a split-K GEMM's fp32 partials
 // (W rows of pitch N, slices of M*N), 8 columns per thread; N % 8 == 0.
+constexpr int kSplitChunk = 4;
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ W, int splits, int M,
                                                          int N, bf16* __restrict__ out, int64_t ldo) {
   const int64_t n8 = N / 8, total = (int64_t)M * n8;
@@ -185,14 +186,23 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += step) {
     const int64_t m = i / n8, c = (i - m * n8) * 8;
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < splits; ++sp) {
-      const float* p = W + sp * slice + m * N + c;
-      const u32x4 lo = ld_nt(p), hi = ld_nt(p + 4);
+    for (int s0 = 0; s0 < splits; s0 += kSplitChunk) {  // a chunk's loads issued together
+      u32x4 lo[kSplitChunk], hi[kSplitChunk];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] += __uint_as_float(lo[e]);
-        a[4 + e] += __uint_as_float(hi[e]);
-      }
+      for (int k = 0; k < kSplitChunk; ++k)
+        if (s0 + k < splits) {
+          const float* p = W + (s0 + k) * slice + m * N + c;
+          lo[k] = ld_nt(p);
+          hi[k] = ld_nt(p + 4);
+        }
+#pragma unroll
+      for (int k = 0; k < kSplitChunk; ++k)
+        if (s0 + k < splits)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] += __uint_as_float(lo[k][e]);
+            a[4 + e] += __uint_as_float(hi[k][e]);
+          }
     }
     Vec8<bf16>::store(out + m * ldo + c, a);
   }
