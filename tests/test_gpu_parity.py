@@ -378,20 +378,26 @@ def test_xent_nan_row_stays_in_its_token():
     assert_close("loss (other tokens)", got[keep], ref, BF16)
 
 
-def test_xent_merge_kernel_matches_oracle_merge():
+@pytest.mark.parametrize("t", [1, 3, 8, 9, 16, 21])
+def test_xent_merge_kernel_matches_oracle_merge(t):
+    """The combine takes ranks in chunks of eight: t past 8 merges chunks with
+    the online identity; t <= 8 is one pass."""
     d = dev()
-    t, n = 8, 5000
-    g = np.random.default_rng(4)
+    n = 5000
+    g = np.random.default_rng(4 + t)
     m = g.normal(size=(t, n)) * 5
     l = g.uniform(1, 100, size=(t, n))
     T = np.where(g.uniform(size=(t, n)) < 1 / t, g.normal(size=(t, n)), 0.0)
     parts = torch.from_numpy(np.stack([m, l, T], axis=1).astype(np.float32)).to(d)
-    step("xent merge kernel")
+    step(f"xent merge kernel, t={t}")
     out = torch.empty(n, dtype=F32, device=d)
+    lse = torch.empty(n, dtype=F32, device=d)
     lgs.shard_partial_sum("xent", t, n, parts, 3 * n, out)
+    lgs.shard_partial_sum("xent_lse", t, n, parts, 3 * n, lse)
     sync()
     p32 = parts.cpu().double().numpy()
     assert_close("merge", out, oracle.xent.merge(p32[:, 0], p32[:, 1], p32[:, 2]), F32)
+    assert_close("lse", lse, oracle.xent.merge_lse(p32[:, 0], p32[:, 1]), F32)
 
 
 # ----------------------------------------------------- full sizes, sampled
