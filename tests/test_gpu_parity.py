@@ -359,6 +359,35 @@ def test_xent_uniform_embedding_gives_ln_v():
     assert np.abs(loss.cpu().numpy() - math.log(V)).max() < 1e-6 * math.log(V)
 
 
+@pytest.mark.parametrize("c", [256.0, 1000.0, 4096.0])
+def test_xent_shift_invariance_large_logits(c):
+    """H[:, 0] = c and E[:, 0] = 1 add c to every logit: the loss must not
+    change (the partials are taken relative to each slab's maximum, so
+    exp never sees the raw logit).  Compared with the oracle on the same
+    inputs and with the oracle's loss for the unshifted logits (H[:, 0] = 0)."""
+    d = dev()
+    b, s, h, V, t = 1, 160, 64, 4 * 448, 4
+    H, E = synth.small(37, (b * s, h), (V, h), dtype="bf16")
+    E = (E.float() * 0.5).to(BF16)
+    H[:, 0] = c
+    E[:, 0] = 1.0
+    y = torch.randint(0, V, (b * s,), generator=torch.Generator().manual_seed(3)).to(torch.int32)
+    step(f"xent with every logit shifted by {c}")
+    stats, _ = run_xent_all_ranks(H.to(d), E.to(d), y.to(d), b, s, t)
+    loss = torch.empty(b * s, dtype=F32, device=d)
+    lgs.shard_partial_sum("xent", t, b * s, stats, 3 * b * s, loss)
+    sync()
+    got = loss.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    H64, E64, yn = f64(H), f64(E), y.numpy()
+    assert_close("loss (shifted logits)", got, oracle.xent.naive_loss(H64, E64, yn), BF16)
+    H0 = H64.copy()
+    H0[:, 0] = 0.0
+    # fp32 accumulation near c keeps about 24 - log2(c) bits of each logit's fraction
+    assert np.abs(got - oracle.xent.naive_loss(H0, E64, yn)).max() < 2e-2 * np.abs(got).max()
+    assert np.all(stats.cpu().numpy()[:, 0] > c - 64)  # the slice maxima carry the shift
+
+
 def test_xent_nan_row_stays_in_its_token():
     d = dev()
     b, s, h, V, t = 1, 96, 64, 2 * 512, 2
