@@ -429,6 +429,51 @@ def test_xent_merge_kernel_matches_oracle_merge(t):
     assert_close("lse", lse, oracle.xent.merge_lse(p32[:, 0], p32[:, 1]), F32)
 
 
+# ------------------------------------------------------ degenerate sizes
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("M", [1, 2, 9])
+def test_single_token_and_tiny_batches(M, dtype):
+    """One to nine tokens through the whole path: MLP forward and backward
+    (the weight gradients then have K = M), the sums, and the fused CE with
+    its combine."""
+    d = dev()
+    h, ffn, t, V = 64, 256, 2, 2 * 160
+    dn = "bf16" if dtype == BF16 else "f32"
+    X, A, B, dZ = synth.small(500 + M, (M, h), (h, ffn), (ffn, h), (M, h), dtype=dn)
+    A, B = (A.float() * 0.1).to(dtype), (B.float() * 0.1).to(dtype)
+    X64, A64, B64, dZ64 = f64(X), f64(A), f64(B), f64(dZ)
+    Xd, Ad, Bd, dZd = X.to(d), A.to(d), B.to(d), dZ.to(d)
+    f = ffn // t
+    parts = torch.empty(t, M, h, dtype=dtype, device=d)
+    for r in range(t):
+        step(f"{M} token(s) {dn}: rank {r} forward and backward")
+        U, Y, Z = run_fwd(Xd, Ad, Bd, 1, M, t, r, "erf")
+        parts[r].copy_(Z)
+        dX, dA, dB = run_bwd(Xd, Ad, Bd, U, dZd, 1, M, t, r, "erf")
+        sync()
+        A_i, B_i = A64[:, r * f:(r + 1) * f], B64[r * f:(r + 1) * f]
+        rU, rY, rZ = oracle.mlp.shard_forward(X64, A_i, B_i, "erf")
+        assert_close("Z_i", Z, rZ, dtype)
+        ref = oracle.mlp.shard_backward(X64, A_i, B_i, f64(U), dZ64, "erf")
+        assert_close("dX_i", dX, ref["dX"], dtype)
+        assert_close("dA_i", dA, ref["dA"], dtype)
+        assert_close("dB_i", dB, ref["dB"], dtype)
+    Zs = torch.empty(M, h, dtype=dtype, device=d)
+    lgs.shard_partial_sum("sum", t, M * h, parts, M * h, Zs)
+    sync()
+    assert_close("sum of partials", Zs, oracle.mlp.mlp_forward(X64, A64, B64, "erf")[2], dtype)
+    if dtype == BF16:
+        H, E = synth.small(600 + M, (M, h), (V, h), dtype="bf16")
+        y = (torch.arange(M, dtype=torch.int32) * 37 + 5) % V
+        step(f"{M} token(s): fused CE, {t} ranks")
+        stats, _ = run_xent_all_ranks(H.to(d), E.to(d), y.to(d), 1, M, t)
+        loss = torch.empty(M, dtype=F32, device=d)
+        lgs.shard_partial_sum("xent", t, M, stats, 3 * M, loss)
+        sync()
+        assert_close("loss", loss, oracle.xent.naive_loss(f64(H), f64(E), y.numpy()), BF16)
+
+
 # ----------------------------------------------------- full sizes, sampled
 
 _cache = {}
