@@ -37,6 +37,8 @@ RAGGED = [  # (b, s, h, n_q, n_kv, d, t)
     (2, 130, 264, 12, 4, 24, 4),
     (1, 520, 1032, 16, 8, 64, 8),
     (1, 700, 512, 8, 8, 128, 2),
+    (1, 1, 128, 4, 2, 32, 2),   # a single token
+    (1, 9, 128, 4, 2, 32, 2),
 ]
 
 

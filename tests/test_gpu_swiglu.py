@@ -61,6 +61,8 @@ RAGGED = [  # (b, s, h, ffn, t): several tiles, ragged tails in M, N and K
     (1, 520, 328, 600, 3),
     (1, 33, 72, 128, 8),
     (2, 1100, 1064, 2 * 1048, 2),
+    (1, 1, 64, 256, 2),   # a single token (the weight gradients have K = 1)
+    (1, 9, 64, 256, 2),
 ]
 
 

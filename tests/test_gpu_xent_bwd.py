@@ -58,6 +58,8 @@ SMALL = [  # (b, s, h, V, t): ragged token counts, slices of several tiles with 
     (1, 64, 64, 8 * 136, 8),
     (1, 520, 264, 2 * 1288, 2),
     (2, 1000, 136, 24640, 1),  # wide enough that the logit GEMM splits its columns over two launches
+    (1, 1, 64, 2 * 160, 2),    # a single token (dE's GEMM has K = 1)
+    (1, 9, 64, 2 * 160, 2),
 ]
 
 
