@@ -203,16 +203,27 @@ BLAS_SHAPES = [
 def blas_reference(reps=20):
     """torch.matmul in bf16 (hipBLASLt on ROCm) at the library's GEMM shapes:
     a vendor-library reference point for the same products (plain C = A B,
-    no epilogue), timed with HIP events."""
+    no epilogue), timed with HIP events, next to this library's GEMM core on
+    the same inputs with a plain store epilogue (the testing entry point;
+    A K-contiguous, B N-contiguous, as torch.matmul of two row-major
+    matrices).  The two alternate three times; the best of each is kept."""
     import torch
+    from logit_gemm_shard_amd import binding as lgs
     dev = torch.device("cuda", 0)
     out = []
     for M, N, K, what in BLAS_SHAPES:
         a = torch.randn(M, K, device=dev).to(torch.bfloat16)
         b = torch.randn(K, N, device=dev).to(torch.bfloat16)
-        ms = time_calls(torch, lambda: torch.matmul(a, b), reps, warmup=5)
-        out.append({"M": M, "N": N, "K": K, "what": what, "us": round(ms * 1e3, 1),
-                    "tflops": round(2 * M * N * K / ms / 1e9, 1)})
+        c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        theirs, ours = [], []
+        for _ in range(3):
+            theirs.append(time_calls(torch, lambda: torch.matmul(a, b), reps, warmup=5))
+            ours.append(time_calls(torch, lambda: lgs.gemm_bf16(a, b, c, True, False, -1), reps, warmup=5))
+        t_ms, o_ms = min(theirs), min(ours)
+        out.append({"M": M, "N": N, "K": K, "what": what, "us": round(t_ms * 1e3, 1),
+                    "tflops": round(2 * M * N * K / t_ms / 1e9, 1), "library_us": round(o_ms * 1e3, 1),
+                    "library_tflops": round(2 * M * N * K / o_ms / 1e9, 1),
+                    "library_tile": "x".join(map(str, lgs.tile_shapes()[lgs.pick_tile(M, N)]))})
     print(json.dumps({"blas_reference": out, "library": "torch.matmul bf16 (hipBLASLt)"}), flush=True)
 
 
