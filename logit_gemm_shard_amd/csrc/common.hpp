@@ -25,7 +25,14 @@ enum Act : int { ACT_ERF = 0, ACT_TANH = 1 };
 //   erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2) + e(z),
 //   |e(z)| <= 1.5e-7,
 // which is branch-free (one exp, one reciprocal) and shares exp(-u^2/2) with
-// the density phi(u) needed by GeLU'.  Both values come out of one call.
+// the density phi(u) needed by GeLU'.
+//
+// The epilogues evaluate it per element on the vector ALU, at 4 cycles per
+// 64-lane instruction, so the forms below are arranged for few instructions:
+// z = |u| / sqrt(2) is folded into p, the factor 1/2 of Phi = (1 + erf) / 2
+// into the a_k (halving is exact in binary, so the tail is unchanged), and
+// GeLU(u) = max(u, 0) - |u| (1 - Phi(|u|)) needs no select.  A non-finite u
+// gives a non-finite result.
 struct GeluVals {
   float y;   // GeLU(u)
   float dy;  // GeLU'(u)
@@ -35,24 +42,88 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);  // v_exp_f32 computes 2^x
 }
 
-__device__ __forceinline__ GeluVals gelu_both(float u, int act) {
+// 1 - Phi(|u|) and exp(-u^2 / 2).
+struct PhiTail {
+  float tail, e;
+};
+__device__ __forceinline__ PhiTail phi_tail(float u) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(u), 0.23164188826636040f, 1.0f));  // p / sqrt(2)
+  const float e = __builtin_amdgcn_exp2f(u * u * -0.72134752044448170f);  // 2^(-u^2 log2(e) / 2)
+  float q = fmaf(t, 0.5307027145f, -0.7265760135f);  // a5 / 2, a4 / 2
+  q = fmaf(t, q, 0.7107068705f);
+  q = fmaf(t, q, -0.142248368f);
+  q = fmaf(t, q, 0.127414796f);
+  return {(q * t) * e, e};
+}
+
+// tanh form: with a = sqrt(2/pi) (u + 0.044715 u^3) and r = 1 / (1 + exp(2a)),
+// (1 + tanh a) / 2 = 1 - r, so GeLU(u) = u (1 - r) and
+// GeLU'(u) = (1 - r) (1 + 2 u r a'(u)), a'(u) = sqrt(2/pi) (1 + 0.134145 u^2).
+// exp(2a) overflows to inf for u >> 0 (r = 0) and underflows to 0 for u << 0 (r = 1).
+__device__ __forceinline__ float tanh_r(float u, float uu) {
+  const float a2 = u * fmaf(uu, 0.10294323958002350f, 2.3022081981443250f);  // 2 a log2(e)
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a2));
+}
+
+// max(u, 0) as one integer max on the bit pattern (negative floats, -0
+// included, are negative integers); fmaxf would first quiet u in IEEE mode,
+// one more instruction.
+__device__ __forceinline__ float pos_part(float u) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, u), 0));
+}
+
+__device__ __forceinline__ float gelu_erf(float u) {
+  return fmaf(-fabsf(u), phi_tail(u).tail, pos_part(u));
+}
+
+__device__ __forceinline__ GeluVals gelu_erf_both(float u) {
+  const PhiTail q = phi_tail(u);
+  const float phi = u >= 0.f ? 1.0f - q.tail : q.tail;  // Phi(u)
+  return {fmaf(-fabsf(u), q.tail, pos_part(u)), fmaf(u * 0.39894228040143270f, q.e, phi)};
+}
+
+__device__ __forceinline__ float gelu_tanh(float u) {
+  return fmaf(-u, tanh_r(u, u * u), u);
+}
+
+__device__ __forceinline__ GeluVals gelu_tanh_both(float u) {
+  const float uu = u * u;
+  const float r = tanh_r(u, uu);
+  const float omr = 1.0f - r;
+  const float da2 = fmaf(uu, 0.21406444881780073f, 1.5957691216057308f);  // 2 a'(u)
+  return {u * omr, omr * fmaf(u * r, da2, 1.0f)};
+}
+
+// Elementwise over W values; the form is chosen once per call (act is
+// uniform), so the W evaluations interleave.
+template <int W>
+__device__ __forceinline__ void gelu_vec(const float* u, float* y, int act) {
   if (act == ACT_ERF) {
-    const float z = fabsf(u) * 0.70710678118654752f;  // |u| / sqrt(2)
-    const float e = fast_exp(-z * z);                  // exp(-u^2/2)
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float p = fmaf(t, 1.061405429f, -1.453152027f);
-    p = fmaf(t, p, 1.421413741f);
-    p = fmaf(t, p, -0.284496736f);
-    p = fmaf(t, p, 0.254829592f);
-    const float tail = 0.5f * (p * t) * e;             // 1 - Phi(|u|)
-    const float phi = u >= 0.f ? 1.0f - tail : tail;   // Phi(u)
-    return {u * phi, fmaf(u * 0.39894228040143268f, e, phi)};
+#pragma unroll
+    for (int i = 0; i < W; ++i) y[i] = gelu_erf(u[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) y[i] = gelu_tanh(u[i]);
   }
-  // tanh(a) = 1 - 2 / (1 + exp(2a)), finite at both ends (exp -> 0 or inf)
-  const float a = 0.79788456080286536f * fmaf(0.044715f * u, u * u, u);
-  const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + fast_exp(2.0f * a));
-  const float da = 0.79788456080286536f * fmaf(0.134145f * u, u, 1.0f);
-  return {0.5f * u * (1.0f + th), fmaf(0.5f * u * (1.0f - th * th), da, 0.5f * (1.0f + th))};
+}
+
+template <int W>
+__device__ __forceinline__ void gelu_both_vec(const float* u, float* y, float* dy, int act) {
+  if (act == ACT_ERF) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const GeluVals g = gelu_erf_both(u[i]);
+      y[i] = g.y;
+      dy[i] = g.dy;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const GeluVals g = gelu_tanh_both(u[i]);
+      y[i] = g.y;
+      dy[i] = g.dy;
+    }
+  }
 }
 
 // Swish(g) = g * sigmoid(g), the gate nonlinearity of the SwiGLU MLP block
@@ -96,17 +167,26 @@ __device__ __forceinline__ void store_vec(float* p, const float* v) {
 #pragma unroll
   for (int i = 0; i < W; ++i) p[i] = v[i];
 }
+// bf16 -> fp32 of W packed values: a bf16 is the high half of its fp32, so
+// the even element of each 32-bit pair is one shift and the odd one one mask
+// (the generic conversion spends two shifts on the odd one).
+template <int W, class V>
+__device__ __forceinline__ void unpack_bf16(const V& x, float* v) {
+  static_assert(sizeof(V) == 2 * W && W % 2 == 0, "packed bf16 vector");
+  uint32_t w[W / 2];
+  __builtin_memcpy(w, &x, sizeof(w));
+#pragma unroll
+  for (int i = 0; i < W / 2; ++i) {
+    v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
 template <int W>
 __device__ __forceinline__ void load_vec(const bf16* p, float* v) {
-  if constexpr (W == 8) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
-  } else {
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (float)x[i];
-  }
+  if constexpr (W == 8)
+    unpack_bf16<8>(*reinterpret_cast<const bf16x8*>(p), v);
+  else
+    unpack_bf16<4>(*reinterpret_cast<const bf16x4*>(p), v);
 }
 template <int W>
 __device__ __forceinline__ void load_vec(const float* p, float* v) {

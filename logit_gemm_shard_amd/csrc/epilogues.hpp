@@ -46,8 +46,7 @@ struct EpiGeluFwd {
     if (m >= M || n >= N) return;
     if (U) store_vec<W>(U + (int64_t)m * ldu + n, v);
     float y[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) y[i] = gelu_both(v[i], act).y;
+    gelu_vec<W>(v, y, act);
     store_vec<W>(Y + (int64_t)m * ldy + n, y);
   }
 };
@@ -71,8 +70,7 @@ struct EpiGeluBwd {
   }
   __device__ __forceinline__ void apply8(int m, int n, const float* dy, bf16x8 u8) const {
     float u[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = (float)u8[i];
+    unpack_bf16<8>(u8, u);
     finish<8>(m, n, dy, u);
   }
   template <int W>
@@ -86,12 +84,9 @@ struct EpiGeluBwd {
   __device__ __forceinline__ void finish(int m, int n, const float* dy, const float* u) const {
     if (m >= M || n >= N) return;
     float du[W], y[W];
+    gelu_both_vec<W>(u, y, du, act);
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-      const GeluVals g = gelu_both(u[i], act);
-      du[i] = dy[i] * g.dy;
-      y[i] = g.y;
-    }
+    for (int i = 0; i < W; ++i) du[i] *= dy[i];
     store_vec<W>(dU + (int64_t)m * lddu + n, du);
     store_vec<W>(Y + (int64_t)m * ldy + n, y);
   }
@@ -188,10 +183,12 @@ struct EpiSwigluBwd {
   }
   __device__ __forceinline__ void apply8(int m, int n, const float* dy, GateUp8 in) const {
     if (m >= M || n >= half) return;
-    float dg[8], du[8], y[8];
+    float dg[8], du[8], y[8], gv[8], uv[8];
+    unpack_bf16<8>(in.g, gv);
+    unpack_bf16<8>(in.u, uv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float g = (float)in.g[i], u = (float)in.u[i];
+      const float g = gv[i], u = uv[i];
       const SwishVals sw = swish_both(g);
       dg[i] = dy[i] * u * sw.dy;
       du[i] = dy[i] * sw.y;
