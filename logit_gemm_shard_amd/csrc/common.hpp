@@ -60,9 +60,11 @@ __device__ __forceinline__ PhiTail phi_tail(float u) {
 // (1 + tanh a) / 2 = 1 - r, so GeLU(u) = u (1 - r) and
 // GeLU'(u) = (1 - r) (1 + 2 u r a'(u)), a'(u) = sqrt(2/pi) (1 + 0.134145 u^2).
 // exp(2a) overflows to inf for u >> 0 (r = 0) and underflows to 0 for u << 0 (r = 1).
+__device__ __forceinline__ float tanh_exp2a(float u, float uu) {
+  return __builtin_amdgcn_exp2f(u * fmaf(uu, 0.10294323958002350f, 2.3022081981443250f));  // 2 a log2(e)
+}
 __device__ __forceinline__ float tanh_r(float u, float uu) {
-  const float a2 = u * fmaf(uu, 0.10294323958002350f, 2.3022081981443250f);  // 2 a log2(e)
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a2));
+  return __builtin_amdgcn_rcpf(1.0f + tanh_exp2a(u, uu));
 }
 
 // max(u, 0) as one integer max on the bit pattern (negative floats, -0
@@ -86,10 +88,13 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return fmaf(-u, tanh_r(u, u * u), u);
 }
 
+// For u < 0, 1 - r = exp(2a) r avoids the cancellation of 1 - r with r near
+// 1, which GeLU' multiplies by |2 u a'(u)| (about 30 at u = -5).
 __device__ __forceinline__ GeluVals gelu_tanh_both(float u) {
   const float uu = u * u;
-  const float r = tanh_r(u, uu);
-  const float omr = 1.0f - r;
+  const float e2a = tanh_exp2a(u, uu);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e2a);
+  const float omr = u >= 0.f ? 1.0f - r : e2a * r;
   const float da2 = fmaf(uu, 0.21406444881780073f, 1.5957691216057308f);  // 2 a'(u)
   return {u * omr, omr * fmaf(u * r, da2, 1.0f)};
 }

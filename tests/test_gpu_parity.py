@@ -671,10 +671,16 @@ def test_xent_rows_full_size_sampled():
 def test_gelu_epilogue_error_bound(act):
     """fp32 path with X = I, dZ = I, B_i = 1: then U = A_i exactly, the
     backward's dA_i = GeLU'(U) and dB_i = GeLU(U)^T exactly (one nonzero
-    product per sum), which isolates the device GeLU / GeLU' evaluation."""
+    product per sum), which isolates the device GeLU / GeLU' evaluation.
+    The last row holds large magnitudes, where both forms saturate (the erf
+    tail and exp(-u^2/2) underflow to 0; the tanh form's exp(2a) overflows
+    or underflows): GeLU(u) must be u or 0 and GeLU'(u) 1 or 0 there."""
     d = dev()
     n = 64
     u = torch.linspace(-10.0, 10.0, n * n, dtype=F32).reshape(n, n)
+    big = torch.tensor([-1e4, -1e3, -100.0, -40.0, -30.0, -20.0, -15.0, -12.0,
+                        12.0, 15.0, 20.0, 30.0, 40.0, 100.0, 1e3, 1e4], dtype=F32)
+    u[-1] = big.repeat(n // big.numel())
     eye = torch.eye(n, dtype=F32)
     step(f"GeLU epilogue error bound ({act})")
     U, Y, Z = run_fwd(eye.to(d), u.to(d), torch.ones(n, n, dtype=F32, device=d), 1, n, 1, 0, act)
