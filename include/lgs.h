@@ -142,7 +142,10 @@ int tp_mlp_fwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act
  * Inputs X [M,h], A_i [h,f], B_i [f,h] as in tp_mlp_fwd; U_i [M, f] the saved
  * pre-activation; dZ [M, h].  Outputs dX_i, dA_i, dB_i (same dtype, each with
  * its ld).  dA_i / dB_i may point into full [h, ffn] / [ffn, h] gradients.
- * Workspace: lgs_mlp_bwd_workspace_bytes (holds Y_i and dU_i).
+ * Workspace: lgs_mlp_bwd_workspace_bytes (holds Y_i and dU_i; for bf16 shapes
+ * whose weight gradients are split over the tokens, also their fp32 partial
+ * sums and per-tile counters, which the call clears itself).  Calls that share
+ * one workspace must not overlap.
  */
 int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
                const void* X, int64_t ldx, const void* A_i, int64_t lda, const void* B_i,

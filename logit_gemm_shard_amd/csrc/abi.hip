@@ -117,9 +117,13 @@ LGS_API size_t lgs_mlp_fwd_workspace_bytes(int b, int s, int h, int ffn, int t, 
   return round256((size_t)b * s * (ffn / t) * elt(dtype));
 }
 
+// Y_i and dU_i, then (bf16, when the grouped launch splits dB and dA over K)
+// their partial sums and counters.
 LGS_API size_t lgs_mlp_bwd_workspace_bytes(int b, int s, int h, int ffn, int t, int dtype) {
   if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || ffn <= 0 || ffn % t) return 0;
-  return 2 * round256((size_t)b * s * (ffn / t) * elt(dtype));
+  if ((int64_t)b * s > INT_MAX) return 0;
+  const size_t split = dtype == LGS_BF16 ? lgs::mlp_bwd_split_bytes(b * s, h, ffn / t) : 0;
+  return 2 * round256((size_t)b * s * (ffn / t) * elt(dtype)) + split;
 }
 
 namespace {
@@ -198,11 +202,13 @@ LGS_API int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dU_i, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t half = round256((size_t)M * f * elt(dtype));
   char* y = (char*)workspace;
-  char* du = y + need / 2;
+  char* du = y + half;
+  char* split = need > 2 * half ? y + 2 * half : nullptr;
   (void)hipGetLastError();
   return launched(lgs::mlp_bwd(dtype == LGS_BF16, M, h, f, act, X, ldx, A_i, lda, B_i, ldb, U_i,
-                               ldu, dZ, lddz, dX_i, lddx, dA_i, ldda, dB_i, lddb, y, du,
+                               ldu, dZ, lddz, dX_i, lddx, dA_i, ldda, dB_i, lddb, y, du, split,
                                (hipStream_t)stream));
 }
 
@@ -287,7 +293,7 @@ int bwd_workspace(int b, int s, int h, int ffn, int t, int dtype, void* workspac
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   *y = (char*)workspace;
-  *du = *y + need / 2;
+  *du = *y + round256((size_t)b * s * (ffn / t) * elt(dtype));
   return LGS_OK;
 }
 

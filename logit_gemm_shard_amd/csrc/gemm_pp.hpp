@@ -76,8 +76,85 @@ struct PPProblem {
   __host__ __device__ int tiles() const { return tiles_m() * tiles_n(); }
 };
 
-template <class P>
-__device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, int tni) {
+// No in-launch reduction: the tile's accumulators go straight to its epilogue.
+struct NoFix {
+  static constexpr bool kActive = false;
+};
+
+// In-launch reduction of a tile whose K range is split into `parts` blocks of
+// the same launch.  Every part writes its fp32 accumulators to its slot of the
+// tile's partial buffer (in the accumulator lane layout: one 16-byte vector
+// per lane per 4 values, so every access is a contiguous 1 KB per wave) and
+// counts itself in the tile's counter.  The part that arrives last adds all
+// slots in part order, which makes the sum independent of the arrival order,
+// and continues to the epilogue; the others end.  No part waits for another.
+//
+// The parts may run on different XCDs, each with its own L2.  The slots are
+// written and read with device-scope accesses (sc1: written through to, and
+// read from, the memory side), and each wave's slot stores have completed
+// (vmcnt 0) before the block counts itself, so the last part reads every
+// slot whole.  No L2-wide fence is needed: one (write back and invalidate the
+// XCD's whole L2) costs the other tiles streaming through that L2 their
+// cached operand panels.  The counter must be 0 at launch; the last part
+// sets it back to 0.
+struct KPartFix {
+  static constexpr bool kActive = true;
+  static constexpr int kDeviceScope = 16;  // buffer cache policy: sc1
+  float* part;  // this tile's slots: [parts][kPPWaves][TM][TN][4][64] f32x4
+  int* count;   // this tile's arrival counter
+  int s, parts;
+  template <int TM, int TN>
+  __device__ __forceinline__ bool reduce(f32x16 (&acc)[TM][TN], char* smem, int wave, int lane) const {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kWaveBytes = TM * TN * 4 * 64 * 16;
+    constexpr int kPartBytes = kPPWaves * kWaveBytes;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(part, (uint32_t)(parts * kPartBytes));
+    const int base = wave * kWaveBytes + lane * 16;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                                 s * kPartBytes + base + ((i * TN + j) * 4 + q) * 1024, 0,
+                                                 kDeviceScope);
+        }
+    wait_vmcnt<0>();  // this wave's slot stores are complete
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(smem);  // the LDS ring is free: every wave is past the K loop
+    if (threadIdx.x == 0) {
+      const int last = atomicAdd(count, 1) == parts - 1;
+      if (last) atomicExch(count, 0);
+      *flag = last;
+    }
+    __syncthreads();
+    const bool last = *flag != 0;
+    __syncthreads();
+    if (!last) return false;
+    // Slot 0, then slots 1, 2, ... added in order; each slot's loads are
+    // issued together.
+    for (int u = 0; u < parts; ++u) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 t = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, u * kPartBytes + base + ((i * TN + j) * 4 + q) * 1024,
+                                                             0, kDeviceScope));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = u ? acc[i][j][4 * q + e] + t[e] : t[e];
+          }
+    }
+    return true;
+  }
+};
+
+template <class P, class Fix = NoFix>
+__device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, int tni, const Fix& fix = Fix{}) {
   using T = typename P::T;
   using LA = typename T::LA;
   using LB = typename T::LB;
@@ -224,6 +301,10 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
   }
   if (grp == 0) block_barrier();
   wait_vmcnt<0>();  // the (zero) loads past the end must land before LDS is reused
+  if constexpr (Fix::kActive) {
+    __syncthreads();  // every wave is past its last read of the LDS ring
+    if (!fix.template reduce<TM, TN>(acc, smem, wave, lane)) return;
+  }
 
   const int mb = m0 + wm * T::WM, nb = n0 + wn * T::WN;
   if constexpr (P::Epi::kDirect) {
@@ -313,6 +394,73 @@ template <class P>
 inline hipError_t launch_gemm_pp_splitk(const P& p, int splits, int kchunk, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_pp_splitk_kernel<P>), dim3(p.tiles() * splits), dim3(kPPThreads), 0, stream, p,
                      kchunk);
+  return hipGetLastError();
+}
+
+// The problem restricted to K range [k0, k0 + kc): both operands move to the
+// range's first K row or column, so the range is an ordinary GEMM.
+template <class P>
+__device__ __forceinline__ P k_range(const P& p, int k0, int kc) {
+  P q = p;
+  q.A = P::AK ? p.A + k0 : p.A + (int64_t)k0 * p.lda;
+  q.B = P::BK ? p.B + k0 : p.B + (int64_t)k0 * p.ldb;
+  q.K = min(kc, p.K - k0);
+  return q;
+}
+
+// Partial buffers and counters of the K-split problems of one grouped launch.
+struct KSplit {
+  float* part;  // [tiles of p0, then of p1][parts][BM * BN] fp32
+  int* count;   // [tiles of p0, then of p1]
+  int parts, kchunk;
+};
+
+template <class P>
+__device__ __forceinline__ void run_k_part(const P& p, const KSplit& k, int tile0, int b, char* smem) {
+  const int tiles = p.tiles(), s = b / tiles, t = b - s * tiles;
+  int tmi, tni;
+  tile_of_block(t, tiles, p.tiles_m(), p.tiles_n(), tmi, tni);
+  const int64_t slot = (int64_t)P::BM * P::BN;
+  const KPartFix fix{k.part + (int64_t)(tile0 + t) * k.parts * slot, k.count + tile0 + t, s, k.parts};
+  gemm_tile_pp(k_range(p, s * k.kchunk, k.kchunk), smem, tmi, tni, fix);
+}
+
+// gemm_pp_group3_kernel with p0 and p1 split over K into k.parts parts each,
+// reduced inside the launch (KPartFix).  Blocks: p0's parts (part-major),
+// then p1's, then p2's tiles.
+template <class P0, class P1, class P2>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_group3_ksplit_kernel(P0 p0, P1 p1, P2 p2, KSplit k) {
+  constexpr int kL0 = P0::T::kLdsBytes, kL1 = P1::T::kLdsBytes, kL2 = P2::T::kLdsBytes;
+  constexpr int kL = kL0 > kL1 ? (kL0 > kL2 ? kL0 : kL2) : (kL1 > kL2 ? kL1 : kL2);
+  __shared__ __attribute__((aligned(1024))) char smem[kL];
+  int pid = blockIdx.x;
+  const int t0 = p0.tiles(), t1 = p1.tiles();
+  if (pid < t0 * k.parts) {
+    run_k_part(p0, k, 0, pid, smem);
+  } else if ((pid -= t0 * k.parts) < t1 * k.parts) {
+    run_k_part(p1, k, t0, pid, smem);
+  } else {
+    pid -= t1 * k.parts;
+    int tmi, tni;
+    tile_of_block(pid, p2.tiles(), p2.tiles_m(), p2.tiles_n(), tmi, tni);
+    gemm_tile_pp(p2, smem, tmi, tni);
+  }
+}
+
+static __global__ __launch_bounds__(256) void zero_i32_kernel(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+template <class P0, class P1, class P2>
+inline hipError_t launch_gemm_pp_group3_ksplit(const P0& p0, const P1& p1, const P2& p2, const KSplit& k,
+                                               hipStream_t stream) {
+  const int counters = p0.tiles() + p1.tiles();
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((counters + 255) / 256), dim3(256), 0, stream, k.count, counters);
+  hipLaunchKernelGGL((gemm_pp_group3_ksplit_kernel<P0, P1, P2>),
+                     dim3((p0.tiles() + p1.tiles()) * k.parts + p2.tiles()), dim3(kPPThreads), 0, stream, p0, p1,
+                     p2, k);
   return hipGetLastError();
 }
 

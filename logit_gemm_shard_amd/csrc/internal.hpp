@@ -17,10 +17,21 @@ hipError_t mlp_fwd(bool bf16, int M, int h, int f, int act, const void* X, int64
 // One rank's MLP shard backward from the saved X and U and the incoming dZ.
 //   dY = dZ B_i^T, dU = dY * GeLU'(U), Y = GeLU(U)  (Y, dU in scratch)
 //   dB_i = Y^T dZ, dA_i = X^T dU, dX_i = dU A_i^T
+//   splitws: partial sums and counters of the K-split dB / dA (bf16 only,
+//   mlp_bwd_split_bytes of them; may be null when that is 0).
 hipError_t mlp_bwd(bool bf16, int M, int h, int f, int act, const void* X, int64_t ldx,
                    const void* A, int64_t lda, const void* B, int64_t ldb, const void* U,
                    int64_t ldu, const void* dZ, int64_t lddz, void* dX, int64_t lddx, void* dA,
-                   int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, hipStream_t s);
+                   int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, void* splitws,
+                   hipStream_t s);
+
+// How the bf16 backward's grouped launch splits dB and dA over K: parts (1 =
+// not split), the K rows per part, and the dB plus dA tile count.
+struct BwdSplit {
+  int parts, kchunk, tiles;
+};
+BwdSplit mlp_bwd_wsplit(int M, int h, int f);
+size_t mlp_bwd_split_bytes(int M, int h, int f);  // 0 when not split
 
 // The same backward in three parts: dgelu (dY, dU = dY GeLU'(U), Y into
 // scratch), then dx (dX_i = dU A_i^T) and dw (dB_i = Y^T dZ, dA_i = X^T dU),

@@ -19,12 +19,81 @@
 //   dX = dU A_i^T   : dU K-contiguous,           A_i K-contiguous
 //   dB = Y^T dZ     : Y M-contiguous (K=tokens), dZ N-contiguous
 //   dA = X^T dU     : X M-contiguous,            dU N-contiguous
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "dispatch.hpp"
 #include "epilogues.hpp"
 #include "gemm_f32.hpp"
 #include "internal.hpp"
 
 namespace lgs {
+
+namespace {
+
+// Finish time, in K tiles of one 256x256 tile, of a launch whose blocks are
+// dealt in launch order to the first free of the 256 compute units.  items:
+// (K tiles per block, blocks), in launch order.
+int dispatch_makespan(const std::vector<std::pair<int, int>>& items) {
+  std::priority_queue<int, std::vector<int>, std::greater<int>> cu;
+  for (int i = 0; i < 256; ++i) cu.push(0);
+  int end = 0;
+  for (const auto& it : items)
+    for (int b = 0; b < it.second; ++b) {
+      const int t = cu.top() + it.first;
+      cu.pop();
+      cu.push(t);
+      end = t > end ? t : end;
+    }
+  return end;
+}
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+// The grouped backward launch (dB, dA over K = M tokens; dX over K = f) ends
+// when its longest tiles do: at the 8.3B shape 144 dB / dA tiles of 256 K
+// tiles each, while the whole launch would fill 256 compute units for 216.
+// Splitting dB and dA over K into parts reduced inside the launch shortens
+// them.  The plan simulates the dispatch for 1 to 4 parts, charging each part
+// two K tiles for its partial slot and the last part two per slot it adds.
+// The partial slots' memory traffic also slows every other tile's K loop,
+// which the simulation does not see: measured, a predicted 7% gain (8.3B
+// shape, 3 parts) ran 14% slower, a predicted 40% gain (M = 2200, h = 1064,
+// f = 1048, 2 parts) ran 10% faster.  So the plan splits only where the
+// simulation predicts 30% or more.
+BwdSplit mlp_bwd_wsplit(int M, int h, int f) {
+  BwdSplit no{1, 0, 0};
+  if (M < 256 || h < 256 || f < 256) return no;
+  const int tw = cdiv(f, 256) * cdiv(h, 256), tx = cdiv(M, 256) * cdiv(h, 256);
+  const int nkw = cdiv(M, 32), nkx = cdiv(f, 32);
+  const int unsplit = dispatch_makespan({{nkw, 2 * tw}, {nkx, tx}});
+  int best_cost = unsplit;
+  BwdSplit best = no;
+  for (int parts = 2; parts <= 4; ++parts) {
+    const int kchunk = cdiv(cdiv(M, parts), 32) * 32, n = cdiv(M, kchunk);
+    if (n < 2) continue;
+    const int u = kchunk / 32, last = nkw - (n - 1) * u;
+    // launch order: dB's parts (part-major), dA's parts, dX
+    const std::vector<std::pair<int, int>> items = {{u + 2, tw * (n - 1)}, {last + 2, tw},
+                                                    {u + 2, tw * (n - 1)}, {last + 2, tw}, {nkx, tx}};
+    const int cost = dispatch_makespan(items) + 2 * n;
+    if (cost * 10 < unsplit * 7 && cost < best_cost) {
+      best_cost = cost;
+      best = BwdSplit{n, kchunk, 2 * tw};
+    }
+  }
+  return best;
+}
+
+size_t mlp_bwd_split_bytes(int M, int h, int f) {
+  const BwdSplit k = mlp_bwd_wsplit(M, h, f);
+  if (k.parts < 2) return 0;
+  const size_t part = (size_t)k.tiles * k.parts * 256 * 256 * sizeof(float);
+  return part + (((size_t)k.tiles * sizeof(int) + 255) & ~(size_t)255);
+}
 
 hipError_t mlp_fwd(bool is_bf16, int M, int h, int f, int act, const void* X, int64_t ldx,
                    const void* A, int64_t lda, const void* B, int64_t ldb, void* U, int64_t ldu,
@@ -49,7 +118,8 @@ hipError_t mlp_fwd(bool is_bf16, int M, int h, int f, int act, const void* X, in
 hipError_t mlp_bwd(bool is_bf16, int M, int h, int f, int act, const void* X, int64_t ldx,
                    const void* A, int64_t lda, const void* B, int64_t ldb, const void* U,
                    int64_t ldu, const void* dZ, int64_t lddz, void* dX, int64_t lddx, void* dA,
-                   int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, hipStream_t s) {
+                   int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, void* splitws,
+                   hipStream_t s) {
   hipError_t e;
   const int64_t ldw = f;  // scratch Y / dU are dense [M, f]
   if (is_bf16) {
@@ -64,10 +134,18 @@ hipError_t mlp_bwd(bool is_bf16, int M, int h, int f, int act, const void* X, in
     EpiStore<bf16> eb{(bf16*)dB, lddb, f, h};
     EpiStore<bf16> ea{(bf16*)dA, ldda, h, f};
     EpiStore<bf16> ex{(bf16*)dX, lddx, M, h};
-    if (f >= 256 && h >= 256 && M >= 256)
-      return launch_gemm_pp_group3(pp_problem<256, 256, false, false>(y, ldw, dz, lddz, f, h, M, eb),
-                                   pp_problem<256, 256, false, false>(x, ldx, du, ldw, h, f, M, ea),
-                                   pp_problem<256, 256, true, true>(du, ldw, a, lda, M, h, f, ex), s);
+    if (f >= 256 && h >= 256 && M >= 256) {
+      const auto pb = pp_problem<256, 256, false, false>(y, ldw, dz, lddz, f, h, M, eb);
+      const auto pa = pp_problem<256, 256, false, false>(x, ldx, du, ldw, h, f, M, ea);
+      const auto px = pp_problem<256, 256, true, true>(du, ldw, a, lda, M, h, f, ex);
+      const BwdSplit k = mlp_bwd_wsplit(M, h, f);
+      if (k.parts > 1 && splitws) {
+        float* part = (float*)splitws;
+        int* count = (int*)((char*)splitws + (size_t)k.tiles * k.parts * 256 * 256 * sizeof(float));
+        return launch_gemm_pp_group3_ksplit(pb, pa, px, KSplit{part, count, k.parts, k.kchunk}, s);
+      }
+      return launch_gemm_pp_group3(pb, pa, px, s);
+    }
     return launch_gemm_pp_group3(pp_problem<128, 128, false, false>(y, ldw, dz, lddz, f, h, M, eb),
                                  pp_problem<128, 128, false, false>(x, ldx, du, ldw, h, f, M, ea),
                                  pp_problem<128, 128, true, true>(du, ldw, a, lda, M, h, f, ex), s);

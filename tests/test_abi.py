@@ -119,6 +119,24 @@ def test_mlp_bwd_validation(L):
     assert bwd(ws_bytes=need - 1) == 3
 
 
+def test_mlp_bwd_workspace_holds_the_weight_gradient_split(L):
+    """Y_i and dU_i, plus, for bf16 shapes whose dB / dA tiles are few and
+    long (many tokens, small h and f), the K-split partial sums (fp32, one
+    256x256 slot per tile and part) and one counter per tile."""
+    def plain(b, s, ffn, t, el):
+        return 2 * (((b * s * (ffn // t) * el) + 255) // 256 * 256)
+    L.lgs_mlp_bwd_workspace_bytes.restype = ctypes.c_size_t
+    # the benchmark shapes: not split
+    assert L.lgs_mlp_bwd_workspace_bytes(8, 1024, 3072, 12288, 8, 1) == plain(8, 1024, 12288, 8, 2)
+    assert L.lgs_mlp_bwd_workspace_bytes(1, 4096, 8192, 28672, 8, 1) == plain(1, 4096, 28672, 8, 2)
+    # M = 8264 tokens, h = 776, f = 520: 3 x 4 tiles each for dB and dA, 4 parts
+    tiles, parts = 2 * 3 * 4, 4
+    split = tiles * parts * 256 * 256 * 4 + 256
+    assert L.lgs_mlp_bwd_workspace_bytes(1, 8264, 776, 1040, 2, 1) == plain(1, 8264, 1040, 2, 2) + split
+    # fp32 never splits
+    assert L.lgs_mlp_bwd_workspace_bytes(1, 8264, 776, 1040, 2, 0) == plain(1, 8264, 1040, 2, 4)
+
+
 def _swiglu_fwd(L, **kw):
     # f = ffn / t = 64: Wgu_i is [h, 2f] = [64, 128]
     a = dict(b=1, s=16, h=64, ffn=128, t=2, rank=0, dtype=1, X=FAKE, ldx=64, W=FAKE, ldw=128,

@@ -189,6 +189,40 @@ def test_mlp_bwd_in_three_parts(shape, dtype):
         assert_close(f"{name}: three parts vs one launch", x, f64(y), dtype)
 
 
+def test_mlp_bwd_weight_grads_split_inside_the_launch():
+    """Many tokens with small h and f make few, long dB / dA tiles; the
+    grouped backward launch then splits them over the tokens into parts that
+    it reduces itself (here 4 parts, the last one ragged: M = 8264 is not a
+    multiple of 32).  The gradients match the oracle, and repeat bit for bit:
+    the last part to finish adds the parts' partial sums in part order,
+    whichever part it is."""
+    b, s, h, ffn, t = 1, 8264, 776, 1040, 2
+    M, f = b * s, ffn // t
+    d = dev()
+    X, A, B, dZ = synth.small(41, (M, h), (h, ffn), (ffn, h), (M, h), dtype="bf16")
+    A, B = (A.float() * 0.05).to(BF16), (B.float() * 0.05).to(BF16)
+    X64, A64, B64, dZ64 = f64(X), f64(A), f64(B), f64(dZ)
+    Xd, Ad, Bd, dZd = X.to(d), A.to(d), B.to(d), dZ.to(d)
+    plain = 2 * ((M * f * 2 + 255) // 256 * 256)
+    assert lgs.mlp_bwd_workspace_bytes(b, s, h, ffn, t, BF16) > plain, "expected the K-split plan"
+    for r in range(t):
+        step(f"weight gradients split inside the launch, rank {r}")
+        U = round_like(X64 @ A64[:, r * f:(r + 1) * f], BF16)
+        first = None
+        for rep in range(2):
+            dX, dA, dB = run_bwd(Xd, Ad, Bd, U.to(d), dZd, b, s, t, r, "erf")
+            sync()
+            if first is None:
+                g = oracle.mlp.shard_backward(X64, A64[:, r * f:(r + 1) * f], B64[r * f:(r + 1) * f], f64(U), dZ64)
+                assert_close("dX_i", dX, g["dX"], BF16)
+                assert_close("dA_i", dA, g["dA"], BF16)
+                assert_close("dB_i", dB, g["dB"], BF16)
+                first = (dX, dA, dB)
+            else:
+                for name, x, y in zip(("dX", "dA", "dB"), (dX, dA, dB), first):
+                    assert torch.equal(x, y), f"{name}: second call differs"
+
+
 def test_t1_is_the_unsplit_block():
     d = dev()
     b, s, h, ffn = 1, 300, 264, 520
