@@ -123,3 +123,58 @@ def test_entry_points_replay_under_graph_capture():
         torch.cuda.synchronize()
         for k in ref:
             assert torch.equal(scratch[k], ref[k]), f"eager run after replay {rep}: {k}"
+
+
+def test_k_split_backward_replays_under_graph_capture():
+    """The backward at a shape whose weight gradients are split over the
+    tokens inside the grouped launch (M = 2200, h = 1064, f = 1048: 2 parts)
+    launches a counter-clearing kernel and the grouped GEMM; captured once
+    and replayed, every replay equals the eager result bit for bit."""
+    d = dev()
+    b, s, h, ffn, t, r = 2, 1100, 1064, 2 * 1048, 2, 1
+    M, f = b * s, ffn // t
+    X, A, B, dZ, U = synth.small(81, (M, h), (h, f), (f, h), (M, h), (M, f), dtype="bf16")
+    A = (A.float() * 0.05).to(BF16).to(d)
+    B = (B.float() * 0.05).to(BF16).to(d)
+    X, dZ, U = X.to(d), dZ.to(d), U.to(d)
+    plain = 2 * ((M * f * 2 + 255) // 256 * 256)
+    nws = lgs.mlp_bwd_workspace_bytes(b, s, h, ffn, t, BF16)
+    assert nws > plain, "expected the K-split plan"
+    ws = torch.empty(nws, dtype=torch.uint8, device=d)
+
+    def outs():
+        return (torch.empty(M, h, dtype=BF16, device=d), torch.empty(h, f, dtype=BF16, device=d),
+                torch.empty(f, h, dtype=BF16, device=d))
+
+    def run(o, stream):
+        lgs.tp_mlp_bwd(b, s, h, ffn, t, r, X, A, B, U, dZ, *o, workspace=ws, stream=stream)
+
+    step("K-split backward under graph capture: eager reference")
+    ref = outs()
+    run(ref, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    cap = outs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(cap, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(cap, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        step(f"K-split backward under graph capture: replay {rep}")
+        for x in cap:
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dX", "dA", "dB"), cap, ref):
+            assert torch.equal(x, y), f"replay {rep}: {name} differs from the eager result"
+        eager = outs()  # eager work between replays, on the same workspace
+        run(eager, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dX", "dA", "dB"), eager, ref):
+            assert torch.equal(x, y), f"eager run after replay {rep}: {name}"
