@@ -219,8 +219,14 @@ int tp_swiglu_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, cons
  * Arguments as in tp_mlp_bwd; the three calls share one workspace of
  * lgs_mlp_bwd_workspace_bytes.  dx and dw may run in either order or
  * concurrently on different streams once dgelu has completed (the caller
- * orders them, e.g. with events); the results equal tp_mlp_bwd's.  tp_mlp_bwd
- * runs dx and dw as one launch, which is faster when nothing overlaps them.
+ * orders them, e.g. with events).  tp_mlp_bwd runs dx and dw as one launch,
+ * which is faster when nothing overlaps them.  Results: dgelu and dx give
+ * tp_mlp_bwd's bits.  dw gives tp_mlp_bwd's bits where tp_mlp_bwd runs dB_i
+ * and dA_i unsplit; for bf16 shapes with many tokens against small h and f
+ * (e.g. M = 2200, h = 1064, f = 1048) tp_mlp_bwd splits their sums over token
+ * ranges inside its launch (its workspace then exceeds the two [M, f]
+ * buffers), and dw, which never splits, equals it up to the fp32 summation
+ * order.
  */
 int tp_mlp_bwd_dgelu(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
                      const void* B_i, int64_t ldb, const void* U_i, int64_t ldu, const void* dZ,

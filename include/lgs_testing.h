@@ -39,6 +39,15 @@ int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int N, int K
                        void* stream);
 
 /*
+ * The bf16 MLP backward's plan for the weight gradients of an M-token shard
+ * with hidden size h and f = ffn/t columns: *parts = 1 when tp_mlp_bwd runs
+ * dB_i and dA_i unsplit (then tp_mlp_bwd_dw, which never splits, gives the
+ * same bits), else the number of token ranges it splits them into, with
+ * *kchunk tokens per range.  Returns 0, or -1 for non-positive sizes.
+ */
+int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk);
+
+/*
  * Streaming form of the cross-entropy slice partials, for measuring the CE
  * reductions against the HBM roofline (the product path fuses them into the
  * logit GEMM, vocab_parallel_xent_fwd, and never writes logits).  Z holds a

@@ -69,6 +69,7 @@ SIGNATURES = [
     ("lgs_test_num_tiles", _i, []),
     ("lgs_test_tile_shape", _i, [_i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     ("lgs_test_pick_tile", _i, [_i, _i]),
+    ("lgs_test_mlp_bwd_plan", _i, [_i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     ("lgs_test_gemm_bf16", _i, [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
     ("lgs_test_xent_rows_bf16", _i, [_i, _i, _i, _p, _i64, _p, _p, _p, _p, _p]),
 ]
@@ -131,12 +132,23 @@ def _dtype(x):
         raise ValueError(f"unsupported dtype {x.dtype}") from None
 
 
-def _workspace(nbytes, device, given):
+def _workspace(nbytes, device, given, stream=None):
+    """The caller's workspace, or a temporary one from torch's allocator.  A
+    temporary one is allocated on the current stream and freed when the
+    wrapper returns, while the call's kernels may still be running on
+    `stream`: it is recorded on that stream so the allocator does not hand
+    it out again before that work is done.  A raw stream handle cannot be
+    recorded, so it needs a caller workspace."""
     if nbytes == 0:
         return None, 0
     if given is not None:
         return given.data_ptr(), given.numel() * given.element_size()
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("pass workspace= when stream= is a raw handle: a temporary workspace "
+                         "cannot be tied to that stream's work")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        ws.record_stream(stream)
     return ws, nbytes
 
 
@@ -158,7 +170,7 @@ def tp_mlp_fwd(b, s, h, ffn, t, rank, X, A_i, B_i, Z_i, U_i=None, Y_i=None, act=
     L = lib()
     dt = _dtype(X)
     need = L.lgs_mlp_fwd_workspace_bytes(b, s, h, ffn, t, dt, int(Y_i is not None))
-    ws, ws_bytes = _workspace(need, X.device, workspace)
+    ws, ws_bytes = _workspace(need, X.device, workspace, stream)
     x, ldx = _mat(X)
     a, lda = _mat(A_i)
     bb, ldb = _mat(B_i)
@@ -177,7 +189,7 @@ def tp_mlp_bwd(b, s, h, ffn, t, rank, X, A_i, B_i, U_i, dZ, dX_i, dA_i, dB_i, ac
     L = lib()
     dt = _dtype(X)
     need = L.lgs_mlp_bwd_workspace_bytes(b, s, h, ffn, t, dt)
-    ws, ws_bytes = _workspace(need, X.device, workspace)
+    ws, ws_bytes = _workspace(need, X.device, workspace, stream)
     args = []
     for m in (X, A_i, B_i, U_i, dZ, dX_i, dA_i, dB_i):
         args.extend(_mat(m))
@@ -201,7 +213,7 @@ def tp_swiglu_fwd(b, s, h, ffn, t, rank, X, Wgu_i, Wd_i, Z_i, GU_i=None, Y_i=Non
     L = lib()
     dt = _dtype(X)
     need = L.lgs_swiglu_fwd_workspace_bytes(b, s, h, ffn, t, dt, int(Y_i is not None))
-    ws, ws_bytes = _workspace(need, X.device, workspace)
+    ws, ws_bytes = _workspace(need, X.device, workspace, stream)
     args = []
     for m in (X, Wgu_i, Wd_i, GU_i, Y_i, Z_i):
         args.extend(_mat(m))
@@ -217,7 +229,7 @@ def tp_swiglu_bwd(b, s, h, ffn, t, rank, X, Wgu_i, Wd_i, GU_i, dZ, dX_i, dWgu_i,
     L = lib()
     dt = _dtype(X)
     need = L.lgs_swiglu_bwd_workspace_bytes(b, s, h, ffn, t, dt)
-    ws, ws_bytes = _workspace(need, X.device, workspace)
+    ws, ws_bytes = _workspace(need, X.device, workspace, stream)
     args = []
     for m in (X, Wgu_i, Wd_i, GU_i, dZ, dX_i, dWgu_i, dWd_i):
         args.extend(_mat(m))
@@ -273,7 +285,7 @@ def vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, H, E_r, targets, m_r, l_r, 
     L = lib()
     dt = _dtype(H)
     need = L.lgs_xent_workspace_bytes(b, s, h, vocab, t, dt)
-    ws, ws_bytes = _workspace(need, H.device, workspace)
+    ws, ws_bytes = _workspace(need, H.device, workspace, stream)
     hh, ldh = _mat(H)
     e, lde = _mat(E_r)
     _check(L.vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, dt, hh, ldh, e, lde, _ptr(targets),
@@ -293,7 +305,7 @@ def vocab_parallel_xent_bwd(b, s, h, vocab, t, rank, H, E_r, targets, lse, dH_r,
     L = lib()
     dt = _dtype(H)
     need = L.lgs_xent_bwd_workspace_bytes(b, s, h, vocab, t, dt)
-    ws, ws_bytes = _workspace(need, H.device, workspace)
+    ws, ws_bytes = _workspace(need, H.device, workspace, stream)
     hh, ldh = _mat(H)
     e, lde = _mat(E_r)
     dh, lddh = _mat(dH_r)
@@ -327,7 +339,7 @@ def tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, rank, X, Wqkv_i, QKV_i, workspace=
     L = lib()
     dt = _dtype(X)
     need = L.lgs_attn_qkv_fwd_workspace_bytes(b, s, h, n_q, n_kv, d, t, dt) if split else 0
-    ws, ws_bytes = _workspace(need, X.device, workspace)
+    ws, ws_bytes = _workspace(need, X.device, workspace, stream)
     args = []
     for m in (X, Wqkv_i, QKV_i):
         args.extend(_mat(m))
@@ -365,7 +377,7 @@ def tp_attn_out_bwd(b, s, h, n_q, d, t, rank, A_i, Wo_i, dZ, dA_i, dWo_i, worksp
     L = lib()
     dt = _dtype(A_i)
     need = L.lgs_attn_out_bwd_workspace_bytes(b, s, h, n_q, d, t, dt) if split else 0
-    ws, ws_bytes = _workspace(need, A_i.device, workspace)
+    ws, ws_bytes = _workspace(need, A_i.device, workspace, stream)
     args = []
     for m in (A_i, Wo_i, dZ, dA_i, dWo_i):
         args.extend(_mat(m))
@@ -403,6 +415,15 @@ def tile_shapes():
 
 def pick_tile(M, N):
     return lib().lgs_test_pick_tile(M, N)
+
+
+def mlp_bwd_plan(M, h, f):
+    """(parts, tokens per part) of the bf16 backward's weight gradients:
+    (1, M) when tp_mlp_bwd does not split them over the tokens."""
+    parts, kchunk = ctypes.c_int(), ctypes.c_int()
+    if lib().lgs_test_mlp_bwd_plan(M, h, f, ctypes.byref(parts), ctypes.byref(kchunk)) != 0:
+        raise ValueError("sizes must be positive")
+    return parts.value, kchunk.value
 
 
 def gemm_bf16(A, B, C, a_kmajor=True, b_kmajor=False, tile=-1, stream=None):

@@ -349,11 +349,12 @@ LGS_API int tp_mlp_bwd_dw(int b, int s, int h, int ffn, int t, int rank, int dty
                                   lddb, (hipStream_t)stream));
 }
 
-LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype,
-                                    const void* H, int64_t ldh, const void* E_r, int64_t lde,
-                                    const int32_t* targets, float* m_r, float* l_r, float* tgt_r,
-                                    int32_t* argmax_r, float* loss, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+namespace {
+
+// Argument rules of the fused CE forward (both variants).
+int check_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype, const void* H,
+                   int64_t ldh, const void* E_r, int64_t lde, const int32_t* targets, float* m_r,
+                   float* l_r, float* tgt_r, int32_t* argmax_r, float* loss) {
   int st = check_bst(b, s, h, t, rank);
   if (st) return st;
   if (vocab <= 0 || vocab % t != 0)
@@ -370,6 +371,20 @@ LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int r
     return fail(LGS_ERR_UNSUPPORTED, "per-token arrays must be 4-byte aligned");
   if (loss && t != 1)
     return fail(LGS_ERR_INVALID_ARG, "loss needs the whole vocabulary (t == 1); merge ranks with shard_partial_sum");
+  return LGS_OK;
+}
+
+}  // namespace
+
+LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype,
+                                    const void* H, int64_t ldh, const void* E_r, int64_t lde,
+                                    const int32_t* targets, float* m_r, float* l_r, float* tgt_r,
+                                    int32_t* argmax_r, float* loss, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  int st = check_xent_fwd(b, s, h, vocab, t, rank, dtype, H, ldh, E_r, lde, targets, m_r, l_r, tgt_r,
+                          argmax_r, loss);
+  if (st) return st;
+  const int M = b * s, Vr = vocab / t;
   const size_t need = lgs_xent_workspace_bytes(b, s, h, vocab, t, dtype);
   if (!workspace || workspace_bytes < need)
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -637,6 +652,14 @@ LGS_API int lgs_test_tile_shape(int tile, int* bm, int* bn) {
 LGS_API int lgs_test_pick_tile(int M, int N) {
   if (M <= 0 || N <= 0) return -1;
   return lgs::picked_tile(M, N);
+}
+
+LGS_API int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk) {
+  if (M <= 0 || h <= 0 || f <= 0) return -1;
+  const lgs::BwdSplit k = lgs::mlp_bwd_wsplit(M, h, f);
+  if (parts) *parts = k.parts;
+  if (kchunk) *kchunk = k.parts > 1 ? k.kchunk : M;
+  return 0;
 }
 
 LGS_API int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int N, int K,

@@ -20,7 +20,10 @@
 //   dB = Y^T dZ     : Y M-contiguous (K=tokens), dZ N-contiguous
 //   dA = X^T dU     : X M-contiguous,            dU N-contiguous
 #include <functional>
+#include <map>
+#include <mutex>
 #include <queue>
+#include <tuple>
 #include <vector>
 
 #include "dispatch.hpp"
@@ -61,30 +64,53 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // two K tiles for its partial slot and the last part two per slot it adds.
 // The partial slots' memory traffic also slows every other tile's K loop,
 // which the simulation does not see: measured, a predicted 7% gain (8.3B
-// shape, 3 parts) ran 14% slower, a predicted 40% gain (M = 2200, h = 1064,
-// f = 1048, 2 parts) ran 10% faster.  So the plan splits only where the
-// simulation predicts 30% or more.
+// shape, 3 parts) ran 14% slower, a predicted 41% gain (M = 2200, h = 1064,
+// f = 1048, 2 parts) ran faster.  So the plan splits only where the
+// simulation predicts 30% or more, and takes one more part only when that
+// part's predicted time is at least 5% lower (each part adds slot traffic
+// the simulation cannot price).
+//
+// No split can reach 30% when the longest tile is short against the whole
+// launch: list dispatch finishes within W/256 + L (W the launch's K tiles
+// over all blocks, L the longest block's), while any split needs at least
+// W/256, so if 0.3 W/256 >= 0.7 L the simulation is skipped (both 70B shapes).
+// Plans are cached per shape: the workspace query, the entry point's check
+// and the launch each ask.
 BwdSplit mlp_bwd_wsplit(int M, int h, int f) {
   BwdSplit no{1, 0, 0};
   if (M < 256 || h < 256 || f < 256) return no;
   const int tw = cdiv(f, 256) * cdiv(h, 256), tx = cdiv(M, 256) * cdiv(h, 256);
   const int nkw = cdiv(M, 32), nkx = cdiv(f, 32);
+  const double work = (2.0 * tw * nkw + (double)tx * nkx) / 256.0;
+  if (0.3 * work >= 0.7 * (nkw > nkx ? nkw : nkx)) return no;
+
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int>, BwdSplit> cache;
+  const auto key = std::make_tuple(M, h, f);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
   const int unsplit = dispatch_makespan({{nkw, 2 * tw}, {nkx, tx}});
   int best_cost = unsplit;
   BwdSplit best = no;
   for (int parts = 2; parts <= 4; ++parts) {
     const int kchunk = cdiv(cdiv(M, parts), 32) * 32, n = cdiv(M, kchunk);
-    if (n < 2) continue;
+    if (n < 2 || n == best.parts) continue;
     const int u = kchunk / 32, last = nkw - (n - 1) * u;
     // launch order: dB's parts (part-major), dA's parts, dX
     const std::vector<std::pair<int, int>> items = {{u + 2, tw * (n - 1)}, {last + 2, tw},
                                                     {u + 2, tw * (n - 1)}, {last + 2, tw}, {nkx, tx}};
     const int cost = dispatch_makespan(items) + 2 * n;
-    if (cost * 10 < unsplit * 7 && cost < best_cost) {
+    if (cost * 10 < unsplit * 7 && cost * 20 < best_cost * 19) {
       best_cost = cost;
       best = BwdSplit{n, kchunk, 2 * tw};
     }
   }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache.size() >= 256) cache.clear();
+  cache[key] = best;
   return best;
 }
 

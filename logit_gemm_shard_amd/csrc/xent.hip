@@ -12,12 +12,23 @@
 
 namespace lgs {
 
-// Upper bound on slabs over every tile shape: slabs = ceil(Vr / BN) * BN / WN,
-// wave tile width WN >= 64.
-static int max_slabs(int Vr) { return 2 * ((Vr + 127) / 128); }
+// Slabs the launch plan writes: every wave column of every tile writes one
+// slab (a wave column wholly past the slice end writes -inf / 0 partials that
+// the merge never reads), so a launch of `cols` columns on tile t writes
+// ceil(cols / BN) * BN / WN of them.  The merge reads the first
+// ceil(Vr / WN) (one launch) or c1 / WN + ceil((Vr - c1) / WN) (two).
+static int slabs_written(const ColumnPlan& plan, int Vr) {
+  const int WN = tile_wn(plan.main), bn = tile_bn(plan.main);
+  int n = (plan.c1 + bn - 1) / bn * bn / WN;
+  if (plan.c1 < Vr) {
+    const int bt = tile_bn(plan.tail);
+    n += (Vr - plan.c1 + bt - 1) / bt * bt / WN;
+  }
+  return n;
+}
 
 size_t xent_scratch_bytes(int M, int Vr) {
-  return (size_t)max_slabs(Vr) * (size_t)M * 16u;
+  return (size_t)slabs_written(plan_columns(M, Vr, true), Vr) * (size_t)M * 16u;
 }
 
 // Eight lanes per token fold the slabs into the rank's partials, each lane
@@ -78,7 +89,7 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
   // share the wave width, so that the slabs number consecutively.
   const ColumnPlan plan = plan_columns(M, Vr, true);
   const int WN = tile_wn(plan.main);
-  const size_t slab_elems = (size_t)max_slabs(Vr) * M;
+  const size_t slab_elems = (size_t)slabs_written(plan, Vr) * M;
   XentSlabs sl;
   sl.m = (float*)scratch;
   sl.l = sl.m + slab_elems;

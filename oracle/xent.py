@@ -42,11 +42,6 @@ def _f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def logits(H, E):
-    """z = H E^T."""
-    return _f64(H) @ _f64(E).T
-
-
 def naive_loss(H, E, y, chunk=1024):
     """Full-logit cross-entropy per token, computed chunk by chunk of tokens
     (a memory bound only; each token's loss is independent), with the row

@@ -220,8 +220,9 @@ def test_xent_validation(L):
     assert xe(ws=None) == 3
     assert xe(ws_bytes=16) == 3
     assert xe(lde=32) == 1
-    # the workspace bound covers every tile shape: 2 * ceil(Vr/128) slabs x M x 16 B
-    assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 2 * 50 * 8192 * 16
+    # one 16-byte entry per token and slab written: the 8.3B slice (6400 columns)
+    # runs 5120 columns on 256x320 tiles (32 slabs of 160) and 1280 on 256x160 (8)
+    assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 40 * 8192 * 16
 
 
 def test_xent_bwd_validation(L):
@@ -349,3 +350,13 @@ def test_testing_interface(L):
     assert L.lgs_test_xent_rows_bf16(4, 64, 0, FAKE, 64, None, FAKE, FAKE, FAKE, None) == 1
     assert L.lgs_test_xent_rows_bf16(4, 64, 0, FAKE + 2, 64, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert L.lgs_test_xent_rows_bf16(0, 64, 0, None, 64, None, None, None, None, None) == 0
+
+
+def test_binding_temporary_workspace_needs_a_recordable_stream():
+    """A temporary workspace is recorded on the call's stream (so the caching
+    allocator cannot reuse it under running kernels); a raw stream handle
+    cannot be recorded, so the binding refuses to make one for it."""
+    from logit_gemm_shard_amd import binding
+    with pytest.raises(ValueError, match="raw handle"):
+        binding._workspace(256, "cpu", None, stream=12345)
+    assert binding._workspace(0, "cpu", None, stream=12345) == (None, 0)
