@@ -28,8 +28,9 @@
  *     between consecutive rows, ld >= row width).
  *   - Every pointer is a DEVICE pointer owned by the caller.  The library never
  *     allocates, frees or keeps a pointer after the call returns, never
- *     synchronizes, and keeps no mutable global state; calls on different
- *     streams with disjoint outputs may run concurrently.
+ *     synchronizes, and keeps no mutable global state (one exception:
+ *     vocab_parallel_xent_fwd_noalloc's static device scratch); calls on
+ *     different streams with disjoint outputs may run concurrently.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued asynchronously on it; a device-side fault surfaces at the
  *     caller's next synchronization, as for any HIP launch.
@@ -264,6 +265,34 @@ int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int
                             const int32_t* targets, float* m_r, float* l_r, float* tgt_r,
                             int32_t* argmax_r, float* loss, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * vocab_parallel_xent_fwd_noalloc -- vocab_parallel_xent_fwd for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and rules
+ * as vocab_parallel_xent_fwd (the same kernels), without the workspace: the
+ * slab partials go to a static device array of LGS_XENT_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library holds on each device it runs on until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); its first call on a device looks up that device's copy
+ * of the array once.
+ *
+ * Limit: lgs_xent_workspace_bytes(b, s, h, vocab, t, dtype) must not exceed
+ * LGS_XENT_NOALLOC_SCRATCH_BYTES (e.g. 8192 tokens at vocab/t = 6400 need
+ * 5 MiB; about 25,000 tokens fit at that slice width); larger calls return
+ * LGS_ERR_UNSUPPORTED before anything is enqueued.
+ *
+ * Every call on one device shares that device's array, so calls that overlap
+ * on one device (different streams, or different host threads) race: order
+ * them on one stream, or use vocab_parallel_xent_fwd with separate
+ * workspaces.  Nothing in the array needs clearing: each call writes every
+ * entry it reads.
+ */
+#define LGS_XENT_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int vocab_parallel_xent_fwd_noalloc(int b, int s, int h, int vocab, int t, int rank, int dtype,
+                                    const void* H, int64_t ldh, const void* E_r, int64_t lde,
+                                    const int32_t* targets, float* m_r, float* l_r, float* tgt_r,
+                                    int32_t* argmax_r, float* loss, void* stream);
 
 /*
  * vocab_parallel_xent_bwd -- one rank's backward of the vocab-parallel

@@ -51,6 +51,8 @@ SIGNATURES = [
                            _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _sz, _p]),
     ("vocab_parallel_xent_fwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
                                      _p, _p, _p, _p, _sz, _p]),
+    ("vocab_parallel_xent_fwd_noalloc", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p,
+                                             _p, _p, _p, _p, _p]),
     ("vocab_parallel_xent_bwd", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _p, _p,
                                      _p, _i64, _p, _i64, _p, _sz, _p]),
     ("shard_partial_sum", _i, [_i, _i, _i64, _i, _i, _p, _i64, _p, _p]),
@@ -292,6 +294,23 @@ def vocab_parallel_xent_fwd(b, s, h, vocab, t, rank, H, E_r, targets, m_r, l_r, 
                                      _ptr(m_r), _ptr(l_r), _ptr(tgt_r), _ptr(argmax_r), _ptr(loss),
                                      _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes,
                                      _stream(stream)))
+    return m_r, l_r, tgt_r
+
+
+XENT_NOALLOC_SCRATCH_BYTES = 16 << 20  # LGS_XENT_NOALLOC_SCRATCH_BYTES
+
+
+def vocab_parallel_xent_fwd_noalloc(b, s, h, vocab, t, rank, H, E_r, targets, m_r, l_r, tgt_r,
+                                    argmax_r=None, loss=None, stream=None):
+    """vocab_parallel_xent_fwd with the slab partials in the library's static
+    device scratch: no workspace, nothing allocated (calls that overlap on one
+    device race)."""
+    L = lib()
+    hh, ldh = _mat(H)
+    e, lde = _mat(E_r)
+    _check(L.vocab_parallel_xent_fwd_noalloc(b, s, h, vocab, t, rank, _dtype(H), hh, ldh, e, lde,
+                                             _ptr(targets), _ptr(m_r), _ptr(l_r), _ptr(tgt_r),
+                                             _ptr(argmax_r), _ptr(loss), _stream(stream)))
     return m_r, l_r, tgt_r
 
 

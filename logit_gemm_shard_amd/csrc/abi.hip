@@ -395,6 +395,34 @@ LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int r
                                 argmax_r, loss, workspace, (hipStream_t)stream));
 }
 
+static_assert(LGS_XENT_NOALLOC_SCRATCH_BYTES == lgs::kXentStaticScratchBytes,
+              "the header states the static scratch's size");
+
+LGS_API int vocab_parallel_xent_fwd_noalloc(int b, int s, int h, int vocab, int t, int rank,
+                                            int dtype, const void* H, int64_t ldh, const void* E_r,
+                                            int64_t lde, const int32_t* targets, float* m_r,
+                                            float* l_r, float* tgt_r, int32_t* argmax_r,
+                                            float* loss, void* stream) {
+  int st = check_xent_fwd(b, s, h, vocab, t, rank, dtype, H, ldh, E_r, lde, targets, m_r, l_r, tgt_r,
+                          argmax_r, loss);
+  if (st) return st;
+  const int M = b * s, Vr = vocab / t;
+  const size_t need = lgs_xent_workspace_bytes(b, s, h, vocab, t, dtype);
+  if (need > LGS_XENT_NOALLOC_SCRATCH_BYTES)
+    return fail(LGS_ERR_UNSUPPORTED,
+                "%zu bytes of slab partials needed, the static scratch holds %zu: use "
+                "vocab_parallel_xent_fwd with a workspace",
+                need, (size_t)LGS_XENT_NOALLOC_SCRATCH_BYTES);
+  (void)hipGetLastError();
+  void* scratch = nullptr;
+  const hipError_t e = lgs::xent_static_scratch((hipStream_t)stream, &scratch);
+  if (e != hipSuccess)
+    return fail(LGS_ERR_HIP, "looking up the static scratch failed (nothing enqueued): %s",
+                hipGetErrorString(e));
+  return launched(lgs::xent_fwd(M, h, Vr, rank * Vr, H, ldh, E_r, lde, targets, m_r, l_r, tgt_r,
+                                argmax_r, loss, scratch, (hipStream_t)stream));
+}
+
 LGS_API size_t lgs_xent_bwd_workspace_bytes(int b, int s, int h, int vocab, int t, int dtype) {
   (void)dtype;
   if (b <= 0 || s <= 0 || h <= 0 || t <= 0 || vocab <= 0 || vocab % t) return 0;

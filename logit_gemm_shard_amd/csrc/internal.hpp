@@ -87,6 +87,12 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
                     const void* E, int64_t lde, const int32_t* targets, float* m_r, float* l_r,
                     float* t_r, int32_t* argmax_r, float* loss, void* scratch, hipStream_t s);
 
+// The allocation-free variant's slab partials: a file-scope device array of
+// kXentStaticScratchBytes per device (xent.hip), resolved to its address on
+// the device that runs stream `s` (looked up once per device, then cached).
+constexpr size_t kXentStaticScratchBytes = (size_t)16 << 20;
+hipError_t xent_static_scratch(hipStream_t s, void** out);
+
 // CE backward for one vocabulary slice: G = (exp(z - lse) - onehot) * dloss
 // (z = H E_r^T recomputed, G in bf16 scratch [M, Vr]), dH_r = G E_r,
 // dE_r = G^T H.  dloss may be null (1 per token).

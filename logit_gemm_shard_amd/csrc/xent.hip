@@ -6,6 +6,8 @@
 // target logit T_r (exactly +0 when the target id is outside the slice) and
 // the global id of the slice's first maximum.  Ranks then exchange those
 // numbers instead of logits ("LIT-022: Megatron-LM ...", "Key takeaways").
+#include <mutex>
+
 #include "dispatch.hpp"
 #include "internal.hpp"
 #include "xent.hpp"
@@ -112,6 +114,46 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
   hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 31) / 32), dim3(256), 0, s, sl, nslabs, M,
                      vocab_start, m_r, l_r, t_r, argmax_r, loss);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The slab partials of the allocation-free entry point live in one file-scope
+// device array.  Each device that loads the library holds its own copy until
+// the process ends; its address differs per device and is only known to the
+// runtime, so it is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept.  Host code never passes the array's name to a
+// kernel: on the host that name is a stand-in, not a device address.  The
+// fused CE writes every slab entry the merge reads before the merge runs, so
+// nothing in the array needs clearing between calls; calls that overlap on
+// one device share the array and race.
+static __device__ __align__(256) unsigned char scratch[kXentStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t xent_static_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(s, &dev);  // the device the stream's work runs on
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace lgs

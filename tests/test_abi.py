@@ -225,6 +225,33 @@ def test_xent_validation(L):
     assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 40 * 8192 * 16
 
 
+def test_xent_noalloc_validation(L):
+    """The allocation-free CE forward applies the same argument rules, and
+    rejects calls whose slab partials exceed its static scratch, before any
+    HIP call."""
+    def xn(**kw):
+        a = dict(b=2, s=8, h=64, vocab=1024, t=4, rank=0, dtype=1, H=FAKE, ldh=64, E=FAKE, lde=64,
+                 y=FAKE, m=FAKE, l=FAKE, T=FAKE, am=None, loss=None)
+        a.update(kw)
+        return L.vocab_parallel_xent_fwd_noalloc(a["b"], a["s"], a["h"], a["vocab"], a["t"],
+                                                 a["rank"], a["dtype"], a["H"], a["ldh"], a["E"],
+                                                 a["lde"], a["y"], a["m"], a["l"], a["T"], a["am"],
+                                                 a["loss"], None)
+    assert xn(vocab=1022) == 1
+    assert xn(rank=4) == 1
+    assert xn(dtype=0) == 2
+    assert xn(loss=FAKE) == 1
+    assert xn(y=None) == 1
+    assert xn(lde=32) == 1
+    from logit_gemm_shard_amd import binding
+    cap = binding.XENT_NOALLOC_SCRATCH_BYTES
+    # 8192 tokens at the 8.3B slice fit (5 MiB); 32768 do not (20 MiB)
+    assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) <= cap
+    assert L.lgs_xent_workspace_bytes(32, 1024, 3072, 51200, 8, 1) > cap
+    big = xn(b=32, s=1024, h=3072, vocab=51200, t=8, ldh=3072, lde=3072)
+    assert big == 2 and b"static scratch" in L.lgs_last_error()
+
+
 def test_xent_bwd_validation(L):
     def xb(**kw):
         a = dict(b=2, s=8, h=64, vocab=1024, t=4, rank=0, dtype=1, H=FAKE, ldh=64, E=FAKE, lde=64,
