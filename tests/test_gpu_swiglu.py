@@ -186,7 +186,7 @@ def test_swiglu_gate_saturation():
             assert (Y.float() == 0).all() and (Z.float() == 0).all()
 
 
-# ----------------------------------------------------- full size, sampled
+# ------------------------------------------------ full size, every element
 
 _cache = {}
 
@@ -199,13 +199,8 @@ def _inputs():
     return _cache["w"], _cache["X"], _cache["Wg"], _cache["Wu"], _cache["Wd"]
 
 
-def _rows(M, n=24, seed=0):
-    g = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, M - 1], g.choice(M, n, replace=False)]))
-
-
 @pytest.mark.parametrize("r", [0, 7])
-def test_swiglu_70b_forward_sampled(r):
+def test_swiglu_70b_forward_full(r):
     w, X, Wg, Wu, Wd = _inputs()
     d = dev()
     f = w.f_i
@@ -213,40 +208,35 @@ def test_swiglu_70b_forward_sampled(r):
     GU, Y, Z = run_fwd(X.to(d), synth.gate_up_shard(Wg, Wu, w.t, r).to(d), Wd[r * f:(r + 1) * f].to(d),
                        w.b, w.s, w.ffn, w.t, r)
     sync()
-    rows = _rows(w.M)
-    G, U, rY, rZ = sw.shard_forward(f64(X[rows]), f64(Wg[:, r * f:(r + 1) * f]), f64(Wu[:, r * f:(r + 1) * f]),
+    step(f"swiglu_70b_fwd: oracle forward of rank {r} (host fp64), every element")
+    G, U, rY, rZ = sw.shard_forward(f64(X), f64(Wg[:, r * f:(r + 1) * f]), f64(Wu[:, r * f:(r + 1) * f]),
                                     f64(Wd[r * f:(r + 1) * f]))
     GUh = GU.cpu()
-    assert_close(f"G_{r} rows", GUh[rows, :f], G, BF16)
-    assert_close(f"U_{r} rows", GUh[rows, f:], U, BF16)
-    assert_close(f"Y_{r} rows", Y.cpu()[rows], rY, BF16)
-    assert_close(f"Z_{r} rows", Z.cpu()[rows], rZ, BF16)
+    assert_close(f"G_{r}", GUh[:, :f], G, BF16)
+    assert_close(f"U_{r}", GUh[:, f:], U, BF16)
+    assert_close(f"Y_{r}", Y, rY, BF16)
+    assert_close(f"Z_{r}", Z, rZ, BF16)
 
 
-def test_swiglu_70b_backward_sampled():
+@pytest.mark.parametrize("r", [0, 7])
+def test_swiglu_70b_backward_full(r):
     w, X, Wg, Wu, Wd = _inputs()
     wb = WORKLOADS["swiglu_70b_bwd"]
     d = dev()
-    f, r = w.f_i, 0
-    Wg_r, Wu_r, Wd_r = f64(Wg[:, :f]), f64(Wu[:, :f]), f64(Wd[:f])
+    f = w.f_i
+    Wg_r, Wu_r, Wd_r = f64(Wg[:, r * f:(r + 1) * f]), f64(Wu[:, r * f:(r + 1) * f]), f64(Wd[r * f:(r + 1) * f])
     X64 = f64(X)
-    step("swiglu_70b_bwd: oracle G_0, U_0 in fp64 (host)")
-    G, U = X64 @ Wg_r, X64 @ Wu_r
-    GUin = round_like(np.concatenate([G, U], axis=1), BF16)
-    del G, U
+    step(f"swiglu_70b_bwd: oracle G_{r}, U_{r} in fp64 (host), rounded to bf16")
+    GUin = round_like(np.concatenate([X64 @ Wg_r, X64 @ Wu_r], axis=1), BF16)
     dZ = synth.mlp_grad(wb)
-    step("swiglu_70b_bwd: rank 0 backward at full size")
-    dX, dW, dD = run_bwd(X.to(d), synth.gate_up_shard(Wg, Wu, w.t, r).to(d), Wd[:f].to(d), GUin.to(d),
-                         dZ.to(d), w.b, w.s, w.ffn, w.t, r)
+    step(f"swiglu_70b_bwd: rank {r} backward at full size")
+    dX, dW, dD = run_bwd(X.to(d), synth.gate_up_shard(Wg, Wu, w.t, r).to(d), Wd[r * f:(r + 1) * f].to(d),
+                         GUin.to(d), dZ.to(d), w.b, w.s, w.ffn, w.t, r)
     sync()
-    dX, dW, dD = dX.cpu(), dW.cpu(), dD.cpu()
-    G64, U64, dZ64 = f64(GUin[:, :f]), f64(GUin[:, f:]), f64(dZ)
-    rows = _rows(w.M, 16, 2)
-    g = sw.shard_backward(X64[rows], Wg_r, Wu_r, Wd_r, G64[rows], U64[rows], dZ64[rows])
-    assert_close("dX_0 rows", dX[rows], g["dX"], BF16)
-    hs, fs = _rows(w.h, 24, 3), _rows(f, 24, 4)
-    g = sw.shard_backward(X64[:, hs], Wg_r[np.ix_(hs, fs)], Wu_r[np.ix_(hs, fs)], Wd_r[fs], G64[:, fs],
-                          U64[:, fs], dZ64)
-    assert_close("dW_gate,0 block", dW[hs][:, fs], g["dWg"], BF16)
-    assert_close("dW_up,0 block", dW[hs][:, f + fs], g["dWu"], BF16)
-    assert_close("dW_down,0 rows", dD[fs], g["dWd"], BF16)
+    dW = dW.cpu()
+    step(f"swiglu_70b_bwd: oracle backward of rank {r} (host fp64), every element")
+    g = sw.shard_backward(X64, Wg_r, Wu_r, Wd_r, f64(GUin[:, :f]), f64(GUin[:, f:]), f64(dZ))
+    assert_close(f"dX_{r}", dX, g["dX"], BF16)
+    assert_close(f"dW_gate,{r}", dW[:, :f], g["dWg"], BF16)
+    assert_close(f"dW_up,{r}", dW[:, f:], g["dWu"], BF16)
+    assert_close(f"dW_down,{r}", dD, g["dWd"], BF16)

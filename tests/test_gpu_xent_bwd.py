@@ -147,14 +147,10 @@ def test_xent_bwd_strided_outputs_equal_dense():
     assert torch.isnan(bigE[:, h:]).all()
 
 
-def _rows(M, n=24, seed=0):
-    g = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, M - 1], g.choice(M, n, replace=False)]))
-
-
-def test_xent_bwd_8p3b_sampled():
+def test_xent_bwd_8p3b_full():
     """The 8.3B-shape slice (rank 0 and rank 7 of t = 8) in the benchmark's
-    launch configuration, dloss = 1/M (the mean loss)."""
+    launch configuration, dloss = 1/M (the mean loss): every element of
+    dH_r and dE_r, and the merged lse of every token."""
     w = WORKLOADS["xent_8p3b"]
     d = dev()
     H, E, y = synth.xent_inputs(w)
@@ -176,10 +172,7 @@ def test_xent_bwd_8p3b_sampled():
         dE = torch.empty(Vr, w.h, dtype=BF16, device=d)
         lgs.vocab_parallel_xent_bwd(w.b, w.s, w.h, w.vocab, w.t, r, Hd, Ed[a:a + Vr], yd, lse, dH, dE, dloss=dl)
         sync()
-        rows = _rows(w.M, 24, 10 + r)
-        ref = xo.shard_backward(H64[rows], E64[a:a + Vr], yn[rows], a, rlse[rows], w64[rows])
-        assert_close(f"dH_{r} rows", dH.cpu()[rows], ref["dH"], BF16)
-        dEh = dE.cpu()
-        for lo, hi in ((0, 48), (Vr // 2, Vr // 2 + 40), (Vr - 48, Vr)):
-            ref = xo.shard_backward(H64, E64[a + lo:a + hi], yn, a + lo, rlse, w64)
-            assert_close(f"dE_{r} rows [{lo}, {hi})", dEh[lo:hi], ref["dE"], BF16)
+        step(f"xent_8p3b: oracle backward of rank {r} (host fp64), every element")
+        ref = xo.shard_backward(H64, E64[a:a + Vr], yn, a, rlse, w64)
+        assert_close(f"dH_{r}", dH, ref["dH"], BF16)
+        assert_close(f"dE_{r}", dE, ref["dE"], BF16)
