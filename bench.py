@@ -1,34 +1,39 @@
 """Benchmark: one tensor-parallel rank's transformer-block shard on one MI355X.
 
-A step is one pass of the whole path over one batch, for rank 0 of t = 8 at
-the 8.3B-parameter model's shapes (b = 8, s = 1024, h = 3072, ffn = 12288,
-padded vocabulary 51,200):
+A step is one pass of the whole path for rank 0 of t = 8:
 
-  1. tp_mlp_fwd               U_0 = X A_0, Y_0 = GeLU(U_0), Z_0 = Y_0 B_0
-  2. shard_partial_sum(SUM)   Z = sum of the 8 ranks' partials (rank 0's just
-                              written, the other 7 resident synthetic partials)
-  3. tp_mlp_bwd               dY, dU = dY GeLU'(U_0), dB_0, dA_0, dX_0
+  1. tp_mlp_fwd               70B-shape GeLU MLP shard forward (b = 1, s = 4096,
+                              h = 8192, ffn = 28672): U_0 = X A_0, Y_0 = GeLU(U_0),
+                              Z_0 = Y_0 B_0
+  2. shard_partial_sum(SUM)   Z = sum of the 8 ranks' partials [4096, 8192] (rank 0's
+                              just written, the other 7 resident synthetic partials)
+  3. tp_mlp_bwd               dY, dU = dY GeLU'(U_0), dB_0, dA_0, dX_0 (U_0 from step 1)
   4. shard_partial_sum(SUM)   dX = sum of the 8 ranks' dX partials
-  5. vocab_parallel_xent_fwd  fused logit GEMM + CE partials of slice 0
+  5. vocab_parallel_xent_fwd  fused logit GEMM + CE partials of vocabulary slice 0 of
+                              the 8.3B-shape model (8192 tokens, h = 3072, vocab 51200)
   6. shard_partial_sum(XENT)  per-token loss from the 8 ranks' partials
 
-All inputs are resident in HBM before timing starts.  Order of work: W
-warm-up steps; the per-configuration timings, the streaming CE measurement
-and the clock sampling (so that the timed steps see the device settled);
-then the timed region, K steps between two synchronizations, with HIP
-events around the CE entry point only (its roofline is measured there);
-then an untimed pass of K steps with events between every entry point for
-the per-entry-point breakdown (those events cost the step about 2.5%).
-Prints one JSON line.
+Three input sets (X, A_0, B_0, dZ, H, E_0, targets: about 400 MB each, 1.2 GB in
+all, against the 256 MB Infinity Cache) rotate from step to step, so every step
+reads its operands from HBM.  All inputs are resident in HBM before timing.
+
+Order of work: W warm-up steps; the per-configuration timings, the streaming CE
+measurement and the clock sampling (so that the timed steps see the device
+settled); the timed region, K steps between two synchronizations, with HIP
+events around the backward entry point only (its roofline is measured there);
+then an untimed pass of K steps with events between every entry point for the
+per-entry-point breakdown.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-per-config] [--no-clock]
     python bench.py --copy-calibration   # plain copy for counter scaling
     python bench.py --blas-reference     # torch.matmul (hipBLASLt) at the same GEMM shapes
+    python bench.py --counter-summary DIR  # write the traffic summary from rocprofv3 --pmc passes in DIR
+    python bench.py --kernel-stats CSV TITLE COMMAND  # markdown table from a rocprofv3 kernel_stats.csv
 """
 
 import argparse
-import hashlib
 import glob
+import hashlib
 import json
 import os
 import sys
@@ -41,7 +46,8 @@ METRIC = "TFLOP/s and % bf16 MFMA peak for TP-shard MLP fwd+bwd; CE tokens/s"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_8p3b_hbm_counters.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "mlp_70b_bwd_hbm_counters.txt")
+INFINITY_CACHE_BYTES = 256 << 20
 
 
 def kernel_sources_digest():
@@ -54,9 +60,25 @@ def kernel_sources_digest():
     return h.hexdigest()
 
 
-def step_flops(M, h, f, Vr):
-    """Algorithmic FLOPs (2*M*N*K per GEMM): forward 2 GEMMs, backward 4, plus the logit GEMM."""
-    return {"mlp_fwd": 2 * 2 * M * h * f, "mlp_bwd": 4 * 2 * M * h * f, "xent": 2 * M * h * Vr}
+def mlp_flops(M, h, f):
+    """Algorithmic FLOPs (2 M N K per GEMM) of one rank's MLP shard: forward
+    2 GEMMs, backward 4 (the 6 P T rule)."""
+    return {"fwd": 2 * 2 * M * h * f, "bwd": 4 * 2 * M * h * f}
+
+
+def xent_flops(M, h, Vr):
+    return 2 * M * h * Vr
+
+
+def mlp_bwd_bytes(M, h, f):
+    """Algorithmic HBM bytes of one tp_mlp_bwd call (bf16): its two launches
+    read X, A_i, B_i, U_i and dZ once, write dX_i, dA_i, dB_i once, and pass
+    Y_i and dU_i from the first launch to the second (written and read once)."""
+    e = 2
+    inputs = M * h + h * f + f * h + M * f + M * h
+    outputs = M * h + h * f + f * h
+    between = 2 * (2 * M * f)
+    return e * (inputs + outputs + between)
 
 
 def sample_gpu_clock(torch, run, seconds=3.0, n=4):
@@ -112,6 +134,8 @@ def sample_gpu_clock(torch, run, seconds=3.0, n=4):
 
 
 def read_counters():
+    """HBM bytes per tp_mlp_bwd call from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     vals = {}
@@ -122,9 +146,204 @@ def read_counters():
     if vals.get("kernel_sources_sha256") != kernel_sources_digest():
         return None  # the kernels changed since the counters were taken
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["hbm_bytes_per_call"])
     except (KeyError, ValueError):
         return None
+
+
+def _per_kernel(path, counter):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 CSV
+    (a dispatch's value summed over its rows, e.g. over XCDs)."""
+    import collections
+    import csv
+    by_disp, names = collections.defaultdict(float), {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        by_disp[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for k, v in by_disp.items():
+        out[names[k]].append(v)
+    return out
+
+
+def counter_summary(d):
+    """Write COUNTERS_FILE from four rocprofv3 --pmc passes under directory d:
+    pmc_FETCH_SIZE and pmc_WRITE_SIZE over `bench.py --steps 2 --warmup 1
+    --no-cpu-baseline --no-per-config --no-clock`, and pmc_copy_FETCH_SIZE and
+    pmc_copy_WRITE_SIZE over `bench.py --copy-calibration`.  The counters are
+    KiB per dispatch; each is scaled by what it reads for the plain 1 GiB copy."""
+    import statistics
+
+    def csv_of(sub):
+        found = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not found:
+            raise SystemExit(f"no counter_collection.csv under {os.path.join(d, sub)}")
+        return found[0]
+
+    med = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        step = _per_kernel(csv_of(f"pmc_{c}"), c)
+        copy = _per_kernel(csv_of(f"pmc_copy_{c}"), c)
+        dy = [v for n, v in step.items() if "EpiGeluBwd" in n]
+        grp = [v for n, v in step.items() if "gemm_pp_group3_kernel" in n]
+        cp = [v for n, v in copy.items() if "neg" in n]
+        if len(dy) != 1 or len(grp) != 1 or len(cp) != 1:
+            raise SystemExit(f"{c}: expected one dY+GeLU' kernel, one grouped kernel and one copy kernel, "
+                             f"found {len(dy)}, {len(grp)}, {len(cp)}")
+        med[c] = (statistics.median(dy[0]), statistics.median(grp[0]), statistics.median(cp[0]))
+    fr = (1 << 30) / (med["FETCH_SIZE"][2] * 1024)
+    fw = (1 << 30) / (med["WRITE_SIZE"][2] * 1024)
+
+    def nbytes(i):
+        return med["FETCH_SIZE"][i] * 1024 * fr + med["WRITE_SIZE"][i] * 1024 * fw
+    M, h, f = 4096, 8192, 3584
+    alg = mlp_bwd_bytes(M, h, f)
+    step_cmd = "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-per-config --no-clock"
+    txt = f"""# HBM-side traffic of the MLP backward entry point (tp_mlp_bwd) on the
+# 70B-shape workload (rank 0 of t = 8: M = 4096 tokens, h = 8192, f = 3584),
+# from rocprofv3 counter passes, one counter per run:
+#
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/pmc_FETCH_SIZE -o p -- {step_cmd}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/pmc_WRITE_SIZE -o p -- {step_cmd}
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/pmc_copy_FETCH_SIZE -o p -- python bench.py --copy-calibration
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/pmc_copy_WRITE_SIZE -o p -- python bench.py --copy-calibration
+#   python bench.py --counter-summary gpurun_out/pmc      (writes this file)
+#
+# Calibration: an elementwise pass over 1 GiB (torch.neg: reads 1 GiB, writes
+# 1 GiB) reads FETCH_SIZE = {med['FETCH_SIZE'][2]:.0f} KiB and WRITE_SIZE = {med['WRITE_SIZE'][2]:.0f} KiB per dispatch, so
+# bytes = FETCH_SIZE x 1024 x {fr:.4f} and WRITE_SIZE x 1024 x {fw:.4f}.
+#
+# Per call (median over the dispatches of each kernel):
+#   dY + GeLU' GEMM (writes dU_i and the recomputed Y_i): FETCH_SIZE {med['FETCH_SIZE'][0]:.0f} KiB, WRITE_SIZE {med['WRITE_SIZE'][0]:.0f} KiB -> {nbytes(0) / 1e6:.1f} MB
+#   grouped dB / dA / dX launch:                         FETCH_SIZE {med['FETCH_SIZE'][1]:.0f} KiB, WRITE_SIZE {med['WRITE_SIZE'][1]:.0f} KiB -> {nbytes(1) / 1e6:.1f} MB
+#   algorithmic bytes of the call (X, A_i, B_i, U_i, dZ read once; dX_i, dA_i,
+#   dB_i written once; Y_i and dU_i written and read once): {alg / 1e6:.1f} MB
+#
+# The counters count every request that leaves the L2s for the memory fabric;
+# they cannot separate HBM reads from hits in the 256 MB Infinity Cache in
+# front of HBM.  Traffic above the algorithmic bytes is operand panels fetched
+# again by the L2 of each of the 8 XCDs for its own tiles.
+kernel_sources_sha256: {kernel_sources_digest()}
+hbm_bytes_per_call: {nbytes(0) + nbytes(1):.0f}
+"""
+    open(COUNTERS_FILE, "w").write(txt)
+    print(txt)
+
+
+def kernel_stats_md(src, title, cmd):
+    """A short markdown table of a rocprofv3 kernel_stats.csv (our mangled
+    kernel names shortened to their template arguments)."""
+    import csv
+    import re
+
+    def short(n):
+        if n.startswith("_Z"):
+            parts, i = [], 2
+            while i < len(n):
+                m = re.match(r"Li(\d+)E|Lb([01])E", n[i:])
+                if m:
+                    parts.append(m.group(1) or ("true" if m.group(2) == "1" else "false"))
+                    i += m.end()
+                    continue
+                m = re.match(r"(\d+)", n[i:])
+                if m and i > 0 and not n[i - 1].isdigit():
+                    L = int(m.group(1))
+                    j = i + m.end()
+                    parts.append(n[j:j + L])
+                    i = j + L
+                    continue
+                if n[i:i + 4] == "DF16":
+                    parts.append("bf16")
+                    i += 5
+                    continue
+                i += 1
+            n = " ".join(p for p in parts if p != "lgs")
+        n = n.replace("lgs::", "").replace("__hip_bfloat16", "bf16")
+        return re.sub(r"at::native::.*", lambda m: "torch: " + m.group(0)[:70], n)
+
+    out = [f"# {title}", "", "Command (from the repository root):", "", "```", cmd, "```", "",
+           "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(src)):
+        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    print("\n".join(out))
+
+
+def cpu_baseline(host, reps_budget_s=6.0):
+    """The fp64 oracle as it stands (plain numpy, BLAS dgemm) on the host's
+    cores, on the same seeded inputs as the GPU step's first input set:
+      value       the whole step (70B forward and its sum of 8 partials,
+                  backward and its sum, the CE slice of rank 0 and the merge of
+                  8 ranks' partials), repeated while it fits the time budget;
+      per_config  each configuration's unit of work alone, at full size;
+      xent_full_vocab  the naive full-logit CE over all 51,200 columns.
+    Input conversion to fp64 and the other ranks' partials are outside the
+    timed calls."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    X, A0, B0, dZ = host["X"], host["A0"], host["B0"], host["dZ"]
+    H, E, y, Vr, t = host["H"], host["E"], host["y"], host["Vr"], 8
+    M, h = X.shape
+    f = A0.shape[1]
+    Mc, hc = H.shape
+    rng = np.random.default_rng(0)
+    other = rng.normal(size=(M, h)) * 0.05       # a received partial (the same values for every rank)
+    st = (rng.normal(size=(t - 1, Mc)), rng.uniform(1, 100, (t - 1, Mc)), np.zeros((t - 1, Mc)))
+    E0 = E[:Vr]
+
+    def step():
+        U, Y, Z = oracle.mlp.shard_forward(X, A0, B0)
+        oracle.mlp.partial_sum([Z] + [other] * (t - 1))
+        g = oracle.mlp.shard_backward(X, A0, B0, U, dZ)
+        oracle.mlp.partial_sum([g["dX"]] + [other] * (t - 1))
+        m, l, T, _ = oracle.xent.shard_partials(H, E0, y, 0)
+        oracle.xent.merge(np.vstack([m[None], st[0]]), np.vstack([l[None], st[1]]), np.vstack([T[None], st[2]]))
+        return U
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return time.perf_counter() - t0, r
+
+    mf = mlp_flops(M, h, f)
+    step_fl = mf["fwd"] + mf["bwd"] + xent_flops(Mc, hc, Vr)
+    total, passes = 0.0, 0
+    while passes == 0 or total < reps_budget_s:
+        dt, U = timed(step)
+        total += dt
+        passes += 1
+    per = {}
+    X2, A2, B2 = host["X2"], host["A2_0"], host["B2_0"]
+    fl2 = mlp_flops(X2.shape[0], X2.shape[1], A2.shape[1])["fwd"]
+    for name, fn, fl in (
+            ("mlp_8p3b_fwd", lambda: oracle.mlp.shard_forward(X2, A2, B2), fl2),
+            ("mlp_70b_fwd", lambda: oracle.mlp.shard_forward(X, A0, B0), mf["fwd"]),
+            ("mlp_70b_bwd", lambda: oracle.mlp.shard_backward(X, A0, B0, U, dZ), mf["bwd"]),
+            ("xent_8p3b_slice", lambda: oracle.xent.shard_partials(H, E0, y, 0), xent_flops(Mc, hc, Vr)),
+            ("xent_8p3b_full_vocab", lambda: oracle.xent.naive_loss(H, E, y), xent_flops(Mc, hc, E.shape[0]))):
+        dt, _ = timed(fn)
+        per[name] = {"s": round(dt, 3), "gflop": round(fl / 1e9, 1), "tflops": round(fl / dt / 1e12, 4)}
+        if name.startswith("xent"):
+            per[name]["tokens_per_s"] = round(Mc / dt, 1)
+    per["xent_8p3b_full_vocab"]["note"] = ("naive full-logit CE of all 8192 tokens over the whole "
+                                           "51,200-entry vocabulary (2.58 TFLOP), timed apart from slice 0")
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    return {"value": round(step_fl * passes / total / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": threads,
+            "sample": f"the whole step (all {M} tokens of the 70B MLP forward + backward with both sums of "
+                      f"8 partials, all {Mc} tokens of CE slice 0 and the merge) in fp64 numpy, {passes} "
+                      f"pass(es): {step_fl * passes / 1e9:.0f} GFLOP in {total:.2f} s",
+            "per_config": per}
 
 
 def copy_calibration():
@@ -139,54 +358,6 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "copies": 5,
                       "kernel": "torch.neg elementwise"}))
 
-
-def cpu_baseline(w, xw, inputs, budget_s=10.0):
-    """The fp64 oracle on the host, on a token sample of the same step."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-
-    import oracle
-    X, A0, B0, dZ, H, E0, y = inputs
-    f, h, Vr, t = w.f_i, w.h, xw.v_r, w.t
-    rng = np.random.default_rng(0)
-
-    def one_pass(m):
-        Xs, dZs = X[:m].astype(np.float64), dZ[:m].astype(np.float64)
-        Hs, ys = H[:m].astype(np.float64), y[:m]
-        others = [rng.normal(size=(m, h)) for _ in range(t - 1)]
-        stats = [(rng.normal(size=m), rng.uniform(1, 10, m), np.zeros(m)) for _ in range(t - 1)]
-        t0 = time.perf_counter()
-        U, Y, Z = oracle.mlp.shard_forward(Xs, A0, B0)
-        oracle.mlp.partial_sum([Z] + others)
-        g = oracle.mlp.shard_backward(Xs, A0, B0, U, dZs)
-        oracle.mlp.partial_sum([g["dX"]] + others)
-        mr, lr, Tr, _ = oracle.xent.shard_partials(Hs, E0, ys, 0)
-        oracle.xent.merge(np.stack([mr] + [s[0] for s in stats]), np.stack([lr] + [s[1] for s in stats]),
-                          np.stack([Tr] + [s[2] for s in stats]))
-        return time.perf_counter() - t0
-
-    # grow the token sample until one pass takes the budget, or the whole
-    # step is covered; then repeat whole passes until the budget is spent
-    for m in (256, 512, 1024, 2048, 4096, 8192):
-        m = min(m, w.M)
-        total, passes = one_pass(m), 1
-        if total >= budget_s or m == w.M:
-            break
-    while total < budget_s:
-        total += one_pass(m)
-        passes += 1
-    fl = sum(step_flops(m, h, f, Vr).values()) * passes
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as fh:
-            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
-    except OSError:
-        pass
-    return {"value": fl / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": model, "os_cpu_count": os.cpu_count(),
-            "sample": f"the same step (MLP fwd+bwd, both sums, slice-0 CE, merge) on the first {m} "
-                      f"of {w.M} tokens in fp64 numpy, {passes} passes: {fl / 1e9:.1f} GFLOP in {total:.2f} s"}
 
 
 # The library's GEMM shapes (M, N, K) with the per-configuration entry they
@@ -242,31 +413,42 @@ def time_calls(torch, fn, reps, warmup=3):
     return e0.elapsed_time(e1) / reps
 
 
+def n_sets(bytes_per_set):
+    """Input sets to rotate so that together they exceed twice the Infinity Cache."""
+    return max(3, -(-2 * INFINITY_CACHE_BYTES // bytes_per_set))
+
+
 def per_config(torch, lgs, reps):
-    """The configurations the library is specified on, each timed alone:
-    the tiny fp32 block (both shards + sum), and the 70B-shape rank's forward
-    and backward.  Inputs are device-side draws with the workloads'
-    distributions (the kernels' cost does not depend on the values)."""
+    """Every configuration the library is specified on, each timed alone, call
+    by call (10 warm-up calls, then `reps` calls; median and minimum), with
+    enough input sets rotated between calls to exceed twice the Infinity
+    Cache.  Inputs are device draws with the workloads' distributions (the
+    kernels' cost does not depend on the values)."""
     from logit_gemm_shard_amd import synth
     from logit_gemm_shard_amd.configs import WORKLOADS
     dev = torch.device("cuda", 0)
+    bf = torch.bfloat16
     out = {}
 
+    def randn(*shape, std=1.0, dtype=bf):
+        x = torch.randn(*shape, device=dev)
+        if std != 1.0:
+            x.mul_(std)
+        return x.to(dtype)
+
+    # tiny fp32 block: both shards' forward + sum, replayed as one HIP graph
     w = WORKLOADS["tiny_mlp_t2_f32"]
     X, A, B = (x.to(dev) for x in synth.mlp_weights(w))
     f = w.f_i
     Z = torch.empty(w.t, w.M, w.h, device=dev)
     Zs = torch.empty(w.M, w.h, device=dev)
     Ys = torch.empty(w.t, w.M, f, device=dev)
-
     shards = [(A[:, r * f:(r + 1) * f], B[r * f:(r + 1) * f], Z[r], Ys[r]) for r in range(w.t)]
 
     def tiny():
         for r, (Ar, Br, Zr, Yr) in enumerate(shards):
             lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, r, X, Ar, Br, Zr, Y_i=Yr)
         lgs.shard_partial_sum("sum", w.t, w.M * w.h, Z, w.M * w.h, Zs)
-    # a launch-bound unit: replay it as one HIP graph so that the figure is the
-    # device's time, not the host's launch rate
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -280,91 +462,105 @@ def per_config(torch, lgs, reps):
     out["tiny_mlp_t2_f32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 3),
                               "pct_fp32_peak": round(100 * fl / ms / 1e9 / PEAK_FP32_TFLOPS, 3),
                               "note": "both shards' forward + sum, fp32, replayed as one HIP graph; launch-bound"}
+    del X, A, B, Z, Zs, Ys, shards, graph
 
-    # 70B-shape rank: three input sets (555 MB of operands, more than the
-    # 256 MB Infinity Cache) rotated between calls, 10 warm-up calls, then
-    # `reps` calls each timed alone; median and minimum reported.
-    w = WORKLOADS["mlp_70b_fwd"]
-    f, bf = w.f_i, torch.bfloat16
-    sets = []
-    for _ in range(3):
-        X = torch.randn(w.M, w.h, device=dev).to(bf)
-        A0 = torch.randn(w.h, f, device=dev).mul_(0.02).to(bf)
-        B0 = torch.randn(f, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
-        sets.append((X, A0, B0))
-    U = torch.empty(w.M, f, dtype=bf, device=dev)
-    Y = torch.empty(w.M, f, dtype=bf, device=dev)
-    Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
+    # MLP shard forward and backward at the 8.3B and 70B shapes
+    for fwd_name, bwd_name in (("mlp_8p3b_fwd", None), ("mlp_70b_fwd", "mlp_70b_bwd")):
+        w = WORKLOADS[fwd_name]
+        f = w.f_i
+        per_set = 2 * (2 * w.M * w.h + 2 * w.h * f)
+        sets = [(randn(w.M, w.h), randn(w.h, f, std=0.02), randn(f, w.h, std=synth.residual_std(w.n_blocks)),
+                 randn(w.M, w.h, std=0.01)) for _ in range(n_sets(per_set))]
+        U = torch.empty(w.M, f, dtype=bf, device=dev)
+        Y = torch.empty(w.M, f, dtype=bf, device=dev)
+        Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
 
-    def fwd(i):
-        X, A0, B0 = sets[i % 3]
-        lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, Z, U_i=U, Y_i=Y)
-    fl = 2 * 2 * w.M * w.h * f
-    out["mlp_70b_fwd"] = _timed_report(torch, fwd, fl, reps)
+        def fwd(i, w=w, sets=sets, U=U, Y=Y, Z=Z):
+            X, A0, B0, _ = sets[i % len(sets)]
+            lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, Z, U_i=U, Y_i=Y)
+        fl = mlp_flops(w.M, w.h, f)
+        out[fwd_name] = _timed_report(torch, fwd, fl["fwd"], reps, len(sets))
+        if bwd_name:
+            wb = WORKLOADS[bwd_name]
+            dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
+            dA = torch.empty(w.h, f, dtype=bf, device=dev)
+            dB = torch.empty(f, w.h, dtype=bf, device=dev)
+            ws = torch.empty(lgs.mlp_bwd_workspace_bytes(wb.b, wb.s, wb.h, wb.ffn, wb.t, bf), dtype=torch.uint8,
+                             device=dev)
 
-    w = WORKLOADS["mlp_70b_bwd"]
-    dZs = [torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf) for _ in range(3)]
-    dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
-    dA = torch.empty(w.h, f, dtype=bf, device=dev)
-    dB = torch.empty(f, w.h, dtype=bf, device=dev)
-    ws = torch.empty(lgs.mlp_bwd_workspace_bytes(w.b, w.s, w.h, w.ffn, w.t, bf), dtype=torch.uint8, device=dev)
+            def bwd(i, w=wb, sets=sets, U=U, dX=dX, dA=dA, dB=dB, ws=ws):
+                X, A0, B0, dZ = sets[i % len(sets)]
+                lgs.tp_mlp_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, U, dZ, dX, dA, dB, workspace=ws)
+            out[bwd_name] = _timed_report(torch, bwd, fl["bwd"], reps, len(sets))
+            del dX, dA, dB, ws
+        del sets, U, Y, Z
 
-    def bwd(i):
-        X, A0, B0 = sets[i % 3]
-        lgs.tp_mlp_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, U, dZs[i % 3], dX, dA, dB, workspace=ws)
-    fl = 4 * 2 * w.M * w.h * f
-    out["mlp_70b_bwd"] = _timed_report(torch, bwd, fl, reps)
-    del sets, dZs, dX, dA, dB, ws, U, Y, Z
+    # the fused CE forward and backward of vocabulary slice 0 at the 8.3B shapes
+    xw = WORKLOADS["xent_8p3b"]
+    M, h, V, t, Vr = xw.M, xw.h, xw.vocab, xw.t, xw.v_r
+    sets = [(randn(M, h), randn(Vr, h, std=0.02), torch.randint(0, V, (M,), device=dev, dtype=torch.int32))
+            for _ in range(n_sets(2 * (M * h + Vr * h)))]
+    stats = torch.empty(3, M, device=dev)
+    ws_x = torch.empty(lgs.xent_workspace_bytes(xw.b, xw.s, h, V, t), dtype=torch.uint8, device=dev)
 
-    # 70B-shape SwiGLU rank (the gated MLP of the same model): forward is the
-    # paired [gate | up] GEMM (2 * M * h * 2f) and the down GEMM (2 * M * f * h);
-    # backward is dY, dX, dW_gu, dW_down (2 + 4 + 4 + 2) * M * h * f.
+    def xfwd(i):
+        H, E0, y = sets[i % len(sets)]
+        lgs.vocab_parallel_xent_fwd(xw.b, xw.s, h, V, t, 0, H, E0, y, stats[0], stats[1], stats[2], workspace=ws_x)
+    rep = _timed_report(torch, xfwd, xent_flops(M, h, Vr), reps, len(sets))
+    rep["tokens_per_s"] = round(M / (rep["ms"] * 1e-3), 0)
+    out["xent_8p3b"] = rep
+    lse = (torch.randn(M, device=dev).abs_() + 12.0)
+    dl = torch.full((M,), 1.0 / M, dtype=torch.float32, device=dev)
+    dH0 = torch.empty(M, h, dtype=bf, device=dev)
+    dE0 = torch.empty(Vr, h, dtype=bf, device=dev)
+    ws_xb = torch.empty(lgs.xent_bwd_workspace_bytes(xw.b, xw.s, h, V, t), dtype=torch.uint8, device=dev)
+
+    def xbwd(i):
+        H, E0, y = sets[i % len(sets)]
+        lgs.vocab_parallel_xent_bwd(xw.b, xw.s, h, V, t, 0, H, E0, y, lse, dH0, dE0, dloss=dl, workspace=ws_xb)
+    rep = _timed_report(torch, xbwd, 3 * xent_flops(M, h, Vr), reps, len(sets))
+    rep["tokens_per_s"] = round(M / (rep["ms"] * 1e-3), 0)
+    rep["note"] += "; dloss = 1/M: the recomputed logit GEMM with its gradient epilogue, then dH_0 and dE_0"
+    out["xent_8p3b_bwd"] = rep
+    del sets, stats, ws_x, lse, dl, dH0, dE0, ws_xb
+
+    # SwiGLU block (the gated MLP of the same 70B model): forward = the paired
+    # [gate | up] GEMM (2 M h 2f) + the down GEMM (2 M f h); backward = dY, dX,
+    # dW_gu, dW_down, (2 + 4 + 4 + 2) M h f
     w = WORKLOADS["swiglu_70b_fwd"]
     f = w.f_i
-    sets = []
-    for _ in range(3):
-        X = torch.randn(w.M, w.h, device=dev).to(bf)
-        Wgu = torch.randn(w.h, 2 * f, device=dev).mul_(0.02).to(bf)
-        Wd = torch.randn(f, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
-        sets.append((X, Wgu, Wd))
+    sets = [(randn(w.M, w.h), randn(w.h, 2 * f, std=0.02), randn(f, w.h, std=synth.residual_std(w.n_blocks)),
+             randn(w.M, w.h, std=0.01)) for _ in range(n_sets(2 * (2 * w.M * w.h + 3 * w.h * f)))]
     GU = torch.empty(w.M, 2 * f, dtype=bf, device=dev)
     Y = torch.empty(w.M, f, dtype=bf, device=dev)
     Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
 
     def sfwd(i):
-        X, Wgu, Wd = sets[i % 3]
+        X, Wgu, Wd, _ = sets[i % len(sets)]
         lgs.tp_swiglu_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, Wgu, Wd, Z, GU_i=GU, Y_i=Y)
-    out["swiglu_70b_fwd"] = _timed_report(torch, sfwd, 6 * w.M * w.h * f, reps)
-
-    w = WORKLOADS["swiglu_70b_bwd"]
-    dZs = [torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf) for _ in range(3)]
+    out["swiglu_70b_fwd"] = _timed_report(torch, sfwd, 6 * w.M * w.h * f, reps, len(sets))
+    wb = WORKLOADS["swiglu_70b_bwd"]
     dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
     dWgu = torch.empty(w.h, 2 * f, dtype=bf, device=dev)
     dWd = torch.empty(f, w.h, dtype=bf, device=dev)
-    ws = torch.empty(lgs.swiglu_bwd_workspace_bytes(w.b, w.s, w.h, w.ffn, w.t, bf), dtype=torch.uint8,
+    ws = torch.empty(lgs.swiglu_bwd_workspace_bytes(wb.b, wb.s, wb.h, wb.ffn, wb.t, bf), dtype=torch.uint8,
                      device=dev)
 
     def sbwd(i):
-        X, Wgu, Wd = sets[i % 3]
-        lgs.tp_swiglu_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, Wgu, Wd, GU, dZs[i % 3], dX, dWgu, dWd, workspace=ws)
-    out["swiglu_70b_bwd"] = _timed_report(torch, sbwd, 12 * w.M * w.h * f, reps)
-    del sets, dZs, dX, dWgu, dWd, ws, GU, Y, Z
+        X, Wgu, Wd, dZ = sets[i % len(sets)]
+        lgs.tp_swiglu_bwd(wb.b, wb.s, wb.h, wb.ffn, wb.t, 0, X, Wgu, Wd, GU, dZ, dX, dWgu, dWd, workspace=ws)
+    out["swiglu_70b_bwd"] = _timed_report(torch, sbwd, 12 * w.M * w.h * f, reps, len(sets))
+    del sets, GU, Y, Z, dX, dWgu, dWd, ws
 
-    # 70B-shape attention projections of one rank (8 query heads, 1 KV head of
-    # 128): forward = QKV (2 M h (q + 2 kv)) + W_O (2 M q h); backward = their
-    # input and weight gradients (twice that).
+    # attention projections of one rank (8 query heads, 1 KV head of 128):
+    # forward = QKV (2 M h (q + 2 kv)) + W_O (2 M q h); backward twice that
     w = WORKLOADS["attn_70b"]
     q, kv = w.n_heads // w.t * w.head_dim, w.n_kv_heads // w.t * w.head_dim
     nqkv = q + 2 * kv
-    sets = []
-    for _ in range(3):
-        X = torch.randn(w.M, w.h, device=dev).to(bf)
-        Wqkv = torch.randn(w.h, nqkv, device=dev).mul_(0.02).to(bf)
-        Wo = torch.randn(q, w.h, device=dev).mul_(synth.residual_std(w.n_blocks)).to(bf)
-        A = torch.randn(w.M, q, device=dev).to(bf)
-        dZ = torch.randn(w.M, w.h, device=dev).mul_(w.dz_std).to(bf)
-        dQ = torch.randn(w.M, nqkv, device=dev).mul_(w.dz_std).to(bf)
-        sets.append((X, Wqkv, Wo, A, dZ, dQ))
+    per_set = 2 * (w.M * w.h * 2 + w.h * nqkv + q * w.h + w.M * q + w.M * nqkv)
+    sets = [(randn(w.M, w.h), randn(w.h, nqkv, std=0.02), randn(q, w.h, std=synth.residual_std(w.n_blocks)),
+             randn(w.M, q), randn(w.M, w.h, std=w.dz_std), randn(w.M, nqkv, std=w.dz_std))
+            for _ in range(n_sets(per_set))]
     QKV = torch.empty(w.M, nqkv, dtype=bf, device=dev)
     Z = torch.empty(w.M, w.h, dtype=bf, device=dev)
     dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
@@ -374,43 +570,52 @@ def per_config(torch, lgs, reps):
     a = (w.b, w.s, w.h)
     ws_qkv = torch.empty(max(1, lgs.attn_qkv_fwd_workspace_bytes(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t)),
                          dtype=torch.uint8, device=dev)
-
-    def afwd(i):
-        X, Wqkv, Wo, A, _, _ = sets[i % 3]
-        lgs.tp_attn_qkv_fwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, QKV, workspace=ws_qkv)
-        lgs.tp_attn_out_fwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, Z)
-
     ws_ob = torch.empty(max(1, lgs.attn_out_bwd_workspace_bytes(*a, w.n_heads, w.head_dim, w.t)),
                         dtype=torch.uint8, device=dev)
 
+    def afwd(i):
+        X, Wqkv, Wo, A, _, _ = sets[i % len(sets)]
+        lgs.tp_attn_qkv_fwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, QKV, workspace=ws_qkv)
+        lgs.tp_attn_out_fwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, Z)
+
     def abwd(i):
-        X, Wqkv, Wo, A, dZ, dQ = sets[i % 3]
+        X, Wqkv, Wo, A, dZ, dQ = sets[i % len(sets)]
         lgs.tp_attn_qkv_bwd(*a, w.n_heads, w.n_kv_heads, w.head_dim, w.t, 0, X, Wqkv, dQ, dX, dW)
         lgs.tp_attn_out_bwd(*a, w.n_heads, w.head_dim, w.t, 0, A, Wo, dZ, dA, dWo, workspace=ws_ob)
     fl = 2 * w.M * w.h * (nqkv + q)
-    out["attn_70b_fwd"] = _timed_report(torch, afwd, fl, reps)
-    out["attn_70b_bwd"] = _timed_report(torch, abwd, 2 * fl, reps)
+    out["attn_70b_fwd"] = _timed_report(torch, afwd, fl, reps, len(sets))
+    out["attn_70b_bwd"] = _timed_report(torch, abwd, 2 * fl, reps, len(sets))
+    del sets, QKV, Z, dX, dW, dA, dWo, ws_qkv, ws_ob
+
+    # the exchanges' one-device stand-ins (pure HBM streams): the sum of 8
+    # partials at both shapes, and the sequence-parallel reduce-scatter and
+    # all-gather at the 8.3B shape (s = 1024, b = 8, h = 3072, t = 8)
+    for name, (M, h) in (("sum_partials_8p3b", (8192, 3072)), ("sum_partials_70b", (4096, 8192))):
+        parts = randn(8, M, h, std=0.05)
+        zs = torch.empty(M, h, dtype=bf, device=dev)
+        ms = time_calls(torch, lambda: lgs.shard_partial_sum("sum", 8, M * h, parts, M * h, zs), reps)
+        nb = 9 * M * h * 2
+        out[name] = {"us": round(ms * 1e3, 2), "bytes": nb, "GBs": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "note": "8 partials read once, the sum written once; one buffer (more than twice the "
+                             "Infinity Cache)"}
+        del parts, zs
+    w = WORKLOADS["mlp_8p3b_fwd"]
+    t, M, h = w.t, w.M, w.h
+    chunk = M * h // t
+    parts = randn(t, M, h, std=0.05)
+    rs_out = torch.empty(M // t, h, dtype=bf, device=dev)
+    ag_in = randn(t, M // t, h)
+    ag_out = torch.empty(M, h, dtype=bf, device=dev)
+    rs_ms = time_calls(torch, lambda: lgs.shard_reduce_scatter(t, 0, w.s, w.b, h, parts, M * h, rs_out), reps)
+    ag_ms = time_calls(torch, lambda: lgs.shard_all_gather(t, w.s, w.b, h, ag_in, chunk, ag_out), reps)
+    rs_bytes, ag_bytes = (t + 1) * chunk * 2, 2 * M * h * 2
+    out["sp_8p3b"] = {"reduce_scatter_us": round(rs_ms * 1e3, 2),
+                      "reduce_scatter_GBs": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1),
+                      "all_gather_us": round(ag_ms * 1e3, 2),
+                      "all_gather_GBs": round(ag_bytes / (ag_ms * 1e-3) / 1e9, 1),
+                      "note": "bytes = every byte read once + written once; HBM peak 8000 GB/s"}
     return out
-
-
-def _timed_report(torch, fn, flops, reps, warmup=10):
-    """fn(i) timed call by call with HIP events on the current stream."""
-    for i in range(warmup):
-        fn(i)
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        fn(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
-    med, mn = ms[len(ms) // 2], ms[0]
-    return {"ms": round(med, 4), "ms_min": round(mn, 4), "runs": reps,
-            "tflops": round(flops / med / 1e9, 2), "tflops_best": round(flops / mn / 1e9, 2),
-            "pct_bf16_peak": round(100 * flops / med / 1e9 / PEAK_BF16_TFLOPS, 2),
-            "note": "median of per-call times, 3 rotated input sets"}
 
 
 def ce_reduction_stream(torch, lgs, xw, reps=30):
@@ -437,10 +642,30 @@ def ce_reduction_stream(torch, lgs, xw, reps=30):
             "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def _timed_report(torch, fn, flops, reps, nsets, warmup=10):
+    """fn(i) timed call by call with HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med, mn = ms[len(ms) // 2], ms[0]
+    return {"ms": round(med, 4), "ms_min": round(mn, 4), "runs": reps,
+            "tflops": round(flops / med / 1e9, 2), "tflops_best": round(flops / mn / 1e9, 2),
+            "pct_bf16_peak": round(100 * flops / med / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "note": f"median of per-call times, {nsets} input sets rotated"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -450,7 +675,17 @@ def main():
                     help="skip the per-configuration timings (counter passes)")
     ap.add_argument("--blas-reference", action="store_true",
                     help="time torch.matmul (hipBLASLt) at the library's GEMM shapes and exit")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="write the tp_mlp_bwd traffic summary from rocprofv3 --pmc passes under DIR and exit")
+    ap.add_argument("--kernel-stats", nargs=3, metavar=("CSV", "TITLE", "COMMAND"),
+                    help="print a markdown table of a rocprofv3 kernel_stats.csv and exit")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.kernel_stats:
+        kernel_stats_md(*args.kernel_stats)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard: the library is measured on one GPU "
               "(all t ranks of the split are timed or checked on that one device); use --gpus 1.",
@@ -469,121 +704,105 @@ def main():
     from logit_gemm_shard_amd import synth
     from logit_gemm_shard_amd.configs import WORKLOADS
 
-    w, xw = WORKLOADS["mlp_8p3b_fwd"], WORKLOADS["xent_8p3b"]
+    w, wb, xw = WORKLOADS["mlp_70b_fwd"], WORKLOADS["mlp_70b_bwd"], WORKLOADS["xent_8p3b"]
     M, h, f, t, ffn = w.M, w.h, w.f_i, w.t, w.ffn
-    V, Vr = xw.vocab, xw.v_r
+    Mc, hc, V, Vr = xw.M, xw.h, xw.vocab, xw.v_r
     bf = torch.bfloat16
     dev = torch.device("cuda", 0)
 
-    # ---------------- inputs (host, seeded) -> HBM
+    # ---------------- inputs -> HBM.  Set 0: the workloads' seeded host draws
+    # (X, A, B from the 70B seed, dZ from its own, H, E, targets from the CE
+    # seed), rank 0's slices; sets 1 and 2: device draws with the same
+    # distributions.
     X, A, B = synth.mlp_weights(w)
-    dZ = synth.normal((M, h), 0.01, 6, "bf16")
+    A0, B0 = A[:, :f].contiguous(), B[:f].contiguous()
+    del A, B
+    dZ = synth.mlp_grad(wb)
     H, E, y = synth.xent_inputs(xw)
-    A0, B0, E0 = A[:, :f].contiguous(), B[:f].contiguous(), E[:Vr].contiguous()
-    Xd, A0d, B0d, dZd = X.to(dev), A0.to(dev), B0.to(dev), dZ.to(dev)
-    Hd, E0d, yd = H.to(dev), E0.to(dev), y.to(dev)
-    U = torch.empty(M, f, dtype=bf, device=dev)
+    E0 = E[:Vr].contiguous()
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+
+    def draw(*shape, std=1.0):
+        return (torch.randn(*shape, device=dev, generator=g) * std).to(bf)
+    sets = [(X.to(dev), A0.to(dev), B0.to(dev), dZ.to(dev), H.to(dev), E0.to(dev), y.to(dev))]
+    for _ in range(2):
+        sets.append((draw(M, h), draw(h, f, std=0.02), draw(f, h, std=synth.residual_std(w.n_blocks)),
+                     draw(M, h, std=wb.dz_std), draw(Mc, hc), draw(Vr, hc, std=0.02),
+                     torch.randint(0, V, (Mc,), device=dev, dtype=torch.int32, generator=g)))
+    set_bytes = sum(x.numel() * x.element_size() for x in sets[0])
+    U = [torch.empty(M, f, dtype=bf, device=dev) for _ in sets]     # each set's saved U_0
     Y = torch.empty(M, f, dtype=bf, device=dev)
-    zparts = torch.randn(t, M, h, device=dev).mul_(0.05).to(bf)   # ranks 1..7: "received" partials
-    dxparts = torch.randn(t, M, h, device=dev).mul_(0.01).to(bf)
+    zparts = draw(t, M, h, std=0.05)    # ranks 1..7: "received" partials
+    dxparts = draw(t, M, h, std=0.01)
     Z = torch.empty(M, h, dtype=bf, device=dev)
     dX = torch.empty(M, h, dtype=bf, device=dev)
     dA = torch.empty(h, f, dtype=bf, device=dev)
     dB = torch.empty(f, h, dtype=bf, device=dev)
-    stats = torch.empty(t, 3, M, dtype=torch.float32, device=dev)
+    stats = torch.empty(t, 3, Mc, dtype=torch.float32, device=dev)
     stats[:, 0].normal_()
     stats[:, 1].uniform_(1.0, 100.0)
     stats[:, 2].zero_()
-    loss = torch.empty(M, dtype=torch.float32, device=dev)
+    loss = torch.empty(Mc, dtype=torch.float32, device=dev)
     ws_bwd = torch.empty(lgs.mlp_bwd_workspace_bytes(w.b, w.s, h, ffn, t, bf), dtype=torch.uint8, device=dev)
-    ws_xent = torch.empty(lgs.xent_workspace_bytes(xw.b, xw.s, h, V, t), dtype=torch.uint8, device=dev)
+    ws_xent = torch.empty(lgs.xent_workspace_bytes(xw.b, xw.s, hc, V, t), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     names = ["mlp_fwd", "sum_z", "mlp_bwd", "sum_dx", "xent", "xent_merge"]
+    counter = [0]
 
     def one_step(ev=None, marks=(0, 1, 2, 3, 4, 5, 6)):
+        k = counter[0] % len(sets)
+        counter[0] += 1
+        Xk, Ak, Bk, dZk, Hk, Ek, yk = sets[k]
+
         def mark(i):
             if ev is not None and i in marks:
                 ev[i].record(stream)
         mark(0)
-        lgs.tp_mlp_fwd(w.b, w.s, h, ffn, t, 0, Xd, A0d, B0d, zparts[0], U_i=U, Y_i=Y, stream=stream)
+        lgs.tp_mlp_fwd(w.b, w.s, h, ffn, t, 0, Xk, Ak, Bk, zparts[0], U_i=U[k], Y_i=Y, stream=stream)
         mark(1)
         lgs.shard_partial_sum("sum", t, M * h, zparts, M * h, Z, stream=stream)
         mark(2)
-        lgs.tp_mlp_bwd(w.b, w.s, h, ffn, t, 0, Xd, A0d, B0d, U, dZd, dxparts[0], dA, dB,
+        lgs.tp_mlp_bwd(w.b, w.s, h, ffn, t, 0, Xk, Ak, Bk, U[k], dZk, dxparts[0], dA, dB,
                        workspace=ws_bwd, stream=stream)
         mark(3)
         lgs.shard_partial_sum("sum", t, M * h, dxparts, M * h, dX, stream=stream)
         mark(4)
-        lgs.vocab_parallel_xent_fwd(xw.b, xw.s, h, V, t, 0, Hd, E0d, yd, stats[0, 0], stats[0, 1],
+        lgs.vocab_parallel_xent_fwd(xw.b, xw.s, hc, V, t, 0, Hk, Ek, yk, stats[0, 0], stats[0, 1],
                                     stats[0, 2], workspace=ws_xent, stream=stream)
         mark(5)
-        lgs.shard_partial_sum("xent", t, M, stats, 3 * M, loss, stream=stream)
+        lgs.shard_partial_sum("xent", t, Mc, stats, 3 * Mc, loss, stream=stream)
         mark(6)
 
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, len(sets))):
         one_step()
     torch.cuda.synchronize()
 
-    fl = step_flops(M, h, f, Vr)
+    mf = mlp_flops(M, h, f)
+    fl_x = xent_flops(Mc, hc, Vr)
     # The per-configuration timings, the streaming CE measurement and the clock
     # sampling run before the timed steps, so that those see the device in the
-    # steady state a training run keeps it in (the first tens of steps after
-    # start-up run several percent slower while clocks and caches settle).
+    # steady state a training run keeps it in.
     configs = {} if args.no_per_config else per_config(torch, lgs, reps=50)
-    if not args.no_per_config:
-        # CE backward of the same slice from the merged log-sum-exp, dloss = 1/M:
-        # the recomputed logit GEMM with its gradient epilogue, then dH_0 = G E_0
-        # and dE_0 = G^T H in one launch (3 x 2 M h V_r FLOP).
-        lse = torch.empty(M, dtype=torch.float32, device=dev)
-        lgs.shard_partial_sum("xent_lse", t, M, stats, 3 * M, lse)
-        dl = torch.full((M,), 1.0 / M, dtype=torch.float32, device=dev)
-        dH0 = torch.empty(M, h, dtype=bf, device=dev)
-        dE0 = torch.empty(Vr, h, dtype=bf, device=dev)
-        ws_xb = torch.empty(lgs.xent_bwd_workspace_bytes(xw.b, xw.s, h, V, t), dtype=torch.uint8, device=dev)
-
-        def xbwd(i):
-            lgs.vocab_parallel_xent_bwd(xw.b, xw.s, h, V, t, 0, Hd, E0d, yd, lse, dH0, dE0, dloss=dl,
-                                        workspace=ws_xb, stream=stream)
-        rep = _timed_report(torch, xbwd, 3 * fl["xent"], 50)
-        rep["tokens_per_s"] = round(M / (rep["ms"] * 1e-3), 0)
-        rep["note"] = "median of per-call times; one input set (the step's)"
-        configs["xent_8p3b_bwd"] = rep
-        del lse, dl, dH0, dE0, ws_xb
-        # sequence-parallel stand-ins at the same shape (s = 1024, b = 8, h = 3072,
-        # t = 8): rank 0's reduce-scatter of the 8 partials, and the all-gather of
-        # 8 chunks into [s*b, h]; both pure HBM streams
-        chunk = M * h // t
-        rs_out = torch.empty(M // t, h, dtype=bf, device=dev)
-        ag_in = torch.randn(t, M // t, h, device=dev).to(bf)
-        ag_out = torch.empty(M, h, dtype=bf, device=dev)
-        rs_ms = time_calls(torch, lambda: lgs.shard_reduce_scatter(t, 0, w.s, w.b, h, zparts, M * h, rs_out), 50)
-        ag_ms = time_calls(torch, lambda: lgs.shard_all_gather(t, w.s, w.b, h, ag_in, chunk, ag_out), 50)
-        rs_bytes, ag_bytes = (t + 1) * chunk * 2, 2 * M * h * 2
-        configs["sp_8p3b"] = {
-            "reduce_scatter_us": round(rs_ms * 1e3, 2),
-            "reduce_scatter_GBs": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1),
-            "all_gather_us": round(ag_ms * 1e3, 2),
-            "all_gather_GBs": round(ag_bytes / (ag_ms * 1e-3) / 1e9, 1),
-            "note": "bytes = every byte read once + written once; HBM peak 8000 GB/s"}
-        del rs_out, ag_in, ag_out
-        stream_ce = ce_reduction_stream(torch, lgs, xw)
+    stream_ce = None if args.no_per_config else ce_reduction_stream(torch, lgs, xw)
     gpu_clock = None if args.no_clock else sample_gpu_clock(torch, one_step)
 
-    # Timed region: K whole steps.  Only the CE entry point is bracketed by HIP
-    # events here (its roofline is measured live); events between every entry
-    # point cost the step about 2.5%, so the per-entry-point breakdown comes
-    # from a second, untimed pass of K steps below.
-    ce_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    # Timed region: K whole steps.  Only the backward entry point is bracketed
+    # by HIP events here (its roofline is measured live); events between every
+    # entry point cost the step a few percent, so the per-entry-point
+    # breakdown comes from a second, untimed pass of K steps below.
+    bw_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    counter[0] = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(ce_ev[i], marks=(4, 5))
+        one_step(bw_ev[i], marks=(2, 3))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
-    xent_s = sum(e[4].elapsed_time(e[5]) for e in ce_ev) / args.steps * 1e-3
+    bwd_s = sum(e[2].elapsed_time(e[3]) for e in bw_ev) / args.steps * 1e-3
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     for i in range(args.steps):
@@ -593,12 +812,13 @@ def main():
     for ev in evs:
         for j, n in enumerate(names):
             per[n] += ev[j].elapsed_time(ev[j + 1])
-    per = {n: v / args.steps for n, v in per.items()}   # ms per launch of each entry point
+    per = {n: v / args.steps for n, v in per.items()}   # ms per call of each entry point
 
-    total_flops = sum(fl.values())
+    total_flops = mf["fwd"] + mf["bwd"] + fl_x
     tflops = total_flops / (ms * 1e-3) / 1e12
+    mlp_s = (per["mlp_fwd"] + per["mlp_bwd"]) * 1e-3
     sum_bytes = (t + 1) * M * h * 2
-    traffic = read_counters()
+    bwd_tf = mf["bwd"] / bwd_s / 1e12
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -611,47 +831,52 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, residual weight scaled 1/sqrt(2N), uniform targets)",
-        "config": {"workload": "8.3B-shape TP shard step, rank 0 of t=8: GeLU MLP fwd+bwd "
-                               "(b=8, s=1024, h=3072, ffn=12288) + sums of 8 partials + vocab-parallel "
-                               "fused CE (vocab 51200) + CE merge",
-                   "b": w.b, "s": w.s, "h": h, "ffn": ffn, "t": t, "rank": 0, "vocab": V},
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, residual weight scaled 1/sqrt(2N), "
+                "dZ ~ N(0,0.01), uniform targets)",
+        "config": {"workload": "70B-shape TP shard step, rank 0 of t=8: GeLU MLP fwd+bwd (b=1, s=4096, h=8192, "
+                               "ffn=28672) with the sums of 8 partials, plus the vocab-parallel fused CE of "
+                               "slice 0 (8.3B shapes: 8192 tokens, h=3072, vocab 51200) and its merge",
+                   "b": w.b, "s": w.s, "h": h, "ffn": ffn, "t": t, "rank": 0,
+                   "ce": {"tokens": Mc, "h": hc, "vocab": V},
+                   "input_sets": f"{len(sets)} rotated, {len(sets) * set_bytes / 1e9:.2f} GB of operands in all "
+                                 "(Infinity Cache 0.27 GB): each step reads its operands from HBM"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "gpu_clock": gpu_clock,
-        "timing": "value and ms_per_step: wall clock over the K timed steps (events around the CE call "
-                  "only); entry_point_ms: a separate pass of K steps with events between entry points",
-        "mlp_fwd_bwd_tflops": round((fl["mlp_fwd"] + fl["mlp_bwd"]) / ((per["mlp_fwd"] + per["mlp_bwd"]) * 1e-3) / 1e12, 2),
-        "mlp_fwd_tflops": round(fl["mlp_fwd"] / (per["mlp_fwd"] * 1e-3) / 1e12, 2),
-        "mlp_bwd_tflops": round(fl["mlp_bwd"] / (per["mlp_bwd"] * 1e-3) / 1e12, 2),
-        "ce_tokens_per_s": round(M / xent_s, 0),
-        "ce_tflops": round(fl["xent"] / xent_s / 1e12, 2),
+        "timing": "value and ms_per_step: wall clock over the K timed steps, FLOPs of the MLP forward and "
+                  "backward and the CE logit GEMM (GEMM FLOPs only, 2MNK each); entry_point_ms: a separate "
+                  "pass of K steps with events between entry points",
+        "mlp_fwd_bwd_tflops": round((mf["fwd"] + mf["bwd"]) / mlp_s / 1e12, 2),
+        "mlp_fwd_bwd_pct_bf16_peak": round(100 * (mf["fwd"] + mf["bwd"]) / mlp_s / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "mlp_fwd_tflops": round(mf["fwd"] / (per["mlp_fwd"] * 1e-3) / 1e12, 2),
+        "mlp_bwd_tflops": round(mf["bwd"] / (per["mlp_bwd"] * 1e-3) / 1e12, 2),
+        "ce_tokens_per_s": round(Mc / (per["xent"] * 1e-3), 0),
+        "ce_tflops": round(fl_x / (per["xent"] * 1e-3) / 1e12, 2),
         "sum_partials_gbs": round(sum_bytes / (per["sum_z"] * 1e-3) / 1e9, 1),
         "entry_point_ms": {n: round(v, 4) for n, v in per.items()},
         "roofline": {
-            "kernel": "vocab_parallel_xent_fwd (fused logit GEMM + CE partials, with its slab merge)",
+            "kernel": "tp_mlp_bwd at the 70B shape: the dY+GeLU' GEMM and the grouped dB/dA/dX GEMM "
+                      "(two launches, 962.1 GFLOP per call), timed with HIP events around the entry point",
             "bound": "mfma",
-            "achieved": round(fl["xent"] / xent_s / 1e12, 2),
+            "achieved": round(bwd_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(fl["xent"] / xent_s / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
+            "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": read_counters(),
+            "algorithmic_bytes": mlp_bwd_bytes(M, h, f),
         },
     }
-    configs["mlp_8p3b_fwd"] = {"ms": round(per["mlp_fwd"], 4), "tflops": out["mlp_fwd_tflops"],
-                               "pct_bf16_peak": round(100 * out["mlp_fwd_tflops"] / PEAK_BF16_TFLOPS, 2),
-                               "note": "from the event pass over the step"}
-    configs["xent_8p3b"] = {"ms": round(xent_s * 1e3, 4), "tflops": out["ce_tflops"],
-                            "pct_bf16_peak": round(100 * out["ce_tflops"] / PEAK_BF16_TFLOPS, 2),
-                            "tokens_per_s": out["ce_tokens_per_s"], "note": "from the timed steps"}
     out["per_config"] = configs
-    if not args.no_per_config:
+    if stream_ce is not None:
         out["ce_reduction_stream"] = stream_ce
     if not args.no_cpu_baseline:
-        import numpy as np
-        inputs = (X.float().numpy(), A0.float().double().numpy(), B0.float().double().numpy(),
-                  dZ.float().numpy(), H.float().numpy(), E0.float().double().numpy(),
-                  y.numpy().astype(np.int64))
-        out["cpu_baseline"] = cpu_baseline(w, xw, inputs)
+        w2 = WORKLOADS["mlp_8p3b_fwd"]
+        X2, A2, B2 = synth.mlp_weights(w2)
+        host = {"X": X.double().numpy(), "A0": A0.double().numpy(), "B0": B0.double().numpy(),
+                "dZ": dZ.double().numpy(), "H": H.double().numpy(), "E": E.double().numpy(),
+                "y": y.numpy().astype("int64"), "Vr": Vr, "X2": X2.double().numpy(),
+                "A2_0": A2[:, :w2.f_i].double().numpy(), "B2_0": B2[:w2.f_i].double().numpy()}
+        del X2, A2, B2
+        out["cpu_baseline"] = cpu_baseline(host)
     print(json.dumps(out), flush=True)
 
 

@@ -30,14 +30,22 @@ def test_page_figure_is_the_six_p_t_rule():
 
 @pytest.mark.parametrize("M,h,f", [(8192, 3072, 1536), (4096, 8192, 3584), (7, 40, 24)])
 def test_bench_counts_forward_2pt_and_backward_4pt(M, h, f):
-    fl = bench.step_flops(M, h, f, 0)
+    fl = bench.mlp_flops(M, h, f)
     P = 2 * h * f  # the shard's parameters
-    assert fl["mlp_fwd"] == 2 * P * M
-    assert fl["mlp_bwd"] == 4 * P * M
-    assert fl["mlp_fwd"] + fl["mlp_bwd"] == 6 * P * M
+    assert fl["fwd"] == 2 * P * M
+    assert fl["bwd"] == 4 * P * M
+    assert fl["fwd"] + fl["bwd"] == 6 * P * M
 
 
 def test_bench_logit_gemm_is_one_gemm():
     M, h, Vr = 8192, 3072, 6400
-    assert bench.step_flops(M, h, 1, Vr)["xent"] == 2 * M * h * Vr  # 322.1 GFLOP per launch
-    assert bench.step_flops(M, h, 1, Vr)["xent"] == pytest.approx(322.1e9, rel=1e-3)
+    assert bench.xent_flops(M, h, Vr) == 2 * M * h * Vr  # 322.1 GFLOP per launch
+    assert bench.xent_flops(M, h, Vr) == pytest.approx(322.1e9, rel=1e-3)
+
+
+def test_bench_backward_algorithmic_bytes():
+    """tp_mlp_bwd at the 70B shape: X, U, dZ, dX (3 x [M, h] + [M, f]), A_i,
+    B_i, dA_i, dB_i (4 x h f), and Y_i, dU_i written once and read once
+    (4 x [M, f]), in bf16."""
+    M, h, f = 4096, 8192, 3584
+    assert bench.mlp_bwd_bytes(M, h, f) == 2 * (3 * M * h + M * f + 4 * h * f + 4 * M * f)
