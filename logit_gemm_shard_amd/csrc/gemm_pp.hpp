@@ -258,8 +258,13 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
   };
   // Read phase: this wave's fragments of tile kt, then the loads of tile
   // kt+S-1 (into the stage that tile kt-1 left), then wait for the fragments.
+  // The fragment reads overwrite registers that this wave's previous MFMAs
+  // read as sources: on gfx950 an MFMA reads its A and B operands at issue,
+  // so overwriting them afterwards needs no wait states (the compiler's own
+  // hazard model inserts none for a DS or VALU write there).  Only the
+  // compiler barrier below is needed.
   auto read_phase = [&](int kt) {
-    asm volatile("s_nop 7" ::: "memory");  // earlier MFMAs' operand reads retire first
+    asm volatile("" ::: "memory");
     const uint32_t sb = (uint32_t)((kt % T::kStages) * T::kStage);
     read_sub(sb, std::integral_constant<int, 0>{});
     read_sub(sb, std::integral_constant<int, 1>{});
