@@ -59,6 +59,28 @@ int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk);
 int lgs_test_xent_rows_bf16(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
                             const int32_t* targets, float* m, float* l, float* T, void* stream);
 
+/*
+ * Debug builds (liblgs_debug.so, compiled with -DLGS_DEBUG): every entry point
+ * records the device spans it validated, and every launcher checks, on the
+ * host before each kernel launch, that each span the kernel reads or writes
+ * lies inside one of them (printing the span and aborting if not).
+ *   lgs_test_debug_build:  1 in a debug build, 0 in the product build.
+ *   lgs_test_set_dry_run:  debug builds: with on != 0 the entry points make
+ *                          no HIP call at all (no launch, no error query, no
+ *                          symbol lookup) but run every check, so fake device
+ *                          pointers may be passed; returns 0 (-1 in the
+ *                          product build, where it does nothing).
+ *   lgs_test_debug_checks: checks run so far in this process (0 in the
+ *                          product build).
+ */
+int lgs_test_debug_build(void);
+int lgs_test_set_dry_run(int on);
+long lgs_test_debug_checks(void);
+/* The check itself: registers [allowed, allowed + allowed_bytes) as a validated
+   span, then checks [p, p + bytes) against it (aborting with a message if it
+   is not inside), then drops the span; returns 0 (-1 in the product build). */
+int lgs_test_debug_span(const void* allowed, size_t allowed_bytes, const void* p, size_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,7 +74,12 @@ SIGNATURES = [
     ("lgs_test_mlp_bwd_plan", _i, [_i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     ("lgs_test_gemm_bf16", _i, [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
     ("lgs_test_xent_rows_bf16", _i, [_i, _i, _i, _p, _i64, _p, _p, _p, _p, _p]),
+    ("lgs_test_debug_build", _i, []),
+    ("lgs_test_set_dry_run", _i, [_i]),
+    ("lgs_test_debug_checks", ctypes.c_long, []),
+    ("lgs_test_debug_span", _i, [_p, _sz, _p, _sz]),
 ]
+LIB_DEBUG_PATH = os.path.join(_HERE, "liblgs_debug.so")
 
 
 class LgsError(RuntimeError):

@@ -4,7 +4,10 @@
 
 Each ``csrc/*.hip`` file is compiled by hipcc in parallel into
 ``logit_gemm_shard_amd/_build/``, then linked into
-``logit_gemm_shard_amd/liblgs.so``.  Always rebuilds.
+``logit_gemm_shard_amd/liblgs.so``.  The same sources compiled with
+``-DLGS_DEBUG`` (objects in ``_build_debug/``) give ``liblgs_debug.so``, whose
+launchers check every device span a kernel touches against the buffers the
+entry point validated (used by the tests only).  Always rebuilds.
 """
 
 import argparse
@@ -18,8 +21,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblgs.so")
+LIB_DEBUG = os.path.join(PKG, "liblgs_debug.so")
 ARCH = "gfx950"
 
 # Packed fp32 ops (v_pk_*_f32) are switched off for all device code.
@@ -46,24 +49,36 @@ def _run(cmd, verbose):
     return out
 
 
-def build(jobs=None, verbose=False, extra_flags=()):
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    cc = hipcc()
-    objs = []
-    cmds = []
-    for src in srcs:
-        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+def _objects(debug, extra_flags):
+    build_dir = os.path.join(PKG, "_build_debug" if debug else "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    flags = [*COMMON, *DEVICE_FLAGS, *extra_flags] + (["-DLGS_DEBUG"] if debug else [])
+    objs, cmds = [], []
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON, *DEVICE_FLAGS, *extra_flags, "-c", src, "-o", obj])
+        cmds.append([hipcc(), *flags, "-c", src, "-o", obj])
+    return objs, cmds
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
+    _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    os.replace(tmp, lib)
+
+
+def build(jobs=None, verbose=False, extra_flags=(), debug=True):
+    """Compile and link liblgs.so, and (debug=True) liblgs_debug.so too."""
+    variants = [(False, LIB)] + ([(True, LIB_DEBUG)] if debug else [])
+    plan = [(_objects(d, extra_flags), lib) for d, lib in variants]
+    cmds = [c for (objs, cs), _ in plan for c in cs]
     jobs = jobs or min(len(cmds), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(lambda c: _run(c, verbose), cmds):
             if out.strip() and verbose:
                 print(out)
-    tmp = LIB + ".tmp"
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    for (objs, _), lib in plan:
+        _link(objs, lib, verbose)
     return LIB
 
 

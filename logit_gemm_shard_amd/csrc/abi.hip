@@ -7,6 +7,7 @@
 
 #include <climits>
 
+#include "debug.hpp"
 #include "internal.hpp"
 #include "lgs.h"
 #include "lgs_testing.h"
@@ -22,13 +23,24 @@ int fail(int code, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
+  lgs::debug::end_call();
   return code;
 }
 
 int ok() {
   g_err[0] = 0;
+  lgs::debug::end_call();
   return LGS_OK;
 }
+
+// Drop an error a previous launch left behind, so that the status after this
+// call's launches is this call's own (no HIP call in a debug dry run).
+void clear_hip_error() {
+  if (!lgs::debug::dry_run()) clear_hip_error();
+}
+
+// Debug builds: a device span this call validated (debug.hpp).
+void allow(const void* p, size_t bytes) { lgs::debug::allow(p, bytes); }
 
 size_t elt(int dtype) { return dtype == LGS_BF16 ? 2u : 4u; }
 size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
@@ -72,6 +84,7 @@ int check_mat(const char* name, const void* p, int64_t rows, int64_t ld, int64_t
   } else if (!aligned(p, 4)) {
     return fail(LGS_ERR_UNSUPPORTED, "%s: fp32 operands need a 4-byte aligned base", name);
   }
+  allow(p, lgs::debug::mat_bytes(rows, ld, width, elt(dtype)));
   return LGS_OK;
 }
 
@@ -173,10 +186,11 @@ LGS_API int tp_mlp_fwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
       return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  allow(workspace, workspace_bytes);
     Y_i = workspace;
     ldy = f;
   }
-  (void)hipGetLastError();  // start from a clean error state
+  clear_hip_error();
   return launched(lgs::mlp_fwd(dtype == LGS_BF16, M, h, f, act, X, ldx, A_i, lda, B_i, ldb, U_i,
                                ldu, Y_i, ldy, Z_i, ldz, (hipStream_t)stream));
 }
@@ -202,11 +216,12 @@ LGS_API int tp_mlp_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype,
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dU_i, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  allow(workspace, workspace_bytes);
   const size_t half = round256((size_t)M * f * elt(dtype));
   char* y = (char*)workspace;
   char* du = y + half;
   char* split = need > 2 * half ? y + 2 * half : nullptr;
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::mlp_bwd(dtype == LGS_BF16, M, h, f, act, X, ldx, A_i, lda, B_i, ldb, U_i,
                                ldu, dZ, lddz, dX_i, lddx, dA_i, ldda, dB_i, lddb, y, du, split,
                                (hipStream_t)stream));
@@ -245,10 +260,11 @@ LGS_API int tp_swiglu_fwd(int b, int s, int h, int ffn, int t, int rank, int dty
       return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  allow(workspace, workspace_bytes);
     Y_i = workspace;
     ldy = f;
   }
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::swiglu_fwd(M, h, f, X, ldx, Wgu_i, ldwgu, Wd_i, ldwd, GU_i, ldgu, Y_i, ldy,
                                   Z_i, ldz, (hipStream_t)stream));
 }
@@ -275,9 +291,10 @@ LGS_API int tp_swiglu_bwd(int b, int s, int h, int ffn, int t, int rank, int dty
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dGU_i, %zu given",
                 need, workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  allow(workspace, workspace_bytes);
   char* y = (char*)workspace;
   char* dgu = y + round256((size_t)M * f * 2);
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::swiglu_bwd(M, h, f, X, ldx, Wgu_i, ldwgu, Wd_i, ldwd, GU_i, ldgu, dZ, lddz,
                                   dX_i, lddx, dWgu_i, lddwgu, dWd_i, lddwd, y, dgu,
                                   (hipStream_t)stream));
@@ -292,6 +309,7 @@ int bwd_workspace(int b, int s, int h, int ffn, int t, int dtype, void* workspac
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for Y_i and dU_i, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  allow(workspace, workspace_bytes);
   *y = (char*)workspace;
   *du = *y + round256((size_t)b * s * (ffn / t) * elt(dtype));
   return LGS_OK;
@@ -311,7 +329,7 @@ LGS_API int tp_mlp_bwd_dgelu(int b, int s, int h, int ffn, int t, int rank, int 
   if ((st = check_mat("dZ", dZ, M, lddz, h, dtype, true))) return st;
   char *y, *du;
   if ((st = bwd_workspace(b, s, h, ffn, t, dtype, workspace, workspace_bytes, &y, &du))) return st;
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::mlp_bwd_dgelu(dtype == LGS_BF16, M, h, f, act, B_i, ldb, U_i, ldu, dZ, lddz, y,
                                      du, (hipStream_t)stream));
 }
@@ -326,7 +344,7 @@ LGS_API int tp_mlp_bwd_dx(int b, int s, int h, int ffn, int t, int rank, int dty
   if ((st = check_mat("dX_i", dX_i, M, lddx, h, dtype, true))) return st;
   char *y, *du;
   if ((st = bwd_workspace(b, s, h, ffn, t, dtype, workspace, workspace_bytes, &y, &du))) return st;
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::mlp_bwd_dx(dtype == LGS_BF16, M, h, f, A_i, lda, du, dX_i, lddx,
                                   (hipStream_t)stream));
 }
@@ -344,7 +362,7 @@ LGS_API int tp_mlp_bwd_dw(int b, int s, int h, int ffn, int t, int rank, int dty
   if ((st = check_mat("dB_i", dB_i, f, lddb, h, dtype, true))) return st;
   char *y, *du;
   if ((st = bwd_workspace(b, s, h, ffn, t, dtype, workspace, workspace_bytes, &y, &du))) return st;
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::mlp_bwd_dw(dtype == LGS_BF16, M, h, f, X, ldx, dZ, lddz, y, du, dA_i, ldda, dB_i,
                                   lddb, (hipStream_t)stream));
 }
@@ -371,6 +389,9 @@ int check_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int dtype, c
     return fail(LGS_ERR_UNSUPPORTED, "per-token arrays must be 4-byte aligned");
   if (loss && t != 1)
     return fail(LGS_ERR_INVALID_ARG, "loss needs the whole vocabulary (t == 1); merge ranks with shard_partial_sum");
+  for (const void* a : {(const void*)targets, (const void*)m_r, (const void*)l_r, (const void*)tgt_r,
+                        (const void*)argmax_r, (const void*)loss})
+    allow(a, (size_t)M * 4);
   return LGS_OK;
 }
 
@@ -390,7 +411,8 @@ LGS_API int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int r
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  (void)hipGetLastError();
+  allow(workspace, workspace_bytes);
+  clear_hip_error();
   return launched(lgs::xent_fwd(M, h, Vr, rank * Vr, H, ldh, E_r, lde, targets, m_r, l_r, tgt_r,
                                 argmax_r, loss, workspace, (hipStream_t)stream));
 }
@@ -413,7 +435,7 @@ LGS_API int vocab_parallel_xent_fwd_noalloc(int b, int s, int h, int vocab, int 
                 "%zu bytes of slab partials needed, the static scratch holds %zu: use "
                 "vocab_parallel_xent_fwd with a workspace",
                 need, (size_t)LGS_XENT_NOALLOC_SCRATCH_BYTES);
-  (void)hipGetLastError();
+  clear_hip_error();
   void* scratch = nullptr;
   const hipError_t e = lgs::xent_static_scratch((hipStream_t)stream, &scratch);
   if (e != hipSuccess)
@@ -450,6 +472,7 @@ LGS_API int vocab_parallel_xent_bwd(int b, int s, int h, int vocab, int t, int r
   if (!targets || !lse) return fail(LGS_ERR_INVALID_ARG, "targets and lse are required");
   if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(dloss, 4))
     return fail(LGS_ERR_UNSUPPORTED, "per-token arrays must be 4-byte aligned");
+  for (const void* a : {(const void*)targets, (const void*)lse, (const void*)dloss}) allow(a, (size_t)M * 4);
   if ((int64_t)M * Vr * 2 >= ((int64_t)1 << 31))
     return fail(LGS_ERR_UNSUPPORTED, "the slice's gradient G (M x vocab/t bf16) must span less than 2 GiB");
   const size_t need = lgs_xent_bwd_workspace_bytes(b, s, h, vocab, t, dtype);
@@ -457,7 +480,8 @@ LGS_API int vocab_parallel_xent_bwd(int b, int s, int h, int vocab, int t, int r
     return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes needed for G, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  (void)hipGetLastError();
+  allow(workspace, workspace_bytes);
+  clear_hip_error();
   return launched(lgs::xent_bwd(M, h, Vr, rank * Vr, H, ldh, E_r, lde, targets, lse, dloss, dH_r,
                                 lddh, dE_r, ldde, workspace, (hipStream_t)stream));
 }
@@ -474,7 +498,9 @@ LGS_API int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dt
     if (!aligned(parts, elt(in_dtype)) || !aligned(out, elt(out_dtype)))
       return fail(LGS_ERR_UNSUPPORTED, "misaligned parts or out");
     if (n == 0) return ok();
-    (void)hipGetLastError();
+    allow(parts, (size_t)((t - 1) * part_stride + n) * elt(in_dtype));
+    allow(out, (size_t)n * elt(out_dtype));
+    clear_hip_error();
     return launched(lgs::partial_sum(t, n, in_dtype == LGS_BF16, out_dtype == LGS_BF16, parts,
                                      part_stride, out, (hipStream_t)stream));
   }
@@ -489,7 +515,9 @@ LGS_API int shard_partial_sum(int op, int t, int64_t n, int in_dtype, int out_dt
                   (long long)per, (long long)(per * n));
     if (!aligned(parts, 4) || !aligned(out, 4)) return fail(LGS_ERR_UNSUPPORTED, "misaligned parts or out");
     if (n == 0) return ok();
-    (void)hipGetLastError();
+    allow(parts, (size_t)((t - 1) * part_stride + per * n) * 4);
+    allow(out, (size_t)n * 4);
+    clear_hip_error();
     return launched(lgs::xent_combine(t, n, (const float*)parts, part_stride, lse_only, (float*)out,
                                       (hipStream_t)stream));
   }
@@ -521,7 +549,9 @@ LGS_API int shard_reduce_scatter(int t, int rank, int s, int b, int h, int in_dt
                 (long long)n);
   if (!aligned(parts, elt(in_dtype)) || !aligned(out, elt(out_dtype)))
     return fail(LGS_ERR_UNSUPPORTED, "misaligned parts or out");
-  (void)hipGetLastError();
+  allow(parts, (size_t)((t - 1) * (t > 1 ? part_stride : 0) + n) * elt(in_dtype));
+  allow(out, (size_t)chunk * elt(out_dtype));
+  clear_hip_error();
   return launched(lgs::reduce_scatter(t, chunk, rank, in_dtype == LGS_BF16, out_dtype == LGS_BF16,
                                       parts, part_stride, out, (hipStream_t)stream));
 }
@@ -539,7 +569,9 @@ LGS_API int shard_all_gather(int t, int s, int b, int h, int dtype, const void* 
   if (t > 65535) return fail(LGS_ERR_UNSUPPORTED, "t=%d exceeds the launch grid", t);
   if (!aligned(shards, elt(dtype)) || !aligned(out, elt(dtype)))
     return fail(LGS_ERR_UNSUPPORTED, "misaligned shards or out");
-  (void)hipGetLastError();
+  allow(shards, (size_t)((t - 1) * (t > 1 ? shard_stride : 0) + chunk) * elt(dtype));
+  allow(out, (size_t)t * chunk * elt(dtype));
+  clear_hip_error();
   return launched(lgs::all_gather(t, chunk, dtype == LGS_BF16, shards, shard_stride, out,
                                   (hipStream_t)stream));
 }
@@ -596,7 +628,8 @@ LGS_API int tp_attn_qkv_fwd(int b, int s, int h, int n_q_heads, int n_kv_heads, 
   if (workspace && !aligned(workspace, 256))
     return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   void* scratch = (need && workspace && workspace_bytes >= need) ? workspace : nullptr;
-  (void)hipGetLastError();
+  if (scratch) allow(scratch, workspace_bytes);
+  clear_hip_error();
   return launched(lgs::attn_qkv_fwd(M, h, nqkv, X, ldx, Wqkv_i, ldw, QKV_i, ldqkv, scratch,
                                     (hipStream_t)stream));
 }
@@ -614,7 +647,7 @@ LGS_API int tp_attn_qkv_bwd(int b, int s, int h, int n_q_heads, int n_kv_heads, 
   if ((st = check_mat("dQKV_i", dQKV_i, M, lddqkv, nqkv, dtype, true))) return st;
   if ((st = check_mat("dX_i", dX_i, M, lddx, h, dtype, true))) return st;
   if ((st = check_mat("dWqkv_i", dWqkv_i, h, lddw, nqkv, dtype, true))) return st;
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::attn_qkv_bwd(M, h, nqkv, X, ldx, Wqkv_i, ldw, dQKV_i, lddqkv, dX_i, lddx,
                                     dWqkv_i, lddw, (hipStream_t)stream));
 }
@@ -630,7 +663,7 @@ LGS_API int tp_attn_out_fwd(int b, int s, int h, int n_q_heads, int head_dim, in
   if ((st = check_mat("A_i", A_i, M, lda, hq, dtype, true))) return st;
   if ((st = check_mat("Wo_i", Wo_i, hq, ldwo, h, dtype, true))) return st;
   if ((st = check_mat("Z_i", Z_i, M, ldz, h, dtype, true))) return st;
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::attn_out_fwd(M, hq, h, A_i, lda, Wo_i, ldwo, Z_i, ldz, (hipStream_t)stream));
 }
 
@@ -662,7 +695,8 @@ LGS_API int tp_attn_out_bwd(int b, int s, int h, int n_q_heads, int head_dim, in
   if (workspace && !aligned(workspace, 256))
     return fail(LGS_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   void* scratch = (need && workspace && workspace_bytes >= need) ? workspace : nullptr;
-  (void)hipGetLastError();
+  if (scratch) allow(scratch, workspace_bytes);
+  clear_hip_error();
   return launched(lgs::attn_out_bwd(M, hq, h, A_i, lda, Wo_i, ldwo, dZ, lddz, dA_i, ldda, dWo_i,
                                     lddwo, scratch, (hipStream_t)stream));
 }
@@ -704,7 +738,7 @@ LGS_API int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int 
   if ((st = check_mat("A", A, a_kmajor ? M : K, lda, a_kmajor ? K : M, LGS_BF16, true))) return st;
   if ((st = check_mat("B", B, b_kmajor ? N : K, ldb, b_kmajor ? K : N, LGS_BF16, true))) return st;
   if ((st = check_mat("C", C, M, ldc, N, LGS_BF16, true))) return st;
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::gemm_store_bf16(tile, a_kmajor != 0, b_kmajor != 0, M, N, K, A, lda, B, ldb,
                                        C, ldc, (hipStream_t)stream));
 }
@@ -718,7 +752,9 @@ LGS_API int lgs_test_xent_rows_bf16(int M, int Vr, int vocab_start, const void* 
   if ((st = check_mat("Z", Z, M, ldz, Vr, LGS_BF16, M > 0))) return st;
   if (M > 0 && (!targets || !m || !l || !T))
     return fail(LGS_ERR_INVALID_ARG, "targets, m, l and T are required");
+  for (const void* a : {(const void*)targets, (const void*)m, (const void*)l, (const void*)T})
+    allow(a, (size_t)M * 4);
   if (M == 0) return ok();
-  (void)hipGetLastError();
+  clear_hip_error();
   return launched(lgs::xent_rows(M, Vr, vocab_start, Z, ldz, targets, m, l, T, (hipStream_t)stream));
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "debug.hpp"
+
 namespace lgs {
 
 typedef __bf16 bf16;

@@ -17,6 +17,7 @@ struct EpiStore {
   T* C;
   int64_t ldc;
   int M, N;
+  void debug_spans(int) const { LGS_NEED(C, debug::mat_bytes(M, ldc, N, sizeof(T)), "EpiStore C"); }
   __device__ __forceinline__ bf16x8 load8(int, int) const { return bf16x8{}; }
   __device__ __forceinline__ void apply8(int m, int n, const float* v, bf16x8) const {
     apply<8>(m, n, v);
@@ -37,6 +38,10 @@ struct EpiGeluFwd {
   T* Y;
   int64_t ldy;
   int M, N, act;
+  void debug_spans(int) const {
+    if (U) LGS_NEED(U, debug::mat_bytes(M, ldu, N, sizeof(T)), "EpiGeluFwd U");
+    LGS_NEED(Y, debug::mat_bytes(M, ldy, N, sizeof(T)), "EpiGeluFwd Y");
+  }
   __device__ __forceinline__ bf16x8 load8(int, int) const { return bf16x8{}; }
   __device__ __forceinline__ void apply8(int m, int n, const float* v, bf16x8) const {
     apply<8>(m, n, v);
@@ -63,6 +68,11 @@ struct EpiGeluBwd {
   T* Y;
   int64_t ldy;
   int M, N, act;
+  void debug_spans(int) const {
+    LGS_NEED(U, debug::mat_bytes(M, ldu, N, sizeof(T)), "EpiGeluBwd U");
+    LGS_NEED(dU, debug::mat_bytes(M, lddu, N, sizeof(T)), "EpiGeluBwd dU");
+    LGS_NEED(Y, debug::mat_bytes(M, ldy, N, sizeof(T)), "EpiGeluBwd Y");
+  }
   // bf16 path: the chunk's 8 values of U (zeros outside the matrix).
   __device__ __forceinline__ bf16x8 load8(int m, int n) const {
     if (m >= M || n >= N) return bf16x8{};
@@ -98,7 +108,8 @@ struct EpiPartialF32 {
   float* W;
   int64_t ldw, slice;  // row pitch and slice pitch (floats)
   int M, N;
-  __device__ __forceinline__ EpiPartialF32 split(int s) const {
+  void debug_spans(int) const { LGS_NEED(W, debug::mat_bytes(M, ldw, N, 4), "EpiPartialF32 slice"); }
+  __host__ __device__ __forceinline__ EpiPartialF32 split(int s) const {
     EpiPartialF32 e = *this;
     e.W = W + (int64_t)s * slice;
     return e;
@@ -131,6 +142,9 @@ struct EpiPairStore {
   T* C;  // may be null (nothing kept)
   int64_t ldc;
   int M, half;
+  void debug_spans(int) const {
+    if (C) LGS_NEED(C, debug::mat_bytes(M, ldc, 2 * (int64_t)half, sizeof(T)), "EpiPairStore [G | U]");
+  }
   __device__ __forceinline__ bf16x8 load8(int, int) const { return bf16x8{}; }
   __device__ __forceinline__ void apply8(int m, int n, const float* v, bf16x8) const {
     const int col = ((n >> 6) << 5) + (n & 31);
@@ -147,6 +161,10 @@ struct EpiSwigluFwd {
   EpiPairStore<bf16> pairs;
   EpiStore<bf16> out;
   int half;
+  void debug_spans(int bn) const {
+    pairs.debug_spans(bn);
+    out.debug_spans(bn);
+  }
   __device__ __forceinline__ bool keeps_pairs() const { return pairs.C != nullptr; }
   template <int TM, int TN>
   __device__ __forceinline__ void combine(const f32x16 (&acc)[TM][TN], f32x16 (&y)[TM][TN / 2]) const {
@@ -176,6 +194,11 @@ struct EpiSwigluBwd {
   bf16* Y;
   int64_t ldy;
   int M, half;
+  void debug_spans(int) const {
+    LGS_NEED(GU, debug::mat_bytes(M, ldgu, 2 * (int64_t)half, 2), "EpiSwigluBwd [G | U]");
+    LGS_NEED(dGU, debug::mat_bytes(M, lddgu, 2 * (int64_t)half, 2), "EpiSwigluBwd [dG | dU]");
+    LGS_NEED(Y, debug::mat_bytes(M, ldy, half, 2), "EpiSwigluBwd Y");
+  }
   __device__ __forceinline__ GateUp8 load8(int m, int n) const {
     if (m >= M || n >= half) return GateUp8{};
     const bf16* p = GU + (int64_t)m * ldgu + n;

@@ -353,6 +353,20 @@ struct GemmProblem {
   __host__ __device__ int tiles() const { return tiles_m() * tiles_n(); }
 };
 
+// Debug builds: every span problem p's blocks touch (both operands up to
+// their last element, and each buffer of the epilogue) lies inside a buffer
+// the entry point validated, and the tiles cover the output.
+template <class P>
+inline void debug_problem(const P& p) {
+  LGS_CHECK(p.M > 0 && p.N > 0 && p.K > 0);
+  LGS_CHECK((int64_t)p.tiles_m() * P::BM >= p.M && (int64_t)p.tiles_n() * P::BN >= p.N);
+  LGS_NEED(p.A, P::AK ? debug::mat_bytes(p.M, p.lda, p.K, 2) : debug::mat_bytes(p.K, p.lda, p.M, 2),
+           "GEMM operand A");
+  LGS_NEED(p.B, P::BK ? debug::mat_bytes(p.N, p.ldb, p.K, 2) : debug::mat_bytes(p.K, p.ldb, p.N, 2),
+           "GEMM operand B");
+  p.epi.debug_spans(P::BN);
+}
+
 // The block's work on output tile (tmi, tni) of problem p.
 template <class P>
 __device__ __forceinline__ void gemm_tile(const P& p, char* smem, int tmi, int tni) {
@@ -556,15 +570,19 @@ void gemm_bf16_group3_kernel(P0 p0, P1 p1, P2 p2) {
 
 template <class P>
 inline hipError_t launch_gemm(const P& p, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<P>), dim3(p.tiles()), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  debug_problem(p);
+  LGS_LAUNCH((gemm_bf16_kernel<P>), dim3(p.tiles()), dim3(kThreads), 0, stream, p);
+  return LGS_LAUNCH_STATUS();
 }
 
 template <class P0, class P1, class P2>
 inline hipError_t launch_gemm_group3(const P0& p0, const P1& p1, const P2& p2, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bf16_group3_kernel<P0, P1, P2>), dim3(p0.tiles() + p1.tiles() + p2.tiles()),
-                     dim3(kThreads), 0, stream, p0, p1, p2);
-  return hipGetLastError();
+  debug_problem(p0);
+  debug_problem(p1);
+  debug_problem(p2);
+  LGS_LAUNCH((gemm_bf16_group3_kernel<P0, P1, P2>), dim3(p0.tiles() + p1.tiles() + p2.tiles()), dim3(kThreads),
+             0, stream, p0, p1, p2);
+  return LGS_LAUNCH_STATUS();
 }
 
 }  // namespace lgs

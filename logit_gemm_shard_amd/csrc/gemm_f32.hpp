@@ -142,15 +142,19 @@ template <bool AK, bool BK, class Epi>
 inline hipError_t launch_gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb, int M,
                                   int N, int K, const Epi& epi, hipStream_t stream) {
   const int tiles32 = ((M + 31) / 32) * ((N + 31) / 32);
+  LGS_CHECK(M > 0 && N > 0 && K > 0);
+  LGS_NEED(A, AK ? debug::mat_bytes(M, lda, K, 4) : debug::mat_bytes(K, lda, M, 4), "fp32 GEMM operand A");
+  LGS_NEED(B, BK ? debug::mat_bytes(N, ldb, K, 4) : debug::mat_bytes(K, ldb, N, 4), "fp32 GEMM operand B");
+  epi.debug_spans(0);
   if (tiles32 >= 256) {
-    hipLaunchKernelGGL((gemm_f32_kernel<AK, BK, Epi, 32>), dim3(tiles32), dim3(256), 0, stream, A, lda, B,
-                       ldb, M, N, K, epi);
+    LGS_LAUNCH((gemm_f32_kernel<AK, BK, Epi, 32>), dim3(tiles32), dim3(256), 0, stream, A, lda, B, ldb, M, N, K,
+               epi);
   } else {
     const int tiles16 = ((M + 15) / 16) * ((N + 15) / 16);
-    hipLaunchKernelGGL((gemm_f32_split_kernel<AK, BK, Epi>), dim3(tiles16), dim3(64 * kSplitWaves), 0, stream,
-                       A, lda, B, ldb, M, N, K, epi);
+    LGS_LAUNCH((gemm_f32_split_kernel<AK, BK, Epi>), dim3(tiles16), dim3(64 * kSplitWaves), 0, stream, A, lda,
+               B, ldb, M, N, K, epi);
   }
-  return hipGetLastError();
+  return LGS_LAUNCH_STATUS();
 }
 
 }  // namespace lgs

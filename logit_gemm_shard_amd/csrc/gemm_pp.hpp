@@ -397,9 +397,12 @@ void gemm_pp_splitk_kernel(P p, int kchunk) {
 
 template <class P>
 inline hipError_t launch_gemm_pp_splitk(const P& p, int splits, int kchunk, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_pp_splitk_kernel<P>), dim3(p.tiles() * splits), dim3(kPPThreads), 0, stream, p,
-                     kchunk);
-  return hipGetLastError();
+  debug_problem(p);                 // the operands and slice 0
+  p.epi.split(splits - 1).debug_spans(P::BN);  // the last slice
+  LGS_CHECK(splits >= 1 && kchunk % kBK == 0 && (int64_t)(splits - 1) * kchunk < p.K &&
+            (int64_t)splits * kchunk >= p.K);
+  LGS_LAUNCH((gemm_pp_splitk_kernel<P>), dim3(p.tiles() * splits), dim3(kPPThreads), 0, stream, p, kchunk);
+  return LGS_LAUNCH_STATUS();
 }
 
 // The problem restricted to K range [k0, k0 + kc): both operands move to the
@@ -462,11 +465,18 @@ template <class P0, class P1, class P2>
 inline hipError_t launch_gemm_pp_group3_ksplit(const P0& p0, const P1& p1, const P2& p2, const KSplit& k,
                                                hipStream_t stream) {
   const int counters = p0.tiles() + p1.tiles();
-  hipLaunchKernelGGL(zero_i32_kernel, dim3((counters + 255) / 256), dim3(256), 0, stream, k.count, counters);
-  hipLaunchKernelGGL((gemm_pp_group3_ksplit_kernel<P0, P1, P2>),
-                     dim3((p0.tiles() + p1.tiles()) * k.parts + p2.tiles()), dim3(kPPThreads), 0, stream, p0, p1,
-                     p2, k);
-  return hipGetLastError();
+  debug_problem(p0);
+  debug_problem(p1);
+  debug_problem(p2);
+  static_assert(P0::BM * P0::BN == P1::BM * P1::BN, "one slot size for both split problems");
+  LGS_CHECK(k.parts >= 2 && k.kchunk % kBK == 0 && (int64_t)(k.parts - 1) * k.kchunk < p0.K &&
+            (int64_t)k.parts * k.kchunk >= p0.K && p0.K == p1.K);
+  LGS_NEED(k.part, (size_t)counters * k.parts * P0::BM * P0::BN * 4, "K-split partial slots");
+  LGS_NEED(k.count, (size_t)counters * 4, "K-split counters");
+  LGS_LAUNCH(zero_i32_kernel, dim3((counters + 255) / 256), dim3(256), 0, stream, k.count, counters);
+  LGS_LAUNCH((gemm_pp_group3_ksplit_kernel<P0, P1, P2>), dim3((p0.tiles() + p1.tiles()) * k.parts + p2.tiles()),
+             dim3(kPPThreads), 0, stream, p0, p1, p2, k);
+  return LGS_LAUNCH_STATUS();
 }
 
 // Two independent GEMMs in one launch (p0 first).
@@ -489,22 +499,28 @@ void gemm_pp_group2_kernel(P0 p0, P1 p1) {
 
 template <class P0, class P1>
 inline hipError_t launch_gemm_pp_group2(const P0& p0, const P1& p1, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_pp_group2_kernel<P0, P1>), dim3(p0.tiles() + p1.tiles()), dim3(kPPThreads), 0,
-                     stream, p0, p1);
-  return hipGetLastError();
+  debug_problem(p0);
+  debug_problem(p1);
+  LGS_LAUNCH((gemm_pp_group2_kernel<P0, P1>), dim3(p0.tiles() + p1.tiles()), dim3(kPPThreads), 0, stream, p0,
+             p1);
+  return LGS_LAUNCH_STATUS();
 }
 
 template <class P0, class P1, class P2>
 inline hipError_t launch_gemm_pp_group3(const P0& p0, const P1& p1, const P2& p2, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_pp_group3_kernel<P0, P1, P2>), dim3(p0.tiles() + p1.tiles() + p2.tiles()),
-                     dim3(kPPThreads), 0, stream, p0, p1, p2);
-  return hipGetLastError();
+  debug_problem(p0);
+  debug_problem(p1);
+  debug_problem(p2);
+  LGS_LAUNCH((gemm_pp_group3_kernel<P0, P1, P2>), dim3(p0.tiles() + p1.tiles() + p2.tiles()), dim3(kPPThreads),
+             0, stream, p0, p1, p2);
+  return LGS_LAUNCH_STATUS();
 }
 
 template <class P>
 inline hipError_t launch_gemm_pp(const P& p, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_pp_kernel<P>), dim3(p.tiles()), dim3(kPPThreads), 0, stream, p);
-  return hipGetLastError();
+  debug_problem(p);
+  LGS_LAUNCH((gemm_pp_kernel<P>), dim3(p.tiles()), dim3(kPPThreads), 0, stream, p);
+  return LGS_LAUNCH_STATUS();
 }
 
 template <int BM, int BN, bool AK, bool BK, class Epi>

@@ -106,13 +106,16 @@ static hipError_t psum(int t, int64_t n, const void* parts, int64_t stride, void
   const int64_t per_block = vec ? 256 * 8 : 256;
   const int64_t want = (n + per_block - 1) / per_block;
   const int blocks = (int)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
+  LGS_CHECK(t >= 1 && n >= 1 && (t == 1 || stride >= n));
+  LGS_NEED(parts, (size_t)((t - 1) * stride + n) * sizeof(TI), "partials");
+  LGS_NEED(out, (size_t)n * sizeof(TO), "sum of the partials");
   if (vec)
-    hipLaunchKernelGGL((psum_vec_kernel<TI, TO>), dim3(blocks), dim3(256), 0, s, (const TI*)parts,
-                       stride, t, n, (TO*)out);
+    LGS_LAUNCH((psum_vec_kernel<TI, TO>), dim3(blocks), dim3(256), 0, s, (const TI*)parts, stride, t, n,
+               (TO*)out);
   else
-    hipLaunchKernelGGL((psum_scalar_kernel<TI, TO>), dim3(blocks), dim3(256), 0, s,
-                       (const TI*)parts, stride, t, n, (TO*)out);
-  return hipGetLastError();
+    LGS_LAUNCH((psum_scalar_kernel<TI, TO>), dim3(blocks), dim3(256), 0, s, (const TI*)parts, stride, t, n,
+               (TO*)out);
+  return LGS_LAUNCH_STATUS();
 }
 
 hipError_t partial_sum(int t, int64_t n, bool in_bf16, bool out_bf16, const void* parts,
@@ -163,16 +166,18 @@ hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64
   const int64_t want = (units + 255) / 256;
   const int bx = (int)(want < 2048 ? (want < 1 ? 1 : want) : 2048);
   const dim3 grid(bx, t);
+  LGS_CHECK(t >= 1 && t <= 65535 && chunk >= 1 && (t == 1 || stride >= chunk));
+  LGS_NEED(shards, (size_t)((t - 1) * stride + chunk) * esz, "all-gather shards");
+  LGS_NEED(out, (size_t)t * chunk * esz, "all-gather output");
   if (vec)
-    hipLaunchKernelGGL(gather_vec_kernel, grid, dim3(256), 0, s, (const char*)shards, stride * esz,
-                       units, (char*)out);
+    LGS_LAUNCH(gather_vec_kernel, grid, dim3(256), 0, s, (const char*)shards, stride * esz, units, (char*)out);
   else if (bf16)
-    hipLaunchKernelGGL((gather_scalar_kernel<uint16_t>), grid, dim3(256), 0, s,
-                       (const uint16_t*)shards, stride, chunk, (uint16_t*)out);
+    LGS_LAUNCH((gather_scalar_kernel<uint16_t>), grid, dim3(256), 0, s, (const uint16_t*)shards, stride, chunk,
+               (uint16_t*)out);
   else
-    hipLaunchKernelGGL((gather_scalar_kernel<uint32_t>), grid, dim3(256), 0, s,
-                       (const uint32_t*)shards, stride, chunk, (uint32_t*)out);
-  return hipGetLastError();
+    LGS_LAUNCH((gather_scalar_kernel<uint32_t>), grid, dim3(256), 0, s, (const uint32_t*)shards, stride, chunk,
+               (uint32_t*)out);
+  return LGS_LAUNCH_STATUS();
 }
 
 // out[m, n] = bf16(sum_s W[s][m][n]) for a split-K GEMM's fp32 partials
@@ -212,8 +217,11 @@ hipError_t splitk_sum(const float* W, int splits, int M, int N, void* out, int64
   const int64_t total = (int64_t)M * (N / 8);
   const int64_t want = (total + 255) / 256;
   const int blocks = (int)(want < 4096 ? (want < 1 ? 1 : want) : 4096);
-  hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, W, splits, M, N, (bf16*)out, ldo);
-  return hipGetLastError();
+  LGS_CHECK(splits >= 1 && M >= 1 && N % 8 == 0);
+  LGS_NEED(W, (size_t)splits * M * N * 4, "split-K partial slices");
+  LGS_NEED(out, debug::mat_bytes(M, ldo, N, 2), "split-K sum");
+  LGS_LAUNCH(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, W, splits, M, N, (bf16*)out, ldo);
+  return LGS_LAUNCH_STATUS();
 }
 
 // parts: rank r's block at parts + r*stride holds m[n], l[n], T[n] (T is not
@@ -259,9 +267,12 @@ hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, bo
                         float* loss, hipStream_t s) {
   const int64_t want = (n + 255) / 256;
   const int blocks = (int)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
-  hipLaunchKernelGGL(xent_combine_kernel, dim3(blocks), dim3(256), 0, s, parts, stride, t, n,
-                     lse_only, loss);
-  return hipGetLastError();
+  const int64_t planes = lse_only ? 2 : 3;
+  LGS_CHECK(t >= 1 && n >= 1 && stride >= planes * n);
+  LGS_NEED(parts, (size_t)((t - 1) * stride + planes * n) * 4, "CE partials of every rank");
+  LGS_NEED(loss, (size_t)n * 4, "CE merge output");
+  LGS_LAUNCH(xent_combine_kernel, dim3(blocks), dim3(256), 0, s, parts, stride, t, n, lse_only, loss);
+  return LGS_LAUNCH_STATUS();
 }
 
 }  // namespace lgs

@@ -111,9 +111,20 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
   } else {
     nslabs = (Vr + WN - 1) / WN;
   }
-  hipLaunchKernelGGL(xent_merge_kernel, dim3((M + 31) / 32), dim3(256), 0, s, sl, nslabs, M,
-                     vocab_start, m_r, l_r, t_r, argmax_r, loss);
-  return hipGetLastError();
+  // the merge reads the first nslabs slabs of every plane, all written above
+  LGS_CHECK(nslabs <= slabs_written(plan, Vr));
+  LGS_NEED(sl.m, (size_t)nslabs * M * 4, "slab maxima read by the merge");
+  LGS_NEED(sl.l, (size_t)nslabs * M * 4, "slab sums read by the merge");
+  LGS_NEED(sl.t, (size_t)nslabs * M * 4, "slab targets read by the merge");
+  if (sl.idx) LGS_NEED(sl.idx, (size_t)nslabs * M * 4, "slab argmax read by the merge");
+  LGS_NEED(m_r, (size_t)M * 4, "m_r");
+  LGS_NEED(l_r, (size_t)M * 4, "l_r");
+  LGS_NEED(t_r, (size_t)M * 4, "tgt_r");
+  if (argmax_r) LGS_NEED(argmax_r, (size_t)M * 4, "argmax_r");
+  if (loss) LGS_NEED(loss, (size_t)M * 4, "loss");
+  LGS_LAUNCH(xent_merge_kernel, dim3((M + 31) / 32), dim3(256), 0, s, sl, nslabs, M, vocab_start, m_r, l_r, t_r,
+             argmax_r, loss);
+  return LGS_LAUNCH_STATUS();
 }
 
 // ---------------------------------------------------------------------------
@@ -135,6 +146,11 @@ void* g_scratch_ptr[kMaxDevices];
 }  // namespace
 
 hipError_t xent_static_scratch(hipStream_t s, void** out) {
+  if (debug::dry_run()) {  // debug builds without a GPU: a stand-in address, never dereferenced
+    *out = (void*)((uintptr_t)1 << 46);
+    debug::allow(*out, kXentStaticScratchBytes);
+    return hipSuccess;
+  }
   int dev = -1;
   hipError_t e = hipStreamGetDevice(s, &dev);  // the device the stream's work runs on
   if (e != hipSuccess) return e;
@@ -153,6 +169,7 @@ hipError_t xent_static_scratch(hipStream_t s, void** out) {
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
+  debug::allow(*out, kXentStaticScratchBytes);
   return hipSuccess;
 }
 

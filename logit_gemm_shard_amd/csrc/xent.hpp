@@ -34,6 +34,18 @@ struct EpiXent {
   int WN;                  // wave tile width: slab = slab0 + wave column
   int col0, slab0;         // slice-local column of this launch's column 0; its first slab
 
+  // A launch of tile width bn writes slabs [slab0, slab0 + ceil(N / bn) bn / WN)
+  // of every plane (a wave column wholly past N writes -inf / 0 partials).
+  void debug_spans(int bn) const {
+    const size_t slabs = (size_t)((N + bn - 1) / bn) * bn / WN, bytes = slabs * M * 4;
+    LGS_CHECK(bn % WN == 0);
+    LGS_NEED(s.m + (int64_t)slab0 * M, bytes, "EpiXent slab maxima");
+    LGS_NEED(s.l + (int64_t)slab0 * M, bytes, "EpiXent slab sums");
+    LGS_NEED(s.t + (int64_t)slab0 * M, bytes, "EpiXent slab targets");
+    if (s.idx) LGS_NEED(s.idx + (int64_t)slab0 * M, bytes, "EpiXent slab argmax");
+    LGS_NEED(targets, (size_t)M * 4, "EpiXent targets");
+  }
+
   // Reduces the wave's logit tile straight from the accumulators.  In the
   // 32x32 MFMA output layout lane l holds, for row 32i + l%32 of the wave
   // tile, the 16 TN columns 32j + 8q + 4(l/32) + e (j < TN, q < 4, e < 4) in

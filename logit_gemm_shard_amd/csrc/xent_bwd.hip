@@ -42,6 +42,12 @@ struct EpiXentGrad {
   const float* w;  // may be null: 1 per token
   const int32_t* targets;
   int vocab_start, M, N;
+  void debug_spans(int) const {
+    LGS_NEED(G, debug::mat_bytes(M, ldg, N, 2), "EpiXentGrad G");
+    LGS_NEED(lse, (size_t)M * 4, "EpiXentGrad lse");
+    if (w) LGS_NEED(w, (size_t)M * 4, "EpiXentGrad dloss");
+    LGS_NEED(targets, (size_t)M * 4, "EpiXentGrad targets");
+  }
   __device__ __forceinline__ RowGrad load8(int m, int) const {
     if (m >= M) return RowGrad{0.f, 0.f, -1};
     return RowGrad{lse[m] * kLog2e, w ? w[m] : 1.f, targets[m] - vocab_start};

@@ -95,10 +95,14 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void xent_rows_kernel(
 hipError_t xent_rows(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
                      const int32_t* targets, float* m, float* l, float* t, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(xent_rows_kernel, dim3((M + kRowsPerBlock - 1) / kRowsPerBlock),
-                     dim3(64 * kRowsPerBlock), 0, s, (const bf16*)Z, ldz, M, Vr, vocab_start,
-                     targets, m, l, t);
-  return hipGetLastError();
+  LGS_NEED(Z, debug::mat_bytes(M, ldz, Vr, 2), "materialised logits");
+  LGS_NEED(targets, (size_t)M * 4, "targets");
+  LGS_NEED(m, (size_t)M * 4, "m");
+  LGS_NEED(l, (size_t)M * 4, "l");
+  LGS_NEED(t, (size_t)M * 4, "T");
+  LGS_LAUNCH(xent_rows_kernel, dim3((M + kRowsPerBlock - 1) / kRowsPerBlock), dim3(64 * kRowsPerBlock), 0, s,
+             (const bf16*)Z, ldz, M, Vr, vocab_start, targets, m, l, t);
+  return LGS_LAUNCH_STATUS();
 }
 
 }  // namespace lgs
