@@ -14,7 +14,9 @@
 // back-to-back MFMAs of one wave or the other.
 //
 // Block: 512 threads; block tile BM x BN, wave w owns rows (w & 3) BM/4 and
-// columns (w >> 2) BN/2 (group g = w >> 2 owns one column half).  K tiles of
+// columns (w >> 2) BN/2 (group g = w >> 2 owns one column half), or, for
+// 256x256 tiles with a K-contiguous A and an N-contiguous B, rows g BM/2 and
+// columns (w & 3) BN/4 (group g owns one row half; PPTile::kRowGroups).  K tiles of
 // 32 in a ring of S LDS stages; tile kt is read by group 0 in phase 2kt and
 // by group 1 in phase 2kt+1, and computed by each in its next phase.
 //
@@ -48,13 +50,21 @@ constexpr int kPPThreads = 64 * kPPWaves;
 
 template <int BM, int BN, bool AK, bool BK>
 struct PPTile {
-  static constexpr int WM = BM / 4, WN = BN / 2;
+  // 256x256 tiles with a K-contiguous A and an N-contiguous B: waves in a
+  // 2 x 4 grid (each group owns a row half), so the B fragments, read with
+  // the slower transposing reads, are read twice per K tile instead of four
+  // times (and A's 128-bit reads four times instead of twice).
+  static constexpr bool kRowGroups = BM == 256 && BN == 256 && AK && !BK;
+  static constexpr int WM = kRowGroups ? BM / 2 : BM / 4, WN = kRowGroups ? BN / 4 : BN / 2;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
   using LA = OpLayout<BM, AK>;
   using LB = OpLayout<BN, BK>;
   static constexpr int kStage = LA::kBytes + LB::kBytes;
-  static constexpr int kStages = kLdsMax / kStage < 5 ? kLdsMax / kStage : 5;
+  // Four stages, not the five that fit a 256x256 tile: with fewer loads in
+  // flight the memory system runs less congested, and the K loop is faster
+  // (70B shapes 0-3%; alone or with the 2 x 4 grid above, alternating A/B).
+  static constexpr int kStages = kLdsMax / kStage < 4 ? kLdsMax / kStage : 4;
   static_assert(kStages >= 3, "need at least three stages");
   static constexpr int kLdsBytes = kStages * kStage;
 };
@@ -165,7 +175,7 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
-  const int wm = wave & 3, wn = grp;
+  const int wm = T::kRowGroups ? grp : wave & 3, wn = T::kRowGroups ? wave & 3 : grp;
   const int M = p.M, N = p.N, K = p.K;
   const int m0 = tmi * P::BM, n0 = tni * P::BN;
   // B columns the tile reads: BN of them from n0, or for a paired epilogue
