@@ -223,11 +223,13 @@ int tp_swiglu_bwd(int b, int s, int h, int ffn, int t, int rank, int dtype, cons
  * orders them, e.g. with events).  tp_mlp_bwd runs dx and dw as one launch,
  * which is faster when nothing overlaps them.  Results: dgelu and dx give
  * tp_mlp_bwd's bits.  dw gives tp_mlp_bwd's bits where tp_mlp_bwd runs dB_i
- * and dA_i unsplit; for bf16 shapes with many tokens against small h and f
- * (e.g. M = 2200, h = 1064, f = 1048) tp_mlp_bwd splits their sums over token
- * ranges inside its launch (its workspace then exceeds the two [M, f]
- * buffers), and dw, which never splits, equals it up to the fp32 summation
- * order.
+ * and dA_i unsplit.  For some bf16 shapes tp_mlp_bwd splits their sums over
+ * token ranges inside its launch (its workspace then exceeds the two [M, f]
+ * buffers): both of them where the tokens are many against small h and f
+ * (e.g. M = 2200, h = 1064, f = 1048), or only the last dA_i tiles where its
+ * launch would end in a partly filled round of long tiles (e.g. M = 4096,
+ * h = 8192, f = 3584).  dw, which never splits, then equals it up to the
+ * fp32 summation order of the split tiles.
  */
 int tp_mlp_bwd_dgelu(int b, int s, int h, int ffn, int t, int rank, int dtype, int act,
                      const void* B_i, int64_t ldb, const void* U_i, int64_t ldu, const void* dZ,

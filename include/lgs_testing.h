@@ -43,9 +43,12 @@ int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int N, int K
  * with hidden size h and f = ffn/t columns: *parts = 1 when tp_mlp_bwd runs
  * dB_i and dA_i unsplit (then tp_mlp_bwd_dw, which never splits, gives the
  * same bits), else the number of token ranges it splits them into, with
- * *kchunk tokens per range.  Returns 0, or -1 for non-positive sizes.
+ * *kchunk tokens per range.  *tail = 0 when every dB_i and dA_i tile is
+ * split (or none), else the number of 256x256 dA_i tiles split, the last
+ * ones launched; dB_i is then unsplit.  Returns 0, or -1 for non-positive
+ * sizes.
  */
-int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk);
+int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk, int* tail);
 
 /*
  * Streaming form of the cross-entropy slice partials, for measuring the CE

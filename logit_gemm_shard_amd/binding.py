@@ -71,7 +71,7 @@ SIGNATURES = [
     ("lgs_test_num_tiles", _i, []),
     ("lgs_test_tile_shape", _i, [_i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     ("lgs_test_pick_tile", _i, [_i, _i]),
-    ("lgs_test_mlp_bwd_plan", _i, [_i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    ("lgs_test_mlp_bwd_plan", _i, [_i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     ("lgs_test_gemm_bf16", _i, [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
     ("lgs_test_xent_rows_bf16", _i, [_i, _i, _i, _p, _i64, _p, _p, _p, _p, _p]),
     ("lgs_test_debug_build", _i, []),
@@ -442,12 +442,14 @@ def pick_tile(M, N):
 
 
 def mlp_bwd_plan(M, h, f):
-    """(parts, tokens per part) of the bf16 backward's weight gradients:
-    (1, M) when tp_mlp_bwd does not split them over the tokens."""
-    parts, kchunk = ctypes.c_int(), ctypes.c_int()
-    if lib().lgs_test_mlp_bwd_plan(M, h, f, ctypes.byref(parts), ctypes.byref(kchunk)) != 0:
+    """(parts, tokens per part, tail) of the bf16 backward's weight
+    gradients: (1, M, 0) when tp_mlp_bwd does not split them over the
+    tokens; tail = 0 when it splits every dB and dA tile, else the number of
+    (last) dA tiles it splits, dB then being unsplit."""
+    parts, kchunk, tail = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    if lib().lgs_test_mlp_bwd_plan(M, h, f, ctypes.byref(parts), ctypes.byref(kchunk), ctypes.byref(tail)) != 0:
         raise ValueError("sizes must be positive")
-    return parts.value, kchunk.value
+    return parts.value, kchunk.value, tail.value
 
 
 def gemm_bf16(A, B, C, a_kmajor=True, b_kmajor=False, tile=-1, stream=None):

@@ -716,11 +716,12 @@ LGS_API int lgs_test_pick_tile(int M, int N) {
   return lgs::picked_tile(M, N);
 }
 
-LGS_API int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk) {
+LGS_API int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk, int* tail) {
   if (M <= 0 || h <= 0 || f <= 0) return -1;
   const lgs::BwdSplit k = lgs::mlp_bwd_wsplit(M, h, f);
   if (parts) *parts = k.parts;
   if (kchunk) *kchunk = k.parts > 1 ? k.kchunk : M;
+  if (tail) *tail = k.parts > 1 ? k.tail : 0;
   return 0;
 }
 

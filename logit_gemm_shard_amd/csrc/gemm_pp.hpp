@@ -466,6 +466,38 @@ void gemm_pp_group3_ksplit_kernel(P0 p0, P1 p1, P2 p2, KSplit k) {
   }
 }
 
+// gemm_pp_group3_kernel with only the last `tail` tiles of p1 (in its block
+// order) split over K into k.parts parts, launched after p2's tiles: the
+// launch's unsplit blocks fill whole rounds of the compute units and the
+// split tiles' shorter parts make the last round.  Blocks: p0's tiles,
+// p1's first tiles, p2's tiles, then the tail's parts (part-major).  Slot
+// and counter j belong to tail tile j.
+template <class P0, class P1, class P2>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_group3_tail_kernel(P0 p0, P1 p1, P2 p2, KSplit k, int tail) {
+  constexpr int kL0 = P0::T::kLdsBytes, kL1 = P1::T::kLdsBytes, kL2 = P2::T::kLdsBytes;
+  constexpr int kL = kL0 > kL1 ? (kL0 > kL2 ? kL0 : kL2) : (kL1 > kL2 ? kL1 : kL2);
+  __shared__ __attribute__((aligned(1024))) char smem[kL];
+  int pid = blockIdx.x, tmi, tni;
+  const int t0 = p0.tiles(), t1 = p1.tiles(), head = t1 - tail, t2 = p2.tiles();
+  if (pid < t0) {
+    tile_of_block(pid, t0, p0.tiles_m(), p0.tiles_n(), tmi, tni);
+    gemm_tile_pp(p0, smem, tmi, tni);
+  } else if ((pid -= t0) < head) {
+    tile_of_block(pid, t1, p1.tiles_m(), p1.tiles_n(), tmi, tni);
+    gemm_tile_pp(p1, smem, tmi, tni);
+  } else if ((pid -= head) < t2) {
+    tile_of_block(pid, t2, p2.tiles_m(), p2.tiles_n(), tmi, tni);
+    gemm_tile_pp(p2, smem, tmi, tni);
+  } else {
+    pid -= t2;
+    const int s = pid / tail, j = pid - s * tail;
+    tile_of_block(head + j, t1, p1.tiles_m(), p1.tiles_n(), tmi, tni);
+    const KPartFix fix{k.part + (int64_t)j * k.parts * P1::BM * P1::BN, k.count + j, s, k.parts};
+    gemm_tile_pp(k_range(p1, s * k.kchunk, k.kchunk), smem, tmi, tni, fix);
+  }
+}
+
 static __global__ __launch_bounds__(256) void zero_i32_kernel(int* p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -486,6 +518,23 @@ inline hipError_t launch_gemm_pp_group3_ksplit(const P0& p0, const P1& p1, const
   LGS_LAUNCH(zero_i32_kernel, dim3((counters + 255) / 256), dim3(256), 0, stream, k.count, counters);
   LGS_LAUNCH((gemm_pp_group3_ksplit_kernel<P0, P1, P2>), dim3((p0.tiles() + p1.tiles()) * k.parts + p2.tiles()),
              dim3(kPPThreads), 0, stream, p0, p1, p2, k);
+  return LGS_LAUNCH_STATUS();
+}
+
+template <class P0, class P1, class P2>
+inline hipError_t launch_gemm_pp_group3_tail(const P0& p0, const P1& p1, const P2& p2, const KSplit& k,
+                                             int tail, hipStream_t stream) {
+  debug_problem(p0);
+  debug_problem(p1);
+  debug_problem(p2);
+  LGS_CHECK(tail >= 1 && tail <= p1.tiles() && k.parts >= 2 && k.kchunk % kBK == 0 &&
+            (int64_t)(k.parts - 1) * k.kchunk < p1.K && (int64_t)k.parts * k.kchunk >= p1.K);
+  LGS_NEED(k.part, (size_t)tail * k.parts * P1::BM * P1::BN * 4, "K-split partial slots");
+  LGS_NEED(k.count, (size_t)tail * 4, "K-split counters");
+  LGS_LAUNCH(zero_i32_kernel, dim3((tail + 255) / 256), dim3(256), 0, stream, k.count, tail);
+  LGS_LAUNCH((gemm_pp_group3_tail_kernel<P0, P1, P2>),
+             dim3(p0.tiles() + p1.tiles() - tail + p2.tiles() + tail * k.parts), dim3(kPPThreads), 0, stream, p0,
+             p1, p2, k, tail);
   return LGS_LAUNCH_STATUS();
 }
 

@@ -25,10 +25,12 @@ hipError_t mlp_bwd(bool bf16, int M, int h, int f, int act, const void* X, int64
                    int64_t ldda, void* dB, int64_t lddb, void* Yws, void* dUws, void* splitws,
                    hipStream_t s);
 
-// How the bf16 backward's grouped launch splits dB and dA over K: parts (1 =
-// not split), the K rows per part, and the dB plus dA tile count.
+// How the bf16 backward's grouped launch splits dB and dA over K (the
+// tokens): parts (1 = not split) of kchunk K rows each, over every dB and dA
+// tile (tail == 0, `tiles` = their count) or over the last `tail` dA tiles
+// only (tiles == tail).
 struct BwdSplit {
-  int parts, kchunk, tiles;
+  int parts, kchunk, tiles, tail;
 };
 BwdSplit mlp_bwd_wsplit(int M, int h, int f);
 size_t mlp_bwd_split_bytes(int M, int h, int f);  // 0 when not split

@@ -73,16 +73,47 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // No split can reach 30% when the longest tile is short against the whole
 // launch: list dispatch finishes within W/256 + L (W the launch's K tiles
 // over all blocks, L the longest block's), while any split needs at least
-// W/256, so if 0.3 W/256 >= 0.7 L the simulation is skipped (both 70B shapes).
+// W/256, so if 0.3 W/256 >= 0.7 L the full split is not simulated (both 70B
+// shapes).  Such launches can still end in a partly filled round of long
+// tiles (70B: 448 + 448 + 512 blocks, five and a half rounds).  There the
+// tail split halves only the last dA tiles (mlp_bwd_tail_split).
 // Plans are cached per shape: the workspace query, the entry point's check
 // and the launch each ask.
+namespace {
+
+// Only the last `tail` dA tiles split in two over the tokens, their parts
+// launched after dX: the unsplit blocks make whole rounds and the parts,
+// half as long, the last one; the slot traffic meets only that round.  The
+// simulation charges every block the fixed cost of a tile (prologue, LDS
+// fill and stores: about 12 K tiles' time) and each part four more K tiles
+// for its slot, and the plan is taken for a predicted gain of 4% or more.
+BwdSplit mlp_bwd_tail_split(int M, int tw, int tx, int nkw, int nkx) {
+  constexpr int kFixed = 12, kSlot = 4;
+  BwdSplit best{1, 0, 0, 0};
+  if (M < 512) return best;
+  const int kchunk = cdiv(cdiv(M, 2), 32) * 32, u = kchunk / 32, last = nkw - u;
+  const int unsplit = dispatch_makespan({{nkw + kFixed, 2 * tw}, {nkx + kFixed, tx}});
+  int best_cost = unsplit * 96 / 100;
+  for (int tail = 8; tail <= tw; tail += 8) {
+    const int cost = dispatch_makespan({{nkw + kFixed, 2 * tw - tail},
+                                        {nkx + kFixed, tx},
+                                        {u + kFixed + kSlot, tail},
+                                        {last + kFixed + kSlot, tail}});
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = BwdSplit{2, kchunk, tail, tail};
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
 BwdSplit mlp_bwd_wsplit(int M, int h, int f) {
-  BwdSplit no{1, 0, 0};
+  BwdSplit no{1, 0, 0, 0};
   if (M < 256 || h < 256 || f < 256) return no;
   const int tw = cdiv(f, 256) * cdiv(h, 256), tx = cdiv(M, 256) * cdiv(h, 256);
   const int nkw = cdiv(M, 32), nkx = cdiv(f, 32);
-  const double work = (2.0 * tw * nkw + (double)tx * nkx) / 256.0;
-  if (0.3 * work >= 0.7 * (nkw > nkx ? nkw : nkx)) return no;
 
   static std::mutex mu;
   static std::map<std::tuple<int, int, int>, BwdSplit> cache;
@@ -92,22 +123,26 @@ BwdSplit mlp_bwd_wsplit(int M, int h, int f) {
     const auto it = cache.find(key);
     if (it != cache.end()) return it->second;
   }
-  const int unsplit = dispatch_makespan({{nkw, 2 * tw}, {nkx, tx}});
-  int best_cost = unsplit;
   BwdSplit best = no;
-  for (int parts = 2; parts <= 4; ++parts) {
-    const int kchunk = cdiv(cdiv(M, parts), 32) * 32, n = cdiv(M, kchunk);
-    if (n < 2 || n == best.parts) continue;
-    const int u = kchunk / 32, last = nkw - (n - 1) * u;
-    // launch order: dB's parts (part-major), dA's parts, dX
-    const std::vector<std::pair<int, int>> items = {{u + 2, tw * (n - 1)}, {last + 2, tw},
-                                                    {u + 2, tw * (n - 1)}, {last + 2, tw}, {nkx, tx}};
-    const int cost = dispatch_makespan(items) + 2 * n;
-    if (cost * 10 < unsplit * 7 && cost * 20 < best_cost * 19) {
-      best_cost = cost;
-      best = BwdSplit{n, kchunk, 2 * tw};
+  const double work = (2.0 * tw * nkw + (double)tx * nkx) / 256.0;
+  if (0.3 * work < 0.7 * (nkw > nkx ? nkw : nkx)) {
+    const int unsplit = dispatch_makespan({{nkw, 2 * tw}, {nkx, tx}});
+    int best_cost = unsplit;
+    for (int parts = 2; parts <= 4; ++parts) {
+      const int kchunk = cdiv(cdiv(M, parts), 32) * 32, n = cdiv(M, kchunk);
+      if (n < 2 || n == best.parts) continue;
+      const int u = kchunk / 32, last = nkw - (n - 1) * u;
+      // launch order: dB's parts (part-major), dA's parts, dX
+      const std::vector<std::pair<int, int>> items = {{u + 2, tw * (n - 1)}, {last + 2, tw},
+                                                      {u + 2, tw * (n - 1)}, {last + 2, tw}, {nkx, tx}};
+      const int cost = dispatch_makespan(items) + 2 * n;
+      if (cost * 10 < unsplit * 7 && cost * 20 < best_cost * 19) {
+        best_cost = cost;
+        best = BwdSplit{n, kchunk, 2 * tw, 0};
+      }
     }
   }
+  if (best.parts < 2) best = mlp_bwd_tail_split(M, tw, tx, nkw, nkx);
   std::lock_guard<std::mutex> lock(mu);
   if (cache.size() >= 256) cache.clear();
   cache[key] = best;
@@ -168,6 +203,7 @@ hipError_t mlp_bwd(bool is_bf16, int M, int h, int f, int act, const void* X, in
       if (k.parts > 1 && splitws) {
         float* part = (float*)splitws;
         int* count = (int*)((char*)splitws + (size_t)k.tiles * k.parts * 256 * 256 * sizeof(float));
+        if (k.tail) return launch_gemm_pp_group3_tail(pb, pa, px, KSplit{part, count, k.parts, k.kchunk}, k.tail, s);
         return launch_gemm_pp_group3_ksplit(pb, pa, px, KSplit{part, count, k.parts, k.kchunk}, s);
       }
       return launch_gemm_pp_group3(pb, pa, px, s);

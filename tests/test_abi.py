@@ -122,13 +122,16 @@ def test_mlp_bwd_validation(L):
 def test_mlp_bwd_workspace_holds_the_weight_gradient_split(L):
     """Y_i and dU_i, plus, for bf16 shapes whose dB / dA tiles are few and
     long (many tokens, small h and f), the K-split partial sums (fp32, one
-    256x256 slot per tile and part) and one counter per tile."""
+    256x256 slot per tile and part) and one counter per tile; the same for
+    the split tiles alone where only the last dA tiles are split (the 70B
+    shape: 448 + 448 + 512 blocks, the last 128 dA tiles in 2 parts)."""
     def plain(b, s, ffn, t, el):
         return 2 * (((b * s * (ffn // t) * el) + 255) // 256 * 256)
     L.lgs_mlp_bwd_workspace_bytes.restype = ctypes.c_size_t
-    # the benchmark shapes: not split
+    # the 8.3B shape: not split
     assert L.lgs_mlp_bwd_workspace_bytes(8, 1024, 3072, 12288, 8, 1) == plain(8, 1024, 12288, 8, 2)
-    assert L.lgs_mlp_bwd_workspace_bytes(1, 4096, 8192, 28672, 8, 1) == plain(1, 4096, 28672, 8, 2)
+    tail = 128 * 2 * 256 * 256 * 4 + 512
+    assert L.lgs_mlp_bwd_workspace_bytes(1, 4096, 8192, 28672, 8, 1) == plain(1, 4096, 28672, 8, 2) + tail
     # M = 8264 tokens, h = 776, f = 520: 3 x 4 tiles each for dB and dA, 4 parts
     tiles, parts = 2 * 3 * 4, 4
     split = tiles * parts * 256 * 256 * 4 + 256

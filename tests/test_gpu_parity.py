@@ -146,14 +146,18 @@ def test_mlp_fwd_bwd_ragged(shape, dtype):
 
 
 @pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(3, 200, 136, 528, 2), (2, 1100, 1064, 2 * 1048, 2), (1, 1024, 3072, 8 * 1536, 8)],
+@pytest.mark.parametrize("shape", [(3, 200, 136, 528, 2), (2, 1100, 1064, 2 * 1048, 2), (1, 1024, 3072, 8 * 1536, 8),
+                                   (2, 300, 3584, 4 * 2048, 4)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_mlp_bwd_in_three_parts(shape, dtype):
     """dgelu, then dx and dw on two streams running concurrently, against the
-    oracle and against tp_mlp_bwd: the same bits, except dA and dB where
-    tp_mlp_bwd splits them over the tokens inside its launch (bf16 at
-    M = 2200, h = 1064, f = 1048: 2 parts), which changes only the fp32
-    summation order (the plan comes from the library's testing hook)."""
+    oracle and against tp_mlp_bwd: the same bits, except where tp_mlp_bwd
+    splits a weight gradient over the tokens inside its launch, which changes
+    only the fp32 summation order (the plan comes from the library's testing
+    hook).  bf16 at M = 2200, h = 1064, f = 1048 splits every dA and dB tile
+    in 2 parts; at M = 600, h = 3584, f = 2048 only the last dA tiles (the
+    second part ragged: 280 tokens), dB staying unsplit.  A split launch
+    repeats its bits."""
     b, s, h, ffn, t = shape
     M, f = b * s, ffn // t
     d = dev()
@@ -187,14 +191,20 @@ def test_mlp_bwd_in_three_parts(shape, dtype):
     assert_close("dX (three parts)", dX1, g["dX"], dtype)
     assert_close("dA (three parts)", dA1, g["dA"], dtype)
     assert_close("dB (three parts)", dB1, g["dB"], dtype)
-    split = dtype == BF16 and lgs.mlp_bwd_plan(M, h, f)[0] > 1
-    assert split == (shape[0] * shape[1] == 2200 and dtype == BF16)
+    parts, _, tail = lgs.mlp_bwd_plan(M, h, f) if dtype == BF16 else (1, M, 0)
+    split_a, split_b = parts > 1, parts > 1 and tail == 0
+    assert (split_a, split_b) == {1064: (dtype == BF16,) * 2, 3584: (dtype == BF16, False)}.get(h, (False, False))
     assert torch.equal(dX1, dX2), "dX: three parts vs one launch"
-    for name, x, y in (("dA", dA1, dA2), ("dB", dB1, dB2)):
+    for name, x, y, split in (("dA", dA1, dA2, split_a), ("dB", dB1, dB2, split_b)):
         if split:
             assert_close(f"{name}: three parts vs one split launch", x, f64(y), dtype)
         else:
             assert torch.equal(x, y), f"{name}: three parts vs one launch"
+    if split_a:
+        dX3, dA3, dB3 = torch.empty_like(dX2), torch.empty_like(dA2), torch.empty_like(dB2)
+        lgs.tp_mlp_bwd(b, s, h, ffn, t, 0, Xd, Ad, Bd, Ud, dZd, dX3, dA3, dB3)
+        sync()
+        assert torch.equal(dA3, dA2) and torch.equal(dB3, dB2), "a split launch repeats its bits"
 
 
 def test_mlp_bwd_weight_grads_split_inside_the_launch():
