@@ -187,7 +187,7 @@ def counter_summary(d):
         step = _per_kernel(csv_of(f"pmc_{c}"), c)
         copy = _per_kernel(csv_of(f"pmc_copy_{c}"), c)
         dy = [v for n, v in step.items() if "EpiGeluBwd" in n]
-        grp = [v for n, v in step.items() if "gemm_pp_group3_kernel" in n]
+        grp = [v for n, v in step.items() if "gemm_pp_group3" in n]
         cp = [v for n, v in copy.items() if "neg" in n]
         if len(dy) != 1 or len(grp) != 1 or len(cp) != 1:
             raise SystemExit(f"{c}: expected one dY+GeLU' kernel, one grouped kernel and one copy kernel, "
@@ -217,9 +217,13 @@ def counter_summary(d):
 #
 # Per call (median over the dispatches of each kernel):
 #   dY + GeLU' GEMM (writes dU_i and the recomputed Y_i): FETCH_SIZE {med['FETCH_SIZE'][0]:.0f} KiB, WRITE_SIZE {med['WRITE_SIZE'][0]:.0f} KiB -> {nbytes(0) / 1e6:.1f} MB
-#   grouped dB / dA / dX launch:                         FETCH_SIZE {med['FETCH_SIZE'][1]:.0f} KiB, WRITE_SIZE {med['WRITE_SIZE'][1]:.0f} KiB -> {nbytes(1) / 1e6:.1f} MB
+#   grouped dB / dA / dX launch (the last 128 dA tiles in two parts over the
+#   tokens, with 64 MB of fp32 partial slots written and read back):
+#                                                        FETCH_SIZE {med['FETCH_SIZE'][1]:.0f} KiB, WRITE_SIZE {med['WRITE_SIZE'][1]:.0f} KiB -> {nbytes(1) / 1e6:.1f} MB
 #   algorithmic bytes of the call (X, A_i, B_i, U_i, dZ read once; dX_i, dA_i,
 #   dB_i written once; Y_i and dU_i written and read once): {alg / 1e6:.1f} MB
+#   (the third launch of the call, which clears the 128 split tiles' counters,
+#   writes 512 bytes)
 #
 # The counters count every request that leaves the L2s for the memory fabric;
 # they cannot separate HBM reads from hits in the 256 MB Infinity Cache in
@@ -509,6 +513,7 @@ def per_config(torch, lgs, reps):
     rep = _timed_report(torch, xfwd, xent_flops(M, h, Vr), reps, len(sets))
     rep["tokens_per_s"] = round(M / (rep["ms"] * 1e-3), 0)
     out["xent_8p3b"] = rep
+    progress("xent_8p3b timed")
     lse = (torch.randn(M, device=dev).abs_() + 12.0)
     dl = torch.full((M,), 1.0 / M, dtype=torch.float32, device=dev)
     dH0 = torch.empty(M, h, dtype=bf, device=dev)
@@ -522,6 +527,7 @@ def per_config(torch, lgs, reps):
     rep["tokens_per_s"] = round(M / (rep["ms"] * 1e-3), 0)
     rep["note"] += "; dloss = 1/M: the recomputed logit GEMM with its gradient epilogue, then dH_0 and dE_0"
     out["xent_8p3b_bwd"] = rep
+    progress("xent_8p3b_bwd timed")
     del sets, stats, ws_x, lse, dl, dH0, dE0, ws_xb
 
     # SwiGLU block (the gated MLP of the same 70B model): forward = the paired
@@ -550,6 +556,7 @@ def per_config(torch, lgs, reps):
         X, Wgu, Wd, dZ = sets[i % len(sets)]
         lgs.tp_swiglu_bwd(wb.b, wb.s, wb.h, wb.ffn, wb.t, 0, X, Wgu, Wd, GU, dZ, dX, dWgu, dWd, workspace=ws)
     out["swiglu_70b_bwd"] = _timed_report(torch, sbwd, 12 * w.M * w.h * f, reps, len(sets))
+    progress("swiglu_70b_bwd timed")
     del sets, GU, Y, Z, dX, dWgu, dWd, ws
 
     # attention projections of one rank (8 query heads, 1 KV head of 128):
@@ -585,6 +592,7 @@ def per_config(torch, lgs, reps):
     fl = 2 * w.M * w.h * (nqkv + q)
     out["attn_70b_fwd"] = _timed_report(torch, afwd, fl, reps, len(sets))
     out["attn_70b_bwd"] = _timed_report(torch, abwd, 2 * fl, reps, len(sets))
+    progress("attn_70b_bwd timed")
     del sets, QKV, Z, dX, dW, dA, dWo, ws_qkv, ws_ob
 
     # the exchanges' one-device stand-ins (pure HBM streams): the sum of 8
@@ -640,6 +648,12 @@ def ce_reduction_stream(torch, lgs, xw, reps=30):
                       f"materialised bf16 logits [{M}, {Vr}]",
             "us": round(ms * 1e3, 2), "bytes": nbytes, "achieved_GBs": round(gbs, 1),
             "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def progress(msg):
+    """One line on stderr as each part of the run finishes (the JSON line on
+    stdout stays the only output there)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def _timed_report(torch, fn, flops, reps, nsets, warmup=10):
@@ -779,6 +793,7 @@ def main():
     for _ in range(max(args.warmup, len(sets))):
         one_step()
     torch.cuda.synchronize()
+    progress("inputs resident, warm-up steps done")
 
     mf = mlp_flops(M, h, f)
     fl_x = xent_flops(Mc, hc, Vr)
@@ -788,6 +803,7 @@ def main():
     configs = {} if args.no_per_config else per_config(torch, lgs, reps=50)
     stream_ce = None if args.no_per_config else ce_reduction_stream(torch, lgs, xw)
     gpu_clock = None if args.no_clock else sample_gpu_clock(torch, one_step)
+    progress("per-configuration timings, CE stream and clock done")
 
     # Timed region: K whole steps.  Only the backward entry point is bracketed
     # by HIP events here (its roofline is measured live); events between every
@@ -802,6 +818,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
+    progress(f"{args.steps} timed steps: {ms:.3f} ms per step")
     bwd_s = sum(e[2].elapsed_time(e[3]) for e in bw_ev) / args.steps * 1e-3
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
@@ -854,8 +871,9 @@ def main():
         "sum_partials_gbs": round(sum_bytes / (per["sum_z"] * 1e-3) / 1e9, 1),
         "entry_point_ms": {n: round(v, 4) for n, v in per.items()},
         "roofline": {
-            "kernel": "tp_mlp_bwd at the 70B shape: the dY+GeLU' GEMM and the grouped dB/dA/dX GEMM "
-                      "(two launches, 962.1 GFLOP per call), timed with HIP events around the entry point",
+            "kernel": "tp_mlp_bwd at the 70B shape: the dY+GeLU' GEMM, a 128-counter clear and the grouped "
+                      "dB/dA/dX GEMM with its last 128 dA tiles split in two over the tokens (three launches, "
+                      "962.1 GFLOP per call), timed with HIP events around the entry point",
             "bound": "mfma",
             "achieved": round(bwd_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -876,7 +894,9 @@ def main():
                 "y": y.numpy().astype("int64"), "Vr": Vr, "X2": X2.double().numpy(),
                 "A2_0": A2[:, :w2.f_i].double().numpy(), "B2_0": B2[:w2.f_i].double().numpy()}
         del X2, A2, B2
+        progress("CPU oracle baseline starts")
         out["cpu_baseline"] = cpu_baseline(host)
+        progress("CPU oracle baseline done")
     print(json.dumps(out), flush=True)
 
 
