@@ -78,56 +78,66 @@ __device__ __forceinline__ void static_for(F&& f) {
 // inside the K loop an operand only moves its buffer resource forward by one
 // K tile (scalar arithmetic), and every fragment read is one per-lane
 // register plus a compile-time offset.
-template <int R, bool KMAJ>
+template <int R, bool KMAJ, int KT = kBK>
 struct OpLayout;
 
-template <int R>
-struct OpLayout<R, true> {
+// K-contiguous operand, KT (32 or 64) k values per stage: tile row r's 2 KT
+// bytes form one LDS row of KT / 8 16-byte chunks.  A chunk's slot in its row
+// is swizzled by the row so that the 16 rows a fragment read touches per
+// 16-lane group land in distinct 16-byte slots of 256 bytes (no bank
+// conflict): with 64-byte rows, rows in groups of four ((r >> 2) & 3); with
+// 128-byte rows, rows in pairs ((r >> 1) & 7).  A 1 KB load fills 1024 / (2 KT)
+// whole rows, each group of KT / 8 lanes reading one row's 2 KT contiguous
+// bytes: 64-wide stages read whole 128-byte lines.
+template <int R, int KT>
+struct OpLayout<R, true, KT> {
   static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
-  static constexpr int kBytes = R * 64;
-  static constexpr int kInstr = R / 16;  // 1 KB loads per stage
-  static constexpr uint32_t kColBytes = 64;  // LDS bytes per tile row
-  // element offset of a k step within the operand
-  __device__ __forceinline__ static int64_t step_elems(int64_t) { return kBK; }
+  static_assert(KT == 32 || KT == 64, "stages of 32 or 64 k");
+  static constexpr int kRowBytes = 2 * KT;
+  static constexpr int kChunks = KT / 8;  // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  static constexpr int kBytes = R * kRowBytes;
+  static constexpr int kInstr = kBytes / 1024;  // 1 KB loads per stage
+  static constexpr uint32_t kColBytes = kRowBytes;  // LDS bytes per tile row
+  __device__ __forceinline__ static int swzk(int row) { return KT == 32 ? (row >> 2) & 3 : (row >> 1) & 7; }
   // byte offset (from the tile's first row, k0 = 0) that lane `lane` of load
   // n reads; out of range past the operand's last row
   __device__ __forceinline__ static uint32_t src_off(int n, int lane, int64_t ld, int rows_left) {
-    const int row = 16 * n + (lane >> 2);
+    const int row = kRowsPerLoad * n + lane / kChunks;
     return row < rows_left ? (uint32_t)(row * ld + kcol(n, lane)) * 2u : kOutOfRange;
   }
-  // k (within the K tile) of the 8 elements that lane reads in load n
+  // k (within the stage) of the 8 elements that lane reads in load n
   __device__ __forceinline__ static int kcol(int n, int lane) {
-    return ((lane & 3) ^ swz(16 * n + (lane >> 2))) * 8;
+    return ((lane % kChunks) ^ swzk(kRowsPerLoad * n + lane / kChunks)) * 8;
   }
-  // Fragment of rows row0 + lane%32 (row0 a multiple of 32), k = 16 s +
-  // 8 (lane/32) .. +7: the swizzle only depends on lane%32, so the address is
-  // lane_off(s) + 64 row0.
-  __device__ __forceinline__ static uint32_t lane_off(int s, int lane) {
+  // Fragment of rows row0 + lane%32 (row0 a multiple of 32), k = 16 q +
+  // 8 (lane/32) .. +7 of the stage: the swizzle only depends on lane%32, so
+  // the address is lane_off(q) + kRowBytes row0.
+  __device__ __forceinline__ static uint32_t lane_off(int q, int lane) {
     const int r = lane & 31;
-    return (uint32_t)(r * 64 + (((2 * s) ^ (lane >> 5) ^ swz(r)) << 4));
+    return (uint32_t)(r * kRowBytes + (((2 * q) ^ (lane >> 5) ^ swzk(r)) << 4));
   }
   template <int kRow0>
-  __device__ __forceinline__ static bf16x8 frag(const char* p) {  // p = base + wave part + lane_off(s)
-    return *reinterpret_cast<const bf16x8*>(p + kRow0 * 64);
+  __device__ __forceinline__ static bf16x8 frag(const char* p) {  // p = base + wave part + lane_off(q)
+    return *reinterpret_cast<const bf16x8*>(p + kRow0 * kRowBytes);
   }
 };
 
-template <int R>
-struct OpLayout<R, false> {
+template <int R, int KT>
+struct OpLayout<R, false, KT> {
   // Layout in LDS: k-rows in groups of four; within a group the 64-byte
   // blocks (32 columns) of the four rows alternate: columns 32 b .. 32 b + 31
   // of k-row 4g + r sit at byte 8R g + 256 b + 64 r.  A transposing fragment
   // read takes four consecutive k-rows of 32 columns per half-wave, which
   // this puts in 256 consecutive bytes (all 64 banks, no conflict) without
-  // padding, so a stage holds exactly the tile's 64 R bytes.  Each group of
+  // padding, so a stage holds exactly the tile's 2 KT R bytes.  Each group of
   // four lanes of a load still reads 64 contiguous bytes of one row.
   static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
   static constexpr int kGroupBytes = 8 * R;     // four k-rows
   static constexpr int kGroupChunks = R / 2;    // 16-B chunks per group
-  static constexpr int kBytes = kBK * 2 * R;
+  static constexpr int kBytes = KT * 2 * R;
   static constexpr int kInstr = kBytes / 1024;  // 1 KB loads per stage
   static constexpr uint32_t kColBytes = 8;      // LDS bytes per column, for column offsets that are multiples of 8
-  __device__ __forceinline__ static int64_t step_elems(int64_t ld) { return kBK * ld; }
   // k-row and first column of the chunk that lane `lane` of load n fills
   __device__ __forceinline__ static void chunk_of(int n, int lane, int& krow, int& col) {
     const int p = n * 64 + lane;

@@ -1,5 +1,5 @@
-// 8-wave "ping-pong" variant of the bf16 GEMM core (same LDS layouts, loads
-// and epilogues as gemm_bf16.hpp).
+// 8-wave "ping-pong" variant of the bf16 GEMM core (the LDS layouts of
+// gemm_bf16.hpp with 64-wide stages; the same epilogues).
 //
 // Why: on gfx950 the data an LDS read returns to a wave costs that wave's
 // own MFMA issue about 25 cycles per KB, while reads returning to ANOTHER
@@ -8,23 +8,18 @@
 // tile) therefore adds ~40% to its 1024 MFMA cycles.  Here each SIMD runs two
 // waves, one from each of two groups (waves w and w+4 share a SIMD), and the
 // groups alternate between phases, separated by block barriers: while one
-// group multiplies the K tile whose fragments it holds in registers, the
-// other reads its fragments of that tile from LDS and issues the
-// direct-to-LDS loads of a later tile.  The matrix cores of a SIMD then see
-// back-to-back MFMAs of one wave or the other.
+// group multiplies the K half whose fragments it holds in registers, the
+// other reads its fragments of that half from LDS.  The matrix cores of a
+// SIMD then see back-to-back MFMAs of one wave or the other.
 //
 // Block: 512 threads; block tile BM x BN, wave w owns rows (w & 3) BM/4 and
 // columns (w >> 2) BN/2 (group g = w >> 2 owns one column half), or, for
 // 256x256 tiles with a K-contiguous A and an N-contiguous B, rows g BM/2 and
-// columns (w & 3) BN/4 (group g owns one row half; PPTile::kRowGroups).  K tiles of
-// 32 in a ring of S LDS stages; tile kt is read by group 0 in phase 2kt and
-// by group 1 in phase 2kt+1, and computed by each in its next phase.
-//
-// Phase bookkeeping: in phase 2kt group 0 reads tile kt and issues its loads
-// of tile kt+S-1 (into the stage of tile kt-1, which group 1 finished
-// reading in phase 2kt-1); group 1 does the same one phase later.  Every wave
-// ends every phase by waiting until at most S-2 of its tiles' loads are in
-// flight, which covers every tile read in the next phase.
+// columns (w & 3) BN/4 (group g owns one row half; PPTile::kRowGroups).
+// The LDS ring holds two stages of 64 k; each stage is two 32-wide halves,
+// and half kt is read by group 0 in phase 2kt and by group 1 in phase 2kt+1,
+// and computed by each in its next phase.  The stage bookkeeping is at the
+// K loop.
 #pragma once
 
 #include "gemm_bf16.hpp"
@@ -47,7 +42,6 @@ __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 constexpr int kPPThreads = 64 * kPPWaves;
-
 template <int BM, int BN, bool AK, bool BK>
 struct PPTile {
   // 256x256 tiles with a K-contiguous A and an N-contiguous B: waves in a
@@ -58,16 +52,91 @@ struct PPTile {
   static constexpr int WM = kRowGroups ? BM / 2 : BM / 4, WN = kRowGroups ? BN / 4 : BN / 2;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  using LA = OpLayout<BM, AK>;
-  using LB = OpLayout<BN, BK>;
-  static constexpr int kStage = LA::kBytes + LB::kBytes;
-  // Four stages, not the five that fit a 256x256 tile: with fewer loads in
-  // flight the memory system runs less congested, and the K loop is faster
-  // (70B shapes 0-3%; alone or with the 2 x 4 grid above, alternating A/B).
-  static constexpr int kStages = kLdsMax / kStage < 4 ? kLdsMax / kStage : 4;
-  static_assert(kStages >= 3, "need at least three stages");
-  static constexpr int kLdsBytes = kStages * kStage;
+  // A K-contiguous A is staged 64 k at a time: its LDS rows are then 128
+  // bytes and every load reads whole cache lines (with 32 k each 1 KB load
+  // touches 16 half lines, and a K tile's loads with both operands
+  // K-contiguous took longer than its MFMAs).  Its ring holds three such
+  // stages, so a stage is loaded six phases or more before it is read (with
+  // two, about four: measured much slower).  Every other operand is staged
+  // 32 k at a time in a ring of up to four (four measured faster than five:
+  // fewer loads in flight, less congestion).  Each operand has its own LDS
+  // region.
+  static constexpr bool kAPairs = AK;
+  using LA = OpLayout<BM, AK, kAPairs ? 64 : 32>;
+  using LB = OpLayout<BN, BK, 32>;
+  static constexpr int kAStages = kAPairs ? 3 : 4;
+  static constexpr int kABytes = kAStages * LA::kBytes;
+  static constexpr int kBFit = (kLdsMax - kABytes) / LB::kBytes;
+  static constexpr int kBStages = kBFit < 4 ? kBFit : 4;
+  static_assert(kBStages >= 3, "B needs a ring of at least three stages");
+  static constexpr int kLdsBytes = kABytes + kBStages * LB::kBytes;
+  // loads per stage per wave (every 8th load; a count that is not a
+  // multiple of 8 duplicates the last load in some waves)
+  static constexpr int IA = (LA::kInstr + kPPWaves - 1) / kPPWaves;
+  static constexpr int IB = (LB::kInstr + kPPWaves - 1) / kPPWaves;
+  // A 64-k A stage's loads are split over the two read phases of the
+  // stage before it (IA / 2 per wave in each), so that every read phase
+  // issues the same number of loads.
+  static_assert(!kAPairs || IA % 2 == 0, "a 64-k A stage splits its loads evenly over two halves");
+  static constexpr int kAPerHalf = kAPairs ? IA / 2 : IA;
 };
+
+// A wave's load sequence, simulated at compile time.  The prologue issues
+// A's stages 0 .. kAStages-2 and B's tiles 0 .. kBStages-2 in the order the
+// halves need them (A's stage first on a tie).  The read phase of half j
+// then issues A's part (64-k stages: loads [0, IA/2) of stage j/2 +
+// kAStages - 1 for even j, loads [IA/2, IA) of it for odd j; 32-k stages:
+// tile j + kAStages - 1) and B's tile j + kBStages - 1, A's part first if
+// a_first.  pp_after(h) counts the loads issued after the last one that
+// half h reads, when the wave has issued everything up to the read phase of
+// half h - 1 (h = 0: the prologue alone).  A phase that ends with vmcnt <= n
+// (and a block barrier) guarantees every load of the next half when
+// n <= pp_after(h).
+template <class T>
+constexpr int pp_after(int h, bool a_first) {
+  int issued = 0, needed_end = 0;
+  const int need_a = T::kAPairs ? h / 2 : h, need_b = h;
+  auto note = [&](bool ok) {
+    if (ok && issued > needed_end) needed_end = issued;
+  };
+  // prologue, by the half that first reads each stage
+  const int last = 2 * (T::kAStages + T::kBStages);
+  for (int half = 0; half < last; ++half) {
+    const int sa = T::kAPairs ? half / 2 : half;
+    const bool a_now = sa < T::kAStages - 1 && (T::kAPairs ? half % 2 == 0 : true);
+    if (a_now) {
+      issued += T::IA;
+      note(sa == need_a);
+    }
+    if (half < T::kBStages - 1) {
+      issued += T::IB;
+      note(half == need_b);
+    }
+  }
+  for (int j = 0; j < h; ++j) {
+    const int sa = T::kAPairs ? j / 2 + T::kAStages - 1 : j + T::kAStages - 1, tb = j + T::kBStages - 1;
+    // a 64-k stage is complete after its odd half's part
+    const bool a_done = !T::kAPairs || j % 2 == 1;
+    for (int o = 0; o < 2; ++o) {
+      if ((o == 0) == a_first) {
+        issued += T::kAPerHalf;
+        note(a_done && sa == need_a);
+      } else {
+        issued += T::IB;
+        note(tb == need_b);
+      }
+    }
+  }
+  return issued - needed_end;
+}
+
+// The in-loop wait: the smallest pp_after over the halves from the first on.
+template <class T>
+constexpr int pp_wait_count(bool a_first) {
+  int n = 1 << 30;
+  for (int h = 1; h < 64; ++h) n = pp_after<T>(h, a_first) < n ? pp_after<T>(h, a_first) : n;
+  return n;
+}
 
 template <int BM_, int BN_, bool AK_, bool BK_, class Epi_>
 struct PPProblem {
@@ -194,23 +263,27 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (K + kBK - 1) / kBK;
-  constexpr int IA = (LA::kInstr + kPPWaves - 1) / kPPWaves, IB = (LB::kInstr + kPPWaves - 1) / kPPWaves;
-  constexpr int kPer = IA + IB;  // loads per tile per wave
+  const int nk = (K + kBK - 1) / kBK;  // 32-wide halves (one phase each)
+  constexpr int IA = T::IA, IB = T::IB;
+  constexpr int KA = T::kAPairs ? 64 : 32;  // k per A stage
+  // A's part of a read phase first, or B's tile: whichever lets the phase
+  // ends leave more loads in flight.
+  constexpr bool kAF = pp_wait_count<T>(true) >= pp_wait_count<T>(false);
 
-  // Direct-to-LDS loads: load n of an operand fills bytes [1024 n, +1024) of
-  // its region; waves take every 8th load (duplicating the last one where the
-  // count is not a multiple of eight).  Offsets fixed per tile; the buffer
-  // resources move per K tile; a K-contiguous operand's partial last tile
-  // masks its lanes past K.
+  // Direct-to-LDS loads: load n of an operand's stage fills bytes
+  // [1024 n, +1024) of the stage; waves take every 8th load (duplicating the
+  // last one where the count is not a multiple of eight).  Offsets fixed per
+  // tile; the buffer resources move per stage; a K-contiguous operand's
+  // partial last stage masks its lanes past K.  A K-contiguous operand's k
+  // (within the stage) of a lane's 8 elements is the same in all of a wave's
+  // loads: with 64-byte rows it depends on the lane only, with 128-byte rows
+  // also on the parity of the load index, which is the wave's for loads
+  // n = wave + 8t (a 64-k A stage holds a multiple of 8 loads).
+  static_assert(!T::kAPairs || LA::kInstr % kPPWaves == 0, "whole loads per wave in a 64-k stage");
   uint32_t offa[IA], offb[IB];
-  int kca[IA], kcb[IB];
+  const int kca = LA::kcol(wave, lane), kcb = LB::kcol(wave, lane);
 #pragma unroll
-  for (int t = 0; t < IA; ++t) {
-    const int n = min(wave + kPPWaves * t, LA::kInstr - 1);
-    offa[t] = LA::src_off(n, lane, p.lda, M - m0);
-    kca[t] = LA::kcol(n, lane);
-  }
+  for (int t = 0; t < IA; ++t) offa[t] = LA::src_off(min(wave + kPPWaves * t, LA::kInstr - 1), lane, p.lda, M - m0);
 #pragma unroll
   for (int t = 0; t < IB; ++t) {
     const int n = min(wave + kPPWaves * t, LB::kInstr - 1);
@@ -218,68 +291,102 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
       offb[t] = LB::src_off_paired(n, lane, p.ldb, p.epi.half - bcol0, p.epi.half);
     else
       offb[t] = LB::src_off(n, lane, p.ldb, N - n0);
-    kcb[t] = LB::kcol(n, lane);
   }
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * kBK;
+  // A's stage st (k from st KA) into slot st % kAStages of A's region, B's
+  // tile tl (k from 32 tl) into slot tl % kBStages of B's region.  Stages
+  // past K load nothing (empty resource: zeros), which keeps every wave's
+  // load count per half fixed for the vmcnt waits.
+  // loads [T0, T1) of the wave's share of A's stage st
+  auto load_a = [&](int st, auto t0_c, auto t1_c) {
+    constexpr int T0 = decltype(t0_c)::value, T1 = decltype(t1_c)::value;
+    const int k0 = st * KA;
     const __amdgpu_buffer_rsrc_t ra = tile_rsrc<P::AK>(p.A, p.lda, m0, M, K, k0);
-    const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, bcol0, bcols, K, k0);
-    const bool kfull = k0 + kBK <= K;
-    char* base = smem + (kt % T::kStages) * T::kStage;
+    const bool kfull = k0 + KA <= K;
+    char* base = smem + (st % T::kAStages) * LA::kBytes;
 #pragma unroll
-    for (int t = 0; t < IA; ++t) {
+    for (int t = T0; t < T1; ++t) {
       const int n = min(wave + kPPWaves * t, LA::kInstr - 1);
       uint32_t off = offa[t];
-      if (P::AK && !kfull) off = k0 + kca[t] < K ? off : kOutOfRange;
+      if (P::AK && !kfull) off = k0 + kca < K ? off : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LGS_AS3 void*)(base + n * 1024), 16, (int)off, 0, 0, 0);
     }
+  };
+  auto load_b = [&](int tl) {
+    const int k0 = tl * kBK;
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc<P::BK>(p.B, p.ldb, bcol0, bcols, K, k0);
+    const bool kfull = k0 + kBK <= K;
+    char* base = smem + T::kABytes + (tl % T::kBStages) * LB::kBytes;
 #pragma unroll
     for (int t = 0; t < IB; ++t) {
       const int n = min(wave + kPPWaves * t, LB::kInstr - 1);
       uint32_t off = offb[t];
-      if (P::BK && !kfull) off = k0 + kcb[t] < K ? off : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LGS_AS3 void*)(base + LA::kBytes + n * 1024), 16, (int)off, 0, 0, 0);
+      if (P::BK && !kfull) off = k0 + kcb < K ? off : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LGS_AS3 void*)(base + n * 1024), 16, (int)off, 0, 0, 0);
     }
   };
 
-  // Fragments of both 16-wide sub-steps of one K tile.
+  // Fragments of both 16-wide sub-steps of half kt.  A transposing read's
+  // per-lane offset does not depend on the sub-step (it goes into the
+  // instruction's offset).  A K-contiguous operand's does, through the chunk
+  // swizzle only: in sub-step q of its stage the chunk bits of the byte
+  // offset are (2q) ^ (lane / 32) ^ swizzle(row), so the offset is that of
+  // sub-step 0 with 32 q xor-ed in (every other part of the address is a
+  // multiple of 2 KT bytes).  For a 64-k A stage, half kt is sub-steps
+  // 2 (kt % 2) and 2 (kt % 2) + 1.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LGS_AS3 char*)smem;
-  const uint32_t fa_lane[2] = {LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * LA::kColBytes,
-                               LA::lane_off(1, lane) + (uint32_t)(wm * T::WM) * LA::kColBytes};
-  const uint32_t fb_lane[2] = {LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * LB::kColBytes + LA::kBytes,
-                               LB::lane_off(1, lane) + (uint32_t)(wn * T::WN) * LB::kColBytes + LA::kBytes};
+  const uint32_t fa_lane = LA::lane_off(0, lane) + (uint32_t)(wm * T::WM) * LA::kColBytes;
+  const uint32_t fb_lane = LB::lane_off(0, lane) + (uint32_t)(wn * T::WN) * LB::kColBytes + T::kABytes;
   bf16x8 fa[2][TM], fb[2][TN];
-  auto read_sub = [&](uint32_t sb, auto s_c) {
-    constexpr int s = decltype(s_c)::value;
+  auto read_sub = [&](uint32_t ab, uint32_t bb, auto qa_c, auto s_c) {
+    constexpr int qa = decltype(qa_c)::value, s = decltype(s_c)::value;
     if constexpr (P::AK) {
-      const char* pa = smem + sb + fa_lane[s];
+      const char* pa = smem + ((ab + fa_lane) ^ (32u * qa));
       static_for<TM>([&](auto i) { fa[s][i] = LA::template frag<32 * decltype(i)::value>(pa); });
     } else {
-      const uint32_t a = lds0 + sb + fa_lane[0];
-      static_for<TM>([&](auto i) { fa[s][i] = LA::template frag_tr<s, 32 * decltype(i)::value>(a); });
+      const uint32_t a = lds0 + ab + fa_lane;
+      static_for<TM>([&](auto i) { fa[s][i] = LA::template frag_tr<qa, 32 * decltype(i)::value>(a); });
     }
     if constexpr (P::BK) {
-      const char* pb = smem + sb + fb_lane[s];
+      const char* pb = smem + ((bb + fb_lane) ^ (32u * s));
       static_for<TN>([&](auto j) { fb[s][j] = LB::template frag<32 * decltype(j)::value>(pb); });
     } else {
-      const uint32_t b = lds0 + sb + fb_lane[0];
+      const uint32_t b = lds0 + bb + fb_lane;
       static_for<TN>([&](auto j) { fb[s][j] = LB::template frag_tr<s, 32 * decltype(j)::value>(b); });
     }
   };
-  // Read phase: this wave's fragments of tile kt, then the loads of tile
-  // kt+S-1 (into the stage that tile kt-1 left), then wait for the fragments.
-  // The fragment reads overwrite registers that this wave's previous MFMAs
-  // read as sources: on gfx950 an MFMA reads its A and B operands at issue,
-  // so overwriting them afterwards needs no wait states (the compiler's own
-  // hazard model inserts none for a DS or VALU write there).  Only the
-  // compiler barrier below is needed.
-  auto read_phase = [&](int kt) {
+  // Read phase of half kt: this wave's fragments, then its loads of the
+  // stages that enter the rings now (A's stage kt/2 + kAStages - 1 for even
+  // kt with 64-k stages, else kt + kAStages - 1; B's tile kt + kBStages - 1),
+  // then wait for the fragments.  The fragment reads overwrite registers that
+  // this wave's previous MFMAs read as sources: on gfx950 an MFMA reads its A
+  // and B operands at issue, so overwriting them afterwards needs no wait
+  // states (the compiler's own hazard model inserts none for a DS or VALU
+  // write there).  Only the compiler barrier below is needed.
+  auto read_phase = [&](int kt, auto half_c) {
+    constexpr int half = decltype(half_c)::value;
     asm volatile("" ::: "memory");
-    const uint32_t sb = (uint32_t)((kt % T::kStages) * T::kStage);
-    read_sub(sb, std::integral_constant<int, 0>{});
-    read_sub(sb, std::integral_constant<int, 1>{});
+    const uint32_t ab = (uint32_t)(((T::kAPairs ? kt >> 1 : kt) % T::kAStages) * LA::kBytes);
+    const uint32_t bb = (uint32_t)((kt % T::kBStages) * LB::kBytes);
+    constexpr int q0 = T::kAPairs ? 2 * half : 0;
+    read_sub(ab, bb, std::integral_constant<int, q0>{}, std::integral_constant<int, 0>{});
+    read_sub(ab, bb, std::integral_constant<int, q0 + 1>{}, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
-    load_tile(kt + T::kStages - 1);
+    // A's part: half `half` of the loads of 64-k stage kt/2 + kAStages - 1,
+    // or all of 32-k tile kt + kAStages - 1
+    auto a_part = [&]() {
+      if constexpr (T::kAPairs)
+        load_a((kt >> 1) + T::kAStages - 1, std::integral_constant<int, half * T::kAPerHalf>{},
+               std::integral_constant<int, (half + 1) * T::kAPerHalf>{});
+      else
+        load_a(kt + T::kAStages - 1, std::integral_constant<int, 0>{}, std::integral_constant<int, IA>{});
+    };
+    if constexpr (kAF) {
+      a_part();
+      load_b(kt + T::kBStages - 1);
+    } else {
+      load_b(kt + T::kBStages - 1);
+      a_part();
+    }
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkm0();
   };
@@ -293,26 +400,49 @@ __device__ __forceinline__ void gemm_tile_pp(const P& p, char* smem, int tmi, in
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // End of a phase: this wave's loads older than the last S-2 tiles have
-  // landed (every tile read in the next phase is among them), then barrier.
-  constexpr int S = T::kStages;
+  // End of a phase: this wave's loads that the next half reads have landed
+  // (pp_after: past the prologue the same count of later loads for every
+  // half), then barrier.
+  constexpr int kWait = pp_wait_count<T>(kAF);
+  static_assert(kWait >= 0 && kWait < 64 && pp_after<T>(8, kAF) == kWait && pp_after<T>(9, kAF) == kWait,
+                "the prologue must not leave fewer loads in flight than the steady state");
   auto phase_end = [&]() {
-    wait_vmcnt<(S - 2) * kPer>();
+    wait_vmcnt<kWait>();
     block_barrier();
   };
 
-  // Both groups run the same loop; group 1 starts one barrier later (block
-  // barriers count arrivals, not program points), which staggers the groups
-  // by one phase, and group 0 ends with one extra barrier to match.
-#pragma unroll
-  for (int t = 0; t < S - 1; ++t) load_tile(t);
-  phase_end();
+  // Phases: in phase 2kt group 0 reads half kt and group 1 computes half
+  // kt - 1; in phase 2kt + 1 group 0 computes half kt and group 1 reads it.
+  // A ring slot is reloaded in a read phase only after both groups have read
+  // its previous stage: B's tile kt + kBStages - 1 goes into the slot of tile
+  // kt - 1, which group 1 read in phase 2kt - 1; A's 64-k stage kt/2 + 2
+  // (even kt) into the slot of stage kt/2 - 1, whose last half group 1 read
+  // in phase 2kt - 1.  Group 1 starts one barrier later (block barriers
+  // count arrivals, not program points), and group 0 ends with one extra
+  // barrier to match.
+  // Prologue, in the order pp_after simulates: each stage by the first half
+  // that reads it, A's first on a tie.
+  static_for<2 * (T::kAStages + T::kBStages)>([&](auto h_c) {
+    constexpr int h = decltype(h_c)::value;
+    constexpr int sa = T::kAPairs ? h / 2 : h;
+    if constexpr (sa < T::kAStages - 1 && (!T::kAPairs || h % 2 == 0))
+      load_a(sa, std::integral_constant<int, 0>{}, std::integral_constant<int, IA>{});
+    if constexpr (h < T::kBStages - 1) load_b(h);
+  });
+  wait_vmcnt<pp_after<T>(0, kAF)>();  // half 0's stages have landed
+  block_barrier();
   if (grp == 1) block_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    read_phase(kt);
+  for (int kt = 0; kt < nk; kt += 2) {
+    read_phase(kt, std::integral_constant<int, 0>{});
     phase_end();
     compute_phase();
     phase_end();
+    if (kt + 1 < nk) {
+      read_phase(kt + 1, std::integral_constant<int, 1>{});
+      phase_end();
+      compute_phase();
+      phase_end();
+    }
   }
   if (grp == 0) block_barrier();
   wait_vmcnt<0>();  // the (zero) loads past the end must land before LDS is reused
