@@ -14,7 +14,13 @@
 // one is reduced, and the target logit read straight from memory by one lane
 // instead of picked out of the registers.  Measured on the 8.3B slice
 // ([8192, 6400], three rotating buffers): 21.7 us (7 chunks per batch, no
-// prefetch, register pick) -> about 19 us.
+// prefetch, register pick) -> 19.2-19.5 us (5 per batch, prefetch) ->
+// 18.7-19.0 us (7 per batch: a row is two batches, the second 79% full,
+// instead of 2.5).  A probe without the exponentials (wrong results) takes
+// 18.1-18.2 us, so the per-logit arithmetic costs about 4%.  Variants that
+// measured slower: 4, 8, 10 or 13 chunks per batch, 4 or 16 rows per
+// block, two alternating register sets instead of copying the prefetched
+// batch.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -24,7 +30,7 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowsPerBlock = 8;  // one row per wave
-constexpr int kBatch = 5;         // 16-byte chunks per lane per batch (2560 logits per wave)
+constexpr int kBatch = 7;         // 16-byte chunks per lane per batch (3584 logits per wave)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __global__ __launch_bounds__(64 * kRowsPerBlock) void xent_rows_kernel(
