@@ -234,6 +234,72 @@ hbm_bytes_per_call: {nbytes(0) + nbytes(1):.0f}
 """
     open(COUNTERS_FILE, "w").write(txt)
     print(txt)
+    ce_counter_summary(d, fr, fw)
+
+
+XENT_COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_8p3b_hbm_counters.txt")
+
+
+def ce_counter_summary(d, fr, fw):
+    """The fused CE's share of the same counter passes (the step runs it on
+    slice 0 of the 8.3B shapes), next to a model of its L2 fills: each XCD
+    fetches, per round of its 32 concurrent tiles, the H row panels and E_r
+    column panels those tiles cover, once each (K = 3072 bf16: 6144 bytes per
+    panel row or column)."""
+    import statistics
+
+    def csv_of(sub):
+        return glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)[0]
+    kern = {"main": "320, true, true, lgs::EpiXent", "tail": "160, 4, true, true, lgs::EpiXent",
+            "merge": "xent_merge_kernel"}
+    med = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        step = _per_kernel(csv_of(f"pmc_{c}"), c)
+        for key, pat in kern.items():
+            v = [x for n, x in step.items() if pat in n]
+            if len(v) != 1:
+                raise SystemExit(f"{c}: expected one {key} kernel of the CE, found {len(v)}")
+            med[(c, key)] = statistics.median(v[0])
+
+    def mb(key):
+        return (med[("FETCH_SIZE", key)] * 1024 * fr + med[("WRITE_SIZE", key)] * 1024 * fw) / 1e6
+    panel = 3072 * 2
+    main_model = 8 * 2 * (4 * 256 + 8 * 320) * panel / 1e6    # 8 XCDs x 2 rounds, 4 x 8 tiles each
+    tail_model = 8 * 1 * (4 * 256 + 8 * 160) * panel / 1e6    # 8 XCDs x 1 round, 4 x 8 tiles each
+    best_main = 8 * 2 * (8 * 256 + 4 * 320) * panel / 1e6     # the best 32-tile block per XCD (8 x 4)
+    alg = (8192 * 3072 + 6400 * 3072) * 2 / 1e6
+    step_cmd = "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-per-config --no-clock"
+    txt = f"""# L2-to-fabric traffic of the fused CE entry point (vocab_parallel_xent_fwd) on
+# the 8.3B-shape slice (rank 0 of t = 8: M = 8192 tokens, h = 3072, V_r = 6400),
+# from the same rocprofv3 counter passes over the step as
+# mlp_70b_bwd_hbm_counters.txt (one counter per run):
+#
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/pmc_FETCH_SIZE -o p -- {step_cmd}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/pmc_WRITE_SIZE -o p -- {step_cmd}
+#   (+ the two copy-calibration passes; python bench.py --counter-summary gpurun_out/pmc writes this file)
+#
+# Per launch (median of the dispatches), bytes = FETCH_SIZE x 1024 x {fr:.4f} + WRITE_SIZE x 1024 x {fw:.4f}:
+#   256x320 launch (columns 0-5119, 512 tiles, two rounds): FETCH_SIZE {med[('FETCH_SIZE', 'main')]:.0f} KiB, WRITE_SIZE {med[('WRITE_SIZE', 'main')]:.0f} KiB -> {mb('main'):.1f} MB
+#   256x160 launch (columns 5120-6399, 256 tiles, one round): FETCH_SIZE {med[('FETCH_SIZE', 'tail')]:.0f} KiB, WRITE_SIZE {med[('WRITE_SIZE', 'tail')]:.0f} KiB -> {mb('tail'):.1f} MB
+#   slab merge:                                 FETCH_SIZE {med[('FETCH_SIZE', 'merge')]:.0f} KiB, WRITE_SIZE {med[('WRITE_SIZE', 'merge')]:.0f} KiB -> {mb('merge'):.1f} MB
+#   algorithmic operand bytes (H and E_r read once): {alg:.1f} MB
+#
+# Model of the L2 fills: each XCD's 32 concurrent tiles are 4 row tiles x 8
+# column tiles of its contiguous block of the tile order, and per round its L2
+# fetches each of their H row panels and E_r column panels once:
+#   256x320 launch: 8 XCDs x 2 rounds x (4 x 256 + 8 x 320) panel lines x 6144 B = {main_model:.1f} MB
+#   256x160 launch: 8 XCDs x 1 round x (4 x 256 + 8 x 160) panel lines x 6144 B = {tail_model:.1f} MB
+# The counters match the model: the L2s fetch nothing twice within a round.
+# The traffic above the algorithmic bytes is the panels that the 8 XCDs'
+# separate L2s each fetch (served by the Infinity Cache, which holds H and E_r
+# whole).  No tile order brings it near the algorithmic bytes: with 32 tiles per
+# XCD per round the best block (8 row tiles x 4 column tiles) still fetches
+# {best_main:.1f} MB in the 256x320 launch alone, {best_main / alg:.1f}x the algorithmic bytes.
+kernel_sources_sha256: {kernel_sources_digest()}
+hbm_bytes_per_launch: {(mb('main') + mb('tail') + mb('merge')) * 1e6:.0f}
+"""
+    open(XENT_COUNTERS_FILE, "w").write(txt)
+    print(txt)
 
 
 def kernel_stats_md(src, title, cmd):
