@@ -535,7 +535,7 @@ def per_config(torch, lgs, reps):
     del X, A, B, Z, Zs, Ys, shards, graph
 
     # MLP shard forward and backward at the 8.3B and 70B shapes
-    for fwd_name, bwd_name in (("mlp_8p3b_fwd", None), ("mlp_70b_fwd", "mlp_70b_bwd")):
+    for fwd_name, bwd_name in (("mlp_8p3b_fwd", "mlp_8p3b_bwd"), ("mlp_70b_fwd", "mlp_70b_bwd")):
         w = WORKLOADS[fwd_name]
         f = w.f_i
         per_set = 2 * (2 * w.M * w.h + 2 * w.h * f)
@@ -551,7 +551,7 @@ def per_config(torch, lgs, reps):
         fl = mlp_flops(w.M, w.h, f)
         out[fwd_name] = _timed_report(torch, fwd, fl["fwd"], reps, len(sets))
         if bwd_name:
-            wb = WORKLOADS[bwd_name]
+            wb = WORKLOADS.get(bwd_name, w)  # the 8.3B backward: the forward's shapes, dZ ~ N(0, 0.01)
             dX = torch.empty(w.M, w.h, dtype=bf, device=dev)
             dA = torch.empty(w.h, f, dtype=bf, device=dev)
             dB = torch.empty(f, w.h, dtype=bf, device=dev)
@@ -692,6 +692,126 @@ def per_config(torch, lgs, reps):
     return out
 
 
+MFMA_COUNTERS_FILE = os.path.join(ROOT, "profiles", "mfma_lds_counters_8p3b_step.md")
+MFMA_PASSES = ("SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES",
+               "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA SQ_WAVES")
+# kernels of the 8.3B workload: (row label, algorithmic GFLOP, name patterns (mangled, demangled))
+MFMA_KERNELS = (
+    ("fwd GEMM1 + GeLU (256x192, 256 tiles)", 77.309, ("Li256ELi192ELb1ELb0ENS_10EpiGeluFwd", "256, 192, true, false, lgs::EpiGeluFwd")),
+    ("fwd GEMM2 (256x192, 512 tiles)", 77.309, ("Li256ELi192ELb1ELb0ENS_8EpiStore", "256, 192, true, false, lgs::EpiStore")),
+    ("dY + GeLU' (256x192, 256 tiles)", 77.309, ("Li256ELi192ELb1ELb1ENS_10EpiGeluBwd", "256, 192, true, true, lgs::EpiGeluBwd")),
+    ("group3 dB, dA, dX (256x256, 528 tiles)", 231.928, ("gemm_pp_group3_kernel",)),
+    ("CE logit GEMM + slabs, first 5120 columns (256x320, 512 tiles)", 257.698,
+     ("Li256ELi320ELb1ELb1ENS_7EpiXent", "256, 320, true, true, lgs::EpiXent")),
+    ("CE logit GEMM + slabs, last 1280 columns (256x160, 256 tiles)", 64.425,
+     ("Li256ELi160ELi4ELb1ELb1ENS_7EpiXent", "256, 160, 4, true, true, lgs::EpiXent")),
+)
+
+
+def mfma_workload(torch, lgs, calls=5):
+    """The 8.3B-shape kernels alone, for counter passes: rank 0's MLP forward
+    and backward and the fused CE of slice 0, `calls` times each on three
+    rotated input sets."""
+    from logit_gemm_shard_amd import synth
+    from logit_gemm_shard_amd.configs import WORKLOADS
+    dev, bf = torch.device("cuda", 0), torch.bfloat16
+    w, xw = WORKLOADS["mlp_8p3b_fwd"], WORKLOADS["xent_8p3b"]
+    f = w.f_i
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, device=dev) * std).to(bf)
+    sets = [(randn(w.M, w.h), randn(w.h, f, std=0.02), randn(f, w.h, std=synth.residual_std(w.n_blocks)),
+             randn(w.M, w.h, std=0.01), randn(xw.M, xw.h), randn(xw.v_r, xw.h, std=0.02),
+             torch.randint(0, xw.vocab, (xw.M,), device=dev, dtype=torch.int32)) for _ in range(3)]
+    U, Y = torch.empty(w.M, f, dtype=bf, device=dev), torch.empty(w.M, f, dtype=bf, device=dev)
+    Z, dX = torch.empty(w.M, w.h, dtype=bf, device=dev), torch.empty(w.M, w.h, dtype=bf, device=dev)
+    dA, dB = torch.empty(w.h, f, dtype=bf, device=dev), torch.empty(f, w.h, dtype=bf, device=dev)
+    ws = torch.empty(lgs.mlp_bwd_workspace_bytes(w.b, w.s, w.h, w.ffn, w.t, bf), dtype=torch.uint8, device=dev)
+    wx = torch.empty(lgs.xent_workspace_bytes(xw.b, xw.s, xw.h, xw.vocab, xw.t), dtype=torch.uint8, device=dev)
+    st = torch.empty(3, xw.M, device=dev)
+    for i in range(calls):
+        X, A0, B0, dZ, H, E0, y = sets[i % 3]
+        lgs.tp_mlp_fwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, Z, U_i=U, Y_i=Y)
+        lgs.tp_mlp_bwd(w.b, w.s, w.h, w.ffn, w.t, 0, X, A0, B0, U, dZ, dX, dA, dB, workspace=ws)
+        lgs.vocab_parallel_xent_fwd(xw.b, xw.s, xw.h, xw.vocab, xw.t, 0, H, E0, y, st[0], st[1], st[2], workspace=wx)
+    torch.cuda.synchronize()
+
+
+def mfma_summary(d):
+    """Write MFMA_COUNTERS_FILE from two rocprofv3 --pmc passes (MFMA_PASSES)
+    over `bench.py --mfma-workload` under d/pmc_mfma_A and d/pmc_mfma_B."""
+    import collections
+    import csv
+    import statistics
+    cnt, dur, names = collections.defaultdict(list), collections.defaultdict(list), {}
+    for sub in ("pmc_mfma_A", "pmc_mfma_B"):
+        found = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not found:
+            raise SystemExit(f"no counter_collection.csv under {os.path.join(d, sub)}")
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        span = {}
+        for r in csv.DictReader(open(found[0])):
+            label = next((k[0] for k in MFMA_KERNELS if any(pat in r["Kernel_Name"] for pat in k[2])), None)
+            if label is None:
+                continue
+            per[(label, r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+            span[(label, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        for (label, _), c in per.items():
+            for k, v in c.items():
+                cnt[(label, k)].append(v)
+        for (label, _), v in span.items():
+            dur[label].append(v)
+    med = {k: statistics.median(v) for k, v in cnt.items()}
+    rows1, rows2 = [], []
+    for label, alg, _ in MFMA_KERNELS:
+        if (label, "SQ_WAVES") not in med:
+            raise SystemExit(f"no counters for {label}")
+        us = statistics.median(dur[label])
+        busy = med[(label, "SQ_VALU_MFMA_BUSY_CYCLES")] / 1024
+        active = med[(label, "GRBM_GUI_ACTIVE")] / 8
+        gflop = med[(label, "SQ_INSTS_VALU_MFMA_MOPS_BF16")] * 512 / 1e9
+        waves = med[(label, "SQ_WAVES")]
+        rows1.append(f"| {label} | {us:.1f} | {gflop:.3f} | {alg:.3f} | {busy / 1e3:.1f} k | {active / 1e3:.1f} k | "
+                     f"{100 * busy / active:.1f}% | {active / us / 1e3:.2f} GHz |")
+        rows2.append(f"| {label} | {waves:.0f} | {med[(label, 'SQ_INSTS_VALU')] / waves:.0f} | "
+                     f"{med[(label, 'SQ_INSTS_MFMA')] / waves:.0f} | {med[(label, 'SQ_INSTS_LDS')] / waves:.0f} | "
+                     f"{med[(label, 'SQ_LDS_BANK_CONFLICT')] / 256:.0f} |")
+    cmd = "python bench.py --mfma-workload"
+    txt = f"""# MFMA and LDS counters per kernel: the 8.3B-shape kernels (rank 0 of t=8)
+
+The MLP forward and backward and the fused CE of slice 0, five calls each on three rotated input
+sets (`bench.py --mfma-workload`), under two counter passes, one counter set per run:
+
+```
+rocprofv3 --pmc {MFMA_PASSES[0]} --output-format csv -d gpurun_out/pmc/pmc_mfma_A -o p -- {cmd}
+rocprofv3 --pmc {MFMA_PASSES[1]} --output-format csv -d gpurun_out/pmc/pmc_mfma_B -o p -- {cmd}
+python bench.py --mfma-summary gpurun_out/pmc      (writes this file)
+```
+
+Medians over the launches of each kernel. Counter values are summed over the 8 XCDs. Durations
+are the dispatch timestamps of the same runs, which the counter runs serialise and slow by a
+few percent.
+
+| Kernel | µs | MFMA GFLOP (MOPs × 512) | algorithmic GFLOP | MFMA busy cycles / SIMD | active cycles / XCD | MFMA util | implied clock |
+|---|---|---|---|---|---|---|---|
+{chr(10).join(rows1)}
+
+- MFMA util is rocprof's `MfmaUtil`: MFMA busy cycles summed over the 1024 SIMDs ÷
+  (active cycles × 1024): the matrix cores' duty cycle at the clock the kernel actually ran
+  at, independent of the 2.4 GHz figure behind the spec peak.
+- The implied clock is active cycles ÷ duration; for kernels of under 100 µs the active
+  count includes some time outside the dispatch window, which biases their utilisation low.
+
+| Kernel | waves | VALU instr / wave | MFMA instr / wave | LDS instr / wave | LDS bank-conflict cycles / CU |
+|---|---|---|---|---|---|
+{chr(10).join(rows2)}
+
+kernel_sources_sha256: {kernel_sources_digest()}
+"""
+    open(MFMA_COUNTERS_FILE, "w").write(txt)
+    print(txt)
+
+
 def ce_reduction_stream(torch, lgs, xw, reps=30):
     """The CE reductions alone, streamed from materialised bf16 logits of the
     rank's slice (a testing entry point; the product path fuses them into the
@@ -757,6 +877,10 @@ def main():
                     help="time torch.matmul (hipBLASLt) at the library's GEMM shapes and exit")
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="write the tp_mlp_bwd traffic summary from rocprofv3 --pmc passes under DIR and exit")
+    ap.add_argument("--mfma-workload", action="store_true",
+                    help="run the 8.3B-shape kernels alone (for counter passes) and exit")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="write the MFMA / LDS counter summary from the passes under DIR and exit")
     ap.add_argument("--kernel-stats", nargs=3, metavar=("CSV", "TITLE", "COMMAND"),
                     help="print a markdown table of a rocprofv3 kernel_stats.csv and exit")
     args = ap.parse_args()
@@ -765,6 +889,9 @@ def main():
         return
     if args.kernel_stats:
         kernel_stats_md(*args.kernel_stats)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard: the library is measured on one GPU "
@@ -778,6 +905,10 @@ def main():
         return
     if args.blas_reference:
         blas_reference()
+        return
+    if args.mfma_workload:
+        from logit_gemm_shard_amd import binding as lgs_b
+        mfma_workload(torch, lgs_b)
         return
 
     from logit_gemm_shard_amd import binding as lgs
