@@ -281,7 +281,7 @@ int vocab_parallel_xent_fwd(int b, int s, int h, int vocab, int t, int rank, int
  *
  * Limit: lgs_xent_workspace_bytes(b, s, h, vocab, t, dtype) must not exceed
  * LGS_XENT_NOALLOC_SCRATCH_BYTES (e.g. 8192 tokens at vocab/t = 6400 need
- * 5 MiB; about 25,000 tokens fit at that slice width); larger calls return
+ * 6 MiB; about 22,000 tokens fit at that slice width); larger calls return
  * LGS_ERR_UNSUPPORTED before anything is enqueued.
  *
  * Every call on one device shares that device's array, so calls that overlap

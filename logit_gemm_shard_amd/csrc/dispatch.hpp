@@ -35,6 +35,8 @@ constexpr unsigned kAllTiles = (1u << kNumTiles) - 1;
 // ping-pong tiles whose wave width is a multiple of 64 (whole pairs of
 // 32-column groups per wave, for paired epilogues)
 constexpr unsigned kPairedTiles = (1u << T256x256) | (1u << T128x128);
+// the ping-pong tiles
+constexpr unsigned kPPTiles = (1u << T256x256) | (1u << T256x192) | (1u << T128x128) | (1u << T256x320);
 
 inline TileId pick_tile(int M, int N, unsigned allowed = kAllTiles) {
   constexpr int kCUs = 256;
@@ -72,13 +74,14 @@ struct ColumnPlan {
   TileId tail;
 };
 
-inline ColumnPlan plan_columns(int M, int N, bool same_wn) {
-  const TileId t = pick_tile(M, N);
+inline ColumnPlan plan_columns(int M, int N, bool same_wn, unsigned allowed = kAllTiles) {
+  const TileId t = pick_tile(M, N, allowed);
   ColumnPlan best{t, N, t};
   double best_cost = tile_cost(t, M, N);
   const int bn = kTileShapes[t].bn;
   for (int c1 = bn; c1 < N; c1 += bn)
     for (int u = 0; u < kNumTiles; ++u) {
+      if (!(allowed & (1u << u))) continue;
       if (same_wn && kTileShapes[u].wn != kTileShapes[t].wn) continue;
       const double c = tile_cost(t, M, c1) + tile_cost((TileId)u, M, N - c1);
       if (c < best_cost * 0.97) {  // a second launch costs a few microseconds

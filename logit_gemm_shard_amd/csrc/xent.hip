@@ -14,23 +14,29 @@
 
 namespace lgs {
 
+// The launch plan: the slice's columns in one launch, or two (plan_columns),
+// on the ping-pong tiles (e.g. 8192 x 6400: 5120 columns on 256x320, the last
+// 1280 on 256x192).  Each launch numbers its slabs from where the previous
+// one ended, with its own wave width.
+static ColumnPlan xent_plan(int M, int Vr) { return plan_columns(M, Vr, false, kPPTiles); }
+
 // Slabs the launch plan writes: every wave column of every tile writes one
 // slab (a wave column wholly past the slice end writes -inf / 0 partials that
 // the merge never reads), so a launch of `cols` columns on tile t writes
 // ceil(cols / BN) * BN / WN of them.  The merge reads the first
-// ceil(Vr / WN) (one launch) or c1 / WN + ceil((Vr - c1) / WN) (two).
+// ceil(Vr / WN) (one launch) or c1 / WN + ceil((Vr - c1) / WN_tail) (two).
 static int slabs_written(const ColumnPlan& plan, int Vr) {
-  const int WN = tile_wn(plan.main), bn = tile_bn(plan.main);
-  int n = (plan.c1 + bn - 1) / bn * bn / WN;
+  const int bn = tile_bn(plan.main);
+  int n = (plan.c1 + bn - 1) / bn * bn / tile_wn(plan.main);
   if (plan.c1 < Vr) {
     const int bt = tile_bn(plan.tail);
-    n += (Vr - plan.c1 + bt - 1) / bt * bt / WN;
+    n += (Vr - plan.c1 + bt - 1) / bt * bt / tile_wn(plan.tail);
   }
   return n;
 }
 
 size_t xent_scratch_bytes(int M, int Vr) {
-  return (size_t)slabs_written(plan_columns(M, Vr, true), Vr) * (size_t)M * 16u;
+  return (size_t)slabs_written(xent_plan(M, Vr), Vr) * (size_t)M * 16u;
 }
 
 // Eight lanes per token fold the slabs into the rank's partials, each lane
@@ -87,9 +93,7 @@ __global__ __launch_bounds__(256) void xent_merge_kernel(XentSlabs s, int nslabs
 hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_t ldh,
                     const void* E, int64_t lde, const int32_t* targets, float* m_r, float* l_r,
                     float* t_r, int32_t* argmax_r, float* loss, void* scratch, hipStream_t s) {
-  // The slice's columns in one launch, or two (plan_columns) whose tiles
-  // share the wave width, so that the slabs number consecutively.
-  const ColumnPlan plan = plan_columns(M, Vr, true);
+  const ColumnPlan plan = xent_plan(M, Vr);
   const int WN = tile_wn(plan.main);
   const size_t slab_elems = (size_t)slabs_written(plan, Vr) * M;
   XentSlabs sl;
@@ -103,11 +107,11 @@ hipError_t xent_fwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
   if (err != hipSuccess) return err;
   int nslabs = plan.c1 / WN;
   if (plan.c1 < Vr) {
-    const int rest = Vr - plan.c1;
-    const EpiXent e2{sl, targets, vocab_start + plan.c1, M, rest, WN, plan.c1, nslabs};
+    const int rest = Vr - plan.c1, WNt = tile_wn(plan.tail);
+    const EpiXent e2{sl, targets, vocab_start + plan.c1, M, rest, WNt, plan.c1, nslabs};
     err = gemm_bf16<true, true>(plan.tail, hh, ldh, e + (int64_t)plan.c1 * lde, lde, M, rest, h, e2, s);
     if (err != hipSuccess) return err;
-    nslabs += (rest + WN - 1) / WN;
+    nslabs += (rest + WNt - 1) / WNt;
   } else {
     nslabs = (Vr + WN - 1) / WN;
   }

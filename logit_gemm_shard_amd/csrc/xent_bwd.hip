@@ -74,9 +74,10 @@ hipError_t xent_bwd(int M, int h, int Vr, int vocab_start, const void* H, int64_
                     void* scratch, hipStream_t s) {
   const bf16 *hh = (const bf16*)H, *e = (const bf16*)E;
   bf16* g = (bf16*)scratch;  // G [M, Vr], dense
-  // The slice's columns in one launch or two (plan_columns): the second
-  // covers columns [c1, Vr) with its own tile, writing G from column c1.
-  const ColumnPlan plan = plan_columns(M, Vr, false);
+  // The slice's columns in one launch or two (plan_columns, on the ping-pong
+  // tiles): the second covers columns [c1, Vr) with its own tile, writing G
+  // from column c1.
+  const ColumnPlan plan = plan_columns(M, Vr, false, kPPTiles);
   const EpiXentGrad eg{g, Vr, lse, dloss, targets, vocab_start, M, plan.c1};
   hipError_t err = gemm_bf16<true, true>(plan.main, hh, ldh, e, lde, M, plan.c1, h, eg, s);
   if (err != hipSuccess) return err;

@@ -224,8 +224,9 @@ def test_xent_validation(L):
     assert xe(ws_bytes=16) == 3
     assert xe(lde=32) == 1
     # one 16-byte entry per token and slab written: the 8.3B slice (6400 columns)
-    # runs 5120 columns on 256x320 tiles (32 slabs of 160) and 1280 on 256x160 (8)
-    assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 40 * 8192 * 16
+    # runs 5120 columns on 256x320 tiles (32 slabs of 160) and 1280 on 256x192
+    # (7 tiles of two 96-column slabs: 14)
+    assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 46 * 8192 * 16
 
 
 def test_xent_noalloc_validation(L):
@@ -248,7 +249,7 @@ def test_xent_noalloc_validation(L):
     assert xn(lde=32) == 1
     from logit_gemm_shard_amd import binding
     cap = binding.XENT_NOALLOC_SCRATCH_BYTES
-    # 8192 tokens at the 8.3B slice fit (5 MiB); 32768 do not (20 MiB)
+    # 8192 tokens at the 8.3B slice fit (6 MiB); 32768 do not (23 MiB)
     assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) <= cap
     assert L.lgs_xent_workspace_bytes(32, 1024, 3072, 51200, 8, 1) > cap
     big = xn(b=32, s=1024, h=3072, vocab=51200, t=8, ldh=3072, lde=3072)
