@@ -48,10 +48,11 @@ hipError_t input_and_weight_grads(const bf16* a1, int64_t lda1, const bf16* b1, 
 
 // The QKV product is skinny (at the 70B shape 4096 x 1280 outputs: 80 tiles of
 // 256x256 for 256 compute units) and deep (K = h = 8192).  Split-K fills the
-// chip: S slices of K, each an ordinary GEMM writing an fp32 partial, then
-// one pass sums the slices into bf16.  Used when the unsplit tiles would
-// occupy at most half of the compute units and K is long enough for the
-// slices to stay efficient.
+// chip: every tile's K range in S parts, each an ordinary GEMM, reduced
+// inside the launch (the last part of a tile to finish adds the parts' fp32
+// partials in part order and stores the bf16 tile).  Used when the unsplit
+// tiles would occupy at most half of the compute units and K is long enough
+// for the parts to stay efficient.
 namespace {
 int qkv_kchunk(int h, int splits) { return ((h + splits - 1) / splits + 31) / 32 * 32; }
 }  // namespace
@@ -65,23 +66,29 @@ int attn_qkv_splits(int M, int h, int nqkv) {
   return splits >= 2 ? splits : 0;
 }
 
+// K-split scratch of `tiles` 256x256 tiles in `parts` parts: one fp32 slot
+// per tile and part, then one counter per tile.
+static size_t split_slots_bytes(int tiles, int parts) { return (size_t)tiles * parts * 256 * 256 * sizeof(float); }
+static size_t split_scratch_bytes(int tiles, int parts) {
+  return parts ? split_slots_bytes(tiles, parts) + (size_t)tiles * sizeof(int) : 0;
+}
+static KSplit split_of(void* scratch, int tiles, int parts, int kchunk) {
+  return KSplit{(float*)scratch, (int*)((char*)scratch + split_slots_bytes(tiles, parts)), parts, kchunk};
+}
+
 size_t attn_qkv_scratch_bytes(int M, int h, int nqkv) {
-  return (size_t)attn_qkv_splits(M, h, nqkv) * (size_t)M * (size_t)nqkv * 4u;
+  const int tiles = ((M + 255) / 256) * ((nqkv + 255) / 256);
+  return split_scratch_bytes(tiles, attn_qkv_splits(M, h, nqkv));
 }
 
 hipError_t attn_qkv_fwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
                         int64_t ldw, void* QKV, int64_t ldqkv, void* scratch, hipStream_t s) {
   const int splits = attn_qkv_splits(M, h, nqkv);
-  if (splits && scratch) {
-    float* part = (float*)scratch;
-    const EpiPartialF32 e{part, nqkv, (int64_t)M * nqkv, M, nqkv};
-    const hipError_t err = launch_gemm_pp_splitk(
-        pp_problem<256, 256, true, false>((const bf16*)X, ldx, (const bf16*)W, ldw, M, nqkv, h, e), splits,
-        qkv_kchunk(h, splits), s);
-    if (err != hipSuccess) return err;
-    return splitk_sum(part, splits, M, nqkv, QKV, ldqkv, s);
-  }
   const EpiStore<bf16> e{(bf16*)QKV, ldqkv, M, nqkv};
+  if (splits && scratch) {
+    const auto p = pp_problem<256, 256, true, false>((const bf16*)X, ldx, (const bf16*)W, ldw, M, nqkv, h, e);
+    return launch_gemm_pp_ksplit(p, split_of(scratch, p.tiles(), splits, qkv_kchunk(h, splits)), s);
+  }
   return gemm_bf16<true, false>(pick_tile(M, nqkv), (const bf16*)X, ldx, (const bf16*)W, ldw, M, nqkv,
                                 h, e, s);
 }
@@ -105,8 +112,8 @@ hipError_t attn_qkv_bwd(int M, int h, int nqkv, const void* X, int64_t ldx, cons
 // The output projection's backward at the 70B shape: dA (4096 x 1024, K =
 // h = 8192) is 64 tiles and dW_O (1024 x 8192, K = 4096) 128, so one grouped
 // launch leaves a quarter of the chip idle while the dA tiles, twice as long,
-// finish.  Splitting dA's K in two makes 256 tiles of equal length: both
-// halves write fp32 partials, summed into dA afterwards.
+// finish.  Splitting dA's K in two makes 256 blocks of equal length; the two
+// halves of a dA tile are reduced inside the launch.
 bool attn_out_bwd_split(int M, int hq, int h) {
   if (M < 256 || hq < 256 || h < 4096 || h % 64 != 0) return false;
   const int ta = ((M + 255) / 256) * ((hq + 255) / 256);
@@ -115,7 +122,8 @@ bool attn_out_bwd_split(int M, int hq, int h) {
 }
 
 size_t attn_out_bwd_scratch_bytes(int M, int hq, int h) {
-  return attn_out_bwd_split(M, hq, h) ? 2 * (size_t)M * (size_t)hq * 4u : 0;
+  const int ta = ((M + 255) / 256) * ((hq + 255) / 256);
+  return split_scratch_bytes(ta, attn_out_bwd_split(M, hq, h) ? 2 : 0);
 }
 
 hipError_t attn_out_bwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,
@@ -124,19 +132,12 @@ hipError_t attn_out_bwd(int M, int hq, int h, const void* A, int64_t lda, const 
   if (scratch && attn_out_bwd_split(M, hq, h)) {
     // dA = dZ W_O^T over K = h in two halves (both operands K-contiguous, so a
     // half is the operands moved by h/2 columns), and dW_O = A^T dZ.
-    float* part = (float*)scratch;
-    const int half = h / 2;
-    const EpiPartialF32 e0{part, hq, (int64_t)M * hq, M, hq};
-    const EpiPartialF32 e1{part + (int64_t)M * hq, hq, (int64_t)M * hq, M, hq};
-    const bf16 *dz = (const bf16*)dZ, *wo = (const bf16*)Wo;
-    const hipError_t err = launch_gemm_pp_group3(
-        pp_problem<256, 256, true, true>(dz, lddz, wo, ldwo, M, hq, half, e0),
-        pp_problem<256, 256, true, true>(dz + half, lddz, wo + half, ldwo, M, hq, h - half, e1),
-        pp_problem<256, 256, false, false>((const bf16*)A, lda, dz, lddz, hq, h, M,
-                                           EpiStore<bf16>{(bf16*)dWo, lddwo, hq, h}),
-        s);
-    if (err != hipSuccess) return err;
-    return splitk_sum(part, 2, M, hq, dA, ldda, s);
+    const bf16* dz = (const bf16*)dZ;
+    const auto pa = pp_problem<256, 256, true, true>(dz, lddz, (const bf16*)Wo, ldwo, M, hq, h,
+                                                     EpiStore<bf16>{(bf16*)dA, ldda, M, hq});
+    const auto pw = pp_problem<256, 256, false, false>((const bf16*)A, lda, dz, lddz, hq, h, M,
+                                                       EpiStore<bf16>{(bf16*)dWo, lddwo, hq, h});
+    return launch_gemm_pp_group2_ksplit(pa, pw, split_of(scratch, pa.tiles(), 2, h / 2), s);
   }
   return input_and_weight_grads((const bf16*)dZ, lddz, (const bf16*)Wo, ldwo, M, hq, h,
                                 EpiStore<bf16>{(bf16*)dA, ldda, M, hq}, (const bf16*)A, lda,

@@ -102,27 +102,6 @@ struct EpiGeluBwd {
   }
 };
 
-// fp32 partial of one K range of a split-K GEMM: slice s of [splits][M][ldw].
-struct EpiPartialF32 {
-  static constexpr bool kDirect = false, kLoads = false;
-  float* W;
-  int64_t ldw, slice;  // row pitch and slice pitch (floats)
-  int M, N;
-  void debug_spans(int) const { LGS_NEED(W, debug::mat_bytes(M, ldw, N, 4), "EpiPartialF32 slice"); }
-  __host__ __device__ __forceinline__ EpiPartialF32 split(int s) const {
-    EpiPartialF32 e = *this;
-    e.W = W + (int64_t)s * slice;
-    return e;
-  }
-  __device__ __forceinline__ bf16x8 load8(int, int) const { return bf16x8{}; }
-  __device__ __forceinline__ void apply8(int m, int n, const float* v, bf16x8) const {
-    if (m >= M || n >= N) return;
-    f32x4* p = reinterpret_cast<f32x4*>(W + (int64_t)m * ldw + n);
-    p[0] = f32x4{v[0], v[1], v[2], v[3]};
-    p[1] = f32x4{v[4], v[5], v[6], v[7]};
-  }
-};
-
 // ---------------------------------------------------------------- SwiGLU
 //
 // The mohashari.github.io page on tensor parallelism for fine-tuning 70B

@@ -512,39 +512,6 @@ void gemm_pp_group3_kernel(P0 p0, P1 p1, P2 p2) {
   }
 }
 
-// Split-K: block b works on tile b % tiles over K range
-// [s * kchunk, min(K, (s + 1) * kchunk)), s = b / tiles, with the epilogue's
-// `split(s)` (e.g. a partial-sum slice per s).  kchunk is a multiple of the
-// 32-wide K tile; the operands move to the range's start (K-contiguous A by
-// elements, N-contiguous B by rows), so each range is an ordinary GEMM.
-template <class P>
-__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_pp_splitk_kernel(P p, int kchunk) {
-  static_assert(P::AK && !P::BK, "split-K is built for K-contiguous A and N-contiguous B");
-  __shared__ __attribute__((aligned(1024))) char smem[P::T::kLdsBytes];
-  const int tiles = p.tiles();
-  const int s = blockIdx.x / tiles, b = blockIdx.x - s * tiles;
-  P q = p;
-  const int k0 = s * kchunk;
-  q.A = p.A + k0;
-  q.B = p.B + (int64_t)k0 * p.ldb;
-  q.K = min(kchunk, p.K - k0);
-  q.epi = p.epi.split(s);
-  int tmi, tni;
-  tile_of_block(b, tiles, q.tiles_m(), q.tiles_n(), tmi, tni);
-  gemm_tile_pp(q, smem, tmi, tni);
-}
-
-template <class P>
-inline hipError_t launch_gemm_pp_splitk(const P& p, int splits, int kchunk, hipStream_t stream) {
-  debug_problem(p);                 // the operands and slice 0
-  p.epi.split(splits - 1).debug_spans(P::BN);  // the last slice
-  LGS_CHECK(splits >= 1 && kchunk % kBK == 0 && (int64_t)(splits - 1) * kchunk < p.K &&
-            (int64_t)splits * kchunk >= p.K);
-  LGS_LAUNCH((gemm_pp_splitk_kernel<P>), dim3(p.tiles() * splits), dim3(kPPThreads), 0, stream, p, kchunk);
-  return LGS_LAUNCH_STATUS();
-}
-
 // The problem restricted to K range [k0, k0 + kc): both operands move to the
 // range's first K row or column, so the range is an ordinary GEMM.
 template <class P>
@@ -665,6 +632,62 @@ inline hipError_t launch_gemm_pp_group3_tail(const P0& p0, const P1& p1, const P
   LGS_LAUNCH((gemm_pp_group3_tail_kernel<P0, P1, P2>),
              dim3(p0.tiles() + p1.tiles() - tail + p2.tiles() + tail * k.parts), dim3(kPPThreads), 0, stream, p0,
              p1, p2, k, tail);
+  return LGS_LAUNCH_STATUS();
+}
+
+// Every tile of p split over K into k.parts parts (blocks part-major),
+// reduced inside the launch (KPartFix): slot and counter t belong to tile t.
+template <class P>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_ksplit_kernel(P p, KSplit k) {
+  __shared__ __attribute__((aligned(1024))) char smem[P::T::kLdsBytes];
+  run_k_part(p, k, 0, blockIdx.x, smem);
+}
+
+template <class P>
+inline hipError_t launch_gemm_pp_ksplit(const P& p, const KSplit& k, hipStream_t stream) {
+  const int tiles = p.tiles();
+  debug_problem(p);
+  LGS_CHECK(k.parts >= 2 && k.kchunk % kBK == 0 && (int64_t)(k.parts - 1) * k.kchunk < p.K &&
+            (int64_t)k.parts * k.kchunk >= p.K);
+  LGS_NEED(k.part, (size_t)tiles * k.parts * P::BM * P::BN * 4, "K-split partial slots");
+  LGS_NEED(k.count, (size_t)tiles * 4, "K-split counters");
+  LGS_LAUNCH(zero_i32_kernel, dim3((tiles + 255) / 256), dim3(256), 0, stream, k.count, tiles);
+  LGS_LAUNCH((gemm_pp_ksplit_kernel<P>), dim3(tiles * k.parts), dim3(kPPThreads), 0, stream, p, k);
+  return LGS_LAUNCH_STATUS();
+}
+
+// Two GEMMs in one launch, every tile of p0 split over K (part-major blocks
+// first), p1's tiles unsplit after them.
+template <class P0, class P1>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_group2_ksplit_kernel(P0 p0, P1 p1, KSplit k) {
+  constexpr int kL = P0::T::kLdsBytes > P1::T::kLdsBytes ? P0::T::kLdsBytes : P1::T::kLdsBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kL];
+  int pid = blockIdx.x;
+  const int t0 = p0.tiles();
+  if (pid < t0 * k.parts) {
+    run_k_part(p0, k, 0, pid, smem);
+  } else {
+    pid -= t0 * k.parts;
+    int tmi, tni;
+    tile_of_block(pid, p1.tiles(), p1.tiles_m(), p1.tiles_n(), tmi, tni);
+    gemm_tile_pp(p1, smem, tmi, tni);
+  }
+}
+
+template <class P0, class P1>
+inline hipError_t launch_gemm_pp_group2_ksplit(const P0& p0, const P1& p1, const KSplit& k, hipStream_t stream) {
+  const int tiles = p0.tiles();
+  debug_problem(p0);
+  debug_problem(p1);
+  LGS_CHECK(k.parts >= 2 && k.kchunk % kBK == 0 && (int64_t)(k.parts - 1) * k.kchunk < p0.K &&
+            (int64_t)k.parts * k.kchunk >= p0.K);
+  LGS_NEED(k.part, (size_t)tiles * k.parts * P0::BM * P0::BN * 4, "K-split partial slots");
+  LGS_NEED(k.count, (size_t)tiles * 4, "K-split counters");
+  LGS_LAUNCH(zero_i32_kernel, dim3((tiles + 255) / 256), dim3(256), 0, stream, k.count, tiles);
+  LGS_LAUNCH((gemm_pp_group2_ksplit_kernel<P0, P1>), dim3(tiles * k.parts + p1.tiles()), dim3(kPPThreads), 0,
+             stream, p0, p1, k);
   return LGS_LAUNCH_STATUS();
 }
 

@@ -62,21 +62,21 @@ hipError_t swiglu_bwd(int M, int h, int f, const void* X, int64_t ldx, const voi
 
 // One rank's attention projections (bf16): nqkv = (n_q + 2 n_kv) d / t
 // columns of [Q | K | V], hq = n_q d / t columns of the heads' outputs.
-// Split-K schedule of the QKV projection: the slices (0 = unsplit) and the
-// fp32 scratch they need; the projection runs unsplit when scratch is null.
+// Split-K schedule of the QKV projection: the parts (0 = unsplit) and the
+// scratch their in-launch reduction needs (fp32 slots and counters); the
+// projection runs unsplit when scratch is null.
 int attn_qkv_splits(int M, int h, int nqkv);
 size_t attn_qkv_scratch_bytes(int M, int h, int nqkv);
 hipError_t attn_qkv_fwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
                         int64_t ldw, void* QKV, int64_t ldqkv, void* scratch, hipStream_t s);
-// bf16 out = sum of a split-K GEMM's fp32 partial slices [splits][M][N].
-hipError_t splitk_sum(const float* W, int splits, int M, int N, void* out, int64_t ldo, hipStream_t s);
 hipError_t attn_out_fwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,
                         int64_t ldwo, void* Z, int64_t ldz, hipStream_t s);
 hipError_t attn_qkv_bwd(int M, int h, int nqkv, const void* X, int64_t ldx, const void* W,
                         int64_t ldw, const void* dQKV, int64_t lddqkv, void* dX, int64_t lddx,
                         void* dW, int64_t lddw, hipStream_t s);
-// The output projection's backward splits dA's K in two (fp32 scratch) when
-// that fills the chip; unsplit when scratch is null.
+// The output projection's backward splits dA's K in two (reduced inside the
+// launch: fp32 slots and counters in scratch) when that fills the chip;
+// unsplit when scratch is null.
 bool attn_out_bwd_split(int M, int hq, int h);
 size_t attn_out_bwd_scratch_bytes(int M, int hq, int h);
 hipError_t attn_out_bwd(int M, int hq, int h, const void* A, int64_t lda, const void* Wo,

@@ -180,50 +180,6 @@ hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64
   return LGS_LAUNCH_STATUS();
 }
 
-// out[m, n] = bf16(sum_s W[s][m][n]) for a split-K GEMM's fp32 partials
-// (W rows of pitch N, slices of M*N), 8 columns per thread; N % 8 == 0.
-constexpr int kSplitChunk = 4;
-__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ W, int splits, int M,
-                                                         int N, bf16* __restrict__ out, int64_t ldo) {
-  const int64_t n8 = N / 8, total = (int64_t)M * n8;
-  const int64_t slice = (int64_t)M * N;
-  const int64_t step = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += step) {
-    const int64_t m = i / n8, c = (i - m * n8) * 8;
-    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < splits; s0 += kSplitChunk) {  // a chunk's loads issued together
-      u32x4 lo[kSplitChunk], hi[kSplitChunk];
-#pragma unroll
-      for (int k = 0; k < kSplitChunk; ++k)
-        if (s0 + k < splits) {
-          const float* p = W + (s0 + k) * slice + m * N + c;
-          lo[k] = ld_nt(p);
-          hi[k] = ld_nt(p + 4);
-        }
-#pragma unroll
-      for (int k = 0; k < kSplitChunk; ++k)
-        if (s0 + k < splits)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] += __uint_as_float(lo[k][e]);
-            a[4 + e] += __uint_as_float(hi[k][e]);
-          }
-    }
-    Vec8<bf16>::store(out + m * ldo + c, a);
-  }
-}
-
-hipError_t splitk_sum(const float* W, int splits, int M, int N, void* out, int64_t ldo, hipStream_t s) {
-  const int64_t total = (int64_t)M * (N / 8);
-  const int64_t want = (total + 255) / 256;
-  const int blocks = (int)(want < 4096 ? (want < 1 ? 1 : want) : 4096);
-  LGS_CHECK(splits >= 1 && M >= 1 && N % 8 == 0);
-  LGS_NEED(W, (size_t)splits * M * N * 4, "split-K partial slices");
-  LGS_NEED(out, debug::mat_bytes(M, ldo, N, 2), "split-K sum");
-  LGS_LAUNCH(splitk_sum_kernel, dim3(blocks), dim3(256), 0, s, W, splits, M, N, (bf16*)out, ldo);
-  return LGS_LAUNCH_STATUS();
-}
-
 // parts: rank r's block at parts + r*stride holds m[n], l[n], T[n] (T is not
 // read for the log-sum-exp alone).
 // Ranks are taken in chunks of kCombineChunk whose loads are all issued

@@ -315,11 +315,12 @@ def test_attn_validation(L):
     assert qf(rank=2) == 1
     assert qf(nq=7, ws=FAKE + 64, wsb=1 << 20) == 1  # shape errors come first
     assert qf(d=12, ws=FAKE + 64, wsb=1 << 20) == 2
-    # the split-K workspace: none for small shapes, fp32 slices for the 70B rank
-    # (4096 x 1280 outputs, K = 8192: 80 tiles of 256x256 -> 3 slices)
+    # the split-K workspace: none for small shapes; for the 70B rank (4096 x
+    # 1280 outputs, K = 8192: 80 tiles of 256x256 in 3 parts over K) one fp32
+    # 256x256 slot per tile and part, and one counter per tile
     ws = L.lgs_attn_qkv_fwd_workspace_bytes
     assert ws(1, 16, 64, 8, 4, 8, 2, 1) == 0
-    assert ws(1, 4096, 8192, 64, 8, 128, 8, 1) == 3 * 4096 * 1280 * 4
+    assert ws(1, 4096, 8192, 64, 8, 128, 8, 1) == (80 * 3 * 256 * 256 * 4 + 80 * 4 + 255) // 256 * 256
     assert ws(1, 4096, 8192, 64, 8, 128, 8, 0) == 0  # invalid (fp32): no workspace
     assert L.lgs_last_error() == b""
     of = lambda **kw: L.tp_attn_out_fwd(1, 16, 64, kw.get("nq", 8), 8, 2, kw.get("rank", 0), 1, FAKE,
@@ -328,8 +329,10 @@ def test_attn_validation(L):
     ob = L.tp_attn_out_bwd(1, 16, 64, 8, 8, 2, 0, 1, FAKE, 32, FAKE, 64, FAKE, 64, None, 32, FAKE, 64, None, 0,
                            None)
     assert ob == 1                          # dA_i required
-    # dA's split-K workspace at the 70B shape: two fp32 halves of [4096, 1024]
-    assert L.lgs_attn_out_bwd_workspace_bytes(1, 4096, 8192, 64, 128, 8, 1) == 2 * 4096 * 1024 * 4
+    # dA's split-K workspace at the 70B shape: [4096, 1024] is 64 tiles, each
+    # in two parts over K: two fp32 slots per tile, one counter per tile
+    assert L.lgs_attn_out_bwd_workspace_bytes(1, 4096, 8192, 64, 128, 8, 1) == \
+        (64 * 2 * 256 * 256 * 4 + 64 * 4 + 255) // 256 * 256
     assert L.lgs_attn_out_bwd_workspace_bytes(1, 16, 64, 8, 8, 2, 1) == 0
     qb = L.tp_attn_qkv_bwd(1, 16, 64, 8, 4, 8, 2, 0, 1, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 64, FAKE, 32, None)
     assert qb == 1                          # lddw < q + 2 kv

@@ -84,13 +84,15 @@ def test_attn_projections_ragged(shape):
 
 def test_attn_qkv_split_k_every_element():
     """A deep QKV product (h = 2600) with few output tiles runs split over K
-    (4 slices, the last one a partial K tile) when given its workspace: every
-    element against the oracle, and against the unsplit run (same values up to
-    the fp32 summation order)."""
+    (4 parts, the last one with a partial K tile, reduced inside the launch)
+    when given its workspace: every element against the oracle, and against
+    the unsplit run (same values up to the fp32 summation order)."""
     b, s, h, n_q, n_kv, d, t = 1, 600, 2600, 8, 4, 128, 2
     M, q, kv = b * s, n_q // t * d, n_kv // t * d
     dev_ = dev()
-    assert lgs.attn_qkv_fwd_workspace_bytes(b, s, h, n_q, n_kv, d, t) == 4 * M * (q + 2 * kv) * 4
+    tiles = -(-M // 256) * -(-(q + 2 * kv) // 256)  # 3 x 4 tiles of 256x256, 4 fp32 slots each
+    assert lgs.attn_qkv_fwd_workspace_bytes(b, s, h, n_q, n_kv, d, t) == \
+        (tiles * 4 * 256 * 256 * 4 + tiles * 4 + 255) // 256 * 256
     X, Wq, Wk, Wv = synth.small(21, (M, h), (h, n_q * d), (h, n_kv * d), (h, n_kv * d), dtype="bf16")
     Wq, Wk, Wv = ((w.float() * 0.03).to(BF16) for w in (Wq, Wk, Wv))
     W = synth.qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, 1)
@@ -109,12 +111,14 @@ def test_attn_qkv_split_k_every_element():
 
 def test_attn_out_bwd_split_k_every_element():
     """The output projection's backward with dA split over K in two (few dA
-    tiles, h = 4096): every element of dA and dW_O against the oracle and
-    against the unsplit run."""
+    tiles, h = 4096; the halves reduced inside the launch): every element of
+    dA and dW_O against the oracle and against the unsplit run."""
     b, s, h, n_q, d, t = 1, 520, 4096, 8, 128, 2
     M, q = b * s, n_q // t * d
     dev_ = dev()
-    assert lgs.attn_out_bwd_workspace_bytes(b, s, h, n_q, d, t) == 2 * M * q * 4
+    tiles = -(-M // 256) * -(-q // 256)  # 3 x 2 dA tiles of 256x256, two fp32 slots each
+    assert lgs.attn_out_bwd_workspace_bytes(b, s, h, n_q, d, t) == \
+        (tiles * 2 * 256 * 256 * 4 + tiles * 4 + 255) // 256 * 256
     A, Wo, dZ = synth.small(23, (M, q), (n_q * d, h), (M, h), dtype="bf16")
     Wo_r = (Wo[q:2 * q].float() * 0.05).to(BF16).contiguous()
     step("attn out-proj backward split-K vs unsplit vs oracle")
