@@ -240,35 +240,66 @@ hbm_bytes_per_call: {nbytes(0) + nbytes(1):.0f}
 XENT_COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_8p3b_hbm_counters.txt")
 
 
+def panel_fill_model(tiles_m, tiles_n, bm, bn, k_bytes, xcds=8, group_m=4, cus=256):
+    """L2 fills of one launch if every XCD's L2 fetches, per round of its
+    concurrent tiles, each operand panel those tiles cover once: blocks go to
+    XCDs round-robin, each XCD owns a contiguous run of the grouped tile order
+    (the library's block-to-tile map), and a round is 256 blocks.  Returns
+    bytes."""
+    n = tiles_m * tiles_n
+    per = n // xcds if n % xcds == 0 else None
+
+    def tile(pid):
+        if per is not None:
+            pid = (pid % xcds) * per + pid // xcds
+        width = group_m * tiles_n
+        g, first = pid // width, (pid // width) * group_m
+        gsz = min(tiles_m - first, group_m)
+        inn = pid - g * width
+        return first + inn % gsz, inn // gsz
+    total = 0
+    for r0 in range(0, n, cus):
+        for x in range(xcds):
+            ts = [tile(p) for p in range(r0, min(n, r0 + cus)) if p % xcds == x]
+            total += (len({t[0] for t in ts}) * bm + len({t[1] for t in ts}) * bn) * k_bytes
+    return total
+
+
 def ce_counter_summary(d, fr, fw):
     """The fused CE's share of the same counter passes (the step runs it on
-    slice 0 of the 8.3B shapes), next to a model of its L2 fills: each XCD
-    fetches, per round of its 32 concurrent tiles, the H row panels and E_r
-    column panels those tiles cover, once each (K = 3072 bf16: 6144 bytes per
-    panel row or column)."""
+    slice 0 of the 8.3B shapes), next to panel_fill_model for each of its
+    two GEMM launches (K = 3072 bf16: 6144 bytes per panel row or column)."""
     import statistics
 
     def csv_of(sub):
         return glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)[0]
-    kern = {"main": "320, true, true, lgs::EpiXent", "tail": "160, 4, true, true, lgs::EpiXent",
-            "merge": "xent_merge_kernel"}
+    launches = []  # (kernel name pattern, label, columns, bm, bn)
+    for pat, label, cols, bm, bn in (("256, 320, true, true, lgs::EpiXent>", "256x320 launch (columns 0-2559)", 2560, 256, 320),
+                                      ("256, 256, true, true, lgs::EpiXent>", "256x256 launch (columns 2560-6399)", 3840, 256, 256)):
+        launches.append((pat, label, cols, bm, bn))
     med = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         step = _per_kernel(csv_of(f"pmc_{c}"), c)
-        for key, pat in kern.items():
+        for pat, label, *_ in launches + [("xent_merge_kernel", "merge", 0, 0, 0)]:
             v = [x for n, x in step.items() if pat in n]
             if len(v) != 1:
-                raise SystemExit(f"{c}: expected one {key} kernel of the CE, found {len(v)}")
-            med[(c, key)] = statistics.median(v[0])
+                raise SystemExit(f"{c}: expected one CE kernel matching {pat!r}, found {len(v)}")
+            med[(c, label)] = statistics.median(v[0])
 
-    def mb(key):
-        return (med[("FETCH_SIZE", key)] * 1024 * fr + med[("WRITE_SIZE", key)] * 1024 * fw) / 1e6
-    panel = 3072 * 2
-    main_model = 8 * 2 * (4 * 256 + 8 * 320) * panel / 1e6    # 8 XCDs x 2 rounds, 4 x 8 tiles each
-    tail_model = 8 * 1 * (4 * 256 + 8 * 160) * panel / 1e6    # 8 XCDs x 1 round, 4 x 8 tiles each
-    best_main = 8 * 2 * (8 * 256 + 4 * 320) * panel / 1e6     # the best 32-tile block per XCD (8 x 4)
+    def mb(label):
+        return (med[("FETCH_SIZE", label)] * 1024 * fr + med[("WRITE_SIZE", label)] * 1024 * fw) / 1e6
+    k_bytes = 3072 * 2
     alg = (8192 * 3072 + 6400 * 3072) * 2 / 1e6
+    rows = []
+    model_total = 0.0
+    for pat, label, cols, bm, bn in launches:
+        model = panel_fill_model(-(-8192 // bm), -(-cols // bn), bm, bn, k_bytes) / 1e6
+        model_total += model
+        rows.append(f"#   {label}: FETCH_SIZE {med[('FETCH_SIZE', label)]:.0f} KiB, WRITE_SIZE "
+                    f"{med[('WRITE_SIZE', label)]:.0f} KiB -> {mb(label):.1f} MB; panel model {model:.1f} MB")
+    best = panel_fill_model(32, 20, 256, 320, k_bytes, group_m=8) / 1e6  # all 6400 columns
     step_cmd = "python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-per-config --no-clock"
+    nl = chr(10)
     txt = f"""# L2-to-fabric traffic of the fused CE entry point (vocab_parallel_xent_fwd) on
 # the 8.3B-shape slice (rank 0 of t = 8: M = 8192 tokens, h = 3072, V_r = 6400),
 # from the same rocprofv3 counter passes over the step as
@@ -278,28 +309,28 @@ def ce_counter_summary(d, fr, fw):
 #   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/pmc_WRITE_SIZE -o p -- {step_cmd}
 #   (+ the two copy-calibration passes; python bench.py --counter-summary gpurun_out/pmc writes this file)
 #
-# Per launch (median of the dispatches), bytes = FETCH_SIZE x 1024 x {fr:.4f} + WRITE_SIZE x 1024 x {fw:.4f}:
-#   256x320 launch (columns 0-5119, 512 tiles, two rounds): FETCH_SIZE {med[('FETCH_SIZE', 'main')]:.0f} KiB, WRITE_SIZE {med[('WRITE_SIZE', 'main')]:.0f} KiB -> {mb('main'):.1f} MB
-#   256x160 launch (columns 5120-6399, 256 tiles, one round): FETCH_SIZE {med[('FETCH_SIZE', 'tail')]:.0f} KiB, WRITE_SIZE {med[('WRITE_SIZE', 'tail')]:.0f} KiB -> {mb('tail'):.1f} MB
-#   slab merge:                                 FETCH_SIZE {med[('FETCH_SIZE', 'merge')]:.0f} KiB, WRITE_SIZE {med[('WRITE_SIZE', 'merge')]:.0f} KiB -> {mb('merge'):.1f} MB
+# The library's column plan for this slice: columns 0-2559 on 256x320 tiles
+# (256 tiles, one round), columns 2560-6399 on 256x256 tiles (480 tiles).
+# Per launch (median of the dispatches), bytes = FETCH_SIZE x 1024 x {fr:.4f} + WRITE_SIZE x 1024 x {fw:.4f},
+# next to the panel model: per round of 256 blocks, each XCD's L2 fetches
+# every H row panel and E_r column panel of its 32 concurrent tiles once
+# (bench.panel_fill_model, from the library's block-to-tile map):
+{nl.join(rows)}
+#   slab merge: FETCH_SIZE {med[('FETCH_SIZE', 'merge')]:.0f} KiB, WRITE_SIZE {med[('WRITE_SIZE', 'merge')]:.0f} KiB -> {mb('merge'):.1f} MB
 #   algorithmic operand bytes (H and E_r read once): {alg:.1f} MB
 #
-# Model of the L2 fills: each XCD's 32 concurrent tiles are 4 row tiles x 8
-# column tiles of its contiguous block of the tile order, and per round its L2
-# fetches each of their H row panels and E_r column panels once:
-#   256x320 launch: 8 XCDs x 2 rounds x (4 x 256 + 8 x 320) panel lines x 6144 B = {main_model:.1f} MB
-#   256x160 launch: 8 XCDs x 1 round x (4 x 256 + 8 x 160) panel lines x 6144 B = {tail_model:.1f} MB
-# The counters match the model: the L2s fetch nothing twice within a round.
 # The traffic above the algorithmic bytes is the panels that the 8 XCDs'
 # separate L2s each fetch (served by the Infinity Cache, which holds H and E_r
-# whole).  No tile order brings it near the algorithmic bytes: with 32 tiles per
-# XCD per round the best block (8 row tiles x 4 column tiles) still fetches
-# {best_main:.1f} MB in the 256x320 launch alone, {best_main / alg:.1f}x the algorithmic bytes.
+# whole).  No tile order brings it near the algorithmic bytes: the whole slice
+# on 256x320 tiles with each XCD's concurrent tiles in the most compact block
+# (8 row tiles x 4 column tiles) would still fetch {best:.1f} MB, {best / alg:.1f}x
+# the algorithmic bytes.
 kernel_sources_sha256: {kernel_sources_digest()}
-hbm_bytes_per_launch: {(mb('main') + mb('tail') + mb('merge')) * 1e6:.0f}
+hbm_bytes_per_launch: {(sum(mb(l[1]) for l in launches) + mb('merge')) * 1e6:.0f}
 """
     open(XENT_COUNTERS_FILE, "w").write(txt)
     print(txt)
+
 
 
 def kernel_stats_md(src, title, cmd):
@@ -701,10 +732,10 @@ MFMA_KERNELS = (
     ("fwd GEMM2 (256x192, 512 tiles)", 77.309, ("Li256ELi192ELb1ELb0ENS_8EpiStore", "256, 192, true, false, lgs::EpiStore")),
     ("dY + GeLU' (256x192, 256 tiles)", 77.309, ("Li256ELi192ELb1ELb1ENS_10EpiGeluBwd", "256, 192, true, true, lgs::EpiGeluBwd")),
     ("group3 dB, dA, dX (256x256, 528 tiles)", 231.928, ("gemm_pp_group3_kernel",)),
-    ("CE logit GEMM + slabs, first 5120 columns (256x320, 512 tiles)", 257.698,
+    ("CE logit GEMM + slabs, columns 0-2559 (256x320, 256 tiles)", 128.849,
      ("Li256ELi320ELb1ELb1ENS_7EpiXent", "256, 320, true, true, lgs::EpiXent")),
-    ("CE logit GEMM + slabs, last 1280 columns (256x160, 256 tiles)", 64.425,
-     ("Li256ELi160ELi4ELb1ELb1ENS_7EpiXent", "256, 160, 4, true, true, lgs::EpiXent")),
+    ("CE logit GEMM + slabs, columns 2560-6399 (256x256, 480 tiles)", 193.274,
+     ("Li256ELi256ELb1ELb1ENS_7EpiXent", "256, 256, true, true, lgs::EpiXent")),
 )
 
 

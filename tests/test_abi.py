@@ -224,8 +224,8 @@ def test_xent_validation(L):
     assert xe(ws_bytes=16) == 3
     assert xe(lde=32) == 1
     # one 16-byte entry per token and slab written: the 8.3B slice (6400 columns)
-    # runs 5120 columns on 256x320 tiles (32 slabs of 160) and 1280 on 256x192
-    # (7 tiles of two 96-column slabs: 14)
+    # runs 2560 columns on 256x320 tiles (16 slabs of 160) and 3840 on 256x256
+    # (30 slabs of 128)
     assert L.lgs_xent_workspace_bytes(8, 1024, 3072, 51200, 8, 1) == 46 * 8192 * 16
 
 
