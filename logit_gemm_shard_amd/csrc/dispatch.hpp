@@ -64,10 +64,11 @@ inline double tile_cost(TileId t, int M, int N) {
 // c1 < N) a second launch with another tile on [c1, N).  Splitting pays when
 // the picked tile leaves a partly filled last round that smaller tiles on the
 // remaining columns fill: e.g. 8192 x 6400 is 640 blocks of 256x320 (2.5
-// rounds, cost 3), but 512 of them on the first 5120 columns (2 full rounds)
-// and 256 blocks of 256x160 on the last 1280 (one round of half-size tiles)
-// cost about 2.7.  Both launches' tiles must share `wn` (the caller's slab
-// numbering) when the caller needs it; `same_wn` enforces that.
+// rounds, cost 3 rounds of 256x320), but 256 of them on the first 2560
+// columns (one full round) and 480 blocks of 256x256 on the other 3840 (two
+// rounds of smaller tiles) cost about 2.6.  Both launches' tiles must share
+// `wn` (the caller's slab numbering) when the caller needs it; `same_wn`
+// enforces that.
 struct ColumnPlan {
   TileId main;
   int c1;  // columns of the first launch (a multiple of its tile width), N if not split

@@ -15,9 +15,9 @@
 namespace lgs {
 
 // The launch plan: the slice's columns in one launch, or two (plan_columns),
-// on the ping-pong tiles (e.g. 8192 x 6400: 5120 columns on 256x320, the last
-// 1280 on 256x192).  Each launch numbers its slabs from where the previous
-// one ended, with its own wave width.
+// on the ping-pong tiles (e.g. 8192 x 6400: the first 2560 columns on
+// 256x320, the other 3840 on 256x256).  Each launch numbers its slabs from
+// where the previous one ended, with its own wave width.
 static ColumnPlan xent_plan(int M, int Vr) { return plan_columns(M, Vr, false, kPPTiles); }
 
 // Slabs the launch plan writes: every wave column of every tile writes one

@@ -351,7 +351,7 @@ def test_xent_small_all_ranks(shape):
 
 def test_xent_two_launch_plan_every_element():
     """A slice wide enough that the launch plan splits its columns (the first
-    19520 on 256x320 tiles in 2 full rounds, the rest on 256x160 tiles): every
+    8320 on 256x320 tiles in one full round, the rest on 256x256 tiles): every
     token's partials, first argmax and loss against the oracle, with a K tail
     (h = 136) and a ragged row count; targets chosen on both sides of the
     split and on its boundary."""
@@ -362,7 +362,7 @@ def test_xent_two_launch_plan_every_element():
     E = (E.float() * 0.3).to(BF16)
     g = torch.Generator().manual_seed(11)
     y = torch.randint(0, V, (M,), generator=g, dtype=torch.int64).to(torch.int32)
-    y[:6] = torch.tensor([19519, 19520, 19521, 0, V - 1, 19680], dtype=torch.int32)
+    y[:6] = torch.tensor([8319, 8320, 8321, 0, V - 1, 8448], dtype=torch.int32)  # 8448: a slab edge of the second launch
     step("xent t=1, slice split over two launches: every element")
     m = torch.empty(M, dtype=F32, device=d)
     l, T, loss = torch.empty_like(m), torch.empty_like(m), torch.empty_like(m)
