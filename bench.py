@@ -205,11 +205,11 @@ def counter_summary(d):
 # 70B-shape workload (rank 0 of t = 8: M = 4096 tokens, h = 8192, f = 3584),
 # from rocprofv3 counter passes, one counter per run:
 #
-#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/pmc_FETCH_SIZE -o p -- {step_cmd}
-#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/pmc_WRITE_SIZE -o p -- {step_cmd}
-#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/pmc_copy_FETCH_SIZE -o p -- python bench.py --copy-calibration
-#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/pmc_copy_WRITE_SIZE -o p -- python bench.py --copy-calibration
-#   python bench.py --counter-summary gpurun_out/pmc      (writes this file)
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc/pmc_FETCH_SIZE -o p -- {step_cmd}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc/pmc_WRITE_SIZE -o p -- {step_cmd}
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc/pmc_copy_FETCH_SIZE -o p -- python bench.py --copy-calibration
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc/pmc_copy_WRITE_SIZE -o p -- python bench.py --copy-calibration
+#   python bench.py --counter-summary rocprof_out/pmc      (writes this file)
 #
 # Calibration: an elementwise pass over 1 GiB (torch.neg: reads 1 GiB, writes
 # 1 GiB) reads FETCH_SIZE = {med['FETCH_SIZE'][2]:.0f} KiB and WRITE_SIZE = {med['WRITE_SIZE'][2]:.0f} KiB per dispatch, so
@@ -305,9 +305,9 @@ def ce_counter_summary(d, fr, fw):
 # from the same rocprofv3 counter passes over the step as
 # mlp_70b_bwd_hbm_counters.txt (one counter per run):
 #
-#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/pmc_FETCH_SIZE -o p -- {step_cmd}
-#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/pmc_WRITE_SIZE -o p -- {step_cmd}
-#   (+ the two copy-calibration passes; python bench.py --counter-summary gpurun_out/pmc writes this file)
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc/pmc_FETCH_SIZE -o p -- {step_cmd}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc/pmc_WRITE_SIZE -o p -- {step_cmd}
+#   (+ the two copy-calibration passes; python bench.py --counter-summary rocprof_out/pmc writes this file)
 #
 # The library's column plan for this slice: columns 0-2559 on 256x320 tiles
 # (256 tiles, one round), columns 2560-6399 on 256x256 tiles (480 tiles).
@@ -814,9 +814,9 @@ The MLP forward and backward and the fused CE of slice 0, five calls each on thr
 sets (`bench.py --mfma-workload`), under two counter passes, one counter set per run:
 
 ```
-rocprofv3 --pmc {MFMA_PASSES[0]} --output-format csv -d gpurun_out/pmc/pmc_mfma_A -o p -- {cmd}
-rocprofv3 --pmc {MFMA_PASSES[1]} --output-format csv -d gpurun_out/pmc/pmc_mfma_B -o p -- {cmd}
-python bench.py --mfma-summary gpurun_out/pmc      (writes this file)
+rocprofv3 --pmc {MFMA_PASSES[0]} --output-format csv -d rocprof_out/pmc/pmc_mfma_A -o p -- {cmd}
+rocprofv3 --pmc {MFMA_PASSES[1]} --output-format csv -d rocprof_out/pmc/pmc_mfma_B -o p -- {cmd}
+python bench.py --mfma-summary rocprof_out/pmc      (writes this file)
 ```
 
 Medians over the launches of each kernel. Counter values are summed over the 8 XCDs. Durations
