@@ -16,11 +16,13 @@
 // ([8192, 6400], three rotating buffers): 21.7 us (7 chunks per batch, no
 // prefetch, register pick) -> 19.2-19.5 us (5 per batch, prefetch) ->
 // 18.7-19.0 us (7 per batch: a row is two batches, the second 79% full,
-// instead of 2.5).  A probe without the exponentials (wrong results) takes
-// 18.1-18.2 us, so the per-logit arithmetic costs about 4%.  Variants that
-// measured slower: 4, 8, 10 or 13 chunks per batch, 4 or 16 rows per
-// block, two alternating register sets instead of copying the prefetched
-// batch.
+// instead of 2.5) -> 18.67 us against 18.86 (best of ten, alternating:
+// bounds checks only in a row's last, partial batch).  A probe without the
+// exponentials (wrong results) takes 18.1-18.2 us, so the per-logit
+// arithmetic costs about 4%.  Variants that measured slower: 4, 5, 6, 8, 10
+// or 13 chunks per batch, 4 or 16 rows per block, two alternating register
+// sets instead of copying the prefetched batch, the last batch specialised
+// by its length (seven copies of the row loop).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -42,24 +44,37 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void xent_rows_kernel(
   if (row >= M) return;  // whole waves only
   const bf16* z = Z + (int64_t)row * ldz;
   const int nchunk = Vr / 8;
-  auto load = [&](int base, u32x4 (&dst)[kBatch]) {
+  // Batches that lie wholly inside the row load without bounds checks; only
+  // the last, partial one checks each chunk (and pads with -inf).
+  auto load = [&](int base, u32x4 (&dst)[kBatch], auto checked_c) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int c = base + lane + 64 * u;
-      dst[u] = c < nchunk ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + 8 * c))
-                          : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};  // bf16 -inf
+      if constexpr (decltype(checked_c)::value)
+        dst[u] = c < nchunk ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + 8 * c))
+                            : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};  // bf16 -inf
+      else
+        dst[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + 8 * c));
     }
+  };
+  const int nfull = nchunk / (64 * kBatch);
+  const int nbatch = (nchunk + 64 * kBatch - 1) / (64 * kBatch);
+  auto load_batch = [&](int b, u32x4 (&dst)[kBatch]) {
+    if (b < nfull)
+      load(64 * kBatch * b, dst, std::false_type{});
+    else
+      load(64 * kBatch * b, dst, std::true_type{});
   };
   float m = -INFINITY, l = 0.f;
   // Batches combine with the online identity l' = l exp(m - m') + sum exp(z - m'):
   // one max pass over a batch's registers, then one sum pass with a single shift.
   u32x4 next[kBatch];
-  load(0, next);
-  for (int base = 0; base < nchunk; base += 64 * kBatch) {
+  if (nbatch > 0) load_batch(0, next);
+  for (int b = 0; b < nbatch; ++b) {
     u32x4 raw[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) raw[u] = next[u];
-    if (base + 64 * kBatch < nchunk) load(base + 64 * kBatch, next);
+    if (b + 1 < nbatch) load_batch(b + 1, next);
     float bm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {

@@ -690,7 +690,10 @@ def _rows_partials(Z, y, start):
     return out.cpu()
 
 
-@pytest.mark.parametrize("M,Vr,start", [(300, 1000, 0), (65, 6400, 6400), (1, 8, 3)])
+# Vr / 8 chunks per row against 448 per batch: a tail alone (1000), one full batch and a tail
+# (6400, 3592), two full batches and no tail (7168), one chunk (8)
+@pytest.mark.parametrize("M,Vr,start", [(300, 1000, 0), (65, 6400, 6400), (17, 3592, 0), (70, 7168, 7168),
+                                        (1, 8, 3)])
 def test_xent_rows_match_oracle_slice_partials(M, Vr, start):
     """bf16 logits of H E_r^T (ragged row counts, chunk counts that are not a
     multiple of the wave) -> the oracle's slice partials on the same logits."""
