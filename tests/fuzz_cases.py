@@ -1,0 +1,49 @@
+"""Seeded random shapes for the randomized parity tests (test_gpu_fuzz.py)
+and the debug build's bounds checks (test_debug_build.py).  Plain Python and
+numpy only: importing this module draws the same cases every time."""
+
+import numpy as np
+
+_rng = np.random.default_rng(20261202)
+
+
+def _w8(lo, hi):
+    """A width in [lo, hi], a multiple of 8 (16-byte bf16 rows)."""
+    return 8 * int(_rng.integers(lo // 8, hi // 8 + 1))
+
+
+def _tokens():
+    """(b, s): mostly ragged counts, some single tokens and exact multiples of 256."""
+    kind = _rng.integers(0, 6)
+    if kind == 0:
+        return 1, 1
+    if kind == 1:
+        return 1, 256 * int(_rng.integers(1, 5))
+    return int(_rng.integers(1, 4)), int(_rng.integers(1, 450))
+
+
+# (b, s, h, ffn, t, rank, act)
+MLP_CASES = []
+for _ in range(12):
+    t = int(_rng.choice([1, 2, 3, 4, 8]))
+    b, s = _tokens()
+    MLP_CASES.append((b, s, _w8(8, 1100), t * _w8(8, 1100 // t if t > 1 else 1100), t,
+                      int(_rng.integers(0, t)), str(_rng.choice(["erf", "tanh"]))))
+
+# (b, s, h, vocab, t)
+XENT_CASES = []
+for _ in range(10):
+    t = int(_rng.choice([1, 2, 3, 4, 8]))
+    b, s = _tokens()
+    XENT_CASES.append((b, s, _w8(8, 384), t * _w8(8, 2000), t))
+
+# (b, s, h, ffn, t, rank)
+SWIGLU_CASES = []
+for _ in range(6):
+    t = int(_rng.choice([1, 2, 4, 8]))
+    b, s = _tokens()
+    SWIGLU_CASES.append((b, s, _w8(8, 800), t * _w8(8, 800 // t if t > 1 else 800), t, int(_rng.integers(0, t))))
+
+# (t, n, bf16 output)
+SUM_CASES = [(int(_rng.integers(1, 13)), int(_rng.integers(1, 70000)), bool(_rng.integers(0, 2)))
+             for _ in range(8)]

@@ -148,6 +148,17 @@ sp(4, 12, 3, 72)
 attn(1, 4096, 8192, 64, 8, 128, 8)
 attn(1, 2072, 1032, 8, 2, 72, 2, pad=8)
 testing_entry_points()
+# the randomized parity tests' shapes
+sys.path.insert(0, sys.argv[1] + "/tests")
+from fuzz_cases import MLP_CASES, SUM_CASES, SWIGLU_CASES, XENT_CASES
+for b, s, h, ffn, t, _, _ in MLP_CASES:
+    mlp(b, s, h, ffn, t, BF)
+for b, s, h, V, t in XENT_CASES:
+    xent(b, s, h, V, t)
+for b, s, h, ffn, t, _ in SWIGLU_CASES:
+    swiglu(b, s, h, ffn, t)
+for t, n, _ in SUM_CASES:
+    sums(t, n, n)
 print(json.dumps({"calls": len(calls), "checks": L.lgs_test_debug_checks(),
                   "min_checks_per_call": min(c for _, c in calls)}))
 '''
