@@ -44,6 +44,15 @@ for _ in range(6):
     b, s = _tokens()
     SWIGLU_CASES.append((b, s, _w8(8, 800), t * _w8(8, 800 // t if t > 1 else 800), t, int(_rng.integers(0, t))))
 
+# (b, s, h, n_q, n_kv, d, t, rank): heads divisible by t, n_q a multiple of n_kv
+ATTN_CASES = []
+for _ in range(6):
+    t = int(_rng.choice([1, 2, 4, 8]))
+    n_kv = t * int(_rng.integers(1, 3))
+    n_q = n_kv * int(_rng.choice([1, 2, 4]))
+    b, s = _tokens()
+    ATTN_CASES.append((b, s, _w8(8, 1400), n_q, n_kv, _w8(8, 136), t, int(_rng.integers(0, t))))
+
 # (t, n, bf16 output)
 SUM_CASES = [(int(_rng.integers(1, 13)), int(_rng.integers(1, 70000)), bool(_rng.integers(0, 2)))
              for _ in range(8)]

@@ -2,7 +2,8 @@
 the fp64 oracle on every output element, over shapes drawn at import from a
 fixed seed (so a failure names a reproducible case).
 
-The shapes come from tests/fuzz_cases.py, which the debug build's bounds
+The shapes (MLP, CE, SwiGLU, attention projections, sums) come from
+tests/fuzz_cases.py, which the debug build's bounds
 test also drives on the CPU.  The hand-picked ragged cases elsewhere cover each tile shape and launch plan
 on purpose; these cover the space between them: token counts from 1 to
 about 1300, widths from 8 to about 1100 in steps of 8 (16-byte rows), every
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from fuzz_cases import MLP_CASES, SUM_CASES, SWIGLU_CASES, XENT_CASES
+from fuzz_cases import ATTN_CASES, MLP_CASES, SUM_CASES, SWIGLU_CASES, XENT_CASES
 from gpu_util import assert_close, dev, f64, round_like, step
 from logit_gemm_shard_amd import binding as lgs
 from logit_gemm_shard_amd import synth
@@ -140,6 +141,42 @@ def test_fuzz_swiglu_fwd_bwd(case):
     assert_close("dW_gate,i", dW[:, :f], g["dWg"], BF16)
     assert_close("dW_up,i", dW[:, f:], g["dWu"], BF16)
     assert_close("dW_down,i", dD, g["dWd"], BF16)
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=_ids)
+def test_fuzz_attn_projections(case):
+    b, s, h, n_q, n_kv, d, t, r = case
+    M, q, kv = b * s, n_q // t * d, n_kv // t * d
+    dv = dev()
+    X, Wq, Wk, Wv, Wo, A, dZ, dQ = synth.small(
+        4000 + h + d, (M, h), (h, n_q * d), (h, n_kv * d), (h, n_kv * d), (n_q * d, h), (M, q), (M, h),
+        (M, q + 2 * kv), dtype="bf16")
+    Wq, Wk, Wv, Wo = ((w.float() * 0.05).to(BF16) for w in (Wq, Wk, Wv, Wo))
+    X64 = f64(X)
+    W = synth.qkv_shard(Wq, Wk, Wv, n_q, n_kv, d, t, r)
+    W64 = oracle.attn.qkv_shard(f64(Wq), f64(Wk), f64(Wv), n_q, n_kv, d, t, r)
+    Wo_r = Wo[r * q:(r + 1) * q].contiguous()
+    Xd, Wd, Wod, Ad = X.to(dv), W.to(dv), Wo_r.to(dv), A.to(dv)
+    step(f"fuzz attn {case}")
+    QKV = torch.empty(M, q + 2 * kv, dtype=BF16, device=dv)
+    lgs.tp_attn_qkv_fwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, QKV)
+    Z = torch.empty(M, h, dtype=BF16, device=dv)
+    lgs.tp_attn_out_fwd(b, s, h, n_q, d, t, r, Ad, Wod, Z)
+    dX = torch.empty(M, h, dtype=BF16, device=dv)
+    dW = torch.empty(h, q + 2 * kv, dtype=BF16, device=dv)
+    lgs.tp_attn_qkv_bwd(b, s, h, n_q, n_kv, d, t, r, Xd, Wd, dQ.to(dv), dX, dW)
+    dA = torch.empty(M, q, dtype=BF16, device=dv)
+    dWo = torch.empty(q, h, dtype=BF16, device=dv)
+    lgs.tp_attn_out_bwd(b, s, h, n_q, d, t, r, Ad, Wod, dZ.to(dv), dA, dWo)
+    torch.cuda.synchronize()
+    assert_close("QKV_i", QKV, oracle.attn.qkv_forward(X64, W64), BF16)
+    assert_close("Z_i", Z, oracle.attn.out_forward(f64(A), f64(Wo_r)), BF16)
+    g = oracle.attn.qkv_backward(X64, W64, f64(dQ))
+    assert_close("dX_i", dX, g["dX"], BF16)
+    assert_close("dWqkv_i", dW, g["dW"], BF16)
+    g = oracle.attn.out_backward(f64(A), f64(Wo_r), f64(dZ))
+    assert_close("dA_i", dA, g["dA"], BF16)
+    assert_close("dWo_i", dWo, g["dW"], BF16)
 
 
 @pytest.mark.parametrize("case", SUM_CASES, ids=_ids)
