@@ -63,6 +63,21 @@ def test_fuzz_mlp_fwd_bwd(case):
     assert_close("dX_i", dX, g["dX"], BF16)
     assert_close("dA_i", dA, g["dA"], BF16)
     assert_close("dB_i", dB, g["dB"], BF16)
+    # the same backward in three parts: dX's bits always; dA's and dB's where
+    # the one-launch form does not split them over the tokens
+    ws = torch.empty(lgs.mlp_bwd_workspace_bytes(b, s, h, ffn, t, BF16), dtype=torch.uint8, device=d)
+    dX3, dA3, dB3 = torch.empty_like(dX), torch.empty_like(dA), torch.empty_like(dB)
+    lgs.tp_mlp_bwd_dgelu(b, s, h, ffn, t, r, Bd[r * f:(r + 1) * f], Uin.to(d), dZ.to(d), ws, act=act)
+    lgs.tp_mlp_bwd_dx(b, s, h, ffn, t, r, Ad[:, r * f:(r + 1) * f], dX3, ws)
+    lgs.tp_mlp_bwd_dw(b, s, h, ffn, t, r, Xd, dZ.to(d), dA3, dB3, ws)
+    torch.cuda.synchronize()
+    parts, _, tail = lgs.mlp_bwd_plan(M, h, f)
+    assert torch.equal(dX3, dX), "dX: three parts vs one launch"
+    for name, x, y, split in (("dA", dA3, dA, parts > 1), ("dB", dB3, dB, parts > 1 and tail == 0)):
+        if split:
+            assert_close(f"{name}: three parts vs one split launch", x, f64(y), BF16)
+        else:
+            assert torch.equal(x, y), f"{name}: three parts vs one launch"
 
 
 @pytest.mark.parametrize("case", XENT_CASES, ids=_ids)
@@ -96,6 +111,11 @@ def test_fuzz_xent_fwd_all_ranks_and_bwd(case):
         assert_close(f"l_{r}", sh[r, 1], l, BF16)
         assert_close(f"T_{r}", sh[r, 2], T, BF16)
     assert_close("loss (merged)", loss, oracle.xent.naive_loss(H64, E64, yn), BF16)
+    # rank 0 again through the allocation-free entry point: the same bits
+    st0 = torch.empty(3, M, dtype=F32, device=d)
+    lgs.vocab_parallel_xent_fwd_noalloc(b, s, h, V, t, 0, Hd, Ed[:Vr], yd, st0[0], st0[1], st0[2])
+    torch.cuda.synchronize()
+    assert torch.equal(st0.cpu(), sh[0]), "noalloc partials differ from the workspace call"
     # the backward of one rank from the merged lse (dloss = 1 per token)
     r = t - 1
     dH = torch.empty(M, h, dtype=BF16, device=d)
