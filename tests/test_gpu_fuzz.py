@@ -3,9 +3,9 @@ the fp64 oracle on every output element, over shapes drawn at import from a
 fixed seed (so a failure names a reproducible case).
 
 The shapes (MLP, CE, SwiGLU, attention projections, sums) come from
-tests/fuzz_cases.py, which the debug build's bounds
-test also drives on the CPU.  The hand-picked ragged cases elsewhere cover each tile shape and launch plan
-on purpose; these cover the space between them: token counts from 1 to
+tests/fuzz_cases.py, which the debug build's bounds test also drives on the
+CPU.  The hand-picked ragged cases elsewhere cover each tile shape and
+launch plan on purpose; these cover the space between them: token counts from 1 to
 about 1300, widths from 8 to about 1100 in steps of 8 (16-byte rows), every
 rank of t in {1, 2, 3, 4, 8}, and K ranges that are not multiples of the
 32-wide K step.  Tolerance as in the other parity tests (max|err| / max|ref|
