@@ -240,27 +240,34 @@ hbm_bytes_per_call: {nbytes(0) + nbytes(1):.0f}
 XENT_COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_8p3b_hbm_counters.txt")
 
 
+def block_tile(pid, n, tiles_m, tiles_n, xcds=8, group_m=4):
+    """The library's block-to-tile map for a launch of n blocks over a
+    tiles_m x tiles_n grid: block ids are dealt to the XCDs round-robin, so
+    (when n divides by the XCD count) they are renumbered to give every XCD a
+    contiguous run, which then walks the tiles in groups of group_m tile rows.
+    Returns (tile row, tile column)."""
+    if n % xcds == 0:
+        per = n // xcds
+        pid = (pid % xcds) * per + pid // xcds
+    width = group_m * tiles_n
+    g = pid // width
+    first = g * group_m
+    gsz = min(tiles_m - first, group_m)
+    inn = pid - g * width
+    return first + inn % gsz, inn // gsz
+
+
 def panel_fill_model(tiles_m, tiles_n, bm, bn, k_bytes, xcds=8, group_m=4, cus=256):
     """L2 fills of one launch if every XCD's L2 fetches, per round of its
     concurrent tiles, each operand panel those tiles cover once: blocks go to
     XCDs round-robin, each XCD owns a contiguous run of the grouped tile order
-    (the library's block-to-tile map), and a round is 256 blocks.  Returns
-    bytes."""
+    (block_tile), and a round is `cus` blocks.  Returns bytes."""
     n = tiles_m * tiles_n
-    per = n // xcds if n % xcds == 0 else None
-
-    def tile(pid):
-        if per is not None:
-            pid = (pid % xcds) * per + pid // xcds
-        width = group_m * tiles_n
-        g, first = pid // width, (pid // width) * group_m
-        gsz = min(tiles_m - first, group_m)
-        inn = pid - g * width
-        return first + inn % gsz, inn // gsz
     total = 0
     for r0 in range(0, n, cus):
         for x in range(xcds):
-            ts = [tile(p) for p in range(r0, min(n, r0 + cus)) if p % xcds == x]
+            ts = [block_tile(p, n, tiles_m, tiles_n, xcds, group_m) for p in range(r0, min(n, r0 + cus))
+                  if p % xcds == x]
             total += (len({t[0] for t in ts}) * bm + len({t[1] for t in ts}) * bn) * k_bytes
     return total
 
