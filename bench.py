@@ -29,6 +29,8 @@ per-entry-point breakdown.  Prints one JSON line.
     python bench.py --blas-reference     # torch.matmul (hipBLASLt) at the same GEMM shapes
     python bench.py --counter-summary DIR  # write the traffic summary from rocprofv3 --pmc passes in DIR
     python bench.py --kernel-stats CSV TITLE COMMAND  # markdown table from a rocprofv3 kernel_stats.csv
+    python bench.py --ce-stream-workload   # the streaming CE reductions alone (counter / trace passes)
+    python bench.py --ce-stream-summary DIR  # their HBM bytes and time from rocprofv3 passes under DIR
 """
 
 import argparse
@@ -874,6 +876,73 @@ def ce_reduction_stream(torch, lgs, xw, reps=30):
             "peak_GBs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+XR_COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_rows_8p3b_hbm_counters.txt")
+
+
+def ce_stream_workload(torch, lgs):
+    """The streaming CE reductions alone (the same 3 warm-up and 30 timed
+    calls as the bench line), for the counter and trace passes."""
+    from logit_gemm_shard_amd.configs import WORKLOADS
+    r = ce_reduction_stream(torch, lgs, WORKLOADS["xent_8p3b"])
+    torch.cuda.synchronize()
+    print(json.dumps(r), flush=True)
+
+
+def ce_stream_summary(d):
+    """Write XR_COUNTERS_FILE: the streaming CE reduction kernel's HBM-side
+    bytes per launch from FETCH_SIZE / WRITE_SIZE passes (scaled by the copy
+    calibration passes of the counter summary) and its average duration from
+    a kernel trace, all over `bench.py --ce-stream-workload`."""
+    import csv
+    import statistics
+
+    def one(sub, pattern):
+        found = glob.glob(os.path.join(d, sub, "**", pattern), recursive=True)
+        if not found:
+            raise SystemExit(f"no {pattern} under {os.path.join(d, sub)}")
+        return found[0]
+    med = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        xr = [v for n, v in _per_kernel(one(f"pmc/pmc_xr_{c}", "*counter_collection.csv"), c).items()
+              if "xent_rows_kernel" in n]
+        cp = [v for n, v in _per_kernel(one(f"pmc/pmc_copy_{c}", "*counter_collection.csv"), c).items()
+              if "neg" in n]
+        if len(xr) != 1 or len(cp) != 1:
+            raise SystemExit(f"{c}: expected one streaming CE kernel and one copy kernel")
+        med[c] = (statistics.median(xr[0]), len(xr[0]), statistics.median(cp[0]))
+    fr = (1 << 30) / (med["FETCH_SIZE"][2] * 1024)
+    fw = (1 << 30) / (med["WRITE_SIZE"][2] * 1024)
+    rd, wr = med["FETCH_SIZE"][0] * 1024 * fr, med["WRITE_SIZE"][0] * 1024 * fw
+    rows = [r for r in csv.DictReader(open(one("prof_xr", "*kernel_stats.csv"))) if "xent_rows_kernel" in r["Name"]]
+    if len(rows) != 1:
+        raise SystemExit("expected one streaming CE kernel in the kernel trace")
+    us, calls = float(rows[0]["AverageNs"]) / 1e3, int(rows[0]["Calls"])
+    M, Vr = 8192, 6400
+    alg = M * Vr * 2 + M * 4 + 3 * M * 4
+    wl = "python bench.py --ce-stream-workload"
+    txt = f"""# HBM-side traffic and time of the streaming CE reductions (xent_rows_kernel:
+# per-row max, sum of exponentials and target logit over materialised bf16
+# logits of the 8.3B slice, [{M}, {Vr}]; three 105 MB buffers rotated, more than
+# the 256 MB Infinity Cache), from rocprofv3 passes over the same workload:
+#
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc/pmc_xr_FETCH_SIZE -o p -- {wl}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc/pmc_xr_WRITE_SIZE -o p -- {wl}
+#   rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/prof_xr -o x -- {wl}
+#   (the copy-calibration passes of the MLP counter summary, under rocprof_out/pmc/pmc_copy_*)
+#   python bench.py --ce-stream-summary rocprof_out      (writes this file)
+#
+# Per launch (median over {med['FETCH_SIZE'][1]} dispatches; FETCH_SIZE x 1024 x {fr:.4f}, WRITE_SIZE x 1024 x {fw:.4f}):
+#   read  {rd / 1e6:.1f} MB, written {wr / 1e6:.3f} MB (FETCH_SIZE {med['FETCH_SIZE'][0]:.0f} KiB, WRITE_SIZE {med['WRITE_SIZE'][0]:.0f} KiB)
+#   algorithmic bytes: {alg / 1e6:.1f} MB (every logit read once, the targets read, m, l, T written)
+#   average duration under the kernel trace: {us:.2f} us over {calls} launches
+#   achieved: {(rd + wr) / us / 1e3:.1f} GB/s by the counters, {alg / us / 1e3:.1f} GB/s algorithmic
+#   ({alg / us / 1e3 / PEAK_HBM_GBS:.3f} of the 8000 GB/s HBM peak)
+kernel_sources_sha256: {kernel_sources_digest()}
+"""
+    open(XR_COUNTERS_FILE, "w").write(txt)
+    print(txt)
+
+
 def progress(msg):
     """One line on stderr as each part of the run finishes (the JSON line on
     stdout stays the only output there)."""
@@ -902,6 +971,10 @@ def _timed_report(torch, fn, flops, reps, nsets, warmup=10):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--ce-stream-workload", action="store_true",
+                    help="run the streaming CE reductions alone (for counter and trace passes) and exit")
+    ap.add_argument("--ce-stream-summary", metavar="DIR",
+                    help="write the streaming CE counter summary from rocprofv3 passes under DIR and exit")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
@@ -931,6 +1004,9 @@ def main():
     if args.mfma_summary:
         mfma_summary(args.mfma_summary)
         return
+    if args.ce_stream_summary:
+        ce_stream_summary(args.ce_stream_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard: the library is measured on one GPU "
               "(all t ranks of the split are timed or checked on that one device); use --gpus 1.",
@@ -947,6 +1023,10 @@ def main():
     if args.mfma_workload:
         from logit_gemm_shard_amd import binding as lgs_b
         mfma_workload(torch, lgs_b)
+        return
+    if args.ce_stream_workload:
+        from logit_gemm_shard_amd import binding as lgs_b
+        ce_stream_workload(torch, lgs_b)
         return
 
     from logit_gemm_shard_amd import binding as lgs
