@@ -52,3 +52,35 @@ def comm_volume(kind, t, n):
     the all-reduce they compose (the section's volume identity)."""
     one = (t - 1) / t * n
     return {"reduce_scatter": one, "all_gather": one, "all_reduce": 2 * one}[kind]
+
+
+def layernorm(x, gamma, beta, eps=1e-5):
+    """Per token row of x [n, h]: (x - mean) / sqrt(var + eps) * gamma + beta,
+    with the mean and the (biased, 1/h) variance taken over the h features
+    and gamma, beta [h] per feature.  The section says only that LayerNorm
+    works on each token independently along h; this is the usual definition."""
+    x = _f64(x)
+    mean = x.mean(axis=1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=1, keepdims=True)
+    return (x - mean) / np.sqrt(var + eps) * _f64(gamma)[None, :] + _f64(beta)[None, :]
+
+
+def exit_region(parts, s, b, t, r, residual, gamma, beta, eps=1e-5, keep=None, keep_scale=1.0):
+    """Rank r's sequence-parallel region after the row-parallel exit, on its
+    (s/t, b, h) chunk (the section's "Normalized Execution": LayerNorm,
+    residual additions and dropout run locally on the chunk):
+
+      z   = reduce_scatter(parts)                   rank r's rows of sum_i Z_i
+      d   = z * keep * keep_scale  (keep given)     dropout with a given keep mask
+            z                      (keep None)      (no dropout)
+      hs  = residual + d                            the residual stream's chunk
+      y   = layernorm(hs, gamma, beta, eps)         the next sub-layer's input
+
+    Readings: dropout acts on the block's output before the residual add and
+    LayerNorm follows the add (the next sub-layer's norm, as in Megatron's
+    pre-norm blocks); the keep mask is an input (the pages give no random
+    number generator), keep_scale normally 1 / (1 - p).  Returns (hs, y)."""
+    z = reduce_scatter(parts, s, b, t, r)
+    d = z if keep is None else z * (np.asarray(keep) != 0) * float(keep_scale)
+    hs = _f64(residual) + d
+    return hs, layernorm(hs, gamma, beta, eps)

@@ -700,7 +700,102 @@ def check_sp_volume(sp):
     assert sp.comm_volume("all_gather", 8, 8) == 7.0
 
 
-SP_CHECKS = [check_sp_reduce_scatter_brute, check_sp_identity, check_sp_volume]
+def _ln_row_loops(row, gamma, beta, eps):
+    n = len(row)
+    mean = math.fsum(row) / n
+    var = math.fsum((v - mean) ** 2 for v in row) / n
+    inv = 1.0 / math.sqrt(var + eps)
+    return [(v - mean) * inv * g + bb for v, g, bb in zip(row, gamma, beta)]
+
+
+def check_sp_layernorm_brute(sp):
+    """LayerNorm against loops per row (math.fsum means, the biased
+    variance, eps inside the square root, per-feature gamma and beta)."""
+    r_ = _rng(63)
+    x = r_.normal(size=(4, 7)) * 3 + 1
+    g, b = r_.normal(size=7), r_.normal(size=7)
+    for eps in (1e-5, 0.5):
+        want = np.array([_ln_row_loops(list(row), g, b, eps) for row in x])
+        assert _rel(sp.layernorm(x, g, b, eps), want) < 1e-13, eps
+
+
+def check_sp_layernorm_closed_forms(sp):
+    """A constant row normalises to beta exactly; with gamma = 1, beta = 0 a
+    row comes out with mean 0 and variance var / (var + eps); with eps = 0 the
+    result does not change when the row is scaled by a > 0 and shifted."""
+    r_ = _rng(64)
+    h = 9
+    g, b = r_.normal(size=h), r_.normal(size=h)
+    c = np.full((2, h), 3.25)
+    assert np.array_equal(sp.layernorm(c, g, b, 1e-5), np.stack([b, b]))
+    x = r_.normal(size=(5, h)) * 0.01
+    y = sp.layernorm(x, np.ones(h), np.zeros(h), 1e-5)
+    v = x.var(axis=1)
+    assert np.abs(y.mean(axis=1)).max() < 1e-12
+    assert _rel(y.var(axis=1), v / (v + 1e-5)) < 1e-10
+    assert _rel(sp.layernorm(2.5 * x - 7.0, g, b, 0.0), sp.layernorm(x, g, b, 0.0)) < 1e-9
+
+
+def check_sp_layernorm_library(sp):
+    """The library routine (torch.nn.functional.layer_norm in float64 on the
+    CPU) as a special case."""
+    import torch
+    r_ = _rng(65)
+    x, g, b = r_.normal(size=(6, 40)), r_.normal(size=40), r_.normal(size=40)
+    want = torch.nn.functional.layer_norm(torch.from_numpy(x), (40,), torch.from_numpy(g), torch.from_numpy(b),
+                                          1e-5).numpy()
+    assert _rel(sp.layernorm(x, g, b, 1e-5), want) < 1e-12
+
+
+def check_sp_exit_region_brute(sp):
+    """Rank r's region by loops: every element of its chunk summed over the
+    ranks' partials, masked and scaled, added to the residual, then each row
+    normalised by the loop LayerNorm."""
+    r_ = _rng(66)
+    s, b, h, t = 6, 2, 5, 3
+    parts = [r_.normal(size=(s * b, h)) for _ in range(t)]
+    n = (s // t) * b
+    res = r_.normal(size=(n, h))
+    keep = (r_.random(size=(n, h)) > 0.3).astype(np.uint8)
+    g, bb = r_.normal(size=h), r_.normal(size=h)
+    for r in range(t):
+        hs, y = sp.exit_region(parts, s, b, t, r, res, g, bb, 1e-5, keep, 1 / 0.7)
+        for j in range(n):
+            k = r * n + j
+            row = [res[j, c] + math.fsum(p[k, c] for p in parts) * (1 / 0.7 if keep[j, c] else 0.0)
+                   for c in range(h)]
+            assert _rel(hs[j], row) < 1e-13, (r, j)
+            assert _rel(y[j], _ln_row_loops(row, g, bb, 1e-5)) < 1e-12, (r, j)
+
+
+def check_sp_exit_region_split_identity(sp):
+    """The ranks' chunks, gathered in rank order, equal the region computed on
+    the whole tensor after the all-reduce (LayerNorm works per token, so the
+    split along the sequence changes nothing); a mask of zeros leaves the
+    residual alone, and no mask is dropout off."""
+    r_ = _rng(67)
+    s, b, h = 8, 3, 6
+    for t in (1, 2, 4):
+        parts = [r_.normal(size=(s * b, h)) for _ in range(t)]
+        res = r_.normal(size=(s * b, h))
+        keep = (r_.random(size=(s * b, h)) > 0.1).astype(np.uint8)
+        g, bb = r_.normal(size=h), r_.normal(size=h)
+        n = (s // t) * b
+        out = [sp.exit_region(parts, s, b, t, r, res[r * n:(r + 1) * n], g, bb, 1e-5, keep[r * n:(r + 1) * n],
+                              1 / 0.9) for r in range(t)]
+        z = sum(parts)
+        full_h = res + z * keep / 0.9
+        assert _rel(np.concatenate([o[0] for o in out]), full_h) < 1e-13
+        assert _rel(np.concatenate([o[1] for o in out]), sp.layernorm(full_h, g, bb, 1e-5)) < 1e-12
+        hs0, _ = sp.exit_region(parts, s, b, t, 0, res[:n], g, bb, 1e-5, np.zeros((n, h), np.uint8), 2.0)
+        assert np.array_equal(hs0, res[:n])
+        hs1, _ = sp.exit_region(parts, s, b, t, 0, res[:n], g, bb)
+        assert _rel(hs1, res[:n] + z[:n]) < 1e-13
+
+
+SP_CHECKS = [check_sp_reduce_scatter_brute, check_sp_identity, check_sp_volume, check_sp_layernorm_brute,
+             check_sp_layernorm_closed_forms, check_sp_layernorm_library, check_sp_exit_region_brute,
+             check_sp_exit_region_split_identity]
 
 
 # ------------------------------------------------------ attention projections

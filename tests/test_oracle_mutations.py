@@ -397,7 +397,54 @@ def _volume_no_half(kind, t, n):
     return {"reduce_scatter": one, "all_gather": one, "all_reduce": one}[kind]
 
 
+_REAL_LN, _REAL_EXIT = sp.layernorm, sp.exit_region
+
+
+def _ln_no_eps(x, gamma, beta, eps=1e-5):
+    return _REAL_LN(x, gamma, beta, 0.0)
+
+
+def _ln_unbiased(x, gamma, beta, eps=1e-5):
+    x = np.asarray(x, dtype=np.float64)
+    mean = x.mean(axis=1, keepdims=True)
+    var = ((x - mean) ** 2).sum(axis=1, keepdims=True) / (x.shape[1] - 1)
+    return (x - mean) / np.sqrt(var + eps) * gamma + beta
+
+
+def _ln_stats_over_tokens(x, gamma, beta, eps=1e-5):
+    x = np.asarray(x, dtype=np.float64)
+    mean = x.mean(axis=0, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=0, keepdims=True)
+    return (x - mean) / np.sqrt(var + eps) * gamma + beta
+
+
+def _ln_gamma_beta_swapped(x, gamma, beta, eps=1e-5):
+    return _REAL_LN(x, beta, gamma, eps)
+
+
+def _exit_no_dropout_scale(parts, s, b, t, r, residual, gamma, beta, eps=1e-5, keep=None, keep_scale=1.0):
+    return _REAL_EXIT(parts, s, b, t, r, residual, gamma, beta, eps, keep, 1.0)
+
+
+def _exit_no_residual(parts, s, b, t, r, residual, gamma, beta, eps=1e-5, keep=None, keep_scale=1.0):
+    return _REAL_EXIT(parts, s, b, t, r, np.zeros_like(np.asarray(residual, dtype=np.float64)), gamma, beta, eps,
+                      keep, keep_scale)
+
+
+def _exit_norm_before_add(parts, s, b, t, r, residual, gamma, beta, eps=1e-5, keep=None, keep_scale=1.0):
+    z = sp.reduce_scatter(parts, s, b, t, r)
+    d = z if keep is None else z * (np.asarray(keep) != 0) * keep_scale
+    return residual + d, _REAL_LN(d, gamma, beta, eps) + residual
+
+
 SP_MUTANTS = {
+    "ln_no_eps": ("layernorm", _ln_no_eps),
+    "ln_unbiased_variance": ("layernorm", _ln_unbiased),
+    "ln_stats_over_tokens": ("layernorm", _ln_stats_over_tokens),
+    "ln_gamma_beta_swapped": ("layernorm", _ln_gamma_beta_swapped),
+    "exit_dropout_unscaled": ("exit_region", _exit_no_dropout_scale),
+    "exit_residual_dropped": ("exit_region", _exit_no_residual),
+    "exit_norm_before_add": ("exit_region", _exit_norm_before_add),
     "chunk_wrong_rows": ("chunk_rows", _chunk_b_major),
     "rs_skips_last_rank": ("reduce_scatter", _rs_skips_last),
     "ag_reversed_order": ("all_gather", _ag_reversed),
