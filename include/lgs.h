@@ -424,6 +424,38 @@ int shard_reduce_scatter(int t, int rank, int s, int b, int h, int in_dtype, int
 int shard_all_gather(int t, int s, int b, int h, int dtype, const void* shards,
                      int64_t shard_stride, void* out, void* stream);
 
+/*
+ * shard_reduce_scatter_layernorm -- the sequence-parallel region between the
+ * two halves, fused with the reduce-scatter ("Mathematical Foundations of
+ * Megatron-LM", "Sequence Parallelism": LayerNorm, the residual addition and
+ * dropout run locally on the rank's (s/t, b, h) chunk).  For every row j of
+ * rank r's chunk (rows as for shard_reduce_scatter):
+ *
+ *   z_j  = sum_{i<t} parts[i*part_stride + (r*(s/t)*b + j)*h + (0..h-1)]
+ *          (fp32, ascending i: the bits shard_reduce_scatter sums to)
+ *   d_j  = keep ? (keep[j*h + c] != 0 ? z_j[c] * keep_scale : 0) : z_j[c]
+ *   hs_j = residual_j + d_j                      -> hs   [(s/t)*b, h] bf16
+ *   y_j  = (hs_j - mean) / sqrt(var + eps) * gamma + beta
+ *                                                -> y    [(s/t)*b, h] bf16
+ *
+ * with mean and the biased (1/h) variance of the row's fp32 hs_j (before its
+ * rounding to bf16) over the h features.  Readings: dropout acts on the
+ * block's output before the residual add and LayerNorm is the next
+ * sub-layer's, applied after it; the keep mask is an input (one byte per
+ * element, non-zero = keep; NULL = no dropout), keep_scale normally 1/(1-p).
+ *
+ * dtype must be LGS_BF16 (else LGS_ERR_UNSUPPORTED); parts as for
+ * shard_reduce_scatter (part_stride >= s*b*h and a multiple of 8 when
+ * t > 1); residual, hs, y dense [(s/t)*b, h]; gamma, beta [h]; all 16-byte
+ * aligned, keep 8-byte aligned.  h must be a multiple of 8 and at most 16384
+ * (LGS_ERR_UNSUPPORTED otherwise); eps > 0 and finite.  hs and y must not
+ * overlap the inputs or each other.
+ */
+int shard_reduce_scatter_layernorm(int t, int rank, int s, int b, int h, int dtype, const void* parts,
+                                   int64_t part_stride, const void* residual, const uint8_t* keep,
+                                   float keep_scale, const void* gamma, const void* beta, float eps,
+                                   void* hs, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,8 @@ SIGNATURES = [
                              _p, _i64, _p, _sz, _p]),
     ("shard_reduce_scatter", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _i64, _p, _p]),
     ("shard_all_gather", _i, [_i, _i, _i, _i, _i, _p, _i64, _p, _p]),
+    ("shard_reduce_scatter_layernorm", _i,
+     [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _p, ctypes.c_float, _p, _p, ctypes.c_float, _p, _p, _p]),
     # include/lgs_testing.h
     ("lgs_test_num_tiles", _i, []),
     ("lgs_test_tile_shape", _i, [_i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
@@ -415,6 +417,17 @@ def shard_reduce_scatter(t, rank, s, b, h, parts, part_stride, out, stream=None)
     _check(lib().shard_reduce_scatter(t, rank, s, b, h, _dtype(parts), _dtype(out), parts.data_ptr(),
                                       part_stride, out.data_ptr(), _stream(stream)))
     return out
+
+
+def shard_reduce_scatter_layernorm(t, rank, s, b, h, parts, part_stride, residual, gamma, beta, hs, y,
+                                   keep=None, keep_scale=1.0, eps=1e-5, stream=None):
+    """Rank's sequence-parallel region: hs = residual + dropout(rank's rows of
+    sum_i parts[i]) and y = LayerNorm(hs) (bf16; keep a uint8 mask or None)."""
+    _check(lib().shard_reduce_scatter_layernorm(t, rank, s, b, h, _dtype(parts), parts.data_ptr(), part_stride,
+                                                residual.data_ptr(), None if keep is None else keep.data_ptr(),
+                                                keep_scale, gamma.data_ptr(), beta.data_ptr(), eps, hs.data_ptr(),
+                                                y.data_ptr(), _stream(stream)))
+    return hs, y
 
 
 def shard_all_gather(t, s, b, h, shards, shard_stride, out, stream=None):

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <climits>
+#include <cmath>
 
 #include "debug.hpp"
 #include "internal.hpp"
@@ -554,6 +555,41 @@ LGS_API int shard_reduce_scatter(int t, int rank, int s, int b, int h, int in_dt
   clear_hip_error();
   return launched(lgs::reduce_scatter(t, chunk, rank, in_dtype == LGS_BF16, out_dtype == LGS_BF16,
                                       parts, part_stride, out, (hipStream_t)stream));
+}
+
+LGS_API int shard_reduce_scatter_layernorm(int t, int rank, int s, int b, int h, int dtype,
+                                           const void* parts, int64_t part_stride, const void* residual,
+                                           const uint8_t* keep, float keep_scale, const void* gamma,
+                                           const void* beta, float eps, void* hs, void* y, void* stream) {
+  int st = check_sp(t, s, b, h);
+  if (st) return st;
+  if (rank < 0 || rank >= t) return fail(LGS_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, t);
+  if ((st = check_dtype(dtype))) return st;
+  if (dtype != LGS_BF16) return fail(LGS_ERR_UNSUPPORTED, "the fused sequence-parallel region is bf16 only");
+  if (h % 8 != 0 || h > lgs::rs_layernorm_max_h())
+    return fail(LGS_ERR_UNSUPPORTED, "h=%d must be a multiple of 8 and at most %d", h, lgs::rs_layernorm_max_h());
+  if (!parts || !residual || !gamma || !beta || !hs || !y)
+    return fail(LGS_ERR_INVALID_ARG, "parts, residual, gamma, beta, hs and y are required");
+  if (!(eps > 0.f) || !std::isfinite(eps) || !std::isfinite(keep_scale))
+    return fail(LGS_ERR_INVALID_ARG, "eps must be positive and finite, keep_scale finite");
+  const int64_t n = (int64_t)s * b * h, chunk = n / t;
+  if (t > 1 && part_stride < n)
+    return fail(LGS_ERR_INVALID_ARG, "part_stride %lld < s*b*h = %lld", (long long)part_stride,
+                (long long)n);
+  if (t > 1 && part_stride % 8 != 0) return fail(LGS_ERR_UNSUPPORTED, "part_stride must be a multiple of 8");
+  for (const void* p : {parts, residual, gamma, beta, (const void*)hs, (const void*)y})
+    if (!aligned(p, 16)) return fail(LGS_ERR_UNSUPPORTED, "parts, residual, gamma, beta, hs and y need 16-byte alignment");
+  if (keep && !aligned(keep, 8)) return fail(LGS_ERR_UNSUPPORTED, "the keep mask needs 8-byte alignment");
+  allow(parts, (size_t)((t - 1) * (t > 1 ? part_stride : 0) + n) * 2);
+  allow(residual, (size_t)chunk * 2);
+  if (keep) allow(keep, (size_t)chunk);
+  allow(gamma, (size_t)h * 2);
+  allow(beta, (size_t)h * 2);
+  allow(hs, (size_t)chunk * 2);
+  allow(y, (size_t)chunk * 2);
+  clear_hip_error();
+  return launched(lgs::rs_layernorm(t, (s / t) * b, h, rank, parts, t > 1 ? part_stride : 0, residual, keep,
+                                    keep_scale, gamma, beta, eps, hs, y, (hipStream_t)stream));
 }
 
 LGS_API int shard_all_gather(int t, int s, int b, int h, int dtype, const void* shards,

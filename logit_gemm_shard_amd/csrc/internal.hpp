@@ -113,6 +113,13 @@ hipError_t reduce_scatter(int t, int64_t chunk, int rank, bool in_bf16, bool out
                           const void* parts, int64_t stride, void* out, hipStream_t s);
 hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64_t stride,
                       void* out, hipStream_t s);
+// The sequence-parallel region of rank r's `rows` rows (bf16): the sum of the
+// t partials' rows (rank r's chunk of each), dropout with the keep mask (if
+// any), the residual add (hs) and LayerNorm over h (y).  h <= rs_layernorm_max_h().
+int rs_layernorm_max_h();
+hipError_t rs_layernorm(int t, int rows, int h, int rank, const void* parts, int64_t stride,
+                        const void* residual, const uint8_t* keep, float keep_scale, const void* gamma,
+                        const void* beta, float eps, void* hs, void* y, hipStream_t s);
 hipError_t xent_rows(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
                      const int32_t* targets, float* m, float* l, float* t, hipStream_t s);
 hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, bool lse_only,

@@ -355,6 +355,22 @@ def test_sp_validation(L):
     assert ag(4, 8, 2, 8, 7, FAKE, 32, FAKE, None) == 2
     assert ag(4, 8, 2, 8, 1, FAKE, 32, None, None) == 1
     assert ag(4, 8, 2, 8, 1, FAKE + 1, 32, FAKE, None) == 2
+    ln = L.shard_reduce_scatter_layernorm
+
+    def call(t=4, r=0, s=8, b=2, h=16, dt=1, parts=FAKE, stride=256, res=FAKE, keep=None, scale=1.0, g=FAKE,
+             bb=FAKE, eps=1e-5, hs=FAKE, y=FAKE):
+        return ln(t, r, s, b, h, dt, parts, stride, res, keep, scale, g, bb, eps, hs, y, None)
+    assert call(s=10) == 1                      # s % t
+    assert call(r=4) == 1                       # rank
+    assert call(stride=255) == 1                # stride < s*b*h
+    assert call(stride=260) == 2                # stride not a multiple of 8
+    assert call(dt=0) == 2                      # fp32: bf16 only
+    assert call(h=12) == 2                      # h % 8
+    assert call(h=16392, stride=8 * 2 * 16392) == 2  # h above 16384
+    assert call(eps=0.0) == 1 and call(eps=float("nan")) == 1 and call(scale=float("inf")) == 1
+    assert call(res=None) == 1 and call(g=None) == 1 and call(y=None) == 1
+    assert call(hs=FAKE + 8) == 2               # 16-byte alignment
+    assert call(keep=FAKE + 4) == 2             # the mask's 8-byte alignment
 
 
 def test_binding_raises_when_library_missing(tmp_path, monkeypatch):

@@ -101,6 +101,10 @@ def sums(t, n, stride):
 def sp(t, s, b, h):
     for r in range(t):
         call("shard_reduce_scatter", t, r, s, b, h, BF, BF, buf(), s * b * h, buf(), None)
+        if h % 8 == 0:
+            for keep in (None, buf()):
+                call("shard_reduce_scatter_layernorm", t, r, s, b, h, BF, buf(), s * b * h + 8 * r, buf(), keep,
+                     1.25, buf(), buf(), 1e-5, buf(), buf(), None)
     call("shard_all_gather", t, s, b, h, BF, buf(), (s // t) * b * h + 40, buf(), None)
 
 def attn(b, s, h, nq, nkv, d, t, pad=0):
@@ -145,6 +149,8 @@ sums(8, 4096 * 8192, 4096 * 8192)
 sums(3, 1001, 1024)
 sp(8, 1024, 8, 3072)
 sp(4, 12, 3, 72)
+sp(2, 6, 1, 16384)
+sp(3, 9, 2, 2056)
 attn(1, 4096, 8192, 64, 8, 128, 8)
 attn(1, 2072, 1032, 8, 2, 72, 2, pad=8)
 testing_entry_points()

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import dev, f64, step
+from gpu_util import assert_close, dev, f64, step
 from logit_gemm_shard_amd import binding as lgs
 
 pytestmark = pytest.mark.gpu
@@ -88,3 +88,74 @@ def test_all_gather_strided_shards():
         torch.cuda.synchronize()
         want = oracle.sp.all_gather([f64(shards[q, :c]).reshape((s // t) * b, h) for q in range(t)], s, b, t)
         assert np.array_equal(f64(out).reshape(s * b, h), want)
+
+
+# ------------------------------------------- fused SP region (RS + LayerNorm)
+
+def _region_inputs(t, s, b, h, seed, with_mask):
+    g = torch.Generator().manual_seed(seed)
+    n = (s // t) * b
+    parts = torch.randn(t, s * b, h, generator=g).to(BF16)
+    res = torch.randn(n, h, generator=g).to(BF16)
+    gamma = (1 + 0.1 * torch.randn(h, generator=g)).to(BF16)
+    beta = (0.1 * torch.randn(h, generator=g)).to(BF16)
+    keep = (torch.rand(n, h, generator=g) > 0.1).to(torch.uint8) if with_mask else None
+    return parts, res, gamma, beta, keep
+
+
+@pytest.mark.parametrize("with_mask", [False, True], ids=["nomask", "mask"])
+@pytest.mark.parametrize("shape", [(8, 1024, 8, 3072), (3, 12, 3, 72), (2, 10, 5, 8), (4, 64, 2, 8192),
+                                   (1, 5, 1, 16384), (2, 6, 1, 2056)], ids=lambda s: "x".join(map(str, s)))
+def test_rs_layernorm_every_element(shape, with_mask):
+    """Every rank's hs and y against the oracle's exit region (bf16
+    tolerance); without a mask, hs bit for bit against the reduce-scatter's
+    fp32 chunk plus the residual rounded once (the same fp32 sum in the same
+    order)."""
+    t, s, b, h = shape
+    d = dev()
+    n = (s // t) * b
+    parts, res, gamma, beta, keep = _region_inputs(t, s, b, h, 7 * t + h, with_mask)
+    scale = 1 / 0.9
+    pd = parts.to(d)
+    p64 = [f64(p) for p in parts]
+    for r in sorted({0, t - 1}):
+        step(f"rs+layernorm {shape} mask={with_mask} rank={r}")
+        rd = res.to(d)
+        kd = None if keep is None else keep.to(d)
+        hs = torch.empty(n, h, dtype=BF16, device=d)
+        y = torch.empty(n, h, dtype=BF16, device=d)
+        lgs.shard_reduce_scatter_layernorm(t, r, s, b, h, pd, s * b * h, rd, gamma.to(d), beta.to(d), hs, y,
+                                           keep=kd, keep_scale=scale, eps=1e-5)
+        z = torch.empty(n, h, dtype=F32, device=d)
+        lgs.shard_reduce_scatter(t, r, s, b, h, pd, s * b * h, z)
+        torch.cuda.synchronize()
+        rh, ry = oracle.sp.exit_region(p64, s, b, t, r, f64(res), f64(gamma), f64(beta), 1e-5,
+                                       None if keep is None else keep.numpy(), scale)
+        assert_close("hs", hs, rh, BF16)
+        assert_close("y", y, ry, BF16)
+        if keep is None:  # (with a mask the product and the add may contract into one fma)
+            assert torch.equal(hs.cpu(), (z.cpu() + res.float()).to(BF16)), "hs: one rounding of the fp32 sum"
+
+
+def test_rs_layernorm_unit_rows_and_guards():
+    """With gamma = 1 and beta = 0 every output row has mean ~0 and variance
+    ~1 (checked at the 8.3B chunk size on every row); outputs written into
+    wider sentinel-filled buffers leave everything outside their rows alone."""
+    t, s, b, h = 8, 1024, 8, 3072
+    d = dev()
+    n = (s // t) * b
+    parts, res, _, _, _ = _region_inputs(t, s, b, h, 5, False)
+    pad = 4096
+    hs_buf = torch.full((n * h + 2 * pad,), float("nan"), dtype=BF16, device=d)
+    y_buf = torch.full((n * h + 2 * pad,), float("nan"), dtype=BF16, device=d)
+    hs, y = hs_buf[pad:pad + n * h].view(n, h), y_buf[pad:pad + n * h].view(n, h)
+    step("rs+layernorm: unit rows and guard bands")
+    lgs.shard_reduce_scatter_layernorm(t, 3, s, b, h, parts.to(d), s * b * h, res.to(d),
+                                       torch.ones(h, dtype=BF16, device=d), torch.zeros(h, dtype=BF16, device=d),
+                                       hs, y)
+    torch.cuda.synchronize()
+    yf = f64(y)
+    assert np.abs(yf.mean(axis=1)).max() < 2e-2 and np.abs(yf.var(axis=1) - 1).max() < 2e-2
+    for buf in (hs_buf, y_buf):
+        assert torch.isnan(buf[:pad].float()).all() and torch.isnan(buf[pad + n * h:].float()).all()
+        assert torch.isfinite(buf[pad:pad + n * h].float()).all()
