@@ -717,18 +717,46 @@ def per_config(torch, lgs, reps):
     w = WORKLOADS["mlp_8p3b_fwd"]
     t, M, h = w.t, w.M, w.h
     chunk = M * h // t
+    # successive calls take successive ranks' chunks (and rotate the gather's
+    # inputs), so no call finds its bytes in the Infinity Cache
     parts = randn(t, M, h, std=0.05)
     rs_out = torch.empty(M // t, h, dtype=bf, device=dev)
-    ag_in = randn(t, M // t, h)
+    ag_in = [randn(t, M // t, h) for _ in range(6)]
     ag_out = torch.empty(M, h, dtype=bf, device=dev)
-    rs_ms = time_calls(torch, lambda: lgs.shard_reduce_scatter(t, 0, w.s, w.b, h, parts, M * h, rs_out), reps)
-    ag_ms = time_calls(torch, lambda: lgs.shard_all_gather(t, w.s, w.b, h, ag_in, chunk, ag_out), reps)
+    res = randn(t, M // t, h)
+    keep = (torch.rand(t, M // t, h, device=dev) > 0.1).to(torch.uint8)
+    gamma, beta = randn(h, std=0.1) + 1, randn(h, std=0.1)
+    hs, ys = torch.empty(M // t, h, dtype=bf, device=dev), torch.empty(M // t, h, dtype=bf, device=dev)
+    i = [0]
+
+    def rs():
+        lgs.shard_reduce_scatter(t, i[0] % t, w.s, w.b, h, parts, M * h, rs_out)
+        i[0] += 1
+
+    def ag():
+        lgs.shard_all_gather(t, w.s, w.b, h, ag_in[i[0] % 6], chunk, ag_out)
+        i[0] += 1
+
+    def rs_ln():
+        r = i[0] % t
+        lgs.shard_reduce_scatter_layernorm(t, r, w.s, w.b, h, parts, M * h, res[r], gamma, beta, hs, ys,
+                                           keep=keep[r], keep_scale=1 / 0.9)
+        i[0] += 1
+    rs_ms = time_calls(torch, rs, reps)
+    ag_ms = time_calls(torch, ag, reps)
+    ln_ms = time_calls(torch, rs_ln, reps)
     rs_bytes, ag_bytes = (t + 1) * chunk * 2, 2 * M * h * 2
+    ln_bytes = (t + 1) * chunk * 2 + chunk + 2 * chunk * 2 + 2 * h * 2
     out["sp_8p3b"] = {"reduce_scatter_us": round(rs_ms * 1e3, 2),
                       "reduce_scatter_GBs": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1),
                       "all_gather_us": round(ag_ms * 1e3, 2),
                       "all_gather_GBs": round(ag_bytes / (ag_ms * 1e-3) / 1e9, 1),
-                      "note": "bytes = every byte read once + written once; HBM peak 8000 GB/s"}
+                      "rs_layernorm_us": round(ln_ms * 1e3, 2),
+                      "rs_layernorm_GBs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
+                      "rs_layernorm_frac_hbm": round(ln_bytes / (ln_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "note": "bytes = every byte read once + written once; HBM peak 8000 GB/s; "
+                              "rs_layernorm: the 8 partials' rank rows, residual, keep mask read, hs and y "
+                              "written (dropout p = 0.1)"}
     return out
 
 
