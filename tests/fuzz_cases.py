@@ -56,3 +56,10 @@ for _ in range(6):
 # (t, n, bf16 output)
 SUM_CASES = [(int(_rng.integers(1, 13)), int(_rng.integers(1, 70000)), bool(_rng.integers(0, 2)))
              for _ in range(8)]
+
+# (t, s, b, h, rank, masked): the fused sequence-parallel region
+SPLN_CASES = []
+for _ in range(6):
+    t = int(_rng.choice([1, 2, 4, 8]))
+    SPLN_CASES.append((t, t * int(_rng.integers(1, 40)), int(_rng.integers(1, 5)), _w8(8, 16384),
+                       int(_rng.integers(0, t)), bool(_rng.integers(0, 2))))

@@ -156,7 +156,7 @@ attn(1, 2072, 1032, 8, 2, 72, 2, pad=8)
 testing_entry_points()
 # the randomized parity tests' shapes
 sys.path.insert(0, sys.argv[1] + "/tests")
-from fuzz_cases import ATTN_CASES, MLP_CASES, SUM_CASES, SWIGLU_CASES, XENT_CASES
+from fuzz_cases import ATTN_CASES, MLP_CASES, SPLN_CASES, SUM_CASES, SWIGLU_CASES, XENT_CASES
 for b, s, h, ffn, t, _, _ in MLP_CASES:
     mlp(b, s, h, ffn, t, BF)
 for b, s, h, V, t in XENT_CASES:
@@ -167,6 +167,8 @@ for t, n, _ in SUM_CASES:
     sums(t, n, n)
 for b, s, h, nq, nkv, d, t, _ in ATTN_CASES:
     attn(b, s, h, nq, nkv, d, t)
+for t, s, b, h, _, _ in SPLN_CASES:
+    sp(t, s, b, h)
 print(json.dumps({"calls": len(calls), "checks": L.lgs_test_debug_checks(),
                   "min_checks_per_call": min(c for _, c in calls)}))
 '''

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from fuzz_cases import ATTN_CASES, MLP_CASES, SUM_CASES, SWIGLU_CASES, XENT_CASES
+from fuzz_cases import ATTN_CASES, MLP_CASES, SPLN_CASES, SUM_CASES, SWIGLU_CASES, XENT_CASES
 from gpu_util import assert_close, dev, f64, round_like, step
 from logit_gemm_shard_amd import binding as lgs
 from logit_gemm_shard_amd import synth
@@ -210,3 +210,27 @@ def test_fuzz_partial_sum_exact(case):
     lgs.shard_partial_sum("sum", t, n, parts.to(d), n, out)
     torch.cuda.synchronize()
     assert np.array_equal(f64(out), f64(parts).sum(axis=0))
+
+
+@pytest.mark.parametrize("case", SPLN_CASES, ids=_ids)
+def test_fuzz_sp_region(case):
+    t, s, b, h, r, masked = case
+    n = (s // t) * b
+    d = dev()
+    g = torch.Generator().manual_seed(5000 + h + s)
+    parts = torch.randn(t, s * b, h, generator=g).to(BF16)
+    res = torch.randn(n, h, generator=g).to(BF16)
+    gamma = (1 + 0.1 * torch.randn(h, generator=g)).to(BF16)
+    beta = (0.1 * torch.randn(h, generator=g)).to(BF16)
+    keep = (torch.rand(n, h, generator=g) > 0.2).to(torch.uint8) if masked else None
+    step(f"fuzz sp region {case}")
+    hs = torch.empty(n, h, dtype=BF16, device=d)
+    y = torch.empty(n, h, dtype=BF16, device=d)
+    lgs.shard_reduce_scatter_layernorm(t, r, s, b, h, parts.to(d), s * b * h, res.to(d), gamma.to(d), beta.to(d),
+                                       hs, y, keep=None if keep is None else keep.to(d), keep_scale=1.25)
+    torch.cuda.synchronize()
+    rh, ry = oracle.sp.exit_region([f64(p) for p in parts], s, b, t, r, f64(res), f64(gamma), f64(beta), 1e-5,
+                                   None if keep is None else keep.numpy(), 1.25)
+    assert_close("hs", hs, rh, BF16)
+    assert_close("y", y, ry, BF16)
+
