@@ -84,3 +84,41 @@ def exit_region(parts, s, b, t, r, residual, gamma, beta, eps=1e-5, keep=None, k
     d = z if keep is None else z * (np.asarray(keep) != 0) * float(keep_scale)
     hs = _f64(residual) + d
     return hs, layernorm(hs, gamma, beta, eps)
+
+
+def layernorm_backward(x, gamma, dy, eps=1e-5):
+    """Gradients of y = layernorm(x, gamma, beta, eps) for the upstream dy
+    (the chain rule through the per-row definition above):
+
+      xhat  = (x - mean) / sqrt(var + eps),  dxhat = dy * gamma
+      dx    = (dxhat - mean_h(dxhat) - xhat * mean_h(dxhat * xhat)) / sqrt(var + eps)
+      dgamma = sum over rows of dy * xhat,   dbeta = sum over rows of dy
+
+    Returns (dx, dgamma, dbeta)."""
+    x, dy = _f64(x), _f64(dy)
+    mean = x.mean(axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((x - mean) ** 2).mean(axis=1, keepdims=True) + eps)
+    xhat = (x - mean) * rstd
+    dxhat = dy * _f64(gamma)[None, :]
+    dx = (dxhat - dxhat.mean(axis=1, keepdims=True) - xhat * (dxhat * xhat).mean(axis=1, keepdims=True)) * rstd
+    return dx, (dy * xhat).sum(axis=0), dy.sum(axis=0)
+
+
+def exit_region_backward(hs, gamma, dy, dhs=None, eps=1e-5, keep=None, keep_scale=1.0):
+    """Backward of exit_region on rank r's chunk, from the gradient dy of its
+    LayerNorm output y and the gradient dhs that later layers send back along
+    the residual stream (None: none):
+
+      g      = dhs + dx of LayerNorm at hs     the gradient of hs, which is also
+                                               the residual input's gradient
+      dz     = g * keep * keep_scale  (or g)   the gradient of the rank's rows of
+                                               sum_i Z_i (the all-gather's input
+                                               in the backward)
+      dgamma, dbeta                            the rank's sums over its rows (a
+                                               partial: the ranks' sums add up)
+
+    Returns {"g", "dz", "dgamma", "dbeta"}."""
+    dx, dgamma, dbeta = layernorm_backward(hs, gamma, dy, eps)
+    g = dx if dhs is None else _f64(dhs) + dx
+    dz = g if keep is None else g * (np.asarray(keep) != 0) * float(keep_scale)
+    return {"g": g, "dz": dz, "dgamma": dgamma, "dbeta": dbeta}

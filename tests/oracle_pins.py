@@ -793,9 +793,96 @@ def check_sp_exit_region_split_identity(sp):
         assert _rel(hs1, res[:n] + z[:n]) < 1e-13
 
 
+def _fd(f, x, i, step=1e-6):
+    xp, xm = x.copy(), x.copy()
+    xp.flat[i] += step
+    xm.flat[i] -= step
+    return (f(xp) - f(xm)) / (2 * step)
+
+
+def check_sp_layernorm_backward_fd(sp):
+    """dx, dgamma, dbeta of LayerNorm against central finite differences of
+    L = sum(w * layernorm(x, gamma, beta)), every element."""
+    r_ = _rng(68)
+    x, g, b, w = r_.normal(size=(3, 6)), r_.normal(size=6), r_.normal(size=6), r_.normal(size=(3, 6))
+    eps = 1e-3
+    dx, dg, db = sp.layernorm_backward(x, g, w, eps)
+    for i in range(x.size):
+        assert abs(_fd(lambda v: (w * sp.layernorm(v, g, b, eps)).sum(), x, i) - dx.flat[i]) < 1e-7, i
+    for i in range(6):
+        assert abs(_fd(lambda v: (w * sp.layernorm(x, v, b, eps)).sum(), g, i) - dg[i]) < 1e-7, i
+        assert abs(_fd(lambda v: (w * sp.layernorm(x, g, v, eps)).sum(), b, i) - db[i]) < 1e-7, i
+
+
+def check_sp_layernorm_backward_closed_forms(sp):
+    """A row's dx sums to zero (the output ignores a shift of the row); with
+    eps = 0 it is also orthogonal to the normalised row (the output ignores a
+    scaling); dbeta is the column sum of dy."""
+    r_ = _rng(69)
+    x, g, dy = r_.normal(size=(5, 11)), r_.normal(size=11), r_.normal(size=(5, 11))
+    dx, _, db = sp.layernorm_backward(x, g, dy, 1e-5)
+    assert np.abs(dx.sum(axis=1)).max() < 1e-12
+    assert np.array_equal(db, dy.sum(axis=0))
+    dx0, _, _ = sp.layernorm_backward(x, g, dy, 0.0)
+    xc = x - x.mean(axis=1, keepdims=True)
+    assert np.abs((dx0 * xc).sum(axis=1)).max() < 1e-12
+
+
+def check_sp_region_backward_fd(sp):
+    """The region's backward against finite differences of
+    L = sum(w1 * y) + sum(w2 * hs) through exit_region: g is dL/d(residual),
+    dz is dL/d(part_i) on the rank's rows for every i, dgamma and dbeta."""
+    r_ = _rng(70)
+    s, b, h, t, r = 4, 1, 5, 2, 1
+    n = (s // t) * b
+    parts = [r_.normal(size=(s * b, h)) for _ in range(t)]
+    res, g, bb = r_.normal(size=(n, h)), r_.normal(size=h), r_.normal(size=h)
+    keep = (r_.random(size=(n, h)) > 0.3).astype(np.uint8)
+    w1, w2 = r_.normal(size=(n, h)), r_.normal(size=(n, h))
+    eps, sc = 1e-3, 1.5
+
+    def loss(P=parts, R=res, G=g, B=bb):
+        hs_, y_ = sp.exit_region(P, s, b, t, r, R, G, B, eps, keep, sc)
+        return (w1 * y_).sum() + (w2 * hs_).sum()
+    hs, _ = sp.exit_region(parts, s, b, t, r, res, g, bb, eps, keep, sc)
+    out = sp.exit_region_backward(hs, g, w1, w2, eps, keep, sc)
+    for i in range(res.size):
+        assert abs(_fd(lambda v: loss(R=v), res, i) - out["g"].flat[i]) < 1e-6, i
+    a = r * n * h
+    for k in range(t):
+        for i in range(n * h):
+            def lk(v, k=k):
+                P = [p.copy() for p in parts]
+                P[k] = v
+                return loss(P=P)
+            assert abs(_fd(lk, parts[k], a + i) - out["dz"].flat[i]) < 1e-6, (k, i)
+    for i in range(h):
+        assert abs(_fd(lambda v: loss(G=v), g, i) - out["dgamma"][i]) < 1e-6, i
+        assert abs(_fd(lambda v: loss(B=v), bb, i) - out["dbeta"][i]) < 1e-6, i
+
+
+def check_sp_region_backward_split(sp):
+    """The ranks' dgamma and dbeta add up to those of the whole tensor, and
+    their g and dz chunks, gathered, equal the whole tensor's."""
+    r_ = _rng(71)
+    s, b, h, t = 8, 2, 7, 4
+    hs, dy, dhs = r_.normal(size=(s * b, h)), r_.normal(size=(s * b, h)), r_.normal(size=(s * b, h))
+    keep = (r_.random(size=(s * b, h)) > 0.2).astype(np.uint8)
+    g = r_.normal(size=h)
+    full = sp.exit_region_backward(hs, g, dy, dhs, 1e-5, keep, 1.25)
+    n = (s // t) * b
+    ch = [sp.exit_region_backward(hs[k * n:(k + 1) * n], g, dy[k * n:(k + 1) * n], dhs[k * n:(k + 1) * n], 1e-5,
+                                  keep[k * n:(k + 1) * n], 1.25) for k in range(t)]
+    assert _rel(sum(c["dgamma"] for c in ch), full["dgamma"]) < 1e-12
+    assert _rel(sum(c["dbeta"] for c in ch), full["dbeta"]) < 1e-12
+    assert _rel(np.concatenate([c["g"] for c in ch]), full["g"]) < 1e-13
+    assert _rel(np.concatenate([c["dz"] for c in ch]), full["dz"]) < 1e-13
+
+
 SP_CHECKS = [check_sp_reduce_scatter_brute, check_sp_identity, check_sp_volume, check_sp_layernorm_brute,
              check_sp_layernorm_closed_forms, check_sp_layernorm_library, check_sp_exit_region_brute,
-             check_sp_exit_region_split_identity]
+             check_sp_exit_region_split_identity, check_sp_layernorm_backward_fd,
+             check_sp_layernorm_backward_closed_forms, check_sp_region_backward_fd, check_sp_region_backward_split]
 
 
 # ------------------------------------------------------ attention projections

@@ -437,7 +437,49 @@ def _exit_norm_before_add(parts, s, b, t, r, residual, gamma, beta, eps=1e-5, ke
     return residual + d, _REAL_LN(d, gamma, beta, eps) + residual
 
 
+_REAL_LN_BWD, _REAL_EXIT_BWD = sp.layernorm_backward, sp.exit_region_backward
+
+
+def _lnb_core(x, gamma, dy, eps, drop_mean=False, drop_proj=False, dgamma_plain=False):
+    x, dy = np.asarray(x, dtype=np.float64), np.asarray(dy, dtype=np.float64)
+    mean = x.mean(axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((x - mean) ** 2).mean(axis=1, keepdims=True) + eps)
+    xhat = (x - mean) * rstd
+    dxh = dy * gamma
+    dx = dxh
+    if not drop_mean:
+        dx = dx - dxh.mean(axis=1, keepdims=True)
+    if not drop_proj:
+        dx = dx - xhat * (dxh * xhat).mean(axis=1, keepdims=True)
+    return dx * rstd, (dy if dgamma_plain else dy * xhat).sum(axis=0), dy.sum(axis=0)
+
+
+def _lnb_no_mean(x, gamma, dy, eps=1e-5):
+    return _lnb_core(x, gamma, dy, eps, drop_mean=True)
+
+
+def _lnb_no_projection(x, gamma, dy, eps=1e-5):
+    return _lnb_core(x, gamma, dy, eps, drop_proj=True)
+
+
+def _lnb_dgamma_without_xhat(x, gamma, dy, eps=1e-5):
+    return _lnb_core(x, gamma, dy, eps, dgamma_plain=True)
+
+
+def _exitb_dz_unmasked(hs, gamma, dy, dhs=None, eps=1e-5, keep=None, keep_scale=1.0):
+    return _REAL_EXIT_BWD(hs, gamma, dy, dhs, eps, None, keep_scale)
+
+
+def _exitb_no_residual_grad(hs, gamma, dy, dhs=None, eps=1e-5, keep=None, keep_scale=1.0):
+    return _REAL_EXIT_BWD(hs, gamma, dy, None, eps, keep, keep_scale)
+
+
 SP_MUTANTS = {
+    "lnb_no_mean_term": ("layernorm_backward", _lnb_no_mean),
+    "lnb_no_projection_term": ("layernorm_backward", _lnb_no_projection),
+    "lnb_dgamma_without_xhat": ("layernorm_backward", _lnb_dgamma_without_xhat),
+    "exitb_dz_unmasked": ("exit_region_backward", _exitb_dz_unmasked),
+    "exitb_residual_grad_dropped": ("exit_region_backward", _exitb_no_residual_grad),
     "ln_no_eps": ("layernorm", _ln_no_eps),
     "ln_unbiased_variance": ("layernorm", _ln_unbiased),
     "ln_stats_over_tokens": ("layernorm", _ln_stats_over_tokens),
