@@ -742,9 +742,21 @@ def per_config(torch, lgs, reps):
         lgs.shard_reduce_scatter_layernorm(t, r, w.s, w.b, h, parts, M * h, res[r], gamma, beta, hs, ys,
                                            keep=keep[r], keep_scale=1 / 0.9)
         i[0] += 1
+    dys, dhss = randn(t, M // t, h), randn(t, M // t, h)
+    gg, dzz = torch.empty(M // t, h, dtype=bf, device=dev), torch.empty(M // t, h, dtype=bf, device=dev)
+    dgam, dbet = torch.empty(h, device=dev), torch.empty(h, device=dev)
+    lws = torch.empty(lgs.layernorm_bwd_workspace_bytes(t, w.s, w.b, h), dtype=torch.uint8, device=dev)
+
+    def ln_bwd():
+        r = i[0] % t
+        lgs.shard_layernorm_bwd(t, r, w.s, w.b, h, res[r], dys[r], gamma, gg, dzz, dgam, dbet, dhs=dhss[r],
+                                keep=keep[r], keep_scale=1 / 0.9, workspace=lws)
+        i[0] += 1
     rs_ms = time_calls(torch, rs, reps)
     ag_ms = time_calls(torch, ag, reps)
     ln_ms = time_calls(torch, rs_ln, reps)
+    lb_ms = time_calls(torch, ln_bwd, reps)
+    lb_bytes = 3 * chunk * 2 + chunk + 2 * chunk * 2 + h * 2 + 2 * h * 4
     rs_bytes, ag_bytes = (t + 1) * chunk * 2, 2 * M * h * 2
     ln_bytes = (t + 1) * chunk * 2 + chunk + 2 * chunk * 2 + 2 * h * 2
     out["sp_8p3b"] = {"reduce_scatter_us": round(rs_ms * 1e3, 2),
@@ -754,9 +766,12 @@ def per_config(torch, lgs, reps):
                       "rs_layernorm_us": round(ln_ms * 1e3, 2),
                       "rs_layernorm_GBs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
                       "rs_layernorm_frac_hbm": round(ln_bytes / (ln_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "layernorm_bwd_us": round(lb_ms * 1e3, 2),
+                      "layernorm_bwd_GBs": round(lb_bytes / (lb_ms * 1e-3) / 1e9, 1),
                       "note": "bytes = every byte read once + written once; HBM peak 8000 GB/s; "
                               "rs_layernorm: the 8 partials' rank rows, residual, keep mask read, hs and y "
-                              "written (dropout p = 0.1)"}
+                              "written (dropout p = 0.1); layernorm_bwd: hs, dy, dhs, mask read, g and dz "
+                              "written (the fp32 column partials not counted)"}
     return out
 
 

@@ -456,6 +456,34 @@ int shard_reduce_scatter_layernorm(int t, int rank, int s, int b, int h, int dty
                                    float keep_scale, const void* gamma, const void* beta, float eps,
                                    void* hs, void* y, void* stream);
 
+/*
+ * shard_layernorm_bwd -- the backward of shard_reduce_scatter_layernorm's
+ * region on rank r's rows, from dy (the gradient of y) and dhs (the gradient
+ * later layers send back along the residual stream; NULL = none).  LayerNorm's
+ * statistics are recomputed from the stored hs (bf16).  Per row j:
+ *
+ *   xhat  = (hs_j - mean) / sqrt(var + eps),   dxhat = dy_j * gamma
+ *   g_j   = (dxhat - mean_h(dxhat) - xhat * mean_h(dxhat * xhat))
+ *           / sqrt(var + eps) + dhs_j            -> g  [(s/t)*b, h] bf16
+ *           (the gradient of hs, which is also the residual input's)
+ *   dz_j  = keep ? (keep[j*h + c] != 0 ? g_j[c] * keep_scale : 0) : g_j[c]
+ *                                                -> dz [(s/t)*b, h] bf16
+ *           (the gradient of the rank's rows of sum_i Z_i: in the backward
+ *           the all-gather of the t ranks' dz feeds the row-parallel GEMM)
+ *   dgamma = sum_j dy_j * xhat,  dbeta = sum_j dy_j   -> [h] fp32 each
+ *           (the rank's rows only: the ranks' sums add up to the whole's)
+ *
+ * The column sums go through fp32 partials in the workspace
+ * (lgs_layernorm_bwd_workspace_bytes, 16-byte aligned) and are added in a
+ * fixed order.  Same dtype, alignment and h rules as the forward; eps must be
+ * the forward's.  Outputs must not overlap the inputs or each other.
+ */
+size_t lgs_layernorm_bwd_workspace_bytes(int t, int s, int b, int h, int dtype);
+int shard_layernorm_bwd(int t, int rank, int s, int b, int h, int dtype, const void* hs, const void* dy,
+                        const void* dhs, const uint8_t* keep, float keep_scale, const void* gamma, float eps,
+                        void* g, void* dz, float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

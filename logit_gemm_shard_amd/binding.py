@@ -69,6 +69,9 @@ SIGNATURES = [
     ("shard_all_gather", _i, [_i, _i, _i, _i, _i, _p, _i64, _p, _p]),
     ("shard_reduce_scatter_layernorm", _i,
      [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _p, ctypes.c_float, _p, _p, ctypes.c_float, _p, _p, _p]),
+    ("lgs_layernorm_bwd_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
+    ("shard_layernorm_bwd", _i,
+     [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, ctypes.c_float, _p, ctypes.c_float, _p, _p, _p, _p, _p, _sz, _p]),
     # include/lgs_testing.h
     ("lgs_test_num_tiles", _i, []),
     ("lgs_test_tile_shape", _i, [_i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
@@ -428,6 +431,27 @@ def shard_reduce_scatter_layernorm(t, rank, s, b, h, parts, part_stride, residua
                                                 keep_scale, gamma.data_ptr(), beta.data_ptr(), eps, hs.data_ptr(),
                                                 y.data_ptr(), _stream(stream)))
     return hs, y
+
+
+def layernorm_bwd_workspace_bytes(t, s, b, h, dtype=torch.bfloat16):
+    return lib().lgs_layernorm_bwd_workspace_bytes(t, s, b, h, _DT[dtype])
+
+
+def shard_layernorm_bwd(t, rank, s, b, h, hs, dy, gamma, g, dz, dgamma, dbeta, dhs=None, keep=None,
+                        keep_scale=1.0, eps=1e-5, workspace=None, stream=None):
+    """Backward of the sequence-parallel region on the rank's rows: g (the
+    gradient of hs and of the residual), dz (the masked g) and the rows'
+    dgamma, dbeta (fp32)."""
+    L = lib()
+    dt = _dtype(hs)
+    need = L.lgs_layernorm_bwd_workspace_bytes(t, s, b, h, dt)
+    ws, ws_bytes = _workspace(need, hs.device, workspace, stream)
+    _check(L.shard_layernorm_bwd(t, rank, s, b, h, dt, hs.data_ptr(), dy.data_ptr(),
+                                 None if dhs is None else dhs.data_ptr(), None if keep is None else keep.data_ptr(),
+                                 keep_scale, gamma.data_ptr(), eps, g.data_ptr(), dz.data_ptr(), dgamma.data_ptr(),
+                                 dbeta.data_ptr(), _ptr(ws) if isinstance(ws, torch.Tensor) else ws, ws_bytes,
+                                 _stream(stream)))
+    return g, dz, dgamma, dbeta
 
 
 def shard_all_gather(t, s, b, h, shards, shard_stride, out, stream=None):

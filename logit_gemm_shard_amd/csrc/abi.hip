@@ -592,6 +592,50 @@ LGS_API int shard_reduce_scatter_layernorm(int t, int rank, int s, int b, int h,
                                     keep_scale, gamma, beta, eps, hs, y, (hipStream_t)stream));
 }
 
+LGS_API size_t lgs_layernorm_bwd_workspace_bytes(int t, int s, int b, int h, int dtype) {
+  if (t <= 0 || s <= 0 || b <= 0 || h <= 0 || s % t != 0 || dtype != LGS_BF16 || h % 8 != 0 ||
+      h > lgs::rs_layernorm_max_h() || (int64_t)(s / t) * b > INT_MAX)
+    return 0;
+  return round256(lgs::layernorm_bwd_scratch_bytes((s / t) * b, h));
+}
+
+LGS_API int shard_layernorm_bwd(int t, int rank, int s, int b, int h, int dtype, const void* hs, const void* dy,
+                                const void* dhs, const uint8_t* keep, float keep_scale, const void* gamma,
+                                float eps, void* g, void* dz, float* dgamma, float* dbeta, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  int st = check_sp(t, s, b, h);
+  if (st) return st;
+  if (rank < 0 || rank >= t) return fail(LGS_ERR_INVALID_ARG, "rank %d not in [0, %d)", rank, t);
+  if ((st = check_dtype(dtype))) return st;
+  if (dtype != LGS_BF16) return fail(LGS_ERR_UNSUPPORTED, "the sequence-parallel region's backward is bf16 only");
+  if (h % 8 != 0 || h > lgs::rs_layernorm_max_h())
+    return fail(LGS_ERR_UNSUPPORTED, "h=%d must be a multiple of 8 and at most %d", h, lgs::rs_layernorm_max_h());
+  if (!hs || !dy || !gamma || !g || !dz || !dgamma || !dbeta)
+    return fail(LGS_ERR_INVALID_ARG, "hs, dy, gamma, g, dz, dgamma and dbeta are required");
+  if (!(eps > 0.f) || !std::isfinite(eps) || !std::isfinite(keep_scale))
+    return fail(LGS_ERR_INVALID_ARG, "eps must be positive and finite, keep_scale finite");
+  for (const void* p : {hs, dy, dhs, gamma, (const void*)g, (const void*)dz, (const void*)dgamma, (const void*)dbeta})
+    if (p && !aligned(p, 16))
+      return fail(LGS_ERR_UNSUPPORTED, "hs, dy, dhs, gamma, g, dz, dgamma and dbeta need 16-byte alignment");
+  if (keep && !aligned(keep, 8)) return fail(LGS_ERR_UNSUPPORTED, "the keep mask needs 8-byte alignment");
+  const int rows = (s / t) * b;
+  const size_t need = lgs::layernorm_bwd_scratch_bytes(rows, h);
+  if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return fail(LGS_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, %zu given", need,
+                workspace ? workspace_bytes : 0);
+  const size_t chunk = (size_t)rows * h;
+  for (const void* p : {hs, dy, dhs, (const void*)g, (const void*)dz})
+    if (p) allow(p, chunk * 2);
+  if (keep) allow(keep, chunk);
+  allow(gamma, (size_t)h * 2);
+  allow(dgamma, (size_t)h * 4);
+  allow(dbeta, (size_t)h * 4);
+  if (need) allow(workspace, need);
+  clear_hip_error();
+  return launched(lgs::layernorm_bwd(rows, h, hs, dy, dhs, keep, keep_scale, gamma, eps, g, dz, dgamma, dbeta,
+                                     workspace, (hipStream_t)stream));
+}
+
 LGS_API int shard_all_gather(int t, int s, int b, int h, int dtype, const void* shards,
                              int64_t shard_stride, void* out, void* stream) {
   int st = check_sp(t, s, b, h);

@@ -117,6 +117,13 @@ hipError_t all_gather(int t, int64_t chunk, bool bf16, const void* shards, int64
 // t partials' rows (rank r's chunk of each), dropout with the keep mask (if
 // any), the residual add (hs) and LayerNorm over h (y).  h <= rs_layernorm_max_h().
 int rs_layernorm_max_h();
+// Its backward on `rows` rows (bf16): g = dhs + LayerNorm's dx at hs, dz = the
+// masked and scaled g, and the rows' dgamma, dbeta (fp32; column partials of
+// layernorm_bwd_scratch_bytes in scratch, then summed in order).
+size_t layernorm_bwd_scratch_bytes(int rows, int h);
+hipError_t layernorm_bwd(int rows, int h, const void* hs, const void* dy, const void* dhs, const uint8_t* keep,
+                         float keep_scale, const void* gamma, float eps, void* g, void* dz, float* dgamma,
+                         float* dbeta, void* scratch, hipStream_t s);
 hipError_t rs_layernorm(int t, int rows, int h, int rank, const void* parts, int64_t stride,
                         const void* residual, const uint8_t* keep, float keep_scale, const void* gamma,
                         const void* beta, float eps, void* hs, void* y, hipStream_t s);

@@ -371,6 +371,20 @@ def test_sp_validation(L):
     assert call(res=None) == 1 and call(g=None) == 1 and call(y=None) == 1
     assert call(hs=FAKE + 8) == 2               # 16-byte alignment
     assert call(keep=FAKE + 4) == 2             # the mask's 8-byte alignment
+    # the backward: (t, rank, s, b, h, dtype, hs, dy, dhs, keep, scale, gamma, eps, g, dz, dgamma, dbeta, ws, wsb)
+    wsq = L.lgs_layernorm_bwd_workspace_bytes
+    assert wsq(8, 1024, 8, 3072, 1) == 256 * 2 * 3072 * 4    # 1024 rows: 256 blocks of 4, two fp32 rows each
+    assert wsq(4, 8, 2, 16, 1) == 256 * ((4 * 2 * 16 * 4 + 255) // 256)
+    assert wsq(4, 8, 2, 12, 1) == 0 and wsq(4, 8, 2, 16, 0) == 0 and wsq(4, 10, 2, 16, 1) == 0
+    bw = L.shard_layernorm_bwd
+
+    def bcall(t=4, r=0, s=8, b=2, h=16, dt=1, dhs=None, keep=None, scale=1.0, eps=1e-5, g=FAKE, ws=FAKE,
+              wsb=1 << 20):
+        return bw(t, r, s, b, h, dt, FAKE, FAKE, dhs, keep, scale, FAKE, eps, g, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert bcall(s=10) == 1 and bcall(r=-1) == 1 and bcall(dt=0) == 2 and bcall(h=12) == 2
+    assert bcall(eps=-1.0) == 1 and bcall(g=None) == 1
+    assert bcall(ws=None) == 3 and bcall(wsb=16) == 3      # workspace missing or short
+    assert bcall(dhs=FAKE + 2) == 2 and bcall(keep=FAKE + 1) == 2
 
 
 def test_binding_raises_when_library_missing(tmp_path, monkeypatch):

@@ -105,6 +105,9 @@ def sp(t, s, b, h):
             for keep in (None, buf()):
                 call("shard_reduce_scatter_layernorm", t, r, s, b, h, BF, buf(), s * b * h + 8 * r, buf(), keep,
                      1.25, buf(), buf(), 1e-5, buf(), buf(), None)
+                w, nw = ws(L.lgs_layernorm_bwd_workspace_bytes(t, s, b, h, BF))
+                call("shard_layernorm_bwd", t, r, s, b, h, BF, buf(), buf(), keep and buf(), keep, 1.25, buf(), 1e-5,
+                     buf(), buf(), buf(), buf(), w, nw, None)
     call("shard_all_gather", t, s, b, h, BF, buf(), (s // t) * b * h + 40, buf(), None)
 
 def attn(b, s, h, nq, nkv, d, t, pad=0):

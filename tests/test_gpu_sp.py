@@ -159,3 +159,41 @@ def test_rs_layernorm_unit_rows_and_guards():
     for buf in (hs_buf, y_buf):
         assert torch.isnan(buf[:pad].float()).all() and torch.isnan(buf[pad + n * h:].float()).all()
         assert torch.isfinite(buf[pad:pad + n * h].float()).all()
+
+
+@pytest.mark.parametrize("with_mask,with_dhs", [(False, False), (True, True)], ids=["plain", "mask+dhs"])
+@pytest.mark.parametrize("shape", [(8, 1024, 8, 3072), (3, 12, 3, 72), (2, 10, 5, 8), (4, 64, 2, 8192),
+                                   (1, 5, 1, 16384), (2, 700, 1, 2056)], ids=lambda s: "x".join(map(str, s)))
+def test_layernorm_bwd_every_element(shape, with_mask, with_dhs):
+    """The region's backward on a rank's rows against the oracle: g and dz on
+    every element (bf16 tolerance), dgamma and dbeta (fp32 tolerance); a
+    second call repeats every bit (the column sums go in a fixed order)."""
+    t, s, b, h = shape
+    d = dev()
+    n = (s // t) * b
+    g_ = torch.Generator().manual_seed(9 * t + h)
+    hs = torch.randn(n, h, generator=g_).to(BF16)
+    dy = torch.randn(n, h, generator=g_).to(BF16)
+    dhs = torch.randn(n, h, generator=g_).to(BF16) if with_dhs else None
+    gamma = (1 + 0.1 * torch.randn(h, generator=g_)).to(BF16)
+    keep = (torch.rand(n, h, generator=g_) > 0.1).to(torch.uint8) if with_mask else None
+    step(f"layernorm bwd {shape} mask={with_mask} dhs={with_dhs}")
+    outs = []
+    for _ in range(2):
+        G = torch.empty(n, h, dtype=BF16, device=d)
+        dz = torch.empty(n, h, dtype=BF16, device=d)
+        dg, db = torch.empty(h, dtype=F32, device=d), torch.empty(h, dtype=F32, device=d)
+        lgs.shard_layernorm_bwd(t, t - 1, s, b, h, hs.to(d), dy.to(d), gamma.to(d), G, dz, dg, db,
+                                dhs=None if dhs is None else dhs.to(d), keep=None if keep is None else keep.to(d),
+                                keep_scale=1 / 0.9)
+        outs.append((G, dz, dg, db))
+    torch.cuda.synchronize()
+    ref = oracle.sp.exit_region_backward(f64(hs), f64(gamma), f64(dy), None if dhs is None else f64(dhs), 1e-5,
+                                         None if keep is None else keep.numpy(), 1 / 0.9)
+    G, dz, dg, db = outs[0]
+    assert_close("g", G, ref["g"], BF16)
+    assert_close("dz", dz, ref["dz"], BF16)
+    assert_close("dgamma", dg, ref["dgamma"], F32)
+    assert_close("dbeta", db, ref["dbeta"], F32)
+    for a, c in zip(outs[0], outs[1]):
+        assert torch.equal(a, c)
