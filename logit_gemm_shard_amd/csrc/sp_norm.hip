@@ -124,23 +124,26 @@ __global__ __launch_bounds__(kThreads) void rs_layernorm_kernel(
 //   dx   = (dxhat - mean_h(dxhat) - xhat * mean_h(dxhat * xhat)) * rstd
 //   g    = dx + dhs              the gradient of hs and of the residual input
 //   dz   = keep ? g * keep_scale : 0  (g without a mask)
-// and each block adds dy * xhat and dy over its rows into its own fp32 column
-// partials (dgamma, dbeta), which col_sum_kernel then adds in block order.
-// Block sums of two values at a time (the two means of a row).
-__device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
+// Each block takes a run of rows, RB at a time: every load of a batch (hs,
+// dy, dhs, mask) is issued before its block sums (2 RB values reduced
+// together), so the rows' memory latencies overlap.  The block adds dy * xhat and dy over its
+// rows into its own fp32 column partials (dgamma, dbeta); col_sum_kernel then
+// adds the blocks' partials in block order.
+
+// Block sums of N values at once, the same in every thread; wave order.
+template <int N>
+__device__ __forceinline__ void block_sums(float (&v)[N], float* red) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    a += __shfl_xor(a, off);
-    b += __shfl_xor(b, off);
-  }
+  for (int q = 0; q < N; ++q)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v[q] += __shfl_xor(v[q], off);
+  __syncthreads();  // the previous use of red has been read
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int q = 0; q < N; ++q) red[(threadIdx.x >> 6) * N + q] = v[q];
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    red[threadIdx.x >> 6] = a;
-    red[4 + (threadIdx.x >> 6)] = b;
-  }
-  __syncthreads();
-  a = ((red[0] + red[1]) + red[2]) + red[3];
-  b = ((red[4] + red[5]) + red[6]) + red[7];
+#pragma unroll
+  for (int q = 0; q < N; ++q) v[q] = ((red[q] + red[N + q]) + red[2 * N + q]) + red[3 * N + q];
 }
 
 __device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
@@ -149,83 +152,110 @@ __device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
   for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
 }
 
-template <int KC>  // 16-byte chunks per thread: h <= KC * 2048
+template <int KC, int RB>  // KC 16-byte chunks per thread (h <= KC * 2048), RB rows per batch
 __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
     const bf16* __restrict__ hs, const bf16* __restrict__ dy, const bf16* __restrict__ dhs,
     const uint8_t* __restrict__ keep, float keep_scale, const bf16* __restrict__ gamma, float eps, int rows,
     int rpb, int h, bf16* __restrict__ g, bf16* __restrict__ dz, float* __restrict__ part) {
-  __shared__ float red[8];
+  __shared__ float red[4 * 2 * RB];
   const int nch = h / 8;
-  float cg[KC][8], cb[KC][8];
+  float cg[KC][8], cb[KC][8], gm[KC][8];
 #pragma unroll
-  for (int c = 0; c < KC; ++c)
+  for (int c = 0; c < KC; ++c) {
+    const int k = threadIdx.x + kThreads * c;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cg[c][e] = cb[c][e] = 0.f;
+    for (int e = 0; e < 8; ++e) cg[c][e] = cb[c][e] = gm[c][e] = 0.f;
+    if (k < nch) load8(gamma + 8 * k, gm[c]);
+  }
   const int r0 = blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
-  for (int row = r0; row < r1; ++row) {
-    const int64_t base = (int64_t)row * h;
-    float x[KC][8], d[KC][8];
-    float s1 = 0.f, s2 = 0.f;
+  for (int rb = r0; rb < r1; rb += RB) {
+    float x[RB][KC][8], d[RB][KC][8];
+    u32x4 up[RB][KC];
+    uint64_t mk[RB][KC];
+    float s[2 * RB];
+    // every load of the batch: hs, dy, dhs and the mask (rows past r1 read
+    // as zeros and are not stored)
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int k = threadIdx.x + kThreads * c;
-      if (k >= nch) break;
-      load8(hs + base + 8 * k, x[c]);
+    for (int q = 0; q < RB; ++q) {
+      const int64_t base = (int64_t)(rb + q) * h;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s1 += x[c][e];
-    }
-    block_sum2(s1, s2, red);
-    const float mean = s1 / (float)h;
-    float sq = 0.f, unused = 0.f;
+      for (int c = 0; c < KC; ++c) {
+        const int k = threadIdx.x + kThreads * c;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      if (threadIdx.x + kThreads * c >= nch) break;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[c][e] -= mean;
-        sq += x[c][e] * x[c][e];
+        for (int e = 0; e < 8; ++e) x[q][c][e] = d[q][c][e] = 0.f;
+        up[q][c] = u32x4{0u, 0u, 0u, 0u};
+        mk[q][c] = ~0ull;
+        if (rb + q < r1 && k < nch) {
+          load8(hs + base + 8 * k, x[q][c]);
+          load8(dy + base + 8 * k, d[q][c]);
+          if (dhs) up[q][c] = *reinterpret_cast<const u32x4*>(dhs + base + 8 * k);
+          if (keep) mk[q][c] = *reinterpret_cast<const uint64_t*>(keep + base + 8 * k);
+        }
       }
     }
-    block_sum2(sq, unused, red);
-    const float rstd = 1.f / sqrtf(sq / (float)h + eps);
-    float m1 = 0.f, m2 = 0.f;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int k = threadIdx.x + kThreads * c;
-      if (k >= nch) break;
-      float gm[8];
-      load8(dy + base + 8 * k, d[c]);
-      load8(gamma + 8 * k, gm);
+    for (int q = 0; q < RB; ++q) {
+      s[q] = s[RB + q] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[c][e] *= rstd;  // xhat
-        cg[c][e] += d[c][e] * x[c][e];
-        cb[c][e] += d[c][e];
-        d[c][e] *= gm[e];  // dxhat
-        m1 += d[c][e];
-        m2 += d[c][e] * x[c][e];
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[q] += x[q][c][e];
+    }
+    block_sums<2 * RB>(s, red);  // s[q]: the row sums
+    float rstd[RB];
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const float mean = s[q] / (float)h;
+      s[q] = s[RB + q] = 0.f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        if (threadIdx.x + kThreads * c >= nch) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[q][c][e] -= mean;
+          s[q] += x[q][c][e] * x[q][c][e];
+        }
       }
     }
-    block_sum2(m1, m2, red);
-    m1 /= (float)h;
-    m2 /= (float)h;
+    block_sums<2 * RB>(s, red);  // s[q]: the squared deviations
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int k = threadIdx.x + kThreads * c;
-      if (k >= nch) break;
-      float up[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (dhs) load8(dhs + base + 8 * k, up);
-      uint64_t m = ~0ull;
-      if (keep) m = *reinterpret_cast<const uint64_t*>(keep + base + 8 * k);
-      bf16x8 og, oz;
+    for (int q = 0; q < RB; ++q) {
+      rstd[q] = 1.f / sqrtf(s[q] / (float)h + eps);
+      s[q] = s[RB + q] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gv = (d[c][e] - m1 - x[c][e] * m2) * rstd + up[e];
-        og[e] = (bf16)gv;
-        oz[e] = (bf16)(keep ? (((m >> (8 * e)) & 0xffu) ? gv * keep_scale : 0.f) : gv);
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[q][c][e] *= rstd[q];  // xhat (zero past the row or past h)
+          cg[c][e] += d[q][c][e] * x[q][c][e];
+          cb[c][e] += d[q][c][e];
+          d[q][c][e] *= gm[c][e];  // dxhat
+          s[q] += d[q][c][e];
+          s[RB + q] += d[q][c][e] * x[q][c][e];
+        }
+    }
+    block_sums<2 * RB>(s, red);  // the two means' numerators
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      if (rb + q >= r1) break;
+      const int64_t base = (int64_t)(rb + q) * h;
+      const float m1 = s[q] / (float)h, m2 = s[RB + q] / (float)h;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int k = threadIdx.x + kThreads * c;
+        if (k >= nch) continue;
+        const bf16x8 u8 = __builtin_bit_cast(bf16x8, up[q][c]);
+        const uint64_t m = mk[q][c];
+        bf16x8 og, oz;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float gv = (d[q][c][e] - m1 - x[q][c][e] * m2) * rstd[q] + (float)u8[e];
+          og[e] = (bf16)gv;
+          oz[e] = (bf16)(keep ? (((m >> (8 * e)) & 0xffu) ? gv * keep_scale : 0.f) : gv);
+        }
+        *reinterpret_cast<u32x4*>(g + base + 8 * k) = __builtin_bit_cast(u32x4, og);
+        *reinterpret_cast<u32x4*>(dz + base + 8 * k) = __builtin_bit_cast(u32x4, oz);
       }
-      *reinterpret_cast<u32x4*>(g + base + 8 * k) = __builtin_bit_cast(u32x4, og);
-      *reinterpret_cast<u32x4*>(dz + base + 8 * k) = __builtin_bit_cast(u32x4, oz);
     }
   }
   float* pg = part + (int64_t)blockIdx.x * 2 * h;
@@ -241,17 +271,36 @@ __global__ __launch_bounds__(kThreads) void layernorm_bwd_kernel(
   }
 }
 
-// dgamma[j] and dbeta[j]: the blocks' column partials added in block order.
+// dgamma[j] and dbeta[j] (j over the 2h columns of the partials): block x
+// takes 64 consecutive columns; its four waves sum every fourth block's
+// partial (wave w the blocks w, w + 4, ...; a wave's loads cover 256
+// contiguous bytes), and the four sums are added in wave order.
 __global__ __launch_bounds__(256) void col_sum_kernel(const float* __restrict__ part, int nblk, int h,
                                                      float* __restrict__ dgamma, float* __restrict__ dbeta) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= 2 * h) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
   float acc = 0.f;
-  for (int q = 0; q < nblk; ++q) acc += part[(int64_t)q * 2 * h + j];
-  if (j < h)
-    dgamma[j] = acc;
-  else
-    dbeta[j - h] = acc;
+  if (j < 2 * h)
+    for (int q0 = w; q0 < nblk; q0 += 4 * 8) {  // eight loads in flight, added in block order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + 4 * u;
+        v[u] = q < nblk ? part[(int64_t)q * 2 * h + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w == 0 && j < 2 * h) {
+    const float v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    if (j < h)
+      dgamma[j] = v;
+    else
+      dbeta[j - h] = v;
+  }
 }
 
 // Rows per block of the backward: at most 256 blocks, so the column partials
@@ -276,7 +325,7 @@ hipError_t layernorm_bwd(int rows, int h, const void* hs, const void* dy, const 
   LGS_NEED(dgamma, (size_t)h * 4, "dgamma");
   LGS_NEED(dbeta, (size_t)h * 4, "dbeta");
   if (rows == 0) {  // no rows: the rank's partial sums are zero
-    LGS_LAUNCH(col_sum_kernel, dim3((2 * h + 255) / 256), dim3(256), 0, s, (const float*)nullptr, 0, h, dgamma, dbeta);
+    LGS_LAUNCH(col_sum_kernel, dim3((2 * h + 63) / 64), dim3(256), 0, s, (const float*)nullptr, 0, h, dgamma, dbeta);
     return LGS_LAUNCH_STATUS();
   }
   const int rpb = bwd_rows_per_block(rows), nblk = (rows + rpb - 1) / rpb;
@@ -289,21 +338,24 @@ hipError_t layernorm_bwd(int rows, int h, const void* hs, const void* dy, const 
   LGS_NEED(dz, chunk * 2, "dz");
   LGS_NEED(scratch, layernorm_bwd_scratch_bytes(rows, h), "column partials");
   const int kc = (h / 8 + kThreads - 1) / kThreads;
-  auto launch = [&](auto kc_c) {
-    constexpr int KC = decltype(kc_c)::value;
-    LGS_LAUNCH(layernorm_bwd_kernel<KC>, dim3(nblk), dim3(kThreads), 0, s, (const bf16*)hs, (const bf16*)dy,
-               (const bf16*)dhs, keep, keep_scale, (const bf16*)gamma, eps, rows, rpb, h, (bf16*)g, (bf16*)dz,
-               (float*)scratch);
+  auto launch = [&](auto kc_c, auto rb_c) {
+    constexpr int KC = decltype(kc_c)::value, RB = decltype(rb_c)::value;
+    LGS_LAUNCH((layernorm_bwd_kernel<KC, RB>), dim3(nblk), dim3(kThreads), 0, s, (const bf16*)hs,
+               (const bf16*)dy, (const bf16*)dhs, keep, keep_scale, (const bf16*)gamma, eps, rows, rpb, h,
+               (bf16*)g, (bf16*)dz, (float*)scratch);
   };
+  using I = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
   if (kc <= 1)
-    launch(std::integral_constant<int, 1>{});
+    launch(I{}, I4{});
   else if (kc <= 2)
-    launch(std::integral_constant<int, 2>{});
+    launch(I2{}, I4{});
   else if (kc <= 4)
-    launch(std::integral_constant<int, 4>{});
+    launch(I4{}, I2{});
   else
-    launch(std::integral_constant<int, 8>{});
-  LGS_LAUNCH(col_sum_kernel, dim3((2 * h + 255) / 256), dim3(256), 0, s, (const float*)scratch, nblk, h, dgamma,
+    launch(std::integral_constant<int, 8>{}, I{});
+  LGS_LAUNCH(col_sum_kernel, dim3((2 * h + 63) / 64), dim3(256), 0, s, (const float*)scratch, nblk, h, dgamma,
              dbeta);
   return LGS_LAUNCH_STATUS();
 }
