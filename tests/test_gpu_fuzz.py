@@ -233,4 +233,19 @@ def test_fuzz_sp_region(case):
                                    None if keep is None else keep.numpy(), 1.25)
     assert_close("hs", hs, rh, BF16)
     assert_close("y", y, ry, BF16)
+    # its backward from random dy and dhs, at the hs the forward stored
+    dy = torch.randn(n, h, generator=g).to(BF16)
+    dhs = torch.randn(n, h, generator=g).to(BF16)
+    G = torch.empty(n, h, dtype=BF16, device=d)
+    dz = torch.empty(n, h, dtype=BF16, device=d)
+    dg, db = torch.empty(h, dtype=F32, device=d), torch.empty(h, dtype=F32, device=d)
+    lgs.shard_layernorm_bwd(t, r, s, b, h, hs, dy.to(d), gamma.to(d), G, dz, dg, db, dhs=dhs.to(d),
+                            keep=None if keep is None else keep.to(d), keep_scale=1.25)
+    torch.cuda.synchronize()
+    ref = oracle.sp.exit_region_backward(f64(hs), f64(gamma), f64(dy), f64(dhs), 1e-5,
+                                         None if keep is None else keep.numpy(), 1.25)
+    assert_close("g", G, ref["g"], BF16)
+    assert_close("dz", dz, ref["dz"], BF16)
+    assert_close("dgamma", dg, ref["dgamma"], F32)
+    assert_close("dbeta", db, ref["dbeta"], F32)
 
