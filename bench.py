@@ -986,6 +986,71 @@ kernel_sources_sha256: {kernel_sources_digest()}
     print(txt)
 
 
+MFMA_RATE_CASES = (  # (label, blocks, waves per block, operands)
+    ("256 CUs, 2 waves per SIMD, N(0,1) x N(0,1)", 256, 8, "normal"),
+    ("256 CUs, 1 wave per SIMD, N(0,1) x N(0,1)", 256, 4, "normal"),
+    ("256 CUs, 2 waves per SIMD, N(0,1) x N(0,0.02) (activations x weights)", 256, 8, "weights"),
+    ("256 CUs, 2 waves per SIMD, zero operands", 256, 8, "zeros"),
+    ("128 CUs, 2 waves per SIMD, N(0,1) x N(0,1)", 128, 8, "normal"),
+    ("64 CUs, 2 waves per SIMD, N(0,1) x N(0,1)", 64, 8, "normal"),
+)
+
+
+def mfma_rate(torch, lgs, out_path, iters8=20000, reps=3):
+    """The matrix cores' bf16 rate with nothing but MFMAs to run
+    (lgs_test_mfma_rate): per case, the best of `reps` launches timed with HIP
+    events, and the shader clock the waves measured over their MFMA loops
+    (s_memtime cycles / s_memrealtime ticks at 100 MHz, median over waves).
+    Writes a markdown summary to out_path and prints it as one JSON line."""
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(11)
+
+    def ops_of(kind):
+        x = torch.randn(16, 64, 8, device=dev, generator=g)
+        if kind == "weights":
+            x[1::2] *= 0.02  # the B operands (pairs 2k + 1)
+        elif kind == "zeros":
+            x.zero_()
+        return x.to(torch.bfloat16)
+    rows = []
+    for label, blocks, waves, kind in MFMA_RATE_CASES:
+        ops = ops_of(kind)
+        out = torch.empty(blocks * waves * 8192, device=dev)
+        clocks = torch.empty(2 * blocks * waves, dtype=torch.int64, device=dev)
+        lgs.mfma_rate(blocks, waves, iters8 // 10, ops, out, clocks)  # warm-up
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lgs.mfma_rate(blocks, waves, iters8, ops, out, clocks)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if best is None or ms < best[0]:
+                ck = clocks.cpu().view(-1, 2).double()
+                best = (ms, float((ck[:, 0] / ck[:, 1]).median()) * 100.0)
+        flops = blocks * waves * iters8 * 64 * 32768
+        tf = flops / (best[0] * 1e-3) / 1e12
+        rows.append({"case": label, "blocks": blocks, "waves_per_block": waves, "ms": round(best[0], 3),
+                     "tflops": round(tf, 1), "frac_spec_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "tflops_per_cu": round(tf / blocks, 3), "clock_mhz": round(best[1], 0)})
+        progress(f"mfma rate: {label}: {tf:.1f} TFLOP/s at {best[1]:.0f} MHz")
+    lines = ["# Matrix-core bf16 rate with nothing but MFMAs to run (lgs_test_mfma_rate)", "",
+             "Command (from the repository root):", "", "```", f"python bench.py --mfma-rate {out_path}", "```", "",
+             f"Each wave runs 8 independent accumulator chains of v_mfma_f32_32x32x16_bf16 on operands held in "
+             f"registers (8 operand pairs rotating between consecutive instructions), {iters8 * 64} MFMAs per "
+             f"wave; one block per compute unit. Best of {reps} launches (HIP events). The clock is the shader "
+             "clock the waves counted over their MFMA loops (s_memtime cycles over s_memrealtime ticks of "
+             "100 MHz, median over the waves). Spec peak: 2516.6 TFLOP/s (256 CUs at 2.4 GHz).", "",
+             "| case | ms | TFLOP/s | of spec peak | TFLOP/s per busy CU | clock MHz |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['case']} | {r['ms']} | {r['tflops']} | {100 * r['frac_spec_peak']:.1f}% | "
+                     f"{r['tflops_per_cu']} | {r['clock_mhz']:.0f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps({"mfma_rate": rows}), flush=True)
+
+
 def progress(msg):
     """One line on stderr as each part of the run finishes (the JSON line on
     stdout stays the only output there)."""
@@ -1035,6 +1100,9 @@ def main():
                     help="run the 8.3B-shape kernels alone (for counter passes) and exit")
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="write the MFMA / LDS counter summary from the passes under DIR and exit")
+    ap.add_argument("--mfma-rate", metavar="OUT",
+                    help="measure the matrix cores' rate with nothing but MFMAs to run, write a summary to OUT "
+                         "and exit")
     ap.add_argument("--kernel-stats", nargs=3, metavar=("CSV", "TITLE", "COMMAND"),
                     help="print a markdown table of a rocprofv3 kernel_stats.csv and exit")
     args = ap.parse_args()
@@ -1070,6 +1138,10 @@ def main():
     if args.ce_stream_workload:
         from logit_gemm_shard_amd import binding as lgs_b
         ce_stream_workload(torch, lgs_b)
+        return
+    if args.mfma_rate:
+        from logit_gemm_shard_amd import binding as lgs_b
+        mfma_rate(torch, lgs_b, args.mfma_rate)
         return
 
     from logit_gemm_shard_amd import binding as lgs

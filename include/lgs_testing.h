@@ -1,7 +1,8 @@
 /*
  * lgs_testing.h -- the bf16 GEMM core of liblgs.so exposed for tests and
- * tile-shape sweeps.  Not part of the method's interface (include/lgs.h);
- * every entry point of lgs.h runs on this core.
+ * tile-shape sweeps, with the measurement hooks of the benchmark.  Not part
+ * of the method's interface (include/lgs.h); every entry point of lgs.h runs
+ * on this core.
  *
  * Conventions as in lgs.h (device pointers owned by the caller, row-major with
  * leading dimensions, asynchronous on `stream`, status codes before launch).
@@ -61,6 +62,25 @@ int lgs_test_mlp_bwd_plan(int M, int h, int f, int* parts, int* kchunk, int* tai
  */
 int lgs_test_xent_rows_bf16(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
                             const int32_t* targets, float* m, float* l, float* T, void* stream);
+
+/*
+ * The matrix cores' bf16 rate with nothing else to run, the ceiling against
+ * which the GEMM kernels' fractions of the spec peak are read.  Launches
+ * `blocks` workgroups of `waves` wave64s (1..8); each wave loads 8 operand
+ * pairs from `ops` (16 x 64 x 8 bf16: pair k is A_k at ops[(2k) * 512 + 8 lane
+ * + e], B_k at ops[(2k+1) * 512 + 8 lane + e], in v_mfma_f32_32x32x16_bf16's
+ * register layout) and runs 8 accumulator chains of 8 * iters8 MFMAs each,
+ * chain c in step j multiplying A_{(c+j)%8} by B_c, so chain c ends holding
+ * iters8 * (sum_k A_k) B_c.  Per wave: the chains' accumulators to `out`
+ * (wave w's float (c * 16 + r) * 64 + lane at out[w * 8192 + ...]: element r
+ * of lane `lane` of chain c), and to clocks[2w], clocks[2w+1] the shader clock
+ * cycles (s_memtime) and 100 MHz reference ticks (s_memrealtime) elapsed over
+ * the MFMA loop.  FLOPs per launch: blocks * waves * iters8 * 64 * 32768.
+ * `out` holds blocks * waves * 8192 floats, `clocks` 2 * blocks * waves
+ * uint64; `ops` 16-byte aligned.  1 <= blocks <= 65536, 0 <= iters8 <= 2^24.
+ */
+int lgs_test_mfma_rate(int blocks, int waves, int iters8, const void* ops, float* out, uint64_t* clocks,
+                       void* stream);
 
 /*
  * Debug builds (liblgs_debug.so, compiled with -DLGS_DEBUG): every entry point

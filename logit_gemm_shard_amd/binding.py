@@ -79,6 +79,7 @@ SIGNATURES = [
     ("lgs_test_mlp_bwd_plan", _i, [_i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     ("lgs_test_gemm_bf16", _i, [_i, _i, _i, _i, _i, _i, _p, _i64, _p, _i64, _p, _i64, _p]),
     ("lgs_test_xent_rows_bf16", _i, [_i, _i, _i, _p, _i64, _p, _p, _p, _p, _p]),
+    ("lgs_test_mfma_rate", _i, [_i, _i, _i, _p, _p, _p, _p]),
     ("lgs_test_debug_build", _i, []),
     ("lgs_test_set_dry_run", _i, [_i]),
     ("lgs_test_debug_checks", ctypes.c_long, []),
@@ -510,4 +511,21 @@ def xent_rows_bf16(Z, targets, vocab_start, m, l, T, stream=None):
     _check(lib().lgs_test_xent_rows_bf16(M, Vr, vocab_start, z, ldz, targets.data_ptr(), m.data_ptr(),
                                          l.data_ptr(), T.data_ptr(), _stream(stream)))
     return m, l, T
+
+
+def mfma_rate(blocks, waves, iters8, ops, out, clocks, stream=None):
+    """The matrix cores' rate probe (testing interface): `blocks` workgroups of
+    `waves` waves, 8 chains of 8 * iters8 MFMAs each on the operand pairs in
+    ops (bf16 [16, 64, 8]); accumulators to out (float32, blocks * waves *
+    8192), per-wave shader-clock and reference-tick counts to clocks (int64,
+    2 * blocks * waves)."""
+    if ops.dtype != torch.bfloat16 or ops.numel() != 16 * 64 * 8:
+        raise ValueError("ops must be bf16 with 16 * 64 * 8 elements")
+    if out.dtype != torch.float32 or out.numel() < blocks * waves * 8192:
+        raise ValueError("out must be float32 with blocks * waves * 8192 elements")
+    if clocks.dtype != torch.int64 or clocks.numel() < 2 * blocks * waves:
+        raise ValueError("clocks must be int64 with 2 * blocks * waves elements")
+    _check(lib().lgs_test_mfma_rate(blocks, waves, iters8, ops.data_ptr(), out.data_ptr(), clocks.data_ptr(),
+                                    _stream(stream)))
+    return out, clocks
 

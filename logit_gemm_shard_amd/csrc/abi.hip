@@ -824,6 +824,20 @@ LGS_API int lgs_test_gemm_bf16(int tile, int a_kmajor, int b_kmajor, int M, int 
                                        C, ldc, (hipStream_t)stream));
 }
 
+LGS_API int lgs_test_mfma_rate(int blocks, int waves, int iters8, const void* ops, float* out,
+                               uint64_t* clocks, void* stream) {
+  if (blocks < 1 || blocks > 65536) return fail(LGS_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
+  if (waves < 1 || waves > 8) return fail(LGS_ERR_INVALID_ARG, "waves must be in [1, 8]");
+  if (iters8 < 0 || iters8 > (1 << 24)) return fail(LGS_ERR_INVALID_ARG, "iters8 must be in [0, 2^24]");
+  if (!ops || !out || !clocks) return fail(LGS_ERR_INVALID_ARG, "ops, out and clocks are required");
+  if (!aligned(ops, 16)) return fail(LGS_ERR_UNSUPPORTED, "ops must be 16-byte aligned");
+  allow(ops, (size_t)16 * 64 * 16);
+  allow(out, lgs::mfma_rate_out_floats(blocks, waves) * 4);
+  allow(clocks, (size_t)blocks * waves * 16);
+  clear_hip_error();
+  return launched(lgs::mfma_rate(blocks, waves, iters8, ops, out, clocks, (hipStream_t)stream));
+}
+
 LGS_API int lgs_test_xent_rows_bf16(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
                                     const int32_t* targets, float* m, float* l, float* T,
                                     void* stream) {

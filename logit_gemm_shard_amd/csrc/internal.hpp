@@ -132,6 +132,14 @@ hipError_t xent_rows(int M, int Vr, int vocab_start, const void* Z, int64_t ldz,
 hipError_t xent_combine(int t, int64_t n, const float* parts, int64_t stride, bool lse_only,
                         float* loss, hipStream_t s);
 
+// Matrix-core rate: `blocks` workgroups of `waves` waves, each running
+// 64 iters8 MFMAs per accumulator chain on register operands (ops: 16 x 64
+// lanes x 8 bf16); accumulators to out (mfma_rate_out_floats floats), each
+// wave's shader-clock and 100 MHz reference counts to clocks (2 per wave).
+size_t mfma_rate_out_floats(int blocks, int waves);
+hipError_t mfma_rate(int blocks, int waves, int iters8, const void* ops, float* out, uint64_t* clocks,
+                     hipStream_t s);
+
 // The bf16 GEMM core with a store epilogue and an explicit tile (-1: picked).
 int num_tiles();
 bool tile_shape(int tile, int* bm, int* bn);

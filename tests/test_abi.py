@@ -414,6 +414,14 @@ def test_testing_interface(L):
     assert L.lgs_test_xent_rows_bf16(4, 64, 0, FAKE, 64, None, FAKE, FAKE, FAKE, None) == 1
     assert L.lgs_test_xent_rows_bf16(4, 64, 0, FAKE + 2, 64, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert L.lgs_test_xent_rows_bf16(0, 64, 0, None, 64, None, None, None, None, None) == 0
+    # matrix-core rate probe: block and wave counts, iteration bound, pointers, alignment
+    assert L.lgs_test_mfma_rate(0, 4, 1, FAKE, FAKE, FAKE, None) == 1
+    assert L.lgs_test_mfma_rate(65537, 4, 1, FAKE, FAKE, FAKE, None) == 1
+    assert L.lgs_test_mfma_rate(1, 9, 1, FAKE, FAKE, FAKE, None) == 1
+    assert L.lgs_test_mfma_rate(1, 4, (1 << 24) + 1, FAKE, FAKE, FAKE, None) == 1
+    assert L.lgs_test_mfma_rate(1, 4, -1, FAKE, FAKE, FAKE, None) == 1
+    assert L.lgs_test_mfma_rate(1, 4, 1, None, FAKE, FAKE, None) == 1
+    assert L.lgs_test_mfma_rate(1, 4, 1, FAKE + 8, FAKE, FAKE, None) == 2
 
 
 def test_binding_temporary_workspace_needs_a_recordable_stream():
