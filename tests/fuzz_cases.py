@@ -63,3 +63,16 @@ for _ in range(6):
     t = int(_rng.choice([1, 2, 4, 8]))
     SPLN_CASES.append((t, t * int(_rng.integers(1, 40)), int(_rng.integers(1, 5)), _w8(8, 16384),
                        int(_rng.integers(0, t)), bool(_rng.integers(0, 2))))
+
+# A second batch, drawn after every case above so those stay the same: wider
+# MLP blocks (multi-tile in every dimension, up to 2100) and CE slices with a
+# larger hidden size, to reach the 256-wide tiles and several rounds of blocks.
+for _ in range(6):
+    t = int(_rng.choice([1, 2, 4, 8]))
+    b, s = int(_rng.integers(1, 3)), int(_rng.integers(300, 1100))
+    MLP_CASES.append((b, s, _w8(520, 2100), t * _w8(136, max(136, 2100 // t)), t,
+                      int(_rng.integers(0, t)), str(_rng.choice(["erf", "tanh"]))))
+for _ in range(4):
+    t = int(_rng.choice([2, 4, 8]))
+    b, s = int(_rng.integers(1, 3)), int(_rng.integers(200, 700))
+    XENT_CASES.append((b, s, _w8(264, 1040), t * _w8(520, 3000), t))
