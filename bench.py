@@ -239,6 +239,140 @@ hbm_bytes_per_call: {nbytes(0) + nbytes(1):.0f}
     ce_counter_summary(d, fr, fw)
 
 
+STREAM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_stream_kernels_counters.txt")
+
+
+def stream_workload(torch, lgs, calls=5):
+    """The HBM-bound kernels alone, for counter passes: the sum of 8 partials
+    at the 70B shape, and at the 8.3B shape (s = 1024, b = 8, h = 3072, t = 8)
+    the sequence-parallel reduce-scatter, all-gather, fused region and its
+    backward; `calls` calls each, successive calls on successive ranks'
+    chunks as in the per-configuration timings."""
+    from logit_gemm_shard_amd.configs import WORKLOADS
+    dev = torch.device("cuda", 0)
+    bf = torch.bfloat16
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, device=dev) * std).to(bf)
+    M, h = 4096, 8192
+    parts = randn(8, M, h, std=0.05)
+    zs = torch.empty(M, h, dtype=bf, device=dev)
+    for _ in range(calls):
+        lgs.shard_partial_sum("sum", 8, M * h, parts, M * h, zs)
+    torch.cuda.synchronize()
+    del parts, zs
+    w = WORKLOADS["mlp_8p3b_fwd"]
+    t, M, h = w.t, w.M, w.h
+    chunk = M * h // t
+    parts = randn(t, M, h, std=0.05)
+    rs_out = torch.empty(M // t, h, dtype=bf, device=dev)
+    ag_in = [randn(t, M // t, h) for _ in range(3)]
+    ag_out = torch.empty(M, h, dtype=bf, device=dev)
+    res, dys, dhss = randn(t, M // t, h), randn(t, M // t, h), randn(t, M // t, h)
+    keep = (torch.rand(t, M // t, h, device=dev) > 0.1).to(torch.uint8)
+    gamma, beta = randn(h, std=0.1) + 1, randn(h, std=0.1)
+    hs, ys = torch.empty(M // t, h, dtype=bf, device=dev), torch.empty(M // t, h, dtype=bf, device=dev)
+    gg, dzz = torch.empty(M // t, h, dtype=bf, device=dev), torch.empty(M // t, h, dtype=bf, device=dev)
+    dgam, dbet = torch.empty(h, device=dev), torch.empty(h, device=dev)
+    lws = torch.empty(lgs.layernorm_bwd_workspace_bytes(t, w.s, w.b, h), dtype=torch.uint8, device=dev)
+    for i in range(calls):
+        lgs.shard_reduce_scatter(t, i % t, w.s, w.b, h, parts, M * h, rs_out)
+    for i in range(calls):
+        lgs.shard_all_gather(t, w.s, w.b, h, ag_in[i % 3], chunk, ag_out)
+    for i in range(calls):
+        lgs.shard_reduce_scatter_layernorm(t, i % t, w.s, w.b, h, parts, M * h, res[i % t], gamma, beta, hs, ys,
+                                           keep=keep[i % t], keep_scale=1 / 0.9)
+    for i in range(calls):
+        lgs.shard_layernorm_bwd(t, i % t, w.s, w.b, h, res[i % t], dys[i % t], gamma, gg, dzz, dgam, dbet,
+                                dhs=dhss[i % t], keep=keep[i % t], keep_scale=1 / 0.9, workspace=lws)
+    torch.cuda.synchronize()
+    print(json.dumps({"stream_workload": "done", "calls": calls}), flush=True)
+
+
+def _per_kernel_grid(path, counter):
+    """{(kernel name, grid size): [value per dispatch]} for one counter."""
+    import collections
+    import csv
+    by_disp, keys = collections.defaultdict(float), {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        by_disp[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        keys[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]))
+    out = collections.defaultdict(list)
+    for k, v in by_disp.items():
+        out[keys[k]].append(v)
+    return out
+
+
+def stream_summary(d):
+    """Write STREAM_COUNTERS_FILE from rocprofv3 --pmc passes under directory d:
+    pmc_st_FETCH_SIZE and pmc_st_WRITE_SIZE over `bench.py --stream-workload`,
+    pmc_copy_FETCH_SIZE and pmc_copy_WRITE_SIZE over `bench.py --copy-calibration`."""
+    import statistics
+
+    def csv_of(sub):
+        found = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not found:
+            raise SystemExit(f"no counter_collection.csv under {os.path.join(d, sub)}")
+        return found[0]
+    t, M83, h83 = 8, 8192, 3072
+    chunk = M83 * h83 // t
+    nblk = 256
+    # (label, name pattern, grid size or None, algorithmic bytes)
+    kernels = (
+        ("sum of 8 partials, 70B [4096, 8192] (psum_vec_kernel)", "psum_vec_kernel", 8192 * 256, 9 * 4096 * 8192 * 2),
+        ("SP reduce-scatter, rank rows of 8 partials (psum_vec_kernel)", "psum_vec_kernel", (chunk // 2048) * 256,
+         (t + 1) * chunk * 2),
+        ("SP all-gather (gather_vec_kernel)", "gather_vec_kernel", None, 2 * M83 * h83 * 2),
+        ("SP region fused (rs_layernorm_kernel)", "rs_layernorm_kernel", None,
+         (t + 1) * chunk * 2 + chunk + 2 * chunk * 2 + 2 * h83 * 2),
+        ("SP region backward, rows (layernorm_bwd_kernel)", "layernorm_bwd_kernel", None,
+         3 * chunk * 2 + chunk + 2 * chunk * 2 + h83 * 2 + nblk * 2 * h83 * 4),
+        ("SP region backward, column sum (col_sum_kernel)", "col_sum_kernel", None, nblk * 2 * h83 * 4 + 2 * h83 * 4),
+    )
+    med, cal = {}, {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        got = _per_kernel_grid(csv_of(f"pmc_st_{c}"), c)
+        copy = _per_kernel(csv_of(f"pmc_copy_{c}"), c)
+        cp = [v for n, v in copy.items() if "neg" in n]
+        if len(cp) != 1:
+            raise SystemExit(f"{c}: expected one copy kernel, found {len(cp)}")
+        cal[c] = statistics.median(cp[0])
+        for label, pat, grid, _ in kernels:
+            vals = [v for (n, g), v in got.items() if pat in n and (grid is None or g == grid)]
+            if len(vals) != 1:
+                raise SystemExit(f"{c}: {label}: expected one kernel, found {len(vals)}")
+            med[(label, c)] = statistics.median(vals[0])
+    fr = (1 << 30) / (cal["FETCH_SIZE"] * 1024)
+    fw = (1 << 30) / (cal["WRITE_SIZE"] * 1024)
+    lines = []
+    for label, _, _, alg in kernels:
+        rd, wr = med[(label, "FETCH_SIZE")] * 1024 * fr, med[(label, "WRITE_SIZE")] * 1024 * fw
+        lines.append(f"#   {label}:\n#     read {rd / 1e6:.1f} MB + written {wr / 1e6:.1f} MB = {(rd + wr) / 1e6:.1f} MB"
+                     f" against {alg / 1e6:.1f} MB algorithmic ({(rd + wr) / alg:.3f}x)")
+    body = "\n".join(lines)
+    txt = f"""# L2-to-fabric traffic of the HBM-bound kernels: the sum of 8 partials at the
+# 70B shape and the sequence-parallel kernels at the 8.3B shape (rank chunks of
+# 1024 rows x 3072; t = 8), from rocprofv3 counter passes, one counter per run:
+#
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc_st/pmc_st_FETCH_SIZE -o p -- python bench.py --stream-workload
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc_st/pmc_st_WRITE_SIZE -o p -- python bench.py --stream-workload
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc_st/pmc_copy_FETCH_SIZE -o p -- python bench.py --copy-calibration
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc_st/pmc_copy_WRITE_SIZE -o p -- python bench.py --copy-calibration
+#   python bench.py --stream-summary rocprof_out/pmc_st      (writes this file)
+#
+# Per launch (median over five), FETCH_SIZE x 1024 x {fr:.4f} and WRITE_SIZE x 1024 x {fw:.4f}
+# (the calibration of the plain 1 GiB copy); algorithmic bytes: every input read once and
+# every output written once (the backward's rows kernel also writes its fp32 column partials,
+# which the column sum reads):
+{body}
+kernel_sources_sha256: {kernel_sources_digest()}
+"""
+    open(STREAM_COUNTERS_FILE, "w").write(txt)
+    print(txt)
+
+
 XENT_COUNTERS_FILE = os.path.join(ROOT, "profiles", "xent_8p3b_hbm_counters.txt")
 
 
@@ -1125,6 +1259,10 @@ def main():
                     help="run the 8.3B-shape kernels alone (for counter passes) and exit")
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="write the MFMA / LDS counter summary from the passes under DIR and exit")
+    ap.add_argument("--stream-workload", action="store_true",
+                    help="run the HBM-bound kernels alone (for counter passes) and exit")
+    ap.add_argument("--stream-summary", metavar="DIR",
+                    help="write the HBM-bound kernels' counter summary from the passes under DIR and exit")
     ap.add_argument("--mfma-rate", metavar="OUT",
                     help="measure the matrix cores' rate with nothing but MFMAs to run, write a summary to OUT "
                          "and exit")
@@ -1142,6 +1280,9 @@ def main():
         return
     if args.ce_stream_summary:
         ce_stream_summary(args.ce_stream_summary)
+        return
+    if args.stream_summary:
+        stream_summary(args.stream_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's shard: the library is measured on one GPU "
@@ -1163,6 +1304,10 @@ def main():
     if args.ce_stream_workload:
         from logit_gemm_shard_amd import binding as lgs_b
         ce_stream_workload(torch, lgs_b)
+        return
+    if args.stream_workload:
+        from logit_gemm_shard_amd import binding as lgs_b
+        stream_workload(torch, lgs_b)
         return
     if args.mfma_rate:
         from logit_gemm_shard_amd import binding as lgs_b
