@@ -76,3 +76,17 @@ for _ in range(4):
     t = int(_rng.choice([2, 4, 8]))
     b, s = int(_rng.integers(1, 3)), int(_rng.integers(200, 700))
     XENT_CASES.append((b, s, _w8(264, 1040), t * _w8(520, 3000), t))
+for _ in range(3):
+    t = int(_rng.choice([2, 4, 8]))
+    b, s = int(_rng.integers(1, 3)), int(_rng.integers(300, 900))
+    SWIGLU_CASES.append((b, s, _w8(520, 1600), t * _w8(136, max(136, 1600 // t)), t, int(_rng.integers(0, t))))
+for _ in range(3):
+    t = int(_rng.choice([2, 4, 8]))
+    n_kv = t * int(_rng.integers(1, 3))
+    n_q = n_kv * int(_rng.choice([2, 4]))
+    b, s = int(_rng.integers(1, 3)), int(_rng.integers(300, 900))
+    ATTN_CASES.append((b, s, _w8(1040, 2100), n_q, n_kv, _w8(64, 136), t, int(_rng.integers(0, t))))
+for _ in range(2):
+    t = int(_rng.choice([4, 8]))
+    SPLN_CASES.append((t, t * int(_rng.integers(100, 300)), int(_rng.integers(1, 5)), _w8(1024, 8192),
+                       int(_rng.integers(0, t)), bool(_rng.integers(0, 2))))
